@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the Delta-CoMe multi-tenant decode step on one MI355X.
+
+Workload (synthetic, seeded): Llama-2-7B decoder shapes, 32 layers x 7
+matrices (q,k,v,o 4096x4096; gate,up 11008x4096; down 4096x11008), one
+shared bf16 backbone, 50 distinct tenant deltas resident in HBM, each at the
+1/16 budget (8/3/2-bit rank groups 2/32/968 or 2/47/1414), 64 decode tokens
+routed to tenants by Zipf(1.1).  One step = one dc_apply_multitenant call per
+(layer, matrix): routing, activation staging, backbone product, V side,
+U side and the bf16 epilogue, all on the GPU.
+
+Prints one JSON line.  value = tokens/s of the fused step (backbone +
+delta).  The delta-only step (backbone product skipped) is timed too, as
+the packed-delta bandwidth figure.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "delta-apply tokens/s + effective packed-delta HBM GB/s (% of peak), 7B shapes"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """HIP events through libamdhip64 (plumbing for per-kernel timing)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def build_c2(layers, dev, torch, trs, synth):
+    """Resident deltas for every (layer, matrix, tenant) plus backbone and x."""
+    import numpy as np
+    n_ten, T = synth.C2_TENANTS, synth.C2_TOKENS
+    mats = synth.LLAMA2_7B
+    specs = [(o, i) + synth.groups_for(o, i, 16) for _, o, i in mats]
+    # Per distinct spec: two host-packed templates (scale/zero/sigma) and the
+    # mask of valid code bits; codes of every tenant are drawn on the GPU.
+    tmpl, mask = {}, {}
+    for sp in sorted(set(specs)):
+        out, inn, n8, n3, n2 = sp
+        r = n8 + n3 + n2
+        ts = []
+        for k in range(2):
+            d = synth.random_delta_codes(np.random.default_rng(1000 + 7 * k + out), out, inn, n8, n3, n2)
+            nc = trs.dc_pack_codes(sp, np.zeros_like(d.codes_u), np.zeros_like(d.codes_v), d.sz_u, d.sz_v, d.sigma)
+            ts.append(torch.from_numpy(nc).to(dev))
+        tmpl[sp] = ts
+        widths = np.array([8] * n8 + [3] * n3 + [2] * n2)
+        full = ((1 << widths) - 1).astype(np.uint8)[:, None]
+        mk = trs.dc_pack_codes(sp, np.broadcast_to(full, (r, out)), np.broadcast_to(full, (r, inn)),
+                               np.zeros((r, out // 128, 2), np.uint16), np.zeros((r, inn // 128, 2), np.uint16),
+                               np.zeros(r, np.float32))
+        mask[sp] = torch.from_numpy(mk).to(dev)
+    per_layer = sum(trs.dc_packed_bytes(sp) for sp in specs) * n_ten
+    pool = torch.empty(per_layer * layers, dtype=torch.uint8, device=dev)
+    chunk = 1 << 29
+    for o in range(0, pool.numel(), chunk):
+        n = min(chunk, pool.numel() - o)
+        pool[o:o + n] = torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev)
+    views = []
+    off = 0
+    for l in range(layers):
+        row = []
+        for m, sp in enumerate(specs):
+            nb = trs.dc_packed_bytes(sp)
+            vs = []
+            for k in range(n_ten):
+                buf = pool[off:off + nb]
+                buf.bitwise_and_(mask[sp]).bitwise_or_(tmpl[sp][(k + l + m) % 2])
+                vs.append(trs.DeltaView(sp, buf))
+                off += nb
+            row.append(vs)
+        views.append(row)
+    W = [[(torch.randn(o, i, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16) for _, o, i in mats]
+         for _ in range(layers)]
+    X = [[torch.randn(T, i, device=dev).to(torch.bfloat16).view(torch.int16) for _, o, i in mats]
+         for _ in range(layers)]
+    torch.cuda.synchronize()
+    return specs, views, W, X, pool
+
+
+def cpu_baseline(trs, synth, budget_s=20.0):
+    """The oracle (plain numpy fp64, applied from packed buffers) timed on a
+    bounded sample of the same workload, extrapolated to one whole step."""
+    import numpy as np
+    from oracle import apply as oap
+    from oracle import layout
+    threads = len(os.sched_getaffinity(0))
+    ids = synth.c2_ids()
+    touched = sorted(set(ids.tolist()))
+    per_shape = {}
+    sample = []
+    t_start = time.time()
+    for mi in (0, 4, 6):                      # q (4096^2), gate (11008x4096), down (4096x11008)
+        _, out, inn = synth.LLAMA2_7B[mi]
+        w = synth.make_c2_base(0, mi)
+        x = synth.make_c2_x(0, mi)
+        t0 = time.perf_counter()
+        oap.apply_factored(w, x, np.zeros((0, out)), np.zeros(0), np.zeros((0, inn)))
+        t_base = time.perf_counter() - t0
+        times = []
+        for k in touched[:2]:
+            d = synth.make_c2_delta(0, mi, k)
+            buf = layout.pack(d.spec, d.codes_u, d.codes_v, d.sz_u, d.sz_v, d.sigma)
+            sel = np.nonzero(ids == k)[0]
+            t0 = time.perf_counter()
+            oap.apply_packed(d.spec, buf, None, x[sel])
+            times.append(time.perf_counter() - t0)
+            sample.append("layer0/%s/tenant%d" % (synth.LLAMA2_7B[mi][0], k))
+        per_shape[mi] = (t_base, float(np.mean(times)))
+        if time.time() - t_start > budget_s:
+            break
+    # step = 32 layers x (4 square + 2 up-proj + 1 down-proj) x (base + touched tenants)
+    counts = {0: 4, 4: 2, 6: 1}
+    step_s = 0.0
+    for mi, c in counts.items():
+        tb, td = per_shape.get(mi, per_shape[0])
+        step_s += synth.C2_LAYERS * c * (tb + len(touched) * td)
+    return {"value": synth.C2_TOKENS / step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "numpy fp64 oracle from packed buffers (unpack, dequant, W x + U(s*(V x))) on "
+                      "%s, averaged per matrix shape and extrapolated to 32 layers x 7 matrices x %d "
+                      "touched tenants + backbone; %.1f s of CPU work" % (", ".join(sample), len(touched),
+                                                                          time.time() - t_start)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path shards by tenant with no collective, and "
+              "this build runs on a single MI355X (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import tenant_rank_serving_amd as trs
+
+    trs.lib()
+    dev = torch.device("cuda:0")
+    hip = Hip()
+    log("building c2 workload: %d layers x 7 matrices x %d tenants" % (args.layers, synth.C2_TENANTS))
+    t0 = time.time()
+    specs, views, W, X, pool = build_c2(args.layers, dev, torch, trs, synth)
+    ids_h = synth.c2_ids()
+    ids = torch.from_numpy(ids_h).to(dev)
+    touched = sorted(set(ids_h.tolist()))
+    T = synth.C2_TOKENS
+    log("resident deltas: %.2f GB, backbone %.2f GB, built in %.1f s" %
+        (pool.numel() / 1e9, sum(w.numel() * 2 for row in W for w in row) / 1e9, time.time() - t0))
+    ws_bytes = max(trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, [sp] * synth.C2_TENANTS, T) for sp in specs)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ys = {sp[0]: torch.empty((T, sp[0]), dtype=torch.int16, device=dev) for sp in specs}
+
+    def calls(fused):
+        return [trs.MultitenantCall(views[l][m], W[l][m] if fused else None, X[l][m], ids, ys[specs[m][0]], ws)
+                for l in range(args.layers) for m in range(len(specs))]
+
+    # bytes per step: packed deltas of the touched tenants (algorithmic), backbone
+    delta_bytes = args.layers * len(touched) * sum(trs.dc_algorithmic_bytes(sp) for sp in specs)
+    base_bytes = args.layers * sum(sp[0] * sp[1] * 2 for sp in specs)
+
+    def timed_steps(cl, steps, warmup):
+        for _ in range(warmup):
+            for c in cl:
+                c()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            for c in cl:
+                c()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    results = {}
+    for mode in ("fused", "delta"):
+        cl = calls(mode == "fused")
+        log("timing %s step: warmup %d, steps %d" % (mode, args.warmup, args.steps))
+        results[mode] = timed_steps(cl, args.steps, args.warmup)
+        log("%s: %.3f ms/step" % (mode, results[mode]))
+
+    # Per-kernel durations: one more pass of the fused step with HIP events
+    # recorded between the stages of every call, on the launch stream.
+    cl = calls(True)
+    evs = [[hip.event() for _ in range(len(trs.STAGES) + 1)] for _ in cl]
+    for c, ev in zip(cl, evs):
+        c.timed(ev)
+    torch.cuda.synchronize()
+    stage_ms = {s: [] for s in trs.STAGES}
+    for ev in evs:
+        for si, s in enumerate(trs.STAGES):
+            stage_ms[s].append(hip.elapsed_ms(ev[si], ev[si + 1]))
+    for ev in evs:
+        for e in ev:
+            hip.destroy(e)
+    stage_avg = {s: float(np.mean(v)) for s, v in stage_ms.items()}
+    stage_tot = {s: float(np.sum(v)) for s, v in stage_ms.items()}
+    log("stage averages (ms/call): " + ", ".join("%s %.4f" % kv for kv in stage_avg.items()))
+
+    # Algorithmic bytes per launch of each heavy stage, averaged over calls.
+    def side_bytes(sp, side):
+        out, inn, n8, n3, n2 = sp
+        r = n8 + n3 + n2
+        n = inn if side == "v" else out
+        g = (inn if side == "v" else out) // 128
+        return (8 * n8 + 3 * n3 + 2 * n2) * n // 8 + r * g * 4 + (4 * r if side == "v" else 0)
+
+    ncalls = len(cl)
+    per_launch = {
+        "vside": np.mean([len(touched) * side_bytes(specs[i % len(specs)], "v") + T * specs[i % len(specs)][1] * 2
+                          for i in range(ncalls)]),
+        "uside": np.mean([len(touched) * side_bytes(specs[i % len(specs)], "u") + T * specs[i % len(specs)][0] * 2
+                          for i in range(ncalls)]),
+        "base": np.mean([specs[i % len(specs)][0] * specs[i % len(specs)][1] * 2 + T * specs[i % len(specs)][1] * 2
+                         for i in range(ncalls)]),
+    }
+    dom = max(per_launch, key=lambda s: stage_tot[s])
+    achieved = per_launch[dom] / (stage_avg[dom] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_launch": int(per_launch[dom]), "avg_launch_ms": round(stage_avg[dom], 5),
+            "stages_avg_ms": {s: round(v, 5) for s, v in stage_avg.items()}}
+
+    ms = results["fused"]
+    ms_d = results["delta"]
+    out = {
+        "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "multi-tenant decode, Llama-2-7B shapes: %d layers x 7 matrices, 50 resident "
+                               "1/16 deltas (8/3/2-bit), shared bf16 backbone, 64 tokens Zipf(1.1)" % args.layers,
+                   "layers": args.layers, "tenants_resident": synth.C2_TENANTS, "tenants_touched": len(touched),
+                   "tokens": T, "step": "fused"},
+        "packed_delta_GBps": round(delta_bytes / (ms * 1e-3) / 1e9, 1),
+        "fused_total_GBps": round((delta_bytes + base_bytes) / (ms * 1e-3) / 1e9, 1),
+        "delta_only": {"ms_per_step": round(ms_d, 4), "tokens_per_s": round(T / (ms_d * 1e-3), 1),
+                       "packed_delta_GBps": round(delta_bytes / (ms_d * 1e-3) / 1e9, 1),
+                       "pct_of_hbm_peak": round(100 * delta_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(trs, synth)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,274 @@
+/*
+ * deltacome.h -- C ABI of libdeltacome.so: the Delta-CoMe mixed-precision
+ * low-rank delta apply on AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  A fine-tuned model is served as its backbone W_base plus
+ * a compressed delta.  The delta is decomposed by SVD into singular pairs
+ * (u_i, sigma_i, v_i); pairs with larger singular values keep more bits: a
+ * first group at 8 bits, the next at 3 bits, the next at 2 bits, the rest
+ * dropped (0 bits).  Many such deltas share one bf16 backbone.  For a token x
+ * served by tenant k:
+ *
+ *     y = W_base x + U_k diag(sigma_k) (V_k x)        (bf16 out, fp32 sums)
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "Delta-CoMe - 清华联合OpenBMB等高校开源的新型增量压缩算法" (paooo.com):
+ *        "Delta-CoMe的技术原理" (low-rank decomposition of the delta by SVD;
+ *        mixed-precision bits per singular vector, larger singular values at
+ *        higher precision; long-tail spectrum) and "Delta-CoMe的应用场景"
+ *        (multi-tenant serving of many fine-tuned models).
+ *   [P2] "Delta-CoMe: Training-Free Delta-Compression with Mixed-Precision for
+ *        Large Language Models" (atlas.scime.ai summary): "Approach" (8/3/2
+ *        bits for successive groups, smallest dropped at 0 bits, same size as
+ *        BitDelta at 1/16), "Key results" (a GPU kernel for the apply; 50
+ *        models served on one GPU), "Problem" (delta = fine-tuned minus
+ *        backbone).
+ *   [P4] "Enhancing Delta Compression in LLMs via SVD-based Quantization
+ *        Error Minimization" (gist.science): §2.1 (W = U Sigma V, V quantized
+ *        row by row).
+ *
+ * Storage format.  The pages fix no layout.  This library fixes one: b-bit
+ * codes packed little-endian into uint32 words (3-bit codes 32 per 3 words)
+ * and, for each group of 128 consecutive elements of a singular vector, an
+ * fp16 scale s and an fp16 zero z from asymmetric round-to-nearest min/max
+ * quantization; the dequantized value of code q is fp16(s * (q - z)).
+ *
+ * One packed buffer = one tenant's delta for one matrix, spec
+ * (out, in, n8, n3, n2); r = n8+n3+n2; Gi = in/128; Go = out/128.  Ranks are
+ * numbered 0..r-1: the 8-bit segment, then the 3-bit, then the 2-bit one;
+ * "local rank" is the index inside a segment of n = n_b ranks.
+ * Bitstream rule: codes c_0, c_1, ... at b bits occupy bits [b*k, b*k+b) of
+ * a stream of uint32 words, bit t of the stream being bit t%32 of word t/32.
+ * Regions, each at a multiple of 256 bytes from the buffer start, in order:
+ *   SIGMA  fp32 [r]
+ *   VC_b   b = 8,3,2: V codes, [n][Gi][4b] words; the group's 128 codes of
+ *          v_i form one bitstream.
+ *   VS_b   V scale/zero, uint32 [Gi][pad4(n)]: fp16 scale | fp16 zero << 16.
+ *   UC_8   U codes at 8 bits, bytes [out][n8], byte (o,i) = code of u_i at
+ *          row o.
+ *   UC_b   b = 3,2: U codes packed along the rank axis.  Ranks are cut into
+ *          K-blocks of 32 (KB = ceil(n/32)); K-block kb of row o is the
+ *          bitstream of the codes of u_{32kb}..u_{32kb+31} at row o (codes
+ *          past n are 0), b words long, except the last K-block, which keeps
+ *          wl = ceil(m*b/32) words for its m = n-32(KB-1) ranks.  Rows go in
+ *          16-row tiles; a tile is [KB-1][16][b] words then [16][wl] words
+ *          (the 16 rows of one K-block contiguous).
+ *   US_b   U scale/zero, uint32 [Go][pad4(n)]; entry (g,i) covers rows
+ *          128g..128g+127 of u_i.
+ * Pad entries are zero.  Total size rounded up to 256 bytes.
+ *
+ * Conventions for every call.
+ *   - Every argument is checked on the host before anything is enqueued; a
+ *     call that returns an error has enqueued nothing and written nothing.
+ *   - Device calls are asynchronous on `stream` (a hipStream_t passed as
+ *     void*; NULL = the null stream) and never synchronize; device faults show
+ *     at the caller's next synchronization.
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     and keeps no mutable global state; calls on different streams with
+ *     different workspaces may run concurrently.  Two calls that share a
+ *     workspace must be ordered by the caller.
+ *   - bf16 and fp16 tensors are passed as uint16_t bit patterns, row-major.
+ *   - Device pointers must be 16-byte aligned (DC_ERR_ALIGN), the workspace
+ *     256-byte aligned.
+ */
+#ifndef DELTACOME_H
+#define DELTACOME_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dc_status;
+enum {
+  DC_OK = 0,
+  DC_ERR_INVALID_ARG = -1, /* null pointer, overlap of x and y, n/T out of range */
+  DC_ERR_SHAPE = -2,       /* out/in not a positive multiple of 128, negative
+                              counts, r > min(out,in), tenants of one call with
+                              different out/in */
+  DC_ERR_ALIGN = -3,       /* device pointer not 16-B aligned (workspace 256-B) */
+  DC_ERR_BUFFER = -4,      /* buffer or workspace smaller than required */
+  DC_ERR_RANGE = -5,       /* dc_pack: non-finite input or fp16 scale overflow */
+  DC_ERR_HIP = -6,         /* a HIP launch or query failed */
+  DC_ERR_UNSUPPORTED = -7  /* a limit of this build (see DC_MAX_TENANTS) */
+};
+
+/* Most tenants one multi-tenant or prefill call can address. */
+#define DC_MAX_TENANTS 128
+
+typedef struct dc_spec {
+  int32_t out; /* rows of the matrix (output features), multiple of 128 */
+  int32_t in;  /* columns (input features), multiple of 128 */
+  int32_t n8;  /* pairs stored at 8 bits (largest singular values) */
+  int32_t n3;  /* next pairs, at 3 bits */
+  int32_t n2;  /* next pairs, at 2 bits; all later pairs are dropped */
+} dc_spec;
+
+/* A packed delta in device memory: the spec and the buffer's first byte.
+ * Built by pointer arithmetic only (no copy). */
+typedef struct dc_delta_view {
+  dc_spec spec;
+  const void* base; /* device pointer to dc_packed_bytes(&spec) bytes */
+} dc_delta_view;
+
+/* Region ids for dc_region, in storage order. */
+enum {
+  DC_REG_SIGMA = 0,
+  DC_REG_VC8, DC_REG_VC3, DC_REG_VC2,
+  DC_REG_VS8, DC_REG_VS3, DC_REG_VS2,
+  DC_REG_UC8, DC_REG_UC3, DC_REG_UC2,
+  DC_REG_US8, DC_REG_US3, DC_REG_US2,
+  DC_REG_COUNT
+};
+
+/* Operation ids for dc_workspace_bytes. */
+enum { DC_OP_DECODE = 0, DC_OP_MULTITENANT = 1, DC_OP_PREFILL = 2 };
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* dc_status_string(dc_status s);
+
+/* Checks a spec against the shape rules (DC_OK or DC_ERR_SHAPE /
+ * DC_ERR_INVALID_ARG for NULL). */
+dc_status dc_check_spec(const dc_spec* spec);
+
+/* Size in bytes of the packed buffer of `spec` (0 if the spec is invalid). */
+size_t dc_packed_bytes(const dc_spec* spec);
+
+/* Bytes the kept pairs need without padding: codes + 4 B of scale/zero per
+ * 128-element group + 4 B of sigma per pair.  This is the "algorithmic"
+ * packed-delta byte count used for bandwidth figures. */
+size_t dc_algorithmic_bytes(const dc_spec* spec);
+
+/* Byte offset and size of region `region` (DC_REG_*) inside the buffer. */
+dc_status dc_region(const dc_spec* spec, int32_t region, size_t* offset, size_t* size);
+
+/*
+ * dc_pack -- quantize and pack one delta (host, synchronous, deterministic).
+ * [P1] technical principles and [P2] "Approach": pairs ordered by descending
+ * singular value, the first n8 at 8 bits, the next n3 at 3, the next n2 at 2.
+ *   U      host fp32 [r][out], row i = u_i (r = n8+n3+n2 rows are read)
+ *   sigma  host fp32 [r], stored unquantized
+ *   V      host fp32 [r][in], row i = v_i
+ *   out    host buffer of out_bytes >= dc_packed_bytes(spec); fully written
+ * Quantizer, per 128-element group w of one vector at b bits, in fp64:
+ *   mn = min(0, min w), mx = max(0, max w), maxq = 2^b-1,
+ *   s_h = fp16_RNE((mx-mn)/maxq) (direct fp64 -> fp16; 1.0 if it is 0),
+ *   z = clamp(rint(-mn/s_h), 0, maxq), q = clamp(rint(w/s_h) + z, 0, maxq),
+ *   rint = round half to even.
+ * Errors: DC_ERR_INVALID_ARG (NULL), DC_ERR_SHAPE, DC_ERR_BUFFER,
+ * DC_ERR_RANGE (non-finite input, or s_h overflows fp16).  On error `out`
+ * may be partly written.
+ */
+dc_status dc_pack(const dc_spec* spec, const float* U, const float* sigma, const float* V,
+                  void* out, size_t out_bytes);
+
+/*
+ * dc_pack_codes -- pack already-quantized codes (host, synchronous).
+ *   codes_u  host uint8 [r][out], code of u_i at row o (< 2^b of its segment)
+ *   codes_v  host uint8 [r][in]
+ *   sz_u     host uint16 [r][out/128][2]: (fp16 scale bits, fp16 zero bits)
+ *   sz_v     host uint16 [r][in/128][2]
+ *   sigma    host fp32 [r]
+ * Errors: DC_ERR_INVALID_ARG (NULL), DC_ERR_SHAPE, DC_ERR_BUFFER,
+ * DC_ERR_RANGE (a code does not fit its segment's width).
+ */
+dc_status dc_pack_codes(const dc_spec* spec, const uint8_t* codes_u, const uint8_t* codes_v,
+                        const uint16_t* sz_u, const uint16_t* sz_v, const float* sigma,
+                        void* out, size_t out_bytes);
+
+/*
+ * dc_unpack -- inverse of dc_pack_codes (host, synchronous).  Reads
+ * dc_packed_bytes(spec) bytes of `packed` (host); writes the five arrays in
+ * the layouts of dc_pack_codes.  Errors: DC_ERR_INVALID_ARG, DC_ERR_SHAPE,
+ * DC_ERR_BUFFER (packed_bytes too small).
+ */
+dc_status dc_unpack(const dc_spec* spec, const void* packed, size_t packed_bytes,
+                    uint8_t* codes_u, uint8_t* codes_v, uint16_t* sz_u, uint16_t* sz_v,
+                    float* sigma);
+
+/*
+ * dc_workspace_bytes -- device workspace that one call of `op` needs.
+ *   specs  host array of n specs (the tenants' specs; n = 1 for decode)
+ *   T      tokens of the call
+ * Returns 0 on invalid arguments.
+ */
+size_t dc_workspace_bytes(int32_t op, const dc_spec* specs, int32_t n, int32_t T);
+
+/*
+ * dc_apply_decode -- one tenant, T tokens.  [P2] "Key results" (the GPU
+ * kernel that applies the mixed-precision delta); [P1] technical principles.
+ *   d       host struct; d->base is device memory holding the packed delta
+ *   W_base  device bf16 [out][in] (nn.Linear layout), or NULL = delta only
+ *   x       device bf16 [T][in]
+ *   y       device bf16 [T][out], fully overwritten with
+ *           RNE_bf16(W_base x + U diag(sigma) V x), sums in fp32, rounded once
+ *   ws      device workspace of ws_bytes >= dc_workspace_bytes(DC_OP_DECODE,..)
+ *   stream  hipStream_t
+ * T = 0 is a no-op returning DC_OK.  x and y must not overlap.
+ */
+dc_status dc_apply_decode(const dc_delta_view* d, const uint16_t* W_base, const uint16_t* x,
+                          uint16_t* y, int32_t T, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dc_apply_multitenant -- n tenants over one backbone, tokens routed by id.
+ * [P1] application scenarios (multi-tenant serving); [P2] "Key results" (50
+ * models on one GPU).
+ *   views       host array [n] (n <= DC_MAX_TENANTS); all with the same
+ *               out/in; n8/n3/n2 may differ per tenant
+ *   W_base      device bf16 [out][in] or NULL
+ *   x           device bf16 [T][in]
+ *   tenant_ids  device int32 [T]; id k in [0,n) selects views[k]; -1 means
+ *               backbone only.  Any other id is a contract violation: the
+ *               token is served backbone-only and bit 0 of the uint32 at byte
+ *               0 of ws is set (the word is cleared by every call).
+ *   y           device bf16 [T][out], fully overwritten, original token order
+ * Routing happens on the device; the call never reads the ids on the host.
+ */
+dc_status dc_apply_multitenant(const dc_delta_view* views, int32_t n, const uint16_t* W_base,
+                               const uint16_t* x, const int32_t* tenant_ids, uint16_t* y,
+                               int32_t T, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dc_apply_multitenant_timed -- dc_apply_multitenant that also records
+ * caller-owned HIP events on `stream` between its kernels, so a caller can
+ * time each stage (hipEventElapsedTime) without a profiler.
+ *   events  host array of DC_STAGE_COUNT + 1 hipEvent_t (as void*); entry s
+ *           is recorded just before stage s is enqueued, the last entry
+ *           after the final stage; NULL entries are skipped.  A stage that
+ *           does not run (no backbone, no ranks) leaves its start and the
+ *           next stage's start on the same point of the stream.
+ * Results are identical to dc_apply_multitenant.
+ */
+enum { DC_STAGE_ROUTE = 0, DC_STAGE_XPREP, DC_STAGE_BASE, DC_STAGE_VSIDE, DC_STAGE_USIDE,
+       DC_STAGE_COUNT };
+dc_status dc_apply_multitenant_timed(const dc_delta_view* views, int32_t n, const uint16_t* W_base,
+                                     const uint16_t* x, const int32_t* tenant_ids, uint16_t* y,
+                                     int32_t T, void* ws, size_t ws_bytes, void* stream,
+                                     void* const* events);
+
+/*
+ * dc_apply_prefill -- n tenants, tokens grouped by tenant: tokens
+ * seg_offsets[k] .. seg_offsets[k+1]-1 belong to views[k].
+ *   seg_offsets  host int32 [n+1], non-decreasing, seg_offsets[0] = 0;
+ *                T = seg_offsets[n]
+ *   x, y         device bf16 [T][in], [T][out]
+ * Same conventions as dc_apply_multitenant.
+ */
+dc_status dc_apply_prefill(const dc_delta_view* views, int32_t n, const uint16_t* W_base,
+                           const uint16_t* x, const int32_t* seg_offsets, uint16_t* y,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dc_dequant -- the dequantized fp16 singular vectors, for tests.
+ *   u_fp16  device fp16 bits [r][out], row i = fp16(s*(q-z)) of u_i
+ *   v_fp16  device fp16 bits [r][in]
+ * Values are bit-identical to the quantizer's definition above.
+ */
+dc_status dc_dequant(const dc_delta_view* d, uint16_t* u_fp16, uint16_t* v_fp16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DELTACOME_H */

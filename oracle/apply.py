@@ -75,9 +75,10 @@ def brute_force(w_bits, x_bits, u_hat, sigma, v_hat) -> np.ndarray:
     return np.array(y)
 
 
-def dequant_pairs(codes_u, codes_v, sz_u, sz_v):
-    """fp16 singular vectors from codes and (scale, zero) bit patterns."""
-    return quant.dequant_all(codes_u, sz_u), quant.dequant_all(codes_v, sz_v)
+def dequant_pairs(codes_u, codes_v, sz_u, sz_v, exact: bool = False):
+    """fp16 singular vectors from codes and (scale, zero) bit patterns (or
+    the exact fp64 grid values s*(q-z) if `exact`)."""
+    return quant.dequant_all(codes_u, sz_u, exact), quant.dequant_all(codes_v, sz_v, exact)
 
 
 def apply_codes(w_bits, x_bits, codes_u, codes_v, sz_u, sz_v, sigma) -> np.ndarray:

@@ -20,16 +20,18 @@ Regions, in this order, each starting at a multiple of 256 bytes:
   SIGMA  fp32 [r]
   VC_b   (b = 8, 3, 2)  V codes: for local rank i, for group g < Gi, the
          group's 128 codes as one bitstream of 4b words.  [n][Gi][4b] words.
-  VS_b   V scale/zero: uint32 [Gi][pad32(n)], entry (g, i) = fp16 scale bits
+  VS_b   V scale/zero: uint32 [Gi][pad4(n)], entry (g, i) = fp16 scale bits
          | fp16 zero bits << 16 of v_i's group g; pad entries are 0.
-  UC_8   U codes, 8-bit: bytes [out][pad4(n8)], byte (o, i) = code of u_i at
-         row o; pad bytes 0.
+  UC_8   U codes, 8-bit: bytes [out][n8], byte (o, i) = code of u_i at row o.
   UC_b   (b = 3, 2)  U codes packed along the rank axis: ranks cut into
-         K-blocks of 32 (KB = ceil(n/32) per row; codes past n are 0); the
-         K-block kb of row o is the bitstream of codes of u_{32kb..32kb+31}
-         at row o, b words long.  Order [out/16][KB][16][b] words: all 16 rows
-         of a 16-row tile for one K-block are contiguous.
-  US_b   U scale/zero: uint32 [Go][pad32(n)], entry (g, i) for u_i's group g
+         K-blocks of 32 (KB = ceil(n/32)); the K-block kb of row o is the
+         bitstream of the codes of u_{32kb}..u_{32kb+31} at row o (codes past
+         n are 0), b words long, except the last K-block, which keeps only
+         wl = ceil(m*b/32) words for its m = n - 32(KB-1) ranks.  Rows go in
+         16-row tiles; inside a tile, K-block by K-block, the 16 rows' words
+         of one K-block are contiguous: a tile is [KB-1][16][b] words followed
+         by [16][wl] words.
+  US_b   U scale/zero: uint32 [Go][pad4(n)], entry (g, i) for u_i's group g
          (rows 128g..128g+127); pad entries 0.
 Total size rounded up to 256 bytes.  Empty segments give empty regions.
 """
@@ -62,10 +64,10 @@ def regions(spec) -> Dict[str, Tuple[int, int]]:
     gi, go = inn // GROUP, out // GROUP
     sizes = [("SIGMA", 4 * r)]
     sizes += [("VC%d" % b, cnt[b] * gi * 16 * b) for b in SEGS]
-    sizes += [("VS%d" % b, gi * pad(cnt[b], 32) * 4) for b in SEGS]
-    sizes += [("UC8", out * pad(cnt[8], 4))]
-    sizes += [("UC%d" % b, (out // 16) * (-(-cnt[b] // 32)) * 16 * 4 * b) for b in (3, 2)]
-    sizes += [("US%d" % b, go * pad(cnt[b], 32) * 4) for b in SEGS]
+    sizes += [("VS%d" % b, gi * pad(cnt[b], 4) * 4) for b in SEGS]
+    sizes += [("UC8", out * cnt[8])]
+    sizes += [("UC%d" % b, (out // 16) * 16 * 4 * u_row_words(cnt[b], b)) for b in (3, 2)]
+    sizes += [("US%d" % b, go * pad(cnt[b], 4) * 4) for b in SEGS]
     res = {}
     off = 0
     for name, size in sizes:
@@ -74,6 +76,15 @@ def regions(spec) -> Dict[str, Tuple[int, int]]:
         off += size
     res["END"] = (pad(off, ALIGN), 0)
     return res
+
+
+def u_row_words(n: int, b: int) -> int:
+    """Words one row of a 3- or 2-bit U segment of n ranks takes."""
+    if n == 0:
+        return 0
+    kb = -(-n // 32)
+    m = n - 32 * (kb - 1)
+    return (kb - 1) * b + (-(-(m * b) // 32))
 
 
 def packed_bytes(spec) -> int:
@@ -138,21 +149,24 @@ def pack(spec, codes_u, codes_v, sz_u, sz_v, sigma) -> np.ndarray:
         n = hi - lo
         cv = np.asarray(codes_v[lo:hi]).reshape(n, gi, GROUP)
         put("VC%d" % b, bitstream(cv, b))
-        vs = np.zeros((gi, pad(n, 32)), "<u4")
+        vs = np.zeros((gi, pad(n, 4)), "<u4")
         vs[:, :n] = _sz_words(sz_v[lo:hi]).T
         put("VS%d" % b, vs)
         cu = np.asarray(codes_u[lo:hi]).T                     # [out][n]
         if b == 8:
-            uc = np.zeros((out, pad(n, 4)), np.uint8)
-            uc[:, :n] = cu
-            put("UC8", uc)
-        else:
+            put("UC8", np.ascontiguousarray(cu))
+        elif n:
             kb = -(-n // 32)
+            wl = u_row_words(n, b) - (kb - 1) * b
             uc = np.zeros((out, kb * 32), np.uint8)
             uc[:, :n] = cu
             words = bitstream(uc.reshape(out // 16, 16, kb, 32), b)   # [T][16][KB][b]
-            put("UC%d" % b, words.transpose(0, 2, 1, 3))             # [T][KB][16][b]
-        us = np.zeros((out // GROUP, pad(n, 32)), "<u4")
+            words = words.transpose(0, 2, 1, 3)                       # [T][KB][16][b]
+            assert not words[:, kb - 1, :, wl:].any()                 # dropped words hold only pad zeros
+            full = words[:, :kb - 1].reshape(out // 16, -1)
+            last = np.ascontiguousarray(words[:, kb - 1, :, :wl]).reshape(out // 16, -1)
+            put("UC%d" % b, np.concatenate([full, last], axis=1))
+        us = np.zeros((out // GROUP, pad(n, 4)), "<u4")
         us[:, :n] = _sz_words(sz_u[lo:hi]).T
         put("US%d" % b, us)
     return buf
@@ -181,17 +195,21 @@ def unpack(spec, buf):
             continue
         words = get("VC%d" % b, "<u4").reshape(n, gi, 4 * b)
         codes_v[lo:hi] = unbitstream(words, b, GROUP).reshape(n, inn)
-        vs = get("VS%d" % b, "<u4").reshape(gi, pad(n, 32))[:, :n].T
+        vs = get("VS%d" % b, "<u4").reshape(gi, pad(n, 4))[:, :n].T
         sz_v[lo:hi, :, 0] = vs & 0xFFFF
         sz_v[lo:hi, :, 1] = vs >> 16
         if b == 8:
-            uc = get("UC8", np.uint8).reshape(out, pad(n, 4))[:, :n]
+            uc = get("UC8", np.uint8).reshape(out, n)
         else:
             kb = -(-n // 32)
-            words = get("UC%d" % b, "<u4").reshape(out // 16, kb, 16, b).transpose(0, 2, 1, 3)
-            uc = unbitstream(words, b, 32).reshape(out, kb * 32)[:, :n]
+            wl = u_row_words(n, b) - (kb - 1) * b
+            tiles = get("UC%d" % b, "<u4").reshape(out // 16, -1)
+            words = np.zeros((out // 16, kb, 16, b), "<u4")
+            words[:, :kb - 1] = tiles[:, :(kb - 1) * 16 * b].reshape(out // 16, kb - 1, 16, b)
+            words[:, kb - 1, :, :wl] = tiles[:, (kb - 1) * 16 * b:].reshape(out // 16, 16, wl)
+            uc = unbitstream(words.transpose(0, 2, 1, 3), b, 32).reshape(out, kb * 32)[:, :n]
         codes_u[lo:hi] = uc.T
-        us = get("US%d" % b, "<u4").reshape(go, pad(n, 32))[:, :n].T
+        us = get("US%d" % b, "<u4").reshape(go, pad(n, 4))[:, :n].T
         sz_u[lo:hi, :, 0] = us & 0xFFFF
         sz_u[lo:hi, :, 1] = us >> 16
     return codes_u, codes_v, sz_u, sz_v, sigma

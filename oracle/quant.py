@@ -151,6 +151,20 @@ def dequantize(codes, scale, zero) -> np.ndarray:
     return fp16_rne(s * (codes - z))
 
 
+def dequantize_exact(codes, scale, zero) -> np.ndarray:
+    """The unrounded grid values s_h * (q_k - z) in fp64 (exact).
+
+    A kernel may multiply by these exact products instead of their fp16
+    roundings (e.g. when it folds the zero point out of a dot product:
+    sum_k s(q_k - z) x_k = s (sum_k q_k x_k - z sum_k x_k)).  Rounding them
+    to fp16 gives `dequantize` bit for bit."""
+    codes = np.asarray(codes, dtype=np.float64)
+    n = codes.shape[-1]
+    s = np.repeat(np.asarray(scale, dtype=np.float64), GROUP, axis=-1)[..., :n]
+    z = np.repeat(np.asarray(zero, dtype=np.float64), GROUP, axis=-1)[..., :n]
+    return s * (codes - z)
+
+
 def compress(u, sigma, v, n8: int, n3: int, n2: int):
     """Quantize the first r = n8+n3+n2 pairs: 8-bit, then 3-bit, then 2-bit.
 
@@ -179,10 +193,11 @@ def compress(u, sigma, v, n8: int, n3: int, n2: int):
     return codes_u, codes_v, sz_u, sz_v, np.asarray(sigma[:r], dtype=np.float32)
 
 
-def dequant_all(codes, sz):
-    """fp16 values for all ranks: codes [r][n], sz [r][n/128][2] (bit patterns)."""
+def dequant_all(codes, sz, exact: bool = False):
+    """fp16 values for all ranks (or the exact fp64 products if `exact`):
+    codes [r][n], sz [r][n/128][2] (bit patterns)."""
     codes = np.asarray(codes)
     sz = np.asarray(sz, dtype=np.uint16)
     s = sz[..., 0].view(np.float16)
     z = sz[..., 1].view(np.float16)
-    return dequantize(codes, s, z)
+    return dequantize_exact(codes, s, z) if exact else dequantize(codes, s, z)

@@ -1,0 +1,13 @@
+"""Delta-CoMe mixed-precision delta apply for AMD Instinct MI355X (gfx950).
+
+The compute lives in libdeltacome.so (C ABI, include/deltacome.h): hand-written
+HIP kernels for gfx950 plus a host packer.  This package is its thin Python
+binding; torch supplies device memory and streams only.
+"""
+from ._lib import (  # noqa: F401
+    DC_ERR_ALIGN, DC_ERR_BUFFER, DC_ERR_HIP, DC_ERR_INVALID_ARG, DC_ERR_RANGE, DC_ERR_SHAPE,
+    DC_ERR_UNSUPPORTED, DC_MAX_TENANTS, DC_OK, DC_OP_DECODE, DC_OP_MULTITENANT, DC_OP_PREFILL,
+    EXPORTS, LIB_PATH, MultitenantCall, REGIONS, DcError, DeltaView, dc_algorithmic_bytes, dc_apply_decode,
+    dc_apply_multitenant, dc_apply_multitenant_timed, dc_apply_prefill, STAGES, dc_check_spec, dc_dequant, dc_pack, dc_pack_codes,
+    dc_packed_bytes, dc_region, dc_status_string, dc_unpack, dc_workspace_bytes, lib, make_spec,
+)

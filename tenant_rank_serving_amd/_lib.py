@@ -1,0 +1,281 @@
+"""ctypes binding of libdeltacome.so.  Argument marshalling only: every step
+of the apply runs in the library's HIP kernels.  Device buffers are torch
+tensors (memory and streams only); host buffers are numpy arrays.
+
+There is no fallback: if the library is not built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdeltacome.so")
+
+DC_OK = 0
+DC_ERR_INVALID_ARG = -1
+DC_ERR_SHAPE = -2
+DC_ERR_ALIGN = -3
+DC_ERR_BUFFER = -4
+DC_ERR_RANGE = -5
+DC_ERR_HIP = -6
+DC_ERR_UNSUPPORTED = -7
+DC_MAX_TENANTS = 128
+DC_OP_DECODE, DC_OP_MULTITENANT, DC_OP_PREFILL = 0, 1, 2
+REGIONS = ("SIGMA", "VC8", "VC3", "VC2", "VS8", "VS3", "VS2",
+           "UC8", "UC3", "UC2", "US8", "US3", "US2")
+EXPORTS = ("dc_status_string", "dc_check_spec", "dc_packed_bytes", "dc_algorithmic_bytes",
+           "dc_region", "dc_pack", "dc_pack_codes", "dc_unpack", "dc_workspace_bytes",
+           "dc_apply_decode", "dc_apply_multitenant", "dc_apply_multitenant_timed",
+           "dc_apply_prefill", "dc_dequant")
+STAGES = ("route", "xprep", "base", "vside", "uside")
+
+
+class DcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (where, _status_name(status), status))
+
+
+class dc_spec(ctypes.Structure):
+    _fields_ = [("out", ctypes.c_int32), ("in_", ctypes.c_int32), ("n8", ctypes.c_int32),
+                ("n3", ctypes.c_int32), ("n2", ctypes.c_int32)]
+
+
+class dc_delta_view(ctypes.Structure):
+    _fields_ = [("spec", dc_spec), ("base", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libdeltacome.so is not built (python -m tenant_rank_serving_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        sp = ctypes.POINTER(dc_spec)
+        vp = ctypes.POINTER(dc_delta_view)
+        L.dc_status_string.restype = ctypes.c_char_p
+        L.dc_status_string.argtypes = [ctypes.c_int32]
+        L.dc_check_spec.argtypes = [sp]
+        L.dc_packed_bytes.restype = ctypes.c_size_t
+        L.dc_packed_bytes.argtypes = [sp]
+        L.dc_algorithmic_bytes.restype = ctypes.c_size_t
+        L.dc_algorithmic_bytes.argtypes = [sp]
+        L.dc_region.argtypes = [sp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t),
+                                ctypes.POINTER(ctypes.c_size_t)]
+        L.dc_pack.argtypes = [sp, _P, _P, _P, _P, ctypes.c_size_t]
+        L.dc_pack_codes.argtypes = [sp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t]
+        L.dc_unpack.argtypes = [sp, _P, ctypes.c_size_t, _P, _P, _P, _P, _P]
+        L.dc_workspace_bytes.restype = ctypes.c_size_t
+        L.dc_workspace_bytes.argtypes = [ctypes.c_int32, sp, ctypes.c_int32, ctypes.c_int32]
+        L.dc_apply_decode.argtypes = [vp, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]
+        L.dc_apply_multitenant.argtypes = [vp, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, _P,
+                                           ctypes.c_size_t, _P]
+        L.dc_apply_multitenant_timed.argtypes = [vp, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32,
+                                                 _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]
+        L.dc_apply_prefill.argtypes = [vp, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.dc_dequant.argtypes = [vp, _P, _P, _P]
+        for name in EXPORTS:
+            if name not in ("dc_status_string", "dc_packed_bytes", "dc_algorithmic_bytes",
+                            "dc_workspace_bytes"):
+                getattr(L, name).restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return lib().dc_status_string(int(s)).decode()
+    except ImportError:
+        return str(s)
+
+
+def _check(status: int, where: str) -> None:
+    if status != DC_OK:
+        raise DcError(status, where)
+
+
+def make_spec(spec) -> dc_spec:
+    if isinstance(spec, dc_spec):
+        return spec
+    out, inn, n8, n3, n2 = (int(v) for v in spec)
+    return dc_spec(out, inn, n8, n3, n2)
+
+
+def _np_ptr(a, dtype) -> Tuple[np.ndarray, int]:
+    arr = np.ascontiguousarray(a, dtype=dtype)
+    return arr, arr.ctypes.data
+
+
+# ------------------------------------------------------------------- host
+def dc_status_string(status: int) -> str:
+    return lib().dc_status_string(int(status)).decode()
+
+
+def dc_check_spec(spec) -> int:
+    return int(lib().dc_check_spec(ctypes.byref(make_spec(spec))))
+
+
+def dc_packed_bytes(spec) -> int:
+    return int(lib().dc_packed_bytes(ctypes.byref(make_spec(spec))))
+
+
+def dc_algorithmic_bytes(spec) -> int:
+    return int(lib().dc_algorithmic_bytes(ctypes.byref(make_spec(spec))))
+
+
+def dc_region(spec, region) -> Tuple[int, int]:
+    rid = REGIONS.index(region) if isinstance(region, str) else int(region)
+    off, size = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().dc_region(ctypes.byref(make_spec(spec)), rid, ctypes.byref(off), ctypes.byref(size)),
+           "dc_region")
+    return off.value, size.value
+
+
+def dc_pack(spec, U, sigma, V) -> np.ndarray:
+    s = make_spec(spec)
+    _check(lib().dc_check_spec(ctypes.byref(s)), "dc_pack")
+    nbytes = dc_packed_bytes(s)
+    out = np.zeros(max(nbytes, 1), np.uint8)
+    u, pu = _np_ptr(U, np.float32)
+    g, pg = _np_ptr(sigma, np.float32)
+    v, pv = _np_ptr(V, np.float32)
+    _check(lib().dc_pack(ctypes.byref(s), pu, pg, pv, out.ctypes.data, out.size), "dc_pack")
+    return out[:nbytes]
+
+
+def dc_pack_codes(spec, codes_u, codes_v, sz_u, sz_v, sigma) -> np.ndarray:
+    s = make_spec(spec)
+    _check(lib().dc_check_spec(ctypes.byref(s)), "dc_pack_codes")
+    nbytes = dc_packed_bytes(s)
+    out = np.zeros(max(nbytes, 1), np.uint8)
+    cu, p1 = _np_ptr(codes_u, np.uint8)
+    cv, p2 = _np_ptr(codes_v, np.uint8)
+    su, p3 = _np_ptr(sz_u, np.uint16)
+    sv, p4 = _np_ptr(sz_v, np.uint16)
+    g, p5 = _np_ptr(sigma, np.float32)
+    _check(lib().dc_pack_codes(ctypes.byref(s), p1, p2, p3, p4, p5, out.ctypes.data, out.size),
+           "dc_pack_codes")
+    return out[:nbytes]
+
+
+def dc_unpack(spec, buf):
+    s = make_spec(spec)
+    r = s.n8 + s.n3 + s.n2
+    b, pb = _np_ptr(buf, np.uint8)
+    cu = np.zeros((r, s.out), np.uint8)
+    cv = np.zeros((r, s.in_), np.uint8)
+    su = np.zeros((r, s.out // 128, 2), np.uint16)
+    sv = np.zeros((r, s.in_ // 128, 2), np.uint16)
+    sg = np.zeros(r, np.float32)
+    _check(lib().dc_unpack(ctypes.byref(s), pb, b.size, cu.ctypes.data, cv.ctypes.data,
+                           su.ctypes.data, sv.ctypes.data, sg.ctypes.data), "dc_unpack")
+    return cu, cv, su, sv, sg
+
+
+def dc_workspace_bytes(op: int, specs, T: int) -> int:
+    arr = (dc_spec * len(specs))(*[make_spec(s) for s in specs])
+    return int(lib().dc_workspace_bytes(int(op), arr, len(specs), int(T)))
+
+
+# ----------------------------------------------------------------- device
+class DeltaView:
+    """A packed delta resident in device memory (keeps its tensor alive)."""
+
+    def __init__(self, spec, buf):
+        self.spec = make_spec(spec)
+        self.buf = buf
+        self.c = dc_delta_view(self.spec, ctypes.c_void_p(int(buf.data_ptr())))
+
+
+def _dptr(t, what: str) -> int:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+    return int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def _views(views: Sequence[DeltaView]):
+    return (dc_delta_view * len(views))(*[v.c for v in views])
+
+
+def dc_apply_decode(view: DeltaView, W_base, x, y, ws, T: int = None, stream=None) -> None:
+    T = x.shape[0] if T is None else T
+    _check(lib().dc_apply_decode(ctypes.byref(view.c), _dptr(W_base, "W_base"), _dptr(x, "x"),
+                                 _dptr(y, "y"), int(T), _dptr(ws, "ws"), ws.numel() * ws.element_size(),
+                                 _stream(stream)), "dc_apply_decode")
+
+
+def dc_apply_multitenant(views: Sequence[DeltaView], W_base, x, tenant_ids, y, ws, T: int = None,
+                         stream=None) -> None:
+    T = x.shape[0] if T is None else T
+    _check(lib().dc_apply_multitenant(_views(views), len(views), _dptr(W_base, "W_base"), _dptr(x, "x"),
+                                      _dptr(tenant_ids, "tenant_ids"), _dptr(y, "y"), int(T),
+                                      _dptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
+           "dc_apply_multitenant")
+
+
+def dc_apply_multitenant_timed(views: Sequence[DeltaView], W_base, x, tenant_ids, y, ws, events,
+                               T: int = None, stream=None) -> None:
+    """events: len(STAGES)+1 raw hipEvent_t handles (ints) or None entries."""
+    T = x.shape[0] if T is None else T
+    ev = (_P * (len(STAGES) + 1))(*[None if e is None else int(e) for e in events])
+    _check(lib().dc_apply_multitenant_timed(_views(views), len(views), _dptr(W_base, "W_base"),
+                                            _dptr(x, "x"), _dptr(tenant_ids, "tenant_ids"), _dptr(y, "y"),
+                                            int(T), _dptr(ws, "ws"), ws.numel() * ws.element_size(),
+                                            _stream(stream), ev), "dc_apply_multitenant_timed")
+
+
+def dc_apply_prefill(views: Sequence[DeltaView], W_base, x, seg_offsets, y, ws, stream=None) -> None:
+    seg = np.ascontiguousarray(seg_offsets, dtype=np.int32)
+    _check(lib().dc_apply_prefill(_views(views), len(views), _dptr(W_base, "W_base"), _dptr(x, "x"),
+                                  seg.ctypes.data, _dptr(y, "y"), _dptr(ws, "ws"),
+                                  ws.numel() * ws.element_size(), _stream(stream)), "dc_apply_prefill")
+
+
+def dc_dequant(view: DeltaView, u_fp16, v_fp16, stream=None) -> None:
+    _check(lib().dc_dequant(ctypes.byref(view.c), _dptr(u_fp16, "u_fp16"), _dptr(v_fp16, "v_fp16"),
+                            _stream(stream)), "dc_dequant")
+
+
+class MultitenantCall:
+    """dc_apply_multitenant with its arguments marshalled once, for callers
+    that issue the same call many times (a serving loop, a benchmark)."""
+
+    def __init__(self, views: Sequence[DeltaView], W_base, x, tenant_ids, y, ws, T: int = None,
+                 stream=None):
+        self._keep = (list(views), W_base, x, tenant_ids, y, ws)
+        T = x.shape[0] if T is None else T
+        self._arr = _views(views)
+        self.args = (self._arr, len(views), _dptr(W_base, "W_base"), _dptr(x, "x"),
+                     _dptr(tenant_ids, "tenant_ids"), _dptr(y, "y"), int(T), _dptr(ws, "ws"),
+                     ws.numel() * ws.element_size(), _stream(stream))
+        self._fn = lib().dc_apply_multitenant
+        self._fn_t = lib().dc_apply_multitenant_timed
+
+    def __call__(self) -> None:
+        st = self._fn(*self.args)
+        if st != DC_OK:
+            raise DcError(st, "dc_apply_multitenant")
+
+    def timed(self, events) -> None:
+        ev = (_P * (len(STAGES) + 1))(*[None if e is None else int(e) for e in events])
+        st = self._fn_t(*self.args, ev)
+        if st != DC_OK:
+            raise DcError(st, "dc_apply_multitenant_timed")

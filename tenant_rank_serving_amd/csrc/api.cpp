@@ -1,0 +1,145 @@
+// Device entry points of libdeltacome.so: argument checks on the host, then
+// kernel launches on the caller's stream.  No allocation, no synchronization.
+#include <cstdint>
+#include <cstring>
+
+#include "dc_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x0 = reinterpret_cast<uintptr_t>(a), y0 = reinterpret_cast<uintptr_t>(b);
+  return x0 < y0 + nb && y0 < x0 + na;
+}
+
+// Checks the tenant specs of one call; fills out/in/rmax.
+dc_status check_specs(const dc_spec* specs, int32_t n, int32_t* out, int32_t* in, int32_t* rmax) {
+  if (!specs || n < 1) return DC_ERR_INVALID_ARG;
+  if (n > DC_MAX_TENANTS) return DC_ERR_UNSUPPORTED;
+  *out = specs[0].out;
+  *in = specs[0].in;
+  *rmax = 0;
+  for (int k = 0; k < n; ++k) {
+    if (dc_check_spec(&specs[k]) != DC_OK) return DC_ERR_SHAPE;
+    if (specs[k].out != *out || specs[k].in != *in) return DC_ERR_SHAPE;
+    const int32_t r = specs[k].n8 + specs[k].n3 + specs[k].n2;
+    if (r > *rmax) *rmax = r;
+  }
+  return DC_OK;
+}
+
+dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const uint16_t* x,
+              const int32_t* ids, const int32_t* seg, int32_t mode, uint16_t* y, int32_t T, void* ws,
+              size_t ws_bytes, void* stream, void* const* events = nullptr) {
+  if (!views || n < 1) return DC_ERR_INVALID_ARG;
+  if (n > DC_MAX_TENANTS) return DC_ERR_UNSUPPORTED;
+  if (T < 0) return DC_ERR_INVALID_ARG;
+  dc_spec specs[DC_MAX_TENANTS] = {};
+  for (int k = 0; k < n; ++k) specs[k] = views[k].spec;
+  int32_t out, in, rmax;
+  dc_status st = check_specs(specs, n, &out, &in, &rmax);
+  if (st != DC_OK) return st;
+  dc::TenantTable table;
+  std::memset(&table, 0, sizeof(table));
+  for (int k = 0; k < n; ++k) {
+    const int32_t r = specs[k].n8 + specs[k].n3 + specs[k].n2;
+    if (r > 0 && !views[k].base) return DC_ERR_INVALID_ARG;
+    if (!aligned(views[k].base, 16)) return DC_ERR_ALIGN;
+    table.t[k].base = static_cast<const uint8_t*>(views[k].base);
+    table.t[k].n8 = specs[k].n8;
+    table.t[k].n3 = specs[k].n3;
+    table.t[k].n2 = specs[k].n2;
+  }
+  if (!x || !y || !ws) return DC_ERR_INVALID_ARG;
+  if (mode == 1 && !ids) return DC_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || (W && !aligned(W, 16)) || !aligned(ws, 256) ||
+      (ids && !aligned(ids, 4)))
+    return DC_ERR_ALIGN;
+  if (overlap(x, (size_t)T * in * 2, y, (size_t)T * out * 2)) return DC_ERR_INVALID_ARG;
+  dc::WsLayout wl{};
+  dc::ws_layout(T, in, out, rmax, n, true, &wl);
+  if (ws_bytes < wl.total) return DC_ERR_BUFFER;
+  if (T == 0) return DC_OK;
+  dc::ApplyArgs a;
+  a.tenants = &table;
+  a.n = n;
+  a.out = out;
+  a.in = in;
+  a.rmax = rmax;
+  a.T = T;
+  a.W = W;
+  a.x = x;
+  a.ids = ids;
+  a.seg = seg;
+  a.mode = mode;
+  a.y = y;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.wl = wl;
+  a.stream = stream;
+  a.events = events;
+  return dc::launch_apply(a) == 0 ? DC_OK : DC_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dc_workspace_bytes(int32_t op, const dc_spec* specs, int32_t n, int32_t T) {
+  if (op < DC_OP_DECODE || op > DC_OP_PREFILL || T < 0) return 0;
+  if (op == DC_OP_DECODE && n != 1) return 0;
+  int32_t out, in, rmax;
+  if (check_specs(specs, n, &out, &in, &rmax) != DC_OK) return 0;
+  dc::WsLayout wl{};
+  dc::ws_layout(T, in, out, rmax, n, true, &wl);
+  return wl.total;
+}
+
+dc_status dc_apply_decode(const dc_delta_view* d, const uint16_t* W_base, const uint16_t* x,
+                          uint16_t* y, int32_t T, void* ws, size_t ws_bytes, void* stream) {
+  if (!d) return DC_ERR_INVALID_ARG;
+  return run(d, 1, W_base, x, nullptr, nullptr, 0, y, T, ws, ws_bytes, stream);
+}
+
+dc_status dc_apply_multitenant(const dc_delta_view* views, int32_t n, const uint16_t* W_base,
+                               const uint16_t* x, const int32_t* tenant_ids, uint16_t* y,
+                               int32_t T, void* ws, size_t ws_bytes, void* stream) {
+  return run(views, n, W_base, x, tenant_ids, nullptr, 1, y, T, ws, ws_bytes, stream);
+}
+
+dc_status dc_apply_multitenant_timed(const dc_delta_view* views, int32_t n, const uint16_t* W_base,
+                                     const uint16_t* x, const int32_t* tenant_ids, uint16_t* y,
+                                     int32_t T, void* ws, size_t ws_bytes, void* stream,
+                                     void* const* events) {
+  return run(views, n, W_base, x, tenant_ids, nullptr, 1, y, T, ws, ws_bytes, stream, events);
+}
+
+dc_status dc_apply_prefill(const dc_delta_view* views, int32_t n, const uint16_t* W_base,
+                           const uint16_t* x, const int32_t* seg_offsets, uint16_t* y, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!seg_offsets || n < 1) return DC_ERR_INVALID_ARG;
+  if (n > DC_MAX_TENANTS) return DC_ERR_UNSUPPORTED;
+  if (seg_offsets[0] != 0) return DC_ERR_INVALID_ARG;
+  for (int k = 0; k < n; ++k)
+    if (seg_offsets[k + 1] < seg_offsets[k]) return DC_ERR_INVALID_ARG;
+  return run(views, n, W_base, x, nullptr, seg_offsets, 2, y, seg_offsets[n], ws, ws_bytes, stream);
+}
+
+dc_status dc_dequant(const dc_delta_view* d, uint16_t* u_fp16, uint16_t* v_fp16, void* stream) {
+  if (!d) return DC_ERR_INVALID_ARG;
+  if (dc_check_spec(&d->spec) != DC_OK) return DC_ERR_SHAPE;
+  const int32_t r = d->spec.n8 + d->spec.n3 + d->spec.n2;
+  if (r == 0) return DC_OK;
+  if (!d->base || !u_fp16 || !v_fp16) return DC_ERR_INVALID_ARG;
+  if (!aligned(d->base, 16) || !aligned(u_fp16, 16) || !aligned(v_fp16, 16)) return DC_ERR_ALIGN;
+  dc::Tenant t;
+  t.base = static_cast<const uint8_t*>(d->base);
+  t.n8 = d->spec.n8;
+  t.n3 = d->spec.n3;
+  t.n2 = d->spec.n2;
+  t.pad_ = 0;
+  return dc::launch_dequant(t, d->spec.out, d->spec.in, u_fp16, v_fp16, stream) == 0 ? DC_OK : DC_ERR_HIP;
+}
+
+}  // extern "C"

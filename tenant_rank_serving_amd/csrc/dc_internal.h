@@ -1,0 +1,141 @@
+// Internal declarations shared by the host code and the gfx950 kernels of
+// libdeltacome.so.  Not part of the public ABI (include/deltacome.h is).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/deltacome.h"
+
+#if defined(__HIPCC__)
+#define DC_HD __host__ __device__
+#else
+#define DC_HD
+#endif
+
+namespace dc {
+
+constexpr int kGroup = 128;   // elements per quantization group
+constexpr int kAlign = 256;   // region alignment inside a packed buffer
+constexpr int kKBlock = 32;   // ranks per K-block of the U code regions
+
+DC_HD inline size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
+
+// Words one row of a 3- or 2-bit U code segment of n ranks takes: full
+// K-blocks of 32 ranks take b words, the last one ceil(m*b/32) for its m ranks.
+DC_HD inline int u_row_words(int n, int b) {
+  if (n <= 0) return 0;
+  const int kb = (n + kKBlock - 1) / kKBlock;
+  const int m = n - kKBlock * (kb - 1);
+  return (kb - 1) * b + (m * b + 31) / 32;
+}
+
+// Word offset of K-block kb of row o inside a 3- or 2-bit U code region of n
+// ranks (16-row tiles, K-block by K-block), and the words it holds.
+DC_HD inline size_t u_kblock_word(int o, int kb, int n, int b, int* nw) {
+  const int kbn = (n + kKBlock - 1) / kKBlock;
+  const int rw = u_row_words(n, b);
+  const int w = (kb == kbn - 1) ? rw - (kbn - 1) * b : b;
+  *nw = w;
+  return (size_t)(o / 16) * 16 * rw + (size_t)kb * 16 * b + (size_t)(o % 16) * w;
+}
+
+// Byte offsets of the DC_REG_* regions of a packed buffer and its total size.
+// This is the format stated in include/deltacome.h.
+struct Layout {
+  size_t off[DC_REG_COUNT];
+  size_t size[DC_REG_COUNT];
+  size_t total;
+};
+
+DC_HD inline void layout_of(int32_t out, int32_t in, int32_t n8, int32_t n3, int32_t n2, Layout* L) {
+  const size_t gi = (size_t)in / kGroup, go = (size_t)out / kGroup;
+  const size_t r = (size_t)n8 + n3 + n2;
+  size_t sz[DC_REG_COUNT];
+  sz[DC_REG_SIGMA] = 4 * r;
+  sz[DC_REG_VC8] = (size_t)n8 * gi * 16 * 8;
+  sz[DC_REG_VC3] = (size_t)n3 * gi * 16 * 3;
+  sz[DC_REG_VC2] = (size_t)n2 * gi * 16 * 2;
+  sz[DC_REG_VS8] = gi * round_up(n8, 4) * 4;
+  sz[DC_REG_VS3] = gi * round_up(n3, 4) * 4;
+  sz[DC_REG_VS2] = gi * round_up(n2, 4) * 4;
+  sz[DC_REG_UC8] = (size_t)out * n8;
+  sz[DC_REG_UC3] = (size_t)out * 4 * u_row_words(n3, 3);
+  sz[DC_REG_UC2] = (size_t)out * 4 * u_row_words(n2, 2);
+  sz[DC_REG_US8] = go * round_up(n8, 4) * 4;
+  sz[DC_REG_US3] = go * round_up(n3, 4) * 4;
+  sz[DC_REG_US2] = go * round_up(n2, 4) * 4;
+  size_t o = 0;
+  for (int i = 0; i < DC_REG_COUNT; ++i) {
+    o = round_up(o, kAlign);
+    L->off[i] = o;
+    L->size[i] = sz[i];
+    o += sz[i];
+  }
+  L->total = round_up(o, kAlign);
+}
+
+// One tenant as the kernels see it (kernel-argument table, no device copy).
+struct Tenant {
+  const uint8_t* base;
+  int32_t n8, n3, n2;
+  int32_t pad_;
+};
+
+struct TenantTable {
+  Tenant t[DC_MAX_TENANTS];
+};
+
+// Workspace layout of one apply call.
+struct WsLayout {
+  size_t flags;   // uint32 status word (+ padding to 256 B)
+  size_t offs;    // int32 [n+2] bucket starts in sorted order (bucket n = backbone only)
+  size_t perm;    // int32 [T] sorted position -> token index
+  size_t xs;      // fp32 [T][in] activations in sorted order
+  size_t tv;      // fp32 [T][rs] V-side results t = sigma * (V x), sorted order
+  size_t ybase;   // fp32 [T][out] backbone product, original order
+  size_t total;
+  int32_t rs;     // row stride of tv (max r over tenants, rounded up to 4)
+};
+
+inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rmax, int32_t n, bool with_base,
+                      WsLayout* W) {
+  if (T < 0 || n < 0) return false;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = round_up(o, kAlign); o = at + bytes; return at; };
+  W->rs = (int32_t)round_up((size_t)(rmax > 0 ? rmax : 1), 4);
+  W->flags = take(256);
+  W->offs = take(4 * ((size_t)n + 2));
+  W->perm = take(4 * (size_t)T);
+  W->xs = take(4 * (size_t)T * in);
+  W->tv = take(4 * (size_t)T * W->rs);
+  W->ybase = take(with_base ? 4 * (size_t)T * out : 0);
+  W->total = round_up(o, kAlign);
+  return true;
+}
+
+}  // namespace dc
+
+// Kernel launchers (defined in the .hip files).  All enqueue on `stream`
+// and return a hipError_t as int.
+namespace dc {
+struct ApplyArgs {
+  const TenantTable* tenants;  // host pointer: copied into kernel arguments
+  int32_t n;
+  int32_t out, in;
+  int32_t rmax;
+  int32_t T;
+  const uint16_t* W;           // may be null
+  const uint16_t* x;
+  const int32_t* ids;          // device, mode 1
+  const int32_t* seg;          // host, mode 2 ([n+1])
+  int32_t mode;                // 0 decode (all tokens tenant 0), 1 ids, 2 segments
+  uint16_t* y;
+  uint8_t* ws;
+  WsLayout wl;
+  void* stream;
+  void* const* events;         // optional DC_STAGE_COUNT + 1 hipEvent_t, may be null
+};
+int launch_apply(const ApplyArgs& a);
+int launch_dequant(const Tenant& t, int32_t out, int32_t in, uint16_t* u16, uint16_t* v16, void* stream);
+}  // namespace dc

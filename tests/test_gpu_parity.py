@@ -1,0 +1,289 @@
+"""GPU parity through the C ABI against the fp64 oracle.
+
+Bars: dequantized fp16 values bit-exact; bf16 outputs within 2e-3 relative
+L2 per token of the unrounded fp64 oracle, for the fused output, the
+delta-only output and each bit-width segment packed alone (a wrong 2-bit
+path would otherwise hide under the 8-bit pairs)."""
+import numpy as np
+import pytest
+
+import synth
+import tenant_rank_serving_amd as trs
+from oracle import apply as oap
+from oracle import quant
+from gpu_util import (TOL, check_close, dev_i32, dev_u16, note, oracle_tenant, run_decode, torch,
+                      upload, workspace, y_to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    trs.lib()  # fail loudly if the library is missing
+
+
+# ------------------------------------------------------------------ dequant
+DEQ_SPECS = [(256, 256, 2, 8, 22), (384, 128, 3, 37, 71), (128, 512, 0, 33, 0), (128, 128, 1, 0, 0),
+             (4096, 4096, 2, 32, 968)]
+
+
+@pytest.mark.parametrize("spec", DEQ_SPECS)
+def test_dequant_bit_exact(spec):
+    note("dequant", spec)
+    t = torch()
+    d = synth.small_delta(31, *spec)
+    view = upload(spec, d)
+    u = t.empty((d.r, d.out), dtype=t.int16, device="cuda")
+    v = t.empty((d.r, d.inn), dtype=t.int16, device="cuda")
+    trs.dc_dequant(view, u, v)
+    t.cuda.synchronize()
+    uh, vh = oap.dequant_pairs(d.codes_u, d.codes_v, d.sz_u, d.sz_v)
+    assert np.array_equal(u.cpu().numpy().view(np.uint16), uh.view(np.uint16))
+    assert np.array_equal(v.cpu().numpy().view(np.uint16), vh.view(np.uint16))
+
+
+def test_dequant_c0_from_svd():
+    note("dequant c0")
+    t = torch()
+    c0 = synth.make_c0()
+    u, s, v = quant.svd_pairs(c0["delta"])
+    spec = (256, 256) + tuple(c0["groups"])
+    buf = trs.dc_pack(spec, u[:32].astype(np.float32), s[:32].astype(np.float32), v[:32].astype(np.float32))
+    view = trs.DeltaView(spec, t.from_numpy(buf.copy()).cuda())
+    ud = t.empty((32, 256), dtype=t.int16, device="cuda")
+    vd = t.empty((32, 256), dtype=t.int16, device="cuda")
+    trs.dc_dequant(view, ud, vd)
+    t.cuda.synchronize()
+    cu, cv, su, sv, _ = quant.compress(u.astype(np.float32), s.astype(np.float32), v.astype(np.float32), 2, 8, 22)
+    uh, vh = oap.dequant_pairs(cu, cv, su, sv)
+    assert np.array_equal(ud.cpu().numpy().view(np.uint16), uh.view(np.uint16))
+    assert np.array_equal(vd.cpu().numpy().view(np.uint16), vh.view(np.uint16))
+
+
+# ------------------------------------------------------------- decode c0
+def test_c0_end_to_end():
+    """SVD on the host, dc_pack, decode on the GPU: fused and delta-only."""
+    note("c0 end to end")
+    t = torch()
+    c0 = synth.make_c0()
+    u, s, v = quant.svd_pairs(c0["delta"])
+    u32, s32, v32 = u.astype(np.float32), s.astype(np.float32), v.astype(np.float32)
+    spec = (256, 256, 2, 8, 22)
+    buf = trs.dc_pack(spec, u32[:32], s32[:32], v32[:32])
+    view = trs.DeltaView(spec, t.from_numpy(buf.copy()).cuda())
+    cu, cv, su, sv, sg = quant.compress(u32, s32, v32, 2, 8, 22)
+    ws = workspace(trs.DC_OP_DECODE, [spec], 4)
+    x = dev_u16(c0["x"])
+    for w in (c0["w"], None):
+        y = t.empty((4, 256), dtype=t.int16, device="cuda")
+        trs.dc_apply_decode(view, dev_u16(w) if w is not None else None, x, y, ws)
+        t.cuda.synchronize()
+        ref = oap.apply_codes(w, c0["x"], cu, cv, su, sv, sg)
+        check_close(y_to_f64(y), ref, what="c0 %s" % ("fused" if w is not None else "delta"))
+
+
+# ----------------------------------------------- decode, segments and tails
+SEG_CASES = [(256, 256, 2, 8, 22, 4), (384, 256, 3, 37, 71, 1), (384, 256, 3, 37, 71, 5),
+             (256, 384, 2, 40, 100, 17), (128, 128, 0, 0, 5, 2), (128, 128, 1, 0, 0, 3),
+             (512, 640, 4, 65, 129, 9)]
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_decode_fused_delta_and_segments(case):
+    out, inn, n8, n3, n2, T = case
+    note("decode", case)
+    c = synth.small_case(100 + T, out, inn, n8, n3, n2, T)
+    d = c["delta"]
+    y, _ = run_decode(d, c["w"], c["x"])
+    check_close(y, oap.apply_factored(c["w"], c["x"], *oracle_tenant(d)), what="fused",
+                ref_exact=oap.apply_factored(c["w"], c["x"], *oracle_tenant(d, True)))
+    y, _ = run_decode(d, c["w"], c["x"], with_base=False)
+    check_close(y, oap.apply_factored(None, c["x"], *oracle_tenant(d)), what="delta",
+                ref_exact=oap.apply_factored(None, c["x"], *oracle_tenant(d, True)))
+    lo = 0
+    for b, n, sp in ((8, n8, (n8, 0, 0)), (3, n3, (0, n3, 0)), (2, n2, (0, 0, n2))):
+        if n:
+            sub = d.subset(lo, lo + n, sp)
+            y, _ = run_decode(sub, c["w"], c["x"], with_base=False)
+            check_close(y, oap.apply_factored(None, c["x"], *oracle_tenant(sub)), what="segment %d" % b,
+                        ref_exact=oap.apply_factored(None, c["x"], *oracle_tenant(sub, True)))
+        lo += n
+
+
+# ------------------------------------------------------------ c1 full size
+@pytest.mark.parametrize("mi", [0, 4, 6])
+def test_c1_matrix_full_size(mi):
+    """Llama-2-7B layer matrices (q 4096x4096, gate 11008x4096, down
+    4096x11008) at decode batch 1, 8 and 64, fused, delta-only and per segment."""
+    note("c1 matrix", mi)
+    m = synth.make_c1_matrix(mi)
+    d = m["delta"]
+    for B in (1, 8, 64):
+        x = m["x"][:B]
+        y, _ = run_decode(d, m["w"], x)
+        check_close(y, oap.apply_factored(m["w"], x, *oracle_tenant(d)), what="c1 fused B=%d" % B)
+    x = m["x"][:8]
+    y, _ = run_decode(d, m["w"], x, with_base=False)
+    check_close(y, oap.apply_factored(None, x, *oracle_tenant(d)), what="c1 delta")
+    lo = 0
+    for b, n, sp in ((8, d.n8, (d.n8, 0, 0)), (3, d.n3, (0, d.n3, 0)), (2, d.n2, (0, 0, d.n2))):
+        sub = d.subset(lo, lo + n, sp)
+        y, _ = run_decode(sub, m["w"], x, with_base=False)
+        check_close(y, oap.apply_factored(None, x, *oracle_tenant(sub)), what="c1 segment %d" % b)
+        lo += n
+
+
+# -------------------------------------------------------------- invariants
+def test_deterministic_and_base_only():
+    note("invariants")
+    c = synth.small_case(5, 256, 256, 2, 8, 22, 6)
+    d = c["delta"]
+    _, a = run_decode(d, c["w"], c["x"])
+    _, b = run_decode(d, c["w"], c["x"])
+    assert np.array_equal(a, b)                      # no float atomics: bit-identical
+    z = d.subset(0, d.r, (d.n8, d.n3, d.n2))
+    z.sigma[:] = 0
+    y, _ = run_decode(z, c["w"], c["x"])
+    ref = oap.apply_factored(c["w"], c["x"], *oracle_tenant(z))
+    check_close(y, ref, what="sigma=0")
+    yb = synth.to_bf16_bits(ref.astype(np.float32))
+    _, bits = run_decode(z, c["w"], c["x"])
+    # sigma = 0 gives the backbone only; the rounding of a fp32 sum may differ
+    # from the fp64 reference in the last bit, nowhere more
+    diff = np.abs(bits.view(np.uint16).astype(np.int64) - yb.astype(np.int64))
+    assert diff.max() <= 1
+
+
+# ------------------------------------------------------------ multi-tenant
+def _mt_run(views, w, x, ids):
+    t = torch()
+    T = x.shape[0]
+    specs = [v.spec for v in views]
+    ws = workspace(trs.DC_OP_MULTITENANT, [(s.out, s.in_, s.n8, s.n3, s.n2) for s in specs], T)
+    y = t.empty((T, views[0].spec.out), dtype=t.int16, device="cuda")
+    trs.dc_apply_multitenant(views, dev_u16(w) if w is not None else None, dev_u16(x), dev_i32(ids), y, ws)
+    t.cuda.synchronize()
+    flag = int(ws[:4].cpu().numpy().view(np.uint32)[0])
+    return y_to_f64(y), y.cpu().numpy(), flag
+
+
+def test_multitenant_small_mixed_specs():
+    note("multitenant small")
+    rng = np.random.default_rng(8)
+    specs = [(256, 384, 2, 8, 22), (256, 384, 1, 40, 0), (256, 384, 0, 0, 70), (256, 384, 3, 5, 7)]
+    ds = [synth.small_delta(40 + k, *s) for k, s in enumerate(specs)]
+    views = [upload(s, d) for s, d in zip(specs, ds)]
+    w = synth.base_weight(rng, 256, 384)
+    x = synth.activations(rng, 23, 384)
+    ids = rng.integers(-1, 4, size=23).astype(np.int32)
+    ids[3] = 2
+    ts = [oracle_tenant(d) for d in ds]
+    for wb in (w, None):
+        y, bits, flag = _mt_run(views, wb, x, ids)
+        assert flag == 0
+        check_close(y, oap.apply_multitenant(wb, x, ids, ts) if wb is not None else
+                    _delta_only_mt(x, ids, ts, 256), what="mt")
+    # each token equals its single-tenant decode bit for bit
+    _, bits, _ = _mt_run(views, w, x, ids)
+    for k in range(4):
+        sel = np.nonzero(ids == k)[0]
+        if sel.size:
+            _, single = run_decode(ds[k], w, x[sel])
+            assert np.array_equal(bits[sel], single)
+    # permuting tokens permutes outputs
+    perm = rng.permutation(23)
+    _, bp, _ = _mt_run(views, w, x[perm], ids[perm])
+    assert np.array_equal(bp, bits[perm])
+
+
+def _delta_only_mt(x, ids, ts, out):
+    y = np.zeros((x.shape[0], out))
+    for k, tk in enumerate(ts):
+        sel = np.nonzero(ids == k)[0]
+        if sel.size:
+            y[sel] = oap.apply_factored(None, x[sel], *tk)
+    return y
+
+
+def test_multitenant_invalid_ids_flag():
+    note("multitenant invalid ids")
+    rng = np.random.default_rng(9)
+    spec = (128, 256, 1, 3, 9)
+    ds = [synth.small_delta(60 + k, *spec) for k in range(3)]
+    views = [upload(spec, d) for d in ds]
+    w = synth.base_weight(rng, 128, 256)
+    x = synth.activations(rng, 7, 256)
+    ids = np.array([0, 5, -1, 2, -7, 1, 3], np.int32)
+    y, bits, flag = _mt_run(views, w, x, ids)
+    assert flag == 1
+    ref = oap.apply_multitenant(w, x, ids, [oracle_tenant(d) for d in ds])
+    check_close(y, ref, what="invalid ids")
+    ids2 = np.array([0, 1, 2, 0, 1, 2, -1], np.int32)
+    _, _, flag2 = _mt_run(views, w, x, ids2)
+    assert flag2 == 0                                  # cleared by every call
+
+
+def test_c2_sample_full_size():
+    """Two c2 matrices (layer 0 q and layer 31 gate) over all 50 tenants with
+    the seeded Zipf batch of 64 tokens, fused and delta-only."""
+    ids = synth.c2_ids()
+    for layer, mi in ((0, 0), (31, 4)):
+        note("c2 layer", layer, "matrix", mi)
+        touched = sorted(set(ids.tolist()))
+        ds = {}
+        views = []
+        for k in range(synth.C2_TENANTS):
+            if k in touched:
+                ds[k] = synth.make_c2_delta(layer, mi, k)
+                views.append(upload(ds[k].spec, ds[k]))
+            else:   # untouched tenants: same shape, contents never read
+                views.append(views[0] if views else None)
+        first = views[touched[0]]
+        views = [v if v is not None else first for v in views]
+        w = synth.make_c2_base(layer, mi)
+        x = synth.make_c2_x(layer, mi)
+        ts = [oracle_tenant(ds[k]) if k in ds else (np.zeros((1, 1)), np.zeros(0), np.zeros((1, 1)))
+              for k in range(synth.C2_TENANTS)]
+        y, _, flag = _mt_run(views, w, x, ids)
+        assert flag == 0
+        ref = np.zeros_like(y)
+        xb = synth.bf16_bits_to_f32(x).astype(np.float64)
+        ref += xb @ synth.bf16_bits_to_f32(w).astype(np.float64).T
+        for k in touched:
+            sel = np.nonzero(ids == k)[0]
+            ref[sel] += oap.apply_factored(None, x[sel], *ts[k])
+        check_close(y, ref, what="c2 fused")
+
+
+def test_c4_matrix_full_size():
+    """Mistral GQA k projection (1024x4096) at 1/32, 16 tenants, 128 tokens."""
+    note("c4 k matrix")
+    m = synth.make_c4_matrix(1)
+    views = [upload(d.spec, d) for d in m["deltas"]]
+    y, _, flag = _mt_run(views, m["w"], m["x"], m["ids"])
+    assert flag == 0
+    ref = oap.apply_multitenant(m["w"], m["x"], m["ids"], [oracle_tenant(d) for d in m["deltas"]])
+    check_close(y, ref, what="c4")
+
+
+# ----------------------------------------------------------------- prefill
+def test_prefill_small_segments():
+    note("prefill small")
+    t = torch()
+    rng = np.random.default_rng(12)
+    spec = (256, 384, 2, 9, 40)
+    ds = [synth.small_delta(80 + k, *spec) for k in range(3)]
+    views = [upload(spec, d) for d in ds]
+    seg = np.array([0, 5, 5, 37], np.int32)   # an empty tenant in the middle
+    T = int(seg[-1])
+    w = synth.base_weight(rng, 256, 384)
+    x = synth.activations(rng, T, 384)
+    ws = workspace(trs.DC_OP_PREFILL, [spec] * 3, T)
+    y = t.empty((T, 256), dtype=t.int16, device="cuda")
+    trs.dc_apply_prefill(views, dev_u16(w), dev_u16(x), seg, y, ws)
+    t.cuda.synchronize()
+    ref = oap.apply_prefill(w, x, seg, [oracle_tenant(d) for d in ds])
+    check_close(y_to_f64(y), ref, what="prefill")

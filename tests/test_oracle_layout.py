@@ -30,31 +30,40 @@ def test_group_byte_sizes():
         assert layout.bitstream(np.zeros(128, np.uint8), b).nbytes == size
 
 
-def test_regions_tiny_golden():
-    spec = (128, 128, 1, 1, 1)
+GOLDEN_SPECS = {"layout_tiny.txt": (128, 128, 1, 1, 1), "layout_kblocks.txt": (128, 128, 0, 0, 40)}
+
+
+@pytest.mark.parametrize("fixture", sorted(GOLDEN_SPECS))
+def test_regions_golden(fixture):
+    spec = GOLDEN_SPECS[fixture]
     reg = layout.regions(spec)
-    for ln in read_golden("layout_tiny.txt"):
+    for ln in read_golden(fixture):
         f = ln.split()
         if f[0] == "place":
             continue
         assert reg[f[0]] == (int(f[1]), int(f[2])), f[0]
-    assert layout.packed_bytes(spec) == 5632
+    assert layout.packed_bytes(spec) == reg["END"][0]
 
 
-def test_single_code_placements_golden():
-    spec = (128, 128, 1, 1, 1)
-    seg_rank = {8: 0, 3: 1, 2: 2}
-    for ln in read_golden("layout_tiny.txt"):
+@pytest.mark.parametrize("fixture", sorted(GOLDEN_SPECS))
+def test_single_code_placements_golden(fixture):
+    spec = GOLDEN_SPECS[fixture]
+    out, inn, n8, n3, n2 = spec
+    r = n8 + n3 + n2
+    first = {8: 0, 3: n8, 2: n8 + n3}
+    for ln in read_golden(fixture):
         f = ln.split()
         if f[0] != "place":
             continue
-        side, b, pos, code, off, word = f[1], int(f[2]), int(f[3]), int(f[4]), int(f[5]), int(f[6], 16)
-        cu = np.zeros((3, 128), np.uint8)
-        cv = np.zeros((3, 128), np.uint8)
-        (cu if side == "U" else cv)[seg_rank[b], pos] = code
-        z = np.zeros((3, 1, 2), np.uint16)
-        buf = layout.pack(spec, cu, cv, z, z, np.zeros(3, np.float32))
-        assert buf[off:off + 4].view("<u4")[0] == word
+        side, b, pos, li, code = f[1], int(f[2]), int(f[3]), int(f[4]), int(f[5])
+        off, word = int(f[6]), int(f[7], 16)
+        cu = np.zeros((r, out), np.uint8)
+        cv = np.zeros((r, inn), np.uint8)
+        (cu if side == "U" else cv)[first[b] + li, pos] = code
+        zu = np.zeros((r, out // 128, 2), np.uint16)
+        zv = np.zeros((r, inn // 128, 2), np.uint16)
+        buf = layout.pack(spec, cu, cv, zu, zv, np.zeros(r, np.float32))
+        assert buf[off:off + 4].copy().view("<u4")[0] == word
         nz = np.nonzero(buf)[0]
         assert nz.min() >= off and nz.max() < off + 4   # nothing else was written
 
@@ -97,20 +106,30 @@ def test_pack_roundtrip_hypothesis(go, gi, n8, n3, n2, seed):
 
 
 def test_pad_codes_are_zero():
-    """U ranks past n inside the last K-block, pad s/z entries and pad bytes
-    are zero."""
+    """U ranks past n inside the last K-block and pad s/z entries are zero."""
     spec = (256, 128, 3, 5, 7)
     d = synth.small_delta(1, *spec)
     d.codes_u[:] = np.where(d.bits()[:, None] == 8, 255, np.where(d.bits()[:, None] == 3, 7, 3))
     buf = layout.pack(spec, d.codes_u, d.codes_v, d.sz_u, d.sz_v, d.sigma)
     reg = layout.regions(spec)
     off, size = reg["UC2"]
-    words = buf[off:off + size].view("<u4").reshape(256 // 16, 1, 16, 2)
-    # 7 codes of value 3 -> low 14 bits set in word 0 of each row's K-block
-    assert np.all(words[..., 0] == (1 << 14) - 1) and np.all(words[..., 1] == 0)
+    words = buf[off:off + size].view("<u4").reshape(256 // 16, 16)   # one 1-word K-block per row
+    assert np.all(words == (1 << 14) - 1)        # 7 codes of value 3: low 14 bits
+    off, size = reg["UC3"]
+    words = buf[off:off + size].view("<u4").reshape(256 // 16, 16)   # 5 ranks * 3 bits -> 1 word
+    assert np.all(words == (1 << 15) - 1)
     off, size = reg["US3"]
-    us = buf[off:off + size].view("<u4").reshape(2, 32)
-    assert np.all(us[:, 5:] == 0)
+    us = buf[off:off + size].view("<u4").reshape(2, 8)
+    assert np.all(us[:, 5:] == 0) and np.all(us[:, :5] != 0)
     off, size = reg["UC8"]
-    uc = buf[off:off + size].reshape(256, 4)
-    assert np.all(uc[:, :3] == 255) and np.all(uc[:, 3] == 0)
+    assert np.all(buf[off:off + size] == 255) and size == 256 * 3
+
+
+def test_u_row_words():
+    # full K-blocks take b words; the last keeps ceil(m*b/32)
+    assert layout.u_row_words(968, 2) == 30 * 2 + 1
+    assert layout.u_row_words(47, 3) == 3 + 2
+    assert layout.u_row_words(32, 3) == 3
+    assert layout.u_row_words(16, 3) == 2
+    assert layout.u_row_words(1414, 2) == 44 * 2 + 1
+    assert layout.u_row_words(0, 2) == 0

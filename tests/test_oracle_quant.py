@@ -176,3 +176,19 @@ def test_compress_segments_and_order():
     assert cv[:2].max() > 7 and cv[2:6].max() <= 7 and cv[6:].max() <= 3
     assert cv[2:6].max() == 7 and cv[6:].max() == 3
     assert np.array_equal(sg, s[:11])
+
+
+@pytest.mark.parametrize("bits", [8, 3, 2])
+def test_dequantize_exact_rounds_to_dequantize(bits):
+    """The exact grid values round to the fp16 dequantized values bit for
+    bit, and differ from them by at most half an fp16 ulp."""
+    rng = np.random.default_rng(40 + bits)
+    w = (rng.standard_normal(128 * 6) * 0.01).astype(np.float32)
+    q, s, z = quant.quantize_vector(w, bits)
+    ex = quant.dequantize_exact(q, s, z)
+    h = quant.dequantize(q, s, z)
+    assert np.array_equal(quant.fp16_rne(ex).view(np.uint16), h.view(np.uint16))
+    ulp = np.spacing(np.abs(h).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(ex - h.astype(np.float64)) <= ulp / 2)
+    # a hand value: s = 1 + 2^-10, q - z = 3 -> 3 + 3*2^-10 exactly
+    assert quant.dequantize_exact(np.array([3] + [0] * 127), [np.float16(1 + 2 ** -10)], [0.0])[0] == 3 + 3 * 2 ** -10
