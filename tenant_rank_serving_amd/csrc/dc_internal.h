@@ -91,7 +91,9 @@ struct WsLayout {
   size_t flags;   // uint32 status word (+ padding to 256 B)
   size_t offs;    // int32 [n+2] bucket starts in sorted order (bucket n = backbone only)
   size_t perm;    // int32 [T] sorted position -> token index
-  size_t xs;      // fp32 [T][in] activations in sorted order
+  size_t xf;      // uint8 [T][in/128][256] fp8 hi/lo fragments of x (matrix-core A operand)
+  size_t xsc;     // uint32 [T][in/128] E8M0 block scales of the hi fragments
+  size_t xsum;    // fp32 [T][in/128] sums of x over each 128-group
   size_t tv;      // fp32 [T][rs] V-side results t = sigma * (V x), sorted order
   size_t ybase;   // fp32 [T][out] backbone product, original order
   size_t total;
@@ -107,7 +109,10 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rmax, int32_t 
   W->flags = take(256);
   W->offs = take(4 * ((size_t)n + 2));
   W->perm = take(4 * (size_t)T);
-  W->xs = take(4 * (size_t)T * in);
+  const size_t items = (size_t)T * (in / kGroup);
+  W->xf = take(256 * items);
+  W->xsc = take(4 * items);
+  W->xsum = take(4 * items);
   W->tv = take(4 * (size_t)T * W->rs);
   W->ybase = take(with_base ? 4 * (size_t)T * out : 0);
   W->total = round_up(o, kAlign);
@@ -137,5 +142,6 @@ struct ApplyArgs {
   void* const* events;         // optional DC_STAGE_COUNT + 1 hipEvent_t, may be null
 };
 int launch_apply(const ApplyArgs& a);
+int launch_base(const uint16_t* W, const uint16_t* x, float* ybase, int out, int in, int T, void* stream);
 int launch_dequant(const Tenant& t, int32_t out, int32_t in, uint16_t* u16, uint16_t* v16, void* stream);
 }  // namespace dc
