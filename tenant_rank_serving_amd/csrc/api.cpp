@@ -14,18 +14,27 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x0 < y0 + nb && y0 < x0 + na;
 }
 
-// Checks the tenant specs of one call; fills out/in/rmax.
-dc_status check_specs(const dc_spec* specs, int32_t n, int32_t* out, int32_t* in, int32_t* rmax) {
+// Checks the tenant specs of one call; fills the shape and the work-split maxima.
+struct Dims {
+  int32_t out, in, rmax, vb, us;
+};
+
+dc_status check_specs(const dc_spec* specs, int32_t n, Dims* d) {
   if (!specs || n < 1) return DC_ERR_INVALID_ARG;
   if (n > DC_MAX_TENANTS) return DC_ERR_UNSUPPORTED;
-  *out = specs[0].out;
-  *in = specs[0].in;
-  *rmax = 0;
+  d->out = specs[0].out;
+  d->in = specs[0].in;
+  d->rmax = d->vb = 0;
+  d->us = 1;
   for (int k = 0; k < n; ++k) {
     if (dc_check_spec(&specs[k]) != DC_OK) return DC_ERR_SHAPE;
-    if (specs[k].out != *out || specs[k].in != *in) return DC_ERR_SHAPE;
+    if (specs[k].out != d->out || specs[k].in != d->in) return DC_ERR_SHAPE;
     const int32_t r = specs[k].n8 + specs[k].n3 + specs[k].n2;
-    if (r > *rmax) *rmax = r;
+    if (r > d->rmax) d->rmax = r;
+    const int32_t vb = dc::v_blocks(specs[k].n8, specs[k].n3, specs[k].n2);
+    if (vb > d->vb) d->vb = vb;
+    const int32_t us = dc::u_slices(specs[k].n3, specs[k].n2);
+    if (us > d->us) d->us = us;
   }
   return DC_OK;
 }
@@ -38,9 +47,10 @@ dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const ui
   if (T < 0) return DC_ERR_INVALID_ARG;
   dc_spec specs[DC_MAX_TENANTS] = {};
   for (int k = 0; k < n; ++k) specs[k] = views[k].spec;
-  int32_t out, in, rmax;
-  dc_status st = check_specs(specs, n, &out, &in, &rmax);
+  Dims dm;
+  dc_status st = check_specs(specs, n, &dm);
   if (st != DC_OK) return st;
+  const int32_t out = dm.out, in = dm.in, rmax = dm.rmax;
   dc::TenantTable table;
   std::memset(&table, 0, sizeof(table));
   for (int k = 0; k < n; ++k) {
@@ -59,7 +69,7 @@ dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const ui
     return DC_ERR_ALIGN;
   if (overlap(x, (size_t)T * in * 2, y, (size_t)T * out * 2)) return DC_ERR_INVALID_ARG;
   dc::WsLayout wl{};
-  dc::ws_layout(T, in, out, rmax, n, true, &wl);
+  dc::ws_layout(T, in, out, rmax, n, true, dm.vb, dm.us, &wl);
   if (ws_bytes < wl.total) return DC_ERR_BUFFER;
   if (T == 0) return DC_OK;
   dc::ApplyArgs a;
@@ -89,10 +99,10 @@ extern "C" {
 size_t dc_workspace_bytes(int32_t op, const dc_spec* specs, int32_t n, int32_t T) {
   if (op < DC_OP_DECODE || op > DC_OP_PREFILL || T < 0) return 0;
   if (op == DC_OP_DECODE && n != 1) return 0;
-  int32_t out, in, rmax;
-  if (check_specs(specs, n, &out, &in, &rmax) != DC_OK) return 0;
+  Dims dm;
+  if (check_specs(specs, n, &dm) != DC_OK) return 0;
   dc::WsLayout wl{};
-  dc::ws_layout(T, in, out, rmax, n, true, &wl);
+  dc::ws_layout(T, dm.in, dm.out, dm.rmax, n, true, dm.vb, dm.us, &wl);
   return wl.total;
 }
 

@@ -87,6 +87,21 @@ struct TenantTable {
 };
 
 // Workspace layout of one apply call.
+// Work decomposition of the matrix-core path (shared by host sizing and kernels).
+constexpr int kVSlice = 16;   // 128-groups of the input per V-side work item
+constexpr int kVRows = 8;     // token rows per V-side pass
+constexpr int kUPass = 4;     // 128-rank chunks per U-side work item
+
+DC_HD inline int v_slices(int in) { return (in / kGroup + kVSlice - 1) / kVSlice; }
+// V-side rank blocks of a tenant: [8-bit rows if any] [3-bit 64-rank blocks] [2-bit 64-rank blocks]
+DC_HD inline int v_blocks(int n8, int n3, int n2) { return (n8 > 0 ? 1 : 0) + (n3 + 63) / 64 + (n2 + 63) / 64; }
+// U-side rank slices of a tenant (at least one: it applies the 8-bit pairs and the backbone)
+DC_HD inline int u_slices(int n3, int n2) {
+  const int nc = (n3 + 127) / 128 + (n2 + 127) / 128;
+  const int s = (nc + kUPass - 1) / kUPass;
+  return s > 0 ? s : 1;
+}
+
 struct WsLayout {
   size_t flags;   // uint32 status word (+ padding to 256 B)
   size_t offs;    // int32 [n+2] bucket starts in sorted order (bucket n = backbone only)
@@ -96,13 +111,21 @@ struct WsLayout {
   size_t xsum;    // fp32 [T][in/128] sums of x over each 128-group
   size_t tv;      // fp32 [T][rs] V-side results t = sigma * (V x), sorted order
   size_t ybase;   // fp32 [T][out] backbone product, original order
+  size_t vpart;   // fp32 [v_slices][T][rs] V-side partial sums per input slice
+  size_t upart;   // fp32 [u_slices][T][out] U-side partial sums per rank slice
+  size_t cnt;     // uint32 [n][vb + Go] arrival counters (zeroed by every call)
   size_t total;
   int32_t rs;     // row stride of tv (max r over tenants, rounded up to 4)
+  int32_t vb;     // max V-side rank blocks per tenant
+  int32_t us;     // max U-side rank slices per tenant
 };
 
+// vbmax/usmax: max over tenants of v_blocks and u_slices.
 inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rmax, int32_t n, bool with_base,
-                      WsLayout* W) {
+                      int32_t vbmax, int32_t usmax, WsLayout* W) {
   if (T < 0 || n < 0) return false;
+  W->vb = vbmax;
+  W->us = usmax;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = round_up(o, kAlign); o = at + bytes; return at; };
   W->rs = (int32_t)round_up((size_t)(rmax > 0 ? rmax : 1), 4);
@@ -115,6 +138,9 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rmax, int32_t 
   W->xsum = take(4 * items);
   W->tv = take(4 * (size_t)T * W->rs);
   W->ybase = take(with_base ? 4 * (size_t)T * out : 0);
+  W->vpart = take(4 * (size_t)v_slices(in) * T * W->rs);
+  W->upart = take(4 * (size_t)usmax * T * out);
+  W->cnt = take(4 * (size_t)n * (vbmax + out / kGroup));
   W->total = round_up(o, kAlign);
   return true;
 }

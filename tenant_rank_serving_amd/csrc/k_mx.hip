@@ -101,6 +101,19 @@ __device__ __forceinline__ v8i b_fp6(uint32_t w0, uint32_t w1, uint32_t w2) {
   return b;
 }
 
+// Keeps the source registers of a chain of matrix-core ops allocated until
+// its result has been read back into `d`.  Without it the register allocator
+// may hand an A operand or scale VGPR of an op still in flight to a load
+// issued after it (observed: an LDS load landing in the A and scale VGPRs of
+// the preceding v_mfma_scale changed its result).
+__device__ __forceinline__ void hold(f32x4& d, const v8i& a0, const v8i& a1, const v8i& b, int s0, int s1, int sb) {
+  asm volatile("" : "+v"(d) : "v"(a0), "v"(a1), "v"(b), "v"(s0), "v"(s1), "v"(sb));
+}
+__device__ __forceinline__ void hold(f32x4& d, const v8i& a0, const v8i& a1, const v8i& a2, const v8i& b, int s0,
+                                     int s1, int s2, int sb) {
+  asm volatile("" : "+v"(d) : "v"(a0), "v"(a1), "v"(a2), "v"(b), "v"(s0), "v"(s1), "v"(s2), "v"(sb));
+}
+
 __device__ __forceinline__ f32x4 mma(const v8i& a, const v8i& b, f32x4 c, int sa, int fmt_b, int sb) {
   if (fmt_b == kFmtFp4)
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kFmtFp8, kFmtFp4, 0, sa, 0, sb);
@@ -132,6 +145,29 @@ struct SegArg {
   int32_t v[DC_MAX_TENANTS + 1];
 };
 
+// ------------------------------------------------------- split-K combine
+// Work items of one output block add their partial sums in a fixed order:
+// each item stores its partials with device-coherent stores, waits until
+// they have completed, then bumps the block's arrival counter; the item that
+// arrives last reads every partial back with device-coherent loads.  Only
+// these accesses bypass the per-XCD L2s; nothing writes back or invalidates a
+// whole L2 (which a device-scope fence would).
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// True in every thread of the item that arrives last of `total`.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, int total, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(total - 1);
+  __syncthreads();
+  return *flag != 0;
+}
+
 // ------------------------------------------------------------------- prep
 // Block 0 routes the tokens (stable counting sort by tenant; bucket n holds
 // the backbone-only tokens).  Every other wave turns one (token, 128-group)
@@ -140,9 +176,11 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
                                               int32_t T, int32_t in, int32_t n, int32_t mode, SegArg seg,
                                               int32_t* __restrict__ offs, int32_t* __restrict__ perm,
                                               uint32_t* __restrict__ flags, uint8_t* __restrict__ xf,
-                                              uint32_t* __restrict__ xsc, float* __restrict__ xsum) {
+                                              uint32_t* __restrict__ xsc, float* __restrict__ xsum,
+                                              uint32_t* __restrict__ cnt, int32_t ncnt) {
   const int tid = threadIdx.x;
   if (blockIdx.x == 0) {
+    for (int i = tid; i < ncnt; i += blockDim.x) cnt[i] = 0u;
     if (mode != 1) {
       for (int p = tid; p < T; p += blockDim.x) perm[p] = p;
       if (tid == 0) {
@@ -235,134 +273,204 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
 }
 
 // ------------------------------------------------------------------ V side
-// blockIdx.y = tenant, blockIdx.x = task.  Task 0 of a tenant with 8-bit
-// pairs runs them on the vector ALU; every other task is four 16-rank tiles
-// of the 3- or 2-bit segment, one per wave, each over the whole input.
-__device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, const uint16_t* __restrict__ x,
-                           const int32_t* __restrict__ perm, int p0, int p1, float* __restrict__ tv, int rs) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const Seg sg = seg_of(tn, L, 0);
-  const float* sigma = reinterpret_cast<const float*>(tn.base + L.off[DC_REG_SIGMA]);
-  const int np = (int)round_up(sg.n, 4);
-  const int gi_n = in / kGroup;
-  for (int i = wave; i < sg.n; i += 4) {
-    const uint8_t* row = sg.vc + (size_t)i * in;   // 8-bit group bitstreams are plain bytes
-    for (int pc = p0; pc < p1; pc += 8) {
-      const int nt = min(8, p1 - pc);
-      int tok[8];
+// Work item (block): tenant k = blockIdx.y; blockIdx.x = rank block rb *
+// v_slices + input slice s.  Rank blocks: the 8-bit rows (vector ALU, fp16
+// dequantized weights), then 64-rank blocks of the 3-bit and of the 2-bit
+// segment (four 16-rank tiles, one per wave, on the matrix cores).  An item
+// covers kVSlice 128-groups of the input; it issues all of its loads up
+// front, writes a partial sum per (token, rank), and the last item of a rank
+// block to arrive adds the slices in slice order and writes t = sigma * sum.
+struct VsideLds {
+  int4 frag[kVSlice][kVRows][4][4];   // [group][token row][lane group][hi0 hi1 lo0 lo1]
+  uint32_t sc[kVSlice][kVRows];       // E8M0 words
+  float xs[kVSlice][kVRows];          // group sums
+  int last;
+};
+
+template <int B>
+struct CodeW;
+template <>
+struct CodeW<2> { uint32_t w[2]; };
+template <>
+struct CodeW<3> { uint32_t w[3]; };
+
+template <int B>
+__device__ __forceinline__ CodeW<B> load_codes(const uint32_t* row, int gi, int q) {
+  CodeW<B> c;
+  if constexpr (B == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(row + (size_t)gi * 8 + 2 * q);
+    c.w[0] = v.x; c.w[1] = v.y;
+  } else {
+    const uint32_t* wp = row + (size_t)gi * 12 + 3 * q;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) tok[q] = perm[pc + (q < nt ? q : 0)];
-      float acc[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-      for (int j0 = lane * 4; j0 < in; j0 += 256) {
-        const uint32_t e = sg.vs[(size_t)(j0 / kGroup) * np + i];
-        const float s = f16f(e & 0xFFFFu), z = f16f(e >> 16);
-        const uint32_t c4 = *reinterpret_cast<const uint32_t*>(row + j0);
-        float w[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = (float)(_Float16)(s * ((float)((c4 >> (8 * u)) & 0xFFu) - z));
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          if (q < nt) {
-            const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)tok[q] * in + j0);
-            acc[q] += w[0] * __uint_as_float(xv.x << 16) + w[1] * __uint_as_float(xv.x & 0xFFFF0000u) +
-                      w[2] * __uint_as_float(xv.y << 16) + w[3] * __uint_as_float(xv.y & 0xFFFF0000u);
-          }
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        float v = acc[q];
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-        acc[q] = v;
-      }
-      if (lane == 0)
-        for (int q = 0; q < nt; ++q) tv[(size_t)(pc + q) * rs + i] = sigma[i] * acc[q];
-    }
+    for (int i = 0; i < B; ++i) c.w[i] = wp[i];
   }
-  (void)gi_n;
+  return c;
 }
 
 template <int B>
-__device__ void vside_tile(const Seg& sg, int tile, const float* __restrict__ sigma, int in,
-                           const int32_t* __restrict__ perm, int p0, int p1, const uint8_t* __restrict__ xf,
-                           const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
-                           float* __restrict__ tv, int rs) {
+__device__ __forceinline__ v8i b_op(const CodeW<B>& c) {
+  if constexpr (B == 2) return b_fp4(c.w[0], c.w[1]);
+  else return b_fp6(c.w[0], c.w[1], c.w[2]);
+}
+
+// Stage x fragments of token rows [pb, pb + kVRows) and groups [g0, g0+kVSlice)
+// into LDS: thread tid moves int4 (tid & 3) of lane group (tid>>2)&3 of row
+// (tid>>4)&7 for groups (tid>>7) + 2u; threads < 128 also move one
+// (group, row) scale word and sum.
+__device__ __forceinline__ void x_stage(VsideLds& S, const uint8_t* __restrict__ xf, const uint32_t* __restrict__ xsc,
+                                        const float* __restrict__ xsum, const int32_t* __restrict__ perm, int gi_n,
+                                        int g0, int pb, int nt) {
+  const int tid = threadIdx.x;
+  const int part = tid & 3, qq = (tid >> 2) & 3, row = (tid >> 4) & 7, gh = tid >> 7;
+  const int tok = row < nt ? perm[pb + row] : -1;
+  int4 v[kVSlice / 2];
+#pragma unroll
+  for (int u = 0; u < kVSlice / 2; ++u) {
+    const int gl = gh + 2 * u, gi = g0 + gl;
+    v[u] = make_int4(0, 0, 0, 0);
+    if (tok >= 0 && gi < gi_n) v[u] = reinterpret_cast<const int4*>(xf + ((size_t)tok * gi_n + gi) * kXFrag + qq * 64)[part];
+  }
+  uint32_t scw = 0x7F7F7F7Fu;
+  float xsv = 0.f;
+  const int sr = tid & 7, sg = tid >> 3;   // (row, group) of the scale/sum this thread moves
+  if (tid < kVRows * kVSlice) {
+    const int stok = sr < nt ? perm[pb + sr] : -1;
+    if (stok >= 0 && g0 + sg < gi_n) {
+      scw = xsc[(size_t)stok * gi_n + g0 + sg];
+      xsv = xsum[(size_t)stok * gi_n + g0 + sg];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kVSlice / 2; ++u) S.frag[gh + 2 * u][row][qq][part] = v[u];
+  if (tid < kVRows * kVSlice) {
+    S.sc[sg][sr] = scw;
+    S.xs[sg][sr] = xsv;
+  }
+}
+
+// 8-bit rows of a tenant over one input slice, all tokens; partial sums
+// (without sigma) to part[p][i].
+__device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, const uint16_t* __restrict__ x,
+                           const int32_t* __restrict__ perm, int p0, int p1, float* __restrict__ part, int rs) {
+  constexpr int kQ = kVSlice * kGroup / 4 / 256;   // quads per thread per slice (2)
+  __shared__ float red[4][8];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const Seg sg = seg_of(tn, L, 0);
+  const int np = (int)round_up(sg.n, 4);
+  const int q0 = s * kVSlice * kGroup / 4, nq = in / 4;
+  for (int i = 0; i < sg.n; ++i) {
+    const uint8_t* row = sg.vc + (size_t)i * in;   // 8-bit group bitstreams are plain bytes
+    float w[kQ][4];
+#pragma unroll
+    for (int m = 0; m < kQ; ++m) {
+      const int qd = q0 + tid + 256 * m;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[m][u] = 0.f;
+      if (qd < nq) {
+        const uint32_t e = sg.vs[(size_t)(qd * 4 / kGroup) * np + i];
+        const uint32_t c4 = *reinterpret_cast<const uint32_t*>(row + (size_t)qd * 4);
+        const float sc = f16f(e & 0xFFFFu), z = f16f(e >> 16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[m][u] = (float)(_Float16)(sc * ((float)((c4 >> (8 * u)) & 0xFFu) - z));
+      }
+    }
+    for (int pc = p0; pc < p1; pc += 8) {
+      const int nt = min(8, p1 - pc);
+      float acc[8];
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) {
+        acc[t8] = 0.f;
+        if (t8 < nt) {
+          const uint16_t* xr = x + (size_t)perm[pc + t8] * in;
+#pragma unroll
+          for (int m = 0; m < kQ; ++m) {
+            const int qd = q0 + tid + 256 * m;
+            if (qd < nq) {
+              const uint2 xv = *reinterpret_cast<const uint2*>(xr + (size_t)qd * 4);
+              acc[t8] += w[m][0] * __uint_as_float(xv.x << 16) + w[m][1] * __uint_as_float(xv.x & 0xFFFF0000u) +
+                         w[m][2] * __uint_as_float(xv.y << 16) + w[m][3] * __uint_as_float(xv.y & 0xFFFF0000u);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) {
+        float v = acc[t8];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+        if (lane == 0) red[wave][t8] = v;
+      }
+      __syncthreads();
+      if (tid < nt) st_dev(part + (size_t)(pc + tid) * rs + i, (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]));
+      __syncthreads();
+    }
+  }
+}
+
+// One 16-rank tile per wave over one input slice, all tokens in passes of kVRows.
+template <int B>
+__device__ void vside_tiles(const Seg& sg, int tile, int in, int s, const int32_t* __restrict__ perm, int p0,
+                            int p1, const uint8_t* __restrict__ xf, const uint32_t* __restrict__ xsc,
+                            const float* __restrict__ xsum, float* __restrict__ part, int rs, VsideLds& S) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, q = lane >> 4;
   const int gi_n = in / kGroup;
-  const int li = tile * 16 + col;                 // local rank held by this lane (column)
+  const int g0 = s * kVSlice;
+  const int li = tile * 16 + col;
   const bool rv = li < sg.n;
   const int np = (int)round_up(sg.n, 4);
   const uint32_t* row = reinterpret_cast<const uint32_t*>(sg.vc) + (size_t)(rv ? li : 0) * gi_n * 4 * B;
+  const uint32_t* vsp = sg.vs + (rv ? li : 0);
   const int fmt = B == 2 ? kFmtFp4 : kFmtFp6;
   const int bsc = B == 2 ? kScaleFp4Code : kScaleFp6Code;
-  for (int pb = p0; pb < p1; pb += 64) {
-    const int nt = min(64, p1 - pb);
-    const int ntt = (nt + 15) >> 4;
-    int arow[4];     // token (original index) of A row `col` in token tile tt, or -1
-    int drow[4][4];  // token of D row 4q+r in token tile tt, or -1
+  // every code and scale/zero word of the slice, issued at once
+  CodeW<B> cw[kVSlice];
+  uint32_t zw[kVSlice];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int pa = pb + tt * 16 + col;
-      arow[tt] = (tt < ntt && pa < p1) ? perm[pa] : -1;
+  for (int u = 0; u < kVSlice; ++u) {
+    const int gi = g0 + u < gi_n ? g0 + u : gi_n - 1;
+    cw[u] = load_codes<B>(row, gi, q);
+    zw[u] = vsp[(size_t)gi * np];
+  }
+  for (int pb = p0; pb < p1; pb += kVRows) {
+    const int nt = min(kVRows, p1 - pb);
+    __syncthreads();   // LDS reuse across passes
+    x_stage(S, xf, xsc, xsum, perm, gi_n, g0, pb, nt);
+    __syncthreads();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kVSlice; ++u) {
+      if (g0 + u < gi_n) {
+        v8i ah = {0, 0, 0, 0, 0, 0, 0, 0}, al = ah;
+        int sh = 127;
+        if (col < kVRows) {
+          const int4* fr = S.frag[u][col][q];
+          const int4 h0 = fr[0], h1 = fr[1], l0 = fr[2], l1 = fr[3];
+          ah = v8i{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+          al = v8i{l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+          sh = (int)((S.sc[u][col] >> (8 * q)) & 0xFFu);
+        }
+        v8i bop = b_op<B>(cw[u]);
+        if (!rv) bop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        const int sl = sh - 5;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        d = mma(ah, bop, d, sh, fmt, bsc);
+        d = mma(al, bop, d, sl, fmt, bsc);
+        hold(d, ah, al, bop, sh, sl, bsc);
+        const float sc = f16f(zw[u] & 0xFFFFu), z = f16f(zw[u] >> 16);
+        if (q < 2) {   // D rows 4q+r < 8 are the staged tokens
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] += sc * (d[r] - z * S.xs[u][4 * q + r]);
+        }
+      }
+    }
+    if (rv && q < 2) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int pd = pb + tt * 16 + 4 * q + r;
-        drow[tt][r] = (tt < ntt && pd < p1) ? perm[pd] : -1;
+        const int pd = pb + 4 * q + r;
+        if (4 * q + r < nt) st_dev(part + (size_t)pd * rs + sg.lo + li, acc[r]);
       }
-    }
-    f32x4 acc[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int gi = 0; gi < gi_n; ++gi) {
-      v8i bop;
-      if (B == 2) {
-        const uint2 w = *reinterpret_cast<const uint2*>(row + (size_t)gi * 8 + 2 * q);
-        bop = b_fp4(w.x, w.y);
-      } else {
-        const uint32_t* wp = row + (size_t)gi * 12 + 3 * q;
-        bop = b_fp6(wp[0], wp[1], wp[2]);
-      }
-      if (!rv) bop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      const uint32_t e = rv ? sg.vs[(size_t)gi * np + li] : 0u;
-      const float s = f16f(e & 0xFFFFu), z = f16f(e >> 16);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if (tt < ntt) {
-          v8i ah = {0, 0, 0, 0, 0, 0, 0, 0}, al = {0, 0, 0, 0, 0, 0, 0, 0};
-          int sh = 127;
-          if (arow[tt] >= 0) {
-            const size_t item = (size_t)arow[tt] * gi_n + gi;
-            const int4* fp = reinterpret_cast<const int4*>(xf + item * kXFrag + q * 64);
-            const int4 h0 = fp[0], h1 = fp[1], l0 = fp[2], l1 = fp[3];
-            ah = v8i{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-            al = v8i{l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-            sh = (int)((xsc[item] >> (8 * q)) & 0xFFu);
-          }
-          f32x4 d = {0.f, 0.f, 0.f, 0.f};
-          d = mma(ah, bop, d, sh, fmt, bsc);
-          d = mma(al, bop, d, sh - 5, fmt, bsc);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int tk = drow[tt][r];
-            const float X = tk >= 0 ? xsum[(size_t)tk * gi_n + gi] : 0.f;
-            acc[tt][r] += s * (d[r] - z * X);
-          }
-        }
-      }
-    }
-    if (rv) {
-      const float sig = sigma[sg.lo + li];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int pd = pb + tt * 16 + 4 * q + r;
-          if (tt < ntt && pd < p1) tv[(size_t)pd * rs + sg.lo + li] = sig * acc[tt][r];
-        }
     }
   }
 }
@@ -371,53 +479,94 @@ __global__ void __launch_bounds__(256) k_vside(TenantTable tt, int32_t out, int3
                                                const uint16_t* __restrict__ x, const int32_t* __restrict__ offs,
                                                const int32_t* __restrict__ perm, const uint8_t* __restrict__ xf,
                                                const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
-                                               float* __restrict__ tv, int32_t rs) {
+                                               float* __restrict__ vpart, float* __restrict__ tv, int32_t rs,
+                                               int32_t T, uint32_t* __restrict__ cnt, int32_t vbmax) {
   const int k = blockIdx.y;
   const int p0 = offs[k], p1 = offs[k + 1];
   if (p0 >= p1) return;
   const Tenant tn = tt.t[k];
+  const int ns = v_slices(in);
+  const int rb = blockIdx.x / ns, s = blockIdx.x % ns;
+  if (rb >= v_blocks(tn.n8, tn.n3, tn.n2)) return;
   Layout L;
   layout_of(out, in, tn.n8, tn.n3, tn.n2, &L);
-  int task = blockIdx.x;
-  if (tn.n8 > 0) {
-    if (task == 0) { vside_8bit(tn, L, in, x, perm, p0, p1, tv, rs); return; }
-    --task;
+  __shared__ VsideLds S;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  float* part = vpart + (size_t)s * T * rs;
+  const int b3 = (tn.n3 + 63) / 64;
+  int lo, hi;   // global rank range of the block
+  int b = rb;
+  if (tn.n8 > 0 && b == 0) {
+    vside_8bit(tn, L, in, s, x, perm, p0, p1, part, rs);
+    lo = 0; hi = tn.n8;
+  } else {
+    if (tn.n8 > 0) --b;
+    if (b < b3) {
+      const Seg sg = seg_of(tn, L, 1);
+      vside_tiles<3>(sg, b * 4 + wave, in, s, perm, p0, p1, xf, xsc, xsum, part, rs, S);
+      lo = sg.lo + b * 64; hi = min(sg.lo + sg.n, lo + 64);
+    } else {
+      const Seg sg = seg_of(tn, L, 2);
+      vside_tiles<2>(sg, (b - b3) * 4 + wave, in, s, perm, p0, p1, xf, xsc, xsum, part, rs, S);
+      lo = sg.lo + (b - b3) * 64; hi = min(sg.lo + sg.n, lo + 64);
+    }
   }
+  // last arriving slice of this rank block adds the slices in order
+  if (!arrive_last(&cnt[(size_t)k * vbmax + rb], ns, &S.last)) return;
   const float* sigma = reinterpret_cast<const float*>(tn.base + L.off[DC_REG_SIGMA]);
-  const int wave = threadIdx.x >> 6;
-  const int t3 = (tn.n3 + 15) / 16, t2 = (tn.n2 + 15) / 16;
-  const int k3 = (t3 + 3) / 4, k2 = (t2 + 3) / 4;
-  if (task < k3) {
-    const int tile = task * 4 + wave;
-    if (tile < t3) vside_tile<3>(seg_of(tn, L, 1), tile, sigma, in, perm, p0, p1, xf, xsc, xsum, tv, rs);
-  } else if (task < k3 + k2) {
-    const int tile = (task - k3) * 4 + wave;
-    if (tile < t2) vside_tile<2>(seg_of(tn, L, 2), tile, sigma, in, perm, p0, p1, xf, xsc, xsum, tv, rs);
+  const int nr = hi - lo, cells = (p1 - p0) * nr;
+  for (int c = tid; c < cells; c += 256) {
+    const int p = p0 + c / nr, i = lo + c % nr;
+    float v = 0.f;
+    for (int j = 0; j < ns; ++j) v += ld_dev(vpart + ((size_t)j * T + p) * rs + i);
+    tv[(size_t)p * rs + i] = sigma[i] * v;
   }
 }
 
 // ------------------------------------------------------------------ U side
-// blockIdx.x = 128-row output group g, blockIdx.y = tenant (n = the
-// backbone-only bucket).  Wave w owns rows 32w..32w+31 of the group (two
-// 16-row tiles).  Per 128-rank chunk the block builds the A fragments of
-// t'_i = s_ig t_i (three fp8 pieces) in LDS; y = sum_i q_oi t'_i
-// - sum_i z_ig t'_i + (8-bit pairs) + W x, rounded once to bf16.
+// Work item (block): blockIdx.x = 128-row output group g, blockIdx.y =
+// tenant k (n = the backbone-only bucket), blockIdx.z = rank slice su of
+// kUPass chunks of 128 ranks (3-bit chunks first, then 2-bit).  Wave w builds
+// the A fragments of t'_i = s_ig t_i (three fp8 pieces, E8M0 block scales)
+// for chunk w of the slice: lane (token row i, lane group gq) writes exactly
+// the 32-byte rows an MFMA lane (i, gq) reads.  Then every wave runs its two
+// 16-row output tiles against the slice; its codes were loaded before the
+// A-prep.  The slice's partial sum_i (q_oi - z_ig) t'_i goes to upart; the
+// last slice to arrive adds the slices in order, the 8-bit pairs and W x,
+// rounds once to bf16 and writes y.
 struct UsideLds {
-  uint8_t frag[3][4][16][32];   // [piece][lane group][token row][byte]
-  uint8_t sc[16][4];            // E8M0 of piece 0 per (token row, K-block)
-  float cz[16][16];             // partial sum_i z t' per (token row, thread slot)
+  int4 frag[kUPass][3][4][16][2];   // [chunk][piece][lane group][token row][32 bytes]
+  uint8_t sc[kUPass][16][4];        // E8M0 of piece 0 per (chunk, token row, K-block)
+  float cz[16][16];                 // partial sum_i z t' per (token row, slot)
+  int last;
 };
 
-__global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_t out, int32_t in,
-                                               const int32_t* __restrict__ offs, const int32_t* __restrict__ perm,
-                                               const float* __restrict__ tv, int32_t rs,
-                                               const float* __restrict__ ybase, uint16_t* __restrict__ y) {
-  const int g = blockIdx.x, k = blockIdx.y;
+struct UChunk {
+  int which;   // 1: 3-bit segment, 2: 2-bit segment
+  int c;       // chunk index inside the segment
+};
+
+__device__ __forceinline__ UChunk chunk_of(int ci, int nc3) {
+  UChunk u;
+  if (ci < nc3) { u.which = 1; u.c = ci; }
+  else { u.which = 2; u.c = ci - nc3; }
+  return u;
+}
+
+__global__ void __launch_bounds__(256, 2) k_uside(TenantTable tt, int32_t n, int32_t out, int32_t in,
+                                                  const int32_t* __restrict__ offs, const int32_t* __restrict__ perm,
+                                                  const float* __restrict__ tv, int32_t rs,
+                                                  const float* __restrict__ ybase, float* __restrict__ upart,
+                                                  int32_t T, uint32_t* __restrict__ cnt, int32_t vbmax,
+                                                  uint16_t* __restrict__ y) {
+  const int g = blockIdx.x, k = blockIdx.y, su = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, q = lane >> 4;
   const int p0 = offs[k], p1 = offs[k + 1];
   if (p0 >= p1) return;
+  const int go = out / kGroup;
   if (k == n) {  // backbone-only tokens
+    if (su != 0) return;
     for (int idx = tid; idx < (p1 - p0) * kGroup; idx += 256) {
       const int t = perm[p0 + idx / kGroup];
       const int o = g * kGroup + idx % kGroup;
@@ -426,125 +575,180 @@ __global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_
     return;
   }
   const Tenant tn = tt.t[k];
+  const int nsu = u_slices(tn.n3, tn.n2);
+  if (su >= nsu) return;
   Layout L;
   layout_of(out, in, tn.n8, tn.n3, tn.n2, &L);
   __shared__ UsideLds S;
-  // A-prep thread role: token row ai = tid/16, K-block kb4 = (tid/4)%4, part = tid%4 (8 ranks)
-  const int ai = tid >> 4, kb4 = (tid >> 2) & 3, part = tid & 3;
+  const Seg seg3 = seg_of(tn, L, 1), seg2 = seg_of(tn, L, 2);
+  const int kb3 = (seg3.n + kKBlock - 1) / kKBlock, kb2 = (seg2.n + kKBlock - 1) / kKBlock;
+  const int nc3 = (kb3 + 3) / 4, nc = nc3 + (kb2 + 3) / 4;
+  const int orow[2] = {g * kGroup + wave * 32 + col, g * kGroup + wave * 32 + 16 + col};
+  // codes of the slice for this wave's two tiles
+  uint32_t cw[kUPass][2][3];
+#pragma unroll
+  for (int cb = 0; cb < kUPass; ++cb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) { cw[cb][h][0] = 0u; cw[cb][h][1] = 0u; cw[cb][h][2] = 0u; }
+    const int ci = su * kUPass + cb;
+    if (ci < nc) {
+      const UChunk u = chunk_of(ci, nc3);
+      const Seg& sg = u.which == 1 ? seg3 : seg2;
+      const int kb = 4 * u.c + q;
+      if (kb < (u.which == 1 ? kb3 : kb2)) {
+        const uint32_t* base = reinterpret_cast<const uint32_t*>(sg.uc);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          int nw;
+          const uint32_t* wp = base + u_kblock_word(orow[h], kb, sg.n, sg.b, &nw);
+          cw[cb][h][0] = wp[0];
+          if (nw > 1) cw[cb][h][1] = wp[1];
+          if (nw > 2) cw[cb][h][2] = wp[2];
+        }
+      }
+    }
+  }
+  float* part = upart + (size_t)su * T * out;
+  // A-prep role: token row pi = lane % 16, lane group gq = lane / 16; ranks of
+  // run 0 start at mA = 32(gq/2) + (gq&1) (stride 2), run 1 at 64 + mA.
+  const int pi = col, gq = q;
+  const int mA = 32 * (gq >> 1) + (gq & 1);
   for (int pb = p0; pb < p1; pb += 16) {
     const int nt = min(16, p1 - pb);
-    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    float czp = 0.f;   // this thread's share of sum_i z t' for token row ai
-    for (int which = 1; which <= 2; ++which) {
-      const Seg sg = seg_of(tn, L, which);
-      if (sg.n == 0) continue;
-      const int np = (int)round_up(sg.n, 4);
-      const int kbn = (sg.n + kKBlock - 1) / kKBlock;
-      const int fmt = sg.b == 2 ? kFmtFp4 : kFmtFp6;
-      const int bsc = sg.b == 2 ? kScaleFp4Code : kScaleFp6Code;
-      for (int c = 0; c < (kbn + 3) / 4; ++c) {
-        __syncthreads();
-        {  // A-prep: 8 ranks of K-block (4c + kb4) for token row ai
-          const int m0 = kb4 * 32 + part * 8;              // rank offset inside the 128-rank chunk
-          float tp[8];
+    float czp = 0.f;
+    {
+      const int ci = su * kUPass + wave;
+      int4 pk[3][2];
+      int sbA = 127, sbB = 127;
+#pragma unroll
+      for (int pc = 0; pc < 3; ++pc) { pk[pc][0] = make_int4(0, 0, 0, 0); pk[pc][1] = pk[pc][0]; }
+      if (ci < nc) {
+        const UChunk u = chunk_of(ci, nc3);
+        const Seg& sg = u.which == 1 ? seg3 : seg2;
+        const int np = (int)round_up(sg.n, 4);
+        const bool tok_ok = pi < nt;
+        const float* tvr = tv + (size_t)(pb + (tok_ok ? pi : 0)) * rs + sg.lo + u.c * 128;
+        const uint32_t* usr = sg.us + (size_t)g * np + u.c * 128;
+        const int lim = sg.n - u.c * 128;
+#pragma unroll
+        for (int run = 0; run < 2; ++run) {
+          float tpv[16];
+          uint32_t zz[16];
           float mx = 0.f;
-          const bool tok_ok = ai < nt;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int li = c * 128 + m0 + u;
-            float v = 0.f;
-            if (tok_ok && li < sg.n) {
-              const uint32_t e = sg.us[(size_t)g * np + li];
-              v = f16f(e & 0xFFFFu) * tv[(size_t)(pb + ai) * rs + sg.lo + li];
-            }
-            tp[u] = v;
-            mx = fmaxf(mx, fabsf(v));
+          for (int e = 0; e < 16; ++e) {
+            const int m = 64 * run + mA + 2 * e;
+            const bool ok = tok_ok && m < lim;
+            const uint32_t w = ok ? usr[m] : 0u;
+            const float t = ok ? tvr[m] : 0.f;
+            tpv[e] = f16f(w & 0xFFFFu) * t;
+            zz[e] = w >> 16;
+            mx = fmaxf(mx, fabsf(tpv[e]));
           }
-          mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-          mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));   // partner lane group holds the other parity
           const int sb = block_scale_byte(mx);
+          if (run == 0) sbA = sb; else sbB = sb;
           const float inv = pow2f(127 - sb), fwd = pow2f(sb - 127);
+          uint32_t wd[3][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const float v = tp[u] * inv;
-            const uint32_t h0 = fp8_of(v);
-            const float r1 = (v - fp8_val(h0)) * 32.f;
+          for (int e = 0; e < 16; ++e) {
+            const float x0 = tpv[e] * inv;
+            const uint32_t h0 = fp8_of(x0);
+            const float r1 = (x0 - fp8_val(h0)) * 32.f;
             const uint32_t h1 = fp8_of(r1);
             const float r2 = (r1 - fp8_val(h1)) * 32.f;
             const uint32_t h2 = fp8_of(r2);
             const float back = (fp8_val(h0) + (fp8_val(h1) + fp8_val(h2) * (1.f / 32.f)) * (1.f / 32.f)) * fwd;
-            const int li = c * 128 + m0 + u;
-            if (li < sg.n && ai < nt) {
-              const uint32_t e = sg.us[(size_t)g * np + li];
-              czp += f16f(e >> 16) * back;
-            }
-            int ag, ae;
-            a_pos(m0 + u, ag, ae);
-            S.frag[0][ag][ai][ae] = (uint8_t)h0;
-            S.frag[1][ag][ai][ae] = (uint8_t)h1;
-            S.frag[2][ag][ai][ae] = (uint8_t)h2;
+            czp += f16f(zz[e]) * back;   // zero for missing ranks and empty token rows
+            wd[0][e >> 2] |= h0 << (8 * (e & 3));
+            wd[1][e >> 2] |= h1 << (8 * (e & 3));
+            wd[2][e >> 2] |= h2 << (8 * (e & 3));
           }
-          if (part == 0) S.sc[ai][kb4] = (uint8_t)sb;
+#pragma unroll
+          for (int pc = 0; pc < 3; ++pc)
+            pk[pc][run] = make_int4((int)wd[pc][0], (int)wd[pc][1], (int)wd[pc][2], (int)wd[pc][3]);
         }
-        __syncthreads();
-        // A operand: token row col, lane group q
-        const int4* f0 = reinterpret_cast<const int4*>(&S.frag[0][q][col][0]);
-        const int4* f1 = reinterpret_cast<const int4*>(&S.frag[1][q][col][0]);
-        const int4* f2 = reinterpret_cast<const int4*>(&S.frag[2][q][col][0]);
+      }
+      __syncthreads();   // LDS reuse across token tiles
+#pragma unroll
+      for (int pc = 0; pc < 3; ++pc) {
+        S.frag[wave][pc][gq][pi][0] = pk[pc][0];
+        S.frag[wave][pc][gq][pi][1] = pk[pc][1];
+      }
+      if ((gq & 1) == 0) {
+        S.sc[wave][pi][gq >> 1] = (uint8_t)sbA;
+        S.sc[wave][pi][2 + (gq >> 1)] = (uint8_t)sbB;
+      }
+      S.cz[pi][wave * 4 + gq] = czp;
+    }
+    __syncthreads();
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int cb = 0; cb < kUPass; ++cb) {
+      const int ci = su * kUPass + cb;
+      if (ci < nc) {
+        const bool three = ci < nc3;
+        const int4* f0 = S.frag[cb][0][q][col];
+        const int4* f1 = S.frag[cb][1][q][col];
+        const int4* f2 = S.frag[cb][2][q][col];
         const v8i a0 = {f0[0].x, f0[0].y, f0[0].z, f0[0].w, f0[1].x, f0[1].y, f0[1].z, f0[1].w};
         const v8i a1 = {f1[0].x, f1[0].y, f1[0].z, f1[0].w, f1[1].x, f1[1].y, f1[1].z, f1[1].w};
         const v8i a2 = {f2[0].x, f2[0].y, f2[0].z, f2[0].w, f2[1].x, f2[1].y, f2[1].z, f2[1].w};
-        const int s0 = S.sc[col][q];
-        const int kb = 4 * c + q;
-        const uint32_t* ucw = reinterpret_cast<const uint32_t*>(sg.uc);
+        const int s0 = S.sc[cb][col][q];
+        const int bsc = three ? kScaleFp6Code : kScaleFp4Code;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int o = g * kGroup + wave * 32 + h * 16 + col;   // output row of this lane's B column
-          v8i bop = {0, 0, 0, 0, 0, 0, 0, 0};
-          if (kb < kbn) {
-            int nw;
-            const uint32_t* wp = ucw + u_kblock_word(o, kb, sg.n, sg.b, &nw);
-            uint32_t w[3] = {0u, 0u, 0u};
-            for (int i = 0; i < nw; ++i) w[i] = wp[i];
-            bop = sg.b == 2 ? b_fp4(w[0], w[1]) : b_fp6(w[0], w[1], w[2]);
-          }
+          const v8i bop = three ? b_fp6(cw[cb][h][0], cw[cb][h][1], cw[cb][h][2]) : b_fp4(cw[cb][h][0], cw[cb][h][1]);
+          const int fmt = three ? kFmtFp6 : kFmtFp4;
+          const int s1 = s0 - 5, s2 = s0 - 10;
           f32x4 d = {0.f, 0.f, 0.f, 0.f};
           d = mma(a0, bop, d, s0, fmt, bsc);
-          d = mma(a1, bop, d, s0 - 5, fmt, bsc);
-          d = mma(a2, bop, d, s0 - 10, fmt, bsc);
+          d = mma(a1, bop, d, s1, fmt, bsc);
+          d = mma(a2, bop, d, s2, fmt, bsc);
+          hold(d, a0, a1, a2, bop, s0, s1, s2, bsc);
           acc[h] += d;
         }
       }
     }
-    // sum_i z t' per token row: reduce the 16 thread slots of each row
-    __syncthreads();
-    S.cz[ai][tid & 15] = czp;
-    __syncthreads();
-    // 8-bit pairs on the vector ALU, then the epilogue.  Lane: column o, token rows 4q+r.
-    const Seg s8 = seg_of(tn, L, 0);
-    const int np8 = (int)round_up(s8.n, 4);
+    // partial of this slice: acc - sum_i z t'
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int o = g * kGroup + wave * 32 + h * 16 + col;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * q + r;
-        if (row >= nt) continue;
-        float v = acc[h][r];
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * q + r;
+      if (row < nt) {
         float cz = 0.f;
+#pragma unroll
         for (int u = 0; u < 16; ++u) cz += S.cz[row][u];
-        v -= cz;
-        for (int i = 0; i < s8.n; ++i) {
-          const uint32_t e = s8.us[(size_t)g * np8 + i];
-          const float uh = (float)(_Float16)(f16f(e & 0xFFFFu) * ((float)s8.uc[(size_t)o * s8.n + i] - f16f(e >> 16)));
-          v += uh * tv[(size_t)(pb + row) * rs + i];
-        }
-        const int t = perm[pb + row];
-        if (ybase) v += ybase[(size_t)t * out + o];
-        y[(size_t)t * out + o] = to_bf16(v);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) st_dev(part + (size_t)(pb + row) * out + orow[h], acc[h][r] - cz);
       }
     }
-    __syncthreads();   // S.cz is rewritten by the next token tile
+  }
+  // last arriving slice: add the slices in order, the 8-bit pairs and W x
+  if (!arrive_last(&cnt[(size_t)n * vbmax + (size_t)k * go + g], nsu, &S.last)) return;
+  const Seg s8 = seg_of(tn, L, 0);
+  const int np8 = (int)round_up(s8.n, 4);
+  const int ol = tid & 127, o = g * kGroup + ol;
+  float u8[8];
+  const int n8c = min(s8.n, 8);
+  for (int i = 0; i < n8c; ++i) {
+    const uint32_t e = s8.us[(size_t)g * np8 + i];
+    u8[i] = (float)(_Float16)(f16f(e & 0xFFFFu) * ((float)s8.uc[(size_t)o * s8.n + i] - f16f(e >> 16)));
+  }
+  for (int p = p0 + (tid >> 7); p < p1; p += 2) {
+    float v = 0.f;
+    for (int j = 0; j < nsu; ++j) v += ld_dev(upart + ((size_t)j * T + p) * out + o);
+    for (int i = 0; i < s8.n; ++i) {
+      float uh;
+      if (i < n8c) uh = u8[i];
+      else {
+        const uint32_t e = s8.us[(size_t)g * np8 + i];
+        uh = (float)(_Float16)(f16f(e & 0xFFFFu) * ((float)s8.uc[(size_t)o * s8.n + i] - f16f(e >> 16)));
+      }
+      v += uh * tv[(size_t)p * rs + i];
+    }
+    const int t = perm[p];
+    if (ybase) v += ybase[(size_t)t * out + o];
+    y[(size_t)t * out + o] = to_bf16(v);
   }
 }
 
@@ -557,6 +761,11 @@ int launch_apply(const ApplyArgs& a) {
   int32_t* perm = reinterpret_cast<int32_t*>(a.ws + a.wl.perm);
   float* tv = reinterpret_cast<float*>(a.ws + a.wl.tv);
   float* ybase = a.W ? reinterpret_cast<float*>(a.ws + a.wl.ybase) : nullptr;
+  float* vpart = reinterpret_cast<float*>(a.ws + a.wl.vpart);
+  float* upart = reinterpret_cast<float*>(a.ws + a.wl.upart);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(a.ws + a.wl.cnt);
+  const int go = a.out / kGroup;
+  const int ncnt = a.n * (a.wl.vb + go);
   const size_t items = (size_t)a.T * (a.in / kGroup);
   uint8_t* xf = a.ws + a.wl.xf;
   uint32_t* xsc = reinterpret_cast<uint32_t*>(a.ws + a.wl.xsc);
@@ -570,23 +779,17 @@ int launch_apply(const ApplyArgs& a) {
   mark(DC_STAGE_ROUTE);
   mark(DC_STAGE_XPREP);
   hipLaunchKernelGGL(k_prep, dim3((unsigned)(1 + (items + 3) / 4)), dim3(256), 0, st, a.x, a.ids, a.T, a.in, a.n,
-                     a.mode, seg, offs, perm, flags, xf, xsc, xsum);
+                     a.mode, seg, offs, perm, flags, xf, xsc, xsum, cnt, ncnt);
   mark(DC_STAGE_BASE);
   if (a.W) launch_base(a.W, a.x, ybase, a.out, a.in, a.T, a.stream);
   mark(DC_STAGE_VSIDE);
-  int tasks = 0;
-  for (int k = 0; k < a.n; ++k) {
-    const Tenant& t = a.tenants->t[k];
-    const int k3 = ((t.n3 + 15) / 16 + 3) / 4, k2 = ((t.n2 + 15) / 16 + 3) / 4;
-    const int nt = (t.n8 > 0 ? 1 : 0) + k3 + k2;
-    tasks = nt > tasks ? nt : tasks;
-  }
-  if (tasks > 0)
-    hipLaunchKernelGGL(k_vside, dim3((unsigned)tasks, (unsigned)a.n), dim3(256), 0, st, *a.tenants, a.out, a.in, a.x,
-                       offs, perm, xf, xsc, xsum, tv, a.wl.rs);
+  if (a.wl.vb > 0)
+    hipLaunchKernelGGL(k_vside, dim3((unsigned)(a.wl.vb * v_slices(a.in)), (unsigned)a.n), dim3(256), 0, st,
+                       *a.tenants, a.out, a.in, a.x, offs, perm, xf, xsc, xsum, vpart, tv, a.wl.rs, a.T, cnt,
+                       a.wl.vb);
   mark(DC_STAGE_USIDE);
-  hipLaunchKernelGGL(k_uside, dim3((unsigned)(a.out / kGroup), (unsigned)(a.n + 1)), dim3(256), 0, st, *a.tenants,
-                     a.n, a.out, a.in, offs, perm, tv, a.wl.rs, ybase, a.y);
+  hipLaunchKernelGGL(k_uside, dim3((unsigned)go, (unsigned)(a.n + 1), (unsigned)a.wl.us), dim3(256), 0, st,
+                     *a.tenants, a.n, a.out, a.in, offs, perm, tv, a.wl.rs, ybase, upart, a.T, cnt, a.wl.vb, a.y);
   mark(DC_STAGE_COUNT);
   return (int)hipGetLastError();
 }
