@@ -92,6 +92,7 @@ constexpr int kVSlice = 16;   // 128-groups of the input per V-side work item
 constexpr int kVRows = 8;     // token rows per V-side pass
 constexpr int kUPass = 4;     // 128-rank chunks per U-side work item
 
+
 DC_HD inline int v_slices(int in) { return (in / kGroup + kVSlice - 1) / kVSlice; }
 // V-side rank blocks of a tenant: [8-bit rows if any] [3-bit 64-rank blocks] [2-bit 64-rank blocks]
 DC_HD inline int v_blocks(int n8, int n3, int n2) { return (n8 > 0 ? 1 : 0) + (n3 + 63) / 64 + (n2 + 63) / 64; }
@@ -109,6 +110,7 @@ struct WsLayout {
   size_t xf;      // uint8 [T][in/128][256] fp8 hi/lo fragments of x (matrix-core A operand)
   size_t xsc;     // uint32 [T][in/128] E8M0 block scales of the hi fragments
   size_t xsum;    // fp32 [T][in/128] sums of x over each 128-group
+  size_t xt;      // bf16 x in matrix-core B tiles: [in/32][ceil(T/16)][64 lanes][8]
   size_t tv;      // fp32 [T][rs] V-side results t = sigma * (V x), sorted order
   size_t ybase;   // fp32 [T][out] backbone product, original order
   size_t vpart;   // fp32 [v_slices][T][rs] V-side partial sums per input slice
@@ -136,6 +138,7 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rmax, int32_t 
   W->xf = take(256 * items);
   W->xsc = take(4 * items);
   W->xsum = take(4 * items);
+  W->xt = take(with_base ? 2 * (size_t)in * round_up((size_t)T, 16) : 0);
   W->tv = take(4 * (size_t)T * W->rs);
   W->ybase = take(with_base ? 4 * (size_t)T * out : 0);
   W->vpart = take(4 * (size_t)v_slices(in) * T * W->rs);
@@ -168,6 +171,6 @@ struct ApplyArgs {
   void* const* events;         // optional DC_STAGE_COUNT + 1 hipEvent_t, may be null
 };
 int launch_apply(const ApplyArgs& a);
-int launch_base(const uint16_t* W, const uint16_t* x, float* ybase, int out, int in, int T, void* stream);
+int launch_base(const uint16_t* W, const uint16_t* xt, float* ybase, int out, int in, int T, void* stream);
 int launch_dequant(const Tenant& t, int32_t out, int32_t in, uint16_t* u16, uint16_t* v16, void* stream);
 }  // namespace dc

@@ -177,7 +177,7 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
                                               int32_t* __restrict__ offs, int32_t* __restrict__ perm,
                                               uint32_t* __restrict__ flags, uint8_t* __restrict__ xf,
                                               uint32_t* __restrict__ xsc, float* __restrict__ xsum,
-                                              uint32_t* __restrict__ cnt, int32_t ncnt) {
+                                              uint16_t* __restrict__ xt, uint32_t* __restrict__ cnt, int32_t ncnt) {
   const int tid = threadIdx.x;
   if (blockIdx.x == 0) {
     for (int i = tid; i < ncnt; i += blockDim.x) cnt[i] = 0u;
@@ -233,8 +233,18 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
   const int lane = tid & 63;
   const int t = (int)(item / gi_n), gi = (int)(item % gi_n);
   const uint16_t* xr = x + (size_t)t * in + (size_t)gi * kGroup;
-  const float v0 = __uint_as_float((uint32_t)xr[lane] << 16);          // element j = lane (chunk lane/32)
-  const float v1 = __uint_as_float((uint32_t)xr[lane + 64] << 16);     // element j = lane + 64 (chunk 2 + lane/32)
+  const uint16_t x0 = xr[lane], x1 = xr[lane + 64];
+  const float v0 = __uint_as_float((uint32_t)x0 << 16);   // element j = lane (chunk lane/32)
+  const float v1 = __uint_as_float((uint32_t)x1 << 16);   // element j = lane + 64 (chunk 2 + lane/32)
+  if (xt) {  // bf16 B tiles of the backbone product: k = 128 gi + j -> step k/32, lane group (k%32)/8
+    const int tiles = (T + 15) / 16, tl = t & 15, tt = t >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = gi * kGroup + lane + 64 * h;
+      const int l = 16 * ((k & 31) >> 3) + tl;
+      xt[(((size_t)(k >> 5) * tiles + tt) * 64 + l) * 8 + (k & 7)] = h ? x1 : x0;
+    }
+  }
   float m0 = fabsf(v0), m1 = fabsf(v1);
 #pragma unroll
   for (int s = 16; s >= 1; s >>= 1) {
@@ -770,6 +780,7 @@ int launch_apply(const ApplyArgs& a) {
   uint8_t* xf = a.ws + a.wl.xf;
   uint32_t* xsc = reinterpret_cast<uint32_t*>(a.ws + a.wl.xsc);
   float* xsum = reinterpret_cast<float*>(a.ws + a.wl.xsum);
+  uint16_t* xt = a.W ? reinterpret_cast<uint16_t*>(a.ws + a.wl.xt) : nullptr;
   SegArg seg{};
   if (a.mode == 2)
     for (int k = 0; k <= a.n; ++k) seg.v[k] = a.seg[k];
@@ -779,9 +790,9 @@ int launch_apply(const ApplyArgs& a) {
   mark(DC_STAGE_ROUTE);
   mark(DC_STAGE_XPREP);
   hipLaunchKernelGGL(k_prep, dim3((unsigned)(1 + (items + 3) / 4)), dim3(256), 0, st, a.x, a.ids, a.T, a.in, a.n,
-                     a.mode, seg, offs, perm, flags, xf, xsc, xsum, cnt, ncnt);
+                     a.mode, seg, offs, perm, flags, xf, xsc, xsum, xt, cnt, ncnt);
   mark(DC_STAGE_BASE);
-  if (a.W) launch_base(a.W, a.x, ybase, a.out, a.in, a.T, a.stream);
+  if (a.W) launch_base(a.W, xt, ybase, a.out, a.in, a.T, a.stream);
   mark(DC_STAGE_VSIDE);
   if (a.wl.vb > 0)
     hipLaunchKernelGGL(k_vside, dim3((unsigned)(a.wl.vb * v_slices(a.in)), (unsigned)a.n), dim3(256), 0, st,

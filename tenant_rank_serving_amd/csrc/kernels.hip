@@ -68,30 +68,90 @@ __device__ __forceinline__ uint32_t unit_code(const uint32_t* w, int k) {
 }
 
 // ----------------------------------------------------------- backbone GEMM
-// ybase[t][o] = sum_j W[o][j] x[t][j] in fp32 with v_mfma_f32_16x16x32_bf16:
-// each wave computes 16 rows x 16 tokens.
-__global__ void __launch_bounds__(256) k_base(const uint16_t* __restrict__ W, const uint16_t* __restrict__ x,
-                                              float* __restrict__ ybase, int32_t out, int32_t in, int32_t T) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int o0 = (blockIdx.x * 4 + wave) * 16;
-  const int t0 = blockIdx.y * 16;
-  if (o0 >= out) return;
-  const int row = o0 + (lane & 15);
-  const int kq = (lane >> 4) * 8;
-  const int tok = t0 + (lane & 15);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const uint16_t* wp = W + (size_t)row * in + kq;
-  const uint16_t* xp = x + (size_t)(tok < T ? tok : 0) * in + kq;
-  for (int k0 = 0; k0 < in; k0 += 32) {
-    const uint4 a = *reinterpret_cast<const uint4*>(wp + k0);
-    uint4 b = *reinterpret_cast<const uint4*>(xp + k0);
-    if (tok >= T) b = make_uint4(0, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                  acc, 0, 0, 0);
-  }
-  if (tok < T) {
+// ybase[t][o] = sum_j W[o][j] x[t][j] in fp32 with v_mfma_f32_16x16x32_bf16.
+// Work item (block): 16 whole rows of W (one contiguous stretch of memory)
+// and NT tiles of 16 tokens (blockIdx.y selects the group of 64 tokens).
+// Each wave takes a quarter of the input columns for all 16 rows and all
+// tokens, so every element of W is read once per 64 tokens.  W loads run
+// kWDepth K-steps ahead of the matrix cores, x loads (1 KB B tiles written by
+// the prep kernel) kXDepth steps ahead.  The step loop has no branches, so
+// each step waits only for its own loads.  The four waves add their sums
+// through LDS.
+constexpr int kWDepth = 8;
+constexpr int kXDepth = 4;
+
+template <int NT>
+__global__ void __launch_bounds__(256) k_base(const uint16_t* __restrict__ W, const uint16_t* __restrict__ xt,
+                                              float* __restrict__ ybase, int32_t out, int32_t in, int32_t T,
+                                              int32_t tg0) {
+  __shared__ float red[4][16][65];   // [wave][row][token], padded
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r0 = blockIdx.x * 16;
+  const int t0 = (tg0 + blockIdx.y) * 64;
+  const int tiles = (T + 15) / 16;              // token tiles of x in total
+  const int kspan = in / 4;                     // a multiple of 32: in is a multiple of 128
+  const int kw = wave * kspan;
+  const int nst = kspan / 32;                   // K-steps of this wave
+  const int nsp = (nst + kWDepth - 1) / kWDepth * kWDepth;   // padded with zero steps
+  const uint16_t* wa = W + (size_t)(r0 + (lane & 15)) * in + kw + (lane >> 4) * 8;
+  // B tile (k-step kt, token tile tt) is 1 KB: lane l holds token 16tt + l%16, k = 32kt + 8(l/16) .. +8
+  const uint16_t* xb = xt + ((size_t)(kw / 32) * tiles + t0 / 16) * 512 + lane * 8;
+  uint32_t keep[NT];   // all ones for a lane whose token exists
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ybase[(size_t)tok * out + o0 + (lane >> 4) * 4 + j] = acc[j];
+  for (int j = 0; j < NT; ++j) keep[j] = t0 + 16 * j + (lane & 15) < T ? ~0u : 0u;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 a[kWDepth], b[kXDepth][NT];
+  auto load_a = [&](int slot, int st) {
+    a[slot] = *reinterpret_cast<const uint4*>(wa + (size_t)min(st, nst - 1) * 32);
+  };
+  auto load_b = [&](int slot, int st) {
+    const uint16_t* p = xb + (size_t)min(st, nst - 1) * tiles * 512;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) b[slot][j] = *reinterpret_cast<const uint4*>(p + j * 512);
+  };
+  auto step = [&](int sa, int sb, int st) {
+    const uint32_t live = st < nst ? ~0u : 0u;   // zero for the padding steps
+    uint4 av = a[sa];
+    av.x &= live; av.y &= live; av.z &= live; av.w &= live;
+    const bf16x8 ab = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      uint4 bv = b[sb][j];
+      bv.x &= keep[j]; bv.y &= keep[j]; bv.z &= keep[j]; bv.w &= keep[j];
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, __builtin_bit_cast(bf16x8, bv), acc[j], 0, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < kWDepth; ++d) load_a(d, d);
+#pragma unroll
+  for (int d = 0; d < kXDepth; ++d) load_b(d, d);
+  int s0 = 0;
+  for (; s0 < nsp - kWDepth; s0 += kWDepth) {
+#pragma unroll
+    for (int d = 0; d < kWDepth; ++d) {
+      step(d, d % kXDepth, s0 + d);
+      load_a(d, s0 + d + kWDepth);
+      load_b(d % kXDepth, s0 + d + kXDepth);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < kWDepth; ++d) {   // last kWDepth steps: no W loads left
+    step(d, d % kXDepth, s0 + d);
+    if (d + kXDepth < kWDepth) load_b(d % kXDepth, s0 + d + kXDepth);
+  }
+  // D layout: lane holds token column lane%16 of tile j and rows 4(lane/16)+i
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][16 * j + (lane & 15)] = acc[j][i];
+  __syncthreads();
+  const int ntok = min(64, T - t0);
+  for (int c = tid; c < 16 * 64; c += 256) {
+    const int row = c & 15, tl = c >> 4;   // consecutive threads: consecutive rows of one token
+    if (tl < ntok)
+      ybase[(size_t)(t0 + tl) * out + r0 + row] = (red[0][row][tl] + red[1][row][tl]) + (red[2][row][tl] + red[3][row][tl]);
   }
 }
 
@@ -138,9 +198,19 @@ __global__ void __launch_bounds__(256) k_dequant(Tenant tn, int32_t out, int32_t
 
 }  // namespace
 
-int launch_base(const uint16_t* W, const uint16_t* x, float* ybase, int out, int in, int T, void* stream) {
-  hipLaunchKernelGGL(k_base, dim3((unsigned)((out / 16 + 3) / 4), (unsigned)((T + 15) / 16)), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), W, x, ybase, out, in, T);
+int launch_base(const uint16_t* W, const uint16_t* xt, float* ybase, int out, int in, int T, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // full groups of 64 tokens, then the tail group with its own tile count
+  const int full = T / 64, tail = (T % 64 + 15) / 16;
+  const dim3 gf((unsigned)(out / 16), (unsigned)full), gt((unsigned)(out / 16), 1u);
+  if (full > 0) hipLaunchKernelGGL(k_base<4>, gf, dim3(256), 0, st, W, xt, ybase, out, in, T, 0);
+  switch (tail) {
+    case 1: hipLaunchKernelGGL(k_base<1>, gt, dim3(256), 0, st, W, xt, ybase, out, in, T, full); break;
+    case 2: hipLaunchKernelGGL(k_base<2>, gt, dim3(256), 0, st, W, xt, ybase, out, in, T, full); break;
+    case 3: hipLaunchKernelGGL(k_base<3>, gt, dim3(256), 0, st, W, xt, ybase, out, in, T, full); break;
+    case 4: hipLaunchKernelGGL(k_base<4>, gt, dim3(256), 0, st, W, xt, ybase, out, in, T, full); break;
+    default: break;
+  }
   return (int)hipGetLastError();
 }
 
