@@ -16,7 +16,7 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 // Checks the tenant specs of one call; fills the shape and the work-split maxima.
 struct Dims {
-  int32_t out, in, rmax, vb, us;
+  int32_t out, in, rmax, tw, vb;
 };
 
 dc_status check_specs(const dc_spec* specs, int32_t n, Dims* d) {
@@ -24,8 +24,7 @@ dc_status check_specs(const dc_spec* specs, int32_t n, Dims* d) {
   if (n > DC_MAX_TENANTS) return DC_ERR_UNSUPPORTED;
   d->out = specs[0].out;
   d->in = specs[0].in;
-  d->rmax = d->vb = 0;
-  d->us = 1;
+  d->rmax = d->tw = d->vb = 0;
   for (int k = 0; k < n; ++k) {
     if (dc_check_spec(&specs[k]) != DC_OK) return DC_ERR_SHAPE;
     if (specs[k].out != d->out || specs[k].in != d->in) return DC_ERR_SHAPE;
@@ -33,8 +32,8 @@ dc_status check_specs(const dc_spec* specs, int32_t n, Dims* d) {
     if (r > d->rmax) d->rmax = r;
     const int32_t vb = dc::v_blocks(specs[k].n8, specs[k].n3, specs[k].n2);
     if (vb > d->vb) d->vb = vb;
-    const int32_t us = dc::u_slices(specs[k].n3, specs[k].n2);
-    if (us > d->us) d->us = us;
+    const int32_t tw = dc::t_width(specs[k].n8, specs[k].n3, specs[k].n2);
+    if (tw > d->tw) d->tw = tw;
   }
   return DC_OK;
 }
@@ -69,7 +68,7 @@ dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const ui
     return DC_ERR_ALIGN;
   if (overlap(x, (size_t)T * in * 2, y, (size_t)T * out * 2)) return DC_ERR_INVALID_ARG;
   dc::WsLayout wl{};
-  dc::ws_layout(T, in, out, rmax, n, true, dm.vb, dm.us, &wl);
+  dc::ws_layout(T, in, out, dm.tw, n, true, dm.vb, &wl);
   if (ws_bytes < wl.total) return DC_ERR_BUFFER;
   if (T == 0) return DC_OK;
   dc::ApplyArgs a;
@@ -102,7 +101,7 @@ size_t dc_workspace_bytes(int32_t op, const dc_spec* specs, int32_t n, int32_t T
   Dims dm;
   if (check_specs(specs, n, &dm) != DC_OK) return 0;
   dc::WsLayout wl{};
-  dc::ws_layout(T, dm.in, dm.out, dm.rmax, n, true, dm.vb, dm.us, &wl);
+  dc::ws_layout(T, dm.in, dm.out, dm.tw, n, true, dm.vb, &wl);
   return wl.total;
 }
 

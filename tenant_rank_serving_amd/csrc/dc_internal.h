@@ -86,23 +86,20 @@ struct TenantTable {
   Tenant t[DC_MAX_TENANTS];
 };
 
-// Workspace layout of one apply call.
 // Work decomposition of the matrix-core path (shared by host sizing and kernels).
 constexpr int kVSlice = 16;   // 128-groups of the input per V-side work item
 constexpr int kVRows = 8;     // token rows per V-side pass
-constexpr int kUPass = 4;     // 128-rank chunks per U-side work item
-
 
 DC_HD inline int v_slices(int in) { return (in / kGroup + kVSlice - 1) / kVSlice; }
 // V-side rank blocks of a tenant: [8-bit rows if any] [3-bit 64-rank blocks] [2-bit 64-rank blocks]
 DC_HD inline int v_blocks(int n8, int n3, int n2) { return (n8 > 0 ? 1 : 0) + (n3 + 63) / 64 + (n2 + 63) / 64; }
-// U-side rank slices of a tenant (at least one: it applies the 8-bit pairs and the backbone)
-DC_HD inline int u_slices(int n3, int n2) {
-  const int nc = (n3 + 127) / 128 + (n2 + 127) / 128;
-  const int s = (nc + kUPass - 1) / kUPass;
-  return s > 0 ? s : 1;
+// Rank positions of the V-side results: each bit-width segment starts on a multiple of 8.
+DC_HD inline int t_base(int n8, int n3, int which) {
+  return which == 0 ? 0 : (which == 1 ? (int)round_up((size_t)n8, 8) : (int)(round_up((size_t)n8, 8) + round_up((size_t)n3, 8)));
 }
+DC_HD inline int t_width(int n8, int n3, int n2) { return t_base(n8, n3, 2) + (int)round_up((size_t)n2, 8); }
 
+// Workspace layout of one apply call.
 struct WsLayout {
   size_t flags;   // uint32 status word (+ padding to 256 B)
   size_t offs;    // int32 [n+2] bucket starts in sorted order (bucket n = backbone only)
@@ -111,26 +108,21 @@ struct WsLayout {
   size_t xsc;     // uint32 [T][in/128] E8M0 block scales of the hi fragments
   size_t xsum;    // fp32 [T][in/128] sums of x over each 128-group
   size_t xt;      // bf16 x in matrix-core B tiles: [in/32][ceil(T/16)][64 lanes][8]
-  size_t tv;      // fp32 [T][rs] V-side results t = sigma * (V x), sorted order
   size_t ybase;   // fp32 [T][out] backbone product, original order
-  size_t vpart;   // fp32 [v_slices][T][rs] V-side partial sums per input slice
-  size_t upart;   // fp32 [u_slices][T][out] U-side partial sums per rank slice
-  size_t cnt;     // uint32 [n][vb + Go] arrival counters (zeroed by every call)
+  size_t vpart;   // fp32 [T][rs] t = sigma * (V x), sorted order (accumulated over input slices)
   size_t total;
-  int32_t rs;     // row stride of tv (max r over tenants, rounded up to 4)
+  int32_t rs;     // row stride of vpart (max t_width over tenants)
   int32_t vb;     // max V-side rank blocks per tenant
-  int32_t us;     // max U-side rank slices per tenant
 };
 
-// vbmax/usmax: max over tenants of v_blocks and u_slices.
-inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rmax, int32_t n, bool with_base,
-                      int32_t vbmax, int32_t usmax, WsLayout* W) {
+// rs: max t_width over tenants; vbmax: max v_blocks over tenants.
+inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rs, int32_t n, bool with_base, int32_t vbmax,
+                      WsLayout* W) {
   if (T < 0 || n < 0) return false;
   W->vb = vbmax;
-  W->us = usmax;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = round_up(o, kAlign); o = at + bytes; return at; };
-  W->rs = (int32_t)round_up((size_t)(rmax > 0 ? rmax : 1), 4);
+  W->rs = rs > 0 ? rs : 8;
   W->flags = take(256);
   W->offs = take(4 * ((size_t)n + 2));
   W->perm = take(4 * (size_t)T);
@@ -139,11 +131,8 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rmax, int32_t 
   W->xsc = take(4 * items);
   W->xsum = take(4 * items);
   W->xt = take(with_base ? 2 * (size_t)in * round_up((size_t)T, 16) : 0);
-  W->tv = take(4 * (size_t)T * W->rs);
   W->ybase = take(with_base ? 4 * (size_t)T * out : 0);
-  W->vpart = take(4 * (size_t)v_slices(in) * T * W->rs);
-  W->upart = take(4 * (size_t)usmax * T * out);
-  W->cnt = take(4 * (size_t)n * (vbmax + out / kGroup));
+  W->vpart = take(4 * (size_t)T * W->rs);
   W->total = round_up(o, kAlign);
   return true;
 }

@@ -32,6 +32,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kFmtFp8 = 0, kFmtFp6 = 2, kFmtFp4 = 4;
 constexpr int kScaleFp4Code = 128;   // 2^1: fp4 element q/2 -> q
@@ -106,12 +107,19 @@ __device__ __forceinline__ v8i b_fp6(uint32_t w0, uint32_t w1, uint32_t w2) {
 // may hand an A operand or scale VGPR of an op still in flight to a load
 // issued after it (observed: an LDS load landing in the A and scale VGPRs of
 // the preceding v_mfma_scale changed its result).
+__device__ __forceinline__ void hold(f32x4& d, const v8i& a, const v8i& b, int s0, int sb) {
+  asm volatile("" : "+v"(d) : "v"(a), "v"(b), "v"(s0), "v"(sb));
+}
 __device__ __forceinline__ void hold(f32x4& d, const v8i& a0, const v8i& a1, const v8i& b, int s0, int s1, int sb) {
   asm volatile("" : "+v"(d) : "v"(a0), "v"(a1), "v"(b), "v"(s0), "v"(s1), "v"(sb));
 }
 __device__ __forceinline__ void hold(f32x4& d, const v8i& a0, const v8i& a1, const v8i& a2, const v8i& b, int s0,
                                      int s1, int s2, int sb) {
   asm volatile("" : "+v"(d) : "v"(a0), "v"(a1), "v"(a2), "v"(b), "v"(s0), "v"(s1), "v"(s2), "v"(sb));
+}
+
+__device__ __forceinline__ v8i v8_of(const uint4& a, const uint4& b) {
+  return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
 __device__ __forceinline__ f32x4 mma(const v8i& a, const v8i& b, f32x4 c, int sa, int fmt_b, int sb) {
@@ -145,29 +153,6 @@ struct SegArg {
   int32_t v[DC_MAX_TENANTS + 1];
 };
 
-// ------------------------------------------------------- split-K combine
-// Work items of one output block add their partial sums in a fixed order:
-// each item stores its partials with device-coherent stores, waits until
-// they have completed, then bumps the block's arrival counter; the item that
-// arrives last reads every partial back with device-coherent loads.  Only
-// these accesses bypass the per-XCD L2s; nothing writes back or invalidates a
-// whole L2 (which a device-scope fence would).
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// True in every thread of the item that arrives last of `total`.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, int total, int* flag) {
-  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores are complete
-  __syncthreads();
-  if (threadIdx.x == 0)
-    *flag = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(total - 1);
-  __syncthreads();
-  return *flag != 0;
-}
-
 // ------------------------------------------------------------------- prep
 // Block 0 routes the tokens (stable counting sort by tenant; bucket n holds
 // the backbone-only tokens).  Every other wave turns one (token, 128-group)
@@ -177,10 +162,10 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
                                               int32_t* __restrict__ offs, int32_t* __restrict__ perm,
                                               uint32_t* __restrict__ flags, uint8_t* __restrict__ xf,
                                               uint32_t* __restrict__ xsc, float* __restrict__ xsum,
-                                              uint16_t* __restrict__ xt, uint32_t* __restrict__ cnt, int32_t ncnt) {
+                                              uint16_t* __restrict__ xt, float* __restrict__ tv, int32_t ntv) {
   const int tid = threadIdx.x;
+  for (int i = blockIdx.x * 256 + tid; i < ntv; i += gridDim.x * 256) tv[i] = 0.f;   // t accumulates atomically
   if (blockIdx.x == 0) {
-    for (int i = tid; i < ncnt; i += blockDim.x) cnt[i] = 0u;
     if (mode != 1) {
       for (int p = tid; p < T; p += blockDim.x) perm[p] = p;
       if (tid == 0) {
@@ -190,7 +175,7 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
       }
       return;
     }
-    __shared__ int cnt[DC_MAX_TENANTS + 1];
+    __shared__ int cnt[DC_MAX_TENANTS + 1];   // tokens per bucket
     __shared__ int next[DC_MAX_TENANTS + 1];
     __shared__ int bkt[256];
     __shared__ int bad;
@@ -286,121 +271,169 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
 // Work item (block): tenant k = blockIdx.y; blockIdx.x = rank block rb *
 // v_slices + input slice s.  Rank blocks: the 8-bit rows (vector ALU, fp16
 // dequantized weights), then 64-rank blocks of the 3-bit and of the 2-bit
-// segment (four 16-rank tiles, one per wave, on the matrix cores).  An item
-// covers kVSlice 128-groups of the input; it issues all of its loads up
-// front, writes a partial sum per (token, rank), and the last item of a rank
-// block to arrive adds the slices in slice order and writes t = sigma * sum.
-struct VsideLds {
+// segment (four 16-rank tiles, one per wave, on the matrix cores).  Tokens go
+// in passes of kVRows.  An item issues the loads of all its codes, then
+// stages the x fragments of its slice for the pass into LDS, and runs one
+// matrix-core op per group: A rows 0-7 are the hi pieces and rows 8-15 the lo
+// pieces of the pass's tokens.  sigma * (partial V x) is added into t with
+// float atomics; t is zeroed by the prep kernel.  An input of up to
+// 2 kVSlice groups has at most two slices, whose sum is exact in either
+// order, so t is the same on every run.
+struct VLds {
   int4 frag[kVSlice][kVRows][4][4];   // [group][token row][lane group][hi0 hi1 lo0 lo1]
-  uint32_t sc[kVSlice][kVRows];       // E8M0 words
-  float xs[kVSlice][kVRows];          // group sums
-  int last;
+  uint32_t sc[kVSlice][kVRows];       // E8M0 words of the hi pieces
+  float xs[kVSlice][kVRows];          // group sums of x
+};
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// All code words of one lane for the slice (2 or 3 per group) and the
+// group scale/zero words.
+template <int B>
+struct VCodes {
+  uint32_t w[kVSlice][B];
+  uint32_t z[kVSlice];
 };
 
 template <int B>
-struct CodeW;
-template <>
-struct CodeW<2> { uint32_t w[2]; };
-template <>
-struct CodeW<3> { uint32_t w[3]; };
-
-template <int B>
-__device__ __forceinline__ CodeW<B> load_codes(const uint32_t* row, int gi, int q) {
-  CodeW<B> c;
-  if constexpr (B == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(row + (size_t)gi * 8 + 2 * q);
-    c.w[0] = v.x; c.w[1] = v.y;
-  } else {
-    const uint32_t* wp = row + (size_t)gi * 12 + 3 * q;
+__device__ __forceinline__ void v_load_codes(VCodes<B>& c, const uint32_t* row, const uint32_t* vsp, int np, int g0,
+                                             int gi_n, int q) {
 #pragma unroll
-    for (int i = 0; i < B; ++i) c.w[i] = wp[i];
+  for (int u = 0; u < kVSlice; ++u) {
+    const int gi = min(g0 + u, gi_n - 1);
+    const uint32_t* wp = row + (size_t)gi * 4 * B + B * q;
+    if constexpr (B == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(wp);
+      c.w[u][0] = v.x;
+      c.w[u][1] = v.y;
+    } else {
+      c.w[u][0] = wp[0];
+      c.w[u][1] = wp[1];
+      c.w[u][2] = wp[2];
+    }
+    c.z[u] = vsp[(size_t)gi * np];
   }
-  return c;
 }
 
-template <int B>
-__device__ __forceinline__ v8i b_op(const CodeW<B>& c) {
-  if constexpr (B == 2) return b_fp4(c.w[0], c.w[1]);
-  else return b_fp6(c.w[0], c.w[1], c.w[2]);
-}
-
-// Stage x fragments of token rows [pb, pb + kVRows) and groups [g0, g0+kVSlice)
-// into LDS: thread tid moves int4 (tid & 3) of lane group (tid>>2)&3 of row
-// (tid>>4)&7 for groups (tid>>7) + 2u; threads < 128 also move one
-// (group, row) scale word and sum.
-__device__ __forceinline__ void x_stage(VsideLds& S, const uint8_t* __restrict__ xf, const uint32_t* __restrict__ xsc,
-                                        const float* __restrict__ xsum, const int32_t* __restrict__ perm, int gi_n,
-                                        int g0, int pb, int nt) {
+// Stage the x fragments of token rows [pb, pb + kVRows) for groups
+// [g0, g0 + kVSlice) into LDS.  Thread tid moves int4 (tid & 15) of the
+// fragment of row (tid >> 4) & 7 for groups (tid >> 7) + 2u; threads < 128
+// move one (group, row) scale word and group sum.  Rows past the pass repeat
+// its last token and are never read.
+__device__ __forceinline__ void v_stage_x(VLds& S, const uint8_t* __restrict__ xf, const uint32_t* __restrict__ xsc,
+                                          const float* __restrict__ xsum, const int32_t* __restrict__ perm, int gi_n,
+                                          int g0, int pb, int nt) {
   const int tid = threadIdx.x;
-  const int part = tid & 3, qq = (tid >> 2) & 3, row = (tid >> 4) & 7, gh = tid >> 7;
-  const int tok = row < nt ? perm[pb + row] : -1;
-  int4 v[kVSlice / 2];
+  const int k16 = tid & 15, rw = (tid >> 4) & 7, gh = tid >> 7;
+  const int tok = perm[pb + min(rw, nt - 1)];
+  i32x4 v[kVSlice / 2];
 #pragma unroll
   for (int u = 0; u < kVSlice / 2; ++u) {
-    const int gl = gh + 2 * u, gi = g0 + gl;
-    v[u] = make_int4(0, 0, 0, 0);
-    if (tok >= 0 && gi < gi_n) v[u] = reinterpret_cast<const int4*>(xf + ((size_t)tok * gi_n + gi) * kXFrag + qq * 64)[part];
+    const int gi = min(g0 + gh + 2 * u, gi_n - 1);
+    v[u] = reinterpret_cast<const i32x4*>(xf + ((size_t)tok * gi_n + gi) * kXFrag)[k16];
   }
-  uint32_t scw = 0x7F7F7F7Fu;
-  float xsv = 0.f;
-  const int sr = tid & 7, sg = tid >> 3;   // (row, group) of the scale/sum this thread moves
-  if (tid < kVRows * kVSlice) {
-    const int stok = sr < nt ? perm[pb + sr] : -1;
-    if (stok >= 0 && g0 + sg < gi_n) {
-      scw = xsc[(size_t)stok * gi_n + g0 + sg];
-      xsv = xsum[(size_t)stok * gi_n + g0 + sg];
-    }
-  }
+  const int sr = tid & 7, sgl = (tid >> 3) & (kVSlice - 1);
+  const int stok = perm[pb + min(sr, nt - 1)];
+  const int gs = min(g0 + sgl, gi_n - 1);
+  const uint32_t scw = xsc[(size_t)stok * gi_n + gs];
+  const float xsv = xsum[(size_t)stok * gi_n + gs];
 #pragma unroll
-  for (int u = 0; u < kVSlice / 2; ++u) S.frag[gh + 2 * u][row][qq][part] = v[u];
+  for (int u = 0; u < kVSlice / 2; ++u)
+    S.frag[gh + 2 * u][rw][k16 >> 2][k16 & 3] = make_int4(v[u].x, v[u].y, v[u].z, v[u].w);
   if (tid < kVRows * kVSlice) {
-    S.sc[sg][sr] = scw;
-    S.xs[sg][sr] = xsv;
+    S.sc[sgl][sr] = scw;
+    S.xs[sgl][sr] = xsv;
   }
 }
 
-// 8-bit rows of a tenant over one input slice, all tokens; partial sums
-// (without sigma) to part[p][i].
+// One 16-rank tile over one input slice, all tokens in passes of kVRows.
+template <int B>
+__device__ void vside_tile(const Seg& sg, int tbase, int tile, int in, int s, const int32_t* __restrict__ perm,
+                           int p0, int p1, const uint8_t* __restrict__ xf, const uint32_t* __restrict__ xsc,
+                           const float* __restrict__ xsum, const float* __restrict__ sigma, float* __restrict__ tv,
+                           int rs, VLds& S) {
+  constexpr int fmt = B == 2 ? kFmtFp4 : kFmtFp6;
+  constexpr int bsc = B == 2 ? kScaleFp4Code : kScaleFp6Code;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, q = lane >> 4;
+  const int gi_n = in / kGroup;
+  const int g0 = s * kVSlice;
+  const int gn = min(kVSlice, gi_n - g0);   // groups in this slice
+  const int li = tile * 16 + col;
+  const bool rv = li < sg.n;
+  const int np = (int)round_up(sg.n, 4);
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(sg.vc) + (size_t)(rv ? li : 0) * gi_n * 4 * B;
+  const uint32_t* vsp = sg.vs + (rv ? li : 0);
+  const float sig = rv ? sigma[sg.lo + li] : 0.f;
+  VCodes<B> c;
+  v_load_codes<B>(c, row, vsp, np, g0, gi_n, q);
+  const int tr = col & 7;              // token row of this lane's A operand
+  const int piece = col >> 3;          // 0: hi pieces, 1: lo pieces
+  for (int pb = p0; pb < p1; pb += kVRows) {
+    const int nt = min(kVRows, p1 - pb);
+    __syncthreads();   // LDS reuse across passes
+    v_stage_x(S, xf, xsc, xsum, perm, gi_n, g0, pb, nt);
+    __syncthreads();
+    const bool live = tr < nt;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kVSlice; ++u) {
+      if (u < gn) {
+        const int4* fr = S.frag[u][tr][q] + 2 * piece;
+        const int4 f0 = fr[0], f1 = fr[1];
+        const v8i a = live ? v8i{f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w} : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        const int sa = live ? (int)((S.sc[u][tr] >> (8 * q)) & 0xFFu) - 5 * piece : 127;
+        const v8i bo = B == 2 ? b_fp4(c.w[u][0], c.w[u][1]) : b_fp6(c.w[u][0], c.w[u][1], c.w[u][2]);
+        const int bs = bsc;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        d = mma(a, bo, d, sa, fmt, bs);
+        hold(d, a, bo, sa, bs);
+        // D rows 0-7: hi products of tokens 0-7 (lane groups 0, 1); rows 8-15: lo products
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d[r] += __shfl_xor(d[r], 32, 64);
+        const float sc = f16f(c.z[u] & 0xFFFFu), z = f16f(c.z[u] >> 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += sc * (d[r] - z * S.xs[u][(4 * q + r) & 7]);
+      }
+    }
+    if (rv && q < 2) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * q + r < nt) atomicAdd(tv + (size_t)(pb + 4 * q + r) * rs + tbase + li, sig * acc[r]);
+    }
+  }
+}
+
+// 8-bit rows of a tenant over one input slice, all tokens, on the vector ALU
+// with the fp16 dequantized weights; sigma * partial added into t.
 __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, const uint16_t* __restrict__ x,
-                           const int32_t* __restrict__ perm, int p0, int p1, float* __restrict__ part, int rs) {
-  constexpr int kQ = kVSlice * kGroup / 4 / 256;   // quads per thread per slice (2)
+                           const int32_t* __restrict__ perm, int p0, int p1, float* __restrict__ tv, int rs) {
   __shared__ float red[4][8];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const Seg sg = seg_of(tn, L, 0);
+  const float* sigma = reinterpret_cast<const float*>(tn.base + L.off[DC_REG_SIGMA]);
   const int np = (int)round_up(sg.n, 4);
-  const int q0 = s * kVSlice * kGroup / 4, nq = in / 4;
+  const int q0 = s * kVSlice * kGroup / 4, q1 = min(in / 4, q0 + kVSlice * kGroup / 4);
   for (int i = 0; i < sg.n; ++i) {
     const uint8_t* row = sg.vc + (size_t)i * in;   // 8-bit group bitstreams are plain bytes
-    float w[kQ][4];
-#pragma unroll
-    for (int m = 0; m < kQ; ++m) {
-      const int qd = q0 + tid + 256 * m;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) w[m][u] = 0.f;
-      if (qd < nq) {
-        const uint32_t e = sg.vs[(size_t)(qd * 4 / kGroup) * np + i];
-        const uint32_t c4 = *reinterpret_cast<const uint32_t*>(row + (size_t)qd * 4);
-        const float sc = f16f(e & 0xFFFFu), z = f16f(e >> 16);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) w[m][u] = (float)(_Float16)(sc * ((float)((c4 >> (8 * u)) & 0xFFu) - z));
-      }
-    }
     for (int pc = p0; pc < p1; pc += 8) {
       const int nt = min(8, p1 - pc);
       float acc[8];
 #pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8) {
-        acc[t8] = 0.f;
-        if (t8 < nt) {
-          const uint16_t* xr = x + (size_t)perm[pc + t8] * in;
+      for (int t8 = 0; t8 < 8; ++t8) acc[t8] = 0.f;
+      for (int qd = q0 + tid; qd < q1; qd += 256) {
+        const uint32_t e = sg.vs[(size_t)(qd * 4 / kGroup) * np + i];
+        const uint32_t c4 = *reinterpret_cast<const uint32_t*>(row + (size_t)qd * 4);
+        const float sc = f16f(e & 0xFFFFu), z = f16f(e >> 16);
+        float w[4];
 #pragma unroll
-          for (int m = 0; m < kQ; ++m) {
-            const int qd = q0 + tid + 256 * m;
-            if (qd < nq) {
-              const uint2 xv = *reinterpret_cast<const uint2*>(xr + (size_t)qd * 4);
-              acc[t8] += w[m][0] * __uint_as_float(xv.x << 16) + w[m][1] * __uint_as_float(xv.x & 0xFFFF0000u) +
-                         w[m][2] * __uint_as_float(xv.y << 16) + w[m][3] * __uint_as_float(xv.y & 0xFFFF0000u);
-            }
+        for (int u = 0; u < 4; ++u) w[u] = (float)(_Float16)(sc * ((float)((c4 >> (8 * u)) & 0xFFu) - z));
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) {
+          if (t8 < nt) {
+            const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)perm[pc + t8] * in + (size_t)qd * 4);
+            acc[t8] += w[0] * __uint_as_float(xv.x << 16) + w[1] * __uint_as_float(xv.x & 0xFFFF0000u) +
+                       w[2] * __uint_as_float(xv.y << 16) + w[3] * __uint_as_float(xv.y & 0xFFFF0000u);
           }
         }
       }
@@ -412,75 +445,9 @@ __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, con
         if (lane == 0) red[wave][t8] = v;
       }
       __syncthreads();
-      if (tid < nt) st_dev(part + (size_t)(pc + tid) * rs + i, (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]));
+      if (tid < nt)
+        atomicAdd(tv + (size_t)(pc + tid) * rs + i, sigma[i] * ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid])));
       __syncthreads();
-    }
-  }
-}
-
-// One 16-rank tile per wave over one input slice, all tokens in passes of kVRows.
-template <int B>
-__device__ void vside_tiles(const Seg& sg, int tile, int in, int s, const int32_t* __restrict__ perm, int p0,
-                            int p1, const uint8_t* __restrict__ xf, const uint32_t* __restrict__ xsc,
-                            const float* __restrict__ xsum, float* __restrict__ part, int rs, VsideLds& S) {
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 15, q = lane >> 4;
-  const int gi_n = in / kGroup;
-  const int g0 = s * kVSlice;
-  const int li = tile * 16 + col;
-  const bool rv = li < sg.n;
-  const int np = (int)round_up(sg.n, 4);
-  const uint32_t* row = reinterpret_cast<const uint32_t*>(sg.vc) + (size_t)(rv ? li : 0) * gi_n * 4 * B;
-  const uint32_t* vsp = sg.vs + (rv ? li : 0);
-  const int fmt = B == 2 ? kFmtFp4 : kFmtFp6;
-  const int bsc = B == 2 ? kScaleFp4Code : kScaleFp6Code;
-  // every code and scale/zero word of the slice, issued at once
-  CodeW<B> cw[kVSlice];
-  uint32_t zw[kVSlice];
-#pragma unroll
-  for (int u = 0; u < kVSlice; ++u) {
-    const int gi = g0 + u < gi_n ? g0 + u : gi_n - 1;
-    cw[u] = load_codes<B>(row, gi, q);
-    zw[u] = vsp[(size_t)gi * np];
-  }
-  for (int pb = p0; pb < p1; pb += kVRows) {
-    const int nt = min(kVRows, p1 - pb);
-    __syncthreads();   // LDS reuse across passes
-    x_stage(S, xf, xsc, xsum, perm, gi_n, g0, pb, nt);
-    __syncthreads();
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < kVSlice; ++u) {
-      if (g0 + u < gi_n) {
-        v8i ah = {0, 0, 0, 0, 0, 0, 0, 0}, al = ah;
-        int sh = 127;
-        if (col < kVRows) {
-          const int4* fr = S.frag[u][col][q];
-          const int4 h0 = fr[0], h1 = fr[1], l0 = fr[2], l1 = fr[3];
-          ah = v8i{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-          al = v8i{l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-          sh = (int)((S.sc[u][col] >> (8 * q)) & 0xFFu);
-        }
-        v8i bop = b_op<B>(cw[u]);
-        if (!rv) bop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        const int sl = sh - 5;
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
-        d = mma(ah, bop, d, sh, fmt, bsc);
-        d = mma(al, bop, d, sl, fmt, bsc);
-        hold(d, ah, al, bop, sh, sl, bsc);
-        const float sc = f16f(zw[u] & 0xFFFFu), z = f16f(zw[u] >> 16);
-        if (q < 2) {   // D rows 4q+r < 8 are the staged tokens
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] += sc * (d[r] - z * S.xs[u][4 * q + r]);
-        }
-      }
-    }
-    if (rv && q < 2) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pd = pb + 4 * q + r;
-        if (4 * q + r < nt) st_dev(part + (size_t)pd * rs + sg.lo + li, acc[r]);
-      }
     }
   }
 }
@@ -489,94 +456,74 @@ __global__ void __launch_bounds__(256) k_vside(TenantTable tt, int32_t out, int3
                                                const uint16_t* __restrict__ x, const int32_t* __restrict__ offs,
                                                const int32_t* __restrict__ perm, const uint8_t* __restrict__ xf,
                                                const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
-                                               float* __restrict__ vpart, float* __restrict__ tv, int32_t rs,
-                                               int32_t T, uint32_t* __restrict__ cnt, int32_t vbmax) {
+                                               float* __restrict__ tv, int32_t rs) {
   const int k = blockIdx.y;
   const int p0 = offs[k], p1 = offs[k + 1];
   if (p0 >= p1) return;
   const Tenant tn = tt.t[k];
   const int ns = v_slices(in);
-  const int rb = blockIdx.x / ns, s = blockIdx.x % ns;
-  if (rb >= v_blocks(tn.n8, tn.n3, tn.n2)) return;
+  int b = blockIdx.x / ns;
+  const int s = blockIdx.x % ns;
+  if (b >= v_blocks(tn.n8, tn.n3, tn.n2)) return;
   Layout L;
   layout_of(out, in, tn.n8, tn.n3, tn.n2, &L);
-  __shared__ VsideLds S;
-  const int tid = threadIdx.x, wave = tid >> 6;
-  float* part = vpart + (size_t)s * T * rs;
-  const int b3 = (tn.n3 + 63) / 64;
-  int lo, hi;   // global rank range of the block
-  int b = rb;
-  if (tn.n8 > 0 && b == 0) {
-    vside_8bit(tn, L, in, s, x, perm, p0, p1, part, rs);
-    lo = 0; hi = tn.n8;
-  } else {
-    if (tn.n8 > 0) --b;
-    if (b < b3) {
-      const Seg sg = seg_of(tn, L, 1);
-      vside_tiles<3>(sg, b * 4 + wave, in, s, perm, p0, p1, xf, xsc, xsum, part, rs, S);
-      lo = sg.lo + b * 64; hi = min(sg.lo + sg.n, lo + 64);
-    } else {
-      const Seg sg = seg_of(tn, L, 2);
-      vside_tiles<2>(sg, (b - b3) * 4 + wave, in, s, perm, p0, p1, xf, xsc, xsum, part, rs, S);
-      lo = sg.lo + (b - b3) * 64; hi = min(sg.lo + sg.n, lo + 64);
-    }
+  if (tn.n8 > 0) {
+    if (b == 0) { vside_8bit(tn, L, in, s, x, perm, p0, p1, tv, rs); return; }
+    --b;
   }
-  // last arriving slice of this rank block adds the slices in order
-  if (!arrive_last(&cnt[(size_t)k * vbmax + rb], ns, &S.last)) return;
+  __shared__ VLds S;
   const float* sigma = reinterpret_cast<const float*>(tn.base + L.off[DC_REG_SIGMA]);
-  const int nr = hi - lo, cells = (p1 - p0) * nr;
-  for (int c = tid; c < cells; c += 256) {
-    const int p = p0 + c / nr, i = lo + c % nr;
-    float v = 0.f;
-    for (int j = 0; j < ns; ++j) v += ld_dev(vpart + ((size_t)j * T + p) * rs + i);
-    tv[(size_t)p * rs + i] = sigma[i] * v;
-  }
+  const int wave = threadIdx.x >> 6;
+  const int b3 = (tn.n3 + 63) / 64;
+  if (b < b3)
+    vside_tile<3>(seg_of(tn, L, 1), t_base(tn.n8, tn.n3, 1), b * 4 + wave, in, s, perm, p0, p1, xf, xsc, xsum, sigma,
+                  tv, rs, S);
+  else
+    vside_tile<2>(seg_of(tn, L, 2), t_base(tn.n8, tn.n3, 2), (b - b3) * 4 + wave, in, s, perm, p0, p1, xf, xsc, xsum,
+                  sigma, tv, rs, S);
 }
 
 // ------------------------------------------------------------------ U side
-// Work item (block): blockIdx.x = 128-row output group g, blockIdx.y =
-// tenant k (n = the backbone-only bucket), blockIdx.z = rank slice su of
-// kUPass chunks of 128 ranks (3-bit chunks first, then 2-bit).  Wave w builds
-// the A fragments of t'_i = s_ig t_i (three fp8 pieces, E8M0 block scales)
-// for chunk w of the slice: lane (token row i, lane group gq) writes exactly
-// the 32-byte rows an MFMA lane (i, gq) reads.  Then every wave runs its two
-// 16-row output tiles against the slice; its codes were loaded before the
-// A-prep.  The slice's partial sum_i (q_oi - z_ig) t'_i goes to upart; the
-// last slice to arrive adds the slices in order, the 8-bit pairs and W x,
-// rounds once to bf16 and writes y.
-struct UsideLds {
-  int4 frag[kUPass][3][4][16][2];   // [chunk][piece][lane group][token row][32 bytes]
-  uint8_t sc[kUPass][16][4];        // E8M0 of piece 0 per (chunk, token row, K-block)
-  float cz[16][16];                 // partial sum_i z t' per (token row, slot)
-  int last;
+// Work item (block): 128-row output group g = blockIdx.x of tenant
+// k = blockIdx.y (n = the backbone-only bucket), all ranks, tokens in passes
+// of up to kURows.  A pass first stages the scale/zero words of row group g
+// and the pass's rows of t into LDS.  The ranks then go in 128-rank chunks,
+// 3-bit chunks first: the block turns t'_i = s_ig t_i into three fp8 pieces
+// with E8M0 block scales (thread: token row, K-block, 4 ranks; its even and
+// odd bytes land as one 16-bit word each in the A fragments), and wave w runs
+// its two 16-row output tiles (rows 32w..32w+31) on the matrix cores.  The
+// only global loads in the chunk loop are the codes, kept kUDepth-1 chunks
+// ahead in a register ring.  The epilogue takes sum_i z_ig t'_i off, adds
+// the 8-bit pairs and W x and rounds once to bf16.
+constexpr int kURows = 8;    // token rows per pass
+constexpr int kU8Max = 4;    // 8-bit pairs whose U weights a lane keeps in registers
+constexpr int kUDepth = 4;   // register ring of codes, in chunks
+
+struct UCodes {
+  uint32_t w[2][3];   // B operand words of the lane's two output tiles
 };
 
-struct UChunk {
-  int which;   // 1: 3-bit segment, 2: 2-bit segment
-  int c;       // chunk index inside the segment
+// LDS of one block (dynamic): fixed part, then us[rs] and t[rows][rs].
+struct UFixed {
+  uint16_t frag[2][3][4][16][16];   // [slot][piece][lane group][A row][32 bytes]; rows >= the pass's tokens stay 0
+  uint8_t sc[2][16][4];             // E8M0 of piece 0 per (slot, A row, K-block)
+  float cz[kURows];                 // sum_i z t' per token row
 };
 
-__device__ __forceinline__ UChunk chunk_of(int ci, int nc3) {
-  UChunk u;
-  if (ci < nc3) { u.which = 1; u.c = ci; }
-  else { u.which = 2; u.c = ci - nc3; }
-  return u;
+__host__ __device__ inline size_t u_lds_bytes(int rs, int rows) {
+  return round_up(sizeof(UFixed), 16) + 4 * (size_t)rs * (1 + rows);
 }
 
-__global__ void __launch_bounds__(256, 2) k_uside(TenantTable tt, int32_t n, int32_t out, int32_t in,
-                                                  const int32_t* __restrict__ offs, const int32_t* __restrict__ perm,
-                                                  const float* __restrict__ tv, int32_t rs,
-                                                  const float* __restrict__ ybase, float* __restrict__ upart,
-                                                  int32_t T, uint32_t* __restrict__ cnt, int32_t vbmax,
-                                                  uint16_t* __restrict__ y) {
-  const int g = blockIdx.x, k = blockIdx.y, su = blockIdx.z;
+__global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_t out, int32_t in,
+                                               const int32_t* __restrict__ offs, const int32_t* __restrict__ perm,
+                                               const float* __restrict__ tv, int32_t rs, int32_t rows,
+                                               const float* __restrict__ ybase, uint16_t* __restrict__ y) {
+  const int g = blockIdx.x, k = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, q = lane >> 4;
   const int p0 = offs[k], p1 = offs[k + 1];
   if (p0 >= p1) return;
-  const int go = out / kGroup;
   if (k == n) {  // backbone-only tokens
-    if (su != 0) return;
     for (int idx = tid; idx < (p1 - p0) * kGroup; idx += 256) {
       const int t = perm[p0 + idx / kGroup];
       const int o = g * kGroup + idx % kGroup;
@@ -584,181 +531,265 @@ __global__ void __launch_bounds__(256, 2) k_uside(TenantTable tt, int32_t n, int
     }
     return;
   }
+  extern __shared__ __align__(16) uint8_t u_lds[];
+  UFixed& S = *reinterpret_cast<UFixed*>(u_lds);
+  uint32_t* us_s = reinterpret_cast<uint32_t*>(u_lds + round_up(sizeof(UFixed), 16));   // [rs]
+  float* t_s = reinterpret_cast<float*>(us_s + rs);                                        // [rows][rs]
   const Tenant tn = tt.t[k];
-  const int nsu = u_slices(tn.n3, tn.n2);
-  if (su >= nsu) return;
   Layout L;
   layout_of(out, in, tn.n8, tn.n3, tn.n2, &L);
-  __shared__ UsideLds S;
-  const Seg seg3 = seg_of(tn, L, 1), seg2 = seg_of(tn, L, 2);
-  const int kb3 = (seg3.n + kKBlock - 1) / kKBlock, kb2 = (seg2.n + kKBlock - 1) / kKBlock;
-  const int nc3 = (kb3 + 3) / 4, nc = nc3 + (kb2 + 3) / 4;
+  const Seg seg3 = seg_of(tn, L, 1), seg2 = seg_of(tn, L, 2), s8 = seg_of(tn, L, 0);
+  const int tb3 = t_base(tn.n8, tn.n3, 1), tb2 = t_base(tn.n8, tn.n3, 2);
+  const int nc3 = (seg3.n + 127) / 128, nc = nc3 + (seg2.n + 127) / 128;
   const int orow[2] = {g * kGroup + wave * 32 + col, g * kGroup + wave * 32 + 16 + col};
-  // codes of the slice for this wave's two tiles
-  uint32_t cw[kUPass][2][3];
+  // fp16 dequantized 8-bit U weights of this lane's two output rows (first kU8Max pairs)
+  float u8w[2][kU8Max];
+  {
+    const int np8 = (int)round_up(s8.n, 4);
 #pragma unroll
-  for (int cb = 0; cb < kUPass; ++cb) {
+    for (int i = 0; i < kU8Max; ++i) {
+      const int ii = min(i, s8.n > 0 ? s8.n - 1 : 0);
+      const uint32_t e = s8.n > 0 ? s8.us[(size_t)g * np8 + ii] : 0u;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) { cw[cb][h][0] = 0u; cw[cb][h][1] = 0u; cw[cb][h][2] = 0u; }
-    const int ci = su * kUPass + cb;
-    if (ci < nc) {
-      const UChunk u = chunk_of(ci, nc3);
-      const Seg& sg = u.which == 1 ? seg3 : seg2;
-      const int kb = 4 * u.c + q;
-      if (kb < (u.which == 1 ? kb3 : kb2)) {
-        const uint32_t* base = reinterpret_cast<const uint32_t*>(sg.uc);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          int nw;
-          const uint32_t* wp = base + u_kblock_word(orow[h], kb, sg.n, sg.b, &nw);
-          cw[cb][h][0] = wp[0];
-          if (nw > 1) cw[cb][h][1] = wp[1];
-          if (nw > 2) cw[cb][h][2] = wp[2];
-        }
+      for (int h = 0; h < 2; ++h) {
+        const float code = s8.n > 0 ? (float)s8.uc[(size_t)orow[h] * s8.n + ii] : 0.f;
+        u8w[h][i] = (float)(_Float16)(f16f(e & 0xFFFFu) * (code - f16f(e >> 16)));
       }
     }
   }
-  float* part = upart + (size_t)su * T * out;
-  // A-prep role: token row pi = lane % 16, lane group gq = lane / 16; ranks of
-  // run 0 start at mA = 32(gq/2) + (gq&1) (stride 2), run 1 at 64 + mA.
-  const int pi = col, gq = q;
-  const int mA = 32 * (gq >> 1) + (gq & 1);
-  for (int pb = p0; pb < p1; pb += 16) {
-    const int nt = min(16, p1 - pb);
-    float czp = 0.f;
+  // A-prep role: token row ai, K-block kb4 of the chunk, ranks m0..m0+3
+  const int ai = tid >> 5, kb4 = (tid >> 3) & 3, part = tid & 7;
+  const int m0 = kb4 * 32 + part * 4;
+  const int lg_even = 2 * (kb4 & 1), hw = (kb4 >= 2 ? 8 : 0) + part;   // lane group, 16-bit word
+  // word offsets of this lane's K-block words in the U code tiles (same formula
+  // as u_kblock_word, split into per-tile constants and a per-chunk term)
+  struct UAddr {
+    int kbn, cb, tile[2], ro[2], rl[2];
+  };
+  auto uaddr = [&](int sn, int bb) __attribute__((always_inline)) {
+    UAddr a;
+    const int rw = (int)u_row_words(sn, bb);
+    a.kbn = (sn + kKBlock - 1) / kKBlock;
+    a.cb = 16 * bb;
+    const int wl = rw - (a.kbn - 1) * bb;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      a.tile[h] = (orow[h] >> 4) * 16 * rw;
+      a.ro[h] = (orow[h] & 15) * bb;
+      a.rl[h] = (orow[h] & 15) * wl;
+    }
+    return a;
+  };
+  const UAddr ad3 = uaddr(seg3.n, 3), ad2 = uaddr(seg2.n, 2);
+  auto load_codes = [&](UCodes& uc, int c) __attribute__((always_inline)) {
+    c = min(c, nc - 1);
+    const bool three = c < nc3;
+    const int cc = three ? c : c - nc3;
+    const int kbn = three ? ad3.kbn : ad2.kbn;
+    const int kb = min(4 * cc + q, kbn - 1);
+    const bool last = kb == kbn - 1;
+    const uint32_t* ub = reinterpret_cast<const uint32_t*>(three ? seg3.uc : seg2.uc);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tile = three ? ad3.tile[h] : ad2.tile[h];
+      const int ro = last ? (three ? ad3.rl[h] : ad2.rl[h]) : (three ? ad3.ro[h] : ad2.ro[h]);
+      const uint32_t* wp = ub + tile + kb * (three ? ad3.cb : ad2.cb) + ro;
+      uc.w[h][0] = wp[0];
+      uc.w[h][1] = wp[1];
+      uc.w[h][2] = wp[2];
+    }
+  };
+  for (int pb = p0; pb < p1; pb += rows) {
+    const int nt = min(rows, p1 - pb);
+    UCodes cr[kUDepth];
+    if (nc > 0) {
+#pragma unroll
+      for (int d = 0; d < kUDepth - 1; ++d) load_codes(cr[d], d);
+    }
+    // ---- zero the A fragments (rows past the pass's tokens stay 0), stage the
+    // scale/zero words of row group g and the pass's rows of t
     {
-      const int ci = su * kUPass + wave;
-      int4 pk[3][2];
-      int sbA = 127, sbB = 127;
+      uint4* fz = reinterpret_cast<uint4*>(&S);
+      for (int i = tid; i < (int)((sizeof(S.frag) + sizeof(S.sc)) / 16); i += 256) fz[i] = make_uint4(0, 0, 0, 0);
+      const int n83 = tn.n8 + tn.n3, nr = n83 + tn.n2;
+      constexpr int kUs = 8;   // rank words per thread per batch, loads issued together
+      for (int b0 = 0; b0 < nr; b0 += 256 * kUs) {
+        uint32_t w[kUs];
+        int at[kUs];
 #pragma unroll
-      for (int pc = 0; pc < 3; ++pc) { pk[pc][0] = make_int4(0, 0, 0, 0); pk[pc][1] = pk[pc][0]; }
-      if (ci < nc) {
-        const UChunk u = chunk_of(ci, nc3);
-        const Seg& sg = u.which == 1 ? seg3 : seg2;
-        const int np = (int)round_up(sg.n, 4);
-        const bool tok_ok = pi < nt;
-        const float* tvr = tv + (size_t)(pb + (tok_ok ? pi : 0)) * rs + sg.lo + u.c * 128;
-        const uint32_t* usr = sg.us + (size_t)g * np + u.c * 128;
-        const int lim = sg.n - u.c * 128;
+        for (int b = 0; b < kUs; ++b) {
+          const int i = min(b0 + b * 256 + tid, nr - 1);
+          const int which = i < tn.n8 ? 0 : (i < n83 ? 1 : 2);
+          const uint32_t* usb = which == 0 ? s8.us : (which == 1 ? seg3.us : seg2.us);
+          const int sn = which == 0 ? s8.n : (which == 1 ? seg3.n : seg2.n);
+          const int li = i - (which == 0 ? 0 : (which == 1 ? tn.n8 : n83));
+          w[b] = usb[(size_t)g * round_up(sn, 4) + li];
+          at[b] = t_base(tn.n8, tn.n3, which) + li;
+        }
 #pragma unroll
-        for (int run = 0; run < 2; ++run) {
-          float tpv[16];
-          uint32_t zz[16];
-          float mx = 0.f;
+        for (int b = 0; b < kUs; ++b)
+          if (b0 + b * 256 + tid < nr) us_s[at[b]] = w[b];
+      }
+      const int w4 = rs / 4, tot = nt * w4;
+      constexpr int kB = 8;
+      for (int b0 = 0; b0 < tot; b0 += 256 * kB) {
+        float4 v[kB];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int m = 64 * run + mA + 2 * e;
-            const bool ok = tok_ok && m < lim;
-            const uint32_t w = ok ? usr[m] : 0u;
-            const float t = ok ? tvr[m] : 0.f;
-            tpv[e] = f16f(w & 0xFFFFu) * t;
-            zz[e] = w >> 16;
-            mx = fmaxf(mx, fabsf(tpv[e]));
-          }
-          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));   // partner lane group holds the other parity
-          const int sb = block_scale_byte(mx);
-          if (run == 0) sbA = sb; else sbB = sb;
-          const float inv = pow2f(127 - sb), fwd = pow2f(sb - 127);
-          uint32_t wd[3][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+        for (int b = 0; b < kB; ++b) {
+          const int idx = min(b0 + b * 256 + tid, tot - 1);
+          v[b] = reinterpret_cast<const float4*>(tv + (size_t)(pb + idx / w4) * rs)[idx % w4];
+        }
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float x0 = tpv[e] * inv;
-            const uint32_t h0 = fp8_of(x0);
-            const float r1 = (x0 - fp8_val(h0)) * 32.f;
-            const uint32_t h1 = fp8_of(r1);
-            const float r2 = (r1 - fp8_val(h1)) * 32.f;
-            const uint32_t h2 = fp8_of(r2);
-            const float back = (fp8_val(h0) + (fp8_val(h1) + fp8_val(h2) * (1.f / 32.f)) * (1.f / 32.f)) * fwd;
-            czp += f16f(zz[e]) * back;   // zero for missing ranks and empty token rows
-            wd[0][e >> 2] |= h0 << (8 * (e & 3));
-            wd[1][e >> 2] |= h1 << (8 * (e & 3));
-            wd[2][e >> 2] |= h2 << (8 * (e & 3));
-          }
-#pragma unroll
-          for (int pc = 0; pc < 3; ++pc)
-            pk[pc][run] = make_int4((int)wd[pc][0], (int)wd[pc][1], (int)wd[pc][2], (int)wd[pc][3]);
+        for (int b = 0; b < kB; ++b) {
+          const int idx = b0 + b * 256 + tid;
+          if (idx < tot) reinterpret_cast<float4*>(t_s)[idx] = v[b];
         }
       }
-      __syncthreads();   // LDS reuse across token tiles
-#pragma unroll
-      for (int pc = 0; pc < 3; ++pc) {
-        S.frag[wave][pc][gq][pi][0] = pk[pc][0];
-        S.frag[wave][pc][gq][pi][1] = pk[pc][1];
-      }
-      if ((gq & 1) == 0) {
-        S.sc[wave][pi][gq >> 1] = (uint8_t)sbA;
-        S.sc[wave][pi][2 + (gq >> 1)] = (uint8_t)sbB;
-      }
-      S.cz[pi][wave * 4 + gq] = czp;
     }
     __syncthreads();
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float czp = 0.f;
+    const bool row_ok = ai < nt;
+    const bool prep_wave = 2 * wave < nt;   // this wave holds token rows 2w, 2w+1
+    // A-prep of chunk c into fragment slot `slot`: t'_i = s_ig t_i as three fp8 pieces
+    auto aprep = [&](int c, int slot) __attribute__((always_inline)) {
+      if (!prep_wave) return;
+      const bool three = c < nc3;
+      const int sn = three ? seg3.n : seg2.n;
+      const int li = (three ? c : c - nc3) * 128 + m0;
+      const int tb = three ? tb3 : tb2;
+      const int lr = min(li, (int)round_up(sn, 4) - 4);   // stay inside the staged segment
+      const uint4 uw = *reinterpret_cast<const uint4*>(us_s + tb + lr);
+      const float4 tw = *reinterpret_cast<const float4*>(t_s + (size_t)min(ai, nt - 1) * rs + tb + lr);
+      const uint32_t usw[4] = {uw.x, uw.y, uw.z, uw.w};
+      const float tt4[4] = {tw.x, tw.y, tw.z, tw.w};
+      float tp[4];
+      float mx = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < kUPass; ++cb) {
-      const int ci = su * kUPass + cb;
-      if (ci < nc) {
-        const bool three = ci < nc3;
-        const int4* f0 = S.frag[cb][0][q][col];
-        const int4* f1 = S.frag[cb][1][q][col];
-        const int4* f2 = S.frag[cb][2][q][col];
-        const v8i a0 = {f0[0].x, f0[0].y, f0[0].z, f0[0].w, f0[1].x, f0[1].y, f0[1].z, f0[1].w};
-        const v8i a1 = {f1[0].x, f1[0].y, f1[0].z, f1[0].w, f1[1].x, f1[1].y, f1[1].z, f1[1].w};
-        const v8i a2 = {f2[0].x, f2[0].y, f2[0].z, f2[0].w, f2[1].x, f2[1].y, f2[1].z, f2[1].w};
-        const int s0 = S.sc[cb][col][q];
-        const int bsc = three ? kScaleFp6Code : kScaleFp4Code;
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = row_ok && c < nc && li + u < sn;
+        tp[u] = ok ? f16f(usw[u] & 0xFFFFu) * tt4[u] : 0.f;
+        mx = fmaxf(mx, fabsf(tp[u]));
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+      const int sb = block_scale_byte(mx);
+      const float inv = pow2f(127 - sb), fwd = pow2f(sb - 127);
+      // three fp8 pieces, two values per conversion: the low half of word w[pc]
+      // holds ranks u = 0, 2 (even lane group), the high half ranks 1, 3
+      float r[4] = {tp[0] * inv, tp[1] * inv, tp[2] * inv, tp[3] * inv};
+      float bk[4] = {0.f, 0.f, 0.f, 0.f};
+      uint32_t w[3];
+      float sc_pc = 1.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const v8i bop = three ? b_fp6(cw[cb][h][0], cw[cb][h][1], cw[cb][h][2]) : b_fp4(cw[cb][h][0], cw[cb][h][1]);
-          const int fmt = three ? kFmtFp6 : kFmtFp4;
-          const int s1 = s0 - 5, s2 = s0 - 10;
-          f32x4 d = {0.f, 0.f, 0.f, 0.f};
-          d = mma(a0, bop, d, s0, fmt, bsc);
-          d = mma(a1, bop, d, s1, fmt, bsc);
-          d = mma(a2, bop, d, s2, fmt, bsc);
-          hold(d, a0, a1, a2, bop, s0, s1, s2, bsc);
-          acc[h] += d;
+      for (int pc = 0; pc < 3; ++pc) {
+        int ww = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[2], 0, false);
+        ww = __builtin_amdgcn_cvt_pk_fp8_f32(r[1], r[3], ww, true);
+        w[pc] = (uint32_t)ww;
+        const f32x2 e02 = __builtin_amdgcn_cvt_pk_f32_fp8(ww, false), e13 = __builtin_amdgcn_cvt_pk_f32_fp8(ww, true);
+        bk[0] += e02.x * sc_pc; bk[2] += e02.y * sc_pc; bk[1] += e13.x * sc_pc; bk[3] += e13.y * sc_pc;
+        r[0] = (r[0] - e02.x) * 32.f; r[2] = (r[2] - e02.y) * 32.f;
+        r[1] = (r[1] - e13.x) * 32.f; r[3] = (r[3] - e13.y) * 32.f;
+        sc_pc *= 1.f / 32.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) czp += f16f(usw[u] >> 16) * (bk[u] * fwd);   // zero for masked ranks and rows
+      if (ai < rows) {
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc) {
+          S.frag[slot][pc][lg_even][ai][hw] = (uint16_t)w[pc];
+          S.frag[slot][pc][lg_even + 1][ai][hw] = (uint16_t)(w[pc] >> 16);
+        }
+        if (part == 0) S.sc[slot][ai][kb4] = (uint8_t)sb;
+      }
+    };
+    // chunk c: matrix-core ops on slot c % 2, then (while they run) the code
+    // loads of chunk c + kUDepth - 1 and the A-prep of chunk c + 1 into the
+    // other slot; one barrier publishes it
+    auto step = [&](int c, int slot, UCodes& cur, UCodes& nxt) __attribute__((always_inline)) {
+      const bool three = c < nc3;
+      const uint4* f0 = reinterpret_cast<const uint4*>(S.frag[slot][0][q][col]);
+      const uint4* f1 = reinterpret_cast<const uint4*>(S.frag[slot][1][q][col]);
+      const uint4* f2 = reinterpret_cast<const uint4*>(S.frag[slot][2][q][col]);
+      const v8i a0 = v8_of(f0[0], f0[1]);
+      const v8i a1 = v8_of(f1[0], f1[1]);
+      const v8i a2 = v8_of(f2[0], f2[1]);
+      const int s0 = S.sc[slot][col][q], s1 = s0 - 5, s2 = s0 - 10;
+      f32x4 d[2];
+      v8i bop[2];
+      const int bs = three ? kScaleFp6Code : kScaleFp4Code;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        d[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (three) {
+          bop[h] = b_fp6(cur.w[h][0], cur.w[h][1], cur.w[h][2]);
+          d[h] = mma(a0, bop[h], d[h], s0, kFmtFp6, bs);
+          d[h] = mma(a1, bop[h], d[h], s1, kFmtFp6, bs);
+          d[h] = mma(a2, bop[h], d[h], s2, kFmtFp6, bs);
+        } else {
+          bop[h] = b_fp4(cur.w[h][0], cur.w[h][1]);
+          d[h] = mma(a0, bop[h], d[h], s0, kFmtFp4, bs);
+          d[h] = mma(a1, bop[h], d[h], s1, kFmtFp4, bs);
+          d[h] = mma(a2, bop[h], d[h], s2, kFmtFp4, bs);
+        }
+      }
+      load_codes(nxt, c + kUDepth - 1);
+      aprep(c + 1, slot ^ 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        hold(d[h], a0, a1, a2, bop[h], s0, s1, s2, bs);
+        acc[h] += d[h];
+      }
+      __syncthreads();
+    };
+    aprep(0, 0);
+    __syncthreads();
+    int c0 = 0;
+    for (; c0 + kUDepth <= nc; c0 += kUDepth) {
+      step(c0 + 0, 0, cr[0], cr[3]);
+      step(c0 + 1, 1, cr[1], cr[0]);
+      step(c0 + 2, 0, cr[2], cr[1]);
+      step(c0 + 3, 1, cr[3], cr[2]);
+    }
+    // tail: fewer than kUDepth chunks left (uniform guards)
+    if (c0 + 0 < nc) step(c0 + 0, 0, cr[0], cr[3]);
+    if (c0 + 1 < nc) step(c0 + 1, 1, cr[1], cr[0]);
+    if (c0 + 2 < nc) step(c0 + 2, 0, cr[2], cr[1]);
+    // ---- epilogue: sum_i z t' per token row, 8-bit pairs, W x, one rounding
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) czp += __shfl_xor(czp, m, 64);   // the 32 threads of row ai
+    if ((tid & 31) == 0 && ai < rows) S.cz[ai] = czp;
+    __syncthreads();
+    float yb[2][4];
+    int tk[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rw = min(4 * q + r, nt - 1);
+      tk[r] = perm[pb + rw];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) yb[h][r] = ybase ? ybase[(size_t)tk[r] * out + orow[h]] : 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rw = 4 * q + r;
+        if (rw < nt) {
+          float v = acc[h][r] - S.cz[rw];
+#pragma unroll
+          for (int i = 0; i < kU8Max; ++i)
+            if (i < s8.n) v += u8w[h][i] * t_s[(size_t)rw * rs + i];
+          for (int i = kU8Max; i < s8.n; ++i) {   // more 8-bit pairs than kept in registers
+            const uint32_t e = us_s[i];
+            const float uh = (float)(_Float16)(f16f(e & 0xFFFFu) * ((float)s8.uc[(size_t)orow[h] * s8.n + i] - f16f(e >> 16)));
+            v += uh * t_s[(size_t)rw * rs + i];
+          }
+          y[(size_t)tk[r] * out + orow[h]] = to_bf16(v + yb[h][r]);
         }
       }
     }
-    // partial of this slice: acc - sum_i z t'
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * q + r;
-      if (row < nt) {
-        float cz = 0.f;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) cz += S.cz[row][u];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) st_dev(part + (size_t)(pb + row) * out + orow[h], acc[h][r] - cz);
-      }
-    }
-  }
-  // last arriving slice: add the slices in order, the 8-bit pairs and W x
-  if (!arrive_last(&cnt[(size_t)n * vbmax + (size_t)k * go + g], nsu, &S.last)) return;
-  const Seg s8 = seg_of(tn, L, 0);
-  const int np8 = (int)round_up(s8.n, 4);
-  const int ol = tid & 127, o = g * kGroup + ol;
-  float u8[8];
-  const int n8c = min(s8.n, 8);
-  for (int i = 0; i < n8c; ++i) {
-    const uint32_t e = s8.us[(size_t)g * np8 + i];
-    u8[i] = (float)(_Float16)(f16f(e & 0xFFFFu) * ((float)s8.uc[(size_t)o * s8.n + i] - f16f(e >> 16)));
-  }
-  for (int p = p0 + (tid >> 7); p < p1; p += 2) {
-    float v = 0.f;
-    for (int j = 0; j < nsu; ++j) v += ld_dev(upart + ((size_t)j * T + p) * out + o);
-    for (int i = 0; i < s8.n; ++i) {
-      float uh;
-      if (i < n8c) uh = u8[i];
-      else {
-        const uint32_t e = s8.us[(size_t)g * np8 + i];
-        uh = (float)(_Float16)(f16f(e & 0xFFFFu) * ((float)s8.uc[(size_t)o * s8.n + i] - f16f(e >> 16)));
-      }
-      v += uh * tv[(size_t)p * rs + i];
-    }
-    const int t = perm[p];
-    if (ybase) v += ybase[(size_t)t * out + o];
-    y[(size_t)t * out + o] = to_bf16(v);
+    __syncthreads();   // LDS is restaged by the next token pass
   }
 }
 
@@ -769,13 +800,8 @@ int launch_apply(const ApplyArgs& a) {
   uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + a.wl.flags);
   int32_t* offs = reinterpret_cast<int32_t*>(a.ws + a.wl.offs);
   int32_t* perm = reinterpret_cast<int32_t*>(a.ws + a.wl.perm);
-  float* tv = reinterpret_cast<float*>(a.ws + a.wl.tv);
+  float* tv = reinterpret_cast<float*>(a.ws + a.wl.vpart);
   float* ybase = a.W ? reinterpret_cast<float*>(a.ws + a.wl.ybase) : nullptr;
-  float* vpart = reinterpret_cast<float*>(a.ws + a.wl.vpart);
-  float* upart = reinterpret_cast<float*>(a.ws + a.wl.upart);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(a.ws + a.wl.cnt);
-  const int go = a.out / kGroup;
-  const int ncnt = a.n * (a.wl.vb + go);
   const size_t items = (size_t)a.T * (a.in / kGroup);
   uint8_t* xf = a.ws + a.wl.xf;
   uint32_t* xsc = reinterpret_cast<uint32_t*>(a.ws + a.wl.xsc);
@@ -790,17 +816,21 @@ int launch_apply(const ApplyArgs& a) {
   mark(DC_STAGE_ROUTE);
   mark(DC_STAGE_XPREP);
   hipLaunchKernelGGL(k_prep, dim3((unsigned)(1 + (items + 3) / 4)), dim3(256), 0, st, a.x, a.ids, a.T, a.in, a.n,
-                     a.mode, seg, offs, perm, flags, xf, xsc, xsum, xt, cnt, ncnt);
+                     a.mode, seg, offs, perm, flags, xf, xsc, xsum, xt, tv, a.T * a.wl.rs);
   mark(DC_STAGE_BASE);
   if (a.W) launch_base(a.W, xt, ybase, a.out, a.in, a.T, a.stream);
   mark(DC_STAGE_VSIDE);
   if (a.wl.vb > 0)
     hipLaunchKernelGGL(k_vside, dim3((unsigned)(a.wl.vb * v_slices(a.in)), (unsigned)a.n), dim3(256), 0, st,
-                       *a.tenants, a.out, a.in, a.x, offs, perm, xf, xsc, xsum, vpart, tv, a.wl.rs, a.T, cnt,
-                       a.wl.vb);
+                       *a.tenants, a.out, a.in,
+                       a.x, offs, perm, xf, xsc, xsum, tv, a.wl.rs);
   mark(DC_STAGE_USIDE);
-  hipLaunchKernelGGL(k_uside, dim3((unsigned)go, (unsigned)(a.n + 1), (unsigned)a.wl.us), dim3(256), 0, st,
-                     *a.tenants, a.n, a.out, a.in, offs, perm, tv, a.wl.rs, ybase, upart, a.T, cnt, a.wl.vb, a.y);
+  // token rows per U pass: as many as fit in 64 KB of LDS with the staged t rows
+  int urows = kURows;
+  while (urows > 1 && u_lds_bytes(a.wl.rs, urows) > 65536) urows >>= 1;
+  hipLaunchKernelGGL(k_uside, dim3((unsigned)(a.out / kGroup), (unsigned)(a.n + 1)), dim3(256),
+                     (unsigned)u_lds_bytes(a.wl.rs, urows), st, *a.tenants, a.n, a.out, a.in, offs, perm, tv, a.wl.rs,
+                     urows, ybase, a.y);
   mark(DC_STAGE_COUNT);
   return (int)hipGetLastError();
 }
