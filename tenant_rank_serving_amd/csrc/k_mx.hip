@@ -486,37 +486,34 @@ __global__ void __launch_bounds__(256) k_vside(TenantTable tt, int32_t out, int3
 // ------------------------------------------------------------------ U side
 // Work item (block): 128-row output group g = blockIdx.x of tenant
 // k = blockIdx.y (n = the backbone-only bucket), all ranks, tokens in passes
-// of up to kURows.  A pass first stages the scale/zero words of row group g
-// and the pass's rows of t into LDS.  The ranks then go in 128-rank chunks,
-// 3-bit chunks first: the block turns t'_i = s_ig t_i into three fp8 pieces
-// with E8M0 block scales (thread: token row, K-block, 4 ranks; its even and
-// odd bytes land as one 16-bit word each in the A fragments), and wave w runs
-// its two 16-row output tiles (rows 32w..32w+31) on the matrix cores.  The
-// only global loads in the chunk loop are the codes, kept kUDepth-1 chunks
-// ahead in a register ring.  The epilogue takes sum_i z_ig t'_i off, adds
-// the 8-bit pairs and W x and rounds once to bf16.
+// of up to kURows.  The ranks go in 128-rank chunks, 3-bit chunks first.  Per
+// chunk the block turns t'_i = s_ig t_i into three fp8 pieces with E8M0
+// block scales (thread: token row, K-block, 4 ranks; its even and odd bytes
+// land as one 16-bit word each in the A fragments in LDS), and wave w runs
+// its two 16-row output tiles (rows 32w..32w+31) on the matrix cores.  Each
+// thread's codes, scale/zero words and t values of the next kUDepth-1 chunks
+// are in flight in a register ring; the matrix-core ops of chunk c overlap
+// the A-prep of chunk c+1.  The epilogue takes sum_i z_ig t'_i off, adds the
+// 8-bit pairs and W x and rounds once to bf16.
 constexpr int kURows = 8;    // token rows per pass
 constexpr int kU8Max = 4;    // 8-bit pairs whose U weights a lane keeps in registers
-constexpr int kUDepth = 4;   // register ring of codes, in chunks
+constexpr int kUDepth = 4;   // register ring, in chunks
 
-struct UCodes {
-  uint32_t w[2][3];   // B operand words of the lane's two output tiles
+struct UIn {           // one thread's loads for one chunk
+  uint32_t w[2][3];    // B operand words of the lane's two output tiles
+  uint4 us;            // scale/zero words of its 4 A-prep ranks
+  float4 t;            // t of those ranks for its token row
 };
 
-// LDS of one block (dynamic): fixed part, then us[rs] and t[rows][rs].
-struct UFixed {
+struct ULds {
   uint16_t frag[2][3][4][16][16];   // [slot][piece][lane group][A row][32 bytes]; rows >= the pass's tokens stay 0
   uint8_t sc[2][16][4];             // E8M0 of piece 0 per (slot, A row, K-block)
   float cz[kURows];                 // sum_i z t' per token row
 };
 
-__host__ __device__ inline size_t u_lds_bytes(int rs, int rows) {
-  return round_up(sizeof(UFixed), 16) + 4 * (size_t)rs * (1 + rows);
-}
-
 __global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_t out, int32_t in,
                                                const int32_t* __restrict__ offs, const int32_t* __restrict__ perm,
-                                               const float* __restrict__ tv, int32_t rs, int32_t rows,
+                                               const float* __restrict__ tv, int32_t rs,
                                                const float* __restrict__ ybase, uint16_t* __restrict__ y) {
   const int g = blockIdx.x, k = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -531,15 +528,13 @@ __global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_
     }
     return;
   }
-  extern __shared__ __align__(16) uint8_t u_lds[];
-  UFixed& S = *reinterpret_cast<UFixed*>(u_lds);
-  uint32_t* us_s = reinterpret_cast<uint32_t*>(u_lds + round_up(sizeof(UFixed), 16));   // [rs]
-  float* t_s = reinterpret_cast<float*>(us_s + rs);                                        // [rows][rs]
+  __shared__ ULds S;
   const Tenant tn = tt.t[k];
   Layout L;
   layout_of(out, in, tn.n8, tn.n3, tn.n2, &L);
   const Seg seg3 = seg_of(tn, L, 1), seg2 = seg_of(tn, L, 2), s8 = seg_of(tn, L, 0);
   const int tb3 = t_base(tn.n8, tn.n3, 1), tb2 = t_base(tn.n8, tn.n3, 2);
+  const int np3 = (int)round_up(seg3.n, 4), np2 = (int)round_up(seg2.n, 4);
   const int nc3 = (seg3.n + 127) / 128, nc = nc3 + (seg2.n + 127) / 128;
   const int orow[2] = {g * kGroup + wave * 32 + col, g * kGroup + wave * 32 + 16 + col};
   // fp16 dequantized 8-bit U weights of this lane's two output rows (first kU8Max pairs)
@@ -561,8 +556,8 @@ __global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_
   const int ai = tid >> 5, kb4 = (tid >> 3) & 3, part = tid & 7;
   const int m0 = kb4 * 32 + part * 4;
   const int lg_even = 2 * (kb4 & 1), hw = (kb4 >= 2 ? 8 : 0) + part;   // lane group, 16-bit word
-  // word offsets of this lane's K-block words in the U code tiles (same formula
-  // as u_kblock_word, split into per-tile constants and a per-chunk term)
+  // word offsets of this lane's K-block words in the U code tiles (the formula of
+  // u_kblock_word, split into per-tile constants and a per-chunk term)
   struct UAddr {
     int kbn, cb, tile[2], ro[2], rl[2];
   };
@@ -581,70 +576,41 @@ __global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_
     return a;
   };
   const UAddr ad3 = uaddr(seg3.n, 3), ad2 = uaddr(seg2.n, 2);
-  auto load_codes = [&](UCodes& uc, int c) __attribute__((always_inline)) {
-    c = min(c, nc - 1);
-    const bool three = c < nc3;
-    const int cc = three ? c : c - nc3;
-    const int kbn = three ? ad3.kbn : ad2.kbn;
-    const int kb = min(4 * cc + q, kbn - 1);
-    const bool last = kb == kbn - 1;
-    const uint32_t* ub = reinterpret_cast<const uint32_t*>(three ? seg3.uc : seg2.uc);
+  for (int pb = p0; pb < p1; pb += kURows) {
+    const int nt = min(kURows, p1 - pb);
+    const float* trow = tv + (size_t)(pb + min(ai, nt - 1)) * rs;   // clamped; masked below
+    // all of one thread's loads for chunk c (indices past a segment are clamped into it)
+    auto load = [&](UIn& in_, int c) __attribute__((always_inline)) {
+      c = min(c, nc - 1);
+      const bool three = c < nc3;
+      const int cc = three ? c : c - nc3;
+      const int kbn = three ? ad3.kbn : ad2.kbn;
+      const int kb = min(4 * cc + q, kbn - 1);
+      const bool last = kb == kbn - 1;
+      const uint32_t* ub = reinterpret_cast<const uint32_t*>(three ? seg3.uc : seg2.uc);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int tile = three ? ad3.tile[h] : ad2.tile[h];
-      const int ro = last ? (three ? ad3.rl[h] : ad2.rl[h]) : (three ? ad3.ro[h] : ad2.ro[h]);
-      const uint32_t* wp = ub + tile + kb * (three ? ad3.cb : ad2.cb) + ro;
-      uc.w[h][0] = wp[0];
-      uc.w[h][1] = wp[1];
-      uc.w[h][2] = wp[2];
-    }
-  };
-  for (int pb = p0; pb < p1; pb += rows) {
-    const int nt = min(rows, p1 - pb);
-    UCodes cr[kUDepth];
+      for (int h = 0; h < 2; ++h) {
+        const int tile = three ? ad3.tile[h] : ad2.tile[h];
+        const int ro = last ? (three ? ad3.rl[h] : ad2.rl[h]) : (three ? ad3.ro[h] : ad2.ro[h]);
+        const uint32_t* wp = ub + tile + kb * (three ? ad3.cb : ad2.cb) + ro;
+        in_.w[h][0] = wp[0];
+        in_.w[h][1] = wp[1];
+        in_.w[h][2] = wp[2];
+      }
+      const int li = cc * 128 + m0;
+      const int np = three ? np3 : np2;
+      in_.us = *reinterpret_cast<const uint4*>((three ? seg3.us : seg2.us) + (size_t)g * np + min(li, np - 4));
+      in_.t = *reinterpret_cast<const float4*>(trow + (three ? tb3 : tb2) + min(li, np - 4));
+    };
+    UIn cr[kUDepth];
     if (nc > 0) {
 #pragma unroll
-      for (int d = 0; d < kUDepth - 1; ++d) load_codes(cr[d], d);
+      for (int d = 0; d < kUDepth - 1; ++d) load(cr[d], d);
     }
-    // ---- zero the A fragments (rows past the pass's tokens stay 0), stage the
-    // scale/zero words of row group g and the pass's rows of t
+    // zero the A fragments: rows past the pass's tokens stay 0
     {
       uint4* fz = reinterpret_cast<uint4*>(&S);
       for (int i = tid; i < (int)((sizeof(S.frag) + sizeof(S.sc)) / 16); i += 256) fz[i] = make_uint4(0, 0, 0, 0);
-      const int n83 = tn.n8 + tn.n3, nr = n83 + tn.n2;
-      constexpr int kUs = 8;   // rank words per thread per batch, loads issued together
-      for (int b0 = 0; b0 < nr; b0 += 256 * kUs) {
-        uint32_t w[kUs];
-        int at[kUs];
-#pragma unroll
-        for (int b = 0; b < kUs; ++b) {
-          const int i = min(b0 + b * 256 + tid, nr - 1);
-          const int which = i < tn.n8 ? 0 : (i < n83 ? 1 : 2);
-          const uint32_t* usb = which == 0 ? s8.us : (which == 1 ? seg3.us : seg2.us);
-          const int sn = which == 0 ? s8.n : (which == 1 ? seg3.n : seg2.n);
-          const int li = i - (which == 0 ? 0 : (which == 1 ? tn.n8 : n83));
-          w[b] = usb[(size_t)g * round_up(sn, 4) + li];
-          at[b] = t_base(tn.n8, tn.n3, which) + li;
-        }
-#pragma unroll
-        for (int b = 0; b < kUs; ++b)
-          if (b0 + b * 256 + tid < nr) us_s[at[b]] = w[b];
-      }
-      const int w4 = rs / 4, tot = nt * w4;
-      constexpr int kB = 8;
-      for (int b0 = 0; b0 < tot; b0 += 256 * kB) {
-        float4 v[kB];
-#pragma unroll
-        for (int b = 0; b < kB; ++b) {
-          const int idx = min(b0 + b * 256 + tid, tot - 1);
-          v[b] = reinterpret_cast<const float4*>(tv + (size_t)(pb + idx / w4) * rs)[idx % w4];
-        }
-#pragma unroll
-        for (int b = 0; b < kB; ++b) {
-          const int idx = b0 + b * 256 + tid;
-          if (idx < tot) reinterpret_cast<float4*>(t_s)[idx] = v[b];
-        }
-      }
     }
     __syncthreads();
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -652,17 +618,13 @@ __global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_
     const bool row_ok = ai < nt;
     const bool prep_wave = 2 * wave < nt;   // this wave holds token rows 2w, 2w+1
     // A-prep of chunk c into fragment slot `slot`: t'_i = s_ig t_i as three fp8 pieces
-    auto aprep = [&](int c, int slot) __attribute__((always_inline)) {
+    auto aprep = [&](int c, int slot, const UIn& cur) __attribute__((always_inline)) {
       if (!prep_wave) return;
       const bool three = c < nc3;
       const int sn = three ? seg3.n : seg2.n;
       const int li = (three ? c : c - nc3) * 128 + m0;
-      const int tb = three ? tb3 : tb2;
-      const int lr = min(li, (int)round_up(sn, 4) - 4);   // stay inside the staged segment
-      const uint4 uw = *reinterpret_cast<const uint4*>(us_s + tb + lr);
-      const float4 tw = *reinterpret_cast<const float4*>(t_s + (size_t)min(ai, nt - 1) * rs + tb + lr);
-      const uint32_t usw[4] = {uw.x, uw.y, uw.z, uw.w};
-      const float tt4[4] = {tw.x, tw.y, tw.z, tw.w};
+      const uint32_t usw[4] = {cur.us.x, cur.us.y, cur.us.z, cur.us.w};
+      const float tt4[4] = {cur.t.x, cur.t.y, cur.t.z, cur.t.w};
       float tp[4];
       float mx = 0.f;
 #pragma unroll
@@ -695,19 +657,17 @@ __global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) czp += f16f(usw[u] >> 16) * (bk[u] * fwd);   // zero for masked ranks and rows
-      if (ai < rows) {
 #pragma unroll
-        for (int pc = 0; pc < 3; ++pc) {
-          S.frag[slot][pc][lg_even][ai][hw] = (uint16_t)w[pc];
-          S.frag[slot][pc][lg_even + 1][ai][hw] = (uint16_t)(w[pc] >> 16);
-        }
-        if (part == 0) S.sc[slot][ai][kb4] = (uint8_t)sb;
+      for (int pc = 0; pc < 3; ++pc) {
+        S.frag[slot][pc][lg_even][ai][hw] = (uint16_t)w[pc];
+        S.frag[slot][pc][lg_even + 1][ai][hw] = (uint16_t)(w[pc] >> 16);
       }
+      if (part == 0) S.sc[slot][ai][kb4] = (uint8_t)sb;
     };
-    // chunk c: matrix-core ops on slot c % 2, then (while they run) the code
-    // loads of chunk c + kUDepth - 1 and the A-prep of chunk c + 1 into the
-    // other slot; one barrier publishes it
-    auto step = [&](int c, int slot, UCodes& cur, UCodes& nxt) __attribute__((always_inline)) {
+    // chunk c: matrix-core ops on slot c % 2, then (while they run) the loads
+    // of chunk c + kUDepth - 1 and the A-prep of chunk c + 1 into the other
+    // slot; one barrier publishes it
+    auto step = [&](int c, int slot, UIn& cur, UIn& nx1, UIn& nxt) __attribute__((always_inline)) {
       const bool three = c < nc3;
       const uint4* f0 = reinterpret_cast<const uint4*>(S.frag[slot][0][q][col]);
       const uint4* f1 = reinterpret_cast<const uint4*>(S.frag[slot][1][q][col]);
@@ -734,8 +694,8 @@ __global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_
           d[h] = mma(a2, bop[h], d[h], s2, kFmtFp4, bs);
         }
       }
-      load_codes(nxt, c + kUDepth - 1);
-      aprep(c + 1, slot ^ 1);
+      load(nxt, c + kUDepth - 1);
+      aprep(c + 1, slot ^ 1, nx1);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         hold(d[h], a0, a1, a2, bop[h], s0, s1, s2, bs);
@@ -743,25 +703,27 @@ __global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_
       }
       __syncthreads();
     };
-    aprep(0, 0);
-    __syncthreads();
+    if (nc > 0) {
+      aprep(0, 0, cr[0]);
+      __syncthreads();
+    }
     int c0 = 0;
     for (; c0 + kUDepth <= nc; c0 += kUDepth) {
-      step(c0 + 0, 0, cr[0], cr[3]);
-      step(c0 + 1, 1, cr[1], cr[0]);
-      step(c0 + 2, 0, cr[2], cr[1]);
-      step(c0 + 3, 1, cr[3], cr[2]);
+      step(c0 + 0, 0, cr[0], cr[1], cr[3]);
+      step(c0 + 1, 1, cr[1], cr[2], cr[0]);
+      step(c0 + 2, 0, cr[2], cr[3], cr[1]);
+      step(c0 + 3, 1, cr[3], cr[0], cr[2]);
     }
     // tail: fewer than kUDepth chunks left (uniform guards)
-    if (c0 + 0 < nc) step(c0 + 0, 0, cr[0], cr[3]);
-    if (c0 + 1 < nc) step(c0 + 1, 1, cr[1], cr[0]);
-    if (c0 + 2 < nc) step(c0 + 2, 0, cr[2], cr[1]);
+    if (c0 + 0 < nc) step(c0 + 0, 0, cr[0], cr[1], cr[3]);
+    if (c0 + 1 < nc) step(c0 + 1, 1, cr[1], cr[2], cr[0]);
+    if (c0 + 2 < nc) step(c0 + 2, 0, cr[2], cr[3], cr[1]);
     // ---- epilogue: sum_i z t' per token row, 8-bit pairs, W x, one rounding
 #pragma unroll
     for (int m = 1; m < 32; m <<= 1) czp += __shfl_xor(czp, m, 64);   // the 32 threads of row ai
-    if ((tid & 31) == 0 && ai < rows) S.cz[ai] = czp;
+    if ((tid & 31) == 0 && ai < kURows) S.cz[ai] = czp;
     __syncthreads();
-    float yb[2][4];
+    float yb[2][4], t8[4][kU8Max];
     int tk[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -769,6 +731,8 @@ __global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_
       tk[r] = perm[pb + rw];
 #pragma unroll
       for (int h = 0; h < 2; ++h) yb[h][r] = ybase ? ybase[(size_t)tk[r] * out + orow[h]] : 0.f;
+#pragma unroll
+      for (int i = 0; i < kU8Max; ++i) t8[r][i] = tv[(size_t)(pb + rw) * rs + min(i, s8.n > 0 ? s8.n - 1 : 0)];
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -779,17 +743,17 @@ __global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_
           float v = acc[h][r] - S.cz[rw];
 #pragma unroll
           for (int i = 0; i < kU8Max; ++i)
-            if (i < s8.n) v += u8w[h][i] * t_s[(size_t)rw * rs + i];
+            if (i < s8.n) v += u8w[h][i] * t8[r][i];
           for (int i = kU8Max; i < s8.n; ++i) {   // more 8-bit pairs than kept in registers
-            const uint32_t e = us_s[i];
+            const uint32_t e = s8.us[(size_t)g * round_up(s8.n, 4) + i];
             const float uh = (float)(_Float16)(f16f(e & 0xFFFFu) * ((float)s8.uc[(size_t)orow[h] * s8.n + i] - f16f(e >> 16)));
-            v += uh * t_s[(size_t)rw * rs + i];
+            v += uh * tv[(size_t)(pb + rw) * rs + i];
           }
           y[(size_t)tk[r] * out + orow[h]] = to_bf16(v + yb[h][r]);
         }
       }
     }
-    __syncthreads();   // LDS is restaged by the next token pass
+    __syncthreads();   // S.cz and the fragments are rewritten by the next token pass
   }
 }
 
@@ -825,12 +789,8 @@ int launch_apply(const ApplyArgs& a) {
                        *a.tenants, a.out, a.in,
                        a.x, offs, perm, xf, xsc, xsum, tv, a.wl.rs);
   mark(DC_STAGE_USIDE);
-  // token rows per U pass: as many as fit in 64 KB of LDS with the staged t rows
-  int urows = kURows;
-  while (urows > 1 && u_lds_bytes(a.wl.rs, urows) > 65536) urows >>= 1;
-  hipLaunchKernelGGL(k_uside, dim3((unsigned)(a.out / kGroup), (unsigned)(a.n + 1)), dim3(256),
-                     (unsigned)u_lds_bytes(a.wl.rs, urows), st, *a.tenants, a.n, a.out, a.in, offs, perm, tv, a.wl.rs,
-                     urows, ybase, a.y);
+  hipLaunchKernelGGL(k_uside, dim3((unsigned)(a.out / kGroup), (unsigned)(a.n + 1)), dim3(256), 0, st, *a.tenants,
+                     a.n, a.out, a.in, offs, perm, tv, a.wl.rs, ybase, a.y);
   mark(DC_STAGE_COUNT);
   return (int)hipGetLastError();
 }
