@@ -280,7 +280,7 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
 // 2 kVSlice groups has at most two slices, whose sum is exact in either
 // order, so t is the same on every run.
 struct VLds {
-  int4 frag[kVSlice][kVRows][4][4];   // [group][token row][lane group][hi0 hi1 lo0 lo1]
+  int4 frag[kVSlice][kVRows][17];     // [group][token row][lane group * 4 + (hi0 hi1 lo0 lo1)], padded row
   uint32_t sc[kVSlice][kVRows];       // E8M0 words of the hi pieces
   float xs[kVSlice][kVRows];          // group sums of x
 };
@@ -339,7 +339,7 @@ __device__ __forceinline__ void v_stage_x(VLds& S, const uint8_t* __restrict__ x
   const float xsv = xsum[(size_t)stok * gi_n + gs];
 #pragma unroll
   for (int u = 0; u < kVSlice / 2; ++u)
-    S.frag[gh + 2 * u][rw][k16 >> 2][k16 & 3] = make_int4(v[u].x, v[u].y, v[u].z, v[u].w);
+    S.frag[gh + 2 * u][rw][k16] = make_int4(v[u].x, v[u].y, v[u].z, v[u].w);
   if (tid < kVRows * kVSlice) {
     S.sc[sgl][sr] = scw;
     S.xs[sgl][sr] = xsv;
@@ -379,7 +379,7 @@ __device__ void vside_tile(const Seg& sg, int tbase, int tile, int in, int s, co
 #pragma unroll
     for (int u = 0; u < kVSlice; ++u) {
       if (u < gn) {
-        const int4* fr = S.frag[u][tr][q] + 2 * piece;
+        const int4* fr = S.frag[u][tr] + 4 * q + 2 * piece;
         const int4 f0 = fr[0], f1 = fr[1];
         const v8i a = live ? v8i{f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w} : v8i{0, 0, 0, 0, 0, 0, 0, 0};
         const int sa = live ? (int)((S.sc[u][tr] >> (8 * q)) & 0xFFu) - 5 * piece : 127;
@@ -388,14 +388,15 @@ __device__ void vside_tile(const Seg& sg, int tbase, int tile, int in, int s, co
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
         d = mma(a, bo, d, sa, fmt, bs);
         hold(d, a, bo, sa, bs);
-        // D rows 0-7: hi products of tokens 0-7 (lane groups 0, 1); rows 8-15: lo products
-#pragma unroll
-        for (int r = 0; r < 4; ++r) d[r] += __shfl_xor(d[r], 32, 64);
-        const float sc = f16f(c.z[u] & 0xFFFFu), z = f16f(c.z[u] >> 16);
+        // D rows 0-7 (lane groups 0, 1): hi products of tokens 0-7, which also
+        // take the zero-point term; rows 8-15: lo products, added at the end
+        const float sc = f16f(c.z[u] & 0xFFFFu), z = q < 2 ? f16f(c.z[u] >> 16) : 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] += sc * (d[r] - z * S.xs[u][(4 * q + r) & 7]);
       }
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], 32, 64);
     if (rv && q < 2) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
