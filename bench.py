@@ -186,36 +186,69 @@ def main():
     log("resident deltas: %.2f GB, backbone %.2f GB, built in %.1f s" %
         (pool.numel() / 1e9, sum(w.numel() * 2 for row in W for w in row) / 1e9, time.time() - t0))
     ws_bytes = max(trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, [sp] * synth.C2_TENANTS, T) for sp in specs)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    ys = {sp[0]: torch.empty((T, sp[0]), dtype=torch.int16, device=dev) for sp in specs}
+    # A decoder layer's matrices in dependency order: q, k, v read the same
+    # input and run side by side on three streams (default priority), then o;
+    # gate and up side by side, then down.  Each stream has its own workspace
+    # and outputs.
+    waves = [[0, 1, 2], [3], [4, 5], [6]]
+    nstr = max(len(w) for w in waves)
+    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(nstr - 1)]
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(nstr)]
+    yss = [{sp[0]: torch.empty((T, sp[0]), dtype=torch.int16, device=dev) for sp in specs} for _ in range(nstr)]
+    ws, ys = wss[0], yss[0]
 
     def calls(fused):
+        """Sequential list of every call of a step, all on the launch stream."""
         return [trs.MultitenantCall(views[l][m], W[l][m] if fused else None, X[l][m], ids, ys[specs[m][0]], ws)
                 for l in range(args.layers) for m in range(len(specs))]
+
+    def layered_step(fused):
+        """The step as per-layer waves: returns a function that enqueues it."""
+        plan = []
+        for l in range(args.layers):
+            for wv in waves:
+                entry = [(si, trs.MultitenantCall(views[l][m], W[l][m] if fused else None, X[l][m], ids,
+                                                  yss[si][specs[m][0]], wss[si], stream=streams[si].cuda_stream))
+                         for si, m in enumerate(wv)]
+                fork = torch.cuda.Event() if len(wv) > 1 else None
+                joins = [torch.cuda.Event() for _ in wv[1:]]
+                plan.append((entry, fork, joins))
+
+        def run():
+            main = streams[0]
+            for entry, fork, joins in plan:
+                if fork is not None:
+                    fork.record(main)
+                    for si, _ in entry[1:]:
+                        streams[si].wait_event(fork)
+                for _, c in entry:
+                    c()
+                for (si, _), ev in zip(entry[1:], joins):
+                    ev.record(streams[si])
+                    main.wait_event(ev)
+        return run
 
     # bytes per step: packed deltas of the touched tenants (algorithmic), backbone
     delta_bytes = args.layers * len(touched) * sum(trs.dc_algorithmic_bytes(sp) for sp in specs)
     base_bytes = args.layers * sum(sp[0] * sp[1] * 2 for sp in specs)
 
-    def timed_steps(cl, steps, warmup):
+    def timed_steps(run, steps, warmup):
         for _ in range(warmup):
-            for c in cl:
-                c()
+            run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
-            for c in cl:
-                c()
+            run()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
     results = {}
     for mode in ("fused", "delta"):
-        cl = calls(mode == "fused")
+        run = layered_step(mode == "fused")
         log("timing %s step: warmup %d, steps %d" % (mode, args.warmup, args.steps))
-        results[mode] = timed_steps(cl, args.steps, args.warmup)
+        results[mode] = timed_steps(run, args.steps, args.warmup)
         log("%s: %.3f ms/step" % (mode, results[mode]))
 
     # Per-kernel durations: one more pass of the fused step with HIP events

@@ -89,10 +89,15 @@ struct TenantTable {
 // Work decomposition of the matrix-core path (shared by host sizing and kernels).
 constexpr int kVSlice = 16;   // 128-groups of the input per V-side work item
 constexpr int kVRows = 8;     // token rows per V-side pass
+constexpr int kVTiles = 2;    // 16-rank tiles per V-side wave
+constexpr int kVRanks = 4 * 16 * kVTiles;   // ranks per V-side block (4 waves)
+constexpr int kVDepth = 8;    // groups of codes a V-side wave keeps in flight
 
 DC_HD inline int v_slices(int in) { return (in / kGroup + kVSlice - 1) / kVSlice; }
-// V-side rank blocks of a tenant: [8-bit rows if any] [3-bit 64-rank blocks] [2-bit 64-rank blocks]
-DC_HD inline int v_blocks(int n8, int n3, int n2) { return (n8 > 0 ? 1 : 0) + (n3 + 63) / 64 + (n2 + 63) / 64; }
+// V-side rank blocks of a tenant: [8-bit rows if any] [3-bit blocks] [2-bit blocks] of kVRanks
+DC_HD inline int v_blocks(int n8, int n3, int n2) {
+  return (n8 > 0 ? 1 : 0) + (n3 + kVRanks - 1) / kVRanks + (n2 + kVRanks - 1) / kVRanks;
+}
 // Rank positions of the V-side results: each bit-width segment starts on a multiple of 8.
 DC_HD inline int t_base(int n8, int n3, int which) {
   return which == 0 ? 0 : (which == 1 ? (int)round_up((size_t)n8, 8) : (int)(round_up((size_t)n8, 8) + round_up((size_t)n3, 8)));

@@ -38,6 +38,7 @@ constexpr int kFmtFp8 = 0, kFmtFp6 = 2, kFmtFp4 = 4;
 constexpr int kScaleFp4Code = 128;   // 2^1: fp4 element q/2 -> q
 constexpr int kScaleFp6Code = 130;   // 2^3: fp6 element q/8 -> q
 constexpr int kXFrag = 256;          // bytes of x fragments per (token, 128-group)
+constexpr int kBufFlags = 0x00020000; // buffer resource word 3: raw 32-bit dwords, bounds-checked
 
 __device__ __forceinline__ float f16f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 
@@ -270,15 +271,16 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
 // ------------------------------------------------------------------ V side
 // Work item (block): tenant k = blockIdx.y; blockIdx.x = rank block rb *
 // v_slices + input slice s.  Rank blocks: the 8-bit rows (vector ALU, fp16
-// dequantized weights), then 64-rank blocks of the 3-bit and of the 2-bit
-// segment (four 16-rank tiles, one per wave, on the matrix cores).  Tokens go
-// in passes of kVRows.  An item issues the loads of all its codes, then
-// stages the x fragments of its slice for the pass into LDS, and runs one
-// matrix-core op per group: A rows 0-7 are the hi pieces and rows 8-15 the lo
-// pieces of the pass's tokens.  sigma * (partial V x) is added into t with
-// float atomics; t is zeroed by the prep kernel.  An input of up to
-// 2 kVSlice groups has at most two slices, whose sum is exact in either
-// order, so t is the same on every run.
+// dequantized weights), then blocks of kVRanks ranks of the 3-bit and of the
+// 2-bit segment on the matrix cores: wave w takes kVTiles 16-rank tiles, all
+// waves the same kVSlice input groups.  Tokens go in passes of kVRows; per
+// pass the block stages the x fragments of its slice into LDS once and every
+// wave reads them as the A operand (rows 0-7 the hi pieces, rows 8-15 the lo
+// pieces of the pass's tokens).  A wave's codes stream through a register
+// ring kVDepth groups deep: the loads of group u + kVDepth go out before the
+// matrix-core ops of group u (a later pass reloads them, from L2).  The
+// kVTiles ops of a group share one A operand and are independent.  sigma * (partial V x)
+// is added into t with float atomics; t is zeroed by the prep kernel.
 struct VLds {
   int4 frag[kVSlice][kVRows][17];     // [group][token row][lane group * 4 + (hi0 hi1 lo0 lo1)], padded row
   uint32_t sc[kVSlice][kVRows];       // E8M0 words of the hi pieces
@@ -286,46 +288,55 @@ struct VLds {
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+struct U3 {
+  uint32_t a, b, c;
+};
 
-// All code words of one lane for the slice (2 or 3 per group) and the
-// group scale/zero words.
+// One group of one lane's codes (B words per tile) and its scale/zero words.
 template <int B>
-struct VCodes {
-  uint32_t w[kVSlice][B];
-  uint32_t z[kVSlice];
+struct VGrp {
+  uint32_t w[kVTiles][B];
+  uint32_t z[kVTiles];
+};
+
+// Buffer resources of a segment's V codes and scale/zero words, and the byte
+// offsets of the lane's rank in each of its tiles (rank 0 of the segment for
+// ranks past its end); the group goes into the uniform offset.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
+struct VBuf {
+  __amdgpu_buffer_rsrc_t rc, rz;
+  uint32_t oc[kVTiles], oz[kVTiles];
 };
 
 template <int B>
-__device__ __forceinline__ void v_load_codes(VCodes<B>& c, const uint32_t* row, const uint32_t* vsp, int np, int g0,
-                                             int gi_n, int q) {
+__device__ __forceinline__ void v_load_grp(VGrp<B>& c, const VBuf& p, int np, int gi) {
 #pragma unroll
-  for (int u = 0; u < kVSlice; ++u) {
-    const int gi = min(g0 + u, gi_n - 1);
-    const uint32_t* wp = row + (size_t)gi * 4 * B + B * q;
+  for (int h = 0; h < kVTiles; ++h) {
     if constexpr (B == 2) {
-      const uint2 v = *reinterpret_cast<const uint2*>(wp);
-      c.w[u][0] = v.x;
-      c.w[u][1] = v.y;
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(p.rc, p.oc[h], gi * 4 * B * 4, 0);
+      c.w[h][0] = v.x;
+      c.w[h][1] = v.y;
     } else {
-      c.w[u][0] = wp[0];
-      c.w[u][1] = wp[1];
-      c.w[u][2] = wp[2];
+      const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(p.rc, p.oc[h], gi * 4 * B * 4, 0);
+      c.w[h][0] = v.x;
+      c.w[h][1] = v.y;
+      c.w[h][2] = v.z;
     }
-    c.z[u] = vsp[(size_t)gi * np];
+    c.z[h] = __builtin_amdgcn_raw_buffer_load_b32(p.rz, p.oz[h], gi * np * 4, 0);
   }
 }
 
 // Stage the x fragments of token rows [pb, pb + kVRows) for groups
 // [g0, g0 + kVSlice) into LDS.  Thread tid moves int4 (tid & 15) of the
-// fragment of row (tid >> 4) & 7 for groups (tid >> 7) + 2u; threads < 128
-// move one (group, row) scale word and group sum.  Rows past the pass repeat
-// its last token and are never read.
+// fragment of row (tid >> 4) & 7 (token tok) for groups (tid >> 7) + 2u;
+// threads < 128 move the scale word and group sum of row tid & 7 (token
+// stok) and group (tid >> 3) & 15.  Rows past the pass repeat its last token
+// and are never read; groups past the input repeat its last group.
 __device__ __forceinline__ void v_stage_x(VLds& S, const uint8_t* __restrict__ xf, const uint32_t* __restrict__ xsc,
-                                          const float* __restrict__ xsum, const int32_t* __restrict__ perm, int gi_n,
-                                          int g0, int pb, int nt) {
+                                          const float* __restrict__ xsum, int gi_n, int g0, int tok, int stok) {
   const int tid = threadIdx.x;
   const int k16 = tid & 15, rw = (tid >> 4) & 7, gh = tid >> 7;
-  const int tok = perm[pb + min(rw, nt - 1)];
   i32x4 v[kVSlice / 2];
 #pragma unroll
   for (int u = 0; u < kVSlice / 2; ++u) {
@@ -333,7 +344,6 @@ __device__ __forceinline__ void v_stage_x(VLds& S, const uint8_t* __restrict__ x
     v[u] = reinterpret_cast<const i32x4*>(xf + ((size_t)tok * gi_n + gi) * kXFrag)[k16];
   }
   const int sr = tid & 7, sgl = (tid >> 3) & (kVSlice - 1);
-  const int stok = perm[pb + min(sr, nt - 1)];
   const int gs = min(g0 + sgl, gi_n - 1);
   const uint32_t scw = xsc[(size_t)stok * gi_n + gs];
   const float xsv = xsum[(size_t)stok * gi_n + gs];
@@ -346,108 +356,186 @@ __device__ __forceinline__ void v_stage_x(VLds& S, const uint8_t* __restrict__ x
   }
 }
 
-// One 16-rank tile over one input slice, all tokens in passes of kVRows.
+// Token of the fragment row and of the scale row this thread stages for the
+// pass starting at sorted position pb.
+__device__ __forceinline__ void v_stage_tokens(const int32_t* __restrict__ perm, int pb, int nt, int& tok, int& stok) {
+  const int tid = threadIdx.x;
+  tok = perm[pb + min((tid >> 4) & 7, nt - 1)];
+  stok = perm[pb + min(tid & 7, nt - 1)];
+}
+
+__device__ __forceinline__ void hold2(f32x4& d0, f32x4& d1, const v8i& a, const v8i& b0, const v8i& b1, int sa,
+                                      int sb) {
+  asm volatile("" : "+v"(d0), "+v"(d1) : "v"(a), "v"(b0), "v"(b1), "v"(sa), "v"(sb));
+}
+
+// kVTiles 16-rank tiles of one wave (starting at tile0 of the segment) over
+// one input slice, all tokens; the block's other waves run the same slice.
+// live_wave: any of the wave's tiles holds a rank of the segment.
 template <int B>
-__device__ void vside_tile(const Seg& sg, int tbase, int tile, int in, int s, const int32_t* __restrict__ perm,
-                           int p0, int p1, const uint8_t* __restrict__ xf, const uint32_t* __restrict__ xsc,
-                           const float* __restrict__ xsum, const float* __restrict__ sigma, float* __restrict__ tv,
-                           int rs, VLds& S) {
+__device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, int in, int s,
+                          const int32_t* __restrict__ perm, int p0, int p1, const uint8_t* __restrict__ xf,
+                          const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
+                          const float* __restrict__ sigma, float* __restrict__ tv, int rs, VLds& S) {
+  static_assert(kVTiles == 2, "hold2 covers two tiles");
   constexpr int fmt = B == 2 ? kFmtFp4 : kFmtFp6;
   constexpr int bsc = B == 2 ? kScaleFp4Code : kScaleFp6Code;
+  constexpr int kDepth = B == 2 ? kVDepth : kVDepth / 2;   // ring depth in groups (3-bit groups are larger)
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, q = lane >> 4;
   const int gi_n = in / kGroup;
   const int g0 = s * kVSlice;
   const int gn = min(kVSlice, gi_n - g0);   // groups in this slice
-  const int li = tile * 16 + col;
-  const bool rv = li < sg.n;
+  const int glast = g0 + gn - 1;
   const int np = (int)round_up(sg.n, 4);
-  const uint32_t* row = reinterpret_cast<const uint32_t*>(sg.vc) + (size_t)(rv ? li : 0) * gi_n * 4 * B;
-  const uint32_t* vsp = sg.vs + (rv ? li : 0);
-  const float sig = rv ? sigma[sg.lo + li] : 0.f;
-  VCodes<B> c;
-  v_load_codes<B>(c, row, vsp, np, g0, gi_n, q);
+  const int npass = (p1 - p0 + kVRows - 1) / kVRows;
+  int tok, stok;
+  v_stage_tokens(perm, p0, min(kVRows, p1 - p0), tok, stok);
+  VBuf P;
+  P.rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sg.vc), 0, sg.n * gi_n * 16 * B, kBufFlags);
+  P.rz = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(sg.vs), 0, gi_n * np * 4, kBufFlags);
+  int li[kVTiles];
+  bool rv[kVTiles];
+  float sig[kVTiles];
+#pragma unroll
+  for (int h = 0; h < kVTiles; ++h) {
+    li[h] = (tile0 + h) * 16 + col;
+    rv[h] = li[h] < sg.n;
+    P.oc[h] = (uint32_t)((rv[h] ? li[h] : 0) * gi_n * 16 * B + 4 * B * q);
+    P.oz[h] = (uint32_t)(4 * (rv[h] ? li[h] : 0));
+    sig[h] = rv[h] ? sigma[sg.lo + li[h]] : 0.f;
+  }
   const int tr = col & 7;              // token row of this lane's A operand
   const int piece = col >> 3;          // 0: hi pieces, 1: lo pieces
-  for (int pb = p0; pb < p1; pb += kVRows) {
+  for (int ip = 0; ip < npass; ++ip) {
+    const int pb = p0 + ip * kVRows;
     const int nt = min(kVRows, p1 - pb);
+    VGrp<B> ring[kDepth] = {};   // defined on every path: no values carried across passes
+    if (live_wave) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) v_load_grp<B>(ring[d], P, np, min(g0 + d, glast));
+    }
     __syncthreads();   // LDS reuse across passes
-    v_stage_x(S, xf, xsc, xsum, perm, gi_n, g0, pb, nt);
+    v_stage_x(S, xf, xsc, xsum, gi_n, g0, tok, stok);
+    if (ip + 1 < npass) v_stage_tokens(perm, pb + kVRows, min(kVRows, p1 - pb - kVRows), tok, stok);
     __syncthreads();
+    if (!live_wave) continue;
     const bool live = tr < nt;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[kVTiles];
+#pragma unroll
+    for (int h = 0; h < kVTiles; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < kVSlice; ++u) {
-      if (u < gn) {
-        const int4* fr = S.frag[u][tr] + 4 * q + 2 * piece;
-        const int4 f0 = fr[0], f1 = fr[1];
-        const v8i a = live ? v8i{f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w} : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        const int sa = live ? (int)((S.sc[u][tr] >> (8 * q)) & 0xFFu) - 5 * piece : 127;
-        const v8i bo = B == 2 ? b_fp4(c.w[u][0], c.w[u][1]) : b_fp6(c.w[u][0], c.w[u][1], c.w[u][2]);
-        const int bs = bsc;
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
-        d = mma(a, bo, d, sa, fmt, bs);
-        hold(d, a, bo, sa, bs);
-        // D rows 0-7 (lane groups 0, 1): hi products of tokens 0-7, which also
-        // take the zero-point term; rows 8-15: lo products, added at the end
-        const float sc = f16f(c.z[u] & 0xFFFFu), z = q < 2 ? f16f(c.z[u] >> 16) : 0.f;
+      const VGrp<B> c = ring[u % kDepth];
+      if (u + kDepth < kVSlice)   // refill the slot with group u + kDepth (resolved at compile time)
+        v_load_grp<B>(ring[u % kDepth], P, np, min(g0 + u + kDepth, glast));
+      const int4* fr = S.frag[u][tr] + 4 * q + 2 * piece;
+      const int4 f0 = fr[0], f1 = fr[1];
+      const v8i a = live ? v8i{f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w} : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      const int sa = live ? (int)((S.sc[u][tr] >> (8 * q)) & 0xFFu) - 5 * piece : 127;
+      v8i bo[kVTiles];
+      f32x4 d[kVTiles];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += sc * (d[r] - z * S.xs[u][(4 * q + r) & 7]);
+      for (int h = 0; h < kVTiles; ++h) {
+        bo[h] = B == 2 ? b_fp4(c.w[h][0], c.w[h][1]) : b_fp6(c.w[h][0], c.w[h][1], c.w[h][2]);
+        d[h] = mma(a, bo[h], f32x4{0.f, 0.f, 0.f, 0.f}, sa, fmt, bsc);
       }
+      hold2(d[0], d[1], a, bo[0], bo[1], sa, bsc);
+      // D rows 0-7 (lane groups 0, 1): hi products of tokens 0-7, which also
+      // take the zero-point term; rows 8-15: lo products, added at the end.
+      // Groups past the input (u >= gn) are clamped duplicates: scale 0.
+      const bool gv = u < gn;
+      float xsr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xsr[r] = S.xs[u][(4 * q + r) & 7];
+#pragma unroll
+      for (int h = 0; h < kVTiles; ++h) {
+        const float sc = gv ? f16f(c.z[h] & 0xFFFFu) : 0.f, z = q < 2 ? f16f(c.z[h] >> 16) : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[h][r] += sc * (d[h][r] - z * xsr[r]);
+      }
+      // the group's sums land in acc here: without this the compiler defers
+      // them to the end of the pass and keeps every group's products live
+      asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], 32, 64);
-    if (rv && q < 2) {
+    for (int h = 0; h < kVTiles; ++h)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * q + r < nt) atomicAdd(tv + (size_t)(pb + 4 * q + r) * rs + tbase + li, sig * acc[r]);
+      for (int r = 0; r < 4; ++r) acc[h][r] += __shfl_xor(acc[h][r], 32, 64);
+    if (q < 2) {
+#pragma unroll
+      for (int h = 0; h < kVTiles; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (rv[h] && 4 * q + r < nt) atomicAdd(tv + (size_t)(pb + 4 * q + r) * rs + tbase + li[h], sig[h] * acc[h][r]);
     }
   }
 }
 
-// 8-bit rows of a tenant over one input slice, all tokens, on the vector ALU
-// with the fp16 dequantized weights; sigma * partial added into t.
+// 8-bit rows of a tenant over one input slice on the vector ALU with the fp16
+// dequantized weights fp16(s (q - z)).  Thread tid owns 8 inputs of the
+// slice, a pass's kVRows token rows and 4 rows at a time; the block sums per
+// (row, token) and adds sigma * partial into t.
 __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, const uint16_t* __restrict__ x,
                            const int32_t* __restrict__ perm, int p0, int p1, float* __restrict__ tv, int rs) {
-  __shared__ float red[4][8];
+  __shared__ float red[4][4][kVRows];   // [wave][row][token row]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const Seg sg = seg_of(tn, L, 0);
   const float* sigma = reinterpret_cast<const float*>(tn.base + L.off[DC_REG_SIGMA]);
   const int np = (int)round_up(sg.n, 4);
-  const int q0 = s * kVSlice * kGroup / 4, q1 = min(in / 4, q0 + kVSlice * kGroup / 4);
-  for (int i = 0; i < sg.n; ++i) {
-    const uint8_t* row = sg.vc + (size_t)i * in;   // 8-bit group bitstreams are plain bytes
-    for (int pc = p0; pc < p1; pc += 8) {
-      const int nt = min(8, p1 - pc);
-      float acc[8];
+  const int i0 = s * kVSlice * kGroup + 8 * tid;   // first input of this thread
+  const bool ok = i0 < in;
+  const int ic = ok ? i0 : 0;
+  const int gi = ic / kGroup;
+  for (int pb = p0; pb < p1; pb += kVRows) {
+    const int nt = min(kVRows, p1 - pb);
+    uint4 xv[kVRows];
 #pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8) acc[t8] = 0.f;
-      for (int qd = q0 + tid; qd < q1; qd += 256) {
-        const uint32_t e = sg.vs[(size_t)(qd * 4 / kGroup) * np + i];
-        const uint32_t c4 = *reinterpret_cast<const uint32_t*>(row + (size_t)qd * 4);
-        const float sc = f16f(e & 0xFFFFu), z = f16f(e >> 16);
-        float w[4];
+    for (int t = 0; t < kVRows; ++t)
+      xv[t] = *reinterpret_cast<const uint4*>(x + (size_t)perm[pb + min(t, nt - 1)] * in + ic);
+    for (int r0 = 0; r0 < sg.n; r0 += 4) {
+      uint2 cw[4];
+      uint32_t e[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = (float)(_Float16)(sc * ((float)((c4 >> (8 * u)) & 0xFFu) - z));
+      for (int u = 0; u < 4; ++u) {
+        const int i = min(r0 + u, sg.n - 1);
+        cw[u] = *reinterpret_cast<const uint2*>(sg.vc + (size_t)i * in + ic);
+        e[u] = sg.vs[(size_t)gi * np + i];
+      }
+      float part[4][kVRows];
 #pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8) {
-          if (t8 < nt) {
-            const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)perm[pc + t8] * in + (size_t)qd * 4);
-            acc[t8] += w[0] * __uint_as_float(xv.x << 16) + w[1] * __uint_as_float(xv.x & 0xFFFF0000u) +
-                       w[2] * __uint_as_float(xv.y << 16) + w[3] * __uint_as_float(xv.y & 0xFFFF0000u);
-          }
+      for (int u = 0; u < 4; ++u) {
+        const float sc = f16f(e[u] & 0xFFFFu), z = f16f(e[u] >> 16);
+        const uint32_t cwu[2] = {cw[u].x, cw[u].y};
+        float w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = (float)(_Float16)(sc * ((float)((cwu[j >> 2] >> (8 * (j & 3))) & 0xFFu) - z));
+#pragma unroll
+        for (int t = 0; t < kVRows; ++t) {
+          const uint32_t xw[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
+          float a = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            a += w[2 * j] * __uint_as_float(xw[j] << 16) + w[2 * j + 1] * __uint_as_float(xw[j] & 0xFFFF0000u);
+          part[u][t] = ok && t < nt ? a : 0.f;
         }
       }
 #pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8) {
-        float v = acc[t8];
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-        if (lane == 0) red[wave][t8] = v;
-      }
+        for (int t = 0; t < kVRows; ++t) {
+          float v = part[u][t];
+#pragma unroll
+          for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+          if (lane == 0) red[wave][u][t] = v;
+        }
       __syncthreads();
-      if (tid < nt)
-        atomicAdd(tv + (size_t)(pc + tid) * rs + i, sigma[i] * ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid])));
+      if (tid < 4 * kVRows) {
+        const int u = tid / kVRows, t = tid % kVRows;
+        if (r0 + u < sg.n && t < nt)
+          atomicAdd(tv + (size_t)(pb + t) * rs + r0 + u,
+                    sigma[r0 + u] * ((red[0][u][t] + red[1][u][t]) + (red[2][u][t] + red[3][u][t])));
+      }
       __syncthreads();
     }
   }
@@ -475,13 +563,16 @@ __global__ void __launch_bounds__(256) k_vside(TenantTable tt, int32_t out, int3
   __shared__ VLds S;
   const float* sigma = reinterpret_cast<const float*>(tn.base + L.off[DC_REG_SIGMA]);
   const int wave = threadIdx.x >> 6;
-  const int b3 = (tn.n3 + 63) / 64;
-  if (b < b3)
-    vside_tile<3>(seg_of(tn, L, 1), t_base(tn.n8, tn.n3, 1), b * 4 + wave, in, s, perm, p0, p1, xf, xsc, xsum, sigma,
-                  tv, rs, S);
+  const int b3 = (tn.n3 + kVRanks - 1) / kVRanks;
+  const bool three = b < b3;
+  const int tile0 = ((three ? b : b - b3) * 4 + wave) * kVTiles;
+  const int sn = three ? tn.n3 : tn.n2;
+  if (three)
+    vside_blk<3>(seg_of(tn, L, 1), t_base(tn.n8, tn.n3, 1), tile0, tile0 * 16 < sn, in, s, perm, p0, p1, xf, xsc,
+                 xsum, sigma, tv, rs, S);
   else
-    vside_tile<2>(seg_of(tn, L, 2), t_base(tn.n8, tn.n3, 2), (b - b3) * 4 + wave, in, s, perm, p0, p1, xf, xsc, xsum,
-                  sigma, tv, rs, S);
+    vside_blk<2>(seg_of(tn, L, 2), t_base(tn.n8, tn.n3, 2), tile0, tile0 * 16 < sn, in, s, perm, p0, p1, xf, xsc,
+                 xsum, sigma, tv, rs, S);
 }
 
 // ------------------------------------------------------------------ U side
