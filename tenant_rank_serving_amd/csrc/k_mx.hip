@@ -119,6 +119,14 @@ __device__ __forceinline__ void hold(f32x4& d, const v8i& a0, const v8i& a1, con
   asm volatile("" : "+v"(d) : "v"(a0), "v"(a1), "v"(a2), "v"(b), "v"(s0), "v"(s1), "v"(s2), "v"(sb));
 }
 
+// v from lane l ^ X (X < 32) by ds_swizzle: no lane-address register, unlike
+// a general shuffle.
+template <int X>
+__device__ __forceinline__ float swz_xor(float v) {
+  static_assert(X > 0 && X < 32, "swizzle lanes stay within 32-lane halves");
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (X << 10) | 0x1F));
+}
+
 __device__ __forceinline__ v8i v8_of(const uint4& a, const uint4& b) {
   return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
@@ -576,44 +584,46 @@ __global__ void __launch_bounds__(256) k_vside(TenantTable tt, int32_t out, int3
 }
 
 // ------------------------------------------------------------------ U side
-// Work item (block): 128-row output group g = blockIdx.x of tenant
-// k = blockIdx.y (n = the backbone-only bucket), all ranks, tokens in passes
-// of up to kURows.  The ranks go in 128-rank chunks, 3-bit chunks first.  Per
-// chunk the block turns t'_i = s_ig t_i into three fp8 pieces with E8M0
-// block scales (thread: token row, K-block, 4 ranks; its even and odd bytes
-// land as one 16-bit word each in the A fragments in LDS), and wave w runs
-// its two 16-row output tiles (rows 32w..32w+31) on the matrix cores.  Each
-// thread's codes, scale/zero words and t values of the next kUDepth-1 chunks
-// are in flight in a register ring; the matrix-core ops of chunk c overlap
-// the A-prep of chunk c+1.  The epilogue takes sum_i z_ig t'_i off, adds the
-// 8-bit pairs and W x and rounds once to bf16.
-constexpr int kURows = 8;    // token rows per pass
-constexpr int kU8Max = 4;    // 8-bit pairs whose U weights a lane keeps in registers
-constexpr int kUDepth = 4;   // register ring, in chunks
-
-struct UIn {           // one thread's loads for one chunk
-  uint32_t w[2][3];    // B operand words of the lane's two output tiles
-  uint4 us;            // scale/zero words of its 4 A-prep ranks
-  float4 t;            // t of those ranks for its token row
-};
+// Work item (block of kUWaves waves): 128-row output group g = blockIdx.x
+// (one scale group) of tenant k = blockIdx.y (n = the backbone-only bucket),
+// all ranks, tokens in passes of up to kURows.  Wave w takes the 16-row tile
+// 16w..16w+15.  The ranks go in 128-rank chunks, 3-bit chunks first.  Per
+// pass, for a window of up to kUWin chunks at a time, the whole block first
+// turns t'_i = s_ig t_i into three fp8 pieces with E8M0 block scales
+// (thread: chunk, K-block, 4 ranks, every live token row) and writes them to
+// LDS as A operands: token r, piece p goes to row (r % 4) + 4p of
+// matrix-core op r / 4, so one op takes all three pieces of four tokens.
+// After one barrier every wave runs its tile over the window's chunks with
+// no further synchronization: one op per four live tokens per chunk, the
+// codes of the next kUDepth chunks in flight in a register ring (buffer
+// loads).  The epilogue sums each token's three piece rows, takes
+// sum_i z_ig t'_i off, adds the 8-bit pairs and W x and rounds once to bf16.
+constexpr int kURows = 8;     // token rows per pass
+constexpr int kUWaves = 8;    // waves per block, one 16-row tile each
+constexpr int kU8Max = 2;     // 8-bit pairs whose U weights a lane keeps in registers
+constexpr int kUDepth = 8;    // chunks of codes in flight per lane
+constexpr int kUWin = 16;     // chunks whose A operands are prepared at once (a multiple of kUDepth)
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 struct ULds {
-  uint16_t frag[2][3][4][16][16];   // [slot][piece][lane group][A row][32 bytes]; rows >= the pass's tokens stay 0
-  uint8_t sc[2][16][4];             // E8M0 of piece 0 per (slot, A row, K-block)
-  float cz[kURows];                 // sum_i z t' per token row
+  uint16_t frag[kUWin][2][4][16][16];   // [chunk][op][lane group][A row][32 bytes]
+  uint8_t sc[kUWin][kURows][4];         // E8M0 of the hi piece per (chunk, token row, K-block)
+  float cz[kUWaves][kURows];            // per-wave partial sums of z t' per token row
 };
 
-__global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_t out, int32_t in,
-                                               const int32_t* __restrict__ offs, const int32_t* __restrict__ perm,
-                                               const float* __restrict__ tv, int32_t rs,
-                                               const float* __restrict__ ybase, uint16_t* __restrict__ y) {
+__global__ void __launch_bounds__(kUWaves * 64) k_uside(TenantTable tt, int32_t n, int32_t out, int32_t in,
+                                                        const int32_t* __restrict__ offs,
+                                                        const int32_t* __restrict__ perm,
+                                                        const float* __restrict__ tv, int32_t rs, int32_t T,
+                                                        const float* __restrict__ ybase,
+                                                        uint16_t* __restrict__ y) {
   const int g = blockIdx.x, k = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, q = lane >> 4;
   const int p0 = offs[k], p1 = offs[k + 1];
   if (p0 >= p1) return;
   if (k == n) {  // backbone-only tokens
-    for (int idx = tid; idx < (p1 - p0) * kGroup; idx += 256) {
+    for (int idx = tid; idx < (p1 - p0) * kGroup; idx += kUWaves * 64) {
       const int t = perm[p0 + idx / kGroup];
       const int o = g * kGroup + idx % kGroup;
       y[(size_t)t * out + o] = to_bf16(ybase ? ybase[(size_t)t * out + o] : 0.f);
@@ -628,224 +638,219 @@ __global__ void __launch_bounds__(256) k_uside(TenantTable tt, int32_t n, int32_
   const int tb3 = t_base(tn.n8, tn.n3, 1), tb2 = t_base(tn.n8, tn.n3, 2);
   const int np3 = (int)round_up(seg3.n, 4), np2 = (int)round_up(seg2.n, 4);
   const int nc3 = (seg3.n + 127) / 128, nc = nc3 + (seg2.n + 127) / 128;
-  const int orow[2] = {g * kGroup + wave * 32 + col, g * kGroup + wave * 32 + 16 + col};
-  // fp16 dequantized 8-bit U weights of this lane's two output rows (first kU8Max pairs)
-  float u8w[2][kU8Max];
+  const int gn = out / kGroup;
+  const int orow = g * kGroup + wave * 16 + col;
+  const __amdgpu_buffer_rsrc_t rt =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(tv), 0, T * rs * 4, kBufFlags);
+  const __amdgpu_buffer_rsrc_t ru3 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(seg3.us), 0, gn * np3 * 4, kBufFlags);
+  const __amdgpu_buffer_rsrc_t ru2 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(seg2.us), 0, gn * np2 * 4, kBufFlags);
+  // codes: one buffer per segment; the lane's byte offset of K-block kb of its row
+  const int rw3 = (int)u_row_words(seg3.n, 3), rw2 = (int)u_row_words(seg2.n, 2);
+  const int kbn3 = (seg3.n + kKBlock - 1) / kKBlock, kbn2 = (seg2.n + kKBlock - 1) / kKBlock;
+  const __amdgpu_buffer_rsrc_t rc3 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(seg3.uc), 0, out * 4 * rw3, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rc2 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(seg2.uc), 0, out * 4 * rw2, kBufFlags);
+  auto load = [&](uint32_t (&w)[3], int c) __attribute__((always_inline)) {
+    c = min(c, nc - 1);
+    const bool three = c < nc3;
+    const int b = three ? 3 : 2;
+    const int kbn = three ? kbn3 : kbn2, rw = three ? rw3 : rw2;
+    const int kb = min(4 * (three ? c : c - nc3) + q, kbn - 1);
+    const int wl = rw - (kbn - 1) * b;   // words of the last K-block
+    const int off = ((orow >> 4) * 16 * rw + kb * 16 * b + (orow & 15) * (kb == kbn - 1 ? wl : b)) * 4;
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(three ? rc3 : rc2, off, 0, 0);
+    w[0] = v.x;
+    w[1] = v.y;
+    w[2] = v.z;
+  };
+  // fp16 dequantized 8-bit U weights of this lane's output row (first kU8Max pairs)
+  float u8w[kU8Max];
   {
     const int np8 = (int)round_up(s8.n, 4);
 #pragma unroll
     for (int i = 0; i < kU8Max; ++i) {
       const int ii = min(i, s8.n > 0 ? s8.n - 1 : 0);
       const uint32_t e = s8.n > 0 ? s8.us[(size_t)g * np8 + ii] : 0u;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float code = s8.n > 0 ? (float)s8.uc[(size_t)orow[h] * s8.n + ii] : 0.f;
-        u8w[h][i] = (float)(_Float16)(f16f(e & 0xFFFFu) * (code - f16f(e >> 16)));
-      }
+      const float code = s8.n > 0 ? (float)s8.uc[(size_t)orow * s8.n + ii] : 0.f;
+      u8w[i] = (float)(_Float16)(f16f(e & 0xFFFFu) * (code - f16f(e >> 16)));
     }
   }
-  // A-prep role: token row ai, K-block kb4 of the chunk, ranks m0..m0+3
-  const int ai = tid >> 5, kb4 = (tid >> 3) & 3, part = tid & 7;
+  // rows 12-15 of every op carry no piece: zero once
+  for (int i = tid; i < kUWin * 2 * 4 * 4; i += kUWaves * 64) {
+    const int op = (i >> 4) & 1, lg = (i >> 2) & 3, rr = 12 + (i & 3);
+    uint4* p = reinterpret_cast<uint4*>(S.frag[i >> 5][op][lg][rr]);
+    p[0] = make_uint4(0, 0, 0, 0);
+    p[1] = make_uint4(0, 0, 0, 0);
+  }
+  // A-prep role: chunk cl of the window, K-block kb4, ranks m0..m0+3
+  const int pcl = tid >> 5, kb4 = (tid >> 3) & 3, part = tid & 7;
   const int m0 = kb4 * 32 + part * 4;
   const int lg_even = 2 * (kb4 & 1), hw = (kb4 >= 2 ? 8 : 0) + part;   // lane group, 16-bit word
-  // word offsets of this lane's K-block words in the U code tiles (the formula of
-  // u_kblock_word, split into per-tile constants and a per-chunk term)
-  struct UAddr {
-    int kbn, cb, tile[2], ro[2], rl[2];
-  };
-  auto uaddr = [&](int sn, int bb) __attribute__((always_inline)) {
-    UAddr a;
-    const int rw = (int)u_row_words(sn, bb);
-    a.kbn = (sn + kKBlock - 1) / kKBlock;
-    a.cb = 16 * bb;
-    const int wl = rw - (a.kbn - 1) * bb;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      a.tile[h] = (orow[h] >> 4) * 16 * rw;
-      a.ro[h] = (orow[h] & 15) * bb;
-      a.rl[h] = (orow[h] & 15) * wl;
-    }
-    return a;
-  };
-  const UAddr ad3 = uaddr(seg3.n, 3), ad2 = uaddr(seg2.n, 2);
+  const int ps = col >> 2, tr4 = col & 3;   // MFMA lane's A row: piece ps of token 4 op + tr4
   for (int pb = p0; pb < p1; pb += kURows) {
     const int nt = min(kURows, p1 - pb);
-    const float* trow = tv + (size_t)(pb + min(ai, nt - 1)) * rs;   // clamped; masked below
-    // all of one thread's loads for chunk c (indices past a segment are clamped into it)
-    auto load = [&](UIn& in_, int c) __attribute__((always_inline)) {
-      c = min(c, nc - 1);
-      const bool three = c < nc3;
-      const int cc = three ? c : c - nc3;
-      const int kbn = three ? ad3.kbn : ad2.kbn;
-      const int kb = min(4 * cc + q, kbn - 1);
-      const bool last = kb == kbn - 1;
-      const uint32_t* ub = reinterpret_cast<const uint32_t*>(three ? seg3.uc : seg2.uc);
+    const int nops = (nt + 3) >> 2;   // matrix-core ops per tile and chunk
+    uint32_t cr[kUDepth][3];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int tile = three ? ad3.tile[h] : ad2.tile[h];
-        const int ro = last ? (three ? ad3.rl[h] : ad2.rl[h]) : (three ? ad3.ro[h] : ad2.ro[h]);
-        const uint32_t* wp = ub + tile + kb * (three ? ad3.cb : ad2.cb) + ro;
-        in_.w[h][0] = wp[0];
-        in_.w[h][1] = wp[1];
-        in_.w[h][2] = wp[2];
-      }
-      const int li = cc * 128 + m0;
-      const int np = three ? np3 : np2;
-      in_.us = *reinterpret_cast<const uint4*>((three ? seg3.us : seg2.us) + (size_t)g * np + min(li, np - 4));
-      in_.t = *reinterpret_cast<const float4*>(trow + (three ? tb3 : tb2) + min(li, np - 4));
-    };
-    UIn cr[kUDepth];
-    if (nc > 0) {
-#pragma unroll
-      for (int d = 0; d < kUDepth - 1; ++d) load(cr[d], d);
-    }
-    // zero the A fragments: rows past the pass's tokens stay 0
-    {
-      uint4* fz = reinterpret_cast<uint4*>(&S);
-      for (int i = tid; i < (int)((sizeof(S.frag) + sizeof(S.sc)) / 16); i += 256) fz[i] = make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();
+    for (int d = 0; d < kUDepth; ++d) load(cr[d], d);
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    float czp = 0.f;
-    const bool row_ok = ai < nt;
-    const bool prep_wave = 2 * wave < nt;   // this wave holds token rows 2w, 2w+1
-    // A-prep of chunk c into fragment slot `slot`: t'_i = s_ig t_i as three fp8 pieces
-    auto aprep = [&](int c, int slot, const UIn& cur) __attribute__((always_inline)) {
-      if (!prep_wave) return;
+    // A operands of chunks [cw0, cw0 + wc) for the pass's token rows, in two
+    // halves of four rows (the second only for passes of more than four)
+    auto aprep = [&](int cw0, int wc) __attribute__((always_inline)) {
+      const int c = cw0 + pcl;
+      const bool cok = pcl < wc;
       const bool three = c < nc3;
       const int sn = three ? seg3.n : seg2.n;
-      const int li = (three ? c : c - nc3) * 128 + m0;
-      const uint32_t usw[4] = {cur.us.x, cur.us.y, cur.us.z, cur.us.w};
-      const float tt4[4] = {cur.t.x, cur.t.y, cur.t.z, cur.t.w};
-      float tp[4];
-      float mx = 0.f;
+      const int li = (three ? c : c - nc3) * kGroup + m0;
+      const int pc_l = min(pcl, kUWin - 1);
+      const u32x4 usw = __builtin_bit_cast(
+          u32x4, three ? __builtin_amdgcn_raw_buffer_load_b128(ru3, (g * np3 + li) * 4, 0, 0)
+                       : __builtin_amdgcn_raw_buffer_load_b128(ru2, (g * np2 + li) * 4, 0, 0));
+      for (int h = 0; h < nops; ++h) {
+        f32x4 tt[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bool ok = row_ok && c < nc && li + u < sn;
-        tp[u] = ok ? f16f(usw[u] & 0xFFFFu) * tt4[u] : 0.f;
-        mx = fmaxf(mx, fabsf(tp[u]));
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
-      const int sb = block_scale_byte(mx);
-      const float inv = pow2f(127 - sb), fwd = pow2f(sb - 127);
-      // three fp8 pieces, two values per conversion: the low half of word w[pc]
-      // holds ranks u = 0, 2 (even lane group), the high half ranks 1, 3
-      float r[4] = {tp[0] * inv, tp[1] * inv, tp[2] * inv, tp[3] * inv};
-      float bk[4] = {0.f, 0.f, 0.f, 0.f};
-      uint32_t w[3];
-      float sc_pc = 1.f;
+        for (int r = 0; r < 4; ++r)
+          tt[r] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         rt, ((pb + min(4 * h + r, nt - 1)) * rs + (three ? tb3 : tb2) + li) * 4, 0, 0));
 #pragma unroll
-      for (int pc = 0; pc < 3; ++pc) {
-        int ww = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[2], 0, false);
-        ww = __builtin_amdgcn_cvt_pk_fp8_f32(r[1], r[3], ww, true);
-        w[pc] = (uint32_t)ww;
-        const f32x2 e02 = __builtin_amdgcn_cvt_pk_f32_fp8(ww, false), e13 = __builtin_amdgcn_cvt_pk_f32_fp8(ww, true);
-        bk[0] += e02.x * sc_pc; bk[2] += e02.y * sc_pc; bk[1] += e13.x * sc_pc; bk[3] += e13.y * sc_pc;
-        r[0] = (r[0] - e02.x) * 32.f; r[2] = (r[2] - e02.y) * 32.f;
-        r[1] = (r[1] - e13.x) * 32.f; r[3] = (r[3] - e13.y) * 32.f;
-        sc_pc *= 1.f / 32.f;
-      }
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int r = 4 * h + r4;
+          const bool row_ok = r < nt;
+          float tp[4];
+          float mx = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) czp += f16f(usw[u] >> 16) * (bk[u] * fwd);   // zero for masked ranks and rows
+          for (int u = 0; u < 4; ++u) {
+            const bool ok = row_ok && cok && li + u < sn;
+            tp[u] = ok ? f16f(usw[u] & 0xFFFFu) * tt[r4][u] : 0.f;
+            mx = fmaxf(mx, fabsf(tp[u]));
+          }
+          mx = fmaxf(mx, swz_xor<1>(mx));
+          mx = fmaxf(mx, swz_xor<2>(mx));
+          mx = fmaxf(mx, swz_xor<4>(mx));
+          const int sb = block_scale_byte(mx);
+          const float inv = pow2f(127 - sb), fwd = pow2f(sb - 127);
+          // three fp8 pieces, two values per conversion: the low half of word w[pc]
+          // holds ranks u = 0, 2 (even lane group), the high half ranks 1, 3
+          float rr[4] = {tp[0] * inv, tp[1] * inv, tp[2] * inv, tp[3] * inv};
+          float bk[4] = {0.f, 0.f, 0.f, 0.f};
+          uint32_t w[3];
+          float sc_pc = 1.f;
 #pragma unroll
-      for (int pc = 0; pc < 3; ++pc) {
-        S.frag[slot][pc][lg_even][ai][hw] = (uint16_t)w[pc];
-        S.frag[slot][pc][lg_even + 1][ai][hw] = (uint16_t)(w[pc] >> 16);
-      }
-      if (part == 0) S.sc[slot][ai][kb4] = (uint8_t)sb;
-    };
-    // chunk c: matrix-core ops on slot c % 2, then (while they run) the loads
-    // of chunk c + kUDepth - 1 and the A-prep of chunk c + 1 into the other
-    // slot; one barrier publishes it
-    auto step = [&](int c, int slot, UIn& cur, UIn& nx1, UIn& nxt) __attribute__((always_inline)) {
-      const bool three = c < nc3;
-      const uint4* f0 = reinterpret_cast<const uint4*>(S.frag[slot][0][q][col]);
-      const uint4* f1 = reinterpret_cast<const uint4*>(S.frag[slot][1][q][col]);
-      const uint4* f2 = reinterpret_cast<const uint4*>(S.frag[slot][2][q][col]);
-      const v8i a0 = v8_of(f0[0], f0[1]);
-      const v8i a1 = v8_of(f1[0], f1[1]);
-      const v8i a2 = v8_of(f2[0], f2[1]);
-      const int s0 = S.sc[slot][col][q], s1 = s0 - 5, s2 = s0 - 10;
-      f32x4 d[2];
-      v8i bop[2];
-      const int bs = three ? kScaleFp6Code : kScaleFp4Code;
+          for (int pc = 0; pc < 3; ++pc) {
+            int ww = __builtin_amdgcn_cvt_pk_fp8_f32(rr[0], rr[2], 0, false);
+            ww = __builtin_amdgcn_cvt_pk_fp8_f32(rr[1], rr[3], ww, true);
+            w[pc] = (uint32_t)ww;
+            const f32x2 e02 = __builtin_amdgcn_cvt_pk_f32_fp8(ww, false), e13 = __builtin_amdgcn_cvt_pk_f32_fp8(ww, true);
+            bk[0] += e02.x * sc_pc; bk[2] += e02.y * sc_pc; bk[1] += e13.x * sc_pc; bk[3] += e13.y * sc_pc;
+            rr[0] = (rr[0] - e02.x) * 32.f; rr[2] = (rr[2] - e02.y) * 32.f;
+            rr[1] = (rr[1] - e13.x) * 32.f; rr[3] = (rr[3] - e13.y) * 32.f;
+            sc_pc *= 1.f / 32.f;
+          }
+          float cz = 0.f;   // sum over the thread's ranks of z t' (zero for masked ranks and rows)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        d[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (three) {
-          bop[h] = b_fp6(cur.w[h][0], cur.w[h][1], cur.w[h][2]);
-          d[h] = mma(a0, bop[h], d[h], s0, kFmtFp6, bs);
-          d[h] = mma(a1, bop[h], d[h], s1, kFmtFp6, bs);
-          d[h] = mma(a2, bop[h], d[h], s2, kFmtFp6, bs);
-        } else {
-          bop[h] = b_fp4(cur.w[h][0], cur.w[h][1]);
-          d[h] = mma(a0, bop[h], d[h], s0, kFmtFp4, bs);
-          d[h] = mma(a1, bop[h], d[h], s1, kFmtFp4, bs);
-          d[h] = mma(a2, bop[h], d[h], s2, kFmtFp4, bs);
+          for (int u = 0; u < 4; ++u) cz += f16f(usw[u] >> 16) * (bk[u] * fwd);
+          cz += swz_xor<1>(cz);
+          cz += swz_xor<2>(cz);
+          cz += swz_xor<4>(cz);
+          cz += swz_xor<8>(cz);
+          cz += swz_xor<16>(cz);
+          const float cz_hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cz), 32));   // lanes 32-63
+          if (lane == 0) S.cz[wave][r] += cz + cz_hi;
+          if (cok) {
+#pragma unroll
+            for (int pc = 0; pc < 3; ++pc) {
+              S.frag[pc_l][h][lg_even][r4 + 4 * pc][hw] = (uint16_t)w[pc];
+              S.frag[pc_l][h][lg_even + 1][r4 + 4 * pc][hw] = (uint16_t)(w[pc] >> 16);
+            }
+            if (part == 0) S.sc[pc_l][r][kb4] = (uint8_t)sb;
+          }
+          __builtin_amdgcn_sched_barrier(0);   // one token row at a time: bounded register use
         }
       }
-      load(nxt, c + kUDepth - 1);
-      aprep(c + 1, slot ^ 1, nx1);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        hold(d[h], a0, a1, a2, bop[h], s0, s1, s2, bs);
-        acc[h] += d[h];
-      }
-      __syncthreads();
     };
-    if (nc > 0) {
-      aprep(0, 0, cr[0]);
+    // chunk c (window-local cl): matrix-core ops with the codes in cur, then
+    // the loads of chunk c + kUDepth into cur
+    auto step = [&](int c, int cl, uint32_t (&cur)[3]) __attribute__((always_inline)) {
+      const bool three = c < nc3;
+      v8i a[2];
+      int sa[2];
+#pragma unroll
+      for (int op = 0; op < 2; ++op) {
+        const uint4* f = reinterpret_cast<const uint4*>(S.frag[cl][op][q][col]);
+        a[op] = v8_of(f[0], f[1]);
+        sa[op] = ps < 3 ? (int)S.sc[cl][4 * op + tr4][q] - 5 * ps : 127;
+      }
+      const v8i bop = three ? b_fp6(cur[0], cur[1], cur[2]) : b_fp4(cur[0], cur[1]);
+      f32x4 d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      if (three) {
+        d[0] = mma(a[0], bop, d[0], sa[0], kFmtFp6, kScaleFp6Code);
+        if (nops > 1) d[1] = mma(a[1], bop, d[1], sa[1], kFmtFp6, kScaleFp6Code);
+      } else {
+        d[0] = mma(a[0], bop, d[0], sa[0], kFmtFp4, kScaleFp4Code);
+        if (nops > 1) d[1] = mma(a[1], bop, d[1], sa[1], kFmtFp4, kScaleFp4Code);
+      }
+      hold(d[0], a[0], a[1], bop, sa[0], sa[1], three ? kScaleFp6Code : kScaleFp4Code);
+      hold(d[1], a[0], a[1], bop, sa[0], sa[1], three ? kScaleFp6Code : kScaleFp4Code);
+      load(cur, c + kUDepth);
+      acc[0] += d[0];
+      acc[1] += d[1];
+      asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));   // sums land here, not deferred to the end
+    };
+    __syncthreads();   // the previous pass's operands and sums are consumed
+    if (lane < kURows) S.cz[wave][lane] = 0.f;   // this wave's z t' sums of the pass
+    for (int cw0 = 0; cw0 < nc; cw0 += kUWin) {
+      const int wc = min(kUWin, nc - cw0);
+      if (cw0 > 0) __syncthreads();   // the previous window's operands are consumed
+      aprep(cw0, wc);
       __syncthreads();
-    }
-    int c0 = 0;
-    for (; c0 + kUDepth <= nc; c0 += kUDepth) {
-      step(c0 + 0, 0, cr[0], cr[1], cr[3]);
-      step(c0 + 1, 1, cr[1], cr[2], cr[0]);
-      step(c0 + 2, 0, cr[2], cr[3], cr[1]);
-      step(c0 + 3, 1, cr[3], cr[0], cr[2]);
-    }
-    // tail: fewer than kUDepth chunks left (uniform guards)
-    if (c0 + 0 < nc) step(c0 + 0, 0, cr[0], cr[1], cr[3]);
-    if (c0 + 1 < nc) step(c0 + 1, 1, cr[1], cr[2], cr[0]);
-    if (c0 + 2 < nc) step(c0 + 2, 0, cr[2], cr[3], cr[1]);
-    // ---- epilogue: sum_i z t' per token row, 8-bit pairs, W x, one rounding
+      int c0 = cw0;
+      for (; c0 + kUDepth <= cw0 + wc; c0 += kUDepth) {
 #pragma unroll
-    for (int m = 1; m < 32; m <<= 1) czp += __shfl_xor(czp, m, 64);   // the 32 threads of row ai
-    if ((tid & 31) == 0 && ai < kURows) S.cz[ai] = czp;
+        for (int d = 0; d < kUDepth; ++d) step(c0 + d, c0 + d - cw0, cr[d]);
+      }
+      // tail of the last window: fewer than kUDepth chunks (uniform guards)
+#pragma unroll
+      for (int d = 0; d < kUDepth - 1; ++d)
+        if (c0 + d < cw0 + wc) step(c0 + d, c0 + d - cw0, cr[d]);
+    }
+    // ---- epilogue: each token's three piece rows, sum_i z t' per token row, 8-bit pairs, W x, one rounding
+    f32x4 tot[2];
+#pragma unroll
+    for (int op = 0; op < 2; ++op) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = acc[op][r] + swz_xor<16>(acc[op][r]);   // pieces 0+1, 2+(zero row)
+        tot[op][r] = v + __shfl_xor(v, 32, 64);
+      }
+    }
     __syncthreads();
-    float yb[2][4], t8[4][kU8Max];
-    int tk[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rw = min(4 * q + r, nt - 1);
-      tk[r] = perm[pb + rw];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) yb[h][r] = ybase ? ybase[(size_t)tk[r] * out + orow[h]] : 0.f;
-#pragma unroll
-      for (int i = 0; i < kU8Max; ++i) t8[r][i] = tv[(size_t)(pb + rw) * rs + min(i, s8.n > 0 ? s8.n - 1 : 0)];
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    if (q < 2) {   // lane group q writes the tokens of op q
+      const f32x4 tq = q == 0 ? tot[0] : tot[1];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int rw = 4 * q + r;
         if (rw < nt) {
-          float v = acc[h][r] - S.cz[rw];
+          const int tk = perm[pb + rw];
+          float cz = 0.f;
+#pragma unroll
+          for (int w8 = 0; w8 < kUWaves; ++w8) cz += S.cz[w8][rw];
+          float v = tq[r] - cz;
 #pragma unroll
           for (int i = 0; i < kU8Max; ++i)
-            if (i < s8.n) v += u8w[h][i] * t8[r][i];
+            if (i < s8.n) v += u8w[i] * tv[(size_t)(pb + rw) * rs + i];
           for (int i = kU8Max; i < s8.n; ++i) {   // more 8-bit pairs than kept in registers
             const uint32_t e = s8.us[(size_t)g * round_up(s8.n, 4) + i];
-            const float uh = (float)(_Float16)(f16f(e & 0xFFFFu) * ((float)s8.uc[(size_t)orow[h] * s8.n + i] - f16f(e >> 16)));
+            const float uh = (float)(_Float16)(f16f(e & 0xFFFFu) * ((float)s8.uc[(size_t)orow * s8.n + i] - f16f(e >> 16)));
             v += uh * tv[(size_t)(pb + rw) * rs + i];
           }
-          y[(size_t)tk[r] * out + orow[h]] = to_bf16(v + yb[h][r]);
+          y[(size_t)tk * out + orow] = to_bf16(v + (ybase ? ybase[(size_t)tk * out + orow] : 0.f));
         }
       }
     }
-    __syncthreads();   // S.cz and the fragments are rewritten by the next token pass
   }
 }
 
@@ -881,8 +886,8 @@ int launch_apply(const ApplyArgs& a) {
                        *a.tenants, a.out, a.in,
                        a.x, offs, perm, xf, xsc, xsum, tv, a.wl.rs);
   mark(DC_STAGE_USIDE);
-  hipLaunchKernelGGL(k_uside, dim3((unsigned)(a.out / kGroup), (unsigned)(a.n + 1)), dim3(256), 0, st, *a.tenants,
-                     a.n, a.out, a.in, offs, perm, tv, a.wl.rs, ybase, a.y);
+  hipLaunchKernelGGL(k_uside, dim3((unsigned)(a.out / kGroup), (unsigned)(a.n + 1)), dim3(kUWaves * 64), 0, st,
+                     *a.tenants, a.n, a.out, a.in, offs, perm, tv, a.wl.rs, a.T, ybase, a.y);
   mark(DC_STAGE_COUNT);
   return (int)hipGetLastError();
 }
