@@ -226,6 +226,24 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
   if (item >= (size_t)T * gi_n) return;
   const int lane = tid & 63;
   const int t = (int)(item / gi_n), gi = (int)(item % gi_n);
+  // sorted position of token t, as block 0 routes it (bucket, then token
+  // order): the fragments, scales and sums are stored in that order
+  int ps = t;
+  if (mode == 1) {
+    auto bucket = [&](int u) { const int kk = ids[u]; return (kk < 0 || kk >= n) ? n : kk; };
+    const int bt = bucket(t);
+    ps = 0;
+    for (int c0 = 0; c0 < T; c0 += 64) {
+      const int u = c0 + lane;
+      bool before = false;
+      if (u < T) {
+        const int b = bucket(u);
+        before = b < bt || (b == bt && u < t);
+      }
+      ps += __popcll(__ballot(before));
+    }
+  }
+  const size_t sitem = (size_t)ps * gi_n + gi;
   const uint16_t* xr = x + (size_t)t * in + (size_t)gi * kGroup;
   const uint16_t x0 = xr[lane], x1 = xr[lane + 64];
   const float v0 = __uint_as_float((uint32_t)x0 << 16);   // element j = lane (chunk lane/32)
@@ -246,7 +264,7 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
     m1 = fmaxf(m1, __shfl_xor(m1, s, 64));
   }
   const int b0 = block_scale_byte(m0), b1 = block_scale_byte(m1);
-  uint8_t* fr = xf + item * kXFrag;
+  uint8_t* fr = xf + sitem * kXFrag;
   {
     const float v = v0 * pow2f(127 - b0);
     const uint32_t h = fp8_of(v);
@@ -271,8 +289,8 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
   // chunk scales: lanes 0..31 hold chunks 0 (b0) and 2 (b1), lanes 32..63 chunks 1 and 3
   const int c1 = __shfl(b0, 32, 64), c3 = __shfl(b1, 32, 64);
   if (lane == 0) {
-    xsc[item] = (uint32_t)b0 | ((uint32_t)c1 << 8) | ((uint32_t)b1 << 16) | ((uint32_t)c3 << 24);
-    xsum[item] = s;
+    xsc[sitem] = (uint32_t)b0 | ((uint32_t)c1 << 8) | ((uint32_t)b1 << 16) | ((uint32_t)c3 << 24);
+    xsum[sitem] = s;
   }
 }
 
@@ -335,41 +353,47 @@ __device__ __forceinline__ void v_load_grp(VGrp<B>& c, const VBuf& p, int np, in
   }
 }
 
-// Stage the x fragments of token rows [pb, pb + kVRows) for groups
-// [g0, g0 + kVSlice) into LDS.  Thread tid moves int4 (tid & 15) of the
-// fragment of row (tid >> 4) & 7 (token tok) for groups (tid >> 7) + 2u;
-// threads < 128 move the scale word and group sum of row tid & 7 (token
-// stok) and group (tid >> 3) & 15.  Rows past the pass repeat its last token
-// and are never read; groups past the input repeat its last group.
-__device__ __forceinline__ void v_stage_x(VLds& S, const uint8_t* __restrict__ xf, const uint32_t* __restrict__ xsc,
-                                          const float* __restrict__ xsum, int gi_n, int g0, int tok, int stok) {
+// x fragments, scale words and group sums of sorted rows [pb, pb + kVRows)
+// for groups [g0, g0 + kVSlice), staged into LDS in two steps so that the
+// loads can go out ahead of the code ring.  Thread tid moves int4 (tid & 15)
+// of the fragment of row (tid >> 4) & 7 for groups (tid >> 7) + 2u; threads
+// < 128 move the scale word and group sum of row tid & 7 and group
+// (tid >> 3) & 15.  Rows past the pass repeat its last row and are never
+// read; groups past the input repeat its last group.
+struct VStage {
+  i32x4 v[kVSlice / 2];
+  uint32_t scw;
+  float xsv;
+};
+
+__device__ __forceinline__ void v_stage_load(VStage& st, const uint8_t* __restrict__ xf,
+                                             const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
+                                             int gi_n, int g0, int pb, int nt) {
   const int tid = threadIdx.x;
   const int k16 = tid & 15, rw = (tid >> 4) & 7, gh = tid >> 7;
-  i32x4 v[kVSlice / 2];
+  const size_t row = (size_t)(pb + min(rw, nt - 1)) * gi_n;
 #pragma unroll
   for (int u = 0; u < kVSlice / 2; ++u) {
     const int gi = min(g0 + gh + 2 * u, gi_n - 1);
-    v[u] = reinterpret_cast<const i32x4*>(xf + ((size_t)tok * gi_n + gi) * kXFrag)[k16];
+    st.v[u] = reinterpret_cast<const i32x4*>(xf + (row + gi) * kXFrag)[k16];
   }
   const int sr = tid & 7, sgl = (tid >> 3) & (kVSlice - 1);
-  const int gs = min(g0 + sgl, gi_n - 1);
-  const uint32_t scw = xsc[(size_t)stok * gi_n + gs];
-  const float xsv = xsum[(size_t)stok * gi_n + gs];
-#pragma unroll
-  for (int u = 0; u < kVSlice / 2; ++u)
-    S.frag[gh + 2 * u][rw][k16] = make_int4(v[u].x, v[u].y, v[u].z, v[u].w);
-  if (tid < kVRows * kVSlice) {
-    S.sc[sgl][sr] = scw;
-    S.xs[sgl][sr] = xsv;
-  }
+  const size_t srow = (size_t)(pb + min(sr, nt - 1)) * gi_n + min(g0 + sgl, gi_n - 1);
+  st.scw = xsc[srow];
+  st.xsv = xsum[srow];
 }
 
-// Token of the fragment row and of the scale row this thread stages for the
-// pass starting at sorted position pb.
-__device__ __forceinline__ void v_stage_tokens(const int32_t* __restrict__ perm, int pb, int nt, int& tok, int& stok) {
+__device__ __forceinline__ void v_stage_store(VLds& S, const VStage& st) {
   const int tid = threadIdx.x;
-  tok = perm[pb + min((tid >> 4) & 7, nt - 1)];
-  stok = perm[pb + min(tid & 7, nt - 1)];
+  const int k16 = tid & 15, rw = (tid >> 4) & 7, gh = tid >> 7;
+#pragma unroll
+  for (int u = 0; u < kVSlice / 2; ++u)
+    S.frag[gh + 2 * u][rw][k16] = make_int4(st.v[u].x, st.v[u].y, st.v[u].z, st.v[u].w);
+  if (tid < kVRows * kVSlice) {
+    const int sr = tid & 7, sgl = (tid >> 3) & (kVSlice - 1);
+    S.sc[sgl][sr] = st.scw;
+    S.xs[sgl][sr] = st.xsv;
+  }
 }
 
 __device__ __forceinline__ void hold2(f32x4& d0, f32x4& d1, const v8i& a, const v8i& b0, const v8i& b1, int sa,
@@ -397,8 +421,6 @@ __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, i
   const int glast = g0 + gn - 1;
   const int np = (int)round_up(sg.n, 4);
   const int npass = (p1 - p0 + kVRows - 1) / kVRows;
-  int tok, stok;
-  v_stage_tokens(perm, p0, min(kVRows, p1 - p0), tok, stok);
   VBuf P;
   P.rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sg.vc), 0, sg.n * gi_n * 16 * B, kBufFlags);
   P.rz = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(sg.vs), 0, gi_n * np * 4, kBufFlags);
@@ -418,14 +440,15 @@ __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, i
   for (int ip = 0; ip < npass; ++ip) {
     const int pb = p0 + ip * kVRows;
     const int nt = min(kVRows, p1 - pb);
+    VStage st;
+    v_stage_load(st, xf, xsc, xsum, gi_n, g0, pb, nt);   // ahead of the ring: vmcnt is in order
     VGrp<B> ring[kDepth] = {};   // defined on every path: no values carried across passes
     if (live_wave) {
 #pragma unroll
       for (int d = 0; d < kDepth; ++d) v_load_grp<B>(ring[d], P, np, min(g0 + d, glast));
     }
     __syncthreads();   // LDS reuse across passes
-    v_stage_x(S, xf, xsc, xsum, gi_n, g0, tok, stok);
-    if (ip + 1 < npass) v_stage_tokens(perm, pb + kVRows, min(kVRows, p1 - pb - kVRows), tok, stok);
+    v_stage_store(S, st);
     __syncthreads();
     if (!live_wave) continue;
     const bool live = tr < nt;
@@ -601,7 +624,7 @@ __global__ void __launch_bounds__(256) k_vside(TenantTable tt, int32_t out, int3
 constexpr int kURows = 8;     // token rows per pass
 constexpr int kUWaves = 8;    // waves per block, one 16-row tile each
 constexpr int kU8Max = 2;     // 8-bit pairs whose U weights a lane keeps in registers
-constexpr int kUDepth = 8;    // chunks of codes in flight per lane
+constexpr int kUDepth = 4;    // chunks of codes in flight per lane
 constexpr int kUWin = 16;     // chunks whose A operands are prepared at once (a multiple of kUDepth)
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -666,9 +689,10 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(TenantTable tt, int32_t 
     w[1] = v.y;
     w[2] = v.z;
   };
-  // fp16 dequantized 8-bit U weights of this lane's output row (first kU8Max pairs)
+  // fp16 dequantized 8-bit U weights of this lane's output row (first kU8Max
+  // pairs); loaded behind the first window's A-prep inputs and codes
   float u8w[kU8Max];
-  {
+  auto load_u8w = [&]() __attribute__((always_inline)) {
     const int np8 = (int)round_up(s8.n, 4);
 #pragma unroll
     for (int i = 0; i < kU8Max; ++i) {
@@ -677,7 +701,7 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(TenantTable tt, int32_t 
       const float code = s8.n > 0 ? (float)s8.uc[(size_t)orow * s8.n + ii] : 0.f;
       u8w[i] = (float)(_Float16)(f16f(e & 0xFFFFu) * (code - f16f(e >> 16)));
     }
-  }
+  };
   // rows 12-15 of every op carry no piece: zero once
   for (int i = tid; i < kUWin * 2 * 4 * 4; i += kUWaves * 64) {
     const int op = (i >> 4) & 1, lg = (i >> 2) & 3, rr = 12 + (i & 3);
@@ -694,12 +718,12 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(TenantTable tt, int32_t 
     const int nt = min(kURows, p1 - pb);
     const int nops = (nt + 3) >> 2;   // matrix-core ops per tile and chunk
     uint32_t cr[kUDepth][3];
-#pragma unroll
-    for (int d = 0; d < kUDepth; ++d) load(cr[d], d);
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     // A operands of chunks [cw0, cw0 + wc) for the pass's token rows, in two
-    // halves of four rows (the second only for passes of more than four)
-    auto aprep = [&](int cw0, int wc) __attribute__((always_inline)) {
+    // halves of four rows (the second only for passes of more than four).
+    // The first window's loads go out ahead of the code ring's first loads
+    // (vmcnt is in order: behind them they would wait for the whole burst).
+    auto aprep = [&](int cw0, int wc, bool first) __attribute__((always_inline)) {
       const int c = cw0 + pcl;
       const bool cok = pcl < wc;
       const bool three = c < nc3;
@@ -716,15 +740,20 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(TenantTable tt, int32_t 
           tt[r] = __builtin_bit_cast(
               f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                          rt, ((pb + min(4 * h + r, nt - 1)) * rs + (three ? tb3 : tb2) + li) * 4, 0, 0));
+        if (first && h == 0) {
+#pragma unroll
+          for (int d = 0; d < kUDepth; ++d) load(cr[d], d);
+          if (pb == p0) load_u8w();
+        }
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int r = 4 * h + r4;
-          const bool row_ok = r < nt;
+          if (r >= nt) break;   // rows past the pass's tokens: their D rows are never read
           float tp[4];
           float mx = 0.f;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const bool ok = row_ok && cok && li + u < sn;
+            const bool ok = cok && li + u < sn;
             tp[u] = ok ? f16f(usw[u] & 0xFFFFu) * tt[r4][u] : 0.f;
             mx = fmaxf(mx, fabsf(tp[u]));
           }
@@ -802,10 +831,11 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(TenantTable tt, int32_t 
     };
     __syncthreads();   // the previous pass's operands and sums are consumed
     if (lane < kURows) S.cz[wave][lane] = 0.f;   // this wave's z t' sums of the pass
+    if (nc == 0 && pb == p0) load_u8w();
     for (int cw0 = 0; cw0 < nc; cw0 += kUWin) {
       const int wc = min(kUWin, nc - cw0);
       if (cw0 > 0) __syncthreads();   // the previous window's operands are consumed
-      aprep(cw0, wc);
+      aprep(cw0, wc, cw0 == 0);
       __syncthreads();
       int c0 = cw0;
       for (; c0 + kUDepth <= cw0 + wc; c0 += kUDepth) {
