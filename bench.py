@@ -154,6 +154,43 @@ def cpu_baseline(trs, synth, budget_s=20.0):
                                                                           time.time() - t_start)}
 
 
+def counter_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed hardware-counter
+    summary, scaled by its copy calibration; None when there is none for this
+    kernel or its source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_bytes_decode_c2.txt")
+    src = os.path.join(ROOT, "tenant_rank_serving_amd", "csrc", "k_mx.hip")
+    try:
+        kv = {}
+        for line in open(path):
+            if ":" in line:
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip().split()[0] if v.strip() else ""
+        if kv.get("kernel") != "k_" + kernel:
+            return None
+        if kv.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+            return None
+        return int((float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_factor"]) +
+                    float(kv["write_kib_per_dispatch"]) * float(kv["write_factor"])) * 1024)
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mib=256, reps=3):
+    """A plain copy of `mib` MiB, `reps` times: under a hardware-counter run its
+    per-dispatch fetch and write byte counts give the scale of the counters."""
+    import torch
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "dispatches": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,7 +198,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the path shards by tenant with no collective, and "
               "this build runs on a single MI355X (--gpus 1).", file=sys.stderr)
@@ -203,7 +245,9 @@ def main():
                 for l in range(args.layers) for m in range(len(specs))]
 
     def layered_step(fused):
-        """The step as per-layer waves: returns a function that enqueues it."""
+        """The step as per-layer waves: returns run(marks=None), which enqueues
+        it; marks (one event argument per call, in plan order) makes every call
+        record HIP events on its own stream around one stage."""
         plan = []
         for l in range(args.layers):
             for wv in waves:
@@ -214,45 +258,45 @@ def main():
                 joins = [torch.cuda.Event() for _ in wv[1:]]
                 plan.append((entry, fork, joins))
 
-        def run():
+        def run(marks=None):
             main = streams[0]
+            i = 0
             for entry, fork, joins in plan:
                 if fork is not None:
                     fork.record(main)
                     for si, _ in entry[1:]:
                         streams[si].wait_event(fork)
                 for _, c in entry:
-                    c()
+                    if marks is None:
+                        c()
+                    else:
+                        c.timed_array(marks[i])
+                    i += 1
                 for (si, _), ev in zip(entry[1:], joins):
                     ev.record(streams[si])
                     main.wait_event(ev)
+        run.ncalls = sum(len(e) for e, _, _ in plan)
         return run
 
     # bytes per step: packed deltas of the touched tenants (algorithmic), backbone
     delta_bytes = args.layers * len(touched) * sum(trs.dc_algorithmic_bytes(sp) for sp in specs)
     base_bytes = args.layers * sum(sp[0] * sp[1] * 2 for sp in specs)
 
-    def timed_steps(run, steps, warmup):
+    def timed_steps(run, steps, warmup, marks=None):
         for _ in range(warmup):
             run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(steps):
-            run()
+        for k in range(steps):
+            run(None if marks is None else marks[k])
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    results = {}
-    for mode in ("fused", "delta"):
-        run = layered_step(mode == "fused")
-        log("timing %s step: warmup %d, steps %d" % (mode, args.warmup, args.steps))
-        results[mode] = timed_steps(run, args.steps, args.warmup)
-        log("%s: %.3f ms/step" % (mode, results[mode]))
-
-    # Per-kernel durations: one more pass of the fused step with HIP events
-    # recorded between the stages of every call, on the launch stream.
+    # Per-stage durations: one untimed pass of the fused step, calls in
+    # sequence, HIP events between the stages of every call; picks the
+    # dominant kernel (largest total time).
     cl = calls(True)
     evs = [[hip.event() for _ in range(len(trs.STAGES) + 1)] for _ in cl]
     for c, ev in zip(cl, evs):
@@ -267,7 +311,30 @@ def main():
             hip.destroy(e)
     stage_avg = {s: float(np.mean(v)) for s, v in stage_ms.items()}
     stage_tot = {s: float(np.sum(v)) for s, v in stage_ms.items()}
-    log("stage averages (ms/call): " + ", ".join("%s %.4f" % kv for kv in stage_avg.items()))
+    log("stage averages (ms/call, calls in sequence): " + ", ".join("%s %.4f" % kv for kv in stage_avg.items()))
+    heavy = ("base", "vside", "uside")
+    dom = max(heavy, key=lambda s: stage_tot[s])
+    dom_i = trs.STAGES.index(dom)
+
+    results, dom_live = {}, {}
+    for mode in ("fused", "delta"):
+        run = layered_step(mode == "fused")
+        # the timed steps record two events per call around the dominant kernel,
+        # on the stream that call runs on
+        ev = [[(hip.event(), hip.event()) for _ in range(run.ncalls)] for _ in range(args.steps)]
+        marks = [[trs.MultitenantCall.event_array([a if i == dom_i else (b if i == dom_i + 1 else None)
+                                                   for i in range(len(trs.STAGES) + 1)])
+                  for a, b in step_ev] for step_ev in ev]
+        log("timing %s step: warmup %d, steps %d" % (mode, args.warmup, args.steps))
+        results[mode] = timed_steps(run, args.steps, args.warmup, marks)
+        d = [hip.elapsed_ms(a, b) for step_ev in ev for a, b in step_ev if a is not None]
+        dom_live[mode] = float(np.mean([x for x in d if x > 0])) if d else float("nan")
+        for step_ev in ev:
+            for a, b in step_ev:
+                hip.destroy(a)
+                hip.destroy(b)
+        log("%s: %.3f ms/step; %s kernel %.4f ms per launch (timed region)" % (mode, results[mode], dom,
+                                                                               dom_live[mode]))
 
     # Algorithmic bytes per launch of each heavy stage, averaged over calls.
     def side_bytes(sp, side):
@@ -286,12 +353,14 @@ def main():
         "base": np.mean([specs[i % len(specs)][0] * specs[i % len(specs)][1] * 2 + T * specs[i % len(specs)][1] * 2
                          for i in range(ncalls)]),
     }
-    dom = max(per_launch, key=lambda s: stage_tot[s])
-    achieved = per_launch[dom] / (stage_avg[dom] * 1e-3) / 1e9
+    # dom_live: the kernel's average duration per launch inside the timed
+    # (fused) steps, measured with HIP events on each call's stream
+    achieved = per_launch[dom] / (dom_live["fused"] * 1e-3) / 1e9
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "bytes_per_launch": int(per_launch[dom]), "avg_launch_ms": round(stage_avg[dom], 5),
-            "stages_avg_ms": {s: round(v, 5) for s, v in stage_avg.items()}}
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(dom),
+            "bytes_per_launch": int(per_launch[dom]), "avg_launch_ms": round(dom_live["fused"], 5),
+            "avg_launch_ms_in_sequence": round(stage_avg[dom], 5),
+            "stages_avg_ms_in_sequence": {s: round(v, 5) for s, v in stage_avg.items()}}
 
     ms = results["fused"]
     ms_d = results["delta"]

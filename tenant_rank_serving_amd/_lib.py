@@ -275,7 +275,14 @@ class MultitenantCall:
             raise DcError(st, "dc_apply_multitenant")
 
     def timed(self, events) -> None:
-        ev = (_P * (len(STAGES) + 1))(*[None if e is None else int(e) for e in events])
+        self.timed_array(self.event_array(events))
+
+    @staticmethod
+    def event_array(events):
+        """The events argument of dc_apply_multitenant_timed, marshalled once."""
+        return (_P * (len(STAGES) + 1))(*[None if e is None else int(e) for e in events])
+
+    def timed_array(self, ev) -> None:
         st = self._fn_t(*self.args, ev)
         if st != DC_OK:
             raise DcError(st, "dc_apply_multitenant_timed")
