@@ -611,27 +611,28 @@ __global__ void __launch_bounds__(256) k_vside(TenantTable tt, int32_t out, int3
 // (one scale group) of tenant k = blockIdx.y (n = the backbone-only bucket),
 // all ranks, tokens in passes of up to kURows.  Wave w takes the 16-row tile
 // 16w..16w+15.  The ranks go in 128-rank chunks, 3-bit chunks first.  Per
-// pass, for a window of up to kUWin chunks at a time, the whole block first
-// turns t'_i = s_ig t_i into three fp8 pieces with E8M0 block scales
-// (thread: chunk, K-block, 4 ranks, every live token row) and writes them to
-// LDS as A operands: token r, piece p goes to row (r % 4) + 4p of
-// matrix-core op r / 4, so one op takes all three pieces of four tokens.
-// After one barrier every wave runs its tile over the window's chunks with
-// no further synchronization: one op per four live tokens per chunk, the
-// codes of the next kUDepth chunks in flight in a register ring (buffer
-// loads).  The epilogue sums each token's three piece rows, takes
-// sum_i z_ig t'_i off, adds the 8-bit pairs and W x and rounds once to bf16.
+// pass, for a window of chunks at a time, the whole block first turns
+// t'_i = s_ig t_i into three fp8 pieces with E8M0 block scales (thread:
+// chunk, K-block, 4 ranks, four token rows) and writes them to LDS as A
+// operands: token r, piece p goes to row (r % 4) + 4p of matrix-core op
+// r / 4, so one op takes all three pieces of four tokens.  After one barrier
+// every wave runs its tile over the window's chunks with no further
+// synchronization, one op per four live tokens per chunk, the codes of the
+// next kUDepth chunks in flight in a register ring (buffer loads on one
+// resource for the tenant's whole buffer, the region in the uniform offset).
+// The epilogue sums each token's three piece rows, takes sum_i z_ig t'_i
+// off, adds the 8-bit pairs and W x and rounds once to bf16.
 constexpr int kURows = 8;     // token rows per pass
 constexpr int kUWaves = 8;    // waves per block, one 16-row tile each
 constexpr int kU8Max = 2;     // 8-bit pairs whose U weights a lane keeps in registers
 constexpr int kUDepth = 4;    // chunks of codes in flight per lane
-constexpr int kUWin = 16;     // chunks whose A operands are prepared at once (a multiple of kUDepth)
+constexpr int kUWin = 16;     // A operands per window (chunks x ops): 16 chunks with one op, 8 with two
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 struct ULds {
-  uint16_t frag[kUWin][2][4][16][16];   // [chunk][op][lane group][A row][32 bytes]
-  uint8_t sc[kUWin][kURows][4];         // E8M0 of the hi piece per (chunk, token row, K-block)
-  float cz[kUWaves][kURows];            // per-wave partial sums of z t' per token row
+  uint16_t frag[kUWin][4][16][16];   // [chunk * ops + op][lane group][A row][32 bytes]
+  uint8_t sc[kUWin][kURows][4];      // E8M0 of the hi piece per (chunk, token row, K-block)
+  float cz[kUWaves][kURows];         // per-wave partial sums of z t' per token row
 };
 
 __global__ void __launch_bounds__(kUWaves * 64) k_uside(TenantTable tt, int32_t n, int32_t out, int32_t in,
@@ -665,17 +666,14 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(TenantTable tt, int32_t 
   const int orow = g * kGroup + wave * 16 + col;
   const __amdgpu_buffer_rsrc_t rt =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(tv), 0, T * rs * 4, kBufFlags);
-  const __amdgpu_buffer_rsrc_t ru3 =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(seg3.us), 0, gn * np3 * 4, kBufFlags);
-  const __amdgpu_buffer_rsrc_t ru2 =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(seg2.us), 0, gn * np2 * 4, kBufFlags);
-  // codes: one buffer per segment; the lane's byte offset of K-block kb of its row
+  // the tenant's whole packed buffer: code and scale regions go in the uniform offset
+  const __amdgpu_buffer_rsrc_t rten =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(tn.base), 0, (int)L.total, kBufFlags);
+  const int oc3 = (int)L.off[DC_REG_UC3], oc2 = (int)L.off[DC_REG_UC2];
+  const int ou3 = (int)L.off[DC_REG_US3] + g * np3 * 4, ou2 = (int)L.off[DC_REG_US2] + g * np2 * 4;
+  // the lane's byte offset of K-block kb of its row in the 3- or 2-bit code region
   const int rw3 = (int)u_row_words(seg3.n, 3), rw2 = (int)u_row_words(seg2.n, 2);
   const int kbn3 = (seg3.n + kKBlock - 1) / kKBlock, kbn2 = (seg2.n + kKBlock - 1) / kKBlock;
-  const __amdgpu_buffer_rsrc_t rc3 =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(seg3.uc), 0, out * 4 * rw3, kBufFlags);
-  const __amdgpu_buffer_rsrc_t rc2 =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(seg2.uc), 0, out * 4 * rw2, kBufFlags);
   auto load = [&](uint32_t (&w)[3], int c) __attribute__((always_inline)) {
     c = min(c, nc - 1);
     const bool three = c < nc3;
@@ -684,7 +682,7 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(TenantTable tt, int32_t 
     const int kb = min(4 * (three ? c : c - nc3) + q, kbn - 1);
     const int wl = rw - (kbn - 1) * b;   // words of the last K-block
     const int off = ((orow >> 4) * 16 * rw + kb * 16 * b + (orow & 15) * (kb == kbn - 1 ? wl : b)) * 4;
-    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(three ? rc3 : rc2, off, 0, 0);
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rten, off, three ? oc3 : oc2, 0);
     w[0] = v.x;
     w[1] = v.y;
     w[2] = v.z;
@@ -703,137 +701,132 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(TenantTable tt, int32_t 
     }
   };
   // rows 12-15 of every op carry no piece: zero once
-  for (int i = tid; i < kUWin * 2 * 4 * 4; i += kUWaves * 64) {
-    const int op = (i >> 4) & 1, lg = (i >> 2) & 3, rr = 12 + (i & 3);
-    uint4* p = reinterpret_cast<uint4*>(S.frag[i >> 5][op][lg][rr]);
+  for (int i = tid; i < kUWin * 4 * 4; i += kUWaves * 64) {   // i = operand:4 lane group:2 row:2
+    uint4* p = reinterpret_cast<uint4*>(S.frag[i >> 4][(i >> 2) & 3][12 + (i & 3)]);
     p[0] = make_uint4(0, 0, 0, 0);
     p[1] = make_uint4(0, 0, 0, 0);
   }
-  // A-prep role: chunk cl of the window, K-block kb4, ranks m0..m0+3
-  const int pcl = tid >> 5, kb4 = (tid >> 3) & 3, part = tid & 7;
+  // A-prep role: K-block kb4 and ranks m0..m0+3 of a chunk (which chunk and
+  // rows depend on the pass: see aprep)
+  const int kb4 = (tid >> 3) & 3, part = tid & 7;
   const int m0 = kb4 * 32 + part * 4;
   const int lg_even = 2 * (kb4 & 1), hw = (kb4 >= 2 ? 8 : 0) + part;   // lane group, 16-bit word
   const int ps = col >> 2, tr4 = col & 3;   // MFMA lane's A row: piece ps of token 4 op + tr4
   for (int pb = p0; pb < p1; pb += kURows) {
     const int nt = min(kURows, p1 - pb);
     const int nops = (nt + 3) >> 2;   // matrix-core ops per tile and chunk
+    const int wcap = kUWin / nops;     // chunks per window (a multiple of kUDepth)
     uint32_t cr[kUDepth][3];
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    // A operands of chunks [cw0, cw0 + wc) for the pass's token rows, in two
-    // halves of four rows (the second only for passes of more than four).
-    // The first window's loads go out ahead of the code ring's first loads
-    // (vmcnt is in order: behind them they would wait for the whole burst).
+    // A operands of chunks [cw0, cw0 + wc) for the pass's token rows.  Thread
+    // tid takes chunk pcl of the window and rows 4h..4h+3: with one op per
+    // chunk the 512 threads cover 16 chunks x rows 0-3, with two 8 chunks x
+    // both halves.  The first window's loads go out ahead of the code ring's
+    // first loads (vmcnt is in order: behind them they would wait for the
+    // whole burst).
+    const int pcl = nops == 1 ? tid >> 5 : (tid & 255) >> 5;
+    const int hh = nops == 1 ? 0 : tid >> 8;
     auto aprep = [&](int cw0, int wc, bool first) __attribute__((always_inline)) {
       const int c = cw0 + pcl;
       const bool cok = pcl < wc;
       const bool three = c < nc3;
       const int sn = three ? seg3.n : seg2.n;
       const int li = (three ? c : c - nc3) * kGroup + m0;
-      const int pc_l = min(pcl, kUWin - 1);
       const u32x4 usw = __builtin_bit_cast(
-          u32x4, three ? __builtin_amdgcn_raw_buffer_load_b128(ru3, (g * np3 + li) * 4, 0, 0)
-                       : __builtin_amdgcn_raw_buffer_load_b128(ru2, (g * np2 + li) * 4, 0, 0));
-      for (int h = 0; h < nops; ++h) {
-        f32x4 tt[4];
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, li * 4, three ? ou3 : ou2, 0));
+      f32x4 tt[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          tt[r] = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                         rt, ((pb + min(4 * h + r, nt - 1)) * rs + (three ? tb3 : tb2) + li) * 4, 0, 0));
-        if (first && h == 0) {
+      for (int r = 0; r < 4; ++r)
+        tt[r] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rt, ((pb + min(4 * hh + r, nt - 1)) * rs + (three ? tb3 : tb2) + li) * 4, 0, 0));
+      if (first) {
 #pragma unroll
-          for (int d = 0; d < kUDepth; ++d) load(cr[d], d);
-          if (pb == p0) load_u8w();
+        for (int d = 0; d < kUDepth; ++d) load(cr[d], d);
+        if (pb == p0) load_u8w();
+      }
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int r = 4 * hh + r4;
+        if (r >= nt) break;   // rows past the pass's tokens: their D rows are never read
+        float tp[4];
+        float mx = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool ok = cok && li + u < sn;
+          tp[u] = ok ? f16f(usw[u] & 0xFFFFu) * tt[r4][u] : 0.f;
+          mx = fmaxf(mx, fabsf(tp[u]));
         }
+        mx = fmaxf(mx, swz_xor<1>(mx));
+        mx = fmaxf(mx, swz_xor<2>(mx));
+        mx = fmaxf(mx, swz_xor<4>(mx));
+        const int sb = block_scale_byte(mx);
+        const float inv = pow2f(127 - sb), fwd = pow2f(sb - 127);
+        // three fp8 pieces, two values per conversion: the low half of word w[pc]
+        // holds ranks u = 0, 2 (even lane group), the high half ranks 1, 3
+        float rr[4] = {tp[0] * inv, tp[1] * inv, tp[2] * inv, tp[3] * inv};
+        float bk[4] = {0.f, 0.f, 0.f, 0.f};
+        uint32_t w[3];
+        float sc_pc = 1.f;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int r = 4 * h + r4;
-          if (r >= nt) break;   // rows past the pass's tokens: their D rows are never read
-          float tp[4];
-          float mx = 0.f;
+        for (int pc = 0; pc < 3; ++pc) {
+          int ww = __builtin_amdgcn_cvt_pk_fp8_f32(rr[0], rr[2], 0, false);
+          ww = __builtin_amdgcn_cvt_pk_fp8_f32(rr[1], rr[3], ww, true);
+          w[pc] = (uint32_t)ww;
+          const f32x2 e02 = __builtin_amdgcn_cvt_pk_f32_fp8(ww, false), e13 = __builtin_amdgcn_cvt_pk_f32_fp8(ww, true);
+          bk[0] += e02.x * sc_pc; bk[2] += e02.y * sc_pc; bk[1] += e13.x * sc_pc; bk[3] += e13.y * sc_pc;
+          rr[0] = (rr[0] - e02.x) * 32.f; rr[2] = (rr[2] - e02.y) * 32.f;
+          rr[1] = (rr[1] - e13.x) * 32.f; rr[3] = (rr[3] - e13.y) * 32.f;
+          sc_pc *= 1.f / 32.f;
+        }
+        float cz = 0.f;   // sum over the thread's ranks of z t' (zero for masked ranks and rows)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const bool ok = cok && li + u < sn;
-            tp[u] = ok ? f16f(usw[u] & 0xFFFFu) * tt[r4][u] : 0.f;
-            mx = fmaxf(mx, fabsf(tp[u]));
-          }
-          mx = fmaxf(mx, swz_xor<1>(mx));
-          mx = fmaxf(mx, swz_xor<2>(mx));
-          mx = fmaxf(mx, swz_xor<4>(mx));
-          const int sb = block_scale_byte(mx);
-          const float inv = pow2f(127 - sb), fwd = pow2f(sb - 127);
-          // three fp8 pieces, two values per conversion: the low half of word w[pc]
-          // holds ranks u = 0, 2 (even lane group), the high half ranks 1, 3
-          float rr[4] = {tp[0] * inv, tp[1] * inv, tp[2] * inv, tp[3] * inv};
-          float bk[4] = {0.f, 0.f, 0.f, 0.f};
-          uint32_t w[3];
-          float sc_pc = 1.f;
+        for (int u = 0; u < 4; ++u) cz += f16f(usw[u] >> 16) * (bk[u] * fwd);
+        cz += swz_xor<1>(cz);
+        cz += swz_xor<2>(cz);
+        cz += swz_xor<4>(cz);
+        cz += swz_xor<8>(cz);
+        cz += swz_xor<16>(cz);
+        const float cz_hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cz), 32));   // lanes 32-63
+        if (lane == 0) S.cz[wave][r] += cz + cz_hi;
+        if (cok) {
+          const int fi = pcl * nops + hh;
 #pragma unroll
           for (int pc = 0; pc < 3; ++pc) {
-            int ww = __builtin_amdgcn_cvt_pk_fp8_f32(rr[0], rr[2], 0, false);
-            ww = __builtin_amdgcn_cvt_pk_fp8_f32(rr[1], rr[3], ww, true);
-            w[pc] = (uint32_t)ww;
-            const f32x2 e02 = __builtin_amdgcn_cvt_pk_f32_fp8(ww, false), e13 = __builtin_amdgcn_cvt_pk_f32_fp8(ww, true);
-            bk[0] += e02.x * sc_pc; bk[2] += e02.y * sc_pc; bk[1] += e13.x * sc_pc; bk[3] += e13.y * sc_pc;
-            rr[0] = (rr[0] - e02.x) * 32.f; rr[2] = (rr[2] - e02.y) * 32.f;
-            rr[1] = (rr[1] - e13.x) * 32.f; rr[3] = (rr[3] - e13.y) * 32.f;
-            sc_pc *= 1.f / 32.f;
+            S.frag[fi][lg_even][r4 + 4 * pc][hw] = (uint16_t)w[pc];
+            S.frag[fi][lg_even + 1][r4 + 4 * pc][hw] = (uint16_t)(w[pc] >> 16);
           }
-          float cz = 0.f;   // sum over the thread's ranks of z t' (zero for masked ranks and rows)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) cz += f16f(usw[u] >> 16) * (bk[u] * fwd);
-          cz += swz_xor<1>(cz);
-          cz += swz_xor<2>(cz);
-          cz += swz_xor<4>(cz);
-          cz += swz_xor<8>(cz);
-          cz += swz_xor<16>(cz);
-          const float cz_hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cz), 32));   // lanes 32-63
-          if (lane == 0) S.cz[wave][r] += cz + cz_hi;
-          if (cok) {
-#pragma unroll
-            for (int pc = 0; pc < 3; ++pc) {
-              S.frag[pc_l][h][lg_even][r4 + 4 * pc][hw] = (uint16_t)w[pc];
-              S.frag[pc_l][h][lg_even + 1][r4 + 4 * pc][hw] = (uint16_t)(w[pc] >> 16);
-            }
-            if (part == 0) S.sc[pc_l][r][kb4] = (uint8_t)sb;
-          }
-          __builtin_amdgcn_sched_barrier(0);   // one token row at a time: bounded register use
+          if (part == 0) S.sc[pcl][r][kb4] = (uint8_t)sb;
         }
+        __builtin_amdgcn_sched_barrier(0);   // one token row at a time: bounded register use
       }
     };
     // chunk c (window-local cl): matrix-core ops with the codes in cur, then
     // the loads of chunk c + kUDepth into cur
     auto step = [&](int c, int cl, uint32_t (&cur)[3]) __attribute__((always_inline)) {
       const bool three = c < nc3;
-      v8i a[2];
-      int sa[2];
+      const v8i bop = three ? b_fp6(cur[0], cur[1], cur[2]) : b_fp4(cur[0], cur[1]);
+      const int bs = three ? kScaleFp6Code : kScaleFp4Code;
 #pragma unroll
       for (int op = 0; op < 2; ++op) {
-        const uint4* f = reinterpret_cast<const uint4*>(S.frag[cl][op][q][col]);
-        a[op] = v8_of(f[0], f[1]);
-        sa[op] = ps < 3 ? (int)S.sc[cl][4 * op + tr4][q] - 5 * ps : 127;
+        if (op < nops) {   // one A operand at a time: its registers are free again after hold()
+          const uint4* f = reinterpret_cast<const uint4*>(S.frag[cl * nops + op][q][col]);
+          const v8i a = v8_of(f[0], f[1]);
+          const int sa = ps < 3 ? (int)S.sc[cl][4 * op + tr4][q] - 5 * ps : 127;
+          f32x4 d = {0.f, 0.f, 0.f, 0.f};
+          d = three ? mma(a, bop, d, sa, kFmtFp6, kScaleFp6Code) : mma(a, bop, d, sa, kFmtFp4, kScaleFp4Code);
+          hold(d, a, bop, sa, bs);
+          acc[op] += d;
+        }
       }
-      const v8i bop = three ? b_fp6(cur[0], cur[1], cur[2]) : b_fp4(cur[0], cur[1]);
-      f32x4 d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      if (three) {
-        d[0] = mma(a[0], bop, d[0], sa[0], kFmtFp6, kScaleFp6Code);
-        if (nops > 1) d[1] = mma(a[1], bop, d[1], sa[1], kFmtFp6, kScaleFp6Code);
-      } else {
-        d[0] = mma(a[0], bop, d[0], sa[0], kFmtFp4, kScaleFp4Code);
-        if (nops > 1) d[1] = mma(a[1], bop, d[1], sa[1], kFmtFp4, kScaleFp4Code);
-      }
-      hold(d[0], a[0], a[1], bop, sa[0], sa[1], three ? kScaleFp6Code : kScaleFp4Code);
-      hold(d[1], a[0], a[1], bop, sa[0], sa[1], three ? kScaleFp6Code : kScaleFp4Code);
       load(cur, c + kUDepth);
-      acc[0] += d[0];
-      acc[1] += d[1];
       asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));   // sums land here, not deferred to the end
     };
     __syncthreads();   // the previous pass's operands and sums are consumed
     if (lane < kURows) S.cz[wave][lane] = 0.f;   // this wave's z t' sums of the pass
     if (nc == 0 && pb == p0) load_u8w();
-    for (int cw0 = 0; cw0 < nc; cw0 += kUWin) {
-      const int wc = min(kUWin, nc - cw0);
+    for (int cw0 = 0; cw0 < nc; cw0 += wcap) {
+      const int wc = min(wcap, nc - cw0);
       if (cw0 > 0) __syncthreads();   // the previous window's operands are consumed
       aprep(cw0, wc, cw0 == 0);
       __syncthreads();
