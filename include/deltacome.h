@@ -41,8 +41,12 @@
  * a stream of uint32 words, bit t of the stream being bit t%32 of word t/32.
  * Regions, each at a multiple of 256 bytes from the buffer start, in order:
  *   SIGMA  fp32 [r]
- *   VC_b   b = 8,3,2: V codes, [n][Gi][4b] words; the group's 128 codes of
- *          v_i form one bitstream.
+ *   VC_8   V codes at 8 bits, [n][Gi][32] words: the group's 128 codes of
+ *          v_i form one bitstream (plain bytes [n][in]).
+ *   VC_b   b = 3,2: V codes in 16-rank tiles, [ceil(n/16)][Gi][4][16][b]
+ *          words: word block (T, g, q, c) is the bitstream of codes
+ *          32q..32q+31 of group g of local rank 16T+c (ranks past n are 0),
+ *          so the 16 ranks of a tile lie side by side for each 32-code chunk.
  *   VS_b   V scale/zero, uint32 [Gi][pad4(n)]: fp16 scale | fp16 zero << 16.
  *   UC_8   U codes at 8 bits, bytes [out][n8], byte (o,i) = code of u_i at
  *          row o.

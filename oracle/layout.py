@@ -18,8 +18,12 @@ is bit t%32 of word t//32).
 
 Regions, in this order, each starting at a multiple of 256 bytes:
   SIGMA  fp32 [r]
-  VC_b   (b = 8, 3, 2)  V codes: for local rank i, for group g < Gi, the
-         group's 128 codes as one bitstream of 4b words.  [n][Gi][4b] words.
+  VC_8   V codes at 8 bits: for local rank i, for group g < Gi, the group's
+         128 codes as one bitstream of 32 words.  [n][Gi][32] words.
+  VC_b   (b = 3, 2)  V codes in 16-rank tiles: the group's 128 codes cut into
+         4 chunks of 32 codes, each chunk one bitstream of b words; words
+         [ceil(n/16)][Gi][4][16][b]: tile T, group g, chunk q, rank 16T+c of
+         the tile (ranks past n are 0).
   VS_b   V scale/zero: uint32 [Gi][pad4(n)], entry (g, i) = fp16 scale bits
          | fp16 zero bits << 16 of v_i's group g; pad entries are 0.
   UC_8   U codes, 8-bit: bytes [out][n8], byte (o, i) = code of u_i at row o.
@@ -63,7 +67,7 @@ def regions(spec) -> Dict[str, Tuple[int, int]]:
     r = n8 + n3 + n2
     gi, go = inn // GROUP, out // GROUP
     sizes = [("SIGMA", 4 * r)]
-    sizes += [("VC%d" % b, cnt[b] * gi * 16 * b) for b in SEGS]
+    sizes += [("VC%d" % b, (cnt[b] if b == 8 else pad(cnt[b], 16)) * gi * 16 * b) for b in SEGS]
     sizes += [("VS%d" % b, gi * pad(cnt[b], 4) * 4) for b in SEGS]
     sizes += [("UC8", out * cnt[8])]
     sizes += [("UC%d" % b, (out // 16) * 16 * 4 * u_row_words(cnt[b], b)) for b in (3, 2)]
@@ -148,7 +152,15 @@ def pack(spec, codes_u, codes_v, sz_u, sz_v, sigma) -> np.ndarray:
     for b, (lo, hi) in _seg_ranges(spec).items():
         n = hi - lo
         cv = np.asarray(codes_v[lo:hi]).reshape(n, gi, GROUP)
-        put("VC%d" % b, bitstream(cv, b))
+        if b == 8:
+            put("VC8", bitstream(cv, 8))
+        else:
+            nt = pad(n, 16) // 16
+            cvp = np.zeros((nt * 16, gi, 4, 32), np.uint8)
+            cvp[:n] = cv.reshape(n, gi, 4, 32)
+            words = bitstream(cvp, b)                                  # [16T][Gi][4][b]
+            words = words.reshape(nt, 16, gi, 4, b).transpose(0, 2, 3, 1, 4)   # [T][Gi][4][16][b]
+            put("VC%d" % b, np.ascontiguousarray(words))
         vs = np.zeros((gi, pad(n, 4)), "<u4")
         vs[:, :n] = _sz_words(sz_v[lo:hi]).T
         put("VS%d" % b, vs)
@@ -193,8 +205,14 @@ def unpack(spec, buf):
         n = hi - lo
         if n == 0:
             continue
-        words = get("VC%d" % b, "<u4").reshape(n, gi, 4 * b)
-        codes_v[lo:hi] = unbitstream(words, b, GROUP).reshape(n, inn)
+        if b == 8:
+            words = get("VC8", "<u4").reshape(n, gi, 32)
+            codes_v[lo:hi] = unbitstream(words, 8, GROUP).reshape(n, inn)
+        else:
+            nt = pad(n, 16) // 16
+            words = get("VC%d" % b, "<u4").reshape(nt, gi, 4, 16, b).transpose(0, 3, 1, 2, 4)   # [T][16][Gi][4][b]
+            codes = unbitstream(words.reshape(nt * 16, gi, 4, b), b, 32)                       # [16T][Gi][4][32]
+            codes_v[lo:hi] = codes.reshape(nt * 16, inn)[:n]
         vs = get("VS%d" % b, "<u4").reshape(gi, pad(n, 4))[:, :n].T
         sz_v[lo:hi, :, 0] = vs & 0xFFFF
         sz_v[lo:hi, :, 1] = vs >> 16

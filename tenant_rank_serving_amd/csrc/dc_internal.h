@@ -40,6 +40,13 @@ DC_HD inline size_t u_kblock_word(int o, int kb, int n, int b, int* nw) {
   return (size_t)(o / 16) * 16 * rw + (size_t)kb * 16 * b + (size_t)(o % 16) * w;
 }
 
+// Word offset of the b words of chunk q (codes 32q..32q+31) of group grp of
+// local rank i inside a 3- or 2-bit V code region of Gi groups: 16-rank
+// tiles, [ceil(n/16)][Gi][4][16][b] words.
+DC_HD inline size_t v_chunk_word(int i, int grp, int q, int gi, int b) {
+  return ((((size_t)(i / 16) * gi + grp) * 4 + q) * 16 + (i % 16)) * b;
+}
+
 // Byte offsets of the DC_REG_* regions of a packed buffer and its total size.
 // This is the format stated in include/deltacome.h.
 struct Layout {
@@ -54,8 +61,8 @@ DC_HD inline void layout_of(int32_t out, int32_t in, int32_t n8, int32_t n3, int
   size_t sz[DC_REG_COUNT];
   sz[DC_REG_SIGMA] = 4 * r;
   sz[DC_REG_VC8] = (size_t)n8 * gi * 16 * 8;
-  sz[DC_REG_VC3] = (size_t)n3 * gi * 16 * 3;
-  sz[DC_REG_VC2] = (size_t)n2 * gi * 16 * 2;
+  sz[DC_REG_VC3] = round_up(n3, 16) * gi * 16 * 3;
+  sz[DC_REG_VC2] = round_up(n2, 16) * gi * 16 * 2;
   sz[DC_REG_VS8] = gi * round_up(n8, 4) * 4;
   sz[DC_REG_VS3] = gi * round_up(n3, 4) * 4;
   sz[DC_REG_VS2] = gi * round_up(n2, 4) * 4;

@@ -325,9 +325,11 @@ struct VGrp {
   uint32_t z[kVTiles];
 };
 
-// Buffer resources of a segment's V codes and scale/zero words, and the byte
-// offsets of the lane's rank in each of its tiles (rank 0 of the segment for
-// ranks past its end); the group goes into the uniform offset.
+// Buffer resources of a segment's V codes and scale/zero words, and per tile
+// the byte offset of the lane's word block (codes, 16-rank tile-major: one
+// wave load reads 64 consecutive blocks) and of its rank's scale/zero column
+// (rank 0 of the segment for ranks past its end); the group goes into the
+// uniform offset.
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
 struct VBuf {
@@ -340,11 +342,11 @@ __device__ __forceinline__ void v_load_grp(VGrp<B>& c, const VBuf& p, int np, in
 #pragma unroll
   for (int h = 0; h < kVTiles; ++h) {
     if constexpr (B == 2) {
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(p.rc, p.oc[h], gi * 4 * B * 4, 0);
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(p.rc, p.oc[h], gi * 64 * B * 4, 0);
       c.w[h][0] = v.x;
       c.w[h][1] = v.y;
     } else {
-      const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(p.rc, p.oc[h], gi * 4 * B * 4, 0);
+      const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(p.rc, p.oc[h], gi * 64 * B * 4, 0);
       c.w[h][0] = v.x;
       c.w[h][1] = v.y;
       c.w[h][2] = v.z;
@@ -422,7 +424,8 @@ __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, i
   const int np = (int)round_up(sg.n, 4);
   const int npass = (p1 - p0 + kVRows - 1) / kVRows;
   VBuf P;
-  P.rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sg.vc), 0, sg.n * gi_n * 16 * B, kBufFlags);
+  P.rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sg.vc), 0, (int)round_up(sg.n, 16) * gi_n * 16 * B,
+                                          kBufFlags);
   P.rz = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(sg.vs), 0, gi_n * np * 4, kBufFlags);
   int li[kVTiles];
   bool rv[kVTiles];
@@ -431,7 +434,9 @@ __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, i
   for (int h = 0; h < kVTiles; ++h) {
     li[h] = (tile0 + h) * 16 + col;
     rv[h] = li[h] < sg.n;
-    P.oc[h] = (uint32_t)((rv[h] ? li[h] : 0) * gi_n * 16 * B + 4 * B * q);
+    // tile-major codes: lane (col, q) of tile t reads the b words of block
+    // (t, group, q, col), i.e. lane * b words into the tile's group block
+    P.oc[h] = (uint32_t)(((tile0 + h) * gi_n * 64 + lane) * 4 * B);
     P.oz[h] = (uint32_t)(4 * (rv[h] ? li[h] : 0));
     sig[h] = rv[h] ? sigma[sg.lo + li[h]] : 0.f;
   }

@@ -176,9 +176,10 @@ __global__ void __launch_bounds__(256) k_dequant(Tenant tn, int32_t out, int32_t
   uint32_t code, sz;
   if (is_v) {
     const int gi = in / kGroup;
-    const uint32_t* grp = reinterpret_cast<const uint32_t*>(sg.vc) + ((size_t)li * gi + pos / kGroup) * 4 * sg.b;
     const int kk = pos % kGroup;
-    const uint32_t* unit = grp + (kk / 32) * sg.b;
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(sg.vc);
+    const uint32_t* unit = sg.b == 8 ? vw + ((size_t)li * gi + pos / kGroup) * 32 + (kk / 32) * 8
+                                     : vw + v_chunk_word(li, pos / kGroup, kk / 32, gi, sg.b);
     code = sg.b == 8 ? unit_code<8>(unit, kk % 32) : (sg.b == 3 ? unit_code<3>(unit, kk % 32) : unit_code<2>(unit, kk % 32));
     sz = sg.vs[(size_t)(pos / kGroup) * np + li];
   } else {

@@ -128,16 +128,19 @@ dc_status pack_into(const dc_spec* s, const Layout& L, const uint8_t* cu, const 
   segments(s, sg);
   for (const Seg& g : sg) {
     const uint32_t lim = 1u << g.b;
-    // V codes: [n][Gi][4b] words, one bitstream per 128-element group.
+    // V codes: 8-bit [n][Gi][32] words, one bitstream per 128-element group;
+    // 3- and 2-bit in 16-rank tiles, [ceil(n/16)][Gi][4][16][b] words.
     uint32_t* vc = reinterpret_cast<uint32_t*>(out + L.off[g.reg_vc]);
     for (int i = 0; i < g.n; ++i) {
       const uint8_t* row = cv + (size_t)(g.lo + i) * s->in;
       for (int grp = 0; grp < gi; ++grp) {
-        uint32_t* words = vc + ((size_t)i * gi + grp) * 4 * g.b;
         for (int k = 0; k < dc::kGroup; ++k) {
           const uint32_t c = row[grp * dc::kGroup + k];
           if (c >= lim) return DC_ERR_RANGE;
-          put_code(words, g.b, k, c);
+          if (g.b == 8)
+            put_code(vc + ((size_t)i * gi + grp) * 32, 8, k, c);
+          else
+            put_code(vc + dc::v_chunk_word(i, grp, k / 32, gi, g.b), g.b, k % 32, c);
         }
       }
     }
@@ -293,9 +296,11 @@ dc_status dc_unpack(const dc_spec* s, const void* packed, size_t packed_bytes, u
     const uint32_t* vc = reinterpret_cast<const uint32_t*>(in + L.off[g.reg_vc]);
     for (int i = 0; i < g.n; ++i)
       for (int grp = 0; grp < gi; ++grp) {
-        const uint32_t* words = vc + ((size_t)i * gi + grp) * 4 * g.b;
-        for (int k = 0; k < dc::kGroup; ++k)
-          codes_v[(size_t)(g.lo + i) * s->in + grp * dc::kGroup + k] = (uint8_t)get_code(words, g.b, k);
+        for (int k = 0; k < dc::kGroup; ++k) {
+          const uint32_t c = g.b == 8 ? get_code(vc + ((size_t)i * gi + grp) * 32, 8, k)
+                                      : get_code(vc + dc::v_chunk_word(i, grp, k / 32, gi, g.b), g.b, k % 32);
+          codes_v[(size_t)(g.lo + i) * s->in + grp * dc::kGroup + k] = (uint8_t)c;
+        }
       }
     const size_t np = dc::round_up(g.n, 4);
     const uint32_t* vs = reinterpret_cast<const uint32_t*>(in + L.off[g.reg_vs]);
