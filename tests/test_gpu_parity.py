@@ -88,7 +88,9 @@ def test_c0_end_to_end():
 # ----------------------------------------------- decode, segments and tails
 SEG_CASES = [(256, 256, 2, 8, 22, 4), (384, 256, 3, 37, 71, 1), (384, 256, 3, 37, 71, 5),
              (256, 384, 2, 40, 100, 17), (128, 128, 0, 0, 5, 2), (128, 128, 1, 0, 0, 3),
-             (512, 640, 4, 65, 129, 9)]
+             (512, 640, 4, 65, 129, 9),
+             # 17 chunks of 128 3/2-bit ranks: more than one LDS window per output group
+             (2304, 2176, 2, 130, 2000, 6)]
 
 
 @pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: "x".join(map(str, c)))
