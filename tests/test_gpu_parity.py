@@ -289,3 +289,28 @@ def test_prefill_small_segments():
     t.cuda.synchronize()
     ref = oap.apply_prefill(w, x, seg, [oracle_tenant(d) for d in ds])
     check_close(y_to_f64(y), ref, what="prefill")
+
+
+@pytest.mark.parametrize("mi", [0, 6])
+def test_c3_prefill_full_size(mi):
+    """13B-shaped prefill (q 5120x5120, down 5120x13824): 8 tenants x 2048
+    tokens in contiguous segments, the whole matrix on the GPU; per tenant the
+    first, the last and 4 random tokens against the oracle."""
+    note("c3 matrix", mi)
+    t = torch()
+    m = synth.make_c3_matrix(mi)
+    seg = m["seg"].astype(np.int32)
+    T = int(seg[-1])
+    specs = [d.spec for d in m["deltas"]]
+    views = [upload(d.spec, d) for d in m["deltas"]]
+    ws = workspace(trs.DC_OP_PREFILL, specs, T)
+    y = t.empty((T, m["out"]), dtype=t.int16, device="cuda")
+    trs.dc_apply_prefill(views, dev_u16(m["w"]), dev_u16(m["x"]), seg, y, ws)
+    t.cuda.synchronize()
+    rng = np.random.default_rng(30 + mi)
+    for k, d in enumerate(m["deltas"]):
+        lo, hi = int(seg[k]), int(seg[k + 1])
+        sel = np.unique(np.concatenate([[lo, hi - 1], lo + rng.choice(hi - lo, 4, replace=False)]))
+        yk = y_to_f64(y[t.from_numpy(sel).cuda()])
+        ref = oap.apply_factored(m["w"], m["x"][sel], *oracle_tenant(d))
+        check_close(yk, ref, what="c3 %s tenant %d" % (m["name"], k))
