@@ -96,7 +96,9 @@ enum {
   DC_ERR_BUFFER = -4,      /* buffer or workspace smaller than required */
   DC_ERR_RANGE = -5,       /* dc_pack: non-finite input or fp16 scale overflow */
   DC_ERR_HIP = -6,         /* a HIP launch or query failed */
-  DC_ERR_UNSUPPORTED = -7  /* a limit of this build (see DC_MAX_TENANTS) */
+  DC_ERR_UNSUPPORTED = -7  /* a limit of this build: more than DC_MAX_TENANTS tenants, or a
+                              packed buffer, t (T x widest rank row, fp32) or the backbone
+                              partials (up to 8 x T x out, fp32) of 2 GiB or more */
 };
 
 /* Most tenants one multi-tenant or prefill call can address. */

@@ -314,3 +314,60 @@ def test_c3_prefill_full_size(mi):
         yk = y_to_f64(y[t.from_numpy(sel).cuda()])
         ref = oap.apply_factored(m["w"], m["x"][sel], *oracle_tenant(d))
         check_close(yk, ref, what="c3 %s tenant %d" % (m["name"], k))
+
+
+# ---------------------------------------------------------------- HIP graphs
+def test_graph_replay_matches_eager():
+    """Three multi-tenant calls on two streams (fork, two calls side by side,
+    join, a third call) captured as one HIP graph.  Every replay, with eager
+    work and synchronizations between the replays, gives the eager outputs
+    bit for bit (the inputs are 384 columns wide, so t is summed in a fixed
+    order)."""
+    note("graph replay")
+    t = torch()
+    spec = (256, 384, 2, 9, 40)
+    ds = [synth.small_delta(90 + k, *spec) for k in range(3)]
+    views = [upload(spec, d) for d in ds]
+    rng = np.random.default_rng(21)
+    w = dev_u16(synth.base_weight(rng, 256, 384))
+    T = 9
+    ids = dev_i32(np.array([0, 2, 1, -1, 2, 2, 0, 1, 0], np.int32))
+    xs = [dev_u16(synth.activations(rng, T, 384)) for _ in range(4)]
+    ys = [t.empty((T, 256), dtype=t.int16, device="cuda") for _ in range(4)]
+    wss = [workspace(trs.DC_OP_MULTITENANT, [spec] * 3, T) for _ in range(3)]
+    s0, s1 = t.cuda.Stream(), t.cuda.Stream()
+    ca = trs.MultitenantCall(views, w, xs[0], ids, ys[0], wss[0], stream=s0.cuda_stream)
+    cb = trs.MultitenantCall(views, None, xs[1], ids, ys[1], wss[1], stream=s1.cuda_stream)
+    cc = trs.MultitenantCall(views, w, xs[2], ids, ys[2], wss[0], stream=s0.cuda_stream)
+    cd = trs.MultitenantCall(views, w, xs[3], ids, ys[3], wss[2], stream=s0.cuda_stream)   # eager work between replays
+    fork, join = t.cuda.Event(), t.cuda.Event()
+
+    def step():
+        fork.record(s0)
+        s1.wait_event(fork)
+        ca()
+        cb()
+        join.record(s1)
+        s0.wait_event(join)
+        cc()
+
+    with t.cuda.stream(s0):
+        step()
+        t.cuda.synchronize()
+        ref = [y.clone() for y in ys[:3]]
+        g = t.cuda.CUDAGraph()
+        with t.cuda.graph(g, stream=s0):
+            step()
+        t.cuda.synchronize()
+        for rep in range(4):
+            for y in ys[:3]:
+                y.fill_(0x7FC0)    # a NaN pattern: the replay must overwrite every output
+            cd()
+            t.cuda.synchronize()
+            g.replay()
+            t.cuda.synchronize()
+            for i in range(3):
+                assert t.equal(ys[i], ref[i]), "replay %d output %d" % (rep, i)
+    ref_c = oap.apply_multitenant(w.cpu().numpy().view(np.uint16), xs[2].cpu().numpy().view(np.uint16),
+                                  ids.cpu().numpy(), [oracle_tenant(d) for d in ds])
+    check_close(y_to_f64(ys[2]), ref_c, what="graph replay vs oracle")
