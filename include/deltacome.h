@@ -98,7 +98,7 @@ enum {
   DC_ERR_HIP = -6,         /* a HIP launch or query failed */
   DC_ERR_UNSUPPORTED = -7  /* a limit of this build: more than DC_MAX_TENANTS tenants, or a
                               packed buffer, t (T x widest rank row, fp32) or the backbone
-                              partials (up to 8 x T x out, fp32) of 2 GiB or more */
+                              product (T x out, fp32) of 2 GiB or more */
 };
 
 /* Most tenants one multi-tenant or prefill call can address. */

@@ -72,7 +72,7 @@ dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const ui
   if (ws_bytes < wl.total) return DC_ERR_BUFFER;
   // the kernels address t, the backbone partials and each packed buffer with 32-bit byte offsets
   const size_t lim = (size_t)INT32_MAX;
-  if ((size_t)T * wl.rs * 4 > lim || (size_t)wl.ns * T * out * 4 > lim) return DC_ERR_UNSUPPORTED;
+  if ((size_t)T * wl.rs * 4 > lim || (size_t)T * out * 4 > lim) return DC_ERR_UNSUPPORTED;
   for (int k = 0; k < n; ++k)
     if (dc_packed_bytes(&specs[k]) > lim) return DC_ERR_UNSUPPORTED;
   if (T == 0) return DC_OK;
