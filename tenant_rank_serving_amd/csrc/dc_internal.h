@@ -93,6 +93,17 @@ struct TenantTable {
   Tenant t[DC_MAX_TENANTS];
 };
 
+// One bucket of routed tokens that is not empty, as the prep kernel lists
+// them (bucket order; the rest of the list has p0 == p1): the tenant record
+// (zero for the backbone-only bucket k == n) and the routed range [p0, p1).
+struct ActEntry {
+  const uint8_t* base;
+  int32_t n8, n3, n2;
+  int32_t k;
+  int32_t p0, p1;
+};
+static_assert(sizeof(ActEntry) == 32, "one 32-byte load per block");
+
 // Work decomposition of the matrix-core path (shared by host sizing and kernels).
 constexpr int kVSlice = 16;   // 128-groups of the input per V-side work item
 constexpr int kVRows = 8;     // token rows per V-side pass
@@ -116,6 +127,7 @@ struct WsLayout {
   size_t flags;   // uint32 status word (+ padding to 256 B)
   size_t offs;    // int32 [n+2] bucket starts in sorted order (bucket n = backbone only)
   size_t perm;    // int32 [T] sorted position -> token index
+  size_t act;     // ActEntry [n+1] buckets with tokens first
   size_t xf;      // uint8 [T][in/128][256] fp8 hi/lo fragments of x (matrix-core A operand)
   size_t xsc;     // uint32 [T][in/128] E8M0 block scales of the hi fragments
   size_t xsum;    // fp32 [T][in/128] sums of x over each 128-group
@@ -138,6 +150,7 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rs, int32_t n,
   W->flags = take(256);
   W->offs = take(4 * ((size_t)n + 2));
   W->perm = take(4 * (size_t)T);
+  W->act = take(sizeof(ActEntry) * ((size_t)n + 1));
   const size_t items = (size_t)T * (in / kGroup);
   W->xf = take(256 * items);
   W->xsc = take(4 * items);

@@ -164,24 +164,65 @@ struct SegArg {
 
 // ------------------------------------------------------------------- prep
 // Block 0 routes the tokens (stable counting sort by tenant; bucket n holds
-// the backbone-only tokens).  Every other wave turns one (token, 128-group)
-// of x into fp8 hi/lo A fragments, their E8M0 scales and the group sum.
-__global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
+// the backbone-only tokens) and lists the buckets that have tokens, each
+// with its tenant record and routed range, so that the V and U blocks of
+// buckets with tokens come first in their grids and find everything they
+// need in one load.  Every other wave turns one (token, 128-group) of x into
+// fp8 hi/lo A fragments, their E8M0 scales and the group sum.
+__device__ __forceinline__ void list_active(const TenantTable& tt, int32_t n, const int* so,
+                                            ActEntry* __restrict__ act) {
+  __shared__ int wcnt[4];
+  const int tid = threadIdx.x, b = tid, lane = tid & 63, wave = tid >> 6;
+  const bool live = b <= n && so[b + 1] > so[b];
+  const uint64_t m = __ballot(live);
+  if (lane == 0) wcnt[wave] = __popcll(m);
+  __syncthreads();
+  int pos = __popcll(m & ((1ull << lane) - 1)), total = 0;
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) pos += wcnt[w];
+    total += wcnt[w];
+  }
+  if (live) {
+    ActEntry e;
+    e.base = b < n ? tt.t[b].base : nullptr;
+    e.n8 = b < n ? tt.t[b].n8 : 0;
+    e.n3 = b < n ? tt.t[b].n3 : 0;
+    e.n2 = b < n ? tt.t[b].n2 : 0;
+    e.k = b;
+    e.p0 = so[b];
+    e.p1 = so[b + 1];
+    act[pos] = e;
+  }
+  if (b <= n && b >= total) {   // the rest of the list: empty entries
+    ActEntry e{};
+    e.k = -1;
+    act[b] = e;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_prep(TenantTable tt, const uint16_t* __restrict__ x,
+                                              const int32_t* __restrict__ ids,
                                               int32_t T, int32_t in, int32_t n, int32_t mode, SegArg seg,
                                               int32_t* __restrict__ offs, int32_t* __restrict__ perm,
+                                              ActEntry* __restrict__ act,
                                               uint32_t* __restrict__ flags, uint8_t* __restrict__ xf,
                                               uint32_t* __restrict__ xsc, float* __restrict__ xsum,
                                               uint16_t* __restrict__ xt, float* __restrict__ tv, int32_t ntv) {
   const int tid = threadIdx.x;
   for (int i = blockIdx.x * 256 + tid; i < ntv; i += gridDim.x * 256) tv[i] = 0.f;   // t accumulates atomically
   if (blockIdx.x == 0) {
+    static_assert(DC_MAX_TENANTS + 1 <= 256, "one thread per bucket");
+    __shared__ int so[DC_MAX_TENANTS + 2];   // bucket starts
     if (mode != 1) {
       for (int p = tid; p < T; p += blockDim.x) perm[p] = p;
       if (tid == 0) {
-        if (mode == 0) { offs[0] = 0; offs[1] = T; offs[2] = T; }
-        else { for (int k = 0; k <= n; ++k) offs[k] = seg.v[k]; offs[n + 1] = T; }
+        if (mode == 0) { so[0] = 0; so[1] = T; so[2] = T; }
+        else { for (int k = 0; k <= n; ++k) so[k] = seg.v[k]; so[n + 1] = T; }
+        for (int k = 0; k <= n + 1; ++k) offs[k] = so[k];
         *flags = 0;
       }
+      __syncthreads();
+      list_active(tt, n, so, act);
       return;
     }
     __shared__ int cnt[DC_MAX_TENANTS + 1];   // tokens per bucket
@@ -199,11 +240,13 @@ __global__ void __launch_bounds__(256) k_prep(const uint16_t* __restrict__ x, co
     __syncthreads();
     if (tid == 0) {
       int s = 0;
-      for (int b = 0; b <= n; ++b) { offs[b] = s; next[b] = s; s += cnt[b]; }
+      for (int b = 0; b <= n; ++b) { offs[b] = s; so[b] = s; next[b] = s; s += cnt[b]; }
       offs[n + 1] = s;
+      so[n + 1] = s;
       *flags = bad ? 1u : 0u;
     }
     __syncthreads();
+    list_active(tt, n, so, act);
     for (int c0 = 0; c0 < T; c0 += blockDim.x) {
       const int t = c0 + tid;
       int b = -1;
@@ -577,15 +620,20 @@ __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, con
   }
 }
 
-__global__ void __launch_bounds__(256) k_vside(TenantTable tt, int32_t out, int32_t in,
-                                               const uint16_t* __restrict__ x, const int32_t* __restrict__ offs,
+__global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t out, int32_t in,
+                                               const uint16_t* __restrict__ x, const ActEntry* __restrict__ act,
                                                const int32_t* __restrict__ perm, const uint8_t* __restrict__ xf,
                                                const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
                                                float* __restrict__ tv, int32_t rs) {
-  const int k = blockIdx.y;
-  const int p0 = offs[k], p1 = offs[k + 1];
-  if (p0 >= p1) return;
-  const Tenant tn = tt.t[k];
+  const ActEntry e = act[blockIdx.y];   // the blockIdx.y-th bucket with tokens
+  const int p0 = e.p0, p1 = e.p1;
+  if (p0 >= p1 || e.k >= n) return;     // empty entry, or the backbone-only bucket
+  Tenant tn;
+  tn.base = e.base;
+  tn.n8 = e.n8;
+  tn.n3 = e.n3;
+  tn.n2 = e.n2;
+  tn.pad_ = 0;
   const int ns = v_slices(in);
   int b = blockIdx.x / ns;
   const int s = blockIdx.x % ns;
@@ -640,18 +688,19 @@ struct ULds {
   float cz[kUWaves][kURows];         // per-wave partial sums of z t' per token row
 };
 
-__global__ void __launch_bounds__(kUWaves * 64) k_uside(TenantTable tt, int32_t n, int32_t out, int32_t in,
-                                                        const int32_t* __restrict__ offs,
+__global__ void __launch_bounds__(kUWaves * 64) k_uside(int32_t n, int32_t out, int32_t in,
+                                                        const ActEntry* __restrict__ act,
                                                         const int32_t* __restrict__ perm,
                                                         const float* __restrict__ tv, int32_t rs, int32_t T,
                                                         const float* __restrict__ ybase,
                                                         uint16_t* __restrict__ y) {
-  const int g = blockIdx.x, k = blockIdx.y;
+  const int g = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, q = lane >> 4;
-  const int p0 = offs[k], p1 = offs[k + 1];
+  const ActEntry e = act[blockIdx.y];   // the blockIdx.y-th bucket with tokens
+  const int p0 = e.p0, p1 = e.p1;
   if (p0 >= p1) return;
-  if (k == n) {  // backbone-only tokens
+  if (e.k == n) {  // backbone-only tokens
     for (int idx = tid; idx < (p1 - p0) * kGroup; idx += kUWaves * 64) {
       const int t = perm[p0 + idx / kGroup];
       const int o = g * kGroup + idx % kGroup;
@@ -660,7 +709,12 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(TenantTable tt, int32_t 
     return;
   }
   __shared__ ULds S;
-  const Tenant tn = tt.t[k];
+  Tenant tn;
+  tn.base = e.base;
+  tn.n8 = e.n8;
+  tn.n3 = e.n3;
+  tn.n2 = e.n2;
+  tn.pad_ = 0;
   Layout L;
   layout_of(out, in, tn.n8, tn.n3, tn.n2, &L);
   const Seg seg3 = seg_of(tn, L, 1), seg2 = seg_of(tn, L, 2), s8 = seg_of(tn, L, 0);
@@ -889,6 +943,7 @@ int launch_apply(const ApplyArgs& a) {
   uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + a.wl.flags);
   int32_t* offs = reinterpret_cast<int32_t*>(a.ws + a.wl.offs);
   int32_t* perm = reinterpret_cast<int32_t*>(a.ws + a.wl.perm);
+  ActEntry* act = reinterpret_cast<ActEntry*>(a.ws + a.wl.act);
   float* tv = reinterpret_cast<float*>(a.ws + a.wl.vpart);
   float* ybase = a.W ? reinterpret_cast<float*>(a.ws + a.wl.ybase) : nullptr;
   const size_t items = (size_t)a.T * (a.in / kGroup);
@@ -904,18 +959,17 @@ int launch_apply(const ApplyArgs& a) {
   };
   mark(DC_STAGE_ROUTE);
   mark(DC_STAGE_XPREP);
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)(1 + (items + 3) / 4)), dim3(256), 0, st, a.x, a.ids, a.T, a.in, a.n,
-                     a.mode, seg, offs, perm, flags, xf, xsc, xsum, xt, tv, a.T * a.wl.rs);
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)(1 + (items + 3) / 4)), dim3(256), 0, st, *a.tenants, a.x, a.ids, a.T,
+                     a.in, a.n, a.mode, seg, offs, perm, act, flags, xf, xsc, xsum, xt, tv, a.T * a.wl.rs);
   mark(DC_STAGE_BASE);
   if (a.W) launch_base(a.W, xt, ybase, a.out, a.in, a.T, a.stream);
   mark(DC_STAGE_VSIDE);
   if (a.wl.vb > 0)
     hipLaunchKernelGGL(k_vside, dim3((unsigned)(a.wl.vb * v_slices(a.in)), (unsigned)a.n), dim3(256), 0, st,
-                       *a.tenants, a.out, a.in,
-                       a.x, offs, perm, xf, xsc, xsum, tv, a.wl.rs);
+                       a.n, a.out, a.in, a.x, act, perm, xf, xsc, xsum, tv, a.wl.rs);
   mark(DC_STAGE_USIDE);
   hipLaunchKernelGGL(k_uside, dim3((unsigned)(a.out / kGroup), (unsigned)(a.n + 1)), dim3(kUWaves * 64), 0, st,
-                     *a.tenants, a.n, a.out, a.in, offs, perm, tv, a.wl.rs, a.T, ybase, a.y);
+                     a.n, a.out, a.in, act, perm, tv, a.wl.rs, a.T, ybase, a.y);
   mark(DC_STAGE_COUNT);
   return (int)hipGetLastError();
 }
