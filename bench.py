@@ -191,6 +191,79 @@ def calibrate_copy(mib=256, reps=3):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "dispatches": reps}), flush=True)
 
 
+def pack_bench(args):
+    """Quantize + pack on the GPU (dc_pack_device): the 7 matrices of one
+    Llama-2-7B layer at the 1/16 budget, fp32 singular vectors resident in
+    HBM; one JSON line.  The oracle (numpy quantizer + packer) and the host C
+    packer are timed on the q matrix beside it."""
+    import numpy as np
+    import torch
+
+    import synth
+    import tenant_rank_serving_amd as trs
+    from oracle import layout, quant
+
+    trs.lib()
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(5)
+    mats = []
+    for name, out, inn in synth.LLAMA2_7B:
+        spec = (out, inn) + tuple(synth.groups_for(out, inn, 16))
+        r = sum(spec[2:])
+        U = torch.randn(r, out, device=dev) * 0.02
+        V = torch.randn(r, inn, device=dev) * 0.02
+        sg = torch.rand(r, device=dev) + 0.5
+        buf = torch.empty(trs.dc_packed_bytes(spec), dtype=torch.uint8, device=dev)
+        mats.append((spec, U, sg, V, buf))
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    in_bytes = sum(4 * (U.numel() + V.numel() + sg.numel()) for _, U, sg, V, _ in mats)
+    out_bytes = sum(trs.dc_packed_bytes(spec) for spec, *_ in mats)
+
+    def layer():
+        for spec, U, sg, V, buf in mats:
+            trs.dc_pack_device(spec, U, sg, V, buf, flag)
+
+    for _ in range(args.warmup):
+        layer()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        layer()
+    e1.record()
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    ms = e0.elapsed_time(e1) / args.steps
+    # the q matrix on the host: the C packer and the numpy oracle
+    spec, U, sg, V, buf = mats[0]
+    Uh, sgh, Vh = U.cpu().numpy(), sg.cpu().numpy(), V.cpu().numpy()
+    t0 = time.perf_counter()
+    host = trs.dc_pack(spec, Uh, sgh, Vh)
+    t_host = time.perf_counter() - t0
+    assert np.array_equal(host, buf.cpu().numpy()), "device and host packers differ"
+    t0 = time.perf_counter()
+    cu, cv, su, sv, ss = quant.compress(Uh, sgh, Vh, *spec[2:])
+    layout.pack(spec, cu, cv, su, sv, ss)
+    t_orc = time.perf_counter() - t0
+    share = 4 * (Uh.size + Vh.size + sgh.size) / in_bytes     # the q matrix's share of the layer's input
+    achieved = (in_bytes + out_bytes) / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "quantize+pack of a Llama-2-7B layer delta (7 matrices, 1/16 budget)", "value": round(1e3 / ms, 2),
+        "unit": "layers/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "dc_pack_device on q,k,v,o 4096x4096, gate,up 11008x4096, down 4096x11008, "
+                               "ranks per 1/16 budget, fp32 singular vectors in HBM"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_step": int(in_bytes + out_bytes)},
+        "host_packer_layers_per_s": round(share / t_host, 3),
+        "cpu_baseline": {"value": round(share / t_orc, 4), "unit": "layers/s", "cores": 1, "kind": "oracle",
+                         "sample": "numpy quantizer + packer on the q matrix (%.1f s), scaled by its share of the "
+                                   "layer's input bytes" % t_orc},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,11 +271,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pack", action="store_true",
+                    help="time quantize+pack on the GPU (one layer's deltas) instead of the apply step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.pack:
+        pack_bench(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the path shards by tenant with no collective, and "

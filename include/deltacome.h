@@ -171,6 +171,25 @@ dc_status dc_pack(const dc_spec* spec, const float* U, const float* sigma, const
                   void* out, size_t out_bytes);
 
 /*
+ * dc_pack_device -- dc_pack on the GPU (asynchronous on `stream`).  The same
+ * quantizer and format, bit for bit: onboarding a tenant's delta without a
+ * round trip through host memory.  [P1] technical principles and [P2]
+ * "Approach" as for dc_pack.
+ *   U, sigma, V  device fp32, layouts of dc_pack (U and V 8-byte aligned)
+ *   out          device buffer of out_bytes >= dc_packed_bytes(spec),
+ *                16-byte aligned; fully written (padding zeroed)
+ *   flag         device uint32, set to 0 by the call and to 1 if an input
+ *                is non-finite or a scale overflows fp16 (then `out` is
+ *                unspecified); read it after synchronizing the stream
+ * Host checks, before anything is enqueued: DC_ERR_INVALID_ARG (NULL),
+ * DC_ERR_SHAPE, DC_ERR_ALIGN, DC_ERR_BUFFER, DC_ERR_UNSUPPORTED (a packed
+ * buffer of 2 GiB or more); DC_ERR_HIP if a launch fails.  Allocates
+ * nothing; writes only `out` and `flag`.
+ */
+dc_status dc_pack_device(const dc_spec* spec, const float* U, const float* sigma, const float* V,
+                         void* out, size_t out_bytes, uint32_t* flag, void* stream);
+
+/*
  * dc_pack_codes -- pack already-quantized codes (host, synchronous).
  *   codes_u  host uint8 [r][out], code of u_i at row o (< 2^b of its segment)
  *   codes_v  host uint8 [r][in]

@@ -30,7 +30,7 @@ REGIONS = ("SIGMA", "VC8", "VC3", "VC2", "VS8", "VS3", "VS2",
 EXPORTS = ("dc_status_string", "dc_check_spec", "dc_packed_bytes", "dc_algorithmic_bytes",
            "dc_region", "dc_pack", "dc_pack_codes", "dc_unpack", "dc_workspace_bytes",
            "dc_apply_decode", "dc_apply_multitenant", "dc_apply_multitenant_timed",
-           "dc_apply_prefill", "dc_dequant")
+           "dc_apply_prefill", "dc_dequant", "dc_pack_device")
 STAGES = ("route", "xprep", "base", "vside", "uside")
 
 
@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
                                                  _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]
         L.dc_apply_prefill.argtypes = [vp, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.dc_dequant.argtypes = [vp, _P, _P, _P]
+        L.dc_pack_device.argtypes = [sp, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
         for name in EXPORTS:
             if name not in ("dc_status_string", "dc_packed_bytes", "dc_algorithmic_bytes",
                             "dc_workspace_bytes"):
@@ -252,6 +253,18 @@ def dc_apply_prefill(views: Sequence[DeltaView], W_base, x, seg_offsets, y, ws, 
 def dc_dequant(view: DeltaView, u_fp16, v_fp16, stream=None) -> None:
     _check(lib().dc_dequant(ctypes.byref(view.c), _dptr(u_fp16, "u_fp16"), _dptr(v_fp16, "v_fp16"),
                             _stream(stream)), "dc_dequant")
+
+
+def dc_pack_device(spec, U, sigma, V, out, flag, stream=None) -> None:
+    """Quantize and pack on the GPU (asynchronous): U [r][out], sigma [r] and
+    V [r][in] device float32 tensors; out a device uint8 tensor of at least
+    dc_packed_bytes(spec) bytes; flag a device int32/uint32 tensor of one
+    element, 1 after the stream completes if an input was non-finite or a
+    scale overflowed fp16."""
+    s = make_spec(spec)
+    _check(lib().dc_pack_device(ctypes.byref(s), _dptr(U, "U"), _dptr(sigma, "sigma"), _dptr(V, "V"),
+                                _dptr(out, "out"), out.numel() * out.element_size(), _dptr(flag, "flag"),
+                                _stream(stream)), "dc_pack_device")
 
 
 class MultitenantCall:

@@ -140,6 +140,22 @@ dc_status dc_apply_prefill(const dc_delta_view* views, int32_t n, const uint16_t
   return run(views, n, W_base, x, nullptr, seg_offsets, 2, y, seg_offsets[n], ws, ws_bytes, stream);
 }
 
+dc_status dc_pack_device(const dc_spec* spec, const float* U, const float* sigma, const float* V, void* out,
+                         size_t out_bytes, uint32_t* flag, void* stream) {
+  if (!spec || !out || !flag) return DC_ERR_INVALID_ARG;
+  if (dc_check_spec(spec) != DC_OK) return DC_ERR_SHAPE;
+  const int32_t r = spec->n8 + spec->n3 + spec->n2;
+  if (r > 0 && (!U || !V || !sigma)) return DC_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(flag, 4) || (U && !aligned(U, 8)) || (V && !aligned(V, 8)) ||
+      (sigma && !aligned(sigma, 4)))
+    return DC_ERR_ALIGN;
+  const size_t need = dc_packed_bytes(spec);
+  if (out_bytes < need) return DC_ERR_BUFFER;
+  if (need > (size_t)INT32_MAX) return DC_ERR_UNSUPPORTED;
+  return dc::launch_pack(spec->out, spec->in, spec->n8, spec->n3, spec->n2, U, sigma, V,
+                         static_cast<uint8_t*>(out), flag, stream) == 0 ? DC_OK : DC_ERR_HIP;
+}
+
 dc_status dc_dequant(const dc_delta_view* d, uint16_t* u_fp16, uint16_t* v_fp16, void* stream) {
   if (!d) return DC_ERR_INVALID_ARG;
   if (dc_check_spec(&d->spec) != DC_OK) return DC_ERR_SHAPE;

@@ -21,6 +21,45 @@ constexpr int kKBlock = 32;   // ranks per K-block of the U code regions
 
 DC_HD inline size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
 
+// IEEE fp64 -> fp16, round to nearest even, in one step from the fp64 bits
+// (no fp32 intermediate, so no double rounding).
+DC_HD inline uint16_t f64_to_f16(double d) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, d);
+  const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+  const int e = (int)((b >> 52) & 0x7FF);
+  const uint64_t frac = b & ((1ull << 52) - 1);
+  if (e == 0x7FF) return sign | (frac ? 0x7E00 : 0x7C00);
+  if (e == 0) return sign;                  // |d| < 2^-1022: rounds to zero
+  int E = e - 1023;                         // d = 1.frac * 2^E
+  if (E > 15) return sign | 0x7C00;
+  const uint64_t sig = frac | (1ull << 52); // 53-bit significand
+  const int shift = (E >= -14) ? 42 : 42 + (-14 - E);
+  if (shift >= 55) return sign;             // below half the smallest subnormal
+  uint64_t q = sig >> shift;
+  const uint64_t rem = sig & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  if (E >= -14) {
+    if (q == 2048) { q = 1024; ++E; }
+    if (E > 15) return sign | 0x7C00;
+    return (uint16_t)(sign | ((E + 15) << 10) | (q - 1024));
+  }
+  return (uint16_t)(sign | q);              // subnormal; q == 1024 is the smallest normal
+}
+
+// fp16 bits -> fp64 (exact; every fp16 value is an fp64 value).
+DC_HD inline double f16_to_f64(uint16_t h) {
+  const int e = (h >> 10) & 0x1F;
+  const uint64_t m = h & 0x3FF;
+  const uint64_t sign = (uint64_t)(h & 0x8000) << 48;
+  if (e == 31) return __builtin_bit_cast(double, sign | 0x7FF0000000000000ull | (m << 42));
+  if (e == 0) {   // subnormal: m * 2^-24, exact in fp64
+    const double v = (double)m * 5.9604644775390625e-8;
+    return (h & 0x8000) ? -v : v;
+  }
+  return __builtin_bit_cast(double, sign | ((uint64_t)(e - 15 + 1023) << 52) | (m << 42));
+}
+
 // Words one row of a 3- or 2-bit U code segment of n ranks takes: full
 // K-blocks of 32 ranks take b words, the last one ceil(m*b/32) for its m ranks.
 DC_HD inline int u_row_words(int n, int b) {
@@ -187,4 +226,6 @@ struct ApplyArgs {
 int launch_apply(const ApplyArgs& a);
 int launch_base(const uint16_t* W, const uint16_t* xt, float* ybase, int out, int in, int T, void* stream);
 int launch_dequant(const Tenant& t, int32_t out, int32_t in, uint16_t* u16, uint16_t* v16, void* stream);
+int launch_pack(int32_t out, int32_t in, int32_t n8, int32_t n3, int32_t n2, const float* U, const float* sigma,
+                const float* V, uint8_t* dst, uint32_t* flag, void* stream);
 }  // namespace dc

@@ -26,41 +26,8 @@ bool spec_ok(const dc_spec* s) {
   return r <= lim;
 }
 
-// IEEE fp64 -> fp16, round to nearest even, in one step from the fp64 bits.
-uint16_t f64_to_f16(double d) {
-  uint64_t b;
-  std::memcpy(&b, &d, 8);
-  const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
-  const int e = (int)((b >> 52) & 0x7FF);
-  const uint64_t frac = b & ((1ull << 52) - 1);
-  if (e == 0x7FF) return sign | (frac ? 0x7E00 : 0x7C00);
-  if (e == 0) return sign;                  // |d| < 2^-1022: rounds to zero
-  int E = e - 1023;                         // d = 1.frac * 2^E
-  if (E > 15) return sign | 0x7C00;
-  const uint64_t sig = frac | (1ull << 52); // 53-bit significand
-  const int shift = (E >= -14) ? 42 : 42 + (-14 - E);
-  if (shift >= 55) return sign;             // below half the smallest subnormal
-  uint64_t q = sig >> shift;
-  const uint64_t rem = sig & ((1ull << shift) - 1);
-  const uint64_t half = 1ull << (shift - 1);
-  if (rem > half || (rem == half && (q & 1))) ++q;
-  if (E >= -14) {
-    if (q == 2048) { q = 1024; ++E; }
-    if (E > 15) return sign | 0x7C00;
-    return (uint16_t)(sign | ((E + 15) << 10) | (q - 1024));
-  }
-  return (uint16_t)(sign | q);              // subnormal; q == 1024 is the smallest normal
-}
-
-double f16_to_f64(uint16_t h) {
-  const int e = (h >> 10) & 0x1F;
-  const int m = h & 0x3FF;
-  double v;
-  if (e == 0) v = std::ldexp((double)m, -24);
-  else if (e == 31) v = m ? NAN : INFINITY;
-  else v = std::ldexp((double)(m | 0x400), e - 25);
-  return (h & 0x8000) ? -v : v;
-}
+using dc::f16_to_f64;
+using dc::f64_to_f16;
 
 // Quantize one group of 128 values at `bits`; writes codes and the
 // (scale, zero) fp16 bit patterns.  Returns false on non-finite input or

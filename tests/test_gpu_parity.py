@@ -371,3 +371,77 @@ def test_graph_replay_matches_eager():
     ref_c = oap.apply_multitenant(w.cpu().numpy().view(np.uint16), xs[2].cpu().numpy().view(np.uint16),
                                   ids.cpu().numpy(), [oracle_tenant(d) for d in ds])
     check_close(y_to_f64(ys[2]), ref_c, what="graph replay vs oracle")
+
+
+# ------------------------------------------------------- quantize + pack on GPU
+PACK_SPECS = [(256, 256, 2, 8, 22), (384, 128, 3, 0, 17), (128, 384, 0, 33, 0), (512, 256, 5, 31, 65),
+              (128, 128, 0, 0, 0), (1024, 4096, 2, 6, 187), (4096, 4096, 2, 32, 968)]
+
+
+def _pack_inputs(spec, seed):
+    """Singular-vector-like rows at varied magnitudes, plus groups that test
+    the quantizer's edges: all zero (scale 1.0), constant, one-signed, and
+    exact ties w/s = k + 1/2 on the 3-bit grid of a [-1, 1] range."""
+    out, inn, n8, n3, n2 = spec
+    r = n8 + n3 + n2
+    rng = np.random.default_rng(seed)
+    U = (rng.standard_normal((r, out)) * np.exp(rng.uniform(-6, 1, (r, 1)))).astype(np.float32)
+    V = (rng.standard_normal((r, inn)) * np.exp(rng.uniform(-6, 1, (r, 1)))).astype(np.float32)
+    sigma = np.exp(rng.uniform(-3, 2, r)).astype(np.float32)
+    if r:
+        V[0, :128] = 0.0
+        U[-1, :128] = 0.375
+        V[-1, 128:256] = np.abs(V[-1, 128:256]) if inn >= 256 else V[-1, 128:256]
+        if n3:   # s_h = fp16(2/7) = 0.28564453125 on a [-1, 1] range; w = (k + 1/2) s_h is exact in fp32
+            row = U[n8, :128]
+            row[:] = np.linspace(-1, 1, 128, dtype=np.float32)
+            sh = np.float32(0.28564453125)
+            row[1:9] = np.array([-3.5, -2.5, -1.5, -0.5, 0.5, 1.5, 2.5, 3.5], np.float32) * sh
+    return U, sigma, V
+
+
+@pytest.mark.parametrize("spec", PACK_SPECS, ids=lambda s: "x".join(map(str, s)))
+def test_pack_device_matches_host(spec):
+    note("pack device", spec)
+    t = torch()
+    U, sigma, V = _pack_inputs(spec, 40 + sum(spec))
+    host = trs.dc_pack(spec, U, sigma, V)
+    nb = trs.dc_packed_bytes(spec)
+    dev = t.full((max(nb, 16),), 0xA5, dtype=t.uint8, device="cuda")   # stale bytes: the call must write all
+    flag = t.full((1,), 7, dtype=t.int32, device="cuda")
+    trs.dc_pack_device(spec, t.from_numpy(U).cuda(), t.from_numpy(sigma).cuda(), t.from_numpy(V).cuda(), dev, flag)
+    t.cuda.synchronize()
+    assert int(flag.item()) == 0
+    got = dev.cpu().numpy()[:nb]
+    assert np.array_equal(got, host), "first differing byte %d" % int(np.nonzero(got != host)[0][0])
+
+
+def test_pack_device_c0_svd_and_errors():
+    note("pack device c0 + errors")
+    t = torch()
+    c0 = synth.make_c0()
+    u, s, v = quant.svd_pairs(c0["delta"])
+    r = sum(c0["groups"])
+    spec = (256, 256) + tuple(c0["groups"])
+    U, sg, V = u[:r].astype(np.float32), s[:r].astype(np.float32), v[:r].astype(np.float32)
+    host = trs.dc_pack(spec, U, sg, V)
+    dev = t.empty(trs.dc_packed_bytes(spec), dtype=t.uint8, device="cuda")
+    flag = t.zeros(1, dtype=t.int32, device="cuda")
+    args = [t.from_numpy(a.copy()).cuda() for a in (U, sg, V)]
+    trs.dc_pack_device(spec, *args, dev, flag)
+    t.cuda.synchronize()
+    assert int(flag.item()) == 0 and np.array_equal(dev.cpu().numpy(), host)
+    for what, fix in (("nan in V", lambda a: a[2].__setitem__((3, 5), float("nan"))),
+                      ("inf sigma", lambda a: a[1].__setitem__(0, float("inf"))),
+                      ("fp16 scale overflow", lambda a: a[0].__setitem__((r - 1, 7), 1e30))):
+        bad = [a.clone() for a in args]
+        fix(bad)
+        trs.dc_pack_device(spec, *bad, dev, flag)
+        t.cuda.synchronize()
+        assert int(flag.item()) == 1, what
+        with pytest.raises(trs.DcError):
+            trs.dc_pack(spec, *[a.cpu().numpy() for a in bad])
+    # the flag is cleared by the next good call
+    trs.dc_pack_device(spec, *args, dev, flag)
+    t.cuda.synchronize()
+    assert int(flag.item()) == 0 and np.array_equal(dev.cpu().numpy(), host)

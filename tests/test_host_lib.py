@@ -233,3 +233,25 @@ def test_dequant_argument_checks(L):
 def test_status_strings():
     assert trs.dc_status_string(trs.DC_ERR_RANGE) == "DC_ERR_RANGE"
     assert trs.dc_status_string(12345) == "DC_ERR_UNKNOWN"
+
+
+def test_pack_device_argument_checks(L):
+    """Every error of dc_pack_device is found on the host before anything is
+    enqueued (fake device addresses, never dereferenced)."""
+    spec = (256, 256, 2, 8, 22)
+    s = trs.make_spec(spec)
+    nb = trs.dc_packed_bytes(spec)
+    U, G, V, OUT, FLAG = 0x300000, 0x310000, 0x320000, 0x400000, 0x500000
+    pk = L.dc_pack_device
+    assert pk(None, U, G, V, OUT, nb, FLAG, None) == trs.DC_ERR_INVALID_ARG
+    assert pk(ctypes.byref(s), U, G, V, OUT, nb, None, None) == trs.DC_ERR_INVALID_ARG     # no flag
+    assert pk(ctypes.byref(s), None, G, V, OUT, nb, FLAG, None) == trs.DC_ERR_INVALID_ARG
+    assert pk(ctypes.byref(s), U, G, V, None, nb, FLAG, None) == trs.DC_ERR_INVALID_ARG
+    assert pk(ctypes.byref(s), U + 4, G, V, OUT, nb, FLAG, None) == trs.DC_ERR_ALIGN       # U needs 8 B
+    assert pk(ctypes.byref(s), U, G, V, OUT + 8, nb, FLAG, None) == trs.DC_ERR_ALIGN       # out needs 16 B
+    assert pk(ctypes.byref(s), U, G, V, OUT, nb, FLAG + 2, None) == trs.DC_ERR_ALIGN
+    assert pk(ctypes.byref(s), U, G, V, OUT, nb - 1, FLAG, None) == trs.DC_ERR_BUFFER
+    bad = trs.make_spec((256, 200, 2, 8, 22))
+    assert pk(ctypes.byref(bad), U, G, V, OUT, nb, FLAG, None) == trs.DC_ERR_SHAPE
+    big = trs.make_spec((256, 256, 2, 8, 300))                                               # r > min(out, in)
+    assert pk(ctypes.byref(big), U, G, V, OUT, nb, FLAG, None) == trs.DC_ERR_SHAPE
