@@ -201,6 +201,38 @@ def test_multitenant_small_mixed_specs():
     assert np.array_equal(bp, bits[perm])
 
 
+def test_multitenant_max_tenants_and_empty_delta():
+    """DC_MAX_TENANTS tenants in one call, of mixed ranks, one of them with
+    every pair dropped (r = 0: its tokens get W x), tokens on every tenant,
+    on none of some, and backbone-only tokens; fused and delta-only."""
+    note("multitenant 128 tenants")
+    rng = np.random.default_rng(17)
+    n = trs.DC_MAX_TENANTS
+    shapes = [(2, 8, 22), (0, 0, 0), (1, 12, 3), (0, 3, 40), (3, 0, 0), (2, 33, 60)]
+    specs = [(128, 256) + shapes[k % len(shapes)] for k in range(n)]
+    ds = [synth.small_delta(300 + k, *s) for k, s in enumerate(specs)]
+    views = [upload(s, d) for s, d in zip(specs, ds)]
+    w = synth.base_weight(rng, 128, 256)
+    T = 200
+    ids = rng.integers(-1, n, size=T).astype(np.int32)
+    ids[:6] = [1, 1, 7, 127, -1, 0]        # the empty delta, the last tenant, the backbone bucket
+    ids[ids == 5] = 6                       # tenant 5 gets no token
+    x = synth.activations(rng, T, 256)
+    ts = [oracle_tenant(d) for d in ds]
+    te = [oracle_tenant(d, True) for d in ds]   # exact grid values: for outputs of a few 8-bit pairs on 128 rows
+    for wb in (w, None):
+        y, _, flag = _mt_run(views, wb, x, ids)
+        assert flag == 0
+        if wb is not None:
+            check_close(y, oap.apply_multitenant(wb, x, ids, ts), what="128 tenants, fused",
+                        ref_exact=oap.apply_multitenant(wb, x, ids, te))
+        else:   # outputs that are exactly zero (backbone-only or empty-delta tokens) must be zero
+            zero = (ids < 0) | np.isin(ids, [k for k in range(n) if sum(specs[k][2:]) == 0])
+            assert np.all(y[zero] == 0.0)
+            check_close(y[~zero], _delta_only_mt(x, ids, ts, 128)[~zero], what="128 tenants, delta only",
+                        ref_exact=_delta_only_mt(x, ids, te, 128)[~zero])
+
+
 def _delta_only_mt(x, ids, ts, out):
     y = np.zeros((x.shape[0], out))
     for k, tk in enumerate(ts):
