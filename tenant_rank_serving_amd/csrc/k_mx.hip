@@ -581,9 +581,13 @@ __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, con
         cw[u] = *reinterpret_cast<const uint2*>(sg.vc + (size_t)i * in + ic);
         e[u] = sg.vs[(size_t)gi * np + i];
       }
+      // partials of the live (row, token) pairs only: with two 8-bit rows and
+      // a few tokens most of the 4 x kVRows pairs are padding
+      const int nu = min(4, sg.n - r0);
       float part[4][kVRows];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
+        if (u >= nu) break;
         const float sc = f16f(e[u] & 0xFFFFu), z = f16f(e[u] >> 16);
         const uint32_t cwu[2] = {cw[u].x, cw[u].y};
         float w[8];
@@ -591,22 +595,30 @@ __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, con
         for (int j = 0; j < 8; ++j) w[j] = (float)(_Float16)(sc * ((float)((cwu[j >> 2] >> (8 * (j & 3))) & 0xFFu) - z));
 #pragma unroll
         for (int t = 0; t < kVRows; ++t) {
+          if (t >= nt) break;
           const uint32_t xw[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
           float a = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             a += w[2 * j] * __uint_as_float(xw[j] << 16) + w[2 * j + 1] * __uint_as_float(xw[j] & 0xFFFF0000u);
-          part[u][t] = ok && t < nt ? a : 0.f;
+          part[u][t] = ok ? a : 0.f;
         }
       }
+      // their wave sums
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int t = 0; t < kVRows; ++t) {
-          float v = part[u][t];
-#pragma unroll
-          for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-          if (lane == 0) red[wave][u][t] = v;
+          if (u < nu && t < nt) {
+            float v = part[u][t];
+            v += swz_xor<1>(v);
+            v += swz_xor<2>(v);
+            v += swz_xor<4>(v);
+            v += swz_xor<8>(v);
+            v += swz_xor<16>(v);
+            v += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));   // lanes 32-63
+            if (lane == 0) red[wave][u][t] = v;
+          }
         }
       __syncthreads();
       if (tid < 4 * kVRows) {
