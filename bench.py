@@ -110,7 +110,7 @@ def build_c2(layers, dev, torch, trs, synth):
     return specs, views, W, X, pool
 
 
-def cpu_baseline(trs, synth, budget_s=20.0):
+def cpu_baseline(trs, synth, budget_s=15.0):
     """The oracle (plain numpy fp64, applied from packed buffers) timed on a
     bounded sample of the same workload, extrapolated to one whole step."""
     import numpy as np
@@ -123,6 +123,7 @@ def cpu_baseline(trs, synth, budget_s=20.0):
     sample = []
     t_start = time.time()
     for mi in (0, 4, 6):                      # q (4096^2), gate (11008x4096), down (4096x11008)
+        t_shape = time.time()
         _, out, inn = synth.LLAMA2_7B[mi]
         w = synth.make_c2_base(0, mi)
         x = synth.make_c2_x(0, mi)
@@ -130,7 +131,9 @@ def cpu_baseline(trs, synth, budget_s=20.0):
         oap.apply_factored(w, x, np.zeros((0, out)), np.zeros(0), np.zeros((0, inn)))
         t_base = time.perf_counter() - t0
         times = []
-        for k in touched[:2]:
+        for k in touched:                     # at least two tenants, then until a third of the budget
+            if len(times) >= 2 and time.time() - t_shape > budget_s / 3:
+                break
             d = synth.make_c2_delta(0, mi, k)
             buf = layout.pack(d.spec, d.codes_u, d.codes_v, d.sz_u, d.sz_v, d.sigma)
             sel = np.nonzero(ids == k)[0]
@@ -139,8 +142,6 @@ def cpu_baseline(trs, synth, budget_s=20.0):
             times.append(time.perf_counter() - t0)
             sample.append("layer0/%s/tenant%d" % (synth.LLAMA2_7B[mi][0], k))
         per_shape[mi] = (t_base, float(np.mean(times)))
-        if time.time() - t_start > budget_s:
-            break
     # step = 32 layers x (4 square + 2 up-proj + 1 down-proj) x (base + touched tenants)
     counts = {0: 4, 4: 2, 6: 1}
     step_s = 0.0
