@@ -127,6 +127,14 @@ __device__ __forceinline__ float swz_xor(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (X << 10) | 0x1F));
 }
 
+// Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
+// wait for the wave's global loads and stores in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ v8i v8_of(const uint4& a, const uint4& b) {
   return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
@@ -164,19 +172,21 @@ struct SegArg {
 
 // ------------------------------------------------------------------- prep
 // Block 0 routes the tokens (stable counting sort by tenant; bucket n holds
-// the backbone-only tokens) and lists the buckets that have tokens, each
+// the backbone-only tokens; its barriers order LDS only, so they do not wait
+// for its global stores, which only later kernels read) and lists the
+// buckets that have tokens, each
 // with its tenant record and routed range, so that the V and U blocks of
 // buckets with tokens come first in their grids and find everything they
 // need in one load.  Every other wave turns one (token, 128-group) of x into
 // fp8 hi/lo A fragments, their E8M0 scales and the group sum.
-__device__ __forceinline__ void list_active(const TenantTable& tt, int32_t n, const int* so,
+__device__ __forceinline__ void list_active(const Tenant& mine, int32_t n, const int* so,
                                             ActEntry* __restrict__ act) {
   __shared__ int wcnt[4];
   const int tid = threadIdx.x, b = tid, lane = tid & 63, wave = tid >> 6;
   const bool live = b <= n && so[b + 1] > so[b];
   const uint64_t m = __ballot(live);
   if (lane == 0) wcnt[wave] = __popcll(m);
-  __syncthreads();
+  lds_barrier();
   int pos = __popcll(m & ((1ull << lane) - 1)), total = 0;
   for (int w = 0; w < 4; ++w) {
     if (w < wave) pos += wcnt[w];
@@ -184,10 +194,10 @@ __device__ __forceinline__ void list_active(const TenantTable& tt, int32_t n, co
   }
   if (live) {
     ActEntry e;
-    e.base = b < n ? tt.t[b].base : nullptr;
-    e.n8 = b < n ? tt.t[b].n8 : 0;
-    e.n3 = b < n ? tt.t[b].n3 : 0;
-    e.n2 = b < n ? tt.t[b].n2 : 0;
+    e.base = b < n ? mine.base : nullptr;
+    e.n8 = b < n ? mine.n8 : 0;
+    e.n3 = b < n ? mine.n3 : 0;
+    e.n2 = b < n ? mine.n2 : 0;
     e.k = b;
     e.p0 = so[b];
     e.p1 = so[b + 1];
@@ -209,10 +219,17 @@ __global__ void __launch_bounds__(256) k_prep(TenantTable tt, const uint16_t* __
                                               uint32_t* __restrict__ xsc, float* __restrict__ xsum,
                                               uint16_t* __restrict__ xt, float* __restrict__ tv, int32_t ntv) {
   const int tid = threadIdx.x;
-  for (int i = blockIdx.x * 256 + tid; i < ntv; i += gridDim.x * 256) tv[i] = 0.f;   // t accumulates atomically
+  // t accumulates atomically: zeroed by the blocks after the first (the
+  // first block's barriers would wait for its stores to finish)
+  if (blockIdx.x > 0)
+    for (int i = (blockIdx.x - 1) * 256 + tid; i < ntv; i += (gridDim.x - 1) * 256) tv[i] = 0.f;
   if (blockIdx.x == 0) {
     static_assert(DC_MAX_TENANTS + 1 <= 256, "one thread per bucket");
     __shared__ int so[DC_MAX_TENANTS + 2];   // bucket starts
+    // thread b's tenant record, read first: the kernel arguments live in
+    // memory and the indexing is per thread
+    Tenant mine{};
+    if (tid < n) mine = tt.t[tid];
     if (mode != 1) {
       for (int p = tid; p < T; p += blockDim.x) perm[p] = p;
       if (tid == 0) {
@@ -221,46 +238,79 @@ __global__ void __launch_bounds__(256) k_prep(TenantTable tt, const uint16_t* __
         for (int k = 0; k <= n + 1; ++k) offs[k] = so[k];
         *flags = 0;
       }
-      __syncthreads();
-      list_active(tt, n, so, act);
+      lds_barrier();
+      list_active(mine, n, so, act);
       return;
     }
     __shared__ int cnt[DC_MAX_TENANTS + 1];   // tokens per bucket
     __shared__ int next[DC_MAX_TENANTS + 1];
-    __shared__ int bkt[256];
+    __shared__ __attribute__((aligned(16))) int bkt[256];
     __shared__ int bad;
+    __shared__ int wsum[4];
     for (int b = tid; b <= n; b += blockDim.x) cnt[b] = 0;
     if (tid == 0) bad = 0;
-    __syncthreads();
+    lds_barrier();
+    int b0 = -1;   // bucket of token tid (the first chunk is kept for the placement below)
     for (int t = tid; t < T; t += blockDim.x) {
       int k = ids[t];
       if (k < -1 || k >= n) { bad = 1; k = -1; }
-      atomicAdd(&cnt[k < 0 ? n : k], 1);
+      const int b = k < 0 ? n : k;
+      if (t == tid) b0 = b;
+      atomicAdd(&cnt[b], 1);
     }
-    __syncthreads();
-    if (tid == 0) {
-      int s = 0;
-      for (int b = 0; b <= n; ++b) { offs[b] = s; so[b] = s; next[b] = s; s += cnt[b]; }
-      offs[n + 1] = s;
-      so[n + 1] = s;
-      *flags = bad ? 1u : 0u;
+    lds_barrier();
+    {  // exclusive scan of the bucket counts, one thread per bucket
+      const int lane = tid & 63, wv = tid >> 6;
+      const int c = tid <= n ? cnt[tid] : 0;
+      int v = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(v, d, 64);
+        if (lane >= d) v += u;
+      }
+      if (lane == 63) wsum[wv] = v;
+      lds_barrier();
+      for (int w = 0; w < wv; ++w) v += wsum[w];
+      if (tid <= n) {
+        offs[tid] = v - c;
+        so[tid] = v - c;
+        next[tid] = v - c;
+      }
+      if (tid == n) {
+        offs[n + 1] = v;
+        so[n + 1] = v;
+      }
+      if (tid == 0) *flags = bad ? 1u : 0u;
     }
-    __syncthreads();
-    list_active(tt, n, so, act);
+    lds_barrier();
+    list_active(mine, n, so, act);
     for (int c0 = 0; c0 < T; c0 += blockDim.x) {
       const int t = c0 + tid;
       int b = -1;
-      if (t < T) { const int k = ids[t]; b = (k < 0 || k >= n) ? n : k; }
-      bkt[tid] = b;
-      __syncthreads();
       if (t < T) {
+        if (c0 == 0) {
+          b = b0;
+        } else {
+          const int k = ids[t];
+          b = (k < 0 || k >= n) ? n : k;
+        }
+      }
+      bkt[tid] = b;
+      lds_barrier();
+      if (t < T) {   // rank among the chunk's earlier tokens of its bucket: four per LDS read
         int rank = 0;
-        for (int j = 0; j < tid; ++j) rank += (bkt[j] == b);
+        const int4* b4 = reinterpret_cast<const int4*>(bkt);
+#pragma unroll 4
+        for (int j4 = 0; j4 < (tid >> 2); ++j4) {
+          const int4 v = b4[j4];
+          rank += (v.x == b) + (v.y == b) + (v.z == b) + (v.w == b);
+        }
+        for (int j = tid & ~3; j < tid; ++j) rank += (bkt[j] == b);
         perm[next[b] + rank] = t;
       }
-      __syncthreads();
+      lds_barrier();
       if (t < T) atomicAdd(&next[b], 1);
-      __syncthreads();
+      lds_barrier();
     }
     return;
   }
