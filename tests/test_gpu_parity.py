@@ -233,6 +233,40 @@ def test_multitenant_max_tenants_and_empty_delta():
                         ref_exact=_delta_only_mt(x, ids, te, 128)[~zero])
 
 
+def test_multitenant_many_tokens():
+    """More tokens than the routing block has threads (three chunks of 256):
+    the stable sort across chunks, checked against the oracle and, token by
+    token, against single-tenant calls (same order within a tenant, so the
+    same bits); an invalid id in the last chunk still raises the flag."""
+    note("multitenant 700 tokens")
+    rng = np.random.default_rng(23)
+    specs = [(128, 256, 2, 8, 22), (128, 256, 1, 3, 40), (128, 256, 0, 9, 0), (128, 256, 2, 0, 17),
+             (128, 256, 1, 1, 1), (128, 256, 3, 20, 30)]
+    ds = [synth.small_delta(500 + k, *s) for k, s in enumerate(specs)]
+    views = [upload(s, d) for s, d in zip(specs, ds)]
+    w = synth.base_weight(rng, 128, 256)
+    T = 700
+    ids = rng.integers(-1, len(specs), size=T).astype(np.int32)
+    x = synth.activations(rng, T, 256)
+    ts = [oracle_tenant(d) for d in ds]
+    for wb in (w, None):
+        y, bits, flag = _mt_run(views, wb, x, ids)
+        assert flag == 0
+        check_close(y, oap.apply_multitenant(wb, x, ids, ts) if wb is not None else
+                    _delta_only_mt(x, ids, ts, 128), what="mt 700")
+    _, bits, _ = _mt_run(views, w, x, ids)
+    for k in range(len(specs)):
+        sel = np.nonzero(ids == k)[0]
+        assert sel.size > 0
+        _, single = run_decode(ds[k], w, x[sel])
+        assert np.array_equal(bits[sel], single)
+    bad = ids.copy()
+    bad[650] = len(specs)                   # out of range, in the third chunk: backbone only, flagged
+    y2, _, flag2 = _mt_run(views, w, x, bad)
+    assert flag2 == 1
+    check_close(y2, oap.apply_multitenant(w, x, np.where(bad >= len(specs), -1, bad), ts), what="mt 700 bad id")
+
+
 def _delta_only_mt(x, ids, ts, out):
     y = np.zeros((x.shape[0], out))
     for k, tk in enumerate(ts):
