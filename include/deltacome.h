@@ -232,6 +232,10 @@ size_t dc_workspace_bytes(int32_t op, const dc_spec* specs, int32_t n, int32_t T
  *   ws      device workspace of ws_bytes >= dc_workspace_bytes(DC_OP_DECODE,..)
  *   stream  hipStream_t
  * T = 0 is a no-op returning DC_OK.  x and y must not overlap.
+ * Summation order: parts of V x (in wider than 2048) and, for T <= 256, of
+ * W_base x (in wider than 512) are added with float atomics, so two calls may
+ * round an output differently in its last bit; batches of more than 256
+ * tokens compute W_base x in another order.
  */
 dc_status dc_apply_decode(const dc_delta_view* d, const uint16_t* W_base, const uint16_t* x,
                           uint16_t* y, int32_t T, void* ws, size_t ws_bytes, void* stream);

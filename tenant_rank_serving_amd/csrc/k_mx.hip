@@ -217,12 +217,15 @@ __global__ void __launch_bounds__(256) k_prep(TenantTable tt, const uint16_t* __
                                               ActEntry* __restrict__ act,
                                               uint32_t* __restrict__ flags, uint8_t* __restrict__ xf,
                                               uint32_t* __restrict__ xsc, float* __restrict__ xsum,
-                                              uint16_t* __restrict__ xt, float* __restrict__ tv, int32_t ntv) {
+                                              uint16_t* __restrict__ xt, float* __restrict__ tv, int32_t ntv,
+                                              float* __restrict__ yb, int32_t nyb) {
   const int tid = threadIdx.x;
   // t accumulates atomically: zeroed by the blocks after the first (the
   // first block's barriers would wait for its stores to finish)
-  if (blockIdx.x > 0)
+  if (blockIdx.x > 0) {
     for (int i = (blockIdx.x - 1) * 256 + tid; i < ntv; i += (gridDim.x - 1) * 256) tv[i] = 0.f;
+    for (int i = (blockIdx.x - 1) * 256 + tid; i < nyb; i += (gridDim.x - 1) * 256) yb[i] = 0.f;   // W x, when split over K
+  }
   if (blockIdx.x == 0) {
     static_assert(DC_MAX_TENANTS + 1 <= 256, "one thread per bucket");
     __shared__ int so[DC_MAX_TENANTS + 2];   // bucket starts
@@ -1021,8 +1024,9 @@ int launch_apply(const ApplyArgs& a) {
   };
   mark(DC_STAGE_ROUTE);
   mark(DC_STAGE_XPREP);
+  const int nyb = a.W && base_splits(a.out, a.in, a.T) > 1 ? a.T * a.out : 0;
   hipLaunchKernelGGL(k_prep, dim3((unsigned)(1 + (items + 3) / 4)), dim3(256), 0, st, *a.tenants, a.x, a.ids, a.T,
-                     a.in, a.n, a.mode, seg, offs, perm, act, flags, xf, xsc, xsum, xt, tv, a.T * a.wl.rs);
+                     a.in, a.n, a.mode, seg, offs, perm, act, flags, xf, xsc, xsum, xt, tv, a.T * a.wl.rs, ybase, nyb);
   mark(DC_STAGE_BASE);
   if (a.W) launch_base(a.W, xt, ybase, a.out, a.in, a.T, a.stream);
   mark(DC_STAGE_VSIDE);

@@ -16,6 +16,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufFlags = 0x00020000;   // buffer resource word 3: raw 32-bit dwords, bounds-checked
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -155,6 +156,95 @@ __global__ void __launch_bounds__(256) k_base(const uint16_t* __restrict__ W, co
   }
 }
 
+// Split-K form for a few token groups (T <= 256): 64 rows of W per block
+// (wave w: rows 16w..16w+15) and one range of at most kSKSteps K-steps
+// (blockIdx.y), so that the 4 waves share x: at the start each wave copies
+// its 16-token tile of x for the whole range straight into LDS with
+// direct-to-LDS loads (a fixed count, all in flight at once), next to the
+// first kSKDepth K-steps of its W rows; after one barrier the loop streams W
+// kSKDepth steps ahead with no further synchronization.  The partial sums
+// go through LDS transposed, so that one wave instruction adds 64
+// consecutive rows of one token into ybase (zeroed by the prep kernel) with
+// float atomics; a single range stores them.
+constexpr int kSKSteps = 16;   // K-steps per range: 4 KB of x (64 tokens) each, 64 KB of LDS
+constexpr int kSKDepth = 8;    // W K-steps in flight per wave
+typedef __attribute__((address_space(3))) void base_lds_t;
+
+__device__ __forceinline__ void lds_barrier() {   // orders LDS only: W loads stay in flight
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__global__ void __launch_bounds__(256) k_base_sk(const uint16_t* __restrict__ W, const uint16_t* __restrict__ xt,
+                                                 float* __restrict__ ybase, int32_t out, int32_t in, int32_t T,
+                                                 int32_t nks) {
+  __shared__ __attribute__((aligned(16))) uint4 xs[kSKSteps][4][64];   // [step][token tile][lane] B tiles
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r0 = blockIdx.x * 64;
+  const int t0 = blockIdx.z * 64;
+  const int tiles = (T + 15) / 16;
+  const int nall = in / 32;
+  const int s0 = blockIdx.y * kSKSteps, nst = min(kSKSteps, nall - s0);   // this block's K-steps
+  // x: wave w copies token tile w (the last tile again past T: masked below)
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xt), 0, nall * tiles * 1024, kBufFlags);
+  const int tile = min(t0 / 16 + wave, tiles - 1);
+#pragma unroll
+  for (int st = 0; st < kSKSteps; ++st) {
+    const int ks = s0 + min(st, nst - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (base_lds_t*)&xs[st][wave][0], 16,
+                                             (ks * tiles + tile) * 1024 + lane * 16, 0, 0, 0);
+  }
+  // W: lane l holds row l%16 of the wave's 16, k = 8(l/16) .. +8 of a step
+  const uint16_t* wa = W + (size_t)(r0 + 16 * wave + (lane & 15)) * in + (size_t)s0 * 32 + (lane >> 4) * 8;
+  uint4 a[kSKDepth];
+  auto load_a = [&](int slot, int st) __attribute__((always_inline)) {
+    a[slot] = *reinterpret_cast<const uint4*>(wa + (size_t)min(st, nst - 1) * 32);
+  };
+#pragma unroll
+  for (int d = 0; d < kSKDepth; ++d) load_a(d, d);
+  uint32_t keep[4];   // all ones for a lane whose token exists
+#pragma unroll
+  for (int j = 0; j < 4; ++j) keep[j] = t0 + 16 * j + (lane & 15) < T ? ~0u : 0u;
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  lds_barrier();   // every wave's x copies have landed (the fence waits for them)
+#pragma unroll
+  for (int st = 0; st < kSKSteps; ++st) {
+    const uint32_t live = st < nst ? ~0u : 0u;   // zero for the steps past the range
+    uint4 av = a[st % kSKDepth];
+    if (st + kSKDepth < kSKSteps) load_a(st % kSKDepth, st + kSKDepth);
+    av.x &= live; av.y &= live; av.z &= live; av.w &= live;
+    const bf16x8 ab = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 bv = xs[st][j][lane];
+      bv.x &= keep[j]; bv.y &= keep[j]; bv.z &= keep[j]; bv.w &= keep[j];
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, __builtin_bit_cast(bf16x8, bv), acc[j], 0, 0, 0);
+    }
+  }
+  // D layout: lane holds token column lane%16 of tile j and rows 4(lane/16)+i
+  // of the wave's 16; transpose to [token][row] (padded) over the x copies
+  lds_barrier();
+  float* red = reinterpret_cast<float*>(&xs[0][0][0]);   // [64][65]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(16 * j + (lane & 15)) * 65 + 16 * wave + 4 * (lane >> 4) + i] = acc[j][i];
+  lds_barrier();
+  const int ntok = min(64, T - t0);
+  for (int tl = wave; tl < ntok; tl += 4) {   // wave: tokens wave, wave + 4, ..; lane: row
+    float* dst = ybase + (size_t)(t0 + tl) * out + r0 + lane;
+    const float v = red[tl * 65 + lane];
+    if (nks > 1)
+      atomicAdd(dst, v);
+    else
+      *dst = v;
+  }
+}
+
 // -------------------------------------------------------------- dequantize
 // fp16 bits of s*(q-z) for every element of U [r][out] and V [r][in].
 __global__ void __launch_bounds__(256) k_dequant(Tenant tn, int32_t out, int32_t in, uint16_t* __restrict__ u16,
@@ -199,8 +289,18 @@ __global__ void __launch_bounds__(256) k_dequant(Tenant tn, int32_t out, int32_t
 
 }  // namespace
 
+int base_splits(int out, int in, int T) {
+  return T <= 256 ? (in / 32 + kSKSteps - 1) / kSKSteps : 0;
+}
+
 int launch_base(const uint16_t* W, const uint16_t* xt, float* ybase, int out, int in, int T, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int nks = base_splits(out, in, T);
+  if (nks > 0) {
+    const dim3 g((unsigned)(out / 64), (unsigned)nks, (unsigned)((T + 63) / 64));
+    hipLaunchKernelGGL(k_base_sk, g, dim3(256), 0, st, W, xt, ybase, out, in, T, nks);
+    return (int)hipGetLastError();
+  }
   // full groups of 64 tokens, then the tail group with its own tile count
   const int full = T / 64, tail = (T % 64 + 15) / 16;
   const dim3 gf((unsigned)(out / 16), (unsigned)full), gt((unsigned)(out / 16), 1u);
