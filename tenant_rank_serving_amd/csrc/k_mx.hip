@@ -172,13 +172,14 @@ struct SegArg {
 
 // ------------------------------------------------------------------- prep
 // Block 0 routes the tokens (stable counting sort by tenant; bucket n holds
-// the backbone-only tokens; its barriers order LDS only, so they do not wait
-// for its global stores, which only later kernels read) and lists the
-// buckets that have tokens, each
-// with its tenant record and routed range, so that the V and U blocks of
-// buckets with tokens come first in their grids and find everything they
-// need in one load.  Every other wave turns one (token, 128-group) of x into
-// fp8 hi/lo A fragments, their E8M0 scales and the group sum.
+// the backbone-only tokens) and lists the buckets that have tokens, each with
+// its tenant record and routed range, so that the V and U blocks of buckets
+// with tokens come first in their grids and find everything they need in one
+// load.  Its barriers order LDS only: they do not wait for its global
+// stores, which only later kernels read.  Every other wave turns one (token,
+// 128-group) of x into fp8 hi/lo A fragments, their E8M0 scales and the
+// group sum; the other blocks also zero t and, when the backbone product is
+// split over K, W x (both are accumulated with float atomics).
 __device__ __forceinline__ void list_active(const Tenant& mine, int32_t n, const int* so,
                                             ActEntry* __restrict__ act) {
   __shared__ int wcnt[4];
