@@ -190,6 +190,35 @@ dc_status dc_pack_device(const dc_spec* spec, const float* U, const float* sigma
                          void* out, size_t out_bytes, uint32_t* flag, void* stream);
 
 /*
+ * dc_allocate_bits -- one bit width per singular pair for a storage budget
+ * (host, synchronous, deterministic).  [P4] "Enhancing Delta Compression in
+ * LLMs via SVD-based Quantization Error Minimization", §2.2: the widths
+ * minimize the summed quantization error subject to a bit budget, one width
+ * per row, widths from a candidate set (a 0/1 integer program; §2.1 eq. 5
+ * gives the error of row i as about Sigma_ii^2 * Delta V_i X X^T Delta V_i^T
+ * for calibration samples X).  Solved exactly as a multiple-choice knapsack
+ * by dynamic programming over the budget used: time r * (budget+1) * nb,
+ * memory r * (budget+1) bytes.
+ *   r       pairs
+ *   nb      candidate widths, 1..127
+ *   cost    host int32 [nb], storage units of each candidate (>= 0); with
+ *           this format a pair at b bits stores b * (out + in) bits, so
+ *           cost = b and budget = the allowed sum of widths
+ *   err     host double [r][nb], error of pair i at candidate k (finite)
+ *   budget  total units allowed
+ *   choice  host int32 [r], written: the candidate index of each pair
+ *   total   host double, written if not NULL: the least total error
+ * A row's candidates are tried in index order and a later one replaces an
+ * earlier one only if strictly better; among end states of equal error the
+ * one using the least budget wins.  Errors: DC_ERR_INVALID_ARG (NULL, r < 0,
+ * nb out of range, a negative cost, a non-finite error), DC_ERR_RANGE (no
+ * choice fits the budget), DC_ERR_UNSUPPORTED (r * (budget+1) of 2^31 or
+ * more).  Allocates host memory for its tables; writes only choice, total.
+ */
+dc_status dc_allocate_bits(int32_t r, int32_t nb, const int32_t* cost, const double* err, int64_t budget,
+                           int32_t* choice, double* total);
+
+/*
  * dc_pack_codes -- pack already-quantized codes (host, synchronous).
  *   codes_u  host uint8 [r][out], code of u_i at row o (< 2^b of its segment)
  *   codes_v  host uint8 [r][in]

@@ -15,7 +15,8 @@ Pages cited (by title, then section):
        "Approach", "Key results", "Experimental setup" (Builds on: GPTQ).
   [P4] "Enhancing Delta Compression in LLMs via SVD-based Quantization Error
        Minimization" (gist.science explainer of the follow-up PrinMix): §2.1
-       (W = U Sigma V, row-wise quantization of V), §2.4 (pipeline).
+       (W = U Sigma V, row-wise quantization of V; eq. 5, the error of a
+       row), §2.2 (bit allocation as a 0/1 integer program), §2.4 (pipeline).
 
 What the pages fix and what they leave open is listed per function.  Where
 they are silent the reading taken is marked [R]; every [R] is also listed in
@@ -25,6 +26,7 @@ Modules:
   quant   SVD into singular pairs, rank groups, RTN quantizer, dequantizer
   layout  the packed byte format (pack / unpack)
   apply   y = W x + U diag(sigma) V x in fp64, brute-force loop, routing
+  alloc   bit allocation: eq. 5 errors, exact knapsack program, brute force
 
 Every function here is pinned by a test in tests/test_oracle_*.py against
 something other than itself (closed forms, hand-derived values, brute force,

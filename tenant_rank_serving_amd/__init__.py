@@ -9,5 +9,5 @@ from ._lib import (  # noqa: F401
     DC_ERR_UNSUPPORTED, DC_MAX_TENANTS, DC_OK, DC_OP_DECODE, DC_OP_MULTITENANT, DC_OP_PREFILL,
     EXPORTS, LIB_PATH, MultitenantCall, REGIONS, DcError, DeltaView, dc_algorithmic_bytes, dc_apply_decode,
     dc_apply_multitenant, dc_apply_multitenant_timed, dc_apply_prefill, STAGES, dc_check_spec, dc_dequant, dc_pack, dc_pack_codes,
-    dc_pack_device, dc_packed_bytes, dc_region, dc_status_string, dc_unpack, dc_workspace_bytes, lib, make_spec,
+    dc_allocate_bits, dc_pack_device, dc_packed_bytes, dc_region, dc_status_string, dc_unpack, dc_workspace_bytes, lib, make_spec,
 )

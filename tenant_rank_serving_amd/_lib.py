@@ -30,7 +30,7 @@ REGIONS = ("SIGMA", "VC8", "VC3", "VC2", "VS8", "VS3", "VS2",
 EXPORTS = ("dc_status_string", "dc_check_spec", "dc_packed_bytes", "dc_algorithmic_bytes",
            "dc_region", "dc_pack", "dc_pack_codes", "dc_unpack", "dc_workspace_bytes",
            "dc_apply_decode", "dc_apply_multitenant", "dc_apply_multitenant_timed",
-           "dc_apply_prefill", "dc_dequant", "dc_pack_device")
+           "dc_apply_prefill", "dc_dequant", "dc_pack_device", "dc_allocate_bits")
 STAGES = ("route", "xprep", "base", "vside", "uside")
 
 
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.dc_apply_prefill.argtypes = [vp, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.dc_dequant.argtypes = [vp, _P, _P, _P]
         L.dc_pack_device.argtypes = [sp, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
+        L.dc_allocate_bits.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int64, _P, _P]
         for name in EXPORTS:
             if name not in ("dc_status_string", "dc_packed_bytes", "dc_algorithmic_bytes",
                             "dc_workspace_bytes"):
@@ -299,3 +300,19 @@ class MultitenantCall:
         st = self._fn_t(*self.args, ev)
         if st != DC_OK:
             raise DcError(st, "dc_apply_multitenant_timed")
+
+
+def dc_allocate_bits(err, cost, budget: int):
+    """One candidate per pair minimizing the summed error within the budget
+    (host): err [r][nb] float64, cost [nb] int.  Returns (choice int32 [r],
+    total error)."""
+    e = np.ascontiguousarray(err, dtype=np.float64)
+    if e.ndim != 2:
+        raise ValueError("err must be [r][nb]")
+    c = np.ascontiguousarray(cost, dtype=np.int32)
+    r, nb = e.shape
+    choice = np.zeros(r, np.int32)
+    total = ctypes.c_double(0.0)
+    _check(lib().dc_allocate_bits(r, nb, c.ctypes.data, e.ctypes.data, int(budget), choice.ctypes.data,
+                                  ctypes.addressof(total)), "dc_allocate_bits")
+    return choice, total.value

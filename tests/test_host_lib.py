@@ -255,3 +255,48 @@ def test_pack_device_argument_checks(L):
     assert pk(ctypes.byref(bad), U, G, V, OUT, nb, FLAG, None) == trs.DC_ERR_SHAPE
     big = trs.make_spec((256, 256, 2, 8, 300))                                               # r > min(out, in)
     assert pk(ctypes.byref(big), U, G, V, OUT, nb, FLAG, None) == trs.DC_ERR_SHAPE
+
+
+# ----------------------------------------------------------- bit allocation
+def test_allocate_bits_matches_oracle():
+    """dc_allocate_bits against the oracle's dynamic program: the same choice
+    for every pair and the same total, bit for bit (same tie rules, same
+    summation order), on random tables and on a 4096-pair table at the 1/16
+    budget of a 4096 x 4096 matrix."""
+    from oracle import alloc
+    rng = np.random.default_rng(21)
+    cost = [0, 2, 3, 8]
+    for r, budget in ((1, 0), (7, 10), (50, 60), (200, 333)):
+        err = np.sort(rng.random((r, 4)) * rng.choice([1.0, 1e3, 1e-3], (r, 1)), axis=1)[:, ::-1].copy()
+        err[r // 2] = err[0]                       # tied rows
+        ref_choice, ref_total = alloc.allocate_exact(err, cost, budget)
+        choice, total = trs.dc_allocate_bits(err, cost, budget)
+        assert np.array_equal(choice, ref_choice) and total == ref_total
+    sigma = np.sort(rng.random(4096))[::-1] ** 4
+    err = sigma[:, None] ** 2 * np.array([1.0, 0.1, 0.02, 1e-4])[None, :] * (1 + 0.1 * rng.random((4096, 4)))
+    budget = 4096 * 4096 // 8192
+    ref_choice, ref_total = alloc.allocate_exact(err, cost, budget)
+    choice, total = trs.dc_allocate_bits(err, cost, budget)
+    assert np.array_equal(choice, ref_choice) and total == ref_total
+
+
+def test_allocate_bits_argument_checks(L):
+    f = L.dc_allocate_bits
+    err = np.ones((3, 2))
+    cost = np.array([1, 2], np.int32)
+    ch = np.zeros(3, np.int32)
+    P = lambda a: a.ctypes.data
+    assert f(3, 2, P(cost), P(err), 6, P(ch), None) == trs.DC_OK
+    assert f(3, 2, None, P(err), 6, P(ch), None) == trs.DC_ERR_INVALID_ARG
+    assert f(3, 0, P(cost), P(err), 6, P(ch), None) == trs.DC_ERR_INVALID_ARG
+    assert f(-1, 2, P(cost), P(err), 6, P(ch), None) == trs.DC_ERR_INVALID_ARG
+    assert f(3, 2, P(cost), P(err), -1, P(ch), None) == trs.DC_ERR_INVALID_ARG
+    neg = np.array([1, -2], np.int32)
+    assert f(3, 2, P(neg), P(err), 6, P(ch), None) == trs.DC_ERR_INVALID_ARG
+    bad = err.copy()
+    bad[1, 1] = np.nan
+    assert f(3, 2, P(cost), P(bad), 6, P(ch), None) == trs.DC_ERR_INVALID_ARG
+    assert f(3, 2, P(cost), P(err), 2, P(ch), None) == trs.DC_ERR_RANGE        # three rows of cost >= 1
+    assert f(3000, 2, P(cost), P(np.ones((3000, 2))), 1 << 20, P(np.zeros(3000, np.int32)), None) == \
+        trs.DC_ERR_UNSUPPORTED                                                  # 3000 x 2^20 choice bytes
+    assert f(0, 2, P(cost), None, 0, None, None) == trs.DC_OK                  # no pairs
