@@ -85,6 +85,45 @@ def test_c0_end_to_end():
         check_close(y_to_f64(y), ref, what="c0 %s" % ("fused" if w is not None else "delta"))
 
 
+def test_allocated_tenants_end_to_end():
+    """Bit allocation by dc_allocate_bits (eq. 5 errors, exact program) for
+    three tenants with different spectra and calibration sets: each gets its
+    own (n8, n3, n2), its pairs are ordered by width, packed on the host and
+    applied in one multi-tenant call on the GPU, against the oracle."""
+    note("allocated tenants")
+    from oracle import alloc
+    t = torch()
+    rng = np.random.default_rng(31)
+    out = inn = 256
+    budget = sum(b * n for b, n in zip((8, 3, 2), quant.rank_groups(out, inn, 16)))
+    views, tenants, counts = [], [], []
+    for k, p in enumerate((1.5, 0.8, 2.5)):
+        a = np.linalg.qr(rng.standard_normal((out, out)))[0]
+        b = np.linalg.qr(rng.standard_normal((inn, inn)))[0]
+        delta = (a * np.arange(1, out + 1) ** -p) @ b.T * 0.05
+        u, s, v = quant.svd_pairs(delta)
+        err = alloc.error_table(s, v, rng.standard_normal((inn, 16)) * (1 + k))
+        choice, _ = trs.dc_allocate_bits(err, list(alloc.WIDTHS), budget)
+        (n8, n3, n2), order = alloc.counts_and_order(choice, alloc.WIDTHS, s)
+        counts.append((n8, n3, n2))
+        spec = (out, inn, n8, n3, n2)
+        u32, s32, v32 = (a_[order].astype(np.float32) for a_ in (u, s, v))
+        buf = trs.dc_pack(spec, u32, s32, v32)
+        views.append(trs.DeltaView(spec, t.from_numpy(buf.copy()).cuda()))
+        cu, cv, su, sv, sg = quant.compress(u32, s32, v32, n8, n3, n2)
+        tenants.append(oap.dequant_pairs(cu, cv, su, sv) + (sg,))
+    assert len(set(counts)) > 1, counts          # the allocations differ between tenants
+    w = synth.base_weight(rng, out, inn)
+    x = synth.activations(rng, 24, inn)
+    ids = rng.integers(-1, 3, size=24).astype(np.int32)
+    ts = [(uh, sg, vh) for uh, vh, sg in tenants]
+    for wb in (w, None):
+        y, _, flag = _mt_run(views, wb, x, ids)
+        assert flag == 0
+        check_close(y, oap.apply_multitenant(wb, x, ids, ts) if wb is not None else
+                    _delta_only_mt(x, ids, ts, out), what="allocated %s" % ("fused" if wb is not None else "delta"))
+
+
 # ----------------------------------------------- decode, segments and tails
 SEG_CASES = [(256, 256, 2, 8, 22, 4), (384, 256, 3, 37, 71, 1), (384, 256, 3, 37, 71, 5),
              (256, 384, 2, 40, 100, 17), (128, 128, 0, 0, 5, 2), (128, 128, 1, 0, 0, 3),
