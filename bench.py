@@ -58,9 +58,37 @@ class Hip:
         self.L.hipEventDestroy(ctypes.c_void_p(e))
 
 
+def spec_templates(sp, dev, torch, trs, synth):
+    """Two host-packed buffers of one spec (scale/zero/sigma drawn, codes
+    zero) and the mask of its valid code bits: a tenant's buffer is random
+    code bits ANDed with the mask and ORed with a template."""
+    import numpy as np
+    out, inn, n8, n3, n2 = sp
+    r = n8 + n3 + n2
+    ts = []
+    for k in range(2):
+        d = synth.random_delta_codes(np.random.default_rng(1000 + 7 * k + out), out, inn, n8, n3, n2)
+        nc = trs.dc_pack_codes(sp, np.zeros_like(d.codes_u), np.zeros_like(d.codes_v), d.sz_u, d.sz_v, d.sigma)
+        ts.append(torch.from_numpy(nc).to(dev))
+    widths = np.array([8] * n8 + [3] * n3 + [2] * n2)
+    full = ((1 << widths) - 1).astype(np.uint8)[:, None]
+    mk = trs.dc_pack_codes(sp, np.broadcast_to(full, (r, out)), np.broadcast_to(full, (r, inn)),
+                           np.zeros((r, out // 128, 2), np.uint16), np.zeros((r, inn // 128, 2), np.uint16),
+                           np.zeros(r, np.float32))
+    return ts, torch.from_numpy(mk).to(dev)
+
+
+def random_pool(nbytes, dev, torch):
+    pool = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    chunk = 1 << 29
+    for o in range(0, pool.numel(), chunk):
+        n = min(chunk, pool.numel() - o)
+        pool[o:o + n] = torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev)
+    return pool
+
+
 def build_c2(layers, dev, torch, trs, synth):
     """Resident deltas for every (layer, matrix, tenant) plus backbone and x."""
-    import numpy as np
     n_ten, T = synth.C2_TENANTS, synth.C2_TOKENS
     mats = synth.LLAMA2_7B
     specs = [(o, i) + synth.groups_for(o, i, 16) for _, o, i in mats]
@@ -68,26 +96,9 @@ def build_c2(layers, dev, torch, trs, synth):
     # mask of valid code bits; codes of every tenant are drawn on the GPU.
     tmpl, mask = {}, {}
     for sp in sorted(set(specs)):
-        out, inn, n8, n3, n2 = sp
-        r = n8 + n3 + n2
-        ts = []
-        for k in range(2):
-            d = synth.random_delta_codes(np.random.default_rng(1000 + 7 * k + out), out, inn, n8, n3, n2)
-            nc = trs.dc_pack_codes(sp, np.zeros_like(d.codes_u), np.zeros_like(d.codes_v), d.sz_u, d.sz_v, d.sigma)
-            ts.append(torch.from_numpy(nc).to(dev))
-        tmpl[sp] = ts
-        widths = np.array([8] * n8 + [3] * n3 + [2] * n2)
-        full = ((1 << widths) - 1).astype(np.uint8)[:, None]
-        mk = trs.dc_pack_codes(sp, np.broadcast_to(full, (r, out)), np.broadcast_to(full, (r, inn)),
-                               np.zeros((r, out // 128, 2), np.uint16), np.zeros((r, inn // 128, 2), np.uint16),
-                               np.zeros(r, np.float32))
-        mask[sp] = torch.from_numpy(mk).to(dev)
+        tmpl[sp], mask[sp] = spec_templates(sp, dev, torch, trs, synth)
     per_layer = sum(trs.dc_packed_bytes(sp) for sp in specs) * n_ten
-    pool = torch.empty(per_layer * layers, dtype=torch.uint8, device=dev)
-    chunk = 1 << 29
-    for o in range(0, pool.numel(), chunk):
-        n = min(chunk, pool.numel() - o)
-        pool[o:o + n] = torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev)
+    pool = random_pool(per_layer * layers, dev, torch)
     views = []
     off = 0
     for l in range(layers):
@@ -265,6 +276,125 @@ def pack_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def config_bench(args):
+    """The other synthetic workloads, timed one layer at a time (eager calls
+    on one stream; one JSON line per token count):
+      c1  Llama-2-7B layer, one tenant, decode of 1, 8 and 64 tokens
+          (dc_apply_decode), 20 layer copies cycled (569 MB of deltas);
+      c3  Llama-2-13B layer, prefill of 8 tenants x 2048 tokens in contiguous
+          segments (dc_apply_prefill);
+      c4  Mistral-7B layer (grouped-query k, v 1024x4096) at the 1/32 budget,
+          16 tenants, 128 tokens (dc_apply_multitenant), 3 copies cycled.
+    Fused (backbone + delta) and delta-only; flops are 2 T r (out + in) per
+    matrix for the delta and 2 T out in for the backbone."""
+    import numpy as np
+    import torch
+
+    import synth
+    import tenant_rank_serving_amd as trs
+
+    trs.lib()
+    dev = torch.device("cuda:0")
+    w = args.workload
+    if w == "c1":
+        name, mats, budget, n_ten, copies, counts = "Llama-2-7B", synth.LLAMA2_7B, 16, 1, 20, (1, 8, 64)
+    elif w == "c3":
+        name, mats, budget, n_ten, copies = "Llama-2-13B", synth.LLAMA2_13B, 16, synth.C3_TENANTS, 1
+        counts = (synth.C3_TENANTS * synth.C3_TOKENS_PER,)
+    else:
+        name, mats, budget, n_ten, copies = "Mistral-7B", synth.MISTRAL_7B, 32, synth.C4_TENANTS, 3
+        counts = (synth.C4_TOKENS,)
+    specs = [(o, i) + synth.groups_for(o, i, budget) for _, o, i in mats]
+    tmpl = {sp: spec_templates(sp, dev, torch, trs, synth) for sp in sorted(set(specs))}
+    nbytes = [trs.dc_packed_bytes(sp) for sp in specs]
+    pool = random_pool(sum(nbytes) * n_ten * copies, dev, torch)
+    views, W, off = [], [], 0
+    for c in range(copies):
+        row = []
+        for m, sp in enumerate(specs):
+            vs = []
+            for k in range(n_ten):
+                buf = pool[off:off + nbytes[m]]
+                buf.bitwise_and_(tmpl[sp][1]).bitwise_or_(tmpl[sp][0][(k + c + m) % 2])
+                vs.append(trs.DeltaView(sp, buf))
+                off += nbytes[m]
+            row.append(vs)
+        views.append(row)
+        W.append([(torch.randn(o, i, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16) for _, o, i in mats])
+    tmax = max(counts)
+    X = [torch.randn(tmax, i, device=dev).to(torch.bfloat16).view(torch.int16) for _, o, i in mats]
+    ys = {o: torch.empty((tmax, o), dtype=torch.int16, device=dev) for _, o, _ in mats}
+    op = {"c1": trs.DC_OP_DECODE, "c3": trs.DC_OP_PREFILL, "c4": trs.DC_OP_MULTITENANT}[w]
+    ws = torch.empty(max(trs.dc_workspace_bytes(op, [sp] * n_ten, tmax) for sp in specs), dtype=torch.uint8,
+                     device=dev)
+    ids_h = synth.c4_ids() if w == "c4" else None
+    ids = torch.from_numpy(ids_h).to(dev) if w == "c4" else None
+    seg = np.arange(n_ten + 1, dtype=np.int32) * synth.C3_TOKENS_PER
+    torch.cuda.synchronize()
+    log("%s: %s layer, %d tenants, %d copies, %.2f GB of deltas resident" % (w, name, n_ten, copies, pool.numel() / 1e9))
+
+    def call(c, m, T, fused):
+        wb = W[c][m] if fused else None
+        x, y = X[m][:T], ys[mats[m][1]][:T]
+        if w == "c1":
+            trs.dc_apply_decode(views[c][m][0], wb, x, y, ws)
+        elif w == "c3":
+            trs.dc_apply_prefill(views[c][m], wb, x, seg, y, ws)
+        else:
+            trs.dc_apply_multitenant(views[c][m], wb, x, ids, y, ws)
+
+    def ms_per_layer(T, fused):
+        for _ in range(args.warmup):
+            for c in range(copies):
+                for m in range(len(mats)):
+                    call(c, m, T, fused)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            for c in range(copies):
+                for m in range(len(mats)):
+                    call(c, m, T, fused)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (args.steps * copies)
+
+    touched = n_ten if ids_h is None else len(set(ids_h.tolist()))
+    delta_bytes = touched * sum(trs.dc_algorithmic_bytes(sp) for sp in specs)
+    base_bytes = sum(o * i * 2 for _, o, i in mats)
+    for T in counts:
+        rank_work = sum((sp[2] + sp[3] + sp[4]) * (sp[0] + sp[1]) for sp in specs)
+        f_delta = 2.0 * T * rank_work
+        f_base = 2.0 * T * base_bytes / 2
+        xy = T * sum(2 * (o + i) for _, o, i in mats)
+        t_f = ms_per_layer(T, True)
+        t_d = ms_per_layer(T, False)
+        log("%s T=%d: fused %.4f ms/layer, delta-only %.4f ms/layer" % (w, T, t_f, t_d))
+        res = {
+            "metric": "%s layer tokens/s (delta-apply, fused with the backbone)" % name, "value": round(T / t_f * 1e3, 1),
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(t_f, 4), "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": {"c1": "single-tenant decode", "c3": "multi-tenant prefill, contiguous segments",
+                                    "c4": "multi-tenant decode"}[w] + ", %s layer (7 matrices), 1/%d budget" % (name, budget),
+                       "tenants": n_ten, "tenants_touched": touched, "tokens": T, "layer_copies_cycled": copies},
+            "launch": "eager, one stream, one call per matrix",
+            "fused": {"ms_per_layer": round(t_f, 4), "tokens_per_s": round(T / t_f * 1e3, 1),
+                      "total_GBps": round((delta_bytes + base_bytes + xy) / (t_f * 1e-3) / 1e9, 1),
+                      "matrix_TFLOPs": round((f_delta + f_base) / (t_f * 1e-3) / 1e12, 2)},
+            "delta_only": {"ms_per_layer": round(t_d, 4), "tokens_per_s": round(T / t_d * 1e3, 1),
+                           "packed_delta_GBps": round(delta_bytes / (t_d * 1e-3) / 1e9, 1),
+                           "pct_of_hbm_peak": round(100 * delta_bytes / (t_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                           "matrix_TFLOPs": round(f_delta / (t_d * 1e-3) / 1e12, 2)},
+            "bytes_per_layer": {"packed_delta": int(delta_bytes), "backbone": int(base_bytes), "x_y": int(xy)},
+            "flops_per_layer": {"delta": f_delta, "backbone": f_base},
+        }
+        if w == "c3":
+            res["mfma_utilization_vs_2.5PF_dense_bf16"] = {
+                "fused": round((f_delta + f_base) / (t_f * 1e-3) / 2.5e15, 4),
+                "delta_only": round(f_delta / (t_d * 1e-3) / 2.5e15, 4)}
+        print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,19 +404,25 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pack", action="store_true",
                     help="time quantize+pack on the GPU (one layer's deltas) instead of the apply step")
+    ap.add_argument("--workload", choices=("c2", "c1", "c3", "c4"), default="c2",
+                    help="c2 (default): the multi-tenant decode step; c1, c3, c4: the other synthetic "
+                         "workloads, timed per layer")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path shards by tenant with no collective, and "
+              "this build runs on a single MI355X (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
         return
     if args.pack:
         pack_bench(args)
         return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the path shards by tenant with no collective, and "
-              "this build runs on a single MI355X (--gpus 1).", file=sys.stderr)
-        sys.exit(2)
+    if args.workload != "c2":
+        config_bench(args)
+        return
 
     import numpy as np
     import torch

@@ -224,10 +224,12 @@ struct ApplyArgs {
   void* const* events;         // optional DC_STAGE_COUNT + 1 hipEvent_t, may be null
 };
 int launch_apply(const ApplyArgs& a);
-// K ranges of the split backbone product (0: not split; > 1: ybase must be
-// zeroed before it runs, its ranges add into it).
+// K ranges of the split backbone product (0: the tiled product, T > 256;
+// 1: one range; > 1: ybase must be zeroed before it runs, its ranges add
+// into it).
 int base_splits(int out, int in, int T);
-int launch_base(const uint16_t* W, const uint16_t* xt, float* ybase, int out, int in, int T, void* stream);
+int launch_base(const uint16_t* W, const uint16_t* x, const uint16_t* xt, float* ybase, int out, int in, int T,
+                void* stream);
 int launch_dequant(const Tenant& t, int32_t out, int32_t in, uint16_t* u16, uint16_t* v16, void* stream);
 int launch_pack(int32_t out, int32_t in, int32_t n8, int32_t n3, int32_t n2, const float* U, const float* sigma,
                 const float* V, uint8_t* dst, uint32_t* flag, void* stream);

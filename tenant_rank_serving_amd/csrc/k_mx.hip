@@ -1016,7 +1016,8 @@ int launch_apply(const ApplyArgs& a) {
   uint8_t* xf = a.ws + a.wl.xf;
   uint32_t* xsc = reinterpret_cast<uint32_t*>(a.ws + a.wl.xsc);
   float* xsum = reinterpret_cast<float*>(a.ws + a.wl.xsum);
-  uint16_t* xt = a.W ? reinterpret_cast<uint16_t*>(a.ws + a.wl.xt) : nullptr;
+  // the B tiles of x feed the split-K backbone product only
+  uint16_t* xt = a.W && base_splits(a.out, a.in, a.T) > 0 ? reinterpret_cast<uint16_t*>(a.ws + a.wl.xt) : nullptr;
   SegArg seg{};
   if (a.mode == 2)
     for (int k = 0; k <= a.n; ++k) seg.v[k] = a.seg[k];
@@ -1029,7 +1030,7 @@ int launch_apply(const ApplyArgs& a) {
   hipLaunchKernelGGL(k_prep, dim3((unsigned)(1 + (items + 3) / 4)), dim3(256), 0, st, *a.tenants, a.x, a.ids, a.T,
                      a.in, a.n, a.mode, seg, offs, perm, act, flags, xf, xsc, xsum, xt, tv, a.T * a.wl.rs, ybase, nyb);
   mark(DC_STAGE_BASE);
-  if (a.W) launch_base(a.W, xt, ybase, a.out, a.in, a.T, a.stream);
+  if (a.W) launch_base(a.W, a.x, xt, ybase, a.out, a.in, a.T, a.stream);
   mark(DC_STAGE_VSIDE);
   if (a.wl.vb > 0)
     hipLaunchKernelGGL(k_vside, dim3((unsigned)(a.wl.vb * v_slices(a.in)), (unsigned)a.n), dim3(256), 0, st,

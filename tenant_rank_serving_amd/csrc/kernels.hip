@@ -69,90 +69,112 @@ __device__ __forceinline__ uint32_t unit_code(const uint32_t* w, int k) {
 }
 
 // ----------------------------------------------------------- backbone GEMM
-// ybase[t][o] = sum_j W[o][j] x[t][j] in fp32 with v_mfma_f32_16x16x32_bf16.
-// Work item (block): 16 whole rows of W (one contiguous stretch of memory)
-// and NT tiles of 16 tokens (blockIdx.y selects the group of 64 tokens).
-// Each wave takes a quarter of the input columns for all 16 rows and all
-// tokens, so every element of W is read once per 64 tokens.  W loads run
-// kWDepth K-steps ahead of the matrix cores, x loads (1 KB B tiles written by
-// the prep kernel) kXDepth steps ahead.  The step loop has no branches, so
-// each step waits only for its own loads.  The four waves add their sums
-// through LDS.
-constexpr int kWDepth = 8;
-constexpr int kXDepth = 4;
+// ybase[t][o] = sum_j W[o][j] x[t][j] in fp32 with v_mfma_f32_16x16x32_bf16
+// (A operand: lane l holds row l%16 of W, k = 8(l/16) .. +8 of a 32-step; B
+// operand: token l%16, the same k; result: token l%16, rows 4(l/16) .. +4).
+//
+// Tiled form for many tokens (T > 256): 128 rows of W x 128 tokens per block,
+// K in chunks of 64 staged through LDS in two buffers, rows padded by 16
+// bytes so that the 16-byte operand reads of 8 consecutive lanes hit distinct
+// banks.  Wave (wo, wt) computes the 64 x 64 quarter, 4 x 4 ops per 32-step.
+// The next chunk's global loads are in flight while the current one is
+// multiplied; one barrier per chunk (two or four chunks ahead in registers
+// measured slower).  x is read in its row-major layout;
+// tokens past T read the last token, and their columns are not stored.
+// Consecutive workgroup ids go round-robin over the 8 XCDs, so tiles are
+// numbered per XCD: each XCD takes a contiguous range of tiles, ordered as
+// groups of 8 row tiles x all token tiles, so that the blocks it runs at one
+// time share W rows and x rows in its L2.
+constexpr int kGT = 128;                // rows of W and tokens per tile
+constexpr int kGK = 64;                 // K per stage
+constexpr int kGPad = kGK * 2 + 16;     // LDS row stride, bytes
+constexpr int kGGroup = 8;              // row tiles per group
 
-template <int NT>
-__global__ void __launch_bounds__(256) k_base(const uint16_t* __restrict__ W, const uint16_t* __restrict__ xt,
-                                              float* __restrict__ ybase, int32_t out, int32_t in, int32_t T,
-                                              int32_t tg0) {
-  __shared__ float red[4][16][65];   // [wave][row][token], padded
+__global__ void __launch_bounds__(256, 2) k_base_tiled(const uint16_t* __restrict__ W, const uint16_t* __restrict__ x,
+                                                       float* __restrict__ ybase, int32_t out, int32_t in, int32_t T) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kGT * kGPad];   // [stage][W, x][row][144 B]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r0 = blockIdx.x * 16;
-  const int t0 = (tg0 + blockIdx.y) * 64;
-  const int tiles = (T + 15) / 16;              // token tiles of x in total
-  const int kspan = in / 4;                     // a multiple of 32: in is a multiple of 128
-  const int kw = wave * kspan;
-  const int nst = kspan / 32;                   // K-steps of this wave
-  const int nsp = (nst + kWDepth - 1) / kWDepth * kWDepth;   // padded with zero steps
-  const uint16_t* wa = W + (size_t)(r0 + (lane & 15)) * in + kw + (lane >> 4) * 8;
-  // B tile (k-step kt, token tile tt) is 1 KB: lane l holds token 16tt + l%16, k = 32kt + 8(l/16) .. +8
-  const uint16_t* xb = xt + ((size_t)(kw / 32) * tiles + t0 / 16) * 512 + lane * 8;
-  uint32_t keep[NT];   // all ones for a lane whose token exists
+  const int nto = out / kGT, ntt = (T + kGT - 1) / kGT, total = nto * ntt;
+  const int xcd = blockIdx.x & 7, j8 = blockIdx.x >> 3;
+  const int tile = xcd * (total >> 3) + min(xcd, total & 7) + j8;
+  const int g = tile / (kGGroup * ntt), rem = tile - g * (kGGroup * ntt);
+  const int gs = min(kGGroup, nto - g * kGGroup);
+  const int o0 = (g * kGGroup + rem % gs) * kGT, t0 = (rem / gs) * kGT;
+  // staging: piece it of a thread is row 32 it + tid/8, bytes 16 (tid%8) .. +16 of the chunk
+  const uint16_t* wp[4];
+  const uint16_t* xp[4];
+  int so[4];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) keep[j] = t0 + 16 * j + (lane & 15) < T ? ~0u : 0u;
-  f32x4 acc[NT];
+  for (int it = 0; it < 4; ++it) {
+    const int row = it * 32 + (tid >> 3), c = tid & 7;
+    wp[it] = W + (size_t)(o0 + row) * in + c * 8;
+    xp[it] = x + (size_t)min(t0 + row, T - 1) * in + c * 8;
+    so[it] = row * kGPad + c * 16;
+  }
+  // one chunk in flight, in register slot 0 (written this way, with the slot
+  // index and a nested loop, the compiler keeps the loaded values in
+  // registers; a flat loop over chunks made it stage them through scratch
+  // memory, 4x slower)
+  uint4 rw[1][4], rx[1][4];
+  const int nk = in / kGK;
+  auto gload = [&](int slot, int kc) __attribute__((always_inline)) {
 #pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint4 a[kWDepth], b[kXDepth][NT];
-  auto load_a = [&](int slot, int st) {
-    a[slot] = *reinterpret_cast<const uint4*>(wa + (size_t)min(st, nst - 1) * 32);
-  };
-  auto load_b = [&](int slot, int st) {
-    const uint16_t* p = xb + (size_t)min(st, nst - 1) * tiles * 512;
-#pragma unroll
-    for (int j = 0; j < NT; ++j) b[slot][j] = *reinterpret_cast<const uint4*>(p + j * 512);
-  };
-  auto step = [&](int sa, int sb, int st) {
-    const uint32_t live = st < nst ? ~0u : 0u;   // zero for the padding steps
-    uint4 av = a[sa];
-    av.x &= live; av.y &= live; av.z &= live; av.w &= live;
-    const bf16x8 ab = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      uint4 bv = b[sb][j];
-      bv.x &= keep[j]; bv.y &= keep[j]; bv.z &= keep[j]; bv.w &= keep[j];
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, __builtin_bit_cast(bf16x8, bv), acc[j], 0, 0, 0);
+    for (int it = 0; it < 4; ++it) {
+      rw[slot][it] = *reinterpret_cast<const uint4*>(wp[it] + (size_t)kc * kGK);
+      rx[slot][it] = *reinterpret_cast<const uint4*>(xp[it] + (size_t)kc * kGK);
     }
   };
+  auto swrite = [&](int s, int slot) __attribute__((always_inline)) {
 #pragma unroll
-  for (int d = 0; d < kWDepth; ++d) load_a(d, d);
-#pragma unroll
-  for (int d = 0; d < kXDepth; ++d) load_b(d, d);
-  int s0 = 0;
-  for (; s0 < nsp - kWDepth; s0 += kWDepth) {
-#pragma unroll
-    for (int d = 0; d < kWDepth; ++d) {
-      step(d, d % kXDepth, s0 + d);
-      load_a(d, s0 + d + kWDepth);
-      load_b(d % kXDepth, s0 + d + kXDepth);
+    for (int it = 0; it < 4; ++it) {
+      *reinterpret_cast<uint4*>(&lds[s][0][so[it]]) = rw[slot][it];
+      *reinterpret_cast<uint4*>(&lds[s][1][so[it]]) = rx[slot][it];
     }
-  }
+  };
+  const int wo = wave >> 1, wt = wave & 1;
+  const int ra = (64 * wo + (lane & 15)) * kGPad + (lane >> 4) * 16;
+  const int rb = (64 * wt + (lane & 15)) * kGPad + (lane >> 4) * 16;
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int d = 0; d < kWDepth; ++d) {   // last kWDepth steps: no W loads left
-    step(d, d % kXDepth, s0 + d);
-    if (d + kXDepth < kWDepth) load_b(d % kXDepth, s0 + d + kXDepth);
-  }
-  // D layout: lane holds token column lane%16 of tile j and rows 4(lane/16)+i
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int j = 0; j < NT; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][16 * j + (lane & 15)] = acc[j][i];
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gload(0, 0);
+  swrite(0, 0);
   __syncthreads();
-  const int ntok = min(64, T - t0);
-  for (int c = tid; c < 16 * 64; c += 256) {
-    const int row = c & 15, tl = c >> 4;   // consecutive threads: consecutive rows of one token
-    if (tl < ntok)
-      ybase[(size_t)(t0 + tl) * out + r0 + row] = (red[0][row][tl] + red[1][row][tl]) + (red[2][row][tl] + red[3][row][tl]);
+  for (int k0 = 0; k0 < nk; ++k0) {
+#pragma unroll
+    for (int d = 0; d < 1; ++d) {
+      const int kc = k0 + d, s = kc & 1;
+      // unconditional (the last chunk loads itself again), so that the loop
+      // has no branch and the stores to LDS below wait for these loads only
+      gload(0, min(kc + 1, nk - 1));
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4 a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const uint4*>(&lds[s][0][ra + 16 * i * kGPad + ks * 64]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const uint4*>(&lds[s][1][rb + 16 * j * kGPad + ks * 64]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                               __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
+      }
+      swrite(s ^ 1, 0);   // after the last chunk: unused
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tok = t0 + 64 * wt + 16 * j + (lane & 15);
+    if (tok < T) {
+      float* dst = ybase + (size_t)tok * out + o0 + 64 * wo + 4 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(dst + 16 * i) = acc[i][j];
+    }
   }
 }
 
@@ -293,24 +315,16 @@ int base_splits(int out, int in, int T) {
   return T <= 256 ? (in / 32 + kSKSteps - 1) / kSKSteps : 0;
 }
 
-int launch_base(const uint16_t* W, const uint16_t* xt, float* ybase, int out, int in, int T, void* stream) {
+int launch_base(const uint16_t* W, const uint16_t* x, const uint16_t* xt, float* ybase, int out, int in, int T,
+                void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int nks = base_splits(out, in, T);
   if (nks > 0) {
     const dim3 g((unsigned)(out / 64), (unsigned)nks, (unsigned)((T + 63) / 64));
     hipLaunchKernelGGL(k_base_sk, g, dim3(256), 0, st, W, xt, ybase, out, in, T, nks);
-    return (int)hipGetLastError();
-  }
-  // full groups of 64 tokens, then the tail group with its own tile count
-  const int full = T / 64, tail = (T % 64 + 15) / 16;
-  const dim3 gf((unsigned)(out / 16), (unsigned)full), gt((unsigned)(out / 16), 1u);
-  if (full > 0) hipLaunchKernelGGL(k_base<4>, gf, dim3(256), 0, st, W, xt, ybase, out, in, T, 0);
-  switch (tail) {
-    case 1: hipLaunchKernelGGL(k_base<1>, gt, dim3(256), 0, st, W, xt, ybase, out, in, T, full); break;
-    case 2: hipLaunchKernelGGL(k_base<2>, gt, dim3(256), 0, st, W, xt, ybase, out, in, T, full); break;
-    case 3: hipLaunchKernelGGL(k_base<3>, gt, dim3(256), 0, st, W, xt, ybase, out, in, T, full); break;
-    case 4: hipLaunchKernelGGL(k_base<4>, gt, dim3(256), 0, st, W, xt, ybase, out, in, T, full); break;
-    default: break;
+  } else {
+    const unsigned tiles = (unsigned)(out / kGT) * (unsigned)((T + kGT - 1) / kGT);
+    hipLaunchKernelGGL(k_base_tiled, dim3(tiles), dim3(256), 0, st, W, x, ybase, out, in, T);
   }
   return (int)hipGetLastError();
 }

@@ -198,6 +198,35 @@ def test_deterministic_and_base_only():
     assert diff.max() <= 1
 
 
+
+@pytest.mark.parametrize("out,inn,T", [(384, 256, 257), (1152, 384, 700), (256, 640, 300), (1280, 128, 1030)])
+def test_backbone_tiled_many_tokens(out, inn, T):
+    """More than 256 tokens: the backbone product in tiles of 128 rows x 128
+    tokens (a ragged last token tile; 2 to 10 row tiles, so whole and partial
+    groups of 8).  With sigma = 0 the output is the backbone alone: every
+    value within its bf16 rounding (2^-8 relative) of the fp64 product, plus
+    an fp32 summation allowance of 2^-17 sum_j |W_oj x_tj| (for values near
+    zero, where one bf16 unit is finer than the fp32 rounding of the sum);
+    with the delta, against the oracle; two calls give the same bits (no
+    atomics)."""
+    note("backbone tiled", out, inn, T)
+    c = synth.small_case(40 + T, out, inn, 2, 8, 22, T)
+    d = c["delta"]
+    y, a = run_decode(d, c["w"], c["x"])
+    check_close(y, oap.apply_factored(c["w"], c["x"], *oracle_tenant(d)), what="tiled %dx%d T=%d" % (out, inn, T))
+    _, b = run_decode(d, c["w"], c["x"])
+    assert np.array_equal(a, b)
+    z = d.subset(0, d.r, (d.n8, d.n3, d.n2))
+    z.sigma[:] = 0
+    _, bits = run_decode(z, c["w"], c["x"])
+    ref = oap.apply_factored(c["w"], c["x"], *oracle_tenant(z))
+    wf = synth.bf16_bits_to_f32(c["w"]).astype(np.float64)
+    xf = synth.bf16_bits_to_f32(c["x"]).astype(np.float64)
+    allow = 2.0 ** -8 * np.abs(ref) + 2.0 ** -17 * (np.abs(xf) @ np.abs(wf).T)
+    got = synth.bf16_bits_to_f32(bits.view(np.uint16)).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= allow), float(np.max(np.abs(got - ref) / allow))
+
+
 # ------------------------------------------------------------ multi-tenant
 def _mt_run(views, w, x, ids):
     t = torch()
