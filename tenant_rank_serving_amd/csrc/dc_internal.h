@@ -173,14 +173,19 @@ struct WsLayout {
   size_t xt;      // bf16 x in matrix-core B tiles: [in/32][ceil(T/16)][64 lanes][8]
   size_t ybase;   // fp32 [T][out] backbone product, original order
   size_t vpart;   // fp32 [T][rs] t = sigma * (V x), sorted order (accumulated over input slices)
+  size_t dav;     // prefill, dense form: bf16 [drp][2 in] V operand (hi, lo)
+  size_t dau;     // bf16 [out][3 drp] U operand (hi, hi, lo)
+  size_t dtb;     // bf16 [T][3 drp] t of one segment (hi, lo, hi)
   size_t total;
+  int32_t drp;    // rank rows of the dense operands (0: no dense region)
   int32_t rs;     // row stride of vpart (max t_width over tenants)
   int32_t vb;     // max V-side rank blocks per tenant
 };
 
 // rs: max t_width over tenants; vbmax: max v_blocks over tenants.
+// drp: rank rows of the dense prefill operands (0 for decode calls).
 inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rs, int32_t n, bool with_base, int32_t vbmax,
-                      WsLayout* W) {
+                      int32_t drp, WsLayout* W) {
   if (T < 0 || n < 0) return false;
   W->vb = vbmax;
   size_t o = 0;
@@ -197,6 +202,10 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rs, int32_t n,
   W->xt = take(with_base ? 2 * (size_t)in * round_up((size_t)T, 16) : 0);
   W->ybase = take(with_base ? 4 * (size_t)T * out : 0);
   W->vpart = take(4 * (size_t)T * W->rs);
+  W->drp = drp;
+  W->dav = take(2 * (size_t)drp * 2 * in);
+  W->dau = take(2 * (size_t)out * 3 * drp);
+  W->dtb = take(2 * (size_t)T * 3 * drp);
   W->total = round_up(o, kAlign);
   return true;
 }
@@ -230,6 +239,12 @@ int launch_apply(const ApplyArgs& a);
 int base_splits(int out, int in, int T);
 int launch_base(const uint16_t* W, const uint16_t* x, const uint16_t* xt, float* ybase, int out, int in, int T,
                 void* stream);
+// Rank rows of the dense prefill operands of a tenant with r pairs (r rounded
+// up to whole 128-row tiles, at least one tile).
+int dense_rank_pad(int r);
+// Prefill with long segments: backbone product, then per segment the
+// tenant's operands and two dense products (see kernels.hip).
+int launch_dense_prefill(const ApplyArgs& a);
 int launch_dequant(const Tenant& t, int32_t out, int32_t in, uint16_t* u16, uint16_t* v16, void* stream);
 int launch_pack(int32_t out, int32_t in, int32_t n8, int32_t n3, int32_t n2, const float* U, const float* sigma,
                 const float* V, uint8_t* dst, uint32_t* flag, void* stream);

@@ -1004,7 +1004,18 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(int32_t n, int32_t out, 
 
 }  // namespace
 
+// Segments of at least this many tokens take the dense prefill form.
+constexpr int kDenseMin = 256;
+
 int launch_apply(const ApplyArgs& a) {
+  if (a.mode == 2 && a.wl.drp > 0) {
+    bool dense = true;
+    for (int k = 0; k < a.n; ++k) {
+      const int nt = a.seg[k + 1] - a.seg[k];
+      if (nt > 0 && nt < kDenseMin) dense = false;
+    }
+    if (dense) return launch_dense_prefill(a);
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + a.wl.flags);
   int32_t* offs = reinterpret_cast<int32_t*>(a.ws + a.wl.offs);

@@ -39,7 +39,7 @@ struct SegInfo {
   const uint32_t* us;  // U scale/zero
 };
 
-__device__ __forceinline__ SegInfo seg_info(const Tenant& tn, const Layout& L, int which) {
+__host__ __device__ inline SegInfo seg_info(const Tenant& tn, const Layout& L, int which) {
   SegInfo s;
   const int rv[3] = {DC_REG_VC8, DC_REG_VC3, DC_REG_VC2};
   s.b = which == 0 ? 8 : (which == 1 ? 3 : 2);
@@ -90,11 +90,33 @@ constexpr int kGK = 64;                 // K per stage
 constexpr int kGPad = kGK * 2 + 16;     // LDS row stride, bytes
 constexpr int kGGroup = 8;              // row tiles per group
 
-__global__ void __launch_bounds__(256, 2) k_base_tiled(const uint16_t* __restrict__ W, const uint16_t* __restrict__ x,
-                                                       float* __restrict__ ybase, int32_t out, int32_t in, int32_t T) {
+// One product C[n][m] = sum_k A[m][k] B[n][k mod kb] with its epilogue:
+//   EPI 0: c32[n][m] = C (fp32, row stride ldc);
+//   EPI 1: t = sigma_m C (0 for m >= r), split t = hi + lo in bf16, written
+//          as tb[n][m] = hi, tb[n][M + m] = lo, tb[n][2M + m] = hi (ldc = 3M);
+//   EPI 2: y[n][m] = bf16(C + ybase[n][m]) (ybase may be null).
+// A is [M][K] row-major (M a multiple of 128, K of 64), B [N][ldb].
+struct GemmOp {
+  const uint16_t* A;
+  const uint16_t* B;
+  int32_t M, N, K, ldb, kb, ldc;
+  float* c32;
+  const float* sigma;
+  int32_t r;
+  uint16_t* tb;
+  const float* ybase;
+  uint16_t* y;
+};
+
+template <int EPI>
+__global__ void __launch_bounds__(256, 2) k_gemm(GemmOp op) {
+  const uint16_t* __restrict__ W = op.A;
+  const uint16_t* __restrict__ x = op.B;
+  const int out = op.M, T = op.N, in = op.K;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kGT * kGPad];   // [stage][W, x][row][144 B]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nto = out / kGT, ntt = (T + kGT - 1) / kGT, total = nto * ntt;
+  if (blockIdx.x >= (unsigned)total) return;
   const int xcd = blockIdx.x & 7, j8 = blockIdx.x >> 3;
   const int tile = xcd * (total >> 3) + min(xcd, total & 7) + j8;
   const int g = tile / (kGGroup * ntt), rem = tile - g * (kGGroup * ntt);
@@ -108,7 +130,7 @@ __global__ void __launch_bounds__(256, 2) k_base_tiled(const uint16_t* __restric
   for (int it = 0; it < 4; ++it) {
     const int row = it * 32 + (tid >> 3), c = tid & 7;
     wp[it] = W + (size_t)(o0 + row) * in + c * 8;
-    xp[it] = x + (size_t)min(t0 + row, T - 1) * in + c * 8;
+    xp[it] = x + (size_t)min(t0 + row, T - 1) * op.ldb + c * 8;
     so[it] = row * kGPad + c * 16;
   }
   // one chunk in flight, in register slot 0 (written this way, with the slot
@@ -121,7 +143,7 @@ __global__ void __launch_bounds__(256, 2) k_base_tiled(const uint16_t* __restric
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       rw[slot][it] = *reinterpret_cast<const uint4*>(wp[it] + (size_t)kc * kGK);
-      rx[slot][it] = *reinterpret_cast<const uint4*>(xp[it] + (size_t)kc * kGK);
+      rx[slot][it] = *reinterpret_cast<const uint4*>(xp[it] + (size_t)((kc * kGK) % op.kb));
     }
   };
   auto swrite = [&](int s, int slot) __attribute__((always_inline)) {
@@ -170,13 +192,43 @@ __global__ void __launch_bounds__(256, 2) k_base_tiled(const uint16_t* __restric
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tok = t0 + 64 * wt + 16 * j + (lane & 15);
-    if (tok < T) {
-      float* dst = ybase + (size_t)tok * out + o0 + 64 * wo + 4 * (lane >> 4);
+    if (tok >= T) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(dst + 16 * i) = acc[i][j];
+    for (int i = 0; i < 4; ++i) {
+      const int m = o0 + 64 * wo + 16 * i + 4 * (lane >> 4);   // rows m .. m+3 of this lane
+      const f32x4 c = acc[i][j];
+      if constexpr (EPI == 0) {
+        *reinterpret_cast<f32x4*>(op.c32 + (size_t)tok * op.ldc + m) = c;
+      } else if constexpr (EPI == 1) {
+        uint32_t hi[2], lo[2];
+#pragma unroll
+        for (int q = 0; q < 4; q += 2) {
+          uint16_t h[2], l[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float t = c[q + e] * (m + q + e < op.r ? op.sigma[m + q + e] : 0.f);
+            h[e] = f32_to_bf16(t);
+            l[e] = f32_to_bf16(t - bf16_to_f32(h[e]));
+          }
+          hi[q / 2] = h[0] | ((uint32_t)h[1] << 16);
+          lo[q / 2] = l[0] | ((uint32_t)l[1] << 16);
+        }
+        uint16_t* row = op.tb + (size_t)tok * op.ldc + m;
+        *reinterpret_cast<uint2*>(row) = make_uint2(hi[0], hi[1]);
+        *reinterpret_cast<uint2*>(row + out) = make_uint2(lo[0], lo[1]);
+        *reinterpret_cast<uint2*>(row + 2 * out) = make_uint2(hi[0], hi[1]);
+      } else {
+        f32x4 v = c;
+        if (op.ybase) v += *reinterpret_cast<const f32x4*>(op.ybase + (size_t)tok * op.ldc + m);
+        const uint32_t p0 = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t p1 = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<uint2*>(op.y + (size_t)tok * op.ldc + m) = make_uint2(p0, p1);
+      }
     }
   }
 }
+
+unsigned gemm_tiles(int M, int N) { return (unsigned)(M / kGT) * (unsigned)((N + kGT - 1) / kGT); }
 
 // Split-K form for a few token groups (T <= 256): 64 rows of W per block
 // (wave w: rows 16w..16w+15) and one range of at most kSKSteps K-steps
@@ -268,21 +320,9 @@ __global__ void __launch_bounds__(256) k_base_sk(const uint16_t* __restrict__ W,
 }
 
 // -------------------------------------------------------------- dequantize
-// fp16 bits of s*(q-z) for every element of U [r][out] and V [r][in].
-__global__ void __launch_bounds__(256) k_dequant(Tenant tn, int32_t out, int32_t in, uint16_t* __restrict__ u16,
-                                                 uint16_t* __restrict__ v16) {
-  const int r = tn.n8 + tn.n3 + tn.n2;
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t nv = (size_t)r * in, nu = (size_t)r * out;
-  if (idx >= nv + nu) return;
-  Layout L;
-  layout_of(out, in, tn.n8, tn.n3, tn.n2, &L);
-  const bool is_v = idx < nv;
-  const int len = is_v ? in : out;
-  const size_t e = is_v ? idx : idx - nv;
-  const int i = (int)(e / len), pos = (int)(e % len);
-  const int which = i < tn.n8 ? 0 : (i < tn.n8 + tn.n3 ? 1 : 2);
-  const SegInfo sg = seg_info(tn, L, which);
+// Exact fp32 value s*(q - z) of element pos of singular vector i (V_i when
+// is_v, pos < in; else U_i, pos < out), from the tenant's packed codes.
+__device__ __forceinline__ float dq_seg(const SegInfo& sg, bool is_v, int i, int pos, int in) {
   const int li = i - sg.lo;
   const int np = (int)round_up(sg.n, 4);
   uint32_t code, sz;
@@ -304,9 +344,71 @@ __global__ void __launch_bounds__(256) k_dequant(Tenant tn, int32_t out, int32_t
     }
     sz = sg.us[(size_t)(pos / kGroup) * np + li];
   }
-  const float v = f16_to_f32(sz & 0xFFFFu) * ((float)code - f16_to_f32(sz >> 16));  // exact in fp32
-  const uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)v);
+  return f16_to_f32(sz & 0xFFFFu) * ((float)code - f16_to_f32(sz >> 16));   // exact in fp32
+}
+
+__device__ __forceinline__ float dq_value(const Tenant& tn, const Layout& L, bool is_v, int i, int pos, int in) {
+  const int which = i < tn.n8 ? 0 : (i < tn.n8 + tn.n3 ? 1 : 2);
+  return dq_seg(seg_info(tn, L, which), is_v, i, pos, in);
+}
+
+// fp16 bits of s*(q-z) for every element of U [r][out] and V [r][in].
+__global__ void __launch_bounds__(256) k_dequant(Tenant tn, int32_t out, int32_t in, uint16_t* __restrict__ u16,
+                                                 uint16_t* __restrict__ v16) {
+  const int r = tn.n8 + tn.n3 + tn.n2;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t nv = (size_t)r * in, nu = (size_t)r * out;
+  if (idx >= nv + nu) return;
+  Layout L;
+  layout_of(out, in, tn.n8, tn.n3, tn.n2, &L);
+  const bool is_v = idx < nv;
+  const int len = is_v ? in : out;
+  const size_t e = is_v ? idx : idx - nv;
+  const int i = (int)(e / len), pos = (int)(e % len);
+  const uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)dq_value(tn, L, is_v, i, pos, in));
   (is_v ? v16 : u16)[(size_t)i * len + pos] = h;
+}
+
+// Operands of the dense prefill products of one tenant, from its packed codes:
+// av [rp][2 in] (row i: the hi parts of V_i, then its lo parts) and
+// au [out][3 rp] (row o: the hi parts of U_:o, the hi parts again, the lo
+// parts), bf16.  hi = bf16(v) and lo = v - hi for the fp16 value v, exactly
+// (fp16 keeps 11 significant bits, bf16 8, so the remainder has at most 3).
+// Rows of av and columns of au past r are zero.  One block row per rank (V)
+// or output (U), threads along the packed order; the three rank groups'
+// records come from the host.
+struct DenseSegs {
+  SegInfo s[3];   // 8-, 3- and 2-bit groups
+};
+
+__device__ __forceinline__ SegInfo dense_seg(const DenseSegs& d, int i) {
+  return i < d.s[1].lo ? d.s[0] : (i < d.s[2].lo ? d.s[1] : d.s[2]);
+}
+
+__device__ __forceinline__ uint32_t hi_lo(float v) {   // bf16 hi in the low half, lo in the high half
+  const uint16_t hi = f32_to_bf16(v);
+  return hi | ((uint32_t)f32_to_bf16(v - bf16_to_f32(hi)) << 16);
+}
+
+__global__ void __launch_bounds__(256) k_dense_v(DenseSegs d, int32_t r, int32_t in, uint16_t* __restrict__ av) {
+  const int i = blockIdx.y, pos = blockIdx.x * 256 + threadIdx.x;
+  if (pos >= in) return;
+  const float v = i < r ? (float)(_Float16)dq_seg(dense_seg(d, i), true, i, pos, in) : 0.f;
+  const uint32_t hl = hi_lo(v);
+  uint16_t* row = av + (size_t)i * 2 * in;
+  row[pos] = (uint16_t)hl;
+  row[in + pos] = (uint16_t)(hl >> 16);
+}
+
+__global__ void __launch_bounds__(128) k_dense_u(DenseSegs d, int32_t r, int32_t rp, int32_t in,
+                                                 uint16_t* __restrict__ au) {
+  const int o = blockIdx.y, i = blockIdx.x * 128 + threadIdx.x;   // rp is a multiple of 128
+  const float v = i < r ? (float)(_Float16)dq_seg(dense_seg(d, i), false, i, o, in) : 0.f;
+  const uint32_t hl = hi_lo(v);
+  uint16_t* row = au + (size_t)o * 3 * rp;
+  row[i] = (uint16_t)hl;
+  row[rp + i] = (uint16_t)hl;
+  row[2 * rp + i] = (uint16_t)(hl >> 16);
 }
 
 }  // namespace
@@ -323,8 +425,78 @@ int launch_base(const uint16_t* W, const uint16_t* x, const uint16_t* xt, float*
     const dim3 g((unsigned)(out / 64), (unsigned)nks, (unsigned)((T + 63) / 64));
     hipLaunchKernelGGL(k_base_sk, g, dim3(256), 0, st, W, xt, ybase, out, in, T, nks);
   } else {
-    const unsigned tiles = (unsigned)(out / kGT) * (unsigned)((T + kGT - 1) / kGT);
-    hipLaunchKernelGGL(k_base_tiled, dim3(tiles), dim3(256), 0, st, W, x, ybase, out, in, T);
+    GemmOp op{};
+    op.A = W;
+    op.B = x;
+    op.M = out;
+    op.N = T;
+    op.K = in;
+    op.ldb = in;
+    op.kb = in;
+    op.ldc = out;
+    op.c32 = ybase;
+    hipLaunchKernelGGL(k_gemm<0>, dim3(gemm_tiles(out, T)), dim3(256), 0, st, op);
+  }
+  return (int)hipGetLastError();
+}
+
+int dense_rank_pad(int r) { return r > 0 ? (int)round_up((size_t)r, kGT) : kGT; }
+
+int launch_dense_prefill(const ApplyArgs& a) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  float* ybase = a.W ? reinterpret_cast<float*>(a.ws + a.wl.ybase) : nullptr;
+  uint16_t* av = reinterpret_cast<uint16_t*>(a.ws + a.wl.dav);
+  uint16_t* au = reinterpret_cast<uint16_t*>(a.ws + a.wl.dau);
+  uint16_t* tb = reinterpret_cast<uint16_t*>(a.ws + a.wl.dtb);
+  if (a.W) {
+    GemmOp op{};
+    op.A = a.W;
+    op.B = a.x;
+    op.M = a.out;
+    op.N = a.T;
+    op.K = a.in;
+    op.ldb = a.in;
+    op.kb = a.in;
+    op.ldc = a.out;
+    op.c32 = ybase;
+    hipLaunchKernelGGL(k_gemm<0>, dim3(gemm_tiles(a.out, a.T)), dim3(256), 0, st, op);
+  }
+  for (int k = 0; k < a.n; ++k) {
+    const int s0 = a.seg[k], nt = a.seg[k + 1] - a.seg[k];
+    if (nt == 0) continue;
+    const Tenant& tn = a.tenants->t[k];
+    const int r = tn.n8 + tn.n3 + tn.n2, rp = dense_rank_pad(r);
+    Layout L;
+    layout_of(a.out, a.in, tn.n8, tn.n3, tn.n2, &L);
+    DenseSegs ds;
+    for (int w = 0; w < 3; ++w) ds.s[w] = seg_info(tn, L, w);
+    hipLaunchKernelGGL(k_dense_v, dim3((unsigned)((a.in + 255) / 256), (unsigned)rp), dim3(256), 0, st, ds, r, a.in, av);
+    hipLaunchKernelGGL(k_dense_u, dim3((unsigned)(rp / 128), (unsigned)a.out), dim3(128), 0, st, ds, r, rp, a.in, au);
+    GemmOp v{};   // t = sigma (V x) for the segment's tokens
+    v.A = av;
+    v.B = a.x + (size_t)s0 * a.in;
+    v.M = rp;
+    v.N = nt;
+    v.K = 2 * a.in;
+    v.ldb = a.in;
+    v.kb = a.in;
+    v.ldc = 3 * rp;
+    v.sigma = r > 0 ? reinterpret_cast<const float*>(tn.base + L.off[DC_REG_SIGMA]) : nullptr;
+    v.r = r;
+    v.tb = tb;
+    hipLaunchKernelGGL(k_gemm<1>, dim3(gemm_tiles(rp, nt)), dim3(256), 0, st, v);
+    GemmOp u{};   // y = W x + U t, rounded once
+    u.A = au;
+    u.B = tb;
+    u.M = a.out;
+    u.N = nt;
+    u.K = 3 * rp;
+    u.ldb = 3 * rp;
+    u.kb = 3 * rp;
+    u.ldc = a.out;
+    u.ybase = ybase ? ybase + (size_t)s0 * a.out : nullptr;
+    u.y = a.y + (size_t)s0 * a.out;
+    hipLaunchKernelGGL(k_gemm<2>, dim3(gemm_tiles(a.out, nt)), dim3(256), 0, st, u);
   }
   return (int)hipGetLastError();
 }

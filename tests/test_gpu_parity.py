@@ -427,6 +427,45 @@ def test_prefill_small_segments():
     check_close(y_to_f64(y), ref, what="prefill")
 
 
+
+def test_prefill_dense_segments():
+    """Segments of at least 256 tokens take the dense form (each tenant's
+    pairs dequantized once into bf16 hi + lo operands, then matrix-core
+    products over the segment): mixed ranks, an empty delta (r = 0: W x
+    only), an empty segment, ragged token tiles; fused and delta-only
+    against the oracle, and two calls give the same bits."""
+    note("prefill dense")
+    t = torch()
+    rng = np.random.default_rng(44)
+    shapes = [(2, 9, 40), (0, 0, 0), (1, 12, 3), (3, 0, 0), (2, 33, 60)]
+    specs = [(256, 384) + sh for sh in shapes]
+    ds = [synth.small_delta(600 + k, *sp) for k, sp in enumerate(specs)]
+    views = [upload(sp, d) for sp, d in zip(specs, ds)]
+    seg = np.concatenate([[0], np.cumsum([256, 300, 0, 384, 257])]).astype(np.int32)
+    T = int(seg[-1])
+    w = synth.base_weight(rng, 256, 384)
+    x = synth.activations(rng, T, 384)
+    ts = [oracle_tenant(d) for d in ds]
+    ws = workspace(trs.DC_OP_PREFILL, specs, T)
+    bits = []
+    for wb in (w, None, w):
+        y = t.empty((T, 256), dtype=t.int16, device="cuda")
+        trs.dc_apply_prefill(views, dev_u16(wb) if wb is not None else None, dev_u16(x), seg, y, ws)
+        t.cuda.synchronize()
+        yf = y_to_f64(y)
+        bits.append(y.cpu().numpy())
+        for k in range(len(specs)):
+            lo, hi = int(seg[k]), int(seg[k + 1])
+            if hi == lo:
+                continue
+            ref = oap.apply_factored(wb, x[lo:hi], *ts[k])
+            if wb is None and sum(specs[k][2:]) == 0:
+                assert np.all(yf[lo:hi] == 0.0)
+            else:
+                check_close(yf[lo:hi], ref, what="dense prefill tenant %d %s" % (k, "fused" if wb is not None else "delta"))
+    assert np.array_equal(bits[0], bits[2])
+
+
 @pytest.mark.parametrize("mi", [0, 6])
 def test_c3_prefill_full_size(mi):
     """13B-shaped prefill (q 5120x5120, down 5120x13824): 8 tenants x 2048
