@@ -264,7 +264,7 @@ size_t dc_workspace_bytes(int32_t op, const dc_spec* specs, int32_t n, int32_t T
  * Summation order: parts of V x (in wider than 2048) and, for T <= 256, of
  * W_base x (in wider than 512) are added with float atomics, so two calls may
  * round an output differently in its last bit; batches of more than 256
- * tokens compute W_base x in another order.
+ * tokens compute W_base x in tiles of 128 x 128, in a fixed order.
  */
 dc_status dc_apply_decode(const dc_delta_view* d, const uint16_t* W_base, const uint16_t* x,
                           uint16_t* y, int32_t T, void* ws, size_t ws_bytes, void* stream);
@@ -312,7 +312,16 @@ dc_status dc_apply_multitenant_timed(const dc_delta_view* views, int32_t n, cons
  *   seg_offsets  host int32 [n+1], non-decreasing, seg_offsets[0] = 0;
  *                T = seg_offsets[n]
  *   x, y         device bf16 [T][in], [T][out]
- * Same conventions as dc_apply_multitenant.
+ * Same conventions as dc_apply_multitenant.  When every non-empty segment
+ * has at least 256 tokens, the call takes a dense form: per tenant, the
+ * dequantized fp16 pairs are written once into the workspace as bf16
+ * hi + lo operands (an exact split), then t = sigma (V x) and y = W x + U t
+ * run as matrix-core products over the segment (fp32 sums; t carried as
+ * bf16 hi + lo, about 16 significant bits).  Its sums are in a fixed order
+ * (no atomics): repeated calls give the same bits.  Shorter segments take
+ * the decode kernels.  The workspace for DC_OP_PREFILL (dc_workspace_bytes)
+ * includes the dense operands: bf16 [rp][2 in] + [out][3 rp] + [T][3 rp],
+ * rp = the largest tenant rank rounded up to 128.
  */
 dc_status dc_apply_prefill(const dc_delta_view* views, int32_t n, const uint16_t* W_base,
                            const uint16_t* x, const int32_t* seg_offsets, uint16_t* y,
