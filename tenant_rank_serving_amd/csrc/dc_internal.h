@@ -173,11 +173,12 @@ struct WsLayout {
   size_t xt;      // bf16 x in matrix-core B tiles: [in/32][ceil(T/16)][64 lanes][8]
   size_t ybase;   // fp32 [T][out] backbone product, original order
   size_t vpart;   // fp32 [T][rs] t = sigma * (V x), sorted order (accumulated over input slices)
-  size_t dav;     // prefill, dense form: bf16 [drp][2 in] V operand (hi, lo)
-  size_t dau;     // bf16 [out][3 drp] U operand (hi, hi, lo)
+  size_t dav;     // prefill, dense form: dnb slots of bf16 [drp][2 in] V operand (hi, lo)
+  size_t dau;     // dnb slots of bf16 [out][3 drp] U operand (hi, hi, lo)
   size_t dtb;     // bf16 [T][3 drp] t of one segment (hi, lo, hi)
   size_t total;
   int32_t drp;    // rank rows of the dense operands (0: no dense region)
+  int32_t dnb;    // operand slots: tenants whose dense products share one launch
   int32_t rs;     // row stride of vpart (max t_width over tenants)
   int32_t vb;     // max V-side rank blocks per tenant
 };
@@ -203,8 +204,9 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rs, int32_t n,
   W->ybase = take(with_base ? 4 * (size_t)T * out : 0);
   W->vpart = take(4 * (size_t)T * W->rs);
   W->drp = drp;
-  W->dav = take(2 * (size_t)drp * 2 * in);
-  W->dau = take(2 * (size_t)out * 3 * drp);
+  W->dnb = drp > 0 ? (n < 8 ? n : 8) : 0;
+  W->dav = take(2 * (size_t)W->dnb * drp * 2 * in);
+  W->dau = take(2 * (size_t)W->dnb * out * 3 * drp);
   W->dtb = take(2 * (size_t)T * 3 * drp);
   W->total = round_up(o, kAlign);
   return true;

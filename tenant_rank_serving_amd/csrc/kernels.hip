@@ -96,6 +96,8 @@ constexpr int kGGroup = 8;              // row tiles per group
 //          as tb[n][m] = hi, tb[n][M + m] = lo, tb[n][2M + m] = hi (ldc = 3M);
 //   EPI 2: y[n][m] = bf16(C + ybase[n][m]) (ybase may be null).
 // A is [M][K] row-major (M a multiple of 128, K of 64), B [N][ldb].
+constexpr int kGBatch = 8;
+
 struct GemmOp {
   const uint16_t* A;
   const uint16_t* B;
@@ -108,8 +110,15 @@ struct GemmOp {
   uint16_t* y;
 };
 
+// Up to kGBatch independent products per launch (blockIdx.y selects one;
+// blocks past a product's tile count return at once).
+struct GemmBatch {
+  GemmOp op[kGBatch];
+};
+
 template <int EPI>
-__global__ void __launch_bounds__(256, 2) k_gemm(GemmOp op) {
+__global__ void __launch_bounds__(256, 2) k_gemm(GemmBatch gb) {
+  const GemmOp& op = gb.op[blockIdx.y];
   const uint16_t* __restrict__ W = op.A;
   const uint16_t* __restrict__ x = op.B;
   const int out = op.M, T = op.N, in = op.K;
@@ -435,7 +444,9 @@ int launch_base(const uint16_t* W, const uint16_t* x, const uint16_t* xt, float*
     op.kb = in;
     op.ldc = out;
     op.c32 = ybase;
-    hipLaunchKernelGGL(k_gemm<0>, dim3(gemm_tiles(out, T)), dim3(256), 0, st, op);
+    GemmBatch gb{};
+    gb.op[0] = op;
+    hipLaunchKernelGGL(k_gemm<0>, dim3(gemm_tiles(out, T)), dim3(256), 0, st, gb);
   }
   return (int)hipGetLastError();
 }
@@ -445,11 +456,13 @@ int dense_rank_pad(int r) { return r > 0 ? (int)round_up((size_t)r, kGT) : kGT; 
 int launch_dense_prefill(const ApplyArgs& a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   float* ybase = a.W ? reinterpret_cast<float*>(a.ws + a.wl.ybase) : nullptr;
-  uint16_t* av = reinterpret_cast<uint16_t*>(a.ws + a.wl.dav);
-  uint16_t* au = reinterpret_cast<uint16_t*>(a.ws + a.wl.dau);
-  uint16_t* tb = reinterpret_cast<uint16_t*>(a.ws + a.wl.dtb);
+  uint16_t* av0 = reinterpret_cast<uint16_t*>(a.ws + a.wl.dav);
+  uint16_t* au0 = reinterpret_cast<uint16_t*>(a.ws + a.wl.dau);
+  uint16_t* tb0 = reinterpret_cast<uint16_t*>(a.ws + a.wl.dtb);
+  const size_t av_slot = (size_t)a.wl.drp * 2 * a.in, au_slot = (size_t)a.out * 3 * a.wl.drp;
   if (a.W) {
-    GemmOp op{};
+    GemmBatch gb{};
+    GemmOp& op = gb.op[0];
     op.A = a.W;
     op.B = a.x;
     op.M = a.out;
@@ -459,44 +472,61 @@ int launch_dense_prefill(const ApplyArgs& a) {
     op.kb = a.in;
     op.ldc = a.out;
     op.c32 = ybase;
-    hipLaunchKernelGGL(k_gemm<0>, dim3(gemm_tiles(a.out, a.T)), dim3(256), 0, st, op);
+    hipLaunchKernelGGL(k_gemm<0>, dim3(gemm_tiles(a.out, a.T)), dim3(256), 0, st, gb);
   }
-  for (int k = 0; k < a.n; ++k) {
-    const int s0 = a.seg[k], nt = a.seg[k + 1] - a.seg[k];
-    if (nt == 0) continue;
-    const Tenant& tn = a.tenants->t[k];
-    const int r = tn.n8 + tn.n3 + tn.n2, rp = dense_rank_pad(r);
-    Layout L;
-    layout_of(a.out, a.in, tn.n8, tn.n3, tn.n2, &L);
-    DenseSegs ds;
-    for (int w = 0; w < 3; ++w) ds.s[w] = seg_info(tn, L, w);
-    hipLaunchKernelGGL(k_dense_v, dim3((unsigned)((a.in + 255) / 256), (unsigned)rp), dim3(256), 0, st, ds, r, a.in, av);
-    hipLaunchKernelGGL(k_dense_u, dim3((unsigned)(rp / 128), (unsigned)a.out), dim3(128), 0, st, ds, r, rp, a.in, au);
-    GemmOp v{};   // t = sigma (V x) for the segment's tokens
-    v.A = av;
-    v.B = a.x + (size_t)s0 * a.in;
-    v.M = rp;
-    v.N = nt;
-    v.K = 2 * a.in;
-    v.ldb = a.in;
-    v.kb = a.in;
-    v.ldc = 3 * rp;
-    v.sigma = r > 0 ? reinterpret_cast<const float*>(tn.base + L.off[DC_REG_SIGMA]) : nullptr;
-    v.r = r;
-    v.tb = tb;
-    hipLaunchKernelGGL(k_gemm<1>, dim3(gemm_tiles(rp, nt)), dim3(256), 0, st, v);
-    GemmOp u{};   // y = W x + U t, rounded once
-    u.A = au;
-    u.B = tb;
-    u.M = a.out;
-    u.N = nt;
-    u.K = 3 * rp;
-    u.ldb = 3 * rp;
-    u.kb = 3 * rp;
-    u.ldc = a.out;
-    u.ybase = ybase ? ybase + (size_t)s0 * a.out : nullptr;
-    u.y = a.y + (size_t)s0 * a.out;
-    hipLaunchKernelGGL(k_gemm<2>, dim3(gemm_tiles(a.out, nt)), dim3(256), 0, st, u);
+  // tenants with tokens, in batches of up to a.wl.dnb (<= kGBatch) operand slots
+  int k = 0;
+  while (k < a.n) {
+    GemmBatch gv{}, gu{};
+    int cnt = 0;
+    unsigned tv = 0, tu = 0;
+    for (; k < a.n && cnt < a.wl.dnb; ++k) {
+      const int s0 = a.seg[k], nt = a.seg[k + 1] - a.seg[k];
+      if (nt == 0) continue;
+      const Tenant& tn = a.tenants->t[k];
+      const int r = tn.n8 + tn.n3 + tn.n2, rp = dense_rank_pad(r);
+      uint16_t* av = av0 + cnt * av_slot;
+      uint16_t* au = au0 + cnt * au_slot;
+      uint16_t* tb = tb0 + (size_t)s0 * 3 * a.wl.drp;   // segments are disjoint token ranges
+      Layout L;
+      layout_of(a.out, a.in, tn.n8, tn.n3, tn.n2, &L);
+      DenseSegs ds;
+      for (int w = 0; w < 3; ++w) ds.s[w] = seg_info(tn, L, w);
+      hipLaunchKernelGGL(k_dense_v, dim3((unsigned)((a.in + 255) / 256), (unsigned)rp), dim3(256), 0, st, ds, r, a.in,
+                         av);
+      hipLaunchKernelGGL(k_dense_u, dim3((unsigned)(rp / 128), (unsigned)a.out), dim3(128), 0, st, ds, r, rp, a.in,
+                         au);
+      GemmOp& v = gv.op[cnt];   // t = sigma (V x) for the segment's tokens
+      v.A = av;
+      v.B = a.x + (size_t)s0 * a.in;
+      v.M = rp;
+      v.N = nt;
+      v.K = 2 * a.in;
+      v.ldb = a.in;
+      v.kb = a.in;
+      v.ldc = 3 * rp;
+      v.sigma = r > 0 ? reinterpret_cast<const float*>(tn.base + L.off[DC_REG_SIGMA]) : nullptr;
+      v.r = r;
+      v.tb = tb;
+      GemmOp& u = gu.op[cnt];   // y = W x + U t, rounded once
+      u.A = au;
+      u.B = tb;
+      u.M = a.out;
+      u.N = nt;
+      u.K = 3 * rp;
+      u.ldb = 3 * rp;
+      u.kb = 3 * rp;
+      u.ldc = a.out;
+      u.ybase = ybase ? ybase + (size_t)s0 * a.out : nullptr;
+      u.y = a.y + (size_t)s0 * a.out;
+      tv = max(tv, gemm_tiles(rp, nt));
+      tu = max(tu, gemm_tiles(a.out, nt));
+      ++cnt;
+    }
+    if (cnt == 0) break;
+    // grid x a multiple of 8, so that blockIdx.x mod 8 is the XCD the tile numbering assumes
+    hipLaunchKernelGGL(k_gemm<1>, dim3((tv + 7) / 8 * 8, (unsigned)cnt), dim3(256), 0, st, gv);
+    hipLaunchKernelGGL(k_gemm<2>, dim3((tu + 7) / 8 * 8, (unsigned)cnt), dim3(256), 0, st, gu);
   }
   return (int)hipGetLastError();
 }
