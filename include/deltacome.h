@@ -320,8 +320,9 @@ dc_status dc_apply_multitenant_timed(const dc_delta_view* views, int32_t n, cons
  * bf16 hi + lo, about 16 significant bits).  Its sums are in a fixed order
  * (no atomics): repeated calls give the same bits.  Shorter segments take
  * the decode kernels.  The workspace for DC_OP_PREFILL (dc_workspace_bytes)
- * includes the dense operands: bf16 [rp][2 in] + [out][3 rp] + [T][3 rp],
- * rp = the largest tenant rank rounded up to 128.
+ * includes the dense operands: min(n, 8) x (bf16 [rp][2 in] + [out][3 rp])
+ * + bf16 [T][3 rp], rp = the largest tenant rank rounded up to 128; the
+ * products of up to 8 tenants run in one launch.
  */
 dc_status dc_apply_prefill(const dc_delta_view* views, int32_t n, const uint16_t* W_base,
                            const uint16_t* x, const int32_t* seg_offsets, uint16_t* y,
