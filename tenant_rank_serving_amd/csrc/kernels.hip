@@ -399,25 +399,35 @@ __device__ __forceinline__ uint32_t hi_lo(float v) {   // bf16 hi in the low hal
   return hi | ((uint32_t)f32_to_bf16(v - bf16_to_f32(hi)) << 16);
 }
 
+constexpr int kDenseURows = 8;   // output rows per block of k_dense_u
+
 __global__ void __launch_bounds__(256) k_dense_v(DenseSegs d, int32_t r, int32_t in, uint16_t* __restrict__ av) {
-  const int i = blockIdx.y, pos = blockIdx.x * 256 + threadIdx.x;
+  const int i = blockIdx.y, pos = 2 * (blockIdx.x * 256 + threadIdx.x);   // two adjacent elements
   if (pos >= in) return;
-  const float v = i < r ? (float)(_Float16)dq_seg(dense_seg(d, i), true, i, pos, in) : 0.f;
-  const uint32_t hl = hi_lo(v);
+  uint32_t h0 = 0, h1 = 0;
+  if (i < r) {
+    const SegInfo sg = dense_seg(d, i);
+    h0 = hi_lo((float)(_Float16)dq_seg(sg, true, i, pos, in));
+    h1 = hi_lo((float)(_Float16)dq_seg(sg, true, i, pos + 1, in));
+  }
   uint16_t* row = av + (size_t)i * 2 * in;
-  row[pos] = (uint16_t)hl;
-  row[in + pos] = (uint16_t)(hl >> 16);
+  *reinterpret_cast<uint32_t*>(row + pos) = (h0 & 0xFFFFu) | (h1 << 16);
+  *reinterpret_cast<uint32_t*>(row + in + pos) = (h0 >> 16) | (h1 & 0xFFFF0000u);
 }
 
 __global__ void __launch_bounds__(128) k_dense_u(DenseSegs d, int32_t r, int32_t rp, int32_t in,
                                                  uint16_t* __restrict__ au) {
-  const int o = blockIdx.y, i = blockIdx.x * 128 + threadIdx.x;   // rp is a multiple of 128
-  const float v = i < r ? (float)(_Float16)dq_seg(dense_seg(d, i), false, i, o, in) : 0.f;
-  const uint32_t hl = hi_lo(v);
-  uint16_t* row = au + (size_t)o * 3 * rp;
-  row[i] = (uint16_t)hl;
-  row[rp + i] = (uint16_t)hl;
-  row[2 * rp + i] = (uint16_t)(hl >> 16);
+  const int i = blockIdx.x * 128 + threadIdx.x;   // rp is a multiple of 128
+  const bool live = i < r;
+  const SegInfo sg = dense_seg(d, live ? i : 0);
+  for (int j = 0; j < kDenseURows; ++j) {
+    const int o = blockIdx.y * kDenseURows + j;      // out is a multiple of 128
+    const uint32_t hl = live ? hi_lo((float)(_Float16)dq_seg(sg, false, i, o, in)) : 0u;
+    uint16_t* row = au + (size_t)o * 3 * rp;
+    row[i] = (uint16_t)hl;
+    row[rp + i] = (uint16_t)hl;
+    row[2 * rp + i] = (uint16_t)(hl >> 16);
+  }
 }
 
 }  // namespace
@@ -492,10 +502,10 @@ int launch_dense_prefill(const ApplyArgs& a) {
       layout_of(a.out, a.in, tn.n8, tn.n3, tn.n2, &L);
       DenseSegs ds;
       for (int w = 0; w < 3; ++w) ds.s[w] = seg_info(tn, L, w);
-      hipLaunchKernelGGL(k_dense_v, dim3((unsigned)((a.in + 255) / 256), (unsigned)rp), dim3(256), 0, st, ds, r, a.in,
+      hipLaunchKernelGGL(k_dense_v, dim3((unsigned)((a.in + 511) / 512), (unsigned)rp), dim3(256), 0, st, ds, r, a.in,
                          av);
-      hipLaunchKernelGGL(k_dense_u, dim3((unsigned)(rp / 128), (unsigned)a.out), dim3(128), 0, st, ds, r, rp, a.in,
-                         au);
+      hipLaunchKernelGGL(k_dense_u, dim3((unsigned)(rp / 128), (unsigned)(a.out / kDenseURows)), dim3(128), 0, st, ds,
+                         r, rp, a.in, au);
       GemmOp& v = gv.op[cnt];   // t = sigma (V x) for the segment's tokens
       v.A = av;
       v.B = a.x + (size_t)s0 * a.in;
