@@ -170,6 +170,38 @@ def test_workspace_bytes_rules():
         trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, sp * 3, 4)
 
 
+
+def test_prefill_workspace_holds_dense_operands():
+    """A prefill workspace adds the dense operands to the multi-tenant one:
+    min(n, 8) slots of bf16 V [rp][2 in] and U [out][3 rp], and bf16 t
+    [T][3 rp], rp = the largest rank rounded up to 128 (at least 128), each
+    region 256-byte aligned; none at T = 0."""
+    def dense(out, inn, rmax, n, T):
+        rp = max(128, -(-rmax // 128) * 128)
+        nb = min(n, 8)
+        al = lambda b: -(-b // 256) * 256
+        return al(2 * nb * rp * 2 * inn) + al(2 * nb * out * 3 * rp) + al(2 * T * 3 * rp)
+    for specs, T in (([(256, 384, 2, 9, 40)] * 3, 300), ([(256, 384, 2, 9, 40), (256, 384, 0, 0, 0)] * 6, 1000),
+                     ([(1024, 512, 2, 20, 150), (1024, 512, 1, 1, 1)], 513), ([(256, 256, 0, 0, 0)], 256)):
+        mt = trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, specs, T)
+        pf = trs.dc_workspace_bytes(trs.DC_OP_PREFILL, specs, T)
+        rmax = max(sum(sp[2:]) for sp in specs)
+        assert pf - mt == dense(specs[0][0], specs[0][1], rmax, len(specs), T)
+    sp = [(256, 384, 2, 9, 40)] * 3
+    assert trs.dc_workspace_bytes(trs.DC_OP_PREFILL, sp, 0) == trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, sp, 0)
+
+
+def test_prefill_rejects_a_workspace_without_the_dense_operands(L):
+    spec = (256, 256, 2, 8, 22)
+    arr = (trs._lib.dc_delta_view * 2)(_view(spec), _view(spec))
+    T = 512
+    seg = np.array([0, 256, 512], np.int32)
+    need = trs.dc_workspace_bytes(trs.DC_OP_PREFILL, [spec] * 2, T)
+    pf = L.dc_apply_prefill
+    assert pf(arr, 2, WB, X, seg.ctypes.data, 0x40000000, WS, need - 1, None) == trs.DC_ERR_BUFFER
+    assert trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, [spec] * 2, T) < need
+
+
 # Fake device addresses: the host checks reject these calls before any launch.
 X, Y, WB, WS, IDS = 0x10000, 0x900000, 0x4000000, 0x8000000, 0xA000000
 
