@@ -308,21 +308,32 @@ dc_status dc_apply_multitenant_timed(const dc_delta_view* views, int32_t n, cons
 
 /*
  * dc_apply_prefill -- n tenants, tokens grouped by tenant: tokens
- * seg_offsets[k] .. seg_offsets[k+1]-1 belong to views[k].
+ * seg_offsets[k] .. seg_offsets[k+1]-1 belong to views[k].  The prompt
+ * phase of serving many fine-tuned models over one backbone: [P1]
+ * application scenarios (multi-tenant serving of many fine-tuned models);
+ * [P2] "Key results" (50 models served from one GPU) and "Experimental
+ * setup" (13B backbones).
  *   seg_offsets  host int32 [n+1], non-decreasing, seg_offsets[0] = 0;
  *                T = seg_offsets[n]
  *   x, y         device bf16 [T][in], [T][out]
- * Same conventions as dc_apply_multitenant.  When every non-empty segment
- * has at least 256 tokens, the call takes a dense form: per tenant, the
- * dequantized fp16 pairs are written once into the workspace as bf16
- * hi + lo operands (an exact split), then t = sigma (V x) and y = W x + U t
- * run as matrix-core products over the segment (fp32 sums; t carried as
- * bf16 hi + lo, about 16 significant bits).  Its sums are in a fixed order
- * (no atomics): repeated calls give the same bits.  Shorter segments take
- * the decode kernels.  The workspace for DC_OP_PREFILL (dc_workspace_bytes)
- * includes the dense operands: min(n, 8) x (bf16 [rp][2 in] + [out][3 rp])
- * + bf16 [T][3 rp], rp = the largest tenant rank rounded up to 128; the
- * products of up to 8 tenants run in one launch.
+ * Same conventions as dc_apply_multitenant (the status word at byte 0 of ws
+ * is cleared).  When every non-empty segment has at least 256 tokens and the
+ * workspace holds the dense operands, the call takes a dense form: per
+ * tenant, the dequantized fp16 pairs are written once into the workspace as
+ * bf16 hi + lo operands (an exact split), then t = sigma (V x) and
+ * y = W x + U t run as matrix-core products over the segment (fp32 sums; t
+ * carried as bf16 hi + lo, about 16 significant bits).  Its sums are in a
+ * fixed order (no atomics): repeated calls give the same bits.  Otherwise
+ * the call takes the decode kernels of dc_apply_multitenant.  The workspace
+ * for DC_OP_PREFILL (dc_workspace_bytes) includes the dense operands when
+ * T >= 256: min(n, 8) x (bf16 [rp][2 in] + [out][3 rp]) + bf16 [T][3 rp],
+ * rp = the largest tenant rank rounded up to 128; the products of up to 8
+ * tenants run in one launch.  A workspace of the DC_OP_MULTITENANT size is
+ * also accepted (no dense form).
+ * Weights: the dense form multiplies by the fp16 dequantized values
+ * fp16(s (q - z)); the decode kernels multiply 8-bit pairs by the same fp16
+ * values but 3- and 2-bit pairs by the exact grid values s (q - z), within
+ * half an fp16 unit of them (the zero point is folded out of their sums).
  */
 dc_status dc_apply_prefill(const dc_delta_view* views, int32_t n, const uint16_t* W_base,
                            const uint16_t* x, const int32_t* seg_offsets, uint16_t* y,

@@ -68,8 +68,15 @@ dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const ui
     return DC_ERR_ALIGN;
   if (overlap(x, (size_t)T * in * 2, y, (size_t)T * out * 2)) return DC_ERR_INVALID_ARG;
   dc::WsLayout wl{};
-  dc::ws_layout(T, in, out, dm.tw, n, true, dm.vb, mode == 2 && T > 0 ? dc::dense_rank_pad(rmax) : 0, &wl);
+  dc::ws_layout(T, in, out, dm.tw, n, true, dm.vb, 0, &wl);
   if (ws_bytes < wl.total) return DC_ERR_BUFFER;
+  if (mode == 2 && T >= dc::kDenseMin) {
+    // the dense prefill operands, when the workspace holds them; without them
+    // the call takes the decode kernels
+    dc::WsLayout wd{};
+    dc::ws_layout(T, in, out, dm.tw, n, true, dm.vb, dc::dense_rank_pad(rmax), &wd);
+    if (ws_bytes >= wd.total) wl = wd;
+  }
   // the kernels address t, the backbone partials and each packed buffer with 32-bit byte offsets
   const size_t lim = (size_t)INT32_MAX;
   if ((size_t)T * wl.rs * 4 > lim || (size_t)T * out * 4 > lim) return DC_ERR_UNSUPPORTED;
@@ -107,7 +114,7 @@ size_t dc_workspace_bytes(int32_t op, const dc_spec* specs, int32_t n, int32_t T
   if (check_specs(specs, n, &dm) != DC_OK) return 0;
   dc::WsLayout wl{};
   dc::ws_layout(T, dm.in, dm.out, dm.tw, n, true, dm.vb,
-                 op == DC_OP_PREFILL && T > 0 ? dc::dense_rank_pad(dm.rmax) : 0, &wl);
+                 op == DC_OP_PREFILL && T >= dc::kDenseMin ? dc::dense_rank_pad(dm.rmax) : 0, &wl);
   return wl.total;
 }
 

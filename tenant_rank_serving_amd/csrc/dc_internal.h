@@ -150,6 +150,10 @@ constexpr int kVTiles = 2;    // 16-rank tiles per V-side wave
 constexpr int kVRanks = 4 * 16 * kVTiles;   // ranks per V-side block (4 waves)
 constexpr int kVDepth = 8;    // groups of codes a V-side wave keeps in flight
 
+// Prefill segments of at least this many tokens can take the dense form
+// (every non-empty segment of the call must have this many).
+constexpr int kDenseMin = 256;
+
 DC_HD inline int v_slices(int in) { return (in / kGroup + kVSlice - 1) / kVSlice; }
 // V-side rank blocks of a tenant: [8-bit rows if any] [3-bit blocks] [2-bit blocks] of kVRanks
 DC_HD inline int v_blocks(int n8, int n3, int n2) {

@@ -401,8 +401,11 @@ __device__ __forceinline__ uint32_t hi_lo(float v) {   // bf16 hi in the low hal
 
 constexpr int kDenseURows = 8;   // output rows per block of k_dense_u
 
-__global__ void __launch_bounds__(256) k_dense_v(DenseSegs d, int32_t r, int32_t in, uint16_t* __restrict__ av) {
+__global__ void __launch_bounds__(256) k_dense_v(DenseSegs d, int32_t r, int32_t in, uint16_t* __restrict__ av,
+                                                 uint32_t* __restrict__ flags) {
   const int i = blockIdx.y, pos = 2 * (blockIdx.x * 256 + threadIdx.x);   // two adjacent elements
+  // the call's status word (no invalid id can occur in a prefill call)
+  if (flags && i == 0 && blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
   if (pos >= in) return;
   uint32_t h0 = 0, h1 = 0;
   if (i < r) {
@@ -470,6 +473,7 @@ int launch_dense_prefill(const ApplyArgs& a) {
   uint16_t* au0 = reinterpret_cast<uint16_t*>(a.ws + a.wl.dau);
   uint16_t* tb0 = reinterpret_cast<uint16_t*>(a.ws + a.wl.dtb);
   const size_t av_slot = (size_t)a.wl.drp * 2 * a.in, au_slot = (size_t)a.out * 3 * a.wl.drp;
+  uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + a.wl.flags);
   if (a.W) {
     GemmBatch gb{};
     GemmOp& op = gb.op[0];
@@ -503,7 +507,8 @@ int launch_dense_prefill(const ApplyArgs& a) {
       DenseSegs ds;
       for (int w = 0; w < 3; ++w) ds.s[w] = seg_info(tn, L, w);
       hipLaunchKernelGGL(k_dense_v, dim3((unsigned)((a.in + 511) / 512), (unsigned)rp), dim3(256), 0, st, ds, r, a.in,
-                         av);
+                         av, flags);
+      flags = nullptr;   // cleared by the first launch
       hipLaunchKernelGGL(k_dense_u, dim3((unsigned)(rp / 128), (unsigned)(a.out / kDenseURows)), dim3(128), 0, st, ds,
                          r, rp, a.in, au);
       GemmOp& v = gv.op[cnt];   // t = sigma (V x) for the segment's tokens

@@ -11,8 +11,8 @@ import synth
 import tenant_rank_serving_amd as trs
 from oracle import apply as oap
 from oracle import quant
-from gpu_util import (TOL, check_close, dev_i32, dev_u16, note, oracle_tenant, run_decode, torch,
-                      upload, workspace, y_to_f64)
+from gpu_util import (TOL, check_close, check_factored, check_multitenant, delta_only_mt, dev_i32, dev_u16,
+                      note, oracle_tenant, run_decode, torch, upload, workspace, y_to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +63,63 @@ def test_dequant_c0_from_svd():
     assert np.array_equal(vd.cpu().numpy().view(np.uint16), vh.view(np.uint16))
 
 
+def _subnormal_delta(seed, spec, sides=("u", "v")):
+    """A random delta whose fp16 scales are subnormal on the given sides
+    (bit patterns 1..1023, i.e. below 2^-14), so that many dequantized values
+    s (q - z) are fp16 subnormals too, plus one all-zero group per side (codes
+    0, scale 1.0, zero 0: what the quantizer stores for a group of zeros)."""
+    d = synth.small_delta(seed, *spec)
+    rng = np.random.default_rng(seed + 1)
+    for side in sides:
+        sz = d.sz_u if side == "u" else d.sz_v
+        sz[..., 0] = rng.integers(1, 1024, size=sz.shape[:-1])
+    if d.r:
+        d.codes_v[0, :128] = 0
+        d.sz_v[0, 0] = (0x3C00, 0)
+        d.codes_u[-1, :128] = 0
+        d.sz_u[-1, 0] = (0x3C00, 0)
+    return d
+
+
+@pytest.mark.parametrize("spec", [(256, 384, 2, 8, 22), (384, 256, 3, 37, 71)])
+def test_dequant_subnormal_bit_exact(spec):
+    """fp16-subnormal scales and dequantized values, and an all-zero group:
+    dc_dequant equals the oracle's fp16 values bit for bit (the device keeps
+    fp16 denormals; a flush to zero would show here)."""
+    note("dequant subnormal", spec)
+    t = torch()
+    d = _subnormal_delta(71, spec)
+    uh, vh = oap.dequant_pairs(d.codes_u, d.codes_v, d.sz_u, d.sz_v)
+    assert np.any((uh != 0) & (np.abs(uh) < 2.0 ** -14)) and np.any((vh != 0) & (np.abs(vh) < 2.0 ** -14))
+    view = upload(spec, d)
+    u = t.empty((d.r, d.out), dtype=t.int16, device="cuda")
+    v = t.empty((d.r, d.inn), dtype=t.int16, device="cuda")
+    trs.dc_dequant(view, u, v)
+    t.cuda.synchronize()
+    assert np.array_equal(u.cpu().numpy().view(np.uint16), uh.view(np.uint16))
+    assert np.array_equal(v.cpu().numpy().view(np.uint16), vh.view(np.uint16))
+
+
+@pytest.mark.parametrize("sides", [("u", "v"), ("v",), ("u",)], ids=lambda s: "".join(s))
+def test_decode_subnormal_scales(sides):
+    """Decode with fp16-subnormal scales on U, V or both (and an all-zero
+    group on each side): delta-only and per bit-width segment against the
+    oracle (fused, the backbone would hide a delta of this size)."""
+    note("decode subnormal", sides)
+    spec = (384, 512, 2, 37, 71)
+    d = _subnormal_delta(73, spec, sides)
+    rng = np.random.default_rng(74)
+    x = synth.activations(rng, 5, spec[1])
+    y, _ = run_decode(d, None, x, with_base=False)
+    check_factored(y, None, x, d, "subnormal %s delta" % "".join(sides))
+    lo = 0
+    for b, n, sp in ((8, d.n8, (d.n8, 0, 0)), (3, d.n3, (0, d.n3, 0)), (2, d.n2, (0, 0, d.n2))):
+        sub = d.subset(lo, lo + n, sp)
+        y, _ = run_decode(sub, None, x, with_base=False)
+        check_factored(y, None, x, sub, "subnormal %s segment %d" % ("".join(sides), b))
+        lo += n
+
+
 # ------------------------------------------------------------- decode c0
 def test_c0_end_to_end():
     """SVD on the host, dc_pack, decode on the GPU: fused and delta-only."""
@@ -75,14 +132,16 @@ def test_c0_end_to_end():
     buf = trs.dc_pack(spec, u32[:32], s32[:32], v32[:32])
     view = trs.DeltaView(spec, t.from_numpy(buf.copy()).cuda())
     cu, cv, su, sv, sg = quant.compress(u32, s32, v32, 2, 8, 22)
+    d = synth.DeltaCodes(256, 256, 2, 8, 22, cv, cu, sv, su, sg)
     ws = workspace(trs.DC_OP_DECODE, [spec], 4)
     x = dev_u16(c0["x"])
     for w in (c0["w"], None):
         y = t.empty((4, 256), dtype=t.int16, device="cuda")
         trs.dc_apply_decode(view, dev_u16(w) if w is not None else None, x, y, ws)
         t.cuda.synchronize()
-        ref = oap.apply_codes(w, c0["x"], cu, cv, su, sv, sg)
-        check_close(y_to_f64(y), ref, what="c0 %s" % ("fused" if w is not None else "delta"))
+        assert np.array_equal(oap.apply_codes(w, c0["x"], cu, cv, su, sv, sg),
+                              oap.apply_factored(w, c0["x"], *oracle_tenant(d)))
+        check_factored(y_to_f64(y), w, c0["x"], d, "c0 %s" % ("fused" if w is not None else "delta"))
 
 
 def test_allocated_tenants_end_to_end():
@@ -111,17 +170,15 @@ def test_allocated_tenants_end_to_end():
         buf = trs.dc_pack(spec, u32, s32, v32)
         views.append(trs.DeltaView(spec, t.from_numpy(buf.copy()).cuda()))
         cu, cv, su, sv, sg = quant.compress(u32, s32, v32, n8, n3, n2)
-        tenants.append(oap.dequant_pairs(cu, cv, su, sv) + (sg,))
+        tenants.append(synth.DeltaCodes(out, inn, n8, n3, n2, cv, cu, sv, su, sg))
     assert len(set(counts)) > 1, counts          # the allocations differ between tenants
     w = synth.base_weight(rng, out, inn)
     x = synth.activations(rng, 24, inn)
     ids = rng.integers(-1, 3, size=24).astype(np.int32)
-    ts = [(uh, sg, vh) for uh, vh, sg in tenants]
     for wb in (w, None):
         y, _, flag = _mt_run(views, wb, x, ids)
         assert flag == 0
-        check_close(y, oap.apply_multitenant(wb, x, ids, ts) if wb is not None else
-                    _delta_only_mt(x, ids, ts, out), what="allocated %s" % ("fused" if wb is not None else "delta"))
+        check_multitenant(y, wb, x, ids, tenants, out, "allocated %s" % ("fused" if wb is not None else "delta"))
 
 
 # ----------------------------------------------- decode, segments and tails
@@ -139,18 +196,15 @@ def test_decode_fused_delta_and_segments(case):
     c = synth.small_case(100 + T, out, inn, n8, n3, n2, T)
     d = c["delta"]
     y, _ = run_decode(d, c["w"], c["x"])
-    check_close(y, oap.apply_factored(c["w"], c["x"], *oracle_tenant(d)), what="fused",
-                ref_exact=oap.apply_factored(c["w"], c["x"], *oracle_tenant(d, True)))
+    check_factored(y, c["w"], c["x"], d, "fused")
     y, _ = run_decode(d, c["w"], c["x"], with_base=False)
-    check_close(y, oap.apply_factored(None, c["x"], *oracle_tenant(d)), what="delta",
-                ref_exact=oap.apply_factored(None, c["x"], *oracle_tenant(d, True)))
+    check_factored(y, None, c["x"], d, "delta")
     lo = 0
     for b, n, sp in ((8, n8, (n8, 0, 0)), (3, n3, (0, n3, 0)), (2, n2, (0, 0, n2))):
         if n:
             sub = d.subset(lo, lo + n, sp)
             y, _ = run_decode(sub, c["w"], c["x"], with_base=False)
-            check_close(y, oap.apply_factored(None, c["x"], *oracle_tenant(sub)), what="segment %d" % b,
-                        ref_exact=oap.apply_factored(None, c["x"], *oracle_tenant(sub, True)))
+            check_factored(y, None, c["x"], sub, "segment %d" % b)
         lo += n
 
 
@@ -165,15 +219,15 @@ def test_c1_matrix_full_size(mi):
     for B in (1, 8, 64):
         x = m["x"][:B]
         y, _ = run_decode(d, m["w"], x)
-        check_close(y, oap.apply_factored(m["w"], x, *oracle_tenant(d)), what="c1 fused B=%d" % B)
+        check_factored(y, m["w"], x, d, "c1 fused B=%d" % B)
     x = m["x"][:8]
     y, _ = run_decode(d, m["w"], x, with_base=False)
-    check_close(y, oap.apply_factored(None, x, *oracle_tenant(d)), what="c1 delta")
+    check_factored(y, None, x, d, "c1 delta")
     lo = 0
     for b, n, sp in ((8, d.n8, (d.n8, 0, 0)), (3, d.n3, (0, d.n3, 0)), (2, d.n2, (0, 0, d.n2))):
         sub = d.subset(lo, lo + n, sp)
         y, _ = run_decode(sub, m["w"], x, with_base=False)
-        check_close(y, oap.apply_factored(None, x, *oracle_tenant(sub)), what="c1 segment %d" % b)
+        check_factored(y, None, x, sub, "c1 segment %d" % b)
         lo += n
 
 
@@ -189,7 +243,7 @@ def test_deterministic_and_base_only():
     z.sigma[:] = 0
     y, _ = run_decode(z, c["w"], c["x"])
     ref = oap.apply_factored(c["w"], c["x"], *oracle_tenant(z))
-    check_close(y, ref, what="sigma=0")
+    check_factored(y, c["w"], c["x"], z, "sigma=0")
     yb = synth.to_bf16_bits(ref.astype(np.float32))
     _, bits = run_decode(z, c["w"], c["x"])
     # sigma = 0 gives the backbone only; the rounding of a fp32 sum may differ
@@ -213,7 +267,7 @@ def test_backbone_tiled_many_tokens(out, inn, T):
     c = synth.small_case(40 + T, out, inn, 2, 8, 22, T)
     d = c["delta"]
     y, a = run_decode(d, c["w"], c["x"])
-    check_close(y, oap.apply_factored(c["w"], c["x"], *oracle_tenant(d)), what="tiled %dx%d T=%d" % (out, inn, T))
+    check_factored(y, c["w"], c["x"], d, "tiled %dx%d T=%d" % (out, inn, T))
     _, b = run_decode(d, c["w"], c["x"])
     assert np.array_equal(a, b)
     z = d.subset(0, d.r, (d.n8, d.n3, d.n2))
@@ -250,12 +304,10 @@ def test_multitenant_small_mixed_specs():
     x = synth.activations(rng, 23, 384)
     ids = rng.integers(-1, 4, size=23).astype(np.int32)
     ids[3] = 2
-    ts = [oracle_tenant(d) for d in ds]
     for wb in (w, None):
         y, bits, flag = _mt_run(views, wb, x, ids)
         assert flag == 0
-        check_close(y, oap.apply_multitenant(wb, x, ids, ts) if wb is not None else
-                    _delta_only_mt(x, ids, ts, 256), what="mt")
+        check_multitenant(y, wb, x, ids, ds, 256, "mt %s" % ("fused" if wb is not None else "delta"))
     # each token equals its single-tenant decode bit for bit
     _, bits, _ = _mt_run(views, w, x, ids)
     for k in range(4):
@@ -286,19 +338,15 @@ def test_multitenant_max_tenants_and_empty_delta():
     ids[:6] = [1, 1, 7, 127, -1, 0]        # the empty delta, the last tenant, the backbone bucket
     ids[ids == 5] = 6                       # tenant 5 gets no token
     x = synth.activations(rng, T, 256)
-    ts = [oracle_tenant(d) for d in ds]
-    te = [oracle_tenant(d, True) for d in ds]   # exact grid values: for outputs of a few 8-bit pairs on 128 rows
     for wb in (w, None):
         y, _, flag = _mt_run(views, wb, x, ids)
         assert flag == 0
         if wb is not None:
-            check_close(y, oap.apply_multitenant(wb, x, ids, ts), what="128 tenants, fused",
-                        ref_exact=oap.apply_multitenant(wb, x, ids, te))
+            check_multitenant(y, wb, x, ids, ds, 128, "128 tenants, fused")
         else:   # outputs that are exactly zero (backbone-only or empty-delta tokens) must be zero
             zero = (ids < 0) | np.isin(ids, [k for k in range(n) if sum(specs[k][2:]) == 0])
             assert np.all(y[zero] == 0.0)
-            check_close(y[~zero], _delta_only_mt(x, ids, ts, 128)[~zero], what="128 tenants, delta only",
-                        ref_exact=_delta_only_mt(x, ids, te, 128)[~zero])
+            check_multitenant(y, None, x, ids, ds, 128, "128 tenants, delta only", rows=~zero)
 
 
 def test_multitenant_many_tokens():
@@ -318,12 +366,10 @@ def test_multitenant_many_tokens():
     T = 700
     ids = rng.integers(-1, len(specs), size=T).astype(np.int32)
     x = synth.activations(rng, T, 256)
-    ts = [oracle_tenant(d) for d in ds]
     for wb in (w, None):
         y, bits, flag = _mt_run(views, wb, x, ids)
         assert flag == 0
-        check_close(y, oap.apply_multitenant(wb, x, ids, ts) if wb is not None else
-                    _delta_only_mt(x, ids, ts, 128), what="mt 700")
+        check_multitenant(y, wb, x, ids, ds, 128, "mt 700 %s" % ("fused" if wb is not None else "delta"))
     _, bits, _ = _mt_run(views, None, x, ids)
     for k in range(len(specs)):
         sel = np.nonzero(ids == k)[0]
@@ -334,16 +380,7 @@ def test_multitenant_many_tokens():
     bad[650] = len(specs)                   # out of range, in the third chunk: backbone only, flagged
     y2, _, flag2 = _mt_run(views, w, x, bad)
     assert flag2 == 1
-    check_close(y2, oap.apply_multitenant(w, x, np.where(bad >= len(specs), -1, bad), ts), what="mt 700 bad id")
-
-
-def _delta_only_mt(x, ids, ts, out):
-    y = np.zeros((x.shape[0], out))
-    for k, tk in enumerate(ts):
-        sel = np.nonzero(ids == k)[0]
-        if sel.size:
-            y[sel] = oap.apply_factored(None, x[sel], *tk)
-    return y
+    check_multitenant(y2, w, x, np.where(bad >= len(specs), -1, bad), ds, 128, "mt 700 bad id")
 
 
 def test_multitenant_invalid_ids_flag():
@@ -357,8 +394,7 @@ def test_multitenant_invalid_ids_flag():
     ids = np.array([0, 5, -1, 2, -7, 1, 3], np.int32)
     y, bits, flag = _mt_run(views, w, x, ids)
     assert flag == 1
-    ref = oap.apply_multitenant(w, x, ids, [oracle_tenant(d) for d in ds])
-    check_close(y, ref, what="invalid ids")
+    check_multitenant(y, w, x, ids, ds, 128, "invalid ids")
     ids2 = np.array([0, 1, 2, 0, 1, 2, -1], np.int32)
     _, _, flag2 = _mt_run(views, w, x, ids2)
     assert flag2 == 0                                  # cleared by every call
@@ -383,28 +419,33 @@ def test_c2_sample_full_size():
         views = [v if v is not None else first for v in views]
         w = synth.make_c2_base(layer, mi)
         x = synth.make_c2_x(layer, mi)
-        ts = [oracle_tenant(ds[k]) if k in ds else (np.zeros((1, 1)), np.zeros(0), np.zeros((1, 1)))
-              for k in range(synth.C2_TENANTS)]
-        y, _, flag = _mt_run(views, w, x, ids)
-        assert flag == 0
-        ref = np.zeros_like(y)
-        xb = synth.bf16_bits_to_f32(x).astype(np.float64)
-        ref += xb @ synth.bf16_bits_to_f32(w).astype(np.float64).T
-        for k in touched:
-            sel = np.nonzero(ids == k)[0]
-            ref[sel] += oap.apply_factored(None, x[sel], *ts[k])
-        check_close(y, ref, what="c2 fused")
+        deltas = []
+        for exact in (False, True):
+            dl = np.zeros((x.shape[0], ds[touched[0]].out))
+            for k in touched:
+                sel = np.nonzero(ids == k)[0]
+                dl[sel] = oap.apply_factored(None, x[sel], *oracle_tenant(ds[k], exact))
+            deltas.append(dl)
+        base = synth.bf16_bits_to_f32(x).astype(np.float64) @ synth.bf16_bits_to_f32(w).astype(np.float64).T
+        for wb, b, what in ((w, base, "fused"), (None, 0.0, "delta-only")):
+            y, _, flag = _mt_run(views, wb, x, ids)
+            assert flag == 0
+            check_close(y, b + deltas[0], what="c2 layer %d matrix %d %s" % (layer, mi, what), ref_exact=b + deltas[1])
 
 
-def test_c4_matrix_full_size():
-    """Mistral GQA k projection (1024x4096) at 1/32, 16 tenants, 128 tokens."""
-    note("c4 k matrix")
-    m = synth.make_c4_matrix(1)
+@pytest.mark.parametrize("mi", [1, 4, 6])
+def test_c4_matrix_full_size(mi):
+    """Mistral-7B GQA layer at the 1/32 budget, 16 tenants, 128 tokens routed
+    uniformly: k (1024x4096), gate (14336x4096) and down (4096x14336), fused
+    and delta-only."""
+    note("c4 matrix", mi)
+    m = synth.make_c4_matrix(mi)
     views = [upload(d.spec, d) for d in m["deltas"]]
-    y, _, flag = _mt_run(views, m["w"], m["x"], m["ids"])
-    assert flag == 0
-    ref = oap.apply_multitenant(m["w"], m["x"], m["ids"], [oracle_tenant(d) for d in m["deltas"]])
-    check_close(y, ref, what="c4")
+    for wb in (m["w"], None):
+        y, _, flag = _mt_run(views, wb, m["x"], m["ids"])
+        assert flag == 0
+        check_multitenant(y, wb, m["x"], m["ids"], m["deltas"], m["out"],
+                          "c4 %s %s" % (m["name"], "fused" if wb is not None else "delta-only"))
 
 
 # ----------------------------------------------------------------- prefill
@@ -423,8 +464,8 @@ def test_prefill_small_segments():
     y = t.empty((T, 256), dtype=t.int16, device="cuda")
     trs.dc_apply_prefill(views, dev_u16(w), dev_u16(x), seg, y, ws)
     t.cuda.synchronize()
-    ref = oap.apply_prefill(w, x, seg, [oracle_tenant(d) for d in ds])
-    check_close(y_to_f64(y), ref, what="prefill")
+    check_close(y_to_f64(y), oap.apply_prefill(w, x, seg, [oracle_tenant(d) for d in ds]), what="prefill",
+                ref_exact=oap.apply_prefill(w, x, seg, [oracle_tenant(d, True) for d in ds]))
 
 
 
@@ -466,11 +507,49 @@ def test_prefill_dense_segments():
     assert np.array_equal(bits[0], bits[2])
 
 
-@pytest.mark.parametrize("mi", [0, 6])
+def test_prefill_dense_more_than_eight_tenants():
+    """Eleven tenants of at least 256 tokens each in the dense form: the
+    operand slots are reused by a second batch of launches.  Around the
+    8-slot boundary sit an r = 0 tenant (slot 7), an empty segment (tenant 8)
+    and a tenant right after it.  The workspace is dirtied first (status word
+    set, operands garbage): the call clears the word and overwrites every
+    output.  The same call with a workspace of the multi-tenant size (no
+    dense operands) takes the decode kernels; both against the oracle."""
+    note("prefill dense 11 tenants")
+    t = torch()
+    rng = np.random.default_rng(45)
+    shapes = [(2, 9, 40), (1, 12, 3), (0, 20, 0), (3, 0, 0), (2, 33, 60), (0, 0, 17), (1, 1, 1),
+              (0, 0, 0), (2, 8, 22), (1, 30, 50), (2, 0, 9)]
+    specs = [(256, 256) + sh for sh in shapes]
+    ds = [synth.small_delta(700 + k, *sp) for k, sp in enumerate(specs)]
+    views = [upload(sp, d) for sp, d in zip(specs, ds)]
+    lens = [256, 260, 300, 256, 257, 256, 280, 256, 0, 300, 256]
+    seg = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(seg[-1])
+    w = synth.base_weight(rng, 256, 256)
+    x = synth.activations(rng, T, 256)
+    ts = [oracle_tenant(d) for d in ds]
+    te = [oracle_tenant(d, True) for d in ds]
+    ref = oap.apply_prefill(w, x, seg, ts)
+    ref_x = oap.apply_prefill(w, x, seg, te)
+    for op in (trs.DC_OP_PREFILL, trs.DC_OP_MULTITENANT):
+        ws = workspace(op, specs, T)
+        ws.fill_(0xFF)          # status word 0xFFFFFFFF, operands garbage
+        y = t.full((T, 256), 0x7FC0, dtype=t.int16, device="cuda")
+        trs.dc_apply_prefill(views, dev_u16(w), dev_u16(x), seg, y, ws)
+        t.cuda.synchronize()
+        assert int(ws[:4].cpu().numpy().view(np.uint32)[0]) == 0
+        dense = op == trs.DC_OP_PREFILL   # the dense form multiplies by the fp16 values
+        check_close(y_to_f64(y), ref, what="prefill 11 tenants %s" % ("dense" if dense else "decode"),
+                    ref_exact=ref if dense else ref_x)
+
+
+@pytest.mark.parametrize("mi", [0, 4, 6])
 def test_c3_prefill_full_size(mi):
-    """13B-shaped prefill (q 5120x5120, down 5120x13824): 8 tenants x 2048
-    tokens in contiguous segments, the whole matrix on the GPU; per tenant the
-    first, the last and 4 random tokens against the oracle."""
+    """13B-shaped prefill (q 5120x5120, gate 13824x5120, down 5120x13824):
+    8 tenants x 2048 tokens in contiguous segments, the whole matrix on the
+    GPU; per tenant the first and the last token and one random token of
+    every 128-token tile against the oracle."""
     note("c3 matrix", mi)
     t = torch()
     m = synth.make_c3_matrix(mi)
@@ -485,10 +564,12 @@ def test_c3_prefill_full_size(mi):
     rng = np.random.default_rng(30 + mi)
     for k, d in enumerate(m["deltas"]):
         lo, hi = int(seg[k]), int(seg[k + 1])
-        sel = np.unique(np.concatenate([[lo, hi - 1], lo + rng.choice(hi - lo, 4, replace=False)]))
+        tiles = np.arange(lo, hi, 128)
+        pick = tiles + rng.integers(0, 128, size=tiles.size)
+        sel = np.unique(np.concatenate([[lo, hi - 1], np.minimum(pick, hi - 1)]))
         yk = y_to_f64(y[t.from_numpy(sel).cuda()])
         ref = oap.apply_factored(m["w"], m["x"][sel], *oracle_tenant(d))
-        check_close(yk, ref, what="c3 %s tenant %d" % (m["name"], k))
+        check_close(yk, ref, what="c3 %s tenant %d (%d tokens)" % (m["name"], k, sel.size))
 
 
 # ---------------------------------------------------------------- HIP graphs
@@ -543,9 +624,8 @@ def test_graph_replay_matches_eager():
             t.cuda.synchronize()
             for i in range(3):
                 assert t.equal(ys[i], ref[i]), "replay %d output %d" % (rep, i)
-    ref_c = oap.apply_multitenant(w.cpu().numpy().view(np.uint16), xs[2].cpu().numpy().view(np.uint16),
-                                  ids.cpu().numpy(), [oracle_tenant(d) for d in ds])
-    check_close(y_to_f64(ys[2]), ref_c, what="graph replay vs oracle")
+    check_multitenant(y_to_f64(ys[2]), w.cpu().numpy().view(np.uint16), xs[2].cpu().numpy().view(np.uint16),
+                      ids.cpu().numpy(), ds, 256, "graph replay vs oracle")
 
 
 # ------------------------------------------------------- quantize + pack on GPU
@@ -563,6 +643,9 @@ def _pack_inputs(spec, seed):
     U = (rng.standard_normal((r, out)) * np.exp(rng.uniform(-6, 1, (r, 1)))).astype(np.float32)
     V = (rng.standard_normal((r, inn)) * np.exp(rng.uniform(-6, 1, (r, 1)))).astype(np.float32)
     sigma = np.exp(rng.uniform(-3, 2, r)).astype(np.float32)
+    if r >= 3:   # rows of largest magnitude 3e-5: fp16-subnormal scales (below 2^-14) at every width
+        U[1] *= np.float32(3e-5) / np.abs(U[1]).max()
+        V[2] *= np.float32(3e-5) / np.abs(V[2]).max()
     if r:
         V[0, :128] = 0.0
         U[-1, :128] = 0.375
@@ -576,19 +659,30 @@ def _pack_inputs(spec, seed):
 
 
 @pytest.mark.parametrize("spec", PACK_SPECS, ids=lambda s: "x".join(map(str, s)))
-def test_pack_device_matches_host(spec):
+def test_pack_device_matches_oracle(spec):
+    """dc_pack_device against the oracle's quantizer and packer (quant.compress
+    then layout.pack), byte for byte, on rows with edge groups (all zero,
+    constant, one-signed, exact ties, fp16-subnormal scales); the host packer
+    gives the same bytes."""
+    from oracle import layout
     note("pack device", spec)
     t = torch()
     U, sigma, V = _pack_inputs(spec, 40 + sum(spec))
-    host = trs.dc_pack(spec, U, sigma, V)
+    out, inn, n8, n3, n2 = spec
+    ref = layout.pack(spec, *quant.compress(U, sigma, V, n8, n3, n2))
     nb = trs.dc_packed_bytes(spec)
+    assert ref.size == nb
+    if n8 + n3 + n2 >= 3:   # the tiny rows do reach fp16 subnormal scales
+        _, _, szu, szv, _ = quant.compress(U, sigma, V, n8, n3, n2)
+        assert np.any((szu[1, :, 0] & 0x7C00) == 0) and np.any((szv[2, :, 0] & 0x7C00) == 0)
     dev = t.full((max(nb, 16),), 0xA5, dtype=t.uint8, device="cuda")   # stale bytes: the call must write all
     flag = t.full((1,), 7, dtype=t.int32, device="cuda")
     trs.dc_pack_device(spec, t.from_numpy(U).cuda(), t.from_numpy(sigma).cuda(), t.from_numpy(V).cuda(), dev, flag)
     t.cuda.synchronize()
     assert int(flag.item()) == 0
     got = dev.cpu().numpy()[:nb]
-    assert np.array_equal(got, host), "first differing byte %d" % int(np.nonzero(got != host)[0][0])
+    assert np.array_equal(got, ref), "first byte differing from the oracle: %d" % int(np.nonzero(got != ref)[0][0])
+    assert np.array_equal(trs.dc_pack(spec, U, sigma, V), ref)
 
 
 def test_pack_device_c0_svd_and_errors():

@@ -172,10 +172,10 @@ def test_workspace_bytes_rules():
 
 
 def test_prefill_workspace_holds_dense_operands():
-    """A prefill workspace adds the dense operands to the multi-tenant one:
-    min(n, 8) slots of bf16 V [rp][2 in] and U [out][3 rp], and bf16 t
-    [T][3 rp], rp = the largest rank rounded up to 128 (at least 128), each
-    region 256-byte aligned; none at T = 0."""
+    """A prefill workspace of 256 tokens or more adds the dense operands to
+    the multi-tenant one: min(n, 8) slots of bf16 V [rp][2 in] and U
+    [out][3 rp], and bf16 t [T][3 rp], rp = the largest rank rounded up to 128
+    (at least 128), each region 256-byte aligned; none below 256 tokens."""
     def dense(out, inn, rmax, n, T):
         rp = max(128, -(-rmax // 128) * 128)
         nb = min(n, 8)
@@ -188,18 +188,23 @@ def test_prefill_workspace_holds_dense_operands():
         rmax = max(sum(sp[2:]) for sp in specs)
         assert pf - mt == dense(specs[0][0], specs[0][1], rmax, len(specs), T)
     sp = [(256, 384, 2, 9, 40)] * 3
-    assert trs.dc_workspace_bytes(trs.DC_OP_PREFILL, sp, 0) == trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, sp, 0)
+    # fewer than 256 tokens can never take the dense form: no dense operands
+    for T in (0, 1, 100, 255):
+        assert trs.dc_workspace_bytes(trs.DC_OP_PREFILL, sp, T) == trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, sp, T)
 
 
-def test_prefill_rejects_a_workspace_without_the_dense_operands(L):
+def test_prefill_workspace_without_the_dense_operands(L):
+    """A prefill workspace of the multi-tenant size is enough (the call then
+    takes the decode kernels); one byte less is rejected before any launch."""
     spec = (256, 256, 2, 8, 22)
     arr = (trs._lib.dc_delta_view * 2)(_view(spec), _view(spec))
     T = 512
     seg = np.array([0, 256, 512], np.int32)
     need = trs.dc_workspace_bytes(trs.DC_OP_PREFILL, [spec] * 2, T)
+    mt = trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, [spec] * 2, T)
+    assert mt < need
     pf = L.dc_apply_prefill
-    assert pf(arr, 2, WB, X, seg.ctypes.data, 0x40000000, WS, need - 1, None) == trs.DC_ERR_BUFFER
-    assert trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, [spec] * 2, T) < need
+    assert pf(arr, 2, WB, X, seg.ctypes.data, 0x40000000, WS, mt - 1, None) == trs.DC_ERR_BUFFER
 
 
 # Fake device addresses: the host checks reject these calls before any launch.
