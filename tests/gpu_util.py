@@ -103,8 +103,16 @@ def run_decode(d, w, x, with_base=True):
 # expectation: a token of 128 elements holds only a few such roundings, so
 # its own value scatters around it; the per-token maximum is reported).
 OWN_BOUND = 2.0 ** -10
-FMT_HATCH = TOL     # bf16 rounding of the reference alone above the bar: a degenerate output
-OWN_TOL = 1e-3      # then the token must sit this close to the rounded reference
+# Degenerate outputs (a few pairs on 128 rows, whose rounding errors repeat
+# with the codes instead of averaging out): when rounding the reference to
+# bf16 alone already costs 3/4 of the bar, the bar leaves no room for the
+# documented difference between the decode kernels' exact grid values and
+# the fp16 values (up to 2^-11 per weight, which such an output does not
+# average either).  Such a token passes when it lies within OWN_TOL of the
+# rounded reference evaluated with the kernel's own weights; the tokens that
+# pass this way are named in the log.  No token of the C1-C4 workloads does.
+FMT_HATCH = 1.5e-3
+OWN_TOL = 1e-3
 
 LOG = []            # (what, max rel L2, whole-output rel L2 vs RNE_bf16(ref), hatch tokens) of every check
 LOG_PATH = os.environ.get("DC_PARITY_LOG")
@@ -126,11 +134,10 @@ def check_close(y, ref, tol=TOL, what="", ref_exact=None, own_bound=OWN_BOUND):
     oracle with the weights the kernel multiplies by; `ref` if not given)
     <= own_bound.
 
-    Exception, for outputs so degenerate that the bf16 format itself cannot
-    meet the bar (e.g. one rank on 128 rows, where rounding errors repeat with
-    the codes): if rounding the reference to bf16 already costs more than the
-    bar, the token passes when it lies within OWN_TOL of the rounded
-    `ref_exact`.  Such tokens are named in the log line."""
+    Exception, for degenerate outputs (see FMT_HATCH): if rounding the
+    reference to bf16 already costs more than FMT_HATCH, the token passes when
+    it lies within OWN_TOL of the rounded `ref_exact`.  Such tokens are named
+    in the log line."""
     rx = ref if ref_exact is None else ref_exact
     rel = oap.rel_l2_per_token(y, ref)
     fmt = oap.rel_l2_per_token(_round_bf16(ref), ref)
