@@ -307,6 +307,30 @@ dc_status dc_apply_multitenant_timed(const dc_delta_view* views, int32_t n, cons
                                      void* const* events);
 
 /*
+ * dc_apply_multitenant_noalloc -- dc_apply_multitenant for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments without the
+ * workspace: the call uses the library's own scratch array of
+ * DC_SCRATCH_BYTES on the current device, a file-scope device array that
+ * every GPU the library runs on holds until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * its first call on a device looks the array's address up once.
+ *   Limit: a call whose workspace (dc_workspace_bytes(DC_OP_MULTITENANT,..))
+ *   exceeds DC_SCRATCH_BYTES returns DC_ERR_UNSUPPORTED and enqueues nothing.
+ *   Sharing: every call on one GPU uses the same array, which keeps the last
+ *   call's contents (each call writes what it reads before reading it).
+ *   Calls on one GPU that overlap in time (different streams, or host
+ *   threads without ordering) race on the array: the caller must order them.
+ *   The status word of invalid ids lives in the array and is not returned;
+ *   such tokens are still served backbone-only.
+ * Results are identical to dc_apply_multitenant with a workspace of its own.
+ */
+#define DC_SCRATCH_BYTES (32u << 20)
+dc_status dc_apply_multitenant_noalloc(const dc_delta_view* views, int32_t n, const uint16_t* W_base,
+                                       const uint16_t* x, const int32_t* tenant_ids, uint16_t* y,
+                                       int32_t T, void* stream);
+
+/*
  * dc_apply_prefill -- n tenants, tokens grouped by tenant: tokens
  * seg_offsets[k] .. seg_offsets[k+1]-1 belong to views[k].  The prompt
  * phase of serving many fine-tuned models over one backbone: [P1]

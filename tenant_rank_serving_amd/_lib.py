@@ -24,13 +24,15 @@ DC_ERR_RANGE = -5
 DC_ERR_HIP = -6
 DC_ERR_UNSUPPORTED = -7
 DC_MAX_TENANTS = 128
+DC_SCRATCH_BYTES = 32 << 20
 DC_OP_DECODE, DC_OP_MULTITENANT, DC_OP_PREFILL = 0, 1, 2
 REGIONS = ("SIGMA", "VC8", "VC3", "VC2", "VS8", "VS3", "VS2",
            "UC8", "UC3", "UC2", "US8", "US3", "US2")
 EXPORTS = ("dc_status_string", "dc_check_spec", "dc_packed_bytes", "dc_algorithmic_bytes",
            "dc_region", "dc_pack", "dc_pack_codes", "dc_unpack", "dc_workspace_bytes",
            "dc_apply_decode", "dc_apply_multitenant", "dc_apply_multitenant_timed",
-           "dc_apply_prefill", "dc_dequant", "dc_pack_device", "dc_allocate_bits")
+           "dc_apply_prefill", "dc_dequant", "dc_pack_device", "dc_allocate_bits",
+           "dc_apply_multitenant_noalloc")
 STAGES = ("route", "xprep", "base", "vside", "uside")
 
 
@@ -82,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.dc_apply_multitenant_timed.argtypes = [vp, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32,
                                                  _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]
         L.dc_apply_prefill.argtypes = [vp, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.dc_apply_multitenant_noalloc.argtypes = [vp, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, _P]
         L.dc_dequant.argtypes = [vp, _P, _P, _P]
         L.dc_pack_device.argtypes = [sp, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
         L.dc_allocate_bits.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int64, _P, _P]
@@ -231,6 +234,16 @@ def dc_apply_multitenant(views: Sequence[DeltaView], W_base, x, tenant_ids, y, w
                                       _dptr(tenant_ids, "tenant_ids"), _dptr(y, "y"), int(T),
                                       _dptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
            "dc_apply_multitenant")
+
+
+def dc_apply_multitenant_noalloc(views: Sequence[DeltaView], W_base, x, tenant_ids, y, T: int = None,
+                                 stream=None) -> None:
+    """dc_apply_multitenant on the library's own scratch array (no workspace
+    argument, nothing allocated by the call)."""
+    T = x.shape[0] if T is None else T
+    _check(lib().dc_apply_multitenant_noalloc(_views(views), len(views), _dptr(W_base, "W_base"), _dptr(x, "x"),
+                                              _dptr(tenant_ids, "tenant_ids"), _dptr(y, "y"), int(T),
+                                              _stream(stream)), "dc_apply_multitenant_noalloc")
 
 
 def dc_apply_multitenant_timed(views: Sequence[DeltaView], W_base, x, tenant_ids, y, ws, events,

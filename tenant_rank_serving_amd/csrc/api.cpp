@@ -38,9 +38,12 @@ dc_status check_specs(const dc_spec* specs, int32_t n, Dims* d) {
   return DC_OK;
 }
 
-dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const uint16_t* x,
-              const int32_t* ids, const int32_t* seg, int32_t mode, uint16_t* y, int32_t T, void* ws,
-              size_t ws_bytes, void* stream, void* const* events = nullptr) {
+}  // namespace
+
+namespace dc {
+dc_status run_apply(const dc_delta_view* views, int32_t n, const uint16_t* W, const uint16_t* x,
+                    const int32_t* ids, const int32_t* seg, int32_t mode, uint16_t* y, int32_t T, void* ws,
+                    size_t ws_bytes, void* stream, void* const* events, size_t ws_limit) {
   if (!views || n < 1) return DC_ERR_INVALID_ARG;
   if (n > DC_MAX_TENANTS) return DC_ERR_UNSUPPORTED;
   if (T < 0) return DC_ERR_INVALID_ARG;
@@ -61,7 +64,7 @@ dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const ui
     table.t[k].n3 = specs[k].n3;
     table.t[k].n2 = specs[k].n2;
   }
-  if (!x || !y || !ws) return DC_ERR_INVALID_ARG;
+  if (!x || !y || (!ws && ws_limit == 0)) return DC_ERR_INVALID_ARG;
   if (mode == 1 && !ids) return DC_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(y, 16) || (W && !aligned(W, 16)) || !aligned(ws, 256) ||
       (ids && !aligned(ids, 4)))
@@ -69,7 +72,12 @@ dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const ui
   if (overlap(x, (size_t)T * in * 2, y, (size_t)T * out * 2)) return DC_ERR_INVALID_ARG;
   dc::WsLayout wl{};
   dc::ws_layout(T, in, out, dm.tw, n, true, dm.vb, 0, &wl);
-  if (ws_bytes < wl.total) return DC_ERR_BUFFER;
+  if (ws_limit > 0) {   // the library's own scratch array: its size is the limit, its address comes later
+    if (wl.total > ws_limit) return DC_ERR_UNSUPPORTED;
+    ws_bytes = ws_limit;
+  } else if (ws_bytes < wl.total) {
+    return DC_ERR_BUFFER;
+  }
   if (mode == 2 && T >= dc::kDenseMin) {
     // the dense prefill operands, when the workspace holds them; without them
     // the call takes the decode kernels
@@ -83,6 +91,10 @@ dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const ui
   for (int k = 0; k < n; ++k)
     if (dc_packed_bytes(&specs[k]) > lim) return DC_ERR_UNSUPPORTED;
   if (T == 0) return DC_OK;
+  if (ws_limit > 0) {
+    ws = scratch_ptr();
+    if (!ws) return DC_ERR_HIP;
+  }
   dc::ApplyArgs a;
   a.tenants = &table;
   a.n = n;
@@ -102,7 +114,14 @@ dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const ui
   a.events = events;
   return dc::launch_apply(a) == 0 ? DC_OK : DC_ERR_HIP;
 }
+}  // namespace dc
 
+namespace {
+dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const uint16_t* x, const int32_t* ids,
+              const int32_t* seg, int32_t mode, uint16_t* y, int32_t T, void* ws, size_t ws_bytes, void* stream,
+              void* const* events = nullptr) {
+  return dc::run_apply(views, n, W, x, ids, seg, mode, y, T, ws, ws_bytes, stream, events, 0);
+}
 }  // namespace
 
 extern "C" {

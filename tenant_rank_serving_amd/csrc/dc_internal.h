@@ -252,6 +252,15 @@ int dense_rank_pad(int r);
 // tenant's operands and two dense products (see kernels.hip).
 int launch_dense_prefill(const ApplyArgs& a);
 int launch_dequant(const Tenant& t, int32_t out, int32_t in, uint16_t* u16, uint16_t* v16, void* stream);
+// The checks and launches of every apply entry point.  ws_limit > 0: the
+// workspace is the library's scratch array of that many bytes (ws and
+// ws_bytes are ignored); it is looked up only once the checks pass.
+dc_status run_apply(const dc_delta_view* views, int32_t n, const uint16_t* W, const uint16_t* x,
+                    const int32_t* ids, const int32_t* seg, int32_t mode, uint16_t* y, int32_t T, void* ws,
+                    size_t ws_bytes, void* stream, void* const* events, size_t ws_limit);
+// Device address of the scratch array on the current device (null if it
+// cannot be found); defined next to the array.
+void* scratch_ptr();
 int launch_pack(int32_t out, int32_t in, int32_t n8, int32_t n3, int32_t n2, const float* U, const float* sigma,
                 const float* V, uint8_t* dst, uint32_t* flag, void* stream);
 }  // namespace dc
