@@ -27,6 +27,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# The arithmetic of the path: 3- and 2-bit codes as fp6/fp4 matrix-core
+# operands against activations in exact fp8 pieces (block-scaled MFMA), the
+# 8-bit pairs on the vector ALU with fp16 weights, the backbone as bf16 MFMA;
+# every sum in fp32, one bf16 rounding at the end.
+DTYPE = "fp4/fp6 x fp8 mx-MFMA + bf16 MFMA, fp32 sums"
 METRIC = "delta-apply tokens/s + effective packed-delta HBM GB/s (% of peak), 7B shapes"
 
 
@@ -121,49 +126,62 @@ def build_c2(layers, dev, torch, trs, synth):
     return specs, views, W, X, pool
 
 
-def cpu_baseline(trs, synth, budget_s=15.0):
+def cpu_baseline(trs, synth, budget_s=12.0):
     """The oracle (plain numpy fp64, applied from packed buffers) timed on a
-    bounded sample of the same workload, extrapolated to one whole step."""
+    bounded sample of the same workload, extrapolated to one whole step: once
+    with every host core the process may use (BLAS threads = that count) and
+    once with one core (BLAS limited to one thread)."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import apply as oap
     from oracle import layout
     threads = len(os.sched_getaffinity(0))
     ids = synth.c2_ids()
     touched = sorted(set(ids.tolist()))
-    per_shape = {}
-    sample = []
-    t_start = time.time()
-    for mi in (0, 4, 6):                      # q (4096^2), gate (11008x4096), down (4096x11008)
-        t_shape = time.time()
-        _, out, inn = synth.LLAMA2_7B[mi]
-        w = synth.make_c2_base(0, mi)
-        x = synth.make_c2_x(0, mi)
-        t0 = time.perf_counter()
-        oap.apply_factored(w, x, np.zeros((0, out)), np.zeros(0), np.zeros((0, inn)))
-        t_base = time.perf_counter() - t0
-        times = []
-        for k in touched:                     # at least two tenants, then until a third of the budget
-            if len(times) >= 2 and time.time() - t_shape > budget_s / 3:
-                break
-            d = synth.make_c2_delta(0, mi, k)
-            buf = layout.pack(d.spec, d.codes_u, d.codes_v, d.sz_u, d.sz_v, d.sigma)
-            sel = np.nonzero(ids == k)[0]
+
+    def run(budget):
+        per_shape, sample = {}, []
+        t_start = time.time()
+        for mi in (0, 4, 6):                      # q (4096^2), gate (11008x4096), down (4096x11008)
+            t_shape = time.time()
+            _, out, inn = synth.LLAMA2_7B[mi]
+            w = synth.make_c2_base(0, mi)
+            x = synth.make_c2_x(0, mi)
             t0 = time.perf_counter()
-            oap.apply_packed(d.spec, buf, None, x[sel])
-            times.append(time.perf_counter() - t0)
-            sample.append("layer0/%s/tenant%d" % (synth.LLAMA2_7B[mi][0], k))
-        per_shape[mi] = (t_base, float(np.mean(times)))
-    # step = 32 layers x (4 square + 2 up-proj + 1 down-proj) x (base + touched tenants)
-    counts = {0: 4, 4: 2, 6: 1}
-    step_s = 0.0
-    for mi, c in counts.items():
-        tb, td = per_shape.get(mi, per_shape[0])
-        step_s += synth.C2_LAYERS * c * (tb + len(touched) * td)
-    return {"value": synth.C2_TOKENS / step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "numpy fp64 oracle from packed buffers (unpack, dequant, W x + U(s*(V x))) on "
-                      "%s, averaged per matrix shape and extrapolated to 32 layers x 7 matrices x %d "
-                      "touched tenants + backbone; %.1f s of CPU work" % (", ".join(sample), len(touched),
-                                                                          time.time() - t_start)}
+            oap.apply_factored(w, x, np.zeros((0, out)), np.zeros(0), np.zeros((0, inn)))
+            t_base = time.perf_counter() - t0
+            times = []
+            for k in touched:                     # at least two tenants, then until a third of the budget
+                if len(times) >= 2 and time.time() - t_shape > budget / 3:
+                    break
+                d = synth.make_c2_delta(0, mi, k)
+                buf = layout.pack(d.spec, d.codes_u, d.codes_v, d.sz_u, d.sz_v, d.sigma)
+                sel = np.nonzero(ids == k)[0]
+                t0 = time.perf_counter()
+                oap.apply_packed(d.spec, buf, None, x[sel])
+                times.append(time.perf_counter() - t0)
+                sample.append("%s/t%d" % (synth.LLAMA2_7B[mi][0], k))
+            per_shape[mi] = (t_base, float(np.mean(times)))
+        # step = 32 layers x (4 square + 2 up-proj + 1 down-proj) x (base + touched tenants)
+        counts = {0: 4, 4: 2, 6: 1}
+        step_s = sum(synth.C2_LAYERS * c * (per_shape[mi][0] + len(touched) * per_shape[mi][1])
+                     for mi, c in counts.items())
+        return synth.C2_TOKENS / step_s, sample, time.time() - t_start
+
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    blas_threads = blas[0]["num_threads"] if blas else None
+    with threadpool_limits(limits=threads, user_api="blas"):
+        v_all, smp_all, s_all = run(budget_s)
+    with threadpool_limits(limits=1, user_api="blas"):
+        v_one, smp_one, s_one = run(budget_s)
+    what = ("numpy fp64 oracle from packed buffers (unpack, dequant, W x + U(s*(V x))) on layer 0, matrices "
+            "q, gate, down, tenants sampled per shape until about a third of the budget (%s), averaged per shape and "
+            "extrapolated to 32 layers x 7 matrices x %d touched tenants + backbone")
+    return {"value": v_all, "unit": "tokens/s", "cores": threads, "blas_threads": blas_threads, "kind": "oracle",
+            "sample": (what % (", ".join(smp_all), len(touched))) + "; %.1f s of CPU work on %d cores" % (s_all, threads),
+            "value_1core": v_one,
+            "sample_1core": "the same with one core (BLAS limited to one thread): %s; %.1f s" % (
+                ", ".join(smp_one), s_one)}
 
 
 def counter_traffic(kernel):
@@ -186,6 +204,29 @@ def counter_traffic(kernel):
         return int((float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_factor"]) +
                     float(kv["write_kib_per_dispatch"]) * float(kv["write_factor"])) * 1024)
     except (OSError, KeyError, ValueError):
+        return None
+
+
+def profile_avg_ms(kernel):
+    """Average duration of `kernel` per launch (ms) from the committed
+    rocprofv3 kernel-trace summary of this step, or None when there is none
+    for it or the kernel sources have changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "kernels_decode_c2_bench.txt")
+    try:
+        want = None
+        avg = None
+        for line in open(path):
+            f = line.split()
+            if line.startswith("source_sha256:") and len(f) > 1:
+                want = f[1]
+            elif f and f[0] == "k_" + kernel and len(f) >= 3:
+                avg = float(f[2]) * 1e-3
+        h = hashlib.sha256()
+        for name in ("k_mx.hip", "kernels.hip"):
+            h.update(open(os.path.join(ROOT, "tenant_rank_serving_amd", "csrc", name), "rb").read())
+        return avg if want == h.hexdigest() else None
+    except (OSError, ValueError):
         return None
 
 
@@ -373,7 +414,7 @@ def config_bench(args):
         res = {
             "metric": "%s layer tokens/s (delta-apply, fused with the backbone)" % name, "value": round(T / t_f * 1e3, 1),
             "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": round(t_f, 4), "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+            "ms_per_step": round(t_f, 4), "higher_is_better": True, "dtype": DTYPE, "data": "synthetic",
             "config": {"workload": {"c1": "single-tenant decode", "c3": "multi-tenant prefill, contiguous segments",
                                     "c4": "multi-tenant decode"}[w] + ", %s layer (7 matrices), 1/%d budget" % (name, budget),
                        "tenants": n_ten, "tenants_touched": touched, "tokens": T, "layer_copies_cycled": copies},
@@ -537,24 +578,14 @@ def main():
     def outputs():
         return [y.clone() for d in yss for y in d.values()]
 
-    def same_bf16(a, b):
-        """Outputs equal up to about one bf16 unit in the last place of each
-        value (float atomics in the V side may reorder a sum for inputs wider
-        than 4096; a value near zero may then even change sign, hence the
-        small absolute floor relative to the tensor's largest value)."""
-        def f32(t):
-            return (t.view(torch.int16).to(torch.int32) << 16).view(torch.float32)
-        ok, worst = True, 0.0
-        for x, y in zip(a, b):
-            fx, fy = f32(x), f32(y)
-            floor = 1e-6 * float(fx.abs().max())
-            d = (fx - fy).abs()
-            worst = max(worst, float((d / (fx.abs().max() + 1e-30)).max()))
-            ok = ok and bool((d <= 2.0 ** -7 * torch.maximum(fx.abs(), fy.abs()) + floor).all())
-        log("graph replay vs eager: largest difference %.3g of the tensor's largest value" % worst)
-        return ok
+    def same_bits(a, b):
+        """Outputs of the replayed graph equal the eager step's bit for bit
+        (every sum is added in a fixed order)."""
+        diff = sum(int((x != y).sum()) for x, y in zip(a, b))
+        log("graph replay vs eager: %d differing output values" % diff)
+        return diff == 0
 
-    results, eager, dom_live = {}, {}, {}
+    results, eager, dom_live, step_stats = {}, {}, {}, {}
     for mode in ("fused", "delta"):
         run = layered_step(mode == "fused")
         log("timing %s step: warmup %d, steps %d" % (mode, args.warmup, args.steps))
@@ -571,15 +602,18 @@ def main():
         for _ in range(args.warmup):
             g.replay()
         torch.cuda.synchronize()
-        if not same_bf16(ref, outputs()):
+        if not same_bits(ref, outputs()):
             raise RuntimeError("graph replay of the %s step differs from the eager step" % mode)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        marks[0].record()
+        for k in range(args.steps):
             g.replay()
-        e1.record()
+            marks[k + 1].record()
         torch.cuda.synchronize()
-        results[mode] = e0.elapsed_time(e1) / args.steps
+        results[mode] = marks[0].elapsed_time(marks[-1]) / args.steps
+        per = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps))
+        step_stats[mode] = {"median": round(per[len(per) // 2], 4), "min": round(per[0], 4),
+                            "max": round(per[-1], 4)}
         del g
         # (2) the same step issued eagerly, for reference
         eager[mode] = timed_steps(run, args.steps, 1)
@@ -620,9 +654,15 @@ def main():
     # dom_live: the kernel's average duration per launch inside the
     # instrumented fused steps, measured with HIP events on each call's stream
     achieved = per_launch[dom] / (dom_live["fused"] * 1e-3) / 1e9
+    # the same kernel's average duration per launch in the committed
+    # rocprofv3 kernel trace of this step (all its launches)
+    prof_ms = profile_avg_ms(dom)
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(dom),
             "bytes_per_launch": int(per_launch[dom]), "avg_launch_ms": round(dom_live["fused"], 5),
+            "frac_profile": (round(per_launch[dom] / (prof_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                             if prof_ms else None),
+            "avg_launch_ms_profile": prof_ms,
             "avg_launch_ms_in_sequence": round(stage_avg[dom], 5),
             "stages_avg_ms_in_sequence": {s: round(v, 5) for s, v in stage_avg.items()}}
 
@@ -631,7 +671,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
         "config": {"workload": "multi-tenant decode, Llama-2-7B shapes: %d layers x 7 matrices, 50 resident "
                                "1/16 deltas (8/3/2-bit), shared bf16 backbone, 64 tokens Zipf(1.1)" % args.layers,
                    "layers": args.layers, "tenants_resident": synth.C2_TENANTS, "tenants_touched": len(touched),
@@ -639,6 +679,7 @@ def main():
         "packed_delta_GBps": round(delta_bytes / (ms * 1e-3) / 1e9, 1),
         "fused_total_GBps": round((delta_bytes + base_bytes) / (ms * 1e-3) / 1e9, 1),
         "launch": "HIP graph replay of one captured step",
+        "step_ms_per_replay": step_stats,
         "eager_ms_per_step": {"fused": round(eager["fused"], 4), "delta": round(eager["delta"], 4)},
         "delta_only": {"ms_per_step": round(ms_d, 4), "tokens_per_s": round(T / (ms_d * 1e-3), 1),
                        "packed_delta_GBps": round(delta_bytes / (ms_d * 1e-3) / 1e9, 1),
@@ -647,7 +688,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(trs, synth)
+        out["cpu_baseline"] = cpu_baseline(trs, synth, budget_s=8.0)
     print(json.dumps(out), flush=True)
 
 

@@ -261,10 +261,12 @@ size_t dc_workspace_bytes(int32_t op, const dc_spec* specs, int32_t n, int32_t T
  *   ws      device workspace of ws_bytes >= dc_workspace_bytes(DC_OP_DECODE,..)
  *   stream  hipStream_t
  * T = 0 is a no-op returning DC_OK.  x and y must not overlap.
- * Summation order: parts of V x (in wider than 2048) and, for T <= 256, of
- * W_base x (in wider than 512) are added with float atomics, so two calls may
- * round an output differently in its last bit; batches of more than 256
- * tokens compute W_base x in tiles of 128 x 128, in a fixed order.
+ * Summation order is fixed, so repeated calls give the same bits: V x is
+ * summed over slices of 2048 inputs and, for T <= 256, W_base x over K
+ * ranges of 512; two partials are added onto zero (order-independent), more
+ * are added in slice (range) order by the work item that finishes last.
+ * Batches of more than 256 tokens compute W_base x in tiles of 128 x 128
+ * (another fixed order, so they may round differently from smaller batches).
  */
 dc_status dc_apply_decode(const dc_delta_view* d, const uint16_t* W_base, const uint16_t* x,
                           uint16_t* y, int32_t T, void* ws, size_t ws_bytes, void* stream);

@@ -132,9 +132,12 @@ struct TenantTable {
   Tenant t[DC_MAX_TENANTS];
 };
 
-// One bucket of routed tokens that is not empty, as the prep kernel lists
-// them (bucket order; the rest of the list has p0 == p1): the tenant record
-// (zero for the backbone-only bucket k == n) and the routed range [p0, p1).
+// One work item of routed tokens, as the prep kernel lists them: the rows of
+// a bucket in chunks of kChunkRows (bucket order; the rest of the list has
+// p0 == p1): the tenant record (zero for the backbone-only bucket k == n)
+// and the routed range [p0, p1).  The V-side and U-side blocks of different
+// chunks of one tenant run side by side (the codes they share come from
+// the caches after the first read).
 struct ActEntry {
   const uint8_t* base;
   int32_t n8, n3, n2;
@@ -142,6 +145,10 @@ struct ActEntry {
   int32_t p0, p1;
 };
 static_assert(sizeof(ActEntry) == 32, "one 32-byte load per block");
+constexpr int kChunkRows = 8;   // token rows per work item (one V-side and one U-side pass)
+// Work items of a call of n tenants and T tokens: at most one partly filled
+// chunk per bucket (n tenants + the backbone-only bucket) plus T / kChunkRows.
+DC_HD inline int32_t act_capacity(int32_t n, int32_t T) { return n + 1 + (T + kChunkRows - 1) / kChunkRows; }
 
 // Work decomposition of the matrix-core path (shared by host sizing and kernels).
 constexpr int kVSlice = 16;   // 128-groups of the input per V-side work item
@@ -149,6 +156,11 @@ constexpr int kVRows = 8;     // token rows per V-side pass
 constexpr int kVTiles = 2;    // 16-rank tiles per V-side wave
 constexpr int kVRanks = 4 * 16 * kVTiles;   // ranks per V-side block (4 waves)
 constexpr int kVDepth = 8;    // groups of codes a V-side wave keeps in flight
+static_assert(kChunkRows == kVRows, "one V-side pass per work item");
+
+// Split backbone product (T <= 256): K ranges of kSKSteps steps of 32.
+constexpr int kSKSteps = 16;
+DC_HD inline int base_splits(int in, int T) { return T <= 256 ? (in / 32 + kSKSteps - 1) / kSKSteps : 0; }
 
 // Prefill segments of at least this many tokens can take the dense form
 // (every non-empty segment of the call must have this many).
@@ -170,13 +182,16 @@ struct WsLayout {
   size_t flags;   // uint32 status word (+ padding to 256 B)
   size_t offs;    // int32 [n+2] bucket starts in sorted order (bucket n = backbone only)
   size_t perm;    // int32 [T] sorted position -> token index
-  size_t act;     // ActEntry [n+1] buckets with tokens first
+  size_t act;     // ActEntry [nact] work items of the buckets with tokens, in bucket order
   size_t xf;      // uint8 [T][in/128][256] fp8 hi/lo fragments of x (matrix-core A operand)
   size_t xsc;     // uint32 [T][in/128] E8M0 block scales of the hi fragments
   size_t xsum;    // fp32 [T][in/128] sums of x over each 128-group
   size_t xt;      // bf16 x in matrix-core B tiles: [in/32][ceil(T/16)][64 lanes][8]
   size_t ybase;   // fp32 [T][out] backbone product, original order
-  size_t vpart;   // fp32 [T][rs] t = sigma * (V x), sorted order (accumulated over input slices)
+  size_t vpart;   // fp32 [T][rs] t = sigma * (V x), sorted order
+  size_t vpt;     // fp32 [ns][T][rs] per-slice partials of t when ns >= 3 (added in slice order)
+  size_t bpt;     // fp32 [nks][T][out] per-range partials of W x when nks >= 3 (added in range order)
+  size_t cnt;     // uint32 arrival counters of the V rank blocks [nact][vb]
   size_t dav;     // prefill, dense form: dnb slots of bf16 [drp][2 in] V operand (hi, lo)
   size_t dau;     // dnb slots of bf16 [out][3 drp] U operand (hi, hi, lo)
   size_t dtb;     // bf16 [T][3 drp] t of one segment (hi, lo, hi)
@@ -185,7 +200,17 @@ struct WsLayout {
   int32_t dnb;    // operand slots: tenants whose dense products share one launch
   int32_t rs;     // row stride of vpart (max t_width over tenants)
   int32_t vb;     // max V-side rank blocks per tenant
+  int32_t ns;     // V-side input slices
+  int32_t nks;    // K ranges of the split backbone product (0: tiled product)
+  int32_t nact;   // work-item capacity of act
+  int32_t ncnt;   // counters in cnt
+  int32_t nvcnt;  // of which V-side counters
 };
+
+// Sums of more than two partials are added in a fixed order by the work item
+// that arrives last; two partials (or one) are added onto zero with float
+// atomics, which is order-independent for two terms.
+constexpr int kMaxAtomicTerms = 2;
 
 // rs: max t_width over tenants; vbmax: max v_blocks over tenants.
 // drp: rank rows of the dense prefill operands (0 for decode calls).
@@ -199,7 +224,8 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rs, int32_t n,
   W->flags = take(256);
   W->offs = take(4 * ((size_t)n + 2));
   W->perm = take(4 * (size_t)T);
-  W->act = take(sizeof(ActEntry) * ((size_t)n + 1));
+  W->nact = act_capacity(n, T);
+  W->act = take(sizeof(ActEntry) * (size_t)W->nact);
   const size_t items = (size_t)T * (in / kGroup);
   W->xf = take(256 * items);
   W->xsc = take(4 * items);
@@ -207,6 +233,13 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rs, int32_t n,
   W->xt = take(with_base ? 2 * (size_t)in * round_up((size_t)T, 16) : 0);
   W->ybase = take(with_base ? 4 * (size_t)T * out : 0);
   W->vpart = take(4 * (size_t)T * W->rs);
+  W->ns = v_slices(in);
+  W->nks = with_base ? base_splits(in, T) : 0;
+  W->vpt = take(W->ns > kMaxAtomicTerms ? 4 * (size_t)W->ns * T * W->rs : 0);
+  W->bpt = take(W->nks > kMaxAtomicTerms ? 4 * (size_t)W->nks * T * out : 0);
+  W->nvcnt = W->ns > kMaxAtomicTerms ? W->nact * vbmax : 0;
+  W->ncnt = W->nvcnt;
+  W->cnt = take(4 * (size_t)W->ncnt);
   W->drp = drp;
   W->dnb = drp > 0 ? (n < 8 ? n : 8) : 0;
   W->dav = take(2 * (size_t)W->dnb * drp * 2 * in);
@@ -239,12 +272,13 @@ struct ApplyArgs {
   void* const* events;         // optional DC_STAGE_COUNT + 1 hipEvent_t, may be null
 };
 int launch_apply(const ApplyArgs& a);
-// K ranges of the split backbone product (0: the tiled product, T > 256;
-// 1: one range; > 1: ybase must be zeroed before it runs, its ranges add
-// into it).
-int base_splits(int out, int in, int T);
-int launch_base(const uint16_t* W, const uint16_t* x, const uint16_t* xt, float* ybase, int out, int in, int T,
-                void* stream);
+// The backbone product W x into ybase (fp32 [T][out]).  Split over
+// base_splits(in, T) K ranges when T <= 256: with two ranges ybase must be
+// zeroed before it runs (the ranges add into it); with more, the ranges store
+// partials into bpt [nks][T][out], which the V-side kernel adds in range order
+// into ybase.  T > 256: the tiled product.
+int launch_base(const uint16_t* W, const uint16_t* x, const uint16_t* xt, float* ybase, float* bpt, int out, int in,
+                int T, void* stream);
 // Rank rows of the dense prefill operands of a tenant with r pairs (r rounded
 // up to whole 128-row tiles, at least one tile).
 int dense_rank_pad(int r);

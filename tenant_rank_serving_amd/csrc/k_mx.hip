@@ -31,6 +31,7 @@ namespace dc {
 namespace {
 
 #include "mx_common.h"
+#include "combine.h"
 
 struct Seg {
   int b, lo, n;
@@ -67,34 +68,41 @@ struct SegArg {
 // 128-group) of x into fp8 hi/lo A fragments, their E8M0 scales and the
 // group sum; the other blocks also zero t and, when the backbone product is
 // split over K, W x (both are accumulated with float atomics).
-__device__ __forceinline__ void list_active(const Tenant& mine, int32_t n, const int* so,
+__device__ __forceinline__ void list_active(const Tenant& mine, int32_t n, const int* so, int32_t cap,
                                             ActEntry* __restrict__ act) {
-  __shared__ int wcnt[4];
+  __shared__ int wsum[4];
   const int tid = threadIdx.x, b = tid, lane = tid & 63, wave = tid >> 6;
-  const bool live = b <= n && so[b + 1] > so[b];
-  const uint64_t m = __ballot(live);
-  if (lane == 0) wcnt[wave] = __popcll(m);
-  lds_barrier();
-  int pos = __popcll(m & ((1ull << lane) - 1)), total = 0;
-  for (int w = 0; w < 4; ++w) {
-    if (w < wave) pos += wcnt[w];
-    total += wcnt[w];
+  // work items of bucket b: its rows in chunks of kChunkRows
+  const int rows = b <= n ? so[b + 1] - so[b] : 0;
+  const int items = (rows + kChunkRows - 1) / kChunkRows;
+  int v = items;   // inclusive scan over the buckets
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
   }
-  if (live) {
+  if (lane == 63) wsum[wave] = v;
+  lds_barrier();
+  int pos = v - items, total = 0;
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) pos += wsum[w];
+    total += wsum[w];
+  }
+  for (int j = 0; j < items; ++j) {
     ActEntry e;
     e.base = b < n ? mine.base : nullptr;
     e.n8 = b < n ? mine.n8 : 0;
     e.n3 = b < n ? mine.n3 : 0;
     e.n2 = b < n ? mine.n2 : 0;
     e.k = b;
-    e.p0 = so[b];
-    e.p1 = so[b + 1];
-    act[pos] = e;
+    e.p0 = so[b] + j * kChunkRows;
+    e.p1 = min(so[b] + (j + 1) * kChunkRows, so[b + 1]);
+    act[pos + j] = e;
   }
-  if (b <= n && b >= total) {   // the rest of the list: empty entries
+  for (int i = total + tid; i < cap; i += blockDim.x) {   // the rest of the list: empty entries
     ActEntry e{};
     e.k = -1;
-    act[b] = e;
+    act[i] = e;
   }
 }
 
@@ -106,13 +114,16 @@ __global__ void __launch_bounds__(256) k_prep(TenantTable tt, const uint16_t* __
                                               uint32_t* __restrict__ flags, uint8_t* __restrict__ xf,
                                               uint32_t* __restrict__ xsc, float* __restrict__ xsum,
                                               uint16_t* __restrict__ xt, float* __restrict__ tv, int32_t ntv,
-                                              float* __restrict__ yb, int32_t nyb) {
+                                              float* __restrict__ yb, int32_t nyb, uint32_t* __restrict__ cnt,
+                                              int32_t ncnt, int32_t cap) {
   const int tid = threadIdx.x;
-  // t accumulates atomically: zeroed by the blocks after the first (the
-  // first block's barriers would wait for its stores to finish)
+  // t and W x when their parts add up atomically, and the arrival counters of
+  // the fixed-order sums: zeroed by the blocks after the first (the first
+  // block's barriers would wait for its stores to finish)
   if (blockIdx.x > 0) {
     for (int i = (blockIdx.x - 1) * 256 + tid; i < ntv; i += (gridDim.x - 1) * 256) tv[i] = 0.f;
-    for (int i = (blockIdx.x - 1) * 256 + tid; i < nyb; i += (gridDim.x - 1) * 256) yb[i] = 0.f;   // W x, when split over K
+    for (int i = (blockIdx.x - 1) * 256 + tid; i < nyb; i += (gridDim.x - 1) * 256) yb[i] = 0.f;
+    for (int i = (blockIdx.x - 1) * 256 + tid; i < ncnt; i += (gridDim.x - 1) * 256) cnt[i] = 0u;
   }
   if (blockIdx.x == 0) {
     static_assert(DC_MAX_TENANTS + 1 <= 256, "one thread per bucket");
@@ -130,7 +141,7 @@ __global__ void __launch_bounds__(256) k_prep(TenantTable tt, const uint16_t* __
         *flags = 0;
       }
       lds_barrier();
-      list_active(mine, n, so, act);
+      list_active(mine, n, so, cap, act);
       return;
     }
     __shared__ int cnt[DC_MAX_TENANTS + 1];   // tokens per bucket
@@ -174,7 +185,7 @@ __global__ void __launch_bounds__(256) k_prep(TenantTable tt, const uint16_t* __
       if (tid == 0) *flags = bad ? 1u : 0u;
     }
     lds_barrier();
-    list_active(mine, n, so, act);
+    list_active(mine, n, so, cap, act);
     for (int c0 = 0; c0 < T; c0 += blockDim.x) {
       const int t = c0 + tid;
       int b = -1;
@@ -279,6 +290,90 @@ __global__ void __launch_bounds__(256) k_prep(TenantTable tt, const uint16_t* __
 }
 
 // ------------------------------------------------------------------ V side
+// Where a V-side block puts sigma * (its slice's part of V x): with at most
+// kMaxAtomicTerms input slices, added into t (zeroed by prep) with float
+// atomics (order-independent for two terms); with more, stored as the
+// slice's partial and added in slice order by the block of the same ranks
+// that finishes last (counter per bucket and rank block).
+struct VOut {
+  float* tv;         // t [T][rs], sorted rows
+  float* vpt;        // partials [ns][T][rs] (ns > kMaxAtomicTerms)
+  uint32_t* vcnt;    // arrival counters [n + 1][vb]
+  int32_t rs, ns, T, vb;
+};
+
+__device__ __forceinline__ void v_put(const VOut& o, int s, int row, int rank, float v) {
+  if (o.ns <= kMaxAtomicTerms)
+    atomicAdd(o.tv + (size_t)row * o.rs + rank, v);
+  else
+    st_dev(o.vpt + ((size_t)s * o.T + row) * o.rs + rank, v);
+}
+
+// After every pass of the block of work item `item`: the last of the ns
+// slices of ranks [r0, r0 + nr) adds the partials of rows [p0, p1) in slice
+// order into t (the slices of an output are loaded kSliceBatch at a time).
+constexpr int kSliceBatch = 8;   // all the slices of up to 16384 inputs
+__device__ __forceinline__ void v_combine(const VOut& o, int item, int b, int p0, int p1, int r0, int nr) {
+  if (o.ns <= kMaxAtomicTerms) return;
+  __shared__ int last;
+  if (!arrive_last(&o.vcnt[item * o.vb + b], o.ns, &last)) return;
+  const size_t sstride = (size_t)o.T * o.rs;
+  for (int i = threadIdx.x; i < (p1 - p0) * nr; i += blockDim.x) {
+    const int row = p0 + i / nr, rank = r0 + i % nr;
+    const float* src = o.vpt + (size_t)row * o.rs + rank;
+    float v = 0.f;
+    for (int s0 = 0; s0 < o.ns; s0 += kSliceBatch) {
+      float p[kSliceBatch];
+#pragma unroll
+      for (int j = 0; j < kSliceBatch; ++j) p[j] = s0 + j < o.ns ? ld_dev(src + (s0 + j) * sstride) : 0.f;
+#pragma unroll
+      for (int j = 0; j < kSliceBatch; ++j)
+        if (s0 + j < o.ns) v += p[j];
+    }
+    o.tv[(size_t)row * o.rs + rank] = v;
+  }
+}
+
+// The backbone product's K-range partials (more than two ranges) added in
+// range order into W x, by blocks of the V-side launch that run before its
+// V-side blocks: block = 64 rows x 8 tokens, thread = one row, two tokens,
+// all of an output's ranges loaded before the sum.
+struct BaseSum {
+  const float* bpt;   // [nks][T][out]
+  float* ybase;       // [T][out]
+  int32_t nks, out, T;
+  int32_t nblk;       // reduce blocks: out/64 x ceil(T/8)
+  int32_t rows;       // leading grid rows they take
+};
+
+__device__ void base_sum(const BaseSum& bs, int idx) {
+  const int ntb = (bs.T + 7) / 8;
+  const int rb = idx / ntb, tb = idx % ntb;
+  const int ro = rb * 64 + (threadIdx.x & 63), t0 = tb * 8 + 2 * (threadIdx.x >> 6);
+  if (t0 >= bs.T) return;
+  const bool two = t0 + 1 < bs.T;
+  const size_t rstride = (size_t)bs.T * bs.out;
+  const float* src = bs.bpt + (size_t)t0 * bs.out + ro;
+  float v0 = 0.f, v1 = 0.f;
+  for (int r0 = 0; r0 < bs.nks; r0 += 16) {
+    float a[16], c[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool ok = r0 + j < bs.nks;
+      a[j] = ok ? src[(r0 + j) * rstride] : 0.f;
+      c[j] = ok && two ? src[(r0 + j) * rstride + bs.out] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (r0 + j < bs.nks) {
+        v0 += a[j];
+        v1 += c[j];
+      }
+  }
+  bs.ybase[(size_t)t0 * bs.out + ro] = v0;
+  if (two) bs.ybase[(size_t)(t0 + 1) * bs.out + ro] = v1;
+}
+
 // Work item (block): tenant k = blockIdx.y; blockIdx.x = rank block rb *
 // v_slices + input slice s.  Rank blocks: the 8-bit rows (vector ALU, fp16
 // dequantized weights), then blocks of kVRanks ranks of the 3-bit and of the
@@ -394,7 +489,7 @@ template <int B>
 __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, int in, int s,
                           const int32_t* __restrict__ perm, int p0, int p1, const uint8_t* __restrict__ xf,
                           const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
-                          const float* __restrict__ sigma, float* __restrict__ tv, int rs, VLds& S) {
+                          const float* __restrict__ sigma, const VOut& vo, VLds& S) {
   static_assert(kVTiles == 2, "hold2 covers two tiles");
   constexpr int fmt = B == 2 ? kFmtFp4 : kFmtFp6;
   constexpr int bsc = B == 2 ? kScaleFp4Code : kScaleFp6Code;
@@ -487,7 +582,7 @@ __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, i
       for (int h = 0; h < kVTiles; ++h)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (rv[h] && 4 * q + r < nt) atomicAdd(tv + (size_t)(pb + 4 * q + r) * rs + tbase + li[h], sig[h] * acc[h][r]);
+          if (rv[h] && 4 * q + r < nt) v_put(vo, s, pb + 4 * q + r, tbase + li[h], sig[h] * acc[h][r]);
     }
   }
 }
@@ -497,7 +592,7 @@ __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, i
 // slice, a pass's kVRows token rows and 4 rows at a time; the block sums per
 // (row, token) and adds sigma * partial into t.
 __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, const uint16_t* __restrict__ x,
-                           const int32_t* __restrict__ perm, int p0, int p1, float* __restrict__ tv, int rs) {
+                           const int32_t* __restrict__ perm, int p0, int p1, const VOut& vo) {
   __shared__ float red[4][4][kVRows];   // [wave][row][token row]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const Seg sg = seg_of(tn, L, 0);
@@ -565,8 +660,7 @@ __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, con
       if (tid < 4 * kVRows) {
         const int u = tid / kVRows, t = tid % kVRows;
         if (r0 + u < sg.n && t < nt)
-          atomicAdd(tv + (size_t)(pb + t) * rs + r0 + u,
-                    sigma[r0 + u] * ((red[0][u][t] + red[1][u][t]) + (red[2][u][t] + red[3][u][t])));
+          v_put(vo, s, pb + t, r0 + u, sigma[r0 + u] * ((red[0][u][t] + red[1][u][t]) + (red[2][u][t] + red[3][u][t])));
       }
       __syncthreads();
     }
@@ -577,8 +671,14 @@ __global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t out, int32_t i
                                                const uint16_t* __restrict__ x, const ActEntry* __restrict__ act,
                                                const int32_t* __restrict__ perm, const uint8_t* __restrict__ xf,
                                                const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
-                                               float* __restrict__ tv, int32_t rs) {
-  const ActEntry e = act[blockIdx.y];   // the blockIdx.y-th bucket with tokens
+                                               VOut vo, BaseSum bs) {
+  if ((int)blockIdx.y < bs.rows) {   // the backbone product's partial sums
+    const int idx = blockIdx.y * gridDim.x + blockIdx.x;
+    if (idx < bs.nblk) base_sum(bs, idx);
+    return;
+  }
+  const int item = blockIdx.y - bs.rows;
+  const ActEntry e = act[item];         // the item-th work item
   const int p0 = e.p0, p1 = e.p1;
   if (p0 >= p1 || e.k >= n) return;     // empty entry, or the backbone-only bucket
   Tenant tn;
@@ -587,14 +687,19 @@ __global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t out, int32_t i
   tn.n3 = e.n3;
   tn.n2 = e.n2;
   tn.pad_ = 0;
-  const int ns = v_slices(in);
-  int b = blockIdx.x / ns;
+  const int ns = vo.ns;
+  const int bv = blockIdx.x / ns;   // rank block (counter index)
+  int b = bv;
   const int s = blockIdx.x % ns;
   if (b >= v_blocks(tn.n8, tn.n3, tn.n2)) return;
   Layout L;
   layout_of(out, in, tn.n8, tn.n3, tn.n2, &L);
   if (tn.n8 > 0) {
-    if (b == 0) { vside_8bit(tn, L, in, s, x, perm, p0, p1, tv, rs); return; }
+    if (b == 0) {
+      vside_8bit(tn, L, in, s, x, perm, p0, p1, vo);
+      v_combine(vo, item, bv, p0, p1, 0, tn.n8);
+      return;
+    }
     --b;
   }
   __shared__ VLds S;
@@ -604,12 +709,14 @@ __global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t out, int32_t i
   const bool three = b < b3;
   const int tile0 = ((three ? b : b - b3) * 4 + wave) * kVTiles;
   const int sn = three ? tn.n3 : tn.n2;
+  const int tb = t_base(tn.n8, tn.n3, three ? 1 : 2);
   if (three)
-    vside_blk<3>(seg_of(tn, L, 1), t_base(tn.n8, tn.n3, 1), tile0, tile0 * 16 < sn, in, s, perm, p0, p1, xf, xsc,
-                 xsum, sigma, tv, rs, S);
+    vside_blk<3>(seg_of(tn, L, 1), tb, tile0, tile0 * 16 < sn, in, s, perm, p0, p1, xf, xsc, xsum, sigma, vo, S);
   else
-    vside_blk<2>(seg_of(tn, L, 2), t_base(tn.n8, tn.n3, 2), tile0, tile0 * 16 < sn, in, s, perm, p0, p1, xf, xsc,
-                 xsum, sigma, tv, rs, S);
+    vside_blk<2>(seg_of(tn, L, 2), tb, tile0, tile0 * 16 < sn, in, s, perm, p0, p1, xf, xsc, xsum, sigma, vo, S);
+  // ranks of this block: kVRanks consecutive ranks of its segment
+  const int rb0 = (three ? b : b - b3) * kVRanks;
+  v_combine(vo, item, bv, p0, p1, tb + rb0, min(kVRanks, sn - rb0));
 }
 
 // ------------------------------------------------------------------ U side
@@ -912,7 +1019,9 @@ int launch_apply(const ApplyArgs& a) {
   uint32_t* xsc = reinterpret_cast<uint32_t*>(a.ws + a.wl.xsc);
   float* xsum = reinterpret_cast<float*>(a.ws + a.wl.xsum);
   // the B tiles of x feed the split-K backbone product only
-  uint16_t* xt = a.W && base_splits(a.out, a.in, a.T) > 0 ? reinterpret_cast<uint16_t*>(a.ws + a.wl.xt) : nullptr;
+  uint16_t* xt = a.W && a.wl.nks > 0 ? reinterpret_cast<uint16_t*>(a.ws + a.wl.xt) : nullptr;
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(a.ws + a.wl.cnt);
+  float* bpt = reinterpret_cast<float*>(a.ws + a.wl.bpt);
   SegArg seg{};
   if (a.mode == 2)
     for (int k = 0; k <= a.n; ++k) seg.v[k] = a.seg[k];
@@ -921,17 +1030,41 @@ int launch_apply(const ApplyArgs& a) {
   };
   mark(DC_STAGE_ROUTE);
   mark(DC_STAGE_XPREP);
-  const int nyb = a.W && base_splits(a.out, a.in, a.T) > 1 ? a.T * a.out : 0;
+  // t is zeroed when its slices add up atomically, W x when its two K ranges do
+  const int ntv = a.wl.ns <= kMaxAtomicTerms ? a.T * a.wl.rs : 0;
+  const int nyb = a.W && a.wl.nks == kMaxAtomicTerms ? a.T * a.out : 0;
   hipLaunchKernelGGL(k_prep, dim3((unsigned)(1 + (items + 3) / 4)), dim3(256), 0, st, *a.tenants, a.x, a.ids, a.T,
-                     a.in, a.n, a.mode, seg, offs, perm, act, flags, xf, xsc, xsum, xt, tv, a.T * a.wl.rs, ybase, nyb);
+                     a.in, a.n, a.mode, seg, offs, perm, act, flags, xf, xsc, xsum, xt, tv, ntv, ybase, nyb, cnt,
+                     a.wl.ncnt, a.wl.nact);
   mark(DC_STAGE_BASE);
-  if (a.W) launch_base(a.W, a.x, xt, ybase, a.out, a.in, a.T, a.stream);
+  if (a.W) launch_base(a.W, a.x, xt, ybase, bpt, a.out, a.in, a.T, a.stream);
   mark(DC_STAGE_VSIDE);
-  if (a.wl.vb > 0)
-    hipLaunchKernelGGL(k_vside, dim3((unsigned)(a.wl.vb * v_slices(a.in)), (unsigned)a.n), dim3(256), 0, st,
-                       a.n, a.out, a.in, a.x, act, perm, xf, xsc, xsum, tv, a.wl.rs);
+  BaseSum bs{};
+  const int gx = a.wl.vb > 0 ? a.wl.vb * a.wl.ns : 1;
+  if (a.W && a.wl.nks > kMaxAtomicTerms) {
+    bs.bpt = bpt;
+    bs.ybase = ybase;
+    bs.nks = a.wl.nks;
+    bs.out = a.out;
+    bs.T = a.T;
+    bs.nblk = (a.out / 64) * ((a.T + 7) / 8);
+    bs.rows = (bs.nblk + gx - 1) / gx;
+  }
+  if (a.wl.vb > 0 || bs.rows > 0) {
+    VOut vo;
+    vo.tv = tv;
+    vo.vpt = reinterpret_cast<float*>(a.ws + a.wl.vpt);
+    vo.vcnt = cnt;
+    vo.rs = a.wl.rs;
+    vo.ns = a.wl.ns;
+    vo.T = a.T;
+    vo.vb = a.wl.vb;
+    const unsigned gy = (unsigned)(bs.rows + (a.wl.vb > 0 ? a.wl.nact : 0));
+    hipLaunchKernelGGL(k_vside, dim3((unsigned)gx, gy), dim3(256), 0, st, a.n, a.out, a.in, a.x, act, perm, xf, xsc,
+                       xsum, vo, bs);
+  }
   mark(DC_STAGE_USIDE);
-  hipLaunchKernelGGL(k_uside, dim3((unsigned)(a.out / kGroup), (unsigned)(a.n + 1)), dim3(kUWaves * 64), 0, st,
+  hipLaunchKernelGGL(k_uside, dim3((unsigned)(a.out / kGroup), (unsigned)a.wl.nact), dim3(kUWaves * 64), 0, st,
                      a.n, a.out, a.in, act, perm, tv, a.wl.rs, a.T, ybase, a.y);
   mark(DC_STAGE_COUNT);
   return (int)hipGetLastError();

@@ -18,6 +18,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufFlags = 0x00020000;   // buffer resource word 3: raw 32-bit dwords, bounds-checked
 
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
@@ -246,10 +247,14 @@ unsigned gemm_tiles(int M, int N) { return (unsigned)(M / kGT) * (unsigned)((N +
 // direct-to-LDS loads (a fixed count, all in flight at once), next to the
 // first kSKDepth K-steps of its W rows; after one barrier the loop streams W
 // kSKDepth steps ahead with no further synchronization.  The partial sums
-// go through LDS transposed, so that one wave instruction adds 64
-// consecutive rows of one token into ybase (zeroed by the prep kernel) with
-// float atomics; a single range stores them.
-constexpr int kSKSteps = 16;   // K-steps per range: 4 KB of x (64 tokens) each, 64 KB of LDS
+// go through LDS transposed, so that one wave instruction covers 64
+// consecutive rows of one token.  A single range stores them; two ranges add
+// them into ybase (zeroed by the prep kernel) with float atomics, which is
+// order-independent for two terms; with more ranges every range stores its
+// partial into bpt, and the blocks of the next kernel (the V side) add them
+// in range order into ybase (the same bits on every run).
+// kSKSteps (K-steps per range: 4 KB of x for 64 tokens each, 64 KB of LDS)
+// is shared with the host's workspace sizing.
 constexpr int kSKDepth = 8;    // W K-steps in flight per wave
 typedef __attribute__((address_space(3))) void base_lds_t;
 
@@ -260,8 +265,8 @@ __device__ __forceinline__ void lds_barrier() {   // orders LDS only: W loads st
 }
 
 __global__ void __launch_bounds__(256) k_base_sk(const uint16_t* __restrict__ W, const uint16_t* __restrict__ xt,
-                                                 float* __restrict__ ybase, int32_t out, int32_t in, int32_t T,
-                                                 int32_t nks) {
+                                                 float* __restrict__ ybase, float* __restrict__ bpt,
+                                                 int32_t out, int32_t in, int32_t T, int32_t nks) {
   __shared__ __attribute__((aligned(16))) uint4 xs[kSKSteps][4][64];   // [step][token tile][lane] B tiles
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r0 = blockIdx.x * 64;
@@ -318,14 +323,19 @@ __global__ void __launch_bounds__(256) k_base_sk(const uint16_t* __restrict__ W,
     for (int i = 0; i < 4; ++i) red[(16 * j + (lane & 15)) * 65 + 16 * wave + 4 * (lane >> 4) + i] = acc[j][i];
   lds_barrier();
   const int ntok = min(64, T - t0);
-  for (int tl = wave; tl < ntok; tl += 4) {   // wave: tokens wave, wave + 4, ..; lane: row
-    float* dst = ybase + (size_t)(t0 + tl) * out + r0 + lane;
-    const float v = red[tl * 65 + lane];
-    if (nks > 1)
-      atomicAdd(dst, v);
-    else
-      *dst = v;
+  if (nks <= kMaxAtomicTerms) {
+    for (int tl = wave; tl < ntok; tl += 4) {   // wave: tokens wave, wave + 4, ..; lane: row
+      float* dst = ybase + (size_t)(t0 + tl) * out + r0 + lane;
+      const float v = red[tl * 65 + lane];
+      if (nks > 1)
+        atomicAdd(dst, v);
+      else
+        *dst = v;
+    }
+    return;
   }
+  float* part = bpt + blockIdx.y * (size_t)T * out;   // this range's partials
+  for (int tl = wave; tl < ntok; tl += 4) part[(size_t)(t0 + tl) * out + r0 + lane] = red[tl * 65 + lane];
 }
 
 // -------------------------------------------------------------- dequantize
@@ -435,17 +445,13 @@ __global__ void __launch_bounds__(128) k_dense_u(DenseSegs d, int32_t r, int32_t
 
 }  // namespace
 
-int base_splits(int out, int in, int T) {
-  return T <= 256 ? (in / 32 + kSKSteps - 1) / kSKSteps : 0;
-}
-
-int launch_base(const uint16_t* W, const uint16_t* x, const uint16_t* xt, float* ybase, int out, int in, int T,
-                void* stream) {
+int launch_base(const uint16_t* W, const uint16_t* x, const uint16_t* xt, float* ybase, float* bpt, int out, int in,
+                int T, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int nks = base_splits(out, in, T);
+  const int nks = base_splits(in, T);
   if (nks > 0) {
     const dim3 g((unsigned)(out / 64), (unsigned)nks, (unsigned)((T + 63) / 64));
-    hipLaunchKernelGGL(k_base_sk, g, dim3(256), 0, st, W, xt, ybase, out, in, T, nks);
+    hipLaunchKernelGGL(k_base_sk, g, dim3(256), 0, st, W, xt, ybase, bpt, out, in, T, nks);
   } else {
     GemmOp op{};
     op.A = W;

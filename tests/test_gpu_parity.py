@@ -186,7 +186,9 @@ SEG_CASES = [(256, 256, 2, 8, 22, 4), (384, 256, 3, 37, 71, 1), (384, 256, 3, 37
              (256, 384, 2, 40, 100, 17), (128, 128, 0, 0, 5, 2), (128, 128, 1, 0, 0, 3),
              (512, 640, 4, 65, 129, 9),
              # 17 chunks of 128 3/2-bit ranks: more than one LDS window per output group
-             (2304, 2176, 2, 130, 2000, 6)]
+             (2304, 2176, 2, 130, 2000, 6),
+             # 20480 inputs: 10 V-side slices and 40 backbone K ranges, summed in batches
+             (256, 20480, 2, 8, 22, 3)]
 
 
 @pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: "x".join(map(str, c)))
@@ -238,7 +240,7 @@ def test_deterministic_and_base_only():
     d = c["delta"]
     _, a = run_decode(d, c["w"], c["x"])
     _, b = run_decode(d, c["w"], c["x"])
-    assert np.array_equal(a, b)                      # one K range at this width, no float atomics: bit-identical
+    assert np.array_equal(a, b)                      # fixed summation order: bit-identical
     z = d.subset(0, d.r, (d.n8, d.n3, d.n2))
     z.sigma[:] = 0
     y, _ = run_decode(z, c["w"], c["x"])
@@ -251,6 +253,44 @@ def test_deterministic_and_base_only():
     diff = np.abs(bits.view(np.uint16).astype(np.int64) - yb.astype(np.int64))
     assert diff.max() <= 1
 
+
+
+def test_decode_bit_reproducible():
+    """Sums over input slices (V x) and over K ranges (W x) are added in a
+    fixed order (two partials onto zero, or a fixed-order combine by the last
+    work item), so repeated calls give the same bits: C1 q, gate and down at
+    8 tokens (down: 86 input groups, six V slices and 22 K ranges), fused and
+    delta-only, with the workspace refilled with garbage between calls; and a
+    C2 down matrix over 50 tenants with the Zipf batch."""
+    t = torch()
+    for mi in (0, 4, 6):
+        note("reproducible c1", mi)
+        m = synth.make_c1_matrix(mi)
+        d = m["delta"]
+        view = upload(d.spec, d)
+        x = dev_u16(m["x"][:8])
+        w = dev_u16(m["w"])
+        ws = workspace(trs.DC_OP_DECODE, [d.spec], 8)
+        for wb in (w, None):
+            outs = []
+            for fill in (0x00, 0xFF, 0x5A):
+                ws.fill_(fill)
+                y = t.empty((8, d.out), dtype=t.int16, device="cuda")
+                trs.dc_apply_decode(view, wb, x, y, ws)
+                t.cuda.synchronize()
+                outs.append(y.cpu().numpy())
+            assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2]), (mi, wb is None)
+        check_factored(y_to_f64(y), None, m["x"][:8], d, "reproducible c1 %d delta" % mi)
+    note("reproducible c2 down")
+    ids = synth.c2_ids()
+    touched = sorted(set(ids.tolist()))
+    ds = {k: synth.make_c2_delta(0, 6, k) for k in touched}
+    up = {k: upload(ds[k].spec, ds[k]) for k in touched}
+    views = [up.get(k, up[touched[0]]) for k in range(synth.C2_TENANTS)]
+    w = synth.make_c2_base(0, 6)
+    x = synth.make_c2_x(0, 6)
+    outs = [_mt_run(views, w, x, ids)[1] for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
 @pytest.mark.parametrize("out,inn,T", [(384, 256, 257), (1152, 384, 700), (256, 640, 300), (1280, 128, 1030)])
