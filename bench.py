@@ -5,9 +5,10 @@ Workload (synthetic, seeded): Llama-2-7B decoder shapes, 32 layers x 7
 matrices (q,k,v,o 4096x4096; gate,up 11008x4096; down 4096x11008), one
 shared bf16 backbone, 50 distinct tenant deltas resident in HBM, each at the
 1/16 budget (8/3/2-bit rank groups 2/32/968 or 2/47/1414), 64 decode tokens
-routed to tenants by Zipf(1.1).  One step = one dc_apply_multitenant call per
-(layer, matrix): routing, activation staging, backbone product, V side,
-U side and the bf16 epilogue, all on the GPU.
+routed to tenants by Zipf(1.1).  One step = per layer four grouped calls
+(dc_apply_multitenant_group: q+k+v, o, gate+up, down): routing, activation
+staging, backbone product, V side, U side and the bf16 epilogue, all on the
+GPU.
 
 Prints one JSON line.  value = tokens/s of the fused step (backbone +
 delta).  The delta-only step (backbone product skipped) is timed too, as
@@ -483,58 +484,39 @@ def main():
     T = synth.C2_TOKENS
     log("resident deltas: %.2f GB, backbone %.2f GB, built in %.1f s" %
         (pool.numel() / 1e9, sum(w.numel() * 2 for row in W for w in row) / 1e9, time.time() - t0))
-    ws_bytes = max(trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, [sp] * synth.C2_TENANTS, T) for sp in specs)
-    # A decoder layer's matrices in dependency order: q, k, v read the same
-    # input and run side by side on three streams (default priority), then o;
-    # gate and up side by side, then down.  Each stream has its own workspace
-    # and outputs.
-    waves = [[0, 1, 2], [3], [4, 5], [6]]
-    nstr = max(len(w) for w in waves)
-    # non-default streams (a HIP graph is captured from streams[0]); all work of
-    # this script is issued with streams[0] current
-    streams = [torch.cuda.Stream() for _ in range(nstr)]
-    torch.cuda.set_stream(streams[0])
-    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(nstr)]
-    yss = [{sp[0]: torch.empty((T, sp[0]), dtype=torch.int16, device=dev) for sp in specs} for _ in range(nstr)]
-    ws, ys = wss[0], yss[0]
+    # A decoder layer's matrices in dependency order, as grouped calls: q, k
+    # and v read the same input (one call of three matrices), then o; gate
+    # and up read the same input (one call of two), then down.  All calls go
+    # to one non-default stream (default priority), from which one step is
+    # captured as a HIP graph.
+    groups = [[0, 1, 2], [3], [4, 5], [6]]
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    ws_bytes = max(trs.dc_group_workspace_bytes([[specs[m]] * synth.C2_TENANTS for m in g], len(g), T)
+                   for g in groups)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ys = [torch.empty((T, sp[0]), dtype=torch.int16, device=dev) for sp in specs]
 
-    def calls(fused):
-        """Sequential list of every call of a step, all on the launch stream."""
-        return [trs.MultitenantCall(views[l][m], W[l][m] if fused else None, X[l][m], ids, ys[specs[m][0]], ws)
-                for l in range(args.layers) for m in range(len(specs))]
+    def step_calls(fused):
+        """Every call of one step, in order: (group, call)."""
+        return [(g, trs.GroupCall([views[l][m] for m in g], [W[l][m] for m in g] if fused else None, X[l][g[0]],
+                                  ids, [ys[m] for m in g], ws, stream=stream.cuda_stream))
+                for l in range(args.layers) for g in groups]
 
     def layered_step(fused):
-        """The step as per-layer waves: returns run(marks=None), which enqueues
-        it; marks (one event argument per call, in plan order) makes every call
-        record HIP events on its own stream around one stage."""
-        plan = []
-        for l in range(args.layers):
-            for wv in waves:
-                entry = [(si, trs.MultitenantCall(views[l][m], W[l][m] if fused else None, X[l][m], ids,
-                                                  yss[si][specs[m][0]], wss[si], stream=streams[si].cuda_stream))
-                         for si, m in enumerate(wv)]
-                fork = torch.cuda.Event() if len(wv) > 1 else None
-                joins = [torch.cuda.Event() for _ in wv[1:]]
-                plan.append((entry, fork, joins))
+        """The step as a list of grouped calls: returns run(marks=None), which
+        enqueues it; marks (one event argument per call, in order) makes every
+        call record HIP events around one stage."""
+        plan = step_calls(fused)
 
         def run(marks=None):
-            main = streams[0]
-            i = 0
-            for entry, fork, joins in plan:
-                if fork is not None:
-                    fork.record(main)
-                    for si, _ in entry[1:]:
-                        streams[si].wait_event(fork)
-                for _, c in entry:
-                    if marks is None:
-                        c()
-                    else:
-                        c.timed_array(marks[i])
-                    i += 1
-                for (si, _), ev in zip(entry[1:], joins):
-                    ev.record(streams[si])
-                    main.wait_event(ev)
-        run.ncalls = sum(len(e) for e, _, _ in plan)
+            for i, (_, c) in enumerate(plan):
+                if marks is None:
+                    c()
+                else:
+                    c.timed_array(marks[i])
+        run.ncalls = len(plan)
+        run.groups = [g for g, _ in plan]
         return run
 
     # bytes per step: packed deltas of the touched tenants (algorithmic), backbone
@@ -556,10 +538,10 @@ def main():
     # Per-stage durations: one untimed pass of the fused step, calls in
     # sequence, HIP events between the stages of every call; picks the
     # dominant kernel (largest total time).
-    cl = calls(True)
+    cl = step_calls(True)
     evs = [[hip.event() for _ in range(len(trs.STAGES) + 1)] for _ in cl]
-    for c, ev in zip(cl, evs):
-        c.timed(ev)
+    for (_, c), ev in zip(cl, evs):
+        c.timed_array(trs.MultitenantCall.event_array(ev))
     torch.cuda.synchronize()
     stage_ms = {s: [] for s in trs.STAGES}
     for ev in evs:
@@ -576,7 +558,7 @@ def main():
     dom_i = trs.STAGES.index(dom)
 
     def outputs():
-        return [y.clone() for d in yss for y in d.values()]
+        return [y.clone() for y in ys]
 
     def same_bits(a, b):
         """Outputs of the replayed graph equal the eager step's bit for bit
@@ -589,14 +571,14 @@ def main():
     for mode in ("fused", "delta"):
         run = layered_step(mode == "fused")
         log("timing %s step: warmup %d, steps %d" % (mode, args.warmup, args.steps))
-        # (1) the timed steps: one step captured as a HIP graph (all 224 calls,
-        # their kernels and the stream fork/join), replayed K times
+        # (1) the timed steps: one step captured as a HIP graph (all 128 grouped calls and
+        # their kernels), replayed K times
         for _ in range(args.warmup):
             run()
         torch.cuda.synchronize()
         ref = outputs()
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=streams[0]):
+        with torch.cuda.graph(g, stream=stream):
             run()
         torch.cuda.synchronize()
         for _ in range(args.warmup):
@@ -642,14 +624,14 @@ def main():
         g = (inn if side == "v" else out) // 128
         return (8 * n8 + 3 * n3 + 2 * n2) * n // 8 + r * g * 4 + (4 * r if side == "v" else 0)
 
-    ncalls = len(cl)
+    # per launch = per grouped call: the sum over the group's matrices
+    gl = [g for g, _ in cl]
     per_launch = {
-        "vside": np.mean([len(touched) * side_bytes(specs[i % len(specs)], "v") + T * specs[i % len(specs)][1] * 2
-                          for i in range(ncalls)]),
-        "uside": np.mean([len(touched) * side_bytes(specs[i % len(specs)], "u") + T * specs[i % len(specs)][0] * 2
-                          for i in range(ncalls)]),
-        "base": np.mean([specs[i % len(specs)][0] * specs[i % len(specs)][1] * 2 + T * specs[i % len(specs)][1] * 2
-                         for i in range(ncalls)]),
+        "vside": np.mean([sum(len(touched) * side_bytes(specs[m], "v") for m in g) + T * specs[g[0]][1] * 2
+                          for g in gl]),
+        "uside": np.mean([sum(len(touched) * side_bytes(specs[m], "u") + T * specs[m][0] * 2 for m in g)
+                          for g in gl]),
+        "base": np.mean([sum(specs[m][0] * specs[m][1] * 2 for m in g) + T * specs[g[0]][1] * 2 for g in gl]),
     }
     # dom_live: the kernel's average duration per launch inside the
     # instrumented fused steps, measured with HIP events on each call's stream
@@ -678,7 +660,7 @@ def main():
                    "tokens": T, "step": "fused"},
         "packed_delta_GBps": round(delta_bytes / (ms * 1e-3) / 1e9, 1),
         "fused_total_GBps": round((delta_bytes + base_bytes) / (ms * 1e-3) / 1e9, 1),
-        "launch": "HIP graph replay of one captured step",
+        "launch": "HIP graph replay of one captured step: 128 grouped calls (q+k+v, o, gate+up, down per layer)",
         "step_ms_per_replay": step_stats,
         "eager_ms_per_step": {"fused": round(eager["fused"], 4), "delta": round(eager["delta"], 4)},
         "delta_only": {"ms_per_step": round(ms_d, 4), "tokens_per_s": round(T / (ms_d * 1e-3), 1),

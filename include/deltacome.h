@@ -103,6 +103,8 @@ enum {
 
 /* Most tenants one multi-tenant or prefill call can address. */
 #define DC_MAX_TENANTS 128
+/* Most matrices one grouped call (dc_apply_multitenant_group) can take. */
+#define DC_MAX_GROUP 4
 
 typedef struct dc_spec {
   int32_t out; /* rows of the matrix (output features), multiple of 128 */
@@ -291,6 +293,38 @@ dc_status dc_apply_multitenant(const dc_delta_view* views, int32_t n, const uint
                                int32_t T, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dc_apply_multitenant_group -- m matrices that read the same input with
+ * the same tenant routing (q, k and v of attention; gate and up of the MLP)
+ * in one call: the tokens are routed and x is staged once, and each kernel
+ * covers all m matrices in one launch.  [P1] application scenarios
+ * (multi-tenant serving); [P2] "Key results" (50 models on one GPU).
+ *   views       host array [m][n]: views[j*n + k] is tenant k's delta of
+ *               matrix j; every matrix has the same in; within a matrix
+ *               every tenant has the same out (out may differ between
+ *               matrices, e.g. grouped-query k and v)
+ *   m           1 .. DC_MAX_GROUP
+ *   W_base      host array [m] of device bf16 [out_j][in] pointers, or NULL
+ *               (every matrix delta only); a NULL entry makes that matrix
+ *               delta only
+ *   x, tenant_ids, T   as dc_apply_multitenant
+ *   y           host array [m] of device bf16 [T][out_j], fully overwritten
+ *   ws          ws_bytes >= dc_group_workspace_bytes(specs of views, m, n, T)
+ * Output j is bit-identical to dc_apply_multitenant on matrix j alone.
+ * Errors as dc_apply_multitenant; DC_ERR_SHAPE if the matrices' in differ,
+ * DC_ERR_UNSUPPORTED if m > DC_MAX_GROUP, DC_ERR_INVALID_ARG if outputs
+ * overlap each other or x.  The status word of invalid ids is at byte 0 of
+ * ws as for dc_apply_multitenant.
+ */
+dc_status dc_apply_multitenant_group(const dc_delta_view* views, int32_t m, int32_t n,
+                                     const uint16_t* const* W_base, const uint16_t* x,
+                                     const int32_t* tenant_ids, uint16_t* const* y, int32_t T,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace of dc_apply_multitenant_group: specs [m][n] as its views; 0 on
+ * invalid arguments. */
+size_t dc_group_workspace_bytes(const dc_spec* specs, int32_t m, int32_t n, int32_t T);
+
+/*
  * dc_apply_multitenant_timed -- dc_apply_multitenant that also records
  * caller-owned HIP events on `stream` between its kernels, so a caller can
  * time each stage (hipEventElapsedTime) without a profiler.
@@ -303,6 +337,12 @@ dc_status dc_apply_multitenant(const dc_delta_view* views, int32_t n, const uint
  */
 enum { DC_STAGE_ROUTE = 0, DC_STAGE_XPREP, DC_STAGE_BASE, DC_STAGE_VSIDE, DC_STAGE_USIDE,
        DC_STAGE_COUNT };
+/* dc_apply_multitenant_group with the same stage events (each stage covers
+ * the whole group). */
+dc_status dc_apply_multitenant_group_timed(const dc_delta_view* views, int32_t m, int32_t n,
+                                           const uint16_t* const* W_base, const uint16_t* x,
+                                           const int32_t* tenant_ids, uint16_t* const* y, int32_t T,
+                                           void* ws, size_t ws_bytes, void* stream, void* const* events);
 dc_status dc_apply_multitenant_timed(const dc_delta_view* views, int32_t n, const uint16_t* W_base,
                                      const uint16_t* x, const int32_t* tenant_ids, uint16_t* y,
                                      int32_t T, void* ws, size_t ws_bytes, void* stream,

@@ -25,6 +25,7 @@ DC_ERR_HIP = -6
 DC_ERR_UNSUPPORTED = -7
 DC_MAX_TENANTS = 128
 DC_SCRATCH_BYTES = 32 << 20
+DC_MAX_GROUP = 4
 DC_OP_DECODE, DC_OP_MULTITENANT, DC_OP_PREFILL = 0, 1, 2
 REGIONS = ("SIGMA", "VC8", "VC3", "VC2", "VS8", "VS3", "VS2",
            "UC8", "UC3", "UC2", "US8", "US3", "US2")
@@ -32,7 +33,8 @@ EXPORTS = ("dc_status_string", "dc_check_spec", "dc_packed_bytes", "dc_algorithm
            "dc_region", "dc_pack", "dc_pack_codes", "dc_unpack", "dc_workspace_bytes",
            "dc_apply_decode", "dc_apply_multitenant", "dc_apply_multitenant_timed",
            "dc_apply_prefill", "dc_dequant", "dc_pack_device", "dc_allocate_bits",
-           "dc_apply_multitenant_noalloc")
+           "dc_apply_multitenant_noalloc", "dc_apply_multitenant_group", "dc_group_workspace_bytes",
+           "dc_apply_multitenant_group_timed")
 STAGES = ("route", "xprep", "base", "vside", "uside")
 
 
@@ -85,12 +87,18 @@ def lib() -> ctypes.CDLL:
                                                  _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]
         L.dc_apply_prefill.argtypes = [vp, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.dc_apply_multitenant_noalloc.argtypes = [vp, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, _P]
+        L.dc_apply_multitenant_group.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P,
+                                                 ctypes.c_int32, _P, ctypes.c_size_t, _P]
+        L.dc_apply_multitenant_group_timed.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P,
+                                                       ctypes.c_int32, _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]
+        L.dc_group_workspace_bytes.restype = ctypes.c_size_t
+        L.dc_group_workspace_bytes.argtypes = [sp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         L.dc_dequant.argtypes = [vp, _P, _P, _P]
         L.dc_pack_device.argtypes = [sp, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
         L.dc_allocate_bits.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int64, _P, _P]
         for name in EXPORTS:
             if name not in ("dc_status_string", "dc_packed_bytes", "dc_algorithmic_bytes",
-                            "dc_workspace_bytes"):
+                            "dc_workspace_bytes", "dc_group_workspace_bytes"):
                 getattr(L, name).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -191,6 +199,14 @@ def dc_workspace_bytes(op: int, specs, T: int) -> int:
     return int(lib().dc_workspace_bytes(int(op), arr, len(specs), int(T)))
 
 
+def dc_group_workspace_bytes(specs, m: int, T: int) -> int:
+    """specs: [m][n] (a list of m lists of n specs, or m*n specs in order)."""
+    flat = [s for row in specs for s in row] if specs and isinstance(specs[0], (list, tuple)) and \
+        not isinstance(specs[0][0], int) else list(specs)
+    arr = (dc_spec * len(flat))(*[make_spec(s) for s in flat])
+    return int(lib().dc_group_workspace_bytes(arr, int(m), len(flat) // int(m), int(T)))
+
+
 # ----------------------------------------------------------------- device
 class DeltaView:
     """A packed delta resident in device memory (keeps its tensor alive)."""
@@ -244,6 +260,44 @@ def dc_apply_multitenant_noalloc(views: Sequence[DeltaView], W_base, x, tenant_i
     _check(lib().dc_apply_multitenant_noalloc(_views(views), len(views), _dptr(W_base, "W_base"), _dptr(x, "x"),
                                               _dptr(tenant_ids, "tenant_ids"), _dptr(y, "y"), int(T),
                                               _stream(stream)), "dc_apply_multitenant_noalloc")
+
+
+def _ptr_array(ts, what):
+    return (_P * len(ts))(*[_dptr(t, what) for t in ts])
+
+
+class GroupCall:
+    """dc_apply_multitenant_group with its arguments marshalled once.
+    views: [m][n] DeltaViews; W_base: list of m tensors (None entries: delta
+    only) or None; y: list of m output tensors."""
+
+    def __init__(self, views, W_base, x, tenant_ids, y, ws, T: int = None, stream=None):
+        m, n = len(views), len(views[0])
+        T = x.shape[0] if T is None else T
+        flat = [v for row in views for v in row]
+        self._keep = (flat, W_base, x, tenant_ids, y, ws)
+        self._arr = _views(flat)
+        self._w = _ptr_array(W_base, "W_base") if W_base is not None else None
+        self._y = _ptr_array(y, "y")
+        self.args = (self._arr, m, n, self._w, _dptr(x, "x"), _dptr(tenant_ids, "tenant_ids"), self._y, int(T),
+                     _dptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream))
+        self._fn = lib().dc_apply_multitenant_group
+        self._fn_t = lib().dc_apply_multitenant_group_timed
+
+    def __call__(self) -> None:
+        st = self._fn(*self.args)
+        if st != DC_OK:
+            raise DcError(st, "dc_apply_multitenant_group")
+
+    def timed_array(self, ev) -> None:
+        """ev: MultitenantCall.event_array(...) (stage events of the whole group)."""
+        st = self._fn_t(*self.args, ev)
+        if st != DC_OK:
+            raise DcError(st, "dc_apply_multitenant_group_timed")
+
+
+def dc_apply_multitenant_group(views, W_base, x, tenant_ids, y, ws, T: int = None, stream=None) -> None:
+    GroupCall(views, W_base, x, tenant_ids, y, ws, T, stream)()
 
 
 def dc_apply_multitenant_timed(views: Sequence[DeltaView], W_base, x, tenant_ids, y, ws, events,

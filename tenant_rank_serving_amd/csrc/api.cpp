@@ -14,7 +14,8 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x0 < y0 + nb && y0 < x0 + na;
 }
 
-// Checks the tenant specs of one call; fills the shape and the work-split maxima.
+// Checks the tenant specs of one matrix of a call; fills its shape and the
+// work-split maxima.
 struct Dims {
   int32_t out, in, rmax, tw, vb;
 };
@@ -38,76 +39,109 @@ dc_status check_specs(const dc_spec* specs, int32_t n, Dims* d) {
   return DC_OK;
 }
 
+// The specs of a group: specs [m][n]; every matrix with the same in.
+dc_status check_group(const dc_spec* specs, int32_t m, int32_t n, Dims* d) {
+  if (!specs || m < 1 || n < 1) return DC_ERR_INVALID_ARG;
+  if (m > DC_MAX_GROUP || n > DC_MAX_TENANTS) return DC_ERR_UNSUPPORTED;
+  for (int j = 0; j < m; ++j) {
+    const dc_status st = check_specs(specs + (size_t)j * n, n, &d[j]);
+    if (st != DC_OK) return st;
+    if (d[j].in != d[0].in) return DC_ERR_SHAPE;
+  }
+  return DC_OK;
+}
+
+bool layout_of_group(const Dims* d, int32_t m, int32_t n, int32_t T, int32_t drp, dc::WsLayout* wl) {
+  int32_t out[DC_MAX_GROUP], rs[DC_MAX_GROUP], vb[DC_MAX_GROUP];
+  for (int j = 0; j < m; ++j) {
+    out[j] = d[j].out;
+    rs[j] = d[j].tw;
+    vb[j] = d[j].vb;
+  }
+  return dc::ws_layout(T, d[0].in, n, m, out, rs, vb, drp, wl);
+}
+
 }  // namespace
 
 namespace dc {
-dc_status run_apply(const dc_delta_view* views, int32_t n, const uint16_t* W, const uint16_t* x,
-                    const int32_t* ids, const int32_t* seg, int32_t mode, uint16_t* y, int32_t T, void* ws,
+dc_status run_apply(const dc_delta_view* views, int32_t m, int32_t n, const uint16_t* const* W, const uint16_t* x,
+                    const int32_t* ids, const int32_t* seg, int32_t mode, uint16_t* const* y, int32_t T, void* ws,
                     size_t ws_bytes, void* stream, void* const* events, size_t ws_limit) {
-  if (!views || n < 1) return DC_ERR_INVALID_ARG;
-  if (n > DC_MAX_TENANTS) return DC_ERR_UNSUPPORTED;
+  if (!views || n < 1 || m < 1 || !y) return DC_ERR_INVALID_ARG;
+  if (n > DC_MAX_TENANTS || m > DC_MAX_GROUP) return DC_ERR_UNSUPPORTED;
   if (T < 0) return DC_ERR_INVALID_ARG;
-  dc_spec specs[DC_MAX_TENANTS] = {};
-  for (int k = 0; k < n; ++k) specs[k] = views[k].spec;
-  Dims dm;
-  dc_status st = check_specs(specs, n, &dm);
+  dc_spec specs[DC_MAX_GROUP * DC_MAX_TENANTS];
+  for (int i = 0; i < m * n; ++i) specs[i] = views[i].spec;
+  Dims dm[DC_MAX_GROUP];
+  dc_status st = check_group(specs, m, n, dm);
   if (st != DC_OK) return st;
-  const int32_t out = dm.out, in = dm.in, rmax = dm.rmax;
-  dc::TenantTable table;
-  std::memset(&table, 0, sizeof(table));
-  for (int k = 0; k < n; ++k) {
-    const int32_t r = specs[k].n8 + specs[k].n3 + specs[k].n2;
-    if (r > 0 && !views[k].base) return DC_ERR_INVALID_ARG;
-    if (!aligned(views[k].base, 16)) return DC_ERR_ALIGN;
-    table.t[k].base = static_cast<const uint8_t*>(views[k].base);
-    table.t[k].n8 = specs[k].n8;
-    table.t[k].n3 = specs[k].n3;
-    table.t[k].n2 = specs[k].n2;
+  const int32_t in = dm[0].in;
+  dc::TenantTable tables[DC_MAX_GROUP];
+  for (int j = 0; j < m; ++j) {
+    std::memset(&tables[j], 0, sizeof(tables[j]));
+    for (int k = 0; k < n; ++k) {
+      const dc_delta_view& v = views[(size_t)j * n + k];
+      const int32_t r = v.spec.n8 + v.spec.n3 + v.spec.n2;
+      if (r > 0 && !v.base) return DC_ERR_INVALID_ARG;
+      if (!aligned(v.base, 16)) return DC_ERR_ALIGN;
+      tables[j].t[k].base = static_cast<const uint8_t*>(v.base);
+      tables[j].t[k].n8 = v.spec.n8;
+      tables[j].t[k].n3 = v.spec.n3;
+      tables[j].t[k].n2 = v.spec.n2;
+    }
   }
-  if (!x || !y || (!ws && ws_limit == 0)) return DC_ERR_INVALID_ARG;
+  if (!x || (!ws && ws_limit == 0)) return DC_ERR_INVALID_ARG;
   if (mode == 1 && !ids) return DC_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(y, 16) || (W && !aligned(W, 16)) || !aligned(ws, 256) ||
-      (ids && !aligned(ids, 4)))
-    return DC_ERR_ALIGN;
-  if (overlap(x, (size_t)T * in * 2, y, (size_t)T * out * 2)) return DC_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(ws, 256) || (ids && !aligned(ids, 4))) return DC_ERR_ALIGN;
+  for (int j = 0; j < m; ++j) {
+    if (!y[j]) return DC_ERR_INVALID_ARG;
+    if (!aligned(y[j], 16) || (W && W[j] && !aligned(W[j], 16))) return DC_ERR_ALIGN;
+    if (overlap(x, (size_t)T * in * 2, y[j], (size_t)T * dm[j].out * 2)) return DC_ERR_INVALID_ARG;
+    for (int i = 0; i < j; ++i)
+      if (overlap(y[i], (size_t)T * dm[i].out * 2, y[j], (size_t)T * dm[j].out * 2)) return DC_ERR_INVALID_ARG;
+  }
   dc::WsLayout wl{};
-  dc::ws_layout(T, in, out, dm.tw, n, true, dm.vb, 0, &wl);
+  if (!layout_of_group(dm, m, n, T, 0, &wl)) return DC_ERR_INVALID_ARG;
   if (ws_limit > 0) {   // the library's own scratch array: its size is the limit, its address comes later
     if (wl.total > ws_limit) return DC_ERR_UNSUPPORTED;
     ws_bytes = ws_limit;
   } else if (ws_bytes < wl.total) {
     return DC_ERR_BUFFER;
   }
-  if (mode == 2 && T >= dc::kDenseMin) {
+  if (mode == 2 && m == 1 && T >= dc::kDenseMin) {
     // the dense prefill operands, when the workspace holds them; without them
     // the call takes the decode kernels
     dc::WsLayout wd{};
-    dc::ws_layout(T, in, out, dm.tw, n, true, dm.vb, dc::dense_rank_pad(rmax), &wd);
+    layout_of_group(dm, 1, n, T, dc::dense_rank_pad(dm[0].rmax), &wd);
     if (ws_bytes >= wd.total) wl = wd;
   }
-  // the kernels address t, the backbone partials and each packed buffer with 32-bit byte offsets
+  // the kernels address t, the backbone product and each packed buffer with 32-bit byte offsets
   const size_t lim = (size_t)INT32_MAX;
-  if ((size_t)T * wl.rs * 4 > lim || (size_t)T * out * 4 > lim) return DC_ERR_UNSUPPORTED;
-  for (int k = 0; k < n; ++k)
-    if (dc_packed_bytes(&specs[k]) > lim) return DC_ERR_UNSUPPORTED;
+  for (int j = 0; j < m; ++j)
+    if ((size_t)T * wl.mat[j].rs * 4 > lim || (size_t)T * dm[j].out * 4 > lim) return DC_ERR_UNSUPPORTED;
+  for (int i = 0; i < m * n; ++i)
+    if (dc_packed_bytes(&specs[i]) > lim) return DC_ERR_UNSUPPORTED;
   if (T == 0) return DC_OK;
   if (ws_limit > 0) {
     ws = scratch_ptr();
     if (!ws) return DC_ERR_HIP;
   }
-  dc::ApplyArgs a;
-  a.tenants = &table;
+  dc::ApplyArgs a{};
+  a.m = m;
+  for (int j = 0; j < m; ++j) {
+    a.mat[j].tenants = &tables[j];
+    a.mat[j].out = dm[j].out;
+    a.mat[j].rmax = dm[j].rmax;
+    a.mat[j].W = W ? W[j] : nullptr;
+    a.mat[j].y = y[j];
+  }
   a.n = n;
-  a.out = out;
   a.in = in;
-  a.rmax = rmax;
   a.T = T;
-  a.W = W;
   a.x = x;
   a.ids = ids;
   a.seg = seg;
   a.mode = mode;
-  a.y = y;
   a.ws = static_cast<uint8_t*>(ws);
   a.wl = wl;
   a.stream = stream;
@@ -120,7 +154,7 @@ namespace {
 dc_status run(const dc_delta_view* views, int32_t n, const uint16_t* W, const uint16_t* x, const int32_t* ids,
               const int32_t* seg, int32_t mode, uint16_t* y, int32_t T, void* ws, size_t ws_bytes, void* stream,
               void* const* events = nullptr) {
-  return dc::run_apply(views, n, W, x, ids, seg, mode, y, T, ws, ws_bytes, stream, events, 0);
+  return dc::run_apply(views, 1, n, &W, x, ids, seg, mode, &y, T, ws, ws_bytes, stream, events, 0);
 }
 }  // namespace
 
@@ -132,8 +166,18 @@ size_t dc_workspace_bytes(int32_t op, const dc_spec* specs, int32_t n, int32_t T
   Dims dm;
   if (check_specs(specs, n, &dm) != DC_OK) return 0;
   dc::WsLayout wl{};
-  dc::ws_layout(T, dm.in, dm.out, dm.tw, n, true, dm.vb,
-                 op == DC_OP_PREFILL && T >= dc::kDenseMin ? dc::dense_rank_pad(dm.rmax) : 0, &wl);
+  if (!layout_of_group(&dm, 1, n, T, op == DC_OP_PREFILL && T >= dc::kDenseMin ? dc::dense_rank_pad(dm.rmax) : 0,
+                       &wl))
+    return 0;
+  return wl.total;
+}
+
+size_t dc_group_workspace_bytes(const dc_spec* specs, int32_t m, int32_t n, int32_t T) {
+  if (T < 0) return 0;
+  Dims dm[DC_MAX_GROUP];
+  if (check_group(specs, m, n, dm) != DC_OK) return 0;
+  dc::WsLayout wl{};
+  if (!layout_of_group(dm, m, n, T, 0, &wl)) return 0;
   return wl.total;
 }
 
@@ -147,6 +191,19 @@ dc_status dc_apply_multitenant(const dc_delta_view* views, int32_t n, const uint
                                const uint16_t* x, const int32_t* tenant_ids, uint16_t* y,
                                int32_t T, void* ws, size_t ws_bytes, void* stream) {
   return run(views, n, W_base, x, tenant_ids, nullptr, 1, y, T, ws, ws_bytes, stream);
+}
+
+dc_status dc_apply_multitenant_group(const dc_delta_view* views, int32_t m, int32_t n, const uint16_t* const* W_base,
+                                     const uint16_t* x, const int32_t* tenant_ids, uint16_t* const* y, int32_t T,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  return dc::run_apply(views, m, n, W_base, x, tenant_ids, nullptr, 1, y, T, ws, ws_bytes, stream, nullptr, 0);
+}
+
+dc_status dc_apply_multitenant_group_timed(const dc_delta_view* views, int32_t m, int32_t n,
+                                           const uint16_t* const* W_base, const uint16_t* x,
+                                           const int32_t* tenant_ids, uint16_t* const* y, int32_t T, void* ws,
+                                           size_t ws_bytes, void* stream, void* const* events) {
+  return dc::run_apply(views, m, n, W_base, x, tenant_ids, nullptr, 1, y, T, ws, ws_bytes, stream, events, 0);
 }
 
 dc_status dc_apply_multitenant_timed(const dc_delta_view* views, int32_t n, const uint16_t* W_base,

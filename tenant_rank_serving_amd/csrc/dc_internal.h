@@ -177,73 +177,104 @@ DC_HD inline int t_base(int n8, int n3, int which) {
 }
 DC_HD inline int t_width(int n8, int n3, int n2) { return t_base(n8, n3, 2) + (int)round_up((size_t)n2, 8); }
 
-// Workspace layout of one apply call.
-struct WsLayout {
-  size_t flags;   // uint32 status word (+ padding to 256 B)
-  size_t offs;    // int32 [n+2] bucket starts in sorted order (bucket n = backbone only)
-  size_t perm;    // int32 [T] sorted position -> token index
-  size_t act;     // ActEntry [nact] work items of the buckets with tokens, in bucket order
-  size_t xf;      // uint8 [T][in/128][256] fp8 hi/lo fragments of x (matrix-core A operand)
-  size_t xsc;     // uint32 [T][in/128] E8M0 block scales of the hi fragments
-  size_t xsum;    // fp32 [T][in/128] sums of x over each 128-group
-  size_t xt;      // bf16 x in matrix-core B tiles: [in/32][ceil(T/16)][64 lanes][8]
-  size_t ybase;   // fp32 [T][out] backbone product, original order
-  size_t vpart;   // fp32 [T][rs] t = sigma * (V x), sorted order
-  size_t vpt;     // fp32 [ns][T][rs] per-slice partials of t when ns >= 3 (added in slice order)
-  size_t bpt;     // fp32 [nks][T][out] per-range partials of W x when nks >= 3 (added in range order)
-  size_t cnt;     // uint32 arrival counters of the V rank blocks [nact][vb]
-  size_t dav;     // prefill, dense form: dnb slots of bf16 [drp][2 in] V operand (hi, lo)
-  size_t dau;     // dnb slots of bf16 [out][3 drp] U operand (hi, hi, lo)
-  size_t dtb;     // bf16 [T][3 drp] t of one segment (hi, lo, hi)
-  size_t total;
-  int32_t drp;    // rank rows of the dense operands (0: no dense region)
-  int32_t dnb;    // operand slots: tenants whose dense products share one launch
-  int32_t rs;     // row stride of vpart (max t_width over tenants)
-  int32_t vb;     // max V-side rank blocks per tenant
-  int32_t ns;     // V-side input slices
-  int32_t nks;    // K ranges of the split backbone product (0: tiled product)
-  int32_t nact;   // work-item capacity of act
-  int32_t ncnt;   // counters in cnt
-  int32_t nvcnt;  // of which V-side counters
-};
-
 // Sums of more than two partials are added in a fixed order by the work item
 // that arrives last; two partials (or one) are added onto zero with float
 // atomics, which is order-independent for two terms.
 constexpr int kMaxAtomicTerms = 2;
 
-// rs: max t_width over tenants; vbmax: max v_blocks over tenants.
-// drp: rank rows of the dense prefill operands (0 for decode calls).
-inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rs, int32_t n, bool with_base, int32_t vbmax,
-                      int32_t drp, WsLayout* W) {
-  if (T < 0 || n < 0) return false;
-  W->vb = vbmax;
+// Matrices of one grouped call (they read the same x and tenant ids).
+constexpr int kMaxGroup = DC_MAX_GROUP;
+
+// Per-matrix parameters of a call, written into the workspace by the prep
+// kernel: the V-side and U-side kernels select their matrix with one uniform
+// load instead of indexing their kernel arguments.
+struct MatParams {
+  float* tv;           // t [T][rs]
+  float* vpt;          // V-side slice partials [ns][T][rs]
+  uint32_t* vcnt;      // V-side arrival counters [nact][vb]
+  const float* ybase;  // W x [T][out], null: delta only
+  uint16_t* y;         // output [T][out]
+  int32_t out, rs, vb, pad_;
+};
+static_assert(sizeof(MatParams) == 56, "one scalar load per kernel");
+
+// The part of a call's workspace that belongs to one matrix of the group.
+struct WsMat {
+  size_t ybase;   // fp32 [T][out] backbone product, original order
+  size_t vpart;   // fp32 [T][rs] t = sigma * (V x), sorted order
+  size_t vpt;     // fp32 [ns][T][rs] per-slice partials of t when ns > 2 (added in slice order)
+  size_t bpt;     // fp32 [nks][T][out] per-range partials of W x when nks > 2 (added in range order)
+  size_t cnt;     // uint32 arrival counters of the V rank blocks [nact][vb] when ns > 2
+  int32_t out;    // rows of the matrix
+  int32_t rs;     // row stride of vpart (max t_width over tenants)
+  int32_t vb;     // max V-side rank blocks per tenant
+  int32_t ncnt;   // counters in cnt
+};
+
+// Workspace layout of one apply call: the routing and the staged x shared by
+// the group's matrices, then each matrix's part, then the dense prefill
+// operands (single-matrix prefill calls only).
+struct WsLayout {
+  size_t flags;   // uint32 status word (+ padding to 256 B)
+  size_t offs;    // int32 [n+2] bucket starts in sorted order (bucket n = backbone only)
+  size_t perm;    // int32 [T] sorted position -> token index
+  size_t xf;      // uint8 [T][in/128][256] fp8 hi/lo fragments of x (matrix-core A operand)
+  size_t xsc;     // uint32 [T][in/128] E8M0 block scales of the hi fragments
+  size_t xsum;    // fp32 [T][in/128] sums of x over each 128-group
+  size_t xt;      // bf16 x in matrix-core B tiles: [in/32][ceil(T/16)][64 lanes][8]
+  size_t act;     // ActEntry [m][nact] work items of the buckets with tokens, in bucket order, per matrix
+  size_t params;  // MatParams [m]
+  WsMat mat[kMaxGroup];
+  size_t dav;     // prefill, dense form: dnb slots of bf16 [drp][2 in] V operand (hi, lo)
+  size_t dau;     // dnb slots of bf16 [out][3 drp] U operand (hi, hi, lo)
+  size_t dtb;     // bf16 [T][3 drp] t of one segment (hi, lo, hi)
+  size_t total;
+  int32_t m;      // matrices of the group
+  int32_t drp;    // rank rows of the dense operands (0: no dense region)
+  int32_t dnb;    // operand slots: tenants whose dense products share one launch
+  int32_t ns;     // V-side input slices
+  int32_t nks;    // K ranges of the split backbone product (0: tiled product)
+  int32_t nact;   // work-item capacity of each act list
+};
+
+// Per matrix j of the group: out[j], rs[j] (max t_width over its tenants),
+// vb[j] (max v_blocks over its tenants).  drp: rank rows of the dense prefill
+// operands (0 for decode calls; m must be 1 otherwise).
+inline bool ws_layout(int32_t T, int32_t in, int32_t n, int32_t m, const int32_t* out, const int32_t* rs,
+                      const int32_t* vb, int32_t drp, WsLayout* W) {
+  if (T < 0 || n < 0 || m < 1 || m > kMaxGroup || (drp > 0 && m != 1)) return false;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = round_up(o, kAlign); o = at + bytes; return at; };
-  W->rs = rs > 0 ? rs : 8;
+  W->m = m;
   W->flags = take(256);
   W->offs = take(4 * ((size_t)n + 2));
   W->perm = take(4 * (size_t)T);
   W->nact = act_capacity(n, T);
-  W->act = take(sizeof(ActEntry) * (size_t)W->nact);
   const size_t items = (size_t)T * (in / kGroup);
   W->xf = take(256 * items);
   W->xsc = take(4 * items);
   W->xsum = take(4 * items);
-  W->xt = take(with_base ? 2 * (size_t)in * round_up((size_t)T, 16) : 0);
-  W->ybase = take(with_base ? 4 * (size_t)T * out : 0);
-  W->vpart = take(4 * (size_t)T * W->rs);
+  W->xt = take(2 * (size_t)in * round_up((size_t)T, 16));
   W->ns = v_slices(in);
-  W->nks = with_base ? base_splits(in, T) : 0;
-  W->vpt = take(W->ns > kMaxAtomicTerms ? 4 * (size_t)W->ns * T * W->rs : 0);
-  W->bpt = take(W->nks > kMaxAtomicTerms ? 4 * (size_t)W->nks * T * out : 0);
-  W->nvcnt = W->ns > kMaxAtomicTerms ? W->nact * vbmax : 0;
-  W->ncnt = W->nvcnt;
-  W->cnt = take(4 * (size_t)W->ncnt);
+  W->nks = base_splits(in, T);
+  W->act = take(sizeof(ActEntry) * (size_t)m * W->nact);
+  W->params = take(sizeof(MatParams) * kMaxGroup);
+  for (int j = 0; j < m; ++j) {
+    WsMat& M = W->mat[j];
+    M.out = out[j];
+    M.rs = rs[j] > 0 ? rs[j] : 8;
+    M.vb = vb[j];
+    M.ybase = take(4 * (size_t)T * M.out);
+    M.vpart = take(4 * (size_t)T * M.rs);
+    M.vpt = take(W->ns > kMaxAtomicTerms ? 4 * (size_t)W->ns * T * M.rs : 0);
+    M.bpt = take(W->nks > kMaxAtomicTerms ? 4 * (size_t)W->nks * T * M.out : 0);
+    M.ncnt = W->ns > kMaxAtomicTerms ? W->nact * M.vb : 0;
+    M.cnt = take(4 * (size_t)M.ncnt);
+  }
   W->drp = drp;
   W->dnb = drp > 0 ? (n < 8 ? n : 8) : 0;
   W->dav = take(2 * (size_t)W->dnb * drp * 2 * in);
-  W->dau = take(2 * (size_t)W->dnb * out * 3 * drp);
+  W->dau = take(2 * (size_t)W->dnb * out[0] * 3 * drp);
   W->dtb = take(2 * (size_t)T * 3 * drp);
   W->total = round_up(o, kAlign);
   return true;
@@ -254,18 +285,25 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t out, int32_t rs, int32_t n,
 // Kernel launchers (defined in the .hip files).  All enqueue on `stream`
 // and return a hipError_t as int.
 namespace dc {
-struct ApplyArgs {
+// One matrix of a call: its tenants, shape, backbone and output.
+struct MatArgs {
   const TenantTable* tenants;  // host pointer: copied into kernel arguments
-  int32_t n;
-  int32_t out, in;
+  int32_t out;
   int32_t rmax;
-  int32_t T;
   const uint16_t* W;           // may be null
+  uint16_t* y;
+};
+
+struct ApplyArgs {
+  int32_t m;                   // matrices (1 except grouped calls)
+  MatArgs mat[kMaxGroup];
+  int32_t n;
+  int32_t in;
+  int32_t T;
   const uint16_t* x;
   const int32_t* ids;          // device, mode 1
   const int32_t* seg;          // host, mode 2 ([n+1])
   int32_t mode;                // 0 decode (all tokens tenant 0), 1 ids, 2 segments
-  uint16_t* y;
   uint8_t* ws;
   WsLayout wl;
   void* stream;
@@ -277,8 +315,16 @@ int launch_apply(const ApplyArgs& a);
 // zeroed before it runs (the ranges add into it); with more, the ranges store
 // partials into bpt [nks][T][out], which the V-side kernel adds in range order
 // into ybase.  T > 256: the tiled product.
-int launch_base(const uint16_t* W, const uint16_t* x, const uint16_t* xt, float* ybase, float* bpt, int out, int in,
-                int T, void* stream);
+// One matrix of a backbone launch.
+struct BaseMat {
+  const uint16_t* W;
+  float* ybase;
+  float* bpt;
+  int32_t out;
+  int32_t rb0;   // first 64-row block of this matrix in the launch
+};
+// The tiled product (T > 256) covers one matrix (m == 1).
+int launch_base(const BaseMat* mats, int m, const uint16_t* x, const uint16_t* xt, int in, int T, void* stream);
 // Rank rows of the dense prefill operands of a tenant with r pairs (r rounded
 // up to whole 128-row tiles, at least one tile).
 int dense_rank_pad(int r);
@@ -289,8 +335,9 @@ int launch_dequant(const Tenant& t, int32_t out, int32_t in, uint16_t* u16, uint
 // The checks and launches of every apply entry point.  ws_limit > 0: the
 // workspace is the library's scratch array of that many bytes (ws and
 // ws_bytes are ignored); it is looked up only once the checks pass.
-dc_status run_apply(const dc_delta_view* views, int32_t n, const uint16_t* W, const uint16_t* x,
-                    const int32_t* ids, const int32_t* seg, int32_t mode, uint16_t* y, int32_t T, void* ws,
+// views [m][n], W [m] (entries may be null), y [m].
+dc_status run_apply(const dc_delta_view* views, int32_t m, int32_t n, const uint16_t* const* W, const uint16_t* x,
+                    const int32_t* ids, const int32_t* seg, int32_t mode, uint16_t* const* y, int32_t T, void* ws,
                     size_t ws_bytes, void* stream, void* const* events, size_t ws_limit);
 // Device address of the scratch array on the current device (null if it
 // cannot be found); defined next to the array.

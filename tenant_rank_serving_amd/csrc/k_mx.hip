@@ -88,6 +88,7 @@ __device__ __forceinline__ void list_active(const Tenant& mine, int32_t n, const
     if (w < wave) pos += wsum[w];
     total += wsum[w];
   }
+  lds_barrier();   // wsum is read: a next call may write it
   for (int j = 0; j < items; ++j) {
     ActEntry e;
     e.base = b < n ? mine.base : nullptr;
@@ -106,32 +107,55 @@ __device__ __forceinline__ void list_active(const Tenant& mine, int32_t n, const
   }
 }
 
-__global__ void __launch_bounds__(256) k_prep(TenantTable tt, const uint16_t* __restrict__ x,
+template <int M>
+struct GroupTables {
+  TenantTable t[M];
+};
+
+// Per matrix of the group: its work-item list and what prep clears.
+struct PrepMats {
+  MatParams params[kMaxGroup];
+  MatParams* mp;              // where they go in the workspace
+  ActEntry* act[kMaxGroup];
+  float* tv[kMaxGroup];       // t, when its slices add up atomically
+  int32_t ntv[kMaxGroup];
+  float* yb[kMaxGroup];       // W x, when its two K ranges add up atomically
+  int32_t nyb[kMaxGroup];
+  uint32_t* cnt[kMaxGroup];   // arrival counters of the fixed-order sums
+  int32_t ncnt[kMaxGroup];
+};
+
+template <int M>
+__global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t* __restrict__ x,
                                               const int32_t* __restrict__ ids,
                                               int32_t T, int32_t in, int32_t n, int32_t mode, SegArg seg,
                                               int32_t* __restrict__ offs, int32_t* __restrict__ perm,
-                                              ActEntry* __restrict__ act,
                                               uint32_t* __restrict__ flags, uint8_t* __restrict__ xf,
                                               uint32_t* __restrict__ xsc, float* __restrict__ xsum,
-                                              uint16_t* __restrict__ xt, float* __restrict__ tv, int32_t ntv,
-                                              float* __restrict__ yb, int32_t nyb, uint32_t* __restrict__ cnt,
-                                              int32_t ncnt, int32_t cap) {
+                                              uint16_t* __restrict__ xt, PrepMats pm, int32_t cap) {
   const int tid = threadIdx.x;
-  // t and W x when their parts add up atomically, and the arrival counters of
-  // the fixed-order sums: zeroed by the blocks after the first (the first
-  // block's barriers would wait for its stores to finish)
+  // zeroed by the blocks after the first (the first block's barriers would
+  // wait for its stores to finish)
   if (blockIdx.x > 0) {
-    for (int i = (blockIdx.x - 1) * 256 + tid; i < ntv; i += (gridDim.x - 1) * 256) tv[i] = 0.f;
-    for (int i = (blockIdx.x - 1) * 256 + tid; i < nyb; i += (gridDim.x - 1) * 256) yb[i] = 0.f;
-    for (int i = (blockIdx.x - 1) * 256 + tid; i < ncnt; i += (gridDim.x - 1) * 256) cnt[i] = 0u;
+    const int i0 = (blockIdx.x - 1) * 256 + tid, di = (gridDim.x - 1) * 256;
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      for (int i = i0; i < pm.ntv[j]; i += di) pm.tv[j][i] = 0.f;
+      for (int i = i0; i < pm.nyb[j]; i += di) pm.yb[j][i] = 0.f;
+      for (int i = i0; i < pm.ncnt[j]; i += di) pm.cnt[j][i] = 0u;
+    }
   }
   if (blockIdx.x == 0) {
     static_assert(DC_MAX_TENANTS + 1 <= 256, "one thread per bucket");
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+      if (tid == j) pm.mp[j] = pm.params[j];
     __shared__ int so[DC_MAX_TENANTS + 2];   // bucket starts
-    // thread b's tenant record, read first: the kernel arguments live in
+    // thread b's tenant records, read first: the kernel arguments live in
     // memory and the indexing is per thread
-    Tenant mine{};
-    if (tid < n) mine = tt.t[tid];
+    Tenant mine[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) mine[j] = tid < n ? gt.t[j].t[tid] : Tenant{};
     if (mode != 1) {
       for (int p = tid; p < T; p += blockDim.x) perm[p] = p;
       if (tid == 0) {
@@ -141,7 +165,8 @@ __global__ void __launch_bounds__(256) k_prep(TenantTable tt, const uint16_t* __
         *flags = 0;
       }
       lds_barrier();
-      list_active(mine, n, so, cap, act);
+#pragma unroll
+      for (int j = 0; j < M; ++j) list_active(mine[j], n, so, cap, pm.act[j]);
       return;
     }
     __shared__ int cnt[DC_MAX_TENANTS + 1];   // tokens per bucket
@@ -185,7 +210,8 @@ __global__ void __launch_bounds__(256) k_prep(TenantTable tt, const uint16_t* __
       if (tid == 0) *flags = bad ? 1u : 0u;
     }
     lds_barrier();
-    list_active(mine, n, so, cap, act);
+#pragma unroll
+    for (int j = 0; j < M; ++j) list_active(mine[j], n, so, cap, pm.act[j]);
     for (int c0 = 0; c0 < T; c0 += blockDim.x) {
       const int t = c0 + tid;
       int b = -1;
@@ -342,9 +368,8 @@ struct BaseSum {
   const float* bpt;   // [nks][T][out]
   float* ybase;       // [T][out]
   int32_t nks, out, T;
-  int32_t nblk;       // reduce blocks: out/64 x ceil(T/8)
-  int32_t rows;       // leading grid rows they take
 };
+
 
 __device__ void base_sum(const BaseSum& bs, int idx) {
   const int ntb = (bs.T + 7) / 8;
@@ -667,18 +692,36 @@ __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, con
   }
 }
 
-__global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t out, int32_t in,
-                                               const uint16_t* __restrict__ x, const ActEntry* __restrict__ act,
+// The V-side launch of a group of matrices: leading grid rows add the
+// backbone partials of matrices whose W x has more than two K ranges, then
+// one row of blocks per (matrix, work item).
+struct VGroup {
+  const ActEntry* act;           // [m][nact] work items
+  const MatParams* mp;           // [m] per-matrix parameters (workspace)
+  BaseSum bs[kMaxGroup];
+  int32_t red0[kMaxGroup + 1];   // first partial-sum block of each matrix (prefix over the group)
+  int32_t red_rows;              // grid rows of partial-sum blocks
+  int32_t nact;                  // work items per matrix
+  int32_t ns, T;                 // V-side input slices, tokens
+};
+
+__global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t in, const uint16_t* __restrict__ x,
                                                const int32_t* __restrict__ perm, const uint8_t* __restrict__ xf,
                                                const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
-                                               VOut vo, BaseSum bs) {
-  if ((int)blockIdx.y < bs.rows) {   // the backbone product's partial sums
+                                               VGroup g) {
+  if ((int)blockIdx.y < g.red_rows) {   // the backbone product's partial sums
     const int idx = blockIdx.y * gridDim.x + blockIdx.x;
-    if (idx < bs.nblk) base_sum(bs, idx);
+#pragma unroll
+    for (int j = 0; j < kMaxGroup; ++j)
+      if (idx >= g.red0[j] && idx < g.red0[j + 1]) base_sum(g.bs[j], idx - g.red0[j]);
     return;
   }
-  const int item = blockIdx.y - bs.rows;
-  const ActEntry e = act[item];         // the item-th work item
+  const int yy = blockIdx.y - g.red_rows;
+  const int mj = yy / g.nact, item = yy % g.nact;
+  const MatParams P = g.mp[mj];
+  const ActEntry e = g.act[yy];   // the item-th work item of matrix mj
+  const VOut vo{P.tv, P.vpt, P.vcnt, P.rs, g.ns, g.T, P.vb};
+  const int out = P.out;
   const int p0 = e.p0, p1 = e.p1;
   if (p0 >= p1 || e.k >= n) return;     // empty entry, or the backbone-only bucket
   Tenant tn;
@@ -748,16 +791,28 @@ struct ULds {
   float cz[kUWaves][kURows];         // per-wave partial sums of z t' per token row
 };
 
-__global__ void __launch_bounds__(kUWaves * 64) k_uside(int32_t n, int32_t out, int32_t in,
-                                                        const ActEntry* __restrict__ act,
-                                                        const int32_t* __restrict__ perm,
-                                                        const float* __restrict__ tv, int32_t rs, int32_t T,
-                                                        const float* __restrict__ ybase,
-                                                        uint16_t* __restrict__ y) {
+// The U-side launch of a group of matrices: one row of blocks per (matrix,
+// work item), blocks past a matrix's output groups return at once.
+struct UGroup {
+  const ActEntry* act;   // [m][nact] work items
+  const MatParams* mp;   // [m] per-matrix parameters (workspace)
+  int32_t nact;
+};
+
+__global__ void __launch_bounds__(kUWaves * 64) k_uside(int32_t n, int32_t in, const int32_t* __restrict__ perm,
+                                                        int32_t T, UGroup ug) {
   const int g = blockIdx.x;
+  const int mj = blockIdx.y / ug.nact;
+  const MatParams P = ug.mp[mj];
+  const ActEntry e = ug.act[blockIdx.y];   // the work items of the group's matrices, one after another
+  const int out = P.out;
+  if (g * kGroup >= out) return;
+  const int rs = P.rs;
+  const float* __restrict__ tv = P.tv;
+  const float* __restrict__ ybase = P.ybase;
+  uint16_t* __restrict__ y = P.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, q = lane >> 4;
-  const ActEntry e = act[blockIdx.y];   // the blockIdx.y-th bucket with tokens
   const int p0 = e.p0, p1 = e.p1;
   if (p0 >= p1) return;
   if (e.k == n) {  // backbone-only tokens
@@ -1008,20 +1063,54 @@ int launch_apply(const ApplyArgs& a) {
     if (dense) return launch_dense_prefill(a);
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  const int m = a.m;
   uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + a.wl.flags);
   int32_t* offs = reinterpret_cast<int32_t*>(a.ws + a.wl.offs);
   int32_t* perm = reinterpret_cast<int32_t*>(a.ws + a.wl.perm);
-  ActEntry* act = reinterpret_cast<ActEntry*>(a.ws + a.wl.act);
-  float* tv = reinterpret_cast<float*>(a.ws + a.wl.vpart);
-  float* ybase = a.W ? reinterpret_cast<float*>(a.ws + a.wl.ybase) : nullptr;
   const size_t items = (size_t)a.T * (a.in / kGroup);
   uint8_t* xf = a.ws + a.wl.xf;
   uint32_t* xsc = reinterpret_cast<uint32_t*>(a.ws + a.wl.xsc);
   float* xsum = reinterpret_cast<float*>(a.ws + a.wl.xsum);
+  bool any_w = false;
+  for (int j = 0; j < m; ++j) any_w = any_w || a.mat[j].W;
   // the B tiles of x feed the split-K backbone product only
-  uint16_t* xt = a.W && a.wl.nks > 0 ? reinterpret_cast<uint16_t*>(a.ws + a.wl.xt) : nullptr;
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(a.ws + a.wl.cnt);
-  float* bpt = reinterpret_cast<float*>(a.ws + a.wl.bpt);
+  uint16_t* xt = any_w && a.wl.nks > 0 ? reinterpret_cast<uint16_t*>(a.ws + a.wl.xt) : nullptr;
+  auto wsp = [&](size_t off) { return a.ws + off; };
+  PrepMats pm{};
+  VGroup vg{};
+  UGroup ug{};
+  ActEntry* act_all = reinterpret_cast<ActEntry*>(wsp(a.wl.act));
+  MatParams* mp = reinterpret_cast<MatParams*>(wsp(a.wl.params));
+  pm.mp = mp;
+  BaseMat bm[kMaxGroup];
+  int nbm = 0, rb = 0, red = 0, vbmax = 0, outmax = 0;
+  for (int j = 0; j < m; ++j) {
+    const WsMat& M = a.wl.mat[j];
+    const MatArgs& A = a.mat[j];
+    ActEntry* act = act_all + (size_t)j * a.wl.nact;
+    float* tv = reinterpret_cast<float*>(wsp(M.vpart));
+    float* ybase = A.W ? reinterpret_cast<float*>(wsp(M.ybase)) : nullptr;
+    float* bpt = reinterpret_cast<float*>(wsp(M.bpt));
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(wsp(M.cnt));
+    // t is zeroed when its slices add up atomically, W x when its two K ranges do
+    pm.act[j] = act;
+    pm.tv[j] = tv;
+    pm.ntv[j] = a.wl.ns <= kMaxAtomicTerms ? a.T * M.rs : 0;
+    pm.yb[j] = ybase;
+    pm.nyb[j] = A.W && a.wl.nks == kMaxAtomicTerms ? a.T * A.out : 0;
+    pm.cnt[j] = cnt;
+    pm.ncnt[j] = M.ncnt;
+    if (A.W) bm[nbm++] = BaseMat{A.W, ybase, bpt, A.out, rb}, rb += A.out / 64;
+    pm.params[j] = MatParams{tv, reinterpret_cast<float*>(wsp(M.vpt)), cnt, ybase, A.y, A.out, M.rs, M.vb, 0};
+    vg.red0[j] = red;
+    if (A.W && a.wl.nks > kMaxAtomicTerms) {
+      vg.bs[j] = BaseSum{bpt, ybase, a.wl.nks, A.out, a.T};
+      red += (A.out / 64) * ((a.T + 7) / 8);
+    }
+    vbmax = max(vbmax, M.vb);
+    outmax = max(outmax, A.out);
+  }
+  for (int j = m; j <= kMaxGroup; ++j) vg.red0[j] = red;
   SegArg seg{};
   if (a.mode == 2)
     for (int k = 0; k <= a.n; ++k) seg.v[k] = a.seg[k];
@@ -1030,42 +1119,41 @@ int launch_apply(const ApplyArgs& a) {
   };
   mark(DC_STAGE_ROUTE);
   mark(DC_STAGE_XPREP);
-  // t is zeroed when its slices add up atomically, W x when its two K ranges do
-  const int ntv = a.wl.ns <= kMaxAtomicTerms ? a.T * a.wl.rs : 0;
-  const int nyb = a.W && a.wl.nks == kMaxAtomicTerms ? a.T * a.out : 0;
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)(1 + (items + 3) / 4)), dim3(256), 0, st, *a.tenants, a.x, a.ids, a.T,
-                     a.in, a.n, a.mode, seg, offs, perm, act, flags, xf, xsc, xsum, xt, tv, ntv, ybase, nyb, cnt,
-                     a.wl.ncnt, a.wl.nact);
-  mark(DC_STAGE_BASE);
-  if (a.W) launch_base(a.W, a.x, xt, ybase, bpt, a.out, a.in, a.T, a.stream);
-  mark(DC_STAGE_VSIDE);
-  BaseSum bs{};
-  const int gx = a.wl.vb > 0 ? a.wl.vb * a.wl.ns : 1;
-  if (a.W && a.wl.nks > kMaxAtomicTerms) {
-    bs.bpt = bpt;
-    bs.ybase = ybase;
-    bs.nks = a.wl.nks;
-    bs.out = a.out;
-    bs.T = a.T;
-    bs.nblk = (a.out / 64) * ((a.T + 7) / 8);
-    bs.rows = (bs.nblk + gx - 1) / gx;
+  const dim3 gp((unsigned)(1 + (items + 3) / 4)), bp(256);
+#define DC_PREP(M_)                                                                                             \
+  {                                                                                                             \
+    GroupTables<M_> gt;                                                                                         \
+    for (int j = 0; j < M_; ++j) gt.t[j] = *a.mat[j].tenants;                                                  \
+    hipLaunchKernelGGL(k_prep<M_>, gp, bp, 0, st, gt, a.x, a.ids, a.T, a.in, a.n, a.mode, seg, offs, perm,       \
+                       flags, xf, xsc, xsum, xt, pm, a.wl.nact);                                                \
   }
-  if (a.wl.vb > 0 || bs.rows > 0) {
-    VOut vo;
-    vo.tv = tv;
-    vo.vpt = reinterpret_cast<float*>(a.ws + a.wl.vpt);
-    vo.vcnt = cnt;
-    vo.rs = a.wl.rs;
-    vo.ns = a.wl.ns;
-    vo.T = a.T;
-    vo.vb = a.wl.vb;
-    const unsigned gy = (unsigned)(bs.rows + (a.wl.vb > 0 ? a.wl.nact : 0));
-    hipLaunchKernelGGL(k_vside, dim3((unsigned)gx, gy), dim3(256), 0, st, a.n, a.out, a.in, a.x, act, perm, xf, xsc,
-                       xsum, vo, bs);
+  switch (m) {
+    case 1: DC_PREP(1) break;
+    case 2: DC_PREP(2) break;
+    case 3: DC_PREP(3) break;
+    default: DC_PREP(4) break;
+  }
+#undef DC_PREP
+  mark(DC_STAGE_BASE);
+  if (nbm > 0) launch_base(bm, nbm, a.x, xt, a.in, a.T, a.stream);
+  mark(DC_STAGE_VSIDE);
+  const int gx = vbmax > 0 ? vbmax * a.wl.ns : 1;
+  vg.red_rows = (red + gx - 1) / gx;
+  vg.nact = a.wl.nact;
+  vg.act = act_all;
+  vg.mp = mp;
+  vg.ns = a.wl.ns;
+  vg.T = a.T;
+  if (vbmax > 0 || red > 0) {
+    const unsigned gy = (unsigned)(vg.red_rows + (vbmax > 0 ? m * a.wl.nact : 0));
+    hipLaunchKernelGGL(k_vside, dim3((unsigned)gx, gy), dim3(256), 0, st, a.n, a.in, a.x, perm, xf, xsc, xsum, vg);
   }
   mark(DC_STAGE_USIDE);
-  hipLaunchKernelGGL(k_uside, dim3((unsigned)(a.out / kGroup), (unsigned)a.wl.nact), dim3(kUWaves * 64), 0, st,
-                     a.n, a.out, a.in, act, perm, tv, a.wl.rs, a.T, ybase, a.y);
+  ug.nact = a.wl.nact;
+  ug.act = act_all;
+  ug.mp = mp;
+  hipLaunchKernelGGL(k_uside, dim3((unsigned)(outmax / kGroup), (unsigned)(m * a.wl.nact)), dim3(kUWaves * 64), 0,
+                     st, a.n, a.in, perm, a.T, ug);
   mark(DC_STAGE_COUNT);
   return (int)hipGetLastError();
 }

@@ -264,12 +264,28 @@ __device__ __forceinline__ void lds_barrier() {   // orders LDS only: W loads st
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__global__ void __launch_bounds__(256) k_base_sk(const uint16_t* __restrict__ W, const uint16_t* __restrict__ xt,
-                                                 float* __restrict__ ybase, float* __restrict__ bpt,
-                                                 int32_t out, int32_t in, int32_t T, int32_t nks) {
+// The matrices of one launch (a group of matrices that read the same x):
+// row block blockIdx.x belongs to the last matrix whose first row block is
+// at or before it.
+struct BaseMats {
+  BaseMat m[kMaxGroup];
+  int32_t nm;
+};
+
+__global__ void __launch_bounds__(256) k_base_sk(BaseMats bms, const uint16_t* __restrict__ xt, int32_t in,
+                                                 int32_t T, int32_t nks) {
+  int mj = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxGroup; ++j)
+    if (j < bms.nm && (int)blockIdx.x >= bms.m[j].rb0) mj = j;
+  const BaseMat bm = mj == 0 ? bms.m[0] : (mj == 1 ? bms.m[1] : (mj == 2 ? bms.m[2] : bms.m[3]));
+  const uint16_t* __restrict__ W = bm.W;
+  float* __restrict__ ybase = bm.ybase;
+  float* __restrict__ bpt = bm.bpt;
+  const int out = bm.out;
   __shared__ __attribute__((aligned(16))) uint4 xs[kSKSteps][4][64];   // [step][token tile][lane] B tiles
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r0 = blockIdx.x * 64;
+  const int r0 = (blockIdx.x - bm.rb0) * 64;
   const int t0 = blockIdx.z * 64;
   const int tiles = (T + 15) / 16;
   const int nall = in / 32;
@@ -445,14 +461,23 @@ __global__ void __launch_bounds__(128) k_dense_u(DenseSegs d, int32_t r, int32_t
 
 }  // namespace
 
-int launch_base(const uint16_t* W, const uint16_t* x, const uint16_t* xt, float* ybase, float* bpt, int out, int in,
-                int T, void* stream) {
+int launch_base(const BaseMat* mats, int m, const uint16_t* x, const uint16_t* xt, int in, int T, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int nks = base_splits(in, T);
   if (nks > 0) {
-    const dim3 g((unsigned)(out / 64), (unsigned)nks, (unsigned)((T + 63) / 64));
-    hipLaunchKernelGGL(k_base_sk, g, dim3(256), 0, st, W, xt, ybase, bpt, out, in, T, nks);
+    BaseMats bms{};
+    int rows = 0;
+    for (int j = 0; j < m; ++j) {
+      bms.m[j] = mats[j];
+      rows = mats[j].rb0 + mats[j].out / 64;
+    }
+    bms.nm = m;
+    const dim3 g((unsigned)rows, (unsigned)nks, (unsigned)((T + 63) / 64));
+    hipLaunchKernelGGL(k_base_sk, g, dim3(256), 0, st, bms, xt, in, T, nks);
   } else {
+    const uint16_t* W = mats[0].W;
+    float* ybase = mats[0].ybase;
+    const int out = mats[0].out;
     GemmOp op{};
     op.A = W;
     op.B = x;
@@ -474,25 +499,26 @@ int dense_rank_pad(int r) { return r > 0 ? (int)round_up((size_t)r, kGT) : kGT; 
 
 int launch_dense_prefill(const ApplyArgs& a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-  float* ybase = a.W ? reinterpret_cast<float*>(a.ws + a.wl.ybase) : nullptr;
+  const MatArgs& A = a.mat[0];   // a prefill call has one matrix
+  float* ybase = A.W ? reinterpret_cast<float*>(a.ws + a.wl.mat[0].ybase) : nullptr;
   uint16_t* av0 = reinterpret_cast<uint16_t*>(a.ws + a.wl.dav);
   uint16_t* au0 = reinterpret_cast<uint16_t*>(a.ws + a.wl.dau);
   uint16_t* tb0 = reinterpret_cast<uint16_t*>(a.ws + a.wl.dtb);
-  const size_t av_slot = (size_t)a.wl.drp * 2 * a.in, au_slot = (size_t)a.out * 3 * a.wl.drp;
+  const size_t av_slot = (size_t)a.wl.drp * 2 * a.in, au_slot = (size_t)A.out * 3 * a.wl.drp;
   uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + a.wl.flags);
-  if (a.W) {
+  if (A.W) {
     GemmBatch gb{};
     GemmOp& op = gb.op[0];
-    op.A = a.W;
+    op.A = A.W;
     op.B = a.x;
-    op.M = a.out;
+    op.M = A.out;
     op.N = a.T;
     op.K = a.in;
     op.ldb = a.in;
     op.kb = a.in;
-    op.ldc = a.out;
+    op.ldc = A.out;
     op.c32 = ybase;
-    hipLaunchKernelGGL(k_gemm<0>, dim3(gemm_tiles(a.out, a.T)), dim3(256), 0, st, gb);
+    hipLaunchKernelGGL(k_gemm<0>, dim3(gemm_tiles(A.out, a.T)), dim3(256), 0, st, gb);
   }
   // tenants with tokens, in batches of up to a.wl.dnb (<= kGBatch) operand slots
   int k = 0;
@@ -503,19 +529,19 @@ int launch_dense_prefill(const ApplyArgs& a) {
     for (; k < a.n && cnt < a.wl.dnb; ++k) {
       const int s0 = a.seg[k], nt = a.seg[k + 1] - a.seg[k];
       if (nt == 0) continue;
-      const Tenant& tn = a.tenants->t[k];
+      const Tenant& tn = A.tenants->t[k];
       const int r = tn.n8 + tn.n3 + tn.n2, rp = dense_rank_pad(r);
       uint16_t* av = av0 + cnt * av_slot;
       uint16_t* au = au0 + cnt * au_slot;
       uint16_t* tb = tb0 + (size_t)s0 * 3 * a.wl.drp;   // segments are disjoint token ranges
       Layout L;
-      layout_of(a.out, a.in, tn.n8, tn.n3, tn.n2, &L);
+      layout_of(A.out, a.in, tn.n8, tn.n3, tn.n2, &L);
       DenseSegs ds;
       for (int w = 0; w < 3; ++w) ds.s[w] = seg_info(tn, L, w);
       hipLaunchKernelGGL(k_dense_v, dim3((unsigned)((a.in + 511) / 512), (unsigned)rp), dim3(256), 0, st, ds, r, a.in,
                          av, flags);
       flags = nullptr;   // cleared by the first launch
-      hipLaunchKernelGGL(k_dense_u, dim3((unsigned)(rp / 128), (unsigned)(a.out / kDenseURows)), dim3(128), 0, st, ds,
+      hipLaunchKernelGGL(k_dense_u, dim3((unsigned)(rp / 128), (unsigned)(A.out / kDenseURows)), dim3(128), 0, st, ds,
                          r, rp, a.in, au);
       GemmOp& v = gv.op[cnt];   // t = sigma (V x) for the segment's tokens
       v.A = av;
@@ -532,16 +558,16 @@ int launch_dense_prefill(const ApplyArgs& a) {
       GemmOp& u = gu.op[cnt];   // y = W x + U t, rounded once
       u.A = au;
       u.B = tb;
-      u.M = a.out;
+      u.M = A.out;
       u.N = nt;
       u.K = 3 * rp;
       u.ldb = 3 * rp;
       u.kb = 3 * rp;
-      u.ldc = a.out;
-      u.ybase = ybase ? ybase + (size_t)s0 * a.out : nullptr;
-      u.y = a.y + (size_t)s0 * a.out;
+      u.ldc = A.out;
+      u.ybase = ybase ? ybase + (size_t)s0 * A.out : nullptr;
+      u.y = A.y + (size_t)s0 * A.out;
       tv = max(tv, gemm_tiles(rp, nt));
-      tu = max(tu, gemm_tiles(a.out, nt));
+      tu = max(tu, gemm_tiles(A.out, nt));
       ++cnt;
     }
     if (cnt == 0) break;

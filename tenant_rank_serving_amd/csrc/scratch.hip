@@ -45,6 +45,6 @@ void* scratch_ptr() {
 extern "C" dc_status dc_apply_multitenant_noalloc(const dc_delta_view* views, int32_t n, const uint16_t* W_base,
                                                   const uint16_t* x, const int32_t* tenant_ids, uint16_t* y,
                                                   int32_t T, void* stream) {
-  return dc::run_apply(views, n, W_base, x, tenant_ids, nullptr, 1, y, T, nullptr, 0, stream, nullptr,
+  return dc::run_apply(views, 1, n, &W_base, x, tenant_ids, nullptr, 1, &y, T, nullptr, 0, stream, nullptr,
                        dc::kScratchBytes);
 }

@@ -423,6 +423,53 @@ def test_multitenant_many_tokens():
     check_multitenant(y2, w, x, np.where(bad >= len(specs), -1, bad), ds, 128, "mt 700 bad id")
 
 
+GROUP_CASES = [
+    # (outs, in, shapes per tenant, n, T, backbone per matrix)
+    ((512, 128, 256), 384, [(2, 8, 22), (1, 3, 40), (0, 9, 0), (2, 0, 17), (3, 20, 30)], 5, 40, (True, False, True)),
+    # 48 input groups: three V slices (fixed-order combine) and 12 K ranges (partial-sum blocks of two matrices)
+    ((256, 384), 6144, [(2, 8, 22), (1, 30, 100), (0, 0, 0)], 3, 24, (True, True)),
+    # four matrices of DC_MAX_TENANTS tenants: 12 KB of tenant records in one launch's arguments
+    ((128, 256, 128, 384), 256, [(2, 8, 22), (0, 0, 0), (1, 12, 3), (0, 3, 40)], 128, 200, (True, True, False, True)),
+]
+
+
+@pytest.mark.parametrize("case", GROUP_CASES, ids=lambda c: "m%d_in%d_n%d_T%d" % (len(c[0]), c[1], c[3], c[4]))
+def test_group_matches_single_calls(case):
+    """dc_apply_multitenant_group over m matrices (different outs, like
+    grouped-query k and v; some delta only) against dc_apply_multitenant on
+    each matrix alone, bit for bit, and against the oracle; one invalid id
+    sets the status word."""
+    outs, inn, shapes, n, T, with_w = case
+    note("group", outs, inn, n, T)
+    t = torch()
+    rng = np.random.default_rng(1000 + inn + n)
+    m = len(outs)
+    ds = [[synth.small_delta(2000 + 131 * j + k, outs[j], inn, *shapes[k % len(shapes)]) for k in range(n)]
+          for j in range(m)]
+    views = [[upload(d.spec, d) for d in row] for row in ds]
+    ws_np = [synth.base_weight(rng, o, inn) for o in outs]
+    x = synth.activations(rng, T, inn)
+    ids = rng.integers(-1, n, size=T).astype(np.int32)
+    ids[T // 2] = n + 3   # invalid: backbone only, flagged
+    xd, idd = dev_u16(x), dev_i32(ids)
+    wd = [dev_u16(w) if use else None for w, use in zip(ws_np, with_w)]
+    ys = [t.full((T, o), 0x7FC0, dtype=t.int16, device="cuda") for o in outs]
+    specs = [[d.spec for d in row] for row in ds]
+    ws = t.empty(trs.dc_group_workspace_bytes(specs, m, T), dtype=t.uint8, device="cuda")
+    trs.dc_apply_multitenant_group(views, wd, xd, idd, ys, ws)
+    t.cuda.synchronize()
+    assert int(ws[:4].cpu().numpy().view(np.uint32)[0]) == 1
+    ids_ok = np.where(ids >= n, -1, ids)
+    for j in range(m):
+        y1 = t.empty((T, outs[j]), dtype=t.int16, device="cuda")
+        trs.dc_apply_multitenant([v for v in views[j]], wd[j], xd, idd, y1,
+                                 workspace(trs.DC_OP_MULTITENANT, specs[j], T))
+        t.cuda.synchronize()
+        assert t.equal(ys[j], y1), "matrix %d differs from its single call" % j
+        check_multitenant(y_to_f64(ys[j]), ws_np[j] if with_w[j] else None, x, ids_ok, ds[j], outs[j],
+                          "group m=%d matrix %d %s" % (m, j, "fused" if with_w[j] else "delta"))
+
+
 def test_multitenant_invalid_ids_flag():
     note("multitenant invalid ids")
     rng = np.random.default_rng(9)

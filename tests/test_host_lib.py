@@ -337,3 +337,32 @@ def test_allocate_bits_argument_checks(L):
     assert f(3000, 2, P(cost), P(np.ones((3000, 2))), 1 << 20, P(np.zeros(3000, np.int32)), None) == \
         trs.DC_ERR_UNSUPPORTED                                                  # 3000 x 2^20 choice bytes
     assert f(0, 2, P(cost), None, 0, None, None) == trs.DC_OK                  # no pairs
+
+
+def test_group_workspace_and_argument_checks(L):
+    """dc_group_workspace_bytes of one matrix is the multi-tenant size; a
+    group holds each matrix's part once and the shared routing and staged x
+    once; the group call rejects bad groups before any launch."""
+    sq, sk = (512, 384, 2, 8, 22), (128, 384, 1, 3, 9)
+    for T in (1, 40, 300):
+        one = trs.dc_group_workspace_bytes([[sq] * 3], 1, T)
+        assert one == trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, [sq] * 3, T)
+        two = trs.dc_group_workspace_bytes([[sq] * 3, [sk] * 3], 2, T)
+        k_alone = trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, [sk] * 3, T)
+        assert max(one, k_alone) < two < one + k_alone
+    assert trs.dc_group_workspace_bytes([[sq] * 3, [(128, 256, 1, 3, 9)] * 3], 2, 8) == 0   # different in
+    flat = (trs._lib.dc_spec * 10)(*[trs.make_spec(sq)] * 10)
+    assert L.dc_group_workspace_bytes(flat, 0, 2, 8) == 0
+    assert L.dc_group_workspace_bytes(flat, 5, 2, 8) == 0
+    need = trs.dc_group_workspace_bytes([[sq] * 2, [sk] * 2], 2, 8)
+    arr = (trs._lib.dc_delta_view * 4)(_view(sq), _view(sq), _view(sk), _view(sk))
+    P = ctypes.c_void_p
+    W2 = (P * 2)(WB, None)
+    grp = L.dc_apply_multitenant_group
+    assert grp(arr, 2, 2, W2, X, IDS, (P * 2)(Y, Y + 0x100000), 8, WS, need - 1, None) == trs.DC_ERR_BUFFER
+    assert grp(arr, 2, 2, W2, X, IDS, (P * 2)(Y, Y + 64), 8, WS, need, None) == trs.DC_ERR_INVALID_ARG  # y overlap
+    assert grp(arr, 2, 2, W2, X, IDS, (P * 2)(Y, None), 8, WS, need, None) == trs.DC_ERR_INVALID_ARG
+    assert grp(arr, 5, 2, W2, X, IDS, (P * 2)(Y, Y + 0x100000), 8, WS, need, None) == trs.DC_ERR_UNSUPPORTED
+    assert grp(arr, 2, 2, W2, X, IDS, (P * 2)(Y, Y + 0x100000), 0, WS, need, None) == trs.DC_OK    # T = 0
+    bad = (trs._lib.dc_delta_view * 4)(_view(sq), _view(sq), _view((128, 256, 1, 3, 9)), _view((128, 256, 1, 3, 9)))
+    assert grp(bad, 2, 2, W2, X, IDS, (P * 2)(Y, Y + 0x100000), 8, WS, need, None) == trs.DC_ERR_SHAPE
