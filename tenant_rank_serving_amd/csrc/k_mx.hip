@@ -799,7 +799,7 @@ struct UGroup {
   int32_t nact;
 };
 
-__global__ void __launch_bounds__(kUWaves * 64) k_uside(int32_t n, int32_t in, const int32_t* __restrict__ perm,
+__global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) k_uside(int32_t n, int32_t in, const int32_t* __restrict__ perm,
                                                         int32_t T, UGroup ug) {
   const int g = blockIdx.x;
   const int mj = blockIdx.y / ug.nact;
@@ -892,6 +892,13 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(int32_t n, int32_t in, c
     const int wcap = kUWin / nops;     // chunks per window (a multiple of kUDepth)
     uint32_t cr[kUDepth][3];
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // the epilogue's inputs, in flight during the pass: lane group q writes
+    // tokens 2q and 2q + 1 of the pass (their original indices, then W x and
+    // t of the 8-bit pairs)
+    int tko[2];
+    float ybo[2] = {0.f, 0.f}, t8o[2][kU8Max];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) tko[h] = perm[pb + min(2 * q + h, nt - 1)];
     // A operands of chunks [cw0, cw0 + wc) for the pass's token rows.  Thread
     // tid takes chunk pcl of the window and rows 4h..4h+3: with one op per
     // chunk the 512 threads cover 16 chunks x rows 0-3, with two 8 chunks x
@@ -999,6 +1006,13 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(int32_t n, int32_t in, c
     __syncthreads();   // the previous pass's operands and sums are consumed
     if (lane < kURows) S.cz[wave][lane] = 0.f;   // this wave's z t' sums of the pass
     if (nc == 0 && pb == p0) load_u8w();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // every pass, also one with no 3/2-bit chunks
+      const int rw = min(2 * q + h, nt - 1);
+      if (ybase) ybo[h] = ybase[(size_t)tko[h] * out + orow];
+#pragma unroll
+      for (int i = 0; i < kU8Max; ++i) t8o[h][i] = i < s8.n ? tv[(size_t)(pb + rw) * rs + i] : 0.f;
+    }
     for (int cw0 = 0; cw0 < nc; cw0 += wcap) {
       const int wc = min(wcap, nc - cw0);
       if (cw0 > 0) __syncthreads();   // the previous window's operands are consumed
@@ -1025,27 +1039,24 @@ __global__ void __launch_bounds__(kUWaves * 64) k_uside(int32_t n, int32_t in, c
       }
     }
     __syncthreads();
-    if (q < 2) {   // lane group q writes the tokens of op q
-      const f32x4 tq = q == 0 ? tot[0] : tot[1];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rw = 4 * q + r;
-        if (rw < nt) {
-          const int tk = perm[pb + rw];
-          float cz = 0.f;
+    for (int h = 0; h < 2; ++h) {   // lane group q writes tokens 2q and 2q + 1
+      const int rw = 2 * q + h;
+      if (rw < nt) {
+        const f32x4 tq = rw < 4 ? tot[0] : tot[1];
+        const int r = rw & 3;
+        float v = r == 0 ? tq[0] : (r == 1 ? tq[1] : (r == 2 ? tq[2] : tq[3]));
 #pragma unroll
-          for (int w8 = 0; w8 < kUWaves; ++w8) cz += S.cz[w8][rw];
-          float v = tq[r] - cz;
+        for (int w8 = 0; w8 < kUWaves; ++w8) v -= S.cz[w8][rw];
 #pragma unroll
-          for (int i = 0; i < kU8Max; ++i)
-            if (i < s8.n) v += u8w[i] * tv[(size_t)(pb + rw) * rs + i];
-          for (int i = kU8Max; i < s8.n; ++i) {   // more 8-bit pairs than kept in registers
-            const uint32_t e = s8.us[(size_t)g * round_up(s8.n, 4) + i];
-            const float uh = (float)(_Float16)(f16f(e & 0xFFFFu) * ((float)s8.uc[(size_t)orow * s8.n + i] - f16f(e >> 16)));
-            v += uh * tv[(size_t)(pb + rw) * rs + i];
-          }
-          y[(size_t)tk * out + orow] = to_bf16(v + (ybase ? ybase[(size_t)tk * out + orow] : 0.f));
+        for (int i = 0; i < kU8Max; ++i)
+          if (i < s8.n) v += u8w[i] * t8o[h][i];
+        for (int i = kU8Max; i < s8.n; ++i) {   // more 8-bit pairs than kept in registers
+          const uint32_t e = s8.us[(size_t)g * round_up(s8.n, 4) + i];
+          const float uh = (float)(_Float16)(f16f(e & 0xFFFFu) * ((float)s8.uc[(size_t)orow * s8.n + i] - f16f(e >> 16)));
+          v += uh * tv[(size_t)(pb + rw) * rs + i];
         }
+        y[(size_t)tko[h] * out + orow] = to_bf16(v + ybo[h]);
       }
     }
   }
