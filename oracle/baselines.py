@@ -25,8 +25,13 @@ Neither baseline's arithmetic is printed on the pages; the readings [R]:
     (+1 / -1).
 
 Storage layouts (this library's, restated by include/deltacome.h):
-  Low-rank buffer: SIGMA fp32 [r], V fp16 [r][in] (row i = v_i), U fp16
-    [r][out] (row i = u_i), each region at a multiple of 256 bytes.
+  Low-rank buffer: SIGMA fp32 [r], then V and U as fp16 in 16-row tiles of
+    32-element steps, each region at a multiple of 256 bytes:
+      V [ceil(r/16)][in/32][64][8]: v_i[k] sits in tile i/16, step k/32,
+        slot (i % 16) + 16 ((k % 32) / 8), element k % 8;
+      U [out/16][ceil(r/32)][64][8]: u_i[o] sits in tile o/16, step i/32,
+        slot (o % 16) + 16 ((i % 32) / 8), element i % 8;
+    ranks from r up to the tile edge hold zeros.
   BitDelta buffer: SCALE fp32 (one word, region padded to 256 bytes), then
     the sign bits in 16-row tiles, [out/16][in/128][4][16] words: word
     (T, g, c, i) holds the 32 entries of row 16T + i, columns
@@ -69,20 +74,35 @@ def lowrank_compress(u, sigma, v, r: int):
 def lowrank_regions(out: int, inn: int, r: int):
     """name -> (byte offset, byte size), and the total size."""
     res, off = {}, 0
-    for name, size in (("SIGMA", 4 * r), ("V", 2 * r * inn), ("U", 2 * r * out)):
+    for name, size in (("SIGMA", 4 * r), ("V", 2 * _pad(r, 16) * inn), ("U", 2 * out * _pad(r, 32))):
         off = _pad(off, ALIGN)
         res[name] = (off, size)
         off += size
     return res, _pad(off, ALIGN)
 
 
+def _tile(m, rows_pad: int, cols: int):
+    """[rows][cols] -> [rows/16][cols/32][64][8] with slot (row % 16) + 16 ((col % 32) / 8)."""
+    a = np.zeros((rows_pad, cols), m.dtype)
+    a[:m.shape[0]] = m
+    return a.reshape(rows_pad // 16, 16, cols // 32, 4, 8).transpose(0, 2, 3, 1, 4)
+
+
+def _untile(t, rows: int, cols: int):
+    return t.transpose(0, 3, 1, 2, 4).reshape(-1, cols)[:rows]
+
+
 def lowrank_pack(U16, sigma, V16) -> np.ndarray:
-    r, out = np.asarray(U16).shape
-    inn = np.asarray(V16).shape[1]
+    """U16 fp16 [r][out] (row i = u_i), sigma [r], V16 fp16 [r][in] (row i = v_i)."""
+    U16, V16 = np.asarray(U16, np.float16), np.asarray(V16, np.float16)
+    r, out = U16.shape
+    inn = V16.shape[1]
     reg, total = lowrank_regions(out, inn, r)
     buf = np.zeros(total, np.uint8)
-    for name, arr in (("SIGMA", np.asarray(sigma, np.float32)), ("V", np.asarray(V16, np.float16)),
-                      ("U", np.asarray(U16, np.float16))):
+    ut = np.zeros((out, _pad(r, 32)), np.float16)
+    ut[:, :r] = U16.T
+    for name, arr in (("SIGMA", np.asarray(sigma, np.float32)), ("V", _tile(V16, _pad(r, 16), inn)),
+                      ("U", _tile(ut, out, _pad(r, 32)))):
         o, n = reg[name]
         buf[o:o + n] = np.ascontiguousarray(arr).view(np.uint8).ravel()
     return buf
@@ -94,10 +114,10 @@ def lowrank_unpack(buf, out: int, inn: int, r: int):
     o, n = reg["SIGMA"]
     sg = b[o:o + n].view(np.float32).copy()
     o, n = reg["V"]
-    V = b[o:o + n].view(np.float16).reshape(r, inn).copy()
+    V = _untile(b[o:o + n].view(np.float16).reshape(_pad(r, 16) // 16, inn // 32, 4, 16, 8), r, inn).copy()
     o, n = reg["U"]
-    U = b[o:o + n].view(np.float16).reshape(r, out).copy()
-    return U, sg, V
+    ut = _untile(b[o:o + n].view(np.float16).reshape(out // 16, _pad(r, 32) // 32, 4, 16, 8), out, _pad(r, 32))
+    return np.ascontiguousarray(ut[:, :r].T), sg, V
 
 
 # ------------------------------------------------------------------ BitDelta
@@ -170,4 +190,19 @@ def bitdelta_apply_multitenant(w_bits, x_bits, ids, tenants) -> np.ndarray:
         sel = np.nonzero(ids == k)[0]
         if sel.size:
             y[sel] += x[sel] @ (float(alpha) * signs(bits)).T
+    return y
+
+
+def lowrank_apply_multitenant(w_bits, x_bits, ids, tenants) -> np.ndarray:
+    """tenants: list of (U16 [r][out], sigma [r], V16 [r][in]); ids outside
+    [0, n): backbone only.  Each token: y = W x + U (sigma * (V x)) in fp64."""
+    from .apply import apply_factored, bf16_to_f64
+    ids = np.asarray(ids)
+    x = bf16_to_f64(x_bits)
+    out = np.asarray(tenants[0][0]).shape[1]
+    y = np.zeros((x.shape[0], out)) if w_bits is None else x @ bf16_to_f64(w_bits).T
+    for k, (U16, sg, V16) in enumerate(tenants):
+        sel = np.nonzero(ids == k)[0]
+        if sel.size:
+            y[sel] += apply_factored(None, np.asarray(x_bits)[sel], U16, sg, V16)
     return y

@@ -69,6 +69,21 @@ RANK_GROUPS: Dict[Tuple[int, int, int], Tuple[int, int, int]] = {
 }
 C0_GROUPS = (2, 8, 22)
 
+# Pairs kept by the fp16 low-rank baseline at the same budgets (data for the
+# generator; the tests check every entry against the oracle's budget rule).
+LOWRANK_R: Dict[Tuple[int, int, int], int] = {
+    (4096, 4096, 16): 128,
+    (11008, 4096, 16): 186,
+    (4096, 11008, 16): 186,
+    (5120, 5120, 16): 160,
+    (13824, 5120, 16): 233,
+    (5120, 13824, 16): 233,
+    (4096, 4096, 32): 64,
+    (1024, 4096, 32): 25,
+    (14336, 4096, 32): 99,
+    (4096, 14336, 32): 99,
+}
+
 
 # ---------------------------------------------------------------------------
 # dtype rounding of inputs (round-to-nearest-even), bit patterns as uint16
@@ -299,3 +314,38 @@ def random_singular_pairs(seed: int, out: int, inn: int, r: int,
     v = (rng.standard_normal((r, inn)) * scale / np.sqrt(inn)).astype(np.float32)
     s = np.sort(np.abs(rng.standard_normal(r)))[::-1].astype(np.float32)
     return u, s, v
+
+
+# ---------------------------------------------------------------------------
+# the two baselines the pages compare with: fp16 low-rank pairs and 1-bit
+# sign deltas with one scale per matrix
+# ---------------------------------------------------------------------------
+def random_lowrank(rng: np.random.Generator, out: int, inn: int, r: int):
+    """fp16 U [r][out] and V [r][in] with N(0, 1/dim) entries (vectors of
+    about unit norm), fp32 sigma_i = 0.05 i^-0.8.  Draw order: U, V."""
+    u = (rng.standard_normal((r, out)) / np.sqrt(out)).astype(np.float16)
+    v = (rng.standard_normal((r, inn)) / np.sqrt(inn)).astype(np.float16)
+    return u, sigma_profile(r), v
+
+
+def random_bitdelta(rng: np.random.Generator, out: int, inn: int):
+    """Uniform sign bits uint8 [out][in] (1 = +1) and an fp32 scale drawn as
+    |log-normal(-7, 0.5)| (about 1e-3, the size of a fine-tuning delta entry).
+    Draw order: bits, scale."""
+    bits = rng.integers(0, 2, size=(out, inn), dtype=np.uint8)
+    alpha = np.float32(abs(rng.lognormal(-7.0, 0.5)))
+    return bits, alpha
+
+
+def lowrank_r(out: int, inn: int, budget: int) -> int:
+    return LOWRANK_R[(out, inn, budget)]
+
+
+def make_c1_lowrank(mi: int, seed: int = 1):
+    _, out, inn = LLAMA2_7B[mi]
+    return random_lowrank(_child(seed, mi, 7), out, inn, lowrank_r(out, inn, 16))
+
+
+def make_c1_bitdelta(mi: int, seed: int = 1):
+    _, out, inn = LLAMA2_7B[mi]
+    return random_bitdelta(_child(seed, mi, 8), out, inn)

@@ -39,17 +39,29 @@ def test_lowrank_fp16_rounding_and_exact_reconstruction():
     np.testing.assert_allclose(oap.apply_factored(None, x, U16, s32, V16), dense, rtol=1e-12, atol=1e-12)
 
 
-def test_lowrank_layout_round_trip():
+def test_lowrank_layout_golden_and_round_trip():
     reg, total = bl.lowrank_regions(256, 384, 5)
-    # hand-derived: sigma 20 B at 0; V 5*384*2 = 3840 B at 256; U 5*256*2 = 2560 B at 256+3840 = 4096
-    assert reg == {"SIGMA": (0, 20), "V": (256, 3840), "U": (4096, 2560)} and total == 6656
+    # hand-derived: sigma 20 B at 0; V 16 rank rows * 384 * 2 = 12288 B at 256;
+    # U 256 rows * 32 ranks * 2 = 16384 B at 256 + 12288 = 12544
+    assert reg == {"SIGMA": (0, 20), "V": (256, 12288), "U": (12544, 16384)} and total == 28928
+    U = np.zeros((5, 256), np.float16)
+    V = np.zeros((5, 384), np.float16)
+    V[3, 77] = 1.0      # tile 0, step 2, slot 3 + 16 * ((77 % 32) / 8) = 3 + 16, element 5
+    U[4, 33] = 2.0      # tile 2, step 0, slot 1 + 16 * (4 / 8) = 1, element 4
+    buf = bl.lowrank_pack(U, np.arange(5, dtype=np.float32), V)
+    v = buf[256:256 + 12288].view(np.float16)
+    u = buf[12544:12544 + 16384].view(np.float16)
+    assert np.nonzero(v)[0].tolist() == [((0 * 12 + 2) * 64 + 19) * 8 + 5]
+    assert np.nonzero(u)[0].tolist() == [((2 * 1 + 0) * 64 + 1) * 8 + 4] and u[(2 * 64 + 1) * 8 + 4] == 2.0
+    assert buf[:20].view(np.float32).tolist() == [0.0, 1.0, 2.0, 3.0, 4.0]
     rng = np.random.default_rng(4)
-    U = rng.standard_normal((5, 256)).astype(np.float16)
-    V = rng.standard_normal((5, 384)).astype(np.float16)
-    sg = rng.random(5).astype(np.float32)
-    buf = bl.lowrank_pack(U, sg, V)
-    U2, sg2, V2 = bl.lowrank_unpack(buf, 256, 384, 5)
-    assert np.array_equal(U2.view(np.uint16), U.view(np.uint16)) and np.array_equal(V2, V) and np.array_equal(sg2, sg)
+    for r in (5, 16, 37):
+        U = rng.standard_normal((r, 256)).astype(np.float16)
+        V = rng.standard_normal((r, 384)).astype(np.float16)
+        sg = rng.random(r).astype(np.float32)
+        U2, sg2, V2 = bl.lowrank_unpack(bl.lowrank_pack(U, sg, V), 256, 384, r)
+        assert np.array_equal(U2.view(np.uint16), U.view(np.uint16)) and np.array_equal(V2, V)
+        assert np.array_equal(sg2, sg)
 
 
 def test_bitdelta_signs_and_scale_by_hand():
@@ -121,3 +133,39 @@ def test_bitdelta_apply_brute_force():
     y = bl.bitdelta_apply_multitenant(w, x, ids, ten)
     np.testing.assert_allclose(y[0], bl.bitdelta_apply(w, x[:1], bits, a)[0], rtol=1e-12)
     np.testing.assert_allclose(y[1], xf[1] @ wf.T, rtol=1e-12)
+
+
+def test_lowrank_multitenant_brute_force():
+    rng = np.random.default_rng(8)
+    out, inn, T = 6, 5, 4
+    ten = []
+    for r in (2, 0, 3):
+        ten.append((rng.standard_normal((r, out)).astype(np.float16), rng.random(r).astype(np.float32),
+                    rng.standard_normal((r, inn)).astype(np.float16)))
+    w = synth.base_weight(rng, out, inn)
+    x = synth.activations(rng, T, inn)
+    ids = np.array([2, -1, 0, 1])
+    y = bl.lowrank_apply_multitenant(w, x, ids, ten)
+    xf, wf = oap.bf16_to_f64(x), oap.bf16_to_f64(w)
+    for t in range(T):
+        for o in range(out):
+            ref = sum(wf[o][j] * xf[t][j] for j in range(inn))
+            if ids[t] >= 0:
+                U, sg, V = ten[ids[t]]
+                for i in range(len(sg)):
+                    ref += float(U[i][o]) * float(sg[i]) * sum(float(V[i][j]) * xf[t][j] for j in range(inn))
+            assert abs(y[t][o] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_lowrank_rank_table_matches_the_budget_rule():
+    for (out, inn, budget), r in synth.LOWRANK_R.items():
+        assert bl.lowrank_rank(out, inn, budget) == r
+
+
+def test_baseline_generators_are_seeded():
+    u, s, v = synth.make_c1_lowrank(4)
+    assert u.shape == (186, 11008) and v.shape == (186, 4096) and s.shape == (186,)
+    u2, _, _ = synth.make_c1_lowrank(4)
+    assert np.array_equal(u.view(np.uint16), u2.view(np.uint16))
+    b, a = synth.make_c1_bitdelta(0)
+    assert b.shape == (4096, 4096) and set(np.unique(b)) == {0, 1} and 1e-4 < a < 1e-2
