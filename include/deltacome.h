@@ -413,6 +413,110 @@ dc_status dc_apply_prefill(const dc_delta_view* views, int32_t n, const uint16_t
  */
 dc_status dc_dequant(const dc_delta_view* d, uint16_t* u_fp16, uint16_t* v_fp16, void* stream);
 
+/*
+ * Baselines.  The pages compare Delta-CoMe, at the same storage, with a
+ * low-rank delta and with BitDelta's 1-bit delta: [P2] "Experimental setup"
+ * (baselines: low-rank SVD compression and BitDelta) and "Key results"
+ * (Delta-CoMe ahead of both at 1/16); [P2] "Approach" (Delta-CoMe the size
+ * of BitDelta); [P3] "Delta-CoMe: 大型语言模型的无需训练的混合精度增量压缩"
+ * (related work: BitDelta quantizes a fine-tuning delta to 1 bit).  Neither
+ * baseline's arithmetic is printed there; this library serves them as:
+ *   DC_KIND_LOWRANK   the top r singular pairs as fp16 vectors, fp32 sigma:
+ *                     y = W_base x + U (sigma * (V x)); at the budget of
+ *                     Delta-CoMe's 1/16, r = floor(out in / (16 (out + in)))
+ *                     (128 for 4096 x 4096)
+ *   DC_KIND_BITDELTA  one sign bit per delta entry and one fp32 scale alpha:
+ *                     y = W_base x + alpha S x, S in {+1, -1}^(out x in)
+ * Formats (each region at a multiple of 256 bytes from the buffer start;
+ * total rounded up to 256 bytes; pad entries zero):
+ *   low-rank   SIGMA fp32 [r]; V fp16 [ceil(r/16)][in/32][64][8]: v_i[k] at
+ *              tile i/16, step k/32, slot (i%16) + 16((k%32)/8), element
+ *              k%8; U fp16 [out/16][ceil(r/32)][64][8]: u_i[o] at tile o/16,
+ *              step i/32, slot (o%16) + 16((i%32)/8), element i%8.  One
+ *              16-row tile of one 32-element step is 1 KiB, a matrix-core
+ *              operand for 64 lanes.
+ *   BitDelta   SCALE fp32 alpha (region of 256 bytes), then uint32 words
+ *              [out/16][in/128][4][16]: word (T, g, c, i) holds the signs of
+ *              row 16T+i, columns 128g + 32c + k (k < 32), bit set = +1; entry
+ *              k sits at bit 4(k'%8) + k'/8 with k' = k/2 for even k and
+ *              16 + k/2 for odd k, so that word >> s & 0x11111111 (s < 4) holds
+ *              8 entries, one per nibble.
+ * Shapes: out and in positive multiples of 128; low-rank 0 <= r <= min(out,
+ * in).  Calls and conventions as for the Delta-CoMe calls.
+ */
+enum { DC_KIND_LOWRANK = 1, DC_KIND_BITDELTA = 2 };
+
+typedef struct dc_baseline_view {
+  int32_t kind;     /* DC_KIND_LOWRANK or DC_KIND_BITDELTA */
+  int32_t out, in;  /* matrix shape, multiples of 128 */
+  int32_t r;        /* low-rank: pairs kept; BitDelta: 0 */
+  const void* base; /* device pointer to dc_baseline_bytes(kind, out, in, r) bytes */
+} dc_baseline_view;
+
+/* Size in bytes of a baseline buffer; 0 if the arguments are invalid (and
+ * for a low-rank delta with r = 0, which stores nothing and may have a NULL
+ * base). */
+size_t dc_baseline_bytes(int32_t kind, int32_t out, int32_t in, int32_t r);
+
+/* Bytes the baseline must move without padding (bandwidth figures):
+ * low-rank 2 r (out + in) + 4 r; BitDelta out in / 8 + 4. */
+size_t dc_baseline_algorithmic_bytes(int32_t kind, int32_t out, int32_t in, int32_t r);
+
+/*
+ * dc_pack_lowrank -- lay out fp16 pairs in the low-rank format (host).
+ *   U      host fp16 bits [r][out], row i = u_i
+ *   sigma  host fp32 [r]
+ *   V      host fp16 bits [r][in], row i = v_i
+ *   dst    host buffer of dst_bytes >= dc_baseline_bytes(DC_KIND_LOWRANK, ..),
+ *          fully written
+ * Errors: DC_ERR_INVALID_ARG (NULL with r > 0), DC_ERR_SHAPE, DC_ERR_BUFFER.
+ */
+dc_status dc_pack_lowrank(int32_t out, int32_t in, int32_t r, const uint16_t* U, const float* sigma,
+                          const uint16_t* V, void* dst, size_t dst_bytes);
+
+/*
+ * dc_pack_bitdelta -- lay out sign bits and their scale in the BitDelta
+ * format (host).
+ *   signs  host uint8 [out][in], nonzero = +1, 0 = -1
+ *   alpha  the scale (finite)
+ *   dst    host buffer of dst_bytes >= dc_baseline_bytes(DC_KIND_BITDELTA, ..)
+ * Errors: DC_ERR_INVALID_ARG (NULL), DC_ERR_SHAPE, DC_ERR_BUFFER,
+ * DC_ERR_RANGE (alpha not finite).
+ */
+dc_status dc_pack_bitdelta(int32_t out, int32_t in, const uint8_t* signs, float alpha, void* dst,
+                           size_t dst_bytes);
+
+/* Workspace of dc_apply_baseline_multitenant(_group): views [m][n] as its
+ * views; 0 on invalid arguments. */
+size_t dc_baseline_workspace_bytes(const dc_baseline_view* views, int32_t m, int32_t n, int32_t T);
+
+/*
+ * dc_apply_baseline_multitenant -- dc_apply_multitenant for baseline
+ * deltas: n tenants of one kind over one backbone, tokens routed by id
+ * (-1 = backbone only; other ids out of range as for dc_apply_multitenant).
+ *   views  host array [n], one kind, one out/in (low-rank r may differ)
+ *   W_base, x, tenant_ids, y, T, ws, ws_bytes, stream  as dc_apply_multitenant
+ * y = RNE_bf16(W_base x + delta x), fp32 sums in a fixed order (repeated
+ * calls give the same bits).  Arithmetic: BitDelta multiplies x as two fp8
+ * (e4m3) pieces with power-of-two block scales (about 2^-8 relative per
+ * element) by the exact signs; low-rank multiplies x, rescaled by a power of
+ * two per 128 inputs into fp16 (exact for bf16 values in fp16's normal
+ * range), by the fp16 V, and sigma (V x), split into two fp16 pieces per
+ * token, by the fp16 U.
+ * Errors: as dc_apply_multitenant; DC_ERR_SHAPE for mixed kinds or shapes.
+ */
+dc_status dc_apply_baseline_multitenant(const dc_baseline_view* views, int32_t n, const uint16_t* W_base,
+                                        const uint16_t* x, const int32_t* tenant_ids, uint16_t* y, int32_t T,
+                                        void* ws, size_t ws_bytes, void* stream);
+
+/* The grouped form (as dc_apply_multitenant_group): views [m][n], one kind
+ * for the whole group, W_base and y host arrays [m]; output j is
+ * bit-identical to dc_apply_baseline_multitenant on matrix j alone. */
+dc_status dc_apply_baseline_multitenant_group(const dc_baseline_view* views, int32_t m, int32_t n,
+                                              const uint16_t* const* W_base, const uint16_t* x,
+                                              const int32_t* tenant_ids, uint16_t* const* y, int32_t T,
+                                              void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,4 +10,7 @@ from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, MultitenantCall, REGIONS, DcError, DeltaView, dc_algorithmic_bytes, dc_apply_decode,
     dc_apply_multitenant, dc_apply_multitenant_group, dc_apply_multitenant_noalloc, dc_apply_multitenant_timed, dc_apply_prefill, STAGES, dc_check_spec, dc_dequant, dc_pack, dc_pack_codes,
     dc_allocate_bits, dc_pack_device, dc_packed_bytes, dc_region, dc_status_string, dc_unpack, dc_workspace_bytes, dc_group_workspace_bytes, GroupCall, lib, make_spec,
+    DC_KIND_BITDELTA, DC_KIND_LOWRANK, BaselineGroupCall, BaselineView, dc_apply_baseline_multitenant,
+    dc_apply_baseline_multitenant_group, dc_baseline_algorithmic_bytes, dc_baseline_bytes,
+    dc_baseline_workspace_bytes, dc_pack_bitdelta, dc_pack_lowrank,
 )

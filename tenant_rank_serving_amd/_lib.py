@@ -34,7 +34,13 @@ EXPORTS = ("dc_status_string", "dc_check_spec", "dc_packed_bytes", "dc_algorithm
            "dc_apply_decode", "dc_apply_multitenant", "dc_apply_multitenant_timed",
            "dc_apply_prefill", "dc_dequant", "dc_pack_device", "dc_allocate_bits",
            "dc_apply_multitenant_noalloc", "dc_apply_multitenant_group", "dc_group_workspace_bytes",
-           "dc_apply_multitenant_group_timed")
+           "dc_apply_multitenant_group_timed", "dc_baseline_bytes", "dc_baseline_algorithmic_bytes",
+           "dc_pack_lowrank", "dc_pack_bitdelta", "dc_baseline_workspace_bytes",
+           "dc_apply_baseline_multitenant", "dc_apply_baseline_multitenant_group")
+DC_KIND_LOWRANK, DC_KIND_BITDELTA = 1, 2
+_SIZE_FNS = ("dc_status_string", "dc_packed_bytes", "dc_algorithmic_bytes", "dc_workspace_bytes",
+             "dc_group_workspace_bytes", "dc_baseline_bytes", "dc_baseline_algorithmic_bytes",
+             "dc_baseline_workspace_bytes")
 STAGES = ("route", "xprep", "base", "vside", "uside")
 
 
@@ -53,6 +59,11 @@ class dc_delta_view(ctypes.Structure):
     _fields_ = [("spec", dc_spec), ("base", ctypes.c_void_p)]
 
 
+class dc_baseline_view(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("out", ctypes.c_int32), ("in_", ctypes.c_int32),
+                ("r", ctypes.c_int32), ("base", ctypes.c_void_p)]
+
+
 _P = ctypes.c_void_p
 _lib = None
 
@@ -63,6 +74,11 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError("libdeltacome.so is not built (python -m tenant_rank_serving_amd.build)")
+        # torch first: its HIP runtime (libamdhip64.so.7, bundled with torch)
+        # is then the one the library binds to.  Loaded the other way round,
+        # the process holds two HIP runtimes and the library's finds no
+        # device ("no ROCm-capable device is detected").
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         sp = ctypes.POINTER(dc_spec)
         vp = ctypes.POINTER(dc_delta_view)
@@ -96,9 +112,21 @@ def lib() -> ctypes.CDLL:
         L.dc_dequant.argtypes = [vp, _P, _P, _P]
         L.dc_pack_device.argtypes = [sp, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
         L.dc_allocate_bits.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int64, _P, _P]
+        bp = ctypes.POINTER(dc_baseline_view)
+        i32 = ctypes.c_int32
+        L.dc_baseline_bytes.restype = ctypes.c_size_t
+        L.dc_baseline_bytes.argtypes = [i32, i32, i32, i32]
+        L.dc_baseline_algorithmic_bytes.restype = ctypes.c_size_t
+        L.dc_baseline_algorithmic_bytes.argtypes = [i32, i32, i32, i32]
+        L.dc_pack_lowrank.argtypes = [i32, i32, i32, _P, _P, _P, _P, ctypes.c_size_t]
+        L.dc_pack_bitdelta.argtypes = [i32, i32, _P, ctypes.c_float, _P, ctypes.c_size_t]
+        L.dc_baseline_workspace_bytes.restype = ctypes.c_size_t
+        L.dc_baseline_workspace_bytes.argtypes = [bp, i32, i32, i32]
+        L.dc_apply_baseline_multitenant.argtypes = [bp, i32, _P, _P, _P, _P, i32, _P, ctypes.c_size_t, _P]
+        L.dc_apply_baseline_multitenant_group.argtypes = [bp, i32, i32, _P, _P, _P, _P, i32, _P,
+                                                          ctypes.c_size_t, _P]
         for name in EXPORTS:
-            if name not in ("dc_status_string", "dc_packed_bytes", "dc_algorithmic_bytes",
-                            "dc_workspace_bytes", "dc_group_workspace_bytes"):
+            if name not in _SIZE_FNS:
                 getattr(L, name).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -383,3 +411,91 @@ def dc_allocate_bits(err, cost, budget: int):
     _check(lib().dc_allocate_bits(r, nb, c.ctypes.data, e.ctypes.data, int(budget), choice.ctypes.data,
                                   ctypes.addressof(total)), "dc_allocate_bits")
     return choice, total.value
+
+
+# -------------------------------------------------------------- baselines
+def dc_baseline_bytes(kind: int, out: int, inn: int, r: int = 0) -> int:
+    return int(lib().dc_baseline_bytes(int(kind), int(out), int(inn), int(r)))
+
+
+def dc_baseline_algorithmic_bytes(kind: int, out: int, inn: int, r: int = 0) -> int:
+    return int(lib().dc_baseline_algorithmic_bytes(int(kind), int(out), int(inn), int(r)))
+
+
+def dc_pack_lowrank(U16, sigma, V16) -> np.ndarray:
+    """U16 fp16 [r][out], sigma fp32 [r], V16 fp16 [r][in] -> packed bytes."""
+    U16 = np.ascontiguousarray(np.asarray(U16, np.float16))
+    V16 = np.ascontiguousarray(np.asarray(V16, np.float16))
+    r, out = U16.shape
+    inn = V16.shape[1]
+    sg, sp = _np_ptr(sigma, np.float32)
+    n = dc_baseline_bytes(DC_KIND_LOWRANK, out, inn, r)
+    buf = np.zeros(max(n, 1), np.uint8)
+    _check(lib().dc_pack_lowrank(out, inn, r, U16.ctypes.data, sp, V16.ctypes.data, buf.ctypes.data, n),
+           "dc_pack_lowrank")
+    return buf[:n]
+
+
+def dc_pack_bitdelta(signs, alpha) -> np.ndarray:
+    """signs uint8 [out][in] (nonzero = +1), alpha float -> packed bytes."""
+    sg, sp = _np_ptr(signs, np.uint8)
+    out, inn = sg.shape
+    n = dc_baseline_bytes(DC_KIND_BITDELTA, out, inn, 0)
+    buf = np.zeros(max(n, 1), np.uint8)
+    _check(lib().dc_pack_bitdelta(out, inn, sp, ctypes.c_float(float(alpha)), buf.ctypes.data, n),
+           "dc_pack_bitdelta")
+    return buf[:n]
+
+
+class BaselineView:
+    """A packed baseline delta in device memory (keeps its tensor alive)."""
+
+    def __init__(self, kind: int, out: int, inn: int, r: int, buf):
+        self.kind, self.out, self.inn, self.r = int(kind), int(out), int(inn), int(r)
+        self.buf = buf
+        self.c = dc_baseline_view(self.kind, self.out, self.inn, self.r,
+                                  ctypes.c_void_p(int(buf.data_ptr()) if buf is not None else 0))
+
+
+def _bviews(views):
+    return (dc_baseline_view * len(views))(*[v.c for v in views])
+
+
+def dc_baseline_workspace_bytes(views, m: int, T: int) -> int:
+    """views: [m][n] BaselineViews (a list of m lists, or m*n in order)."""
+    flat = [v for row in views for v in row] if isinstance(views[0], (list, tuple)) else list(views)
+    return int(lib().dc_baseline_workspace_bytes(_bviews(flat), int(m), len(flat) // int(m), int(T)))
+
+
+def dc_apply_baseline_multitenant(views, W_base, x, tenant_ids, y, ws, T: int = None, stream=None) -> None:
+    T = x.shape[0] if T is None else T
+    _check(lib().dc_apply_baseline_multitenant(_bviews(views), len(views), _dptr(W_base, "W_base"), _dptr(x, "x"),
+                                               _dptr(tenant_ids, "tenant_ids"), _dptr(y, "y"), int(T),
+                                               _dptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
+           "dc_apply_baseline_multitenant")
+
+
+class BaselineGroupCall:
+    """dc_apply_baseline_multitenant_group with its arguments marshalled once
+    (views [m][n] BaselineViews; W_base list of m tensors or None; y list of m)."""
+
+    def __init__(self, views, W_base, x, tenant_ids, y, ws, T: int = None, stream=None):
+        m, n = len(views), len(views[0])
+        T = x.shape[0] if T is None else T
+        flat = [v for row in views for v in row]
+        self._keep = (flat, W_base, x, tenant_ids, y, ws)
+        self._arr = _bviews(flat)
+        self._w = _ptr_array(W_base, "W_base") if W_base is not None else None
+        self._y = _ptr_array(y, "y")
+        self.args = (self._arr, m, n, self._w, _dptr(x, "x"), _dptr(tenant_ids, "tenant_ids"), self._y, int(T),
+                     _dptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream))
+        self._fn = lib().dc_apply_baseline_multitenant_group
+
+    def __call__(self) -> None:
+        st = self._fn(*self.args)
+        if st != DC_OK:
+            raise DcError(st, "dc_apply_baseline_multitenant_group")
+
+
+def dc_apply_baseline_multitenant_group(views, W_base, x, tenant_ids, y, ws, T: int = None, stream=None) -> None:
+    BaselineGroupCall(views, W_base, x, tenant_ids, y, ws, T, stream)()

@@ -61,6 +61,47 @@ bool layout_of_group(const Dims* d, int32_t m, int32_t n, int32_t T, int32_t drp
   return dc::ws_layout(T, d[0].in, n, m, out, rs, vb, drp, wl);
 }
 
+// Checks baseline views [m][n]: one kind, one out/in per matrix, one in for
+// the group; fills each matrix's shape and largest rank.
+struct BDims {
+  int32_t out, in, rmax;
+};
+
+dc_status check_baseline(const dc_baseline_view* v, int32_t m, int32_t n, int32_t* kind, BDims* d) {
+  if (!v || m < 1 || n < 1) return DC_ERR_INVALID_ARG;
+  if (m > DC_MAX_GROUP || n > DC_MAX_TENANTS) return DC_ERR_UNSUPPORTED;
+  *kind = v[0].kind;
+  if (*kind != DC_KIND_LOWRANK && *kind != DC_KIND_BITDELTA) return DC_ERR_SHAPE;
+  for (int j = 0; j < m; ++j) {
+    d[j].out = v[(size_t)j * n].out;
+    d[j].in = v[(size_t)j * n].in;
+    d[j].rmax = 0;
+    for (int k = 0; k < n; ++k) {
+      const dc_baseline_view& e = v[(size_t)j * n + k];
+      if (e.kind != *kind || e.out != d[j].out || e.in != d[j].in) return DC_ERR_SHAPE;
+      if (!dc::baseline_valid(e.kind, e.out, e.in, e.r)) return DC_ERR_SHAPE;
+      if (e.r > d[j].rmax) d[j].rmax = e.r;
+    }
+    if (d[j].in != d[0].in) return DC_ERR_SHAPE;
+  }
+  return DC_OK;
+}
+
+bool baseline_layout(int32_t kind, const BDims* d, int32_t m, int32_t n, int32_t T, dc::WsLayout* wl) {
+  int32_t out[DC_MAX_GROUP], rs[DC_MAX_GROUP], vb[DC_MAX_GROUP];
+  for (int j = 0; j < m; ++j) {
+    out[j] = d[j].out;
+    if (kind == DC_KIND_LOWRANK) {
+      rs[j] = (int32_t)dc::round_up((size_t)(d[j].rmax > 0 ? d[j].rmax : 1), 16);
+      vb[j] = dc::lr_vblocks(d[j].rmax);
+    } else {
+      rs[j] = 8;
+      vb[j] = d[j].out / dc::kBdRows;
+    }
+  }
+  return dc::ws_layout(T, d[0].in, n, m, out, rs, vb, 0, wl, kind);
+}
+
 }  // namespace
 
 namespace dc {
@@ -148,6 +189,70 @@ dc_status run_apply(const dc_delta_view* views, int32_t m, int32_t n, const uint
   a.events = events;
   return dc::launch_apply(a) == 0 ? DC_OK : DC_ERR_HIP;
 }
+
+dc_status run_baseline(const dc_baseline_view* views, int32_t m, int32_t n, const uint16_t* const* W,
+                       const uint16_t* x, const int32_t* ids, uint16_t* const* y, int32_t T, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!views || n < 1 || m < 1 || !y || T < 0) return DC_ERR_INVALID_ARG;
+  int32_t kind = 0;
+  BDims dm[DC_MAX_GROUP];
+  dc_status st = check_baseline(views, m, n, &kind, dm);
+  if (st != DC_OK) return st;
+  const int32_t in = dm[0].in;
+  dc::TenantTable tables[DC_MAX_GROUP];
+  for (int j = 0; j < m; ++j) {
+    std::memset(&tables[j], 0, sizeof(tables[j]));
+    for (int k = 0; k < n; ++k) {
+      const dc_baseline_view& v = views[(size_t)j * n + k];
+      const bool reads = kind == DC_KIND_BITDELTA || v.r > 0;
+      if (reads && !v.base) return DC_ERR_INVALID_ARG;
+      if (!aligned(v.base, 16)) return DC_ERR_ALIGN;
+      tables[j].t[k].base = static_cast<const uint8_t*>(v.base);
+      tables[j].t[k].n8 = kind == DC_KIND_LOWRANK ? v.r : 0;
+    }
+  }
+  if (!x || !ws || !ids) return DC_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(ids, 4)) return DC_ERR_ALIGN;
+  for (int j = 0; j < m; ++j) {
+    if (!y[j]) return DC_ERR_INVALID_ARG;
+    if (!aligned(y[j], 16) || (W && W[j] && !aligned(W[j], 16))) return DC_ERR_ALIGN;
+    if (overlap(x, (size_t)T * in * 2, y[j], (size_t)T * dm[j].out * 2)) return DC_ERR_INVALID_ARG;
+    for (int i = 0; i < j; ++i)
+      if (overlap(y[i], (size_t)T * dm[i].out * 2, y[j], (size_t)T * dm[j].out * 2)) return DC_ERR_INVALID_ARG;
+  }
+  dc::WsLayout wl{};
+  if (!baseline_layout(kind, dm, m, n, T, &wl)) return DC_ERR_INVALID_ARG;
+  if (ws_bytes < wl.total) return DC_ERR_BUFFER;
+  // the kernels address t, the backbone product and each buffer with 32-bit byte offsets
+  const size_t lim = (size_t)INT32_MAX;
+  for (int j = 0; j < m; ++j)
+    if ((size_t)T * wl.mat[j].rs * 4 > lim || (size_t)T * dm[j].out * 4 > lim ||
+        dc_baseline_bytes(kind, dm[j].out, in, dm[j].rmax) > lim)
+      return DC_ERR_UNSUPPORTED;
+  if (T == 0) return DC_OK;
+  dc::ApplyArgs a{};
+  a.kind = kind;
+  a.m = m;
+  for (int j = 0; j < m; ++j) {
+    a.mat[j].tenants = &tables[j];
+    a.mat[j].out = dm[j].out;
+    a.mat[j].rmax = dm[j].rmax;
+    a.mat[j].W = W ? W[j] : nullptr;
+    a.mat[j].y = y[j];
+  }
+  a.n = n;
+  a.in = in;
+  a.T = T;
+  a.x = x;
+  a.ids = ids;
+  a.seg = nullptr;
+  a.mode = 1;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.wl = wl;
+  a.stream = stream;
+  a.events = nullptr;
+  return dc::launch_apply(a) == 0 ? DC_OK : DC_ERR_HIP;
+}
 }  // namespace dc
 
 namespace {
@@ -222,6 +327,29 @@ dc_status dc_apply_prefill(const dc_delta_view* views, int32_t n, const uint16_t
   for (int k = 0; k < n; ++k)
     if (seg_offsets[k + 1] < seg_offsets[k]) return DC_ERR_INVALID_ARG;
   return run(views, n, W_base, x, nullptr, seg_offsets, 2, y, seg_offsets[n], ws, ws_bytes, stream);
+}
+
+size_t dc_baseline_workspace_bytes(const dc_baseline_view* views, int32_t m, int32_t n, int32_t T) {
+  if (T < 0) return 0;
+  int32_t kind = 0;
+  BDims dm[DC_MAX_GROUP];
+  if (check_baseline(views, m, n, &kind, dm) != DC_OK) return 0;
+  dc::WsLayout wl{};
+  if (!baseline_layout(kind, dm, m, n, T, &wl)) return 0;
+  return wl.total;
+}
+
+dc_status dc_apply_baseline_multitenant(const dc_baseline_view* views, int32_t n, const uint16_t* W_base,
+                                        const uint16_t* x, const int32_t* tenant_ids, uint16_t* y, int32_t T,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  return dc::run_baseline(views, 1, n, &W_base, x, tenant_ids, &y, T, ws, ws_bytes, stream);
+}
+
+dc_status dc_apply_baseline_multitenant_group(const dc_baseline_view* views, int32_t m, int32_t n,
+                                              const uint16_t* const* W_base, const uint16_t* x,
+                                              const int32_t* tenant_ids, uint16_t* const* y, int32_t T,
+                                              void* ws, size_t ws_bytes, void* stream) {
+  return dc::run_baseline(views, m, n, W_base, x, tenant_ids, y, T, ws, ws_bytes, stream);
 }
 
 dc_status dc_pack_device(const dc_spec* spec, const float* U, const float* sigma, const float* V, void* out,

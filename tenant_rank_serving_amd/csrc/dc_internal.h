@@ -122,6 +122,7 @@ DC_HD inline void layout_of(int32_t out, int32_t in, int32_t n8, int32_t n3, int
 }
 
 // One tenant as the kernels see it (kernel-argument table, no device copy).
+// Baseline calls: n8 holds the low-rank r (0 for BitDelta), n3 = n2 = 0.
 struct Tenant {
   const uint8_t* base;
   int32_t n8, n3, n2;
@@ -190,13 +191,50 @@ constexpr int kMaxGroup = DC_MAX_GROUP;
 // load instead of indexing their kernel arguments.
 struct MatParams {
   float* tv;           // t [T][rs]
-  float* vpt;          // V-side slice partials [ns][T][rs]
+  float* vpt;          // V-side slice partials [ns][T][rs] (BitDelta: [ns][T][out])
   uint32_t* vcnt;      // V-side arrival counters [nact][vb]
   const float* ybase;  // W x [T][out], null: delta only
   uint16_t* y;         // output [T][out]
-  int32_t out, rs, vb, pad_;
+  const float* bpt;    // W x partials [nks][T][out] (read by the BitDelta epilogue when nks > 2)
+  int32_t out, rs, vb, nks;
 };
-static_assert(sizeof(MatParams) == 56, "one scalar load per kernel");
+static_assert(sizeof(MatParams) == 64, "one scalar load per kernel");
+
+// Kinds of delta an apply call serves: Delta-CoMe's mixed-precision pairs,
+// or one of the two baselines (include/deltacome.h: DC_KIND_*).
+constexpr int kKindDeltaCoMe = 0;
+constexpr int kKindLowrank = DC_KIND_LOWRANK;
+constexpr int kKindBitdelta = DC_KIND_BITDELTA;
+
+// Low-rank baseline: V side in blocks of kLrRanks ranks (4 waves x one
+// 16-rank tile) over input slices of kLrSlice; t rows padded to 32 ranks.
+constexpr int kLrSlice = 512;
+constexpr int kLrRanks = 64;
+DC_HD inline int lr_slices(int in) { return (in + kLrSlice - 1) / kLrSlice; }
+DC_HD inline int lr_vblocks(int r) { return (r + kLrRanks - 1) / kLrRanks; }
+// BitDelta: blocks of kBdRows output rows (4 waves x two 16-row tiles) over
+// input slices of kVSlice groups.
+constexpr int kBdRows = 128;
+
+// Shape rules of a baseline delta: out and in positive multiples of 128;
+// low-rank 0 <= r <= min(out, in); BitDelta r = 0.
+DC_HD inline bool baseline_valid(int32_t kind, int32_t out, int32_t in, int32_t r) {
+  if (out <= 0 || in <= 0 || out % kGroup || in % kGroup) return false;
+  if (kind == DC_KIND_LOWRANK) return r >= 0 && r <= (out < in ? out : in);
+  return kind == DC_KIND_BITDELTA && r == 0;
+}
+
+// Packed sizes of the baselines (the formats of include/deltacome.h).
+DC_HD inline size_t lowrank_bytes(int32_t out, int32_t in, int32_t r) {
+  const size_t v = round_up(4 * (size_t)r, kAlign);
+  const size_t u = round_up(v + 2 * round_up((size_t)r, 16) * in, kAlign);
+  return round_up(u + 2 * (size_t)out * round_up((size_t)r, 32), kAlign);
+}
+DC_HD inline size_t lowrank_v_offset(int32_t r) { return round_up(4 * (size_t)r, kAlign); }
+DC_HD inline size_t lowrank_u_offset(int32_t in, int32_t r) {
+  return round_up(lowrank_v_offset(r) + 2 * round_up((size_t)r, 16) * in, kAlign);
+}
+DC_HD inline size_t bitdelta_bytes(int32_t out, int32_t in) { return kAlign + (size_t)out * in / 8; }
 
 // The part of a call's workspace that belongs to one matrix of the group.
 struct WsMat {
@@ -240,9 +278,11 @@ struct WsLayout {
 // Per matrix j of the group: out[j], rs[j] (max t_width over its tenants),
 // vb[j] (max v_blocks over its tenants).  drp: rank rows of the dense prefill
 // operands (0 for decode calls; m must be 1 otherwise).
+// kind: kKindDeltaCoMe, or a baseline (rs = t row stride for the low-rank
+// baseline, vb = its V blocks; BitDelta: vb = output row blocks, no t).
 inline bool ws_layout(int32_t T, int32_t in, int32_t n, int32_t m, const int32_t* out, const int32_t* rs,
-                      const int32_t* vb, int32_t drp, WsLayout* W) {
-  if (T < 0 || n < 0 || m < 1 || m > kMaxGroup || (drp > 0 && m != 1)) return false;
+                      const int32_t* vb, int32_t drp, WsLayout* W, int32_t kind = kKindDeltaCoMe) {
+  if (T < 0 || n < 0 || m < 1 || m > kMaxGroup || (drp > 0 && (m != 1 || kind != kKindDeltaCoMe))) return false;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = round_up(o, kAlign); o = at + bytes; return at; };
   W->m = m;
@@ -255,20 +295,23 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t n, int32_t m, const int32_t
   W->xsc = take(4 * items);
   W->xsum = take(4 * items);
   W->xt = take(2 * (size_t)in * round_up((size_t)T, 16));
-  W->ns = v_slices(in);
+  W->ns = kind == kKindLowrank ? lr_slices(in) : v_slices(in);
   W->nks = base_splits(in, T);
   W->act = take(sizeof(ActEntry) * (size_t)m * W->nact);
   W->params = take(sizeof(MatParams) * kMaxGroup);
+  const bool bd = kind == kKindBitdelta;
+  // BitDelta slices always meet in the last one (its epilogue needs the sum)
+  const bool stored = bd ? W->ns > 1 : W->ns > kMaxAtomicTerms;
   for (int j = 0; j < m; ++j) {
     WsMat& M = W->mat[j];
     M.out = out[j];
     M.rs = rs[j] > 0 ? rs[j] : 8;
     M.vb = vb[j];
     M.ybase = take(4 * (size_t)T * M.out);
-    M.vpart = take(4 * (size_t)T * M.rs);
-    M.vpt = take(W->ns > kMaxAtomicTerms ? 4 * (size_t)W->ns * T * M.rs : 0);
+    M.vpart = take(bd ? 0 : 4 * (size_t)T * M.rs);
+    M.vpt = take(stored ? 4 * (size_t)W->ns * T * (bd ? M.out : M.rs) : 0);
     M.bpt = take(W->nks > kMaxAtomicTerms ? 4 * (size_t)W->nks * T * M.out : 0);
-    M.ncnt = W->ns > kMaxAtomicTerms ? W->nact * M.vb : 0;
+    M.ncnt = stored ? W->nact * M.vb : 0;
     M.cnt = take(4 * (size_t)M.ncnt);
   }
   W->drp = drp;
@@ -295,6 +338,7 @@ struct MatArgs {
 };
 
 struct ApplyArgs {
+  int32_t kind;                // kKindDeltaCoMe or a baseline (its tenant records: base, n8 = r)
   int32_t m;                   // matrices (1 except grouped calls)
   MatArgs mat[kMaxGroup];
   int32_t n;
@@ -310,6 +354,27 @@ struct ApplyArgs {
   void* const* events;         // optional DC_STAGE_COUNT + 1 hipEvent_t, may be null
 };
 int launch_apply(const ApplyArgs& a);
+// The delta kernels of a baseline call, after routing, x staging and the
+// backbone product (launched by launch_apply).
+struct BaselineLaunch {
+  int32_t kind, m, n, in, T, nact, ns;
+  const uint16_t* x;
+  const int32_t* perm;
+  const uint8_t* xf;
+  const uint32_t* xsc;
+  const float* xsum;
+  const ActEntry* act;         // [m][nact]
+  const MatParams* mp;         // [m], in the workspace
+  int32_t vbmax, outmax;       // largest V blocks / out of the group
+  // per matrix: W x partials to add in range order into ybase (low-rank
+  // calls whose backbone product has more than two K ranges), else null
+  const float* bpt[kMaxGroup];
+  float* ybase[kMaxGroup];
+  int32_t out[kMaxGroup];
+  int32_t nks;
+  void* stream;
+};
+int launch_baseline(const BaselineLaunch& b);
 // The backbone product W x into ybase (fp32 [T][out]).  Split over
 // base_splits(in, T) K ranges when T <= 256: with two ranges ybase must be
 // zeroed before it runs (the ranges add into it); with more, the ranges store

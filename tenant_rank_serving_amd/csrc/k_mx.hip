@@ -32,6 +32,7 @@ namespace {
 
 #include "mx_common.h"
 #include "combine.h"
+#include "vstage.h"
 
 struct Seg {
   int b, lo, n;
@@ -316,89 +317,6 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
 }
 
 // ------------------------------------------------------------------ V side
-// Where a V-side block puts sigma * (its slice's part of V x): with at most
-// kMaxAtomicTerms input slices, added into t (zeroed by prep) with float
-// atomics (order-independent for two terms); with more, stored as the
-// slice's partial and added in slice order by the block of the same ranks
-// that finishes last (counter per bucket and rank block).
-struct VOut {
-  float* tv;         // t [T][rs], sorted rows
-  float* vpt;        // partials [ns][T][rs] (ns > kMaxAtomicTerms)
-  uint32_t* vcnt;    // arrival counters [n + 1][vb]
-  int32_t rs, ns, T, vb;
-};
-
-__device__ __forceinline__ void v_put(const VOut& o, int s, int row, int rank, float v) {
-  if (o.ns <= kMaxAtomicTerms)
-    atomicAdd(o.tv + (size_t)row * o.rs + rank, v);
-  else
-    st_dev(o.vpt + ((size_t)s * o.T + row) * o.rs + rank, v);
-}
-
-// After every pass of the block of work item `item`: the last of the ns
-// slices of ranks [r0, r0 + nr) adds the partials of rows [p0, p1) in slice
-// order into t (the slices of an output are loaded kSliceBatch at a time).
-constexpr int kSliceBatch = 8;   // all the slices of up to 16384 inputs
-__device__ __forceinline__ void v_combine(const VOut& o, int item, int b, int p0, int p1, int r0, int nr) {
-  if (o.ns <= kMaxAtomicTerms) return;
-  __shared__ int last;
-  if (!arrive_last(&o.vcnt[item * o.vb + b], o.ns, &last)) return;
-  const size_t sstride = (size_t)o.T * o.rs;
-  for (int i = threadIdx.x; i < (p1 - p0) * nr; i += blockDim.x) {
-    const int row = p0 + i / nr, rank = r0 + i % nr;
-    const float* src = o.vpt + (size_t)row * o.rs + rank;
-    float v = 0.f;
-    for (int s0 = 0; s0 < o.ns; s0 += kSliceBatch) {
-      float p[kSliceBatch];
-#pragma unroll
-      for (int j = 0; j < kSliceBatch; ++j) p[j] = s0 + j < o.ns ? ld_dev(src + (s0 + j) * sstride) : 0.f;
-#pragma unroll
-      for (int j = 0; j < kSliceBatch; ++j)
-        if (s0 + j < o.ns) v += p[j];
-    }
-    o.tv[(size_t)row * o.rs + rank] = v;
-  }
-}
-
-// The backbone product's K-range partials (more than two ranges) added in
-// range order into W x, by blocks of the V-side launch that run before its
-// V-side blocks: block = 64 rows x 8 tokens, thread = one row, two tokens,
-// all of an output's ranges loaded before the sum.
-struct BaseSum {
-  const float* bpt;   // [nks][T][out]
-  float* ybase;       // [T][out]
-  int32_t nks, out, T;
-};
-
-
-__device__ void base_sum(const BaseSum& bs, int idx) {
-  const int ntb = (bs.T + 7) / 8;
-  const int rb = idx / ntb, tb = idx % ntb;
-  const int ro = rb * 64 + (threadIdx.x & 63), t0 = tb * 8 + 2 * (threadIdx.x >> 6);
-  if (t0 >= bs.T) return;
-  const bool two = t0 + 1 < bs.T;
-  const size_t rstride = (size_t)bs.T * bs.out;
-  const float* src = bs.bpt + (size_t)t0 * bs.out + ro;
-  float v0 = 0.f, v1 = 0.f;
-  for (int r0 = 0; r0 < bs.nks; r0 += 16) {
-    float a[16], c[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const bool ok = r0 + j < bs.nks;
-      a[j] = ok ? src[(r0 + j) * rstride] : 0.f;
-      c[j] = ok && two ? src[(r0 + j) * rstride + bs.out] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (r0 + j < bs.nks) {
-        v0 += a[j];
-        v1 += c[j];
-      }
-  }
-  bs.ybase[(size_t)t0 * bs.out + ro] = v0;
-  if (two) bs.ybase[(size_t)(t0 + 1) * bs.out + ro] = v1;
-}
-
 // Work item (block): tenant k = blockIdx.y; blockIdx.x = rank block rb *
 // v_slices + input slice s.  Rank blocks: the 8-bit rows (vector ALU, fp16
 // dequantized weights), then blocks of kVRanks ranks of the 3-bit and of the
@@ -411,13 +329,6 @@ __device__ void base_sum(const BaseSum& bs, int idx) {
 // matrix-core ops of group u (a later pass reloads them, from L2).  The
 // kVTiles ops of a group share one A operand and are independent.  sigma * (partial V x)
 // is added into t with float atomics; t is zeroed by the prep kernel.
-struct VLds {
-  int4 frag[kVSlice][kVRows][17];     // [group][token row][lane group * 4 + (hi0 hi1 lo0 lo1)], padded row
-  uint32_t sc[kVSlice][kVRows];       // E8M0 words of the hi pieces
-  float xs[kVSlice][kVRows];          // group sums of x
-};
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 struct U3 {
   uint32_t a, b, c;
 };
@@ -459,53 +370,6 @@ __device__ __forceinline__ void v_load_grp(VGrp<B>& c, const VBuf& p, int np, in
   }
 }
 
-// x fragments, scale words and group sums of sorted rows [pb, pb + kVRows)
-// for groups [g0, g0 + kVSlice), staged into LDS in two steps so that the
-// loads can go out ahead of the code ring.  Thread tid moves int4 (tid & 15)
-// of the fragment of row (tid >> 4) & 7 for groups (tid >> 7) + 2u; threads
-// < 128 move the scale word and group sum of row tid & 7 and group
-// (tid >> 3) & 15.  Rows past the pass repeat its last row and are never
-// read; groups past the input repeat its last group.
-struct VStage {
-  i32x4 v[kVSlice / 2];
-  uint32_t scw;
-  float xsv;
-};
-
-__device__ __forceinline__ void v_stage_load(VStage& st, const uint8_t* __restrict__ xf,
-                                             const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
-                                             int gi_n, int g0, int pb, int nt) {
-  const int tid = threadIdx.x;
-  const int k16 = tid & 15, rw = (tid >> 4) & 7, gh = tid >> 7;
-  const size_t row = (size_t)(pb + min(rw, nt - 1)) * gi_n;
-#pragma unroll
-  for (int u = 0; u < kVSlice / 2; ++u) {
-    const int gi = min(g0 + gh + 2 * u, gi_n - 1);
-    st.v[u] = reinterpret_cast<const i32x4*>(xf + (row + gi) * kXFrag)[k16];
-  }
-  const int sr = tid & 7, sgl = (tid >> 3) & (kVSlice - 1);
-  const size_t srow = (size_t)(pb + min(sr, nt - 1)) * gi_n + min(g0 + sgl, gi_n - 1);
-  st.scw = xsc[srow];
-  st.xsv = xsum[srow];
-}
-
-__device__ __forceinline__ void v_stage_store(VLds& S, const VStage& st) {
-  const int tid = threadIdx.x;
-  const int k16 = tid & 15, rw = (tid >> 4) & 7, gh = tid >> 7;
-#pragma unroll
-  for (int u = 0; u < kVSlice / 2; ++u)
-    S.frag[gh + 2 * u][rw][k16] = make_int4(st.v[u].x, st.v[u].y, st.v[u].z, st.v[u].w);
-  if (tid < kVRows * kVSlice) {
-    const int sr = tid & 7, sgl = (tid >> 3) & (kVSlice - 1);
-    S.sc[sgl][sr] = st.scw;
-    S.xs[sgl][sr] = st.xsv;
-  }
-}
-
-__device__ __forceinline__ void hold2(f32x4& d0, f32x4& d1, const v8i& a, const v8i& b0, const v8i& b1, int sa,
-                                      int sb) {
-  asm volatile("" : "+v"(d0), "+v"(d1) : "v"(a), "v"(b0), "v"(b1), "v"(sa), "v"(sb));
-}
 
 // kVTiles 16-rank tiles of one wave (starting at tile0 of the segment) over
 // one input slice, all tokens; the block's other waves run the same slice.
@@ -783,7 +647,6 @@ constexpr int kUWaves = 8;    // waves per block, one 16-row tile each
 constexpr int kU8Max = 2;     // 8-bit pairs whose U weights a lane keeps in registers
 constexpr int kUDepth = 4;    // chunks of codes in flight per lane
 constexpr int kUWin = 16;     // A operands per window (chunks x ops): 16 chunks with one op, 8 with two
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 struct ULds {
   uint16_t frag[kUWin][4][16][16];   // [chunk * ops + op][lane group][A row][32 bytes]
@@ -1106,13 +969,14 @@ int launch_apply(const ApplyArgs& a) {
     // t is zeroed when its slices add up atomically, W x when its two K ranges do
     pm.act[j] = act;
     pm.tv[j] = tv;
-    pm.ntv[j] = a.wl.ns <= kMaxAtomicTerms ? a.T * M.rs : 0;
+    pm.ntv[j] = a.kind != kKindBitdelta && a.wl.ns <= kMaxAtomicTerms ? a.T * M.rs : 0;
     pm.yb[j] = ybase;
     pm.nyb[j] = A.W && a.wl.nks == kMaxAtomicTerms ? a.T * A.out : 0;
     pm.cnt[j] = cnt;
     pm.ncnt[j] = M.ncnt;
     if (A.W) bm[nbm++] = BaseMat{A.W, ybase, bpt, A.out, rb}, rb += A.out / 64;
-    pm.params[j] = MatParams{tv, reinterpret_cast<float*>(wsp(M.vpt)), cnt, ybase, A.y, A.out, M.rs, M.vb, 0};
+    pm.params[j] = MatParams{tv,   reinterpret_cast<float*>(wsp(M.vpt)), cnt, ybase, A.y, bpt, A.out, M.rs, M.vb,
+                             a.wl.nks};
     vg.red0[j] = red;
     if (A.W && a.wl.nks > kMaxAtomicTerms) {
       vg.bs[j] = BaseSum{bpt, ybase, a.wl.nks, A.out, a.T};
@@ -1147,6 +1011,34 @@ int launch_apply(const ApplyArgs& a) {
 #undef DC_PREP
   mark(DC_STAGE_BASE);
   if (nbm > 0) launch_base(bm, nbm, a.x, xt, a.in, a.T, a.stream);
+  if (a.kind != kKindDeltaCoMe) {
+    BaselineLaunch b{};
+    b.kind = a.kind;
+    b.m = m;
+    b.n = a.n;
+    b.in = a.in;
+    b.T = a.T;
+    b.nact = a.wl.nact;
+    b.ns = a.wl.ns;
+    b.x = a.x;
+    b.perm = perm;
+    b.xf = xf;
+    b.xsc = xsc;
+    b.xsum = xsum;
+    b.act = act_all;
+    b.mp = mp;
+    b.vbmax = vbmax;
+    b.outmax = outmax;
+    b.nks = a.wl.nks;
+    for (int j = 0; j < m; ++j) {
+      const bool sum = a.mat[j].W && a.wl.nks > kMaxAtomicTerms;
+      b.bpt[j] = sum ? reinterpret_cast<const float*>(wsp(a.wl.mat[j].bpt)) : nullptr;
+      b.ybase[j] = reinterpret_cast<float*>(wsp(a.wl.mat[j].ybase));
+      b.out[j] = a.mat[j].out;
+    }
+    b.stream = a.stream;
+    return launch_baseline(b);
+  }
   mark(DC_STAGE_VSIDE);
   const int gx = vbmax > 0 ? vbmax * a.wl.ns : 1;
   vg.red_rows = (red + gx - 1) / gx;

@@ -23,6 +23,7 @@
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFmtFp8 = 0, kFmtFp6 = 2, kFmtFp4 = 4;
 constexpr int kScaleFp4Code = 128;   // 2^1: fp4 element q/2 -> q
@@ -107,6 +108,11 @@ __device__ __forceinline__ void hold(f32x4& d, const v8i& a0, const v8i& a1, con
 __device__ __forceinline__ void hold(f32x4& d, const v8i& a0, const v8i& a1, const v8i& a2, const v8i& b, int s0,
                                      int s1, int s2, int sb) {
   asm volatile("" : "+v"(d) : "v"(a0), "v"(a1), "v"(a2), "v"(b), "v"(s0), "v"(s1), "v"(s2), "v"(sb));
+}
+
+__device__ __forceinline__ void hold2(f32x4& d0, f32x4& d1, const v8i& a, const v8i& b0, const v8i& b1, int sa,
+                                      int sb) {
+  asm volatile("" : "+v"(d0), "+v"(d1) : "v"(a), "v"(b0), "v"(b1), "v"(sa), "v"(sb));
 }
 
 // v from lane l ^ X (X < 32) by ds_swizzle: no lane-address register, unlike
