@@ -127,6 +127,44 @@ def build_c2(layers, dev, torch, trs, synth):
     return specs, views, W, X, pool
 
 
+def build_baselines(kind, layers, n_ten, mats, budget, dev, torch, trs, synth):
+    """Resident baseline deltas for every (layer, matrix, tenant): BitDelta
+    sign bits drawn uniformly on the GPU with one scale per buffer, or
+    low-rank fp16 pairs drawn N(0, 1/64) on the GPU (finite values in every
+    byte, padding included) with sigma_i = 0.05 i^-0.8.  Returns views
+    [layer][matrix][tenant] and the pool."""
+    import numpy as np
+    BD = kind == trs.DC_KIND_BITDELTA
+    rs = [0 if BD else synth.lowrank_r(o, i, budget) for _, o, i in mats]
+    nb = [trs.dc_baseline_bytes(kind, o, i, r) for (_, o, i), r in zip(mats, rs)]
+    total = sum(nb) * n_ten * layers
+    if BD:
+        pool = random_pool(total, dev, torch)
+    else:
+        pool = torch.empty(total, dtype=torch.uint8, device=dev)
+        h = pool.view(torch.float16)
+        chunk = 1 << 28
+        for o in range(0, h.numel(), chunk):
+            n = min(chunk, h.numel() - o)
+            h[o:o + n] = torch.randn(n, device=dev, dtype=torch.float16) * (1.0 / 64)
+    views, off = [], 0
+    for l in range(layers):
+        row = []
+        for m, (_, o, i) in enumerate(mats):
+            blk = pool[off:off + nb[m] * n_ten].view(n_ten, nb[m])
+            if BD:
+                a = np.abs(np.random.default_rng(5000 + 7 * l + m).lognormal(-7.0, 0.5, n_ten)).astype(np.float32)
+                blk[:, :4] = torch.from_numpy(a.view(np.uint8).reshape(n_ten, 4)).to(dev)
+            else:
+                sg = synth.sigma_profile(rs[m])
+                blk[:, :4 * rs[m]] = torch.from_numpy(sg.view(np.uint8)).to(dev)[None, :]
+            row.append([trs.BaselineView(kind, o, i, rs[m], blk[k]) for k in range(n_ten)])
+            off += nb[m] * n_ten
+        views.append(row)
+    torch.cuda.synchronize()
+    return views, pool, rs
+
+
 def cpu_baseline(trs, synth, budget_s=12.0):
     """The oracle (plain numpy fp64, applied from packed buffers) timed on a
     bounded sample of the same workload, extrapolated to one whole step: once
@@ -401,6 +439,39 @@ def config_bench(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (args.steps * copies)
 
+    # c1: the two baselines the pages compare with (1/16 budget), the same
+    # layer copies cycled; one tenant, so every token carries id 0
+    base_legs = {}
+    if w == "c1" and not args.no_baselines:
+        zeros = torch.zeros(tmax, dtype=torch.int32, device=dev)
+        for kind, bname in ((trs.DC_KIND_BITDELTA, "bitdelta"), (trs.DC_KIND_LOWRANK, "lowrank")):
+            bv, bpool, rs = build_baselines(kind, copies, 1, mats, budget, dev, torch, trs, synth)
+            bws = torch.empty(max(trs.dc_baseline_workspace_bytes([bv[0][m][0]], 1, tmax) for m in range(len(mats))),
+                              dtype=torch.uint8, device=dev)
+            alg = sum(trs.dc_baseline_algorithmic_bytes(kind, o, i, r) for (_, o, i), r in zip(mats, rs))
+            base_legs[bname] = (bv, bpool, bws, alg, rs)
+
+    def bcall(leg, c, m, T, fused):
+        bv, _, bws, _, _ = leg
+        trs.dc_apply_baseline_multitenant(bv[c][m], W[c][m] if fused else None, X[m][:T], zeros[:T],
+                                          ys[mats[m][1]][:T], bws)
+
+    def ms_per_layer_with(fn, T, fused):
+        for _ in range(args.warmup):
+            for c in range(copies):
+                for m in range(len(mats)):
+                    fn(c, m, T, fused)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            for c in range(copies):
+                for m in range(len(mats)):
+                    fn(c, m, T, fused)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (args.steps * copies)
+
     touched = n_ten if ids_h is None else len(set(ids_h.tolist()))
     delta_bytes = touched * sum(trs.dc_algorithmic_bytes(sp) for sp in specs)
     base_bytes = sum(o * i * 2 for _, o, i in mats)
@@ -430,6 +501,20 @@ def config_bench(args):
             "bytes_per_layer": {"packed_delta": int(delta_bytes), "backbone": int(base_bytes), "x_y": int(xy)},
             "flops_per_layer": {"delta": f_delta, "backbone": f_base},
         }
+        if base_legs:
+            res["baselines"] = {}
+            for bname, leg in base_legs.items():
+                bf = ms_per_layer_with(lambda c, m, T_, f, leg=leg: bcall(leg, c, m, T_, f), T, True)
+                bd = ms_per_layer_with(lambda c, m, T_, f, leg=leg: bcall(leg, c, m, T_, f), T, False)
+                log("%s T=%d %s: fused %.4f ms/layer, delta-only %.4f ms/layer" % (w, T, bname, bf, bd))
+                res["baselines"][bname] = {
+                    "ms_per_layer": round(bf, 4), "tokens_per_s": round(T / bf * 1e3, 1),
+                    "delta_only": {"ms_per_layer": round(bd, 4),
+                                   "packed_delta_GBps": round(leg[3] / (bd * 1e-3) / 1e9, 1),
+                                   "pct_of_hbm_peak": round(100 * leg[3] / (bd * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
+                    "packed_delta_bytes_per_layer": int(leg[3]),
+                    "launch": "dc_apply_baseline_multitenant per matrix, every token id 0",
+                    "vs_deltacome_fused": round(bf / t_f, 3), "vs_deltacome_delta_only": round(bd / t_d, 3)}
         if w == "c3":
             res["mfma_utilization_vs_2.5PF_dense_bf16"] = {
                 "fused": round((f_delta + f_base) / (t_f * 1e-3) / 2.5e15, 4),
@@ -444,6 +529,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-baselines", action="store_true",
+                    help="skip the low-rank and BitDelta legs (c1, c2)")
     ap.add_argument("--pack", action="store_true",
                     help="time quantize+pack on the GPU (one layer's deltas) instead of the apply step")
     ap.add_argument("--workload", choices=("c2", "c1", "c3", "c4"), default="c2",
@@ -668,6 +755,66 @@ def main():
                        "pct_of_hbm_peak": round(100 * delta_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
         "roofline": roof,
     }
+    if not args.no_baselines:
+        # The two baselines the pages compare with (1/16 budget), through the
+        # same step structure: grouped calls, one captured graph per step.
+        del views, pool, cl, run
+        torch.cuda.empty_cache()
+        out["baselines"] = {}
+        for kind, name in ((trs.DC_KIND_BITDELTA, "bitdelta"), (trs.DC_KIND_LOWRANK, "lowrank")):
+            t0 = time.time()
+            bv, bpool, rs = build_baselines(kind, args.layers, synth.C2_TENANTS, synth.LLAMA2_7B, 16, dev, torch,
+                                            trs, synth)
+            log("%s: %.2f GB resident, built in %.1f s" % (name, bpool.numel() / 1e9, time.time() - t0))
+            bws = torch.empty(max(trs.dc_baseline_workspace_bytes([[bv[0][m][0]] * synth.C2_TENANTS for m in g],
+                                                                  len(g), T) for g in groups),
+                              dtype=torch.uint8, device=dev)
+            leg = {}
+            for mode in ("fused", "delta"):
+                calls = [trs.BaselineGroupCall([bv[l][m] for m in g], [W[l][m] for m in g] if mode == "fused"
+                                               else None, X[l][g[0]], ids, [ys[m] for m in g], bws,
+                                               stream=stream.cuda_stream)
+                         for l in range(args.layers) for g in groups]
+
+                def brun(marks=None, calls=calls):
+                    for c in calls:
+                        c()
+                for _ in range(args.warmup):
+                    brun()
+                torch.cuda.synchronize()
+                ref = outputs()
+                g_ = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g_, stream=stream):
+                    brun()
+                for _ in range(args.warmup):
+                    g_.replay()
+                torch.cuda.synchronize()
+                if not same_bits(ref, outputs()):
+                    raise RuntimeError("graph replay of the %s %s step differs from the eager step" % (name, mode))
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(args.steps):
+                    g_.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                leg[mode] = e0.elapsed_time(e1) / args.steps
+                del g_
+            alg = args.layers * len(touched) * sum(trs.dc_baseline_algorithmic_bytes(kind, o, i, r)
+                                                   for (_, o, i), r in zip(synth.LLAMA2_7B, rs))
+            out["baselines"][name] = {
+                "ms_per_step": round(leg["fused"], 4), "tokens_per_s": round(T / (leg["fused"] * 1e-3), 1),
+                "delta_only": {"ms_per_step": round(leg["delta"], 4),
+                               "tokens_per_s": round(T / (leg["delta"] * 1e-3), 1),
+                               "packed_delta_GBps": round(alg / (leg["delta"] * 1e-3) / 1e9, 1),
+                               "pct_of_hbm_peak": round(100 * alg / (leg["delta"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
+                "packed_delta_bytes_per_step": int(alg),
+                "form": ("1 sign bit per delta entry + one fp32 scale per matrix" if kind == trs.DC_KIND_BITDELTA
+                         else "fp16 top-r pairs, r = %s (q,k,v,o / gate,up / down)" % sorted(set(rs))),
+                "vs_deltacome_fused": round(leg["fused"] / ms, 3),
+                "vs_deltacome_delta_only": round(leg["delta"] / ms_d, 3)}
+            log("%s: fused %.3f ms/step, delta-only %.3f ms/step" % (name, leg["fused"], leg["delta"]))
+            del bv, bpool, bws
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(trs, synth, budget_s=8.0)
