@@ -221,6 +221,36 @@ dc_status dc_allocate_bits(int32_t r, int32_t nb, const int32_t* cost, const dou
                            int32_t* choice, double* total);
 
 /*
+ * dc_error_table -- the error table of dc_allocate_bits on the GPU
+ * (asynchronous on `stream`).  [P4] "Enhancing Delta Compression in LLMs via
+ * SVD-based Quantization Error Minimization", §2.1 eq. 5: quantizing row i of
+ * V at b bits costs about sigma_i^2 ||(V̂_i - V_i) X||^2 for calibration
+ * samples X; V̂_i is the row quantized by this library's quantizer (the one of
+ * dc_pack: 128-element groups, fp16 scale and zero) and dequantized to its
+ * fp16 values; width 0 drops the row (V̂_i = 0).
+ *   r, in    rows of V and their length (in a positive multiple of 128)
+ *   ncal     calibration samples (columns of X), >= 1
+ *   sigma    device fp32 [r]
+ *   V        device fp32 [r][in], row i = v_i, 8-byte aligned
+ *   X        device fp32 [in][ncal] (one sample per column)
+ *   widths   host int32 [nw], each 0..8; 1 <= nw <= DC_ERR_MAX_WIDTHS
+ *   err      device fp64 [r][nw], written: err[i*nw + k] for widths[k]
+ *   flag     device uint32, set to 0 by the call and to 1 if an input is
+ *            non-finite or a scale overflows fp16
+ *   ws       device workspace of ws_bytes >= dc_error_table_workspace_bytes
+ * Arithmetic: the differences V̂_i - V_i in fp32 (exact), the products with X
+ * in fp32, their squares and sums in fp64, in a fixed order.  Errors:
+ * DC_ERR_INVALID_ARG (NULL, r < 0, ncal < 1, nw or a width out of range),
+ * DC_ERR_SHAPE, DC_ERR_ALIGN, DC_ERR_BUFFER, DC_ERR_UNSUPPORTED (more than
+ * 2^31 elements in V, X or the workspace's difference rows).
+ */
+#define DC_ERR_MAX_WIDTHS 8
+size_t dc_error_table_workspace_bytes(int32_t r, int32_t in, int32_t nw);
+dc_status dc_error_table(int32_t r, int32_t in, int32_t ncal, const float* sigma, const float* V, const float* X,
+                         const int32_t* widths, int32_t nw, double* err, uint32_t* flag, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
  * dc_pack_codes -- pack already-quantized codes (host, synchronous).
  *   codes_u  host uint8 [r][out], code of u_i at row o (< 2^b of its segment)
  *   codes_v  host uint8 [r][in]

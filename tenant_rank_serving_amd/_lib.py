@@ -36,11 +36,13 @@ EXPORTS = ("dc_status_string", "dc_check_spec", "dc_packed_bytes", "dc_algorithm
            "dc_apply_multitenant_noalloc", "dc_apply_multitenant_group", "dc_group_workspace_bytes",
            "dc_apply_multitenant_group_timed", "dc_baseline_bytes", "dc_baseline_algorithmic_bytes",
            "dc_pack_lowrank", "dc_pack_bitdelta", "dc_baseline_workspace_bytes",
-           "dc_apply_baseline_multitenant", "dc_apply_baseline_multitenant_group")
+           "dc_apply_baseline_multitenant", "dc_apply_baseline_multitenant_group",
+           "dc_error_table_workspace_bytes", "dc_error_table")
+DC_ERR_MAX_WIDTHS = 8
 DC_KIND_LOWRANK, DC_KIND_BITDELTA = 1, 2
 _SIZE_FNS = ("dc_status_string", "dc_packed_bytes", "dc_algorithmic_bytes", "dc_workspace_bytes",
              "dc_group_workspace_bytes", "dc_baseline_bytes", "dc_baseline_algorithmic_bytes",
-             "dc_baseline_workspace_bytes")
+             "dc_baseline_workspace_bytes", "dc_error_table_workspace_bytes")
 STAGES = ("route", "xprep", "base", "vside", "uside")
 
 
@@ -125,6 +127,9 @@ def lib() -> ctypes.CDLL:
         L.dc_apply_baseline_multitenant.argtypes = [bp, i32, _P, _P, _P, _P, i32, _P, ctypes.c_size_t, _P]
         L.dc_apply_baseline_multitenant_group.argtypes = [bp, i32, i32, _P, _P, _P, _P, i32, _P,
                                                           ctypes.c_size_t, _P]
+        L.dc_error_table_workspace_bytes.restype = ctypes.c_size_t
+        L.dc_error_table_workspace_bytes.argtypes = [i32, i32, i32]
+        L.dc_error_table.argtypes = [i32, i32, i32, _P, _P, _P, _P, i32, _P, _P, _P, ctypes.c_size_t, _P]
         for name in EXPORTS:
             if name not in _SIZE_FNS:
                 getattr(L, name).restype = ctypes.c_int32
@@ -499,3 +504,19 @@ class BaselineGroupCall:
 
 def dc_apply_baseline_multitenant_group(views, W_base, x, tenant_ids, y, ws, T: int = None, stream=None) -> None:
     BaselineGroupCall(views, W_base, x, tenant_ids, y, ws, T, stream)()
+
+
+# ------------------------------------------------------------ error table
+def dc_error_table_workspace_bytes(r: int, inn: int, nw: int) -> int:
+    return int(lib().dc_error_table_workspace_bytes(int(r), int(inn), int(nw)))
+
+
+def dc_error_table(sigma, V, X, widths, err, flag, ws, stream=None) -> None:
+    """sigma fp32 [r], V fp32 [r][in], X fp32 [in][ncal] (device tensors);
+    err fp64 [r][len(widths)] and flag uint32/int32 [1] (device) are written."""
+    w = np.ascontiguousarray(widths, dtype=np.int32)
+    r, inn = V.shape
+    ncal = X.shape[1]
+    _check(lib().dc_error_table(int(r), int(inn), int(ncal), _dptr(sigma, "sigma"), _dptr(V, "V"), _dptr(X, "X"),
+                                w.ctypes.data, int(w.size), _dptr(err, "err"), _dptr(flag, "flag"), _dptr(ws, "ws"),
+                                ws.numel() * ws.element_size(), _stream(stream)), "dc_error_table")

@@ -368,6 +368,30 @@ dc_status dc_pack_device(const dc_spec* spec, const float* U, const float* sigma
                          static_cast<uint8_t*>(out), flag, stream) == 0 ? DC_OK : DC_ERR_HIP;
 }
 
+size_t dc_error_table_workspace_bytes(int32_t r, int32_t in, int32_t nw) {
+  if (r < 0 || in <= 0 || in % dc::kGroup || nw < 1 || nw > DC_ERR_MAX_WIDTHS) return 0;
+  return dc::round_up(4 * (size_t)r * nw * in, 256) + 256;
+}
+
+dc_status dc_error_table(int32_t r, int32_t in, int32_t ncal, const float* sigma, const float* V, const float* X,
+                         const int32_t* widths, int32_t nw, double* err, uint32_t* flag, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (r < 0 || ncal < 1 || !widths || nw < 1 || nw > DC_ERR_MAX_WIDTHS || !flag) return DC_ERR_INVALID_ARG;
+  for (int k = 0; k < nw; ++k)
+    if (widths[k] < 0 || widths[k] > 8) return DC_ERR_INVALID_ARG;
+  if (in <= 0 || in % dc::kGroup) return DC_ERR_SHAPE;
+  if (r > 0 && (!sigma || !V || !X || !err || !ws)) return DC_ERR_INVALID_ARG;
+  if (!aligned(flag, 4) || (V && !aligned(V, 8)) || (X && !aligned(X, 4)) || (sigma && !aligned(sigma, 4)) ||
+      (err && !aligned(err, 8)) || (ws && !aligned(ws, 256)))
+    return DC_ERR_ALIGN;
+  const size_t lim = (size_t)INT32_MAX;
+  if ((size_t)r * in > lim || (size_t)in * ncal > lim || (size_t)r * nw * in > lim) return DC_ERR_UNSUPPORTED;
+  if (ws_bytes < dc_error_table_workspace_bytes(r, in, nw)) return DC_ERR_BUFFER;
+  return dc::launch_error_table(r, in, ncal, sigma, V, X, widths, nw, err, flag, static_cast<float*>(ws), stream) == 0
+             ? DC_OK
+             : DC_ERR_HIP;
+}
+
 dc_status dc_dequant(const dc_delta_view* d, uint16_t* u_fp16, uint16_t* v_fp16, void* stream) {
   if (!d) return DC_ERR_INVALID_ARG;
   if (dc_check_spec(&d->spec) != DC_OK) return DC_ERR_SHAPE;

@@ -407,6 +407,10 @@ dc_status run_apply(const dc_delta_view* views, int32_t m, int32_t n, const uint
 // Device address of the scratch array on the current device (null if it
 // cannot be found); defined next to the array.
 void* scratch_ptr();
+// The error table of dc_error_table: difference rows into dv [r][nw][in],
+// then their products with X; zeroes `flag` first.
+int launch_error_table(int32_t r, int32_t in, int32_t ncal, const float* sigma, const float* V, const float* X,
+                       const int32_t* widths, int32_t nw, double* err, uint32_t* flag, float* dv, void* stream);
 int launch_pack(int32_t out, int32_t in, int32_t n8, int32_t n3, int32_t n2, const float* U, const float* sigma,
                 const float* V, uint8_t* dst, uint32_t* flag, void* stream);
 }  // namespace dc

@@ -232,6 +232,120 @@ __global__ void __launch_bounds__(256) k_quant_u(int32_t out, int32_t in, int32_
   }
 }
 
+// ------------------------------------------------------------ error table
+// "Enhancing Delta Compression in LLMs via SVD-based Quantization Error
+// Minimization", §2.1 eq. 5: quantizing row i of V at b bits costs about
+// sigma_i^2 times the squared norm of (V̂_i - V_i) X over calibration columns
+// X.  Two kernels: every (row, width) difference row V̂_i - V_i (the same
+// quantizer as the packer; width 0 = the row dropped, -V_i), then one
+// product of the stacked differences with X whose epilogue sums the squares.
+struct ErrWidths {
+  int32_t b[DC_ERR_MAX_WIDTHS];
+  int32_t nw;
+};
+
+// One wave per (row i, 128-group): the group at every width, two elements
+// per lane; dv row (i, k) holds V̂_i - V_i at width k (fp32: the fp16 value
+// minus an fp32 value within a factor two of it is exact).
+__global__ void __launch_bounds__(256) k_err_dv(int32_t r, int32_t in, const float* __restrict__ V, ErrWidths W,
+                                                float* __restrict__ dv, uint32_t* __restrict__ flag) {
+  const int lane = threadIdx.x & 63;
+  const int gi = in / kGroup;
+  const int w = (int)(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (w >= r * gi) return;
+  const int i = w / gi, grp = w % gi;
+  const float2 wv = reinterpret_cast<const float2*>(V + (size_t)i * in + (size_t)grp * kGroup)[lane];
+  for (int k = 0; k < W.nw; ++k) {
+    const int b = W.b[k];
+    float2 d = make_float2(-wv.x, -wv.y);
+    if (b > 0) {
+      GroupQ g;
+      if (quant_group(wv, b, g)) {
+        const float sc = (float)f16_to_f64((uint16_t)(g.sz & 0xFFFFu)), z = (float)f16_to_f64((uint16_t)(g.sz >> 16));
+        d.x = (float)(_Float16)(sc * ((float)g.q0 - z)) - wv.x;
+        d.y = (float)(_Float16)(sc * ((float)g.q1 - z)) - wv.y;
+      } else if (lane == 0) {
+        atomicOr(flag, 1u);
+      }
+    } else if (__ballot(!isfinite(wv.x) || !isfinite(wv.y)) && lane == 0) {
+      atomicOr(flag, 1u);
+    }
+    reinterpret_cast<float2*>(dv + ((size_t)i * W.nw + k) * in + (size_t)grp * kGroup)[lane] = d;
+  }
+}
+
+// err[row] = sigma_i^2 sum_c (sum_j dv[row][j] X[j][c])^2, row = i nw + k:
+// block = 64 rows x every column in chunks of 64; thread = 4 rows x 4
+// columns of a chunk; K in steps of 32 through LDS.  Products in fp32, the
+// squares and their sums in fp64, in a fixed order.
+constexpr int kErrRows = 64, kErrCols = 64, kErrK = 32;
+
+__global__ void __launch_bounds__(256) k_err_gemm(int32_t R, int32_t in, int32_t ncal, int32_t nw,
+                                                  const float* __restrict__ dv, const float* __restrict__ X,
+                                                  const float* __restrict__ sigma, double* __restrict__ err) {
+  __shared__ float As[kErrK][kErrRows + 4];   // [k][row]
+  __shared__ float Bs[kErrK][kErrCols + 4];   // [k][column]
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int row0 = blockIdx.x * kErrRows;
+  double ss[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int c0 = 0; c0 < ncal; c0 += kErrCols) {
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < in; k0 += kErrK) {
+      {  // A: row tid / 4, k (tid % 4) * 8 .. +8
+        const int ar = tid >> 2, ak = (tid & 3) * 8;
+        float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+        if (row0 + ar < R) {
+          const float4* src = reinterpret_cast<const float4*>(dv + (size_t)(row0 + ar) * in + k0 + ak);
+          a0 = src[0];
+          a1 = src[1];
+        }
+        As[ak + 0][ar] = a0.x; As[ak + 1][ar] = a0.y; As[ak + 2][ar] = a0.z; As[ak + 3][ar] = a0.w;
+        As[ak + 4][ar] = a1.x; As[ak + 5][ar] = a1.y; As[ak + 6][ar] = a1.z; As[ak + 7][ar] = a1.w;
+      }
+      {  // B: k tid / 8, columns (tid % 8) * 8 .. +8
+        const int bk = tid >> 3, bc = (tid & 7) * 8;
+        const float* src = X + (size_t)(k0 + bk) * ncal + c0 + bc;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Bs[bk][bc + j] = c0 + bc + j < ncal ? src[j] : 0.f;
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int kk = 0; kk < kErrK; ++kk) {
+        float a[4], b[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          a[q] = As[kk][4 * ty + q];
+          b[q] = Bs[kk][4 * tx + q];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[q][c] = fmaf(a[q], b[c], acc[q][c]);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ss[q] += (double)acc[q][c] * (double)acc[q][c];   // columns past ncal are 0
+  }
+  // sum over the 16 threads of a row group (consecutive lanes), in a fixed order
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) ss[q] += __shfl_xor(ss[q], d, 64);
+  if (tx == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = row0 + 4 * ty + q;
+      if (row < R) {
+        const double sg = (double)sigma[row / nw];
+        err[row] = sg * sg * ss[q];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 int launch_pack(int32_t out, int32_t in, int32_t n8, int32_t n3, int32_t n2, const float* U, const float* sigma,
@@ -254,6 +368,23 @@ int launch_pack(int32_t out, int32_t in, int32_t n8, int32_t n3, int32_t n2, con
   if (wu > 0)
     hipLaunchKernelGGL(k_quant_u, dim3((unsigned)((wu + 3) / 4)), dim3(256), 0, st, out, in, n8, n3, n2, L, U, dst,
                        flag);
+  return (int)hipGetLastError();
+}
+
+int launch_error_table(int32_t r, int32_t in, int32_t ncal, const float* sigma, const float* V, const float* X,
+                       const int32_t* widths, int32_t nw, double* err, uint32_t* flag, float* dv, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  ErrWidths W{};
+  for (int k = 0; k < nw; ++k) W.b[k] = widths[k];
+  W.nw = nw;
+  hipLaunchKernelGGL(k_pack_zero, dim3(1), dim3(256), 0, st, reinterpret_cast<uint32_t*>(err), (size_t)0, flag);
+  const int64_t waves = (int64_t)r * (in / kGroup);
+  if (waves > 0) {
+    hipLaunchKernelGGL(k_err_dv, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, r, in, V, W, dv, flag);
+    const int32_t R = r * nw;
+    hipLaunchKernelGGL(k_err_gemm, dim3((unsigned)((R + kErrRows - 1) / kErrRows)), dim3(256), 0, st, R, in, ncal, nw,
+                       dv, X, sigma, err);
+  }
   return (int)hipGetLastError();
 }
 

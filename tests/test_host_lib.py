@@ -366,3 +366,28 @@ def test_group_workspace_and_argument_checks(L):
     assert grp(arr, 2, 2, W2, X, IDS, (P * 2)(Y, Y + 0x100000), 0, WS, need, None) == trs.DC_OK    # T = 0
     bad = (trs._lib.dc_delta_view * 4)(_view(sq), _view(sq), _view((128, 256, 1, 3, 9)), _view((128, 256, 1, 3, 9)))
     assert grp(bad, 2, 2, W2, X, IDS, (P * 2)(Y, Y + 0x100000), 8, WS, need, None) == trs.DC_ERR_SHAPE
+
+
+def test_error_table_argument_checks(L):
+    """dc_error_table rejects bad arguments on the host before any launch."""
+    w = np.array([0, 2, 3, 8], np.int32)
+    r, inn, ncal = 16, 256, 8
+    need = trs.dc_error_table_workspace_bytes(r, inn, 4)
+    assert need >= 4 * r * 4 * inn
+    assert trs.dc_error_table_workspace_bytes(r, 200, 4) == 0
+    assert trs.dc_error_table_workspace_bytes(r, inn, 9) == 0
+    et = L.dc_error_table
+    S, V, Xc, E, F = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    wp = w.ctypes.data
+    assert et(r, inn, ncal, S, V, Xc, wp, 4, E, F, WS, need - 1, None) == trs.DC_ERR_BUFFER
+    assert et(r, 200, ncal, S, V, Xc, wp, 4, E, F, WS, need, None) == trs.DC_ERR_SHAPE
+    assert et(r, inn, 0, S, V, Xc, wp, 4, E, F, WS, need, None) == trs.DC_ERR_INVALID_ARG
+    assert et(r, inn, ncal, S, V, Xc, wp, 0, E, F, WS, need, None) == trs.DC_ERR_INVALID_ARG
+    assert et(r, inn, ncal, S, V, Xc, wp, 9, E, F, WS, need, None) == trs.DC_ERR_INVALID_ARG
+    bad = np.array([0, 9], np.int32)
+    assert et(r, inn, ncal, S, V, Xc, bad.ctypes.data, 2, E, F, WS, need, None) == trs.DC_ERR_INVALID_ARG
+    assert et(r, inn, ncal, None, V, Xc, wp, 4, E, F, WS, need, None) == trs.DC_ERR_INVALID_ARG
+    assert et(r, inn, ncal, S, V, Xc, wp, 4, E, None, WS, need, None) == trs.DC_ERR_INVALID_ARG
+    assert et(r, inn, ncal, S, V + 4, Xc, wp, 4, E, F, WS, need, None) == trs.DC_ERR_ALIGN
+    assert et(r, inn, ncal, S, V, Xc, wp, 4, E + 4, F, WS, need, None) == trs.DC_ERR_ALIGN
+    assert et(-1, inn, ncal, S, V, Xc, wp, 4, E, F, WS, need, None) == trs.DC_ERR_INVALID_ARG
