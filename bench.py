@@ -353,6 +353,35 @@ def pack_bench(args):
                          "sample": "numpy quantizer + packer on the q matrix (%.1f s), scaled by its share of the "
                                    "layer's input bytes" % t_orc},
     }
+    # the eq. 5 error table of the bit allocation for the q matrix's 4096 candidate rows (a full-rank V),
+    # widths 0/2/3/8, 128 calibration samples
+    from oracle import alloc
+    r, inn, ncal, widths = 4096, 4096, 128, (0, 2, 3, 8)
+    Vf = torch.randn(r, inn, device=dev) / 64.0
+    sf = torch.rand(r, device=dev) + 0.5
+    Xc = torch.randn(inn, ncal, device=dev)
+    ews = torch.empty(trs.dc_error_table_workspace_bytes(r, inn, len(widths)), dtype=torch.uint8, device=dev)
+    err = torch.empty((r, len(widths)), dtype=torch.float64, device=dev)
+    for _ in range(args.warmup + 1):
+        trs.dc_error_table(sf, Vf, Xc, widths, err, flag, ews)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        trs.dc_error_table(sf, Vf, Xc, widths, err, flag, ews)
+    e1.record()
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    ms_e = e0.elapsed_time(e1) / args.steps
+    flops = 2.0 * r * len(widths) * inn * ncal
+    nrow = 32
+    t0 = time.perf_counter()
+    alloc.error_table(sf[:nrow].double().cpu().numpy(), Vf[:nrow].cpu().numpy(), Xc.double().cpu().numpy(), widths)
+    t_orc_e = time.perf_counter() - t0
+    line["error_table"] = {
+        "workload": "dc_error_table, %d rows x %d inputs, widths %s, %d calibration samples" % (r, inn, list(widths), ncal),
+        "ms": round(ms_e, 4), "product_TFLOPs_fp32": round(flops / (ms_e * 1e-3) / 1e12, 2),
+        "oracle_ms_scaled": round(t_orc_e * r / nrow * 1e3, 1),
+        "oracle_sample": "alloc.error_table on %d rows (%.2f s), scaled to %d rows" % (nrow, t_orc_e, r)}
     print(json.dumps(line), flush=True)
 
 

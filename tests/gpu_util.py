@@ -191,3 +191,17 @@ def check_multitenant(y, w, x, ids, ds, out, what, rows=None):
         r = oap.apply_multitenant(w, x, ids, ts) if w is not None else delta_only_mt(x, ids, ts, out)
         refs.append(r if rows is None else r[rows])
     return check_close(y if rows is None else y[rows], refs[0], what=what, ref_exact=refs[1])
+
+
+def error_table_gpu(sigma, V, X, widths=(0, 2, 3, 8)):
+    """dc_error_table on the GPU: (err fp64 [r][len(widths)], flag)."""
+    t = torch()
+    r, inn = np.asarray(V).shape
+    ws = t.empty(trs.dc_error_table_workspace_bytes(r, inn, len(widths)), dtype=t.uint8, device="cuda")
+    err = t.empty((r, len(widths)), dtype=t.float64, device="cuda")
+    flag = t.full((1,), 7, dtype=t.int32, device="cuda")
+    trs.dc_error_table(t.from_numpy(np.ascontiguousarray(sigma, np.float32)).cuda(),
+                       t.from_numpy(np.ascontiguousarray(V, np.float32)).cuda(),
+                       t.from_numpy(np.ascontiguousarray(X, np.float32)).cuda(), widths, err, flag, ws)
+    t.cuda.synchronize()
+    return err.cpu().numpy(), int(flag.item())

@@ -7,7 +7,7 @@ import pytest
 import synth
 import tenant_rank_serving_amd as trs
 from oracle import alloc
-from gpu_util import note, torch
+from gpu_util import error_table_gpu, note, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -18,16 +18,7 @@ RTOL = 1e-4
 
 
 def _gpu_table(sigma, V, X, widths=WIDTHS):
-    t = torch()
-    r, inn = V.shape
-    ws = t.empty(trs.dc_error_table_workspace_bytes(r, inn, len(widths)), dtype=t.uint8, device="cuda")
-    err = t.empty((r, len(widths)), dtype=t.float64, device="cuda")
-    flag = t.full((1,), 7, dtype=t.int32, device="cuda")
-    trs.dc_error_table(t.from_numpy(np.ascontiguousarray(sigma, np.float32)).cuda(),
-                       t.from_numpy(np.ascontiguousarray(V, np.float32)).cuda(),
-                       t.from_numpy(np.ascontiguousarray(X, np.float32)).cuda(), widths, err, flag, ws)
-    t.cuda.synchronize()
-    return err.cpu().numpy(), int(flag.item())
+    return error_table_gpu(sigma, V, X, widths)
 
 
 # (seed, r, in, ncal): ragged row blocks (37, 70 rows x 4 widths), a calibration count that is not a

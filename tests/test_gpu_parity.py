@@ -12,7 +12,7 @@ import tenant_rank_serving_amd as trs
 from oracle import apply as oap
 from oracle import quant
 from gpu_util import (TOL, check_close, check_factored, check_multitenant, delta_only_mt, dev_i32, dev_u16,
-                      note, oracle_tenant, run_decode, torch, upload, workspace, y_to_f64)
+                      error_table_gpu, note, oracle_tenant, run_decode, torch, upload, workspace, y_to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -145,10 +145,12 @@ def test_c0_end_to_end():
 
 
 def test_allocated_tenants_end_to_end():
-    """Bit allocation by dc_allocate_bits (eq. 5 errors, exact program) for
-    three tenants with different spectra and calibration sets: each gets its
-    own (n8, n3, n2), its pairs are ordered by width, packed on the host and
-    applied in one multi-tenant call on the GPU, against the oracle."""
+    """Bit allocation for three tenants with different spectra and
+    calibration sets: the eq. 5 error table from the library on the GPU
+    (dc_error_table, checked against the oracle's table), the exact program
+    (dc_allocate_bits), so each tenant gets its own (n8, n3, n2); its pairs
+    are ordered by width, packed on the host and applied in one multi-tenant
+    call on the GPU, against the oracle."""
     note("allocated tenants")
     from oracle import alloc
     t = torch()
@@ -161,7 +163,13 @@ def test_allocated_tenants_end_to_end():
         b = np.linalg.qr(rng.standard_normal((inn, inn)))[0]
         delta = (a * np.arange(1, out + 1) ** -p) @ b.T * 0.05
         u, s, v = quant.svd_pairs(delta)
-        err = alloc.error_table(s, v, rng.standard_normal((inn, 16)) * (1 + k))
+        xc = (rng.standard_normal((inn, 16)) * (1 + k)).astype(np.float32)
+        s32_, v32_ = s.astype(np.float32), v.astype(np.float32)
+        err, eflag = error_table_gpu(s32_, v32_, xc, alloc.WIDTHS)
+        ref = alloc.error_table(s32_.astype(np.float64), v32_, xc.astype(np.float64))
+        assert eflag == 0
+        nz = ref > 0
+        assert np.all(err[~nz] == 0) and (np.abs(err[nz] - ref[nz]) / ref[nz]).max() <= 1e-4
         choice, _ = trs.dc_allocate_bits(err, list(alloc.WIDTHS), budget)
         (n8, n3, n2), order = alloc.counts_and_order(choice, alloc.WIDTHS, s)
         counts.append((n8, n3, n2))
