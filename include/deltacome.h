@@ -414,18 +414,20 @@ dc_status dc_apply_multitenant_noalloc(const dc_delta_view* views, int32_t n, co
  *   x, y         device bf16 [T][in], [T][out]
  * Same conventions as dc_apply_multitenant (the status word at byte 0 of ws
  * is cleared).  When every non-empty segment has at least 256 tokens and the
- * workspace holds the dense operands, the call takes a dense form: per
- * tenant, the dequantized fp16 pairs are written once into the workspace as
- * bf16 hi + lo operands (an exact split), then t = sigma (V x) and
- * y = W x + U t run as matrix-core products over the segment (fp32 sums; t
- * carried as bf16 hi + lo, about 16 significant bits).  Its sums are in a
- * fixed order (no atomics): repeated calls give the same bits.  Otherwise
- * the call takes the decode kernels of dc_apply_multitenant.  The workspace
- * for DC_OP_PREFILL (dc_workspace_bytes) includes the dense operands when
- * T >= 256: min(n, 8) x (bf16 [rp][2 in] + [out][3 rp]) + bf16 [T][3 rp],
- * rp = the largest tenant rank rounded up to 128; the products of up to 8
- * tenants run in one launch.  A workspace of the DC_OP_MULTITENANT size is
- * also accepted (no dense form).
+ * workspace holds the dense form's buffers, the call takes a dense form: per
+ * tenant, t = sigma (V x) and y = W x + U t run as tiled matrix-core products
+ * over the segment whose V and U operand tiles are dequantized from the
+ * packed codes in registers (the fp16 values fp16(s (q - z)), exactly), x
+ * entering as fp16 after a power-of-two rescale per token (exact for bf16
+ * values within 2^24 of the token's largest) and t as fp16 hi + lo after a
+ * power-of-two rescale per token (about 22 significant bits); fp32 sums in a
+ * fixed order, so repeated calls give the same bits.  The products of up to 8
+ * tenants run in one launch.  Otherwise the call takes the decode kernels of
+ * dc_apply_multitenant.  The workspace for DC_OP_PREFILL (dc_workspace_bytes)
+ * includes the dense form's buffers when T >= 256: fp32 t [T][rp] and 8 bytes
+ * per token, rp = max over tenants of pad32(n8) + pad32(n3) + pad32(n2)
+ * rounded up to 128 (at least 128).  A workspace of the DC_OP_MULTITENANT
+ * size is also accepted (no dense form).
  * Weights: the dense form multiplies by the fp16 dequantized values
  * fp16(s (q - z)); the decode kernels multiply 8-bit pairs by the same fp16
  * values but 3- and 2-bit pairs by the exact grid values s (q - z), within

@@ -17,7 +17,7 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 // Checks the tenant specs of one matrix of a call; fills its shape and the
 // work-split maxima.
 struct Dims {
-  int32_t out, in, rmax, tw, vb;
+  int32_t out, in, rmax, tw, vb, prp;   // prp: padded rank rows of the dense prefill form
 };
 
 dc_status check_specs(const dc_spec* specs, int32_t n, Dims* d) {
@@ -25,7 +25,7 @@ dc_status check_specs(const dc_spec* specs, int32_t n, Dims* d) {
   if (n > DC_MAX_TENANTS) return DC_ERR_UNSUPPORTED;
   d->out = specs[0].out;
   d->in = specs[0].in;
-  d->rmax = d->tw = d->vb = 0;
+  d->rmax = d->tw = d->vb = d->prp = 0;
   for (int k = 0; k < n; ++k) {
     if (dc_check_spec(&specs[k]) != DC_OK) return DC_ERR_SHAPE;
     if (specs[k].out != d->out || specs[k].in != d->in) return DC_ERR_SHAPE;
@@ -35,6 +35,8 @@ dc_status check_specs(const dc_spec* specs, int32_t n, Dims* d) {
     if (vb > d->vb) d->vb = vb;
     const int32_t tw = dc::t_width(specs[k].n8, specs[k].n3, specs[k].n2);
     if (tw > d->tw) d->tw = tw;
+    const int32_t prp = dc::pf_rank_pad(specs[k].n8, specs[k].n3, specs[k].n2);
+    if (prp > d->prp) d->prp = prp;
   }
   return DC_OK;
 }
@@ -153,7 +155,7 @@ dc_status run_apply(const dc_delta_view* views, int32_t m, int32_t n, const uint
     // the dense prefill operands, when the workspace holds them; without them
     // the call takes the decode kernels
     dc::WsLayout wd{};
-    layout_of_group(dm, 1, n, T, dc::dense_rank_pad(dm[0].rmax), &wd);
+    layout_of_group(dm, 1, n, T, dm[0].prp, &wd);
     if (ws_bytes >= wd.total) wl = wd;
   }
   // the kernels address t, the backbone product and each packed buffer with 32-bit byte offsets
@@ -271,7 +273,7 @@ size_t dc_workspace_bytes(int32_t op, const dc_spec* specs, int32_t n, int32_t T
   Dims dm;
   if (check_specs(specs, n, &dm) != DC_OK) return 0;
   dc::WsLayout wl{};
-  if (!layout_of_group(&dm, 1, n, T, op == DC_OP_PREFILL && T >= dc::kDenseMin ? dc::dense_rank_pad(dm.rmax) : 0,
+  if (!layout_of_group(&dm, 1, n, T, op == DC_OP_PREFILL && T >= dc::kDenseMin ? dm.prp : 0,
                        &wl))
     return 0;
   return wl.total;

@@ -263,13 +263,12 @@ struct WsLayout {
   size_t act;     // ActEntry [m][nact] work items of the buckets with tokens, in bucket order, per matrix
   size_t params;  // MatParams [m]
   WsMat mat[kMaxGroup];
-  size_t dav;     // prefill, dense form: dnb slots of bf16 [drp][2 in] V operand (hi, lo)
-  size_t dau;     // dnb slots of bf16 [out][3 drp] U operand (hi, hi, lo)
-  size_t dtb;     // bf16 [T][3 drp] t of one segment (hi, lo, hi)
+  size_t dt;      // prefill, dense form: fp32 t [T][drp] (padded ranks, segment by segment)
+  size_t dxs;     // fp32 [T] power-of-two rescale of each token's x
+  size_t dtm;     // uint32 [T] bits of each token's largest |t|
   size_t total;
   int32_t m;      // matrices of the group
-  int32_t drp;    // rank rows of the dense operands (0: no dense region)
-  int32_t dnb;    // operand slots: tenants whose dense products share one launch
+  int32_t drp;    // padded rank rows of the dense form's t (0: no dense region)
   int32_t ns;     // V-side input slices
   int32_t nks;    // K ranges of the split backbone product (0: tiled product)
   int32_t nact;   // work-item capacity of each act list
@@ -315,10 +314,9 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t n, int32_t m, const int32_t
     M.cnt = take(4 * (size_t)M.ncnt);
   }
   W->drp = drp;
-  W->dnb = drp > 0 ? (n < 8 ? n : 8) : 0;
-  W->dav = take(2 * (size_t)W->dnb * drp * 2 * in);
-  W->dau = take(2 * (size_t)W->dnb * out[0] * 3 * drp);
-  W->dtb = take(2 * (size_t)T * 3 * drp);
+  W->dt = take(drp > 0 ? 4 * (size_t)T * drp : 0);
+  W->dxs = take(drp > 0 ? 4 * (size_t)T : 0);
+  W->dtm = take(drp > 0 ? 4 * (size_t)T : 0);
   W->total = round_up(o, kAlign);
   return true;
 }
@@ -390,12 +388,17 @@ struct BaseMat {
 };
 // The tiled product (T > 256) covers one matrix (m == 1).
 int launch_base(const BaseMat* mats, int m, const uint16_t* x, const uint16_t* xt, int in, int T, void* stream);
-// Rank rows of the dense prefill operands of a tenant with r pairs (r rounded
-// up to whole 128-row tiles, at least one tile).
-int dense_rank_pad(int r);
-// Prefill with long segments: backbone product, then per segment the
-// tenant's operands and two dense products (see kernels.hip).
+// Padded rank rows of a tenant in the dense prefill form: each rank group
+// rounded up to 32 (whole K-blocks), the sum to whole 128-row tiles (at
+// least one tile).
+int pf_rank_pad(int n8, int n3, int n2);
+constexpr int kPfBatch = 8;   // tenants whose dense products share one launch
+// Prefill with long segments: backbone product, then per batch of tenants
+// the two products with their operands dequantized in registers
+// (k_prefill.hip).
 int launch_dense_prefill(const ApplyArgs& a);
+// The tiled backbone product (any T): ybase [T][out] = x W^T.
+int launch_tiled_base(const uint16_t* W, const uint16_t* x, float* ybase, int out, int in, int T, void* stream);
 int launch_dequant(const Tenant& t, int32_t out, int32_t in, uint16_t* u16, uint16_t* v16, void* stream);
 // The checks and launches of every apply entry point.  ws_limit > 0: the
 // workspace is the library's scratch array of that many bytes (ws and

@@ -91,12 +91,8 @@ constexpr int kGK = 64;                 // K per stage
 constexpr int kGPad = kGK * 2 + 16;     // LDS row stride, bytes
 constexpr int kGGroup = 8;              // row tiles per group
 
-// One product C[n][m] = sum_k A[m][k] B[n][k mod kb] with its epilogue:
-//   EPI 0: c32[n][m] = C (fp32, row stride ldc);
-//   EPI 1: t = sigma_m C (0 for m >= r), split t = hi + lo in bf16, written
-//          as tb[n][m] = hi, tb[n][M + m] = lo, tb[n][2M + m] = hi (ldc = 3M);
-//   EPI 2: y[n][m] = bf16(C + ybase[n][m]) (ybase may be null).
-// A is [M][K] row-major (M a multiple of 128, K of 64), B [N][ldb].
+// One product c32[n][m] = sum_k A[m][k] B[n][k mod kb] (fp32, row stride
+// ldc); A is [M][K] row-major (M a multiple of 128, K of 64), B [N][ldb].
 constexpr int kGBatch = 8;
 
 struct GemmOp {
@@ -104,11 +100,6 @@ struct GemmOp {
   const uint16_t* B;
   int32_t M, N, K, ldb, kb, ldc;
   float* c32;
-  const float* sigma;
-  int32_t r;
-  uint16_t* tb;
-  const float* ybase;
-  uint16_t* y;
 };
 
 // Up to kGBatch independent products per launch (blockIdx.y selects one;
@@ -117,7 +108,6 @@ struct GemmBatch {
   GemmOp op[kGBatch];
 };
 
-template <int EPI>
 __global__ void __launch_bounds__(256, 2) k_gemm(GemmBatch gb) {
   const GemmOp& op = gb.op[blockIdx.y];
   const uint16_t* __restrict__ W = op.A;
@@ -207,33 +197,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmBatch gb) {
     for (int i = 0; i < 4; ++i) {
       const int m = o0 + 64 * wo + 16 * i + 4 * (lane >> 4);   // rows m .. m+3 of this lane
       const f32x4 c = acc[i][j];
-      if constexpr (EPI == 0) {
-        *reinterpret_cast<f32x4*>(op.c32 + (size_t)tok * op.ldc + m) = c;
-      } else if constexpr (EPI == 1) {
-        uint32_t hi[2], lo[2];
-#pragma unroll
-        for (int q = 0; q < 4; q += 2) {
-          uint16_t h[2], l[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const float t = c[q + e] * (m + q + e < op.r ? op.sigma[m + q + e] : 0.f);
-            h[e] = f32_to_bf16(t);
-            l[e] = f32_to_bf16(t - bf16_to_f32(h[e]));
-          }
-          hi[q / 2] = h[0] | ((uint32_t)h[1] << 16);
-          lo[q / 2] = l[0] | ((uint32_t)l[1] << 16);
-        }
-        uint16_t* row = op.tb + (size_t)tok * op.ldc + m;
-        *reinterpret_cast<uint2*>(row) = make_uint2(hi[0], hi[1]);
-        *reinterpret_cast<uint2*>(row + out) = make_uint2(lo[0], lo[1]);
-        *reinterpret_cast<uint2*>(row + 2 * out) = make_uint2(hi[0], hi[1]);
-      } else {
-        f32x4 v = c;
-        if (op.ybase) v += *reinterpret_cast<const f32x4*>(op.ybase + (size_t)tok * op.ldc + m);
-        const uint32_t p0 = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        const uint32_t p1 = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *reinterpret_cast<uint2*>(op.y + (size_t)tok * op.ldc + m) = make_uint2(p0, p1);
-      }
+      *reinterpret_cast<f32x4*>(op.c32 + (size_t)tok * op.ldc + m) = c;
     }
   }
 }
@@ -404,61 +368,6 @@ __global__ void __launch_bounds__(256) k_dequant(Tenant tn, int32_t out, int32_t
   (is_v ? v16 : u16)[(size_t)i * len + pos] = h;
 }
 
-// Operands of the dense prefill products of one tenant, from its packed codes:
-// av [rp][2 in] (row i: the hi parts of V_i, then its lo parts) and
-// au [out][3 rp] (row o: the hi parts of U_:o, the hi parts again, the lo
-// parts), bf16.  hi = bf16(v) and lo = v - hi for the fp16 value v, exactly
-// (fp16 keeps 11 significant bits, bf16 8, so the remainder has at most 3).
-// Rows of av and columns of au past r are zero.  One block row per rank (V)
-// or output (U), threads along the packed order; the three rank groups'
-// records come from the host.
-struct DenseSegs {
-  SegInfo s[3];   // 8-, 3- and 2-bit groups
-};
-
-__device__ __forceinline__ SegInfo dense_seg(const DenseSegs& d, int i) {
-  return i < d.s[1].lo ? d.s[0] : (i < d.s[2].lo ? d.s[1] : d.s[2]);
-}
-
-__device__ __forceinline__ uint32_t hi_lo(float v) {   // bf16 hi in the low half, lo in the high half
-  const uint16_t hi = f32_to_bf16(v);
-  return hi | ((uint32_t)f32_to_bf16(v - bf16_to_f32(hi)) << 16);
-}
-
-constexpr int kDenseURows = 8;   // output rows per block of k_dense_u
-
-__global__ void __launch_bounds__(256) k_dense_v(DenseSegs d, int32_t r, int32_t in, uint16_t* __restrict__ av,
-                                                 uint32_t* __restrict__ flags) {
-  const int i = blockIdx.y, pos = 2 * (blockIdx.x * 256 + threadIdx.x);   // two adjacent elements
-  // the call's status word (no invalid id can occur in a prefill call)
-  if (flags && i == 0 && blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
-  if (pos >= in) return;
-  uint32_t h0 = 0, h1 = 0;
-  if (i < r) {
-    const SegInfo sg = dense_seg(d, i);
-    h0 = hi_lo((float)(_Float16)dq_seg(sg, true, i, pos, in));
-    h1 = hi_lo((float)(_Float16)dq_seg(sg, true, i, pos + 1, in));
-  }
-  uint16_t* row = av + (size_t)i * 2 * in;
-  *reinterpret_cast<uint32_t*>(row + pos) = (h0 & 0xFFFFu) | (h1 << 16);
-  *reinterpret_cast<uint32_t*>(row + in + pos) = (h0 >> 16) | (h1 & 0xFFFF0000u);
-}
-
-__global__ void __launch_bounds__(128) k_dense_u(DenseSegs d, int32_t r, int32_t rp, int32_t in,
-                                                 uint16_t* __restrict__ au) {
-  const int i = blockIdx.x * 128 + threadIdx.x;   // rp is a multiple of 128
-  const bool live = i < r;
-  const SegInfo sg = dense_seg(d, live ? i : 0);
-  for (int j = 0; j < kDenseURows; ++j) {
-    const int o = blockIdx.y * kDenseURows + j;      // out is a multiple of 128
-    const uint32_t hl = live ? hi_lo((float)(_Float16)dq_seg(sg, false, i, o, in)) : 0u;
-    uint16_t* row = au + (size_t)o * 3 * rp;
-    row[i] = (uint16_t)hl;
-    row[rp + i] = (uint16_t)hl;
-    row[2 * rp + i] = (uint16_t)(hl >> 16);
-  }
-}
-
 }  // namespace
 
 int launch_base(const BaseMat* mats, int m, const uint16_t* x, const uint16_t* xt, int in, int T, void* stream) {
@@ -475,106 +384,25 @@ int launch_base(const BaseMat* mats, int m, const uint16_t* x, const uint16_t* x
     const dim3 g((unsigned)rows, (unsigned)nks, (unsigned)((T + 63) / 64));
     hipLaunchKernelGGL(k_base_sk, g, dim3(256), 0, st, bms, xt, in, T, nks);
   } else {
-    const uint16_t* W = mats[0].W;
-    float* ybase = mats[0].ybase;
-    const int out = mats[0].out;
-    GemmOp op{};
-    op.A = W;
-    op.B = x;
-    op.M = out;
-    op.N = T;
-    op.K = in;
-    op.ldb = in;
-    op.kb = in;
-    op.ldc = out;
-    op.c32 = ybase;
-    GemmBatch gb{};
-    gb.op[0] = op;
-    hipLaunchKernelGGL(k_gemm<0>, dim3(gemm_tiles(out, T)), dim3(256), 0, st, gb);
+    return launch_tiled_base(mats[0].W, x, mats[0].ybase, mats[0].out, in, T, stream);
   }
   return (int)hipGetLastError();
 }
 
-int dense_rank_pad(int r) { return r > 0 ? (int)round_up((size_t)r, kGT) : kGT; }
-
-int launch_dense_prefill(const ApplyArgs& a) {
-  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-  const MatArgs& A = a.mat[0];   // a prefill call has one matrix
-  float* ybase = A.W ? reinterpret_cast<float*>(a.ws + a.wl.mat[0].ybase) : nullptr;
-  uint16_t* av0 = reinterpret_cast<uint16_t*>(a.ws + a.wl.dav);
-  uint16_t* au0 = reinterpret_cast<uint16_t*>(a.ws + a.wl.dau);
-  uint16_t* tb0 = reinterpret_cast<uint16_t*>(a.ws + a.wl.dtb);
-  const size_t av_slot = (size_t)a.wl.drp * 2 * a.in, au_slot = (size_t)A.out * 3 * a.wl.drp;
-  uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + a.wl.flags);
-  if (A.W) {
-    GemmBatch gb{};
-    GemmOp& op = gb.op[0];
-    op.A = A.W;
-    op.B = a.x;
-    op.M = A.out;
-    op.N = a.T;
-    op.K = a.in;
-    op.ldb = a.in;
-    op.kb = a.in;
-    op.ldc = A.out;
-    op.c32 = ybase;
-    hipLaunchKernelGGL(k_gemm<0>, dim3(gemm_tiles(A.out, a.T)), dim3(256), 0, st, gb);
-  }
-  // tenants with tokens, in batches of up to a.wl.dnb (<= kGBatch) operand slots
-  int k = 0;
-  while (k < a.n) {
-    GemmBatch gv{}, gu{};
-    int cnt = 0;
-    unsigned tv = 0, tu = 0;
-    for (; k < a.n && cnt < a.wl.dnb; ++k) {
-      const int s0 = a.seg[k], nt = a.seg[k + 1] - a.seg[k];
-      if (nt == 0) continue;
-      const Tenant& tn = A.tenants->t[k];
-      const int r = tn.n8 + tn.n3 + tn.n2, rp = dense_rank_pad(r);
-      uint16_t* av = av0 + cnt * av_slot;
-      uint16_t* au = au0 + cnt * au_slot;
-      uint16_t* tb = tb0 + (size_t)s0 * 3 * a.wl.drp;   // segments are disjoint token ranges
-      Layout L;
-      layout_of(A.out, a.in, tn.n8, tn.n3, tn.n2, &L);
-      DenseSegs ds;
-      for (int w = 0; w < 3; ++w) ds.s[w] = seg_info(tn, L, w);
-      hipLaunchKernelGGL(k_dense_v, dim3((unsigned)((a.in + 511) / 512), (unsigned)rp), dim3(256), 0, st, ds, r, a.in,
-                         av, flags);
-      flags = nullptr;   // cleared by the first launch
-      hipLaunchKernelGGL(k_dense_u, dim3((unsigned)(rp / 128), (unsigned)(A.out / kDenseURows)), dim3(128), 0, st, ds,
-                         r, rp, a.in, au);
-      GemmOp& v = gv.op[cnt];   // t = sigma (V x) for the segment's tokens
-      v.A = av;
-      v.B = a.x + (size_t)s0 * a.in;
-      v.M = rp;
-      v.N = nt;
-      v.K = 2 * a.in;
-      v.ldb = a.in;
-      v.kb = a.in;
-      v.ldc = 3 * rp;
-      v.sigma = r > 0 ? reinterpret_cast<const float*>(tn.base + L.off[DC_REG_SIGMA]) : nullptr;
-      v.r = r;
-      v.tb = tb;
-      GemmOp& u = gu.op[cnt];   // y = W x + U t, rounded once
-      u.A = au;
-      u.B = tb;
-      u.M = A.out;
-      u.N = nt;
-      u.K = 3 * rp;
-      u.ldb = 3 * rp;
-      u.kb = 3 * rp;
-      u.ldc = A.out;
-      u.ybase = ybase ? ybase + (size_t)s0 * A.out : nullptr;
-      u.y = A.y + (size_t)s0 * A.out;
-      tv = max(tv, gemm_tiles(rp, nt));
-      tu = max(tu, gemm_tiles(A.out, nt));
-      ++cnt;
-    }
-    if (cnt == 0) break;
-    // grid x a multiple of 8, so that blockIdx.x mod 8 is the XCD the tile numbering assumes
-    hipLaunchKernelGGL(k_gemm<1>, dim3((tv + 7) / 8 * 8, (unsigned)cnt), dim3(256), 0, st, gv);
-    hipLaunchKernelGGL(k_gemm<2>, dim3((tu + 7) / 8 * 8, (unsigned)cnt), dim3(256), 0, st, gu);
-  }
+int launch_tiled_base(const uint16_t* W, const uint16_t* x, float* ybase, int out, int in, int T, void* stream) {
+  GemmOp op{};
+  op.A = W;
+  op.B = x;
+  op.M = out;
+  op.N = T;
+  op.K = in;
+  op.ldb = in;
+  op.kb = in;
+  op.ldc = out;
+  op.c32 = ybase;
+  GemmBatch gb{};
+  gb.op[0] = op;
+  hipLaunchKernelGGL(k_gemm, dim3(gemm_tiles(out, T)), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), gb);
   return (int)hipGetLastError();
 }
 

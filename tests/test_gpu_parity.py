@@ -565,11 +565,12 @@ def test_prefill_small_segments():
 
 
 def test_prefill_dense_segments():
-    """Segments of at least 256 tokens take the dense form (each tenant's
-    pairs dequantized once into bf16 hi + lo operands, then matrix-core
-    products over the segment): mixed ranks, an empty delta (r = 0: W x
-    only), an empty segment, ragged token tiles; fused and delta-only
-    against the oracle, and two calls give the same bits."""
+    """Segments of at least 256 tokens take the dense form (matrix-core
+    products over the segment whose operand tiles are dequantized from the
+    packed codes in registers): mixed ranks, rank groups that straddle the
+    32-rank K-blocks, an empty delta (r = 0: W x only), an empty segment,
+    ragged token tiles; fused and delta-only against the oracle, and two
+    calls give the same bits."""
     note("prefill dense")
     t = torch()
     rng = np.random.default_rng(44)
@@ -603,13 +604,13 @@ def test_prefill_dense_segments():
 
 
 def test_prefill_dense_more_than_eight_tenants():
-    """Eleven tenants of at least 256 tokens each in the dense form: the
-    operand slots are reused by a second batch of launches.  Around the
-    8-slot boundary sit an r = 0 tenant (slot 7), an empty segment (tenant 8)
-    and a tenant right after it.  The workspace is dirtied first (status word
-    set, operands garbage): the call clears the word and overwrites every
-    output.  The same call with a workspace of the multi-tenant size (no
-    dense operands) takes the decode kernels; both against the oracle."""
+    """Eleven tenants of at least 256 tokens each in the dense form: a
+    second batch of launches after the first 8 tenants.  Around the batch
+    boundary sit an r = 0 tenant (the 8th), an empty segment (tenant 8) and a
+    tenant right after it.  The workspace is dirtied first (status word set,
+    t garbage): the call clears the word and overwrites every output.  The
+    same call with a workspace of the multi-tenant size (no dense buffers)
+    takes the decode kernels; both against the oracle."""
     note("prefill dense 11 tenants")
     t = torch()
     rng = np.random.default_rng(45)

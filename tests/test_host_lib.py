@@ -172,21 +172,23 @@ def test_workspace_bytes_rules():
 
 
 def test_prefill_workspace_holds_dense_operands():
-    """A prefill workspace of 256 tokens or more adds the dense operands to
-    the multi-tenant one: min(n, 8) slots of bf16 V [rp][2 in] and U
-    [out][3 rp], and bf16 t [T][3 rp], rp = the largest rank rounded up to 128
-    (at least 128), each region 256-byte aligned; none below 256 tokens."""
-    def dense(out, inn, rmax, n, T):
-        rp = max(128, -(-rmax // 128) * 128)
-        nb = min(n, 8)
-        al = lambda b: -(-b // 256) * 256
-        return al(2 * nb * rp * 2 * inn) + al(2 * nb * out * 3 * rp) + al(2 * T * 3 * rp)
+    """A prefill workspace of 256 tokens or more adds the dense form's
+    buffers to the multi-tenant one: fp32 t [T][rp], an fp32 rescale and a
+    uint32 max per token, rp = max over tenants of the rank groups each
+    rounded up to 32, summed and rounded up to 128 (at least 128), each region
+    256-byte aligned; none below 256 tokens."""
+    def pad(v, m):
+        return -(-v // m) * m
+
+    def dense(specs, T):
+        rp = max(max(128, pad(sum(pad(n, 32) for n in sp[2:]), 128)) for sp in specs)
+        return pad(4 * T * rp, 256) + 2 * pad(4 * T, 256)
     for specs, T in (([(256, 384, 2, 9, 40)] * 3, 300), ([(256, 384, 2, 9, 40), (256, 384, 0, 0, 0)] * 6, 1000),
-                     ([(1024, 512, 2, 20, 150), (1024, 512, 1, 1, 1)], 513), ([(256, 256, 0, 0, 0)], 256)):
+                     ([(1024, 512, 2, 20, 150), (1024, 512, 1, 1, 1)], 513), ([(256, 256, 0, 0, 0)], 256),
+                     ([(512, 512, 33, 1, 100)], 256)):
         mt = trs.dc_workspace_bytes(trs.DC_OP_MULTITENANT, specs, T)
         pf = trs.dc_workspace_bytes(trs.DC_OP_PREFILL, specs, T)
-        rmax = max(sum(sp[2:]) for sp in specs)
-        assert pf - mt == dense(specs[0][0], specs[0][1], rmax, len(specs), T)
+        assert pf - mt == dense(specs, T)
     sp = [(256, 384, 2, 9, 40)] * 3
     # fewer than 256 tokens can never take the dense form: no dense operands
     for T in (0, 1, 100, 255):
