@@ -159,8 +159,11 @@ constexpr int kVRanks = 4 * 16 * kVTiles;   // ranks per V-side block (4 waves)
 constexpr int kVDepth = 8;    // groups of codes a V-side wave keeps in flight
 static_assert(kChunkRows == kVRows, "one V-side pass per work item");
 
-// Split backbone product (T <= 256): K ranges of kSKSteps steps of 32.
+// Split backbone product (T <= 256): K ranges of kSKSteps steps of 32,
+// blocks of kBaseRows rows of W (one 16-row tile per wave).
 constexpr int kSKSteps = 16;
+constexpr int kBaseWaves = 8;
+constexpr int kBaseRows = 16 * kBaseWaves;
 DC_HD inline int base_splits(int in, int T) { return T <= 256 ? (in / 32 + kSKSteps - 1) / kSKSteps : 0; }
 
 // Prefill segments of at least this many tokens can take the dense form
@@ -384,7 +387,7 @@ struct BaseMat {
   float* ybase;
   float* bpt;
   int32_t out;
-  int32_t rb0;   // first 64-row block of this matrix in the launch
+  int32_t rb0;   // first kBaseRows-row block of this matrix in the launch
 };
 // The tiled product (T > 256) covers one matrix (m == 1).
 int launch_base(const BaseMat* mats, int m, const uint16_t* x, const uint16_t* xt, int in, int T, void* stream);

@@ -974,7 +974,7 @@ int launch_apply(const ApplyArgs& a) {
     pm.nyb[j] = A.W && a.wl.nks == kMaxAtomicTerms ? a.T * A.out : 0;
     pm.cnt[j] = cnt;
     pm.ncnt[j] = M.ncnt;
-    if (A.W) bm[nbm++] = BaseMat{A.W, ybase, bpt, A.out, rb}, rb += A.out / 64;
+    if (A.W) bm[nbm++] = BaseMat{A.W, ybase, bpt, A.out, rb}, rb += A.out / kBaseRows;
     pm.params[j] = MatParams{tv,   reinterpret_cast<float*>(wsp(M.vpt)), cnt, ybase, A.y, bpt, A.out, M.rs, M.vb,
                              a.wl.nks};
     vg.red0[j] = red;

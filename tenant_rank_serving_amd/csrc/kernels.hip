@@ -204,10 +204,10 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmBatch gb) {
 
 unsigned gemm_tiles(int M, int N) { return (unsigned)(M / kGT) * (unsigned)((N + kGT - 1) / kGT); }
 
-// Split-K form for a few token groups (T <= 256): 64 rows of W per block
-// (wave w: rows 16w..16w+15) and one range of at most kSKSteps K-steps
-// (blockIdx.y), so that the 4 waves share x: at the start each wave copies
-// its 16-token tile of x for the whole range straight into LDS with
+// Split-K form for a few token groups (T <= 256): kBaseRows rows of W per
+// block (wave w: rows 16w..16w+15) and one range of at most kSKSteps K-steps
+// (blockIdx.y), so that the 8 waves share x: at the start wave w copies the
+// 16-token tile w % 4 of x for half w / 4 of the range straight into LDS with
 // direct-to-LDS loads (a fixed count, all in flight at once), next to the
 // first kSKDepth K-steps of its W rows; after one barrier the loop streams W
 // kSKDepth steps ahead with no further synchronization.  The partial sums
@@ -236,7 +236,7 @@ struct BaseMats {
   int32_t nm;
 };
 
-__global__ void __launch_bounds__(256) k_base_sk(BaseMats bms, const uint16_t* __restrict__ xt, int32_t in,
+__global__ void __launch_bounds__(kBaseWaves * 64) k_base_sk(BaseMats bms, const uint16_t* __restrict__ xt, int32_t in,
                                                  int32_t T, int32_t nks) {
   int mj = 0;
 #pragma unroll
@@ -249,19 +249,22 @@ __global__ void __launch_bounds__(256) k_base_sk(BaseMats bms, const uint16_t* _
   const int out = bm.out;
   __shared__ __attribute__((aligned(16))) uint4 xs[kSKSteps][4][64];   // [step][token tile][lane] B tiles
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r0 = (blockIdx.x - bm.rb0) * 64;
+  const int r0 = (blockIdx.x - bm.rb0) * kBaseRows;
   const int t0 = blockIdx.z * 64;
   const int tiles = (T + 15) / 16;
   const int nall = in / 32;
   const int s0 = blockIdx.y * kSKSteps, nst = min(kSKSteps, nall - s0);   // this block's K-steps
-  // x: wave w copies token tile w (the last tile again past T: masked below)
+  // x: wave w copies token tile w % 4 for the steps of half w / 4 of the range
+  // (the last tile again past T: masked below)
   const __amdgpu_buffer_rsrc_t rx =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xt), 0, nall * tiles * 1024, kBufFlags);
-  const int tile = min(t0 / 16 + wave, tiles - 1);
+  const int tile = min(t0 / 16 + (wave & 3), tiles - 1);
+  constexpr int kXSteps = kSKSteps * 4 / kBaseWaves;   // steps of x each wave copies
 #pragma unroll
-  for (int st = 0; st < kSKSteps; ++st) {
+  for (int j = 0; j < kXSteps; ++j) {
+    const int st = (wave >> 2) * kXSteps + j;
     const int ks = s0 + min(st, nst - 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (base_lds_t*)&xs[st][wave][0], 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (base_lds_t*)&xs[st][wave & 3][0], 16,
                                              (ks * tiles + tile) * 1024 + lane * 16, 0, 0, 0);
   }
   // W: lane l holds row l%16 of the wave's 16, k = 8(l/16) .. +8 of a step
@@ -296,26 +299,33 @@ __global__ void __launch_bounds__(256) k_base_sk(BaseMats bms, const uint16_t* _
   // D layout: lane holds token column lane%16 of tile j and rows 4(lane/16)+i
   // of the wave's 16; transpose to [token][row] (padded) over the x copies
   lds_barrier();
-  float* red = reinterpret_cast<float*>(&xs[0][0][0]);   // [64][65]
+  constexpr int kRed = kBaseRows + 1;   // padded row of the transposed sums
+  static_assert(64 * kRed * 4 <= (int)sizeof(xs), "the transposed sums fit over the x copies");
+  float* red = reinterpret_cast<float*>(&xs[0][0][0]);   // [64 tokens][kRed]
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[(16 * j + (lane & 15)) * 65 + 16 * wave + 4 * (lane >> 4) + i] = acc[j][i];
+    for (int i = 0; i < 4; ++i) red[(16 * j + (lane & 15)) * kRed + 16 * wave + 4 * (lane >> 4) + i] = acc[j][i];
   lds_barrier();
   const int ntok = min(64, T - t0);
   if (nks <= kMaxAtomicTerms) {
-    for (int tl = wave; tl < ntok; tl += 4) {   // wave: tokens wave, wave + 4, ..; lane: row
-      float* dst = ybase + (size_t)(t0 + tl) * out + r0 + lane;
-      const float v = red[tl * 65 + lane];
-      if (nks > 1)
-        atomicAdd(dst, v);
-      else
-        *dst = v;
+    for (int tl = wave; tl < ntok; tl += kBaseWaves) {   // wave: tokens wave, wave + 8, ..; lane: rows
+#pragma unroll
+      for (int rr = lane; rr < kBaseRows; rr += 64) {
+        float* dst = ybase + (size_t)(t0 + tl) * out + r0 + rr;
+        const float v = red[tl * kRed + rr];
+        if (nks > 1)
+          atomicAdd(dst, v);
+        else
+          *dst = v;
+      }
     }
     return;
   }
   float* part = bpt + blockIdx.y * (size_t)T * out;   // this range's partials
-  for (int tl = wave; tl < ntok; tl += 4) part[(size_t)(t0 + tl) * out + r0 + lane] = red[tl * 65 + lane];
+  for (int tl = wave; tl < ntok; tl += kBaseWaves)
+#pragma unroll
+    for (int rr = lane; rr < kBaseRows; rr += 64) part[(size_t)(t0 + tl) * out + r0 + rr] = red[tl * kRed + rr];
 }
 
 // -------------------------------------------------------------- dequantize
@@ -378,11 +388,11 @@ int launch_base(const BaseMat* mats, int m, const uint16_t* x, const uint16_t* x
     int rows = 0;
     for (int j = 0; j < m; ++j) {
       bms.m[j] = mats[j];
-      rows = mats[j].rb0 + mats[j].out / 64;
+      rows = mats[j].rb0 + mats[j].out / kBaseRows;
     }
     bms.nm = m;
     const dim3 g((unsigned)rows, (unsigned)nks, (unsigned)((T + 63) / 64));
-    hipLaunchKernelGGL(k_base_sk, g, dim3(256), 0, st, bms, xt, in, T, nks);
+    hipLaunchKernelGGL(k_base_sk, g, dim3(kBaseWaves * 64), 0, st, bms, xt, in, T, nks);
   } else {
     return launch_tiled_base(mats[0].W, x, mats[0].ybase, mats[0].out, in, T, stream);
   }
