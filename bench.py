@@ -501,6 +501,38 @@ def config_bench(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (args.steps * copies)
 
+    # c4: the layer as grouped calls (q+k+v, o, gate+up, down) on one stream,
+    # all layer copies captured as one HIP graph, replayed
+    groups = [[0, 1, 2], [3], [4, 5], [6]]
+    ym = [torch.empty((tmax, o), dtype=torch.int16, device=dev) for _, o, _ in mats]
+
+    def grouped_graph_ms(T, fused):
+        gstream = torch.cuda.Stream()
+        gws = torch.empty(max(trs.dc_group_workspace_bytes([[specs[m]] * n_ten for m in g], len(g), T) for g in groups),
+                          dtype=torch.uint8, device=dev)
+        calls = [trs.GroupCall([views[c][m] for m in g], [W[c][m] for m in g] if fused else None, X[g[0]][:T], ids,
+                               [ym[m][:T] for m in g], gws, stream=gstream.cuda_stream)
+                 for c in range(copies) for g in groups]
+        with torch.cuda.stream(gstream):
+            for _ in range(max(args.warmup, 1)):
+                for cl in calls:
+                    cl()
+            torch.cuda.synchronize()
+            g_ = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_, stream=gstream):
+                for cl in calls:
+                    cl()
+            g_.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(gstream)
+            for _ in range(args.steps):
+                g_.replay()
+            e1.record(gstream)
+            torch.cuda.synchronize()
+        del g_
+        return e0.elapsed_time(e1) / (args.steps * copies)
+
     touched = n_ten if ids_h is None else len(set(ids_h.tolist()))
     delta_bytes = touched * sum(trs.dc_algorithmic_bytes(sp) for sp in specs)
     base_bytes = sum(o * i * 2 for _, o, i in mats)
@@ -530,6 +562,16 @@ def config_bench(args):
             "bytes_per_layer": {"packed_delta": int(delta_bytes), "backbone": int(base_bytes), "x_y": int(xy)},
             "flops_per_layer": {"delta": f_delta, "backbone": f_base},
         }
+        if w == "c4":
+            gf, gd = grouped_graph_ms(T, True), grouped_graph_ms(T, False)
+            log("%s T=%d grouped + graph: fused %.4f ms/layer, delta-only %.4f ms/layer" % (w, T, gf, gd))
+            res["grouped_graph"] = {
+                "launch": "4 grouped calls per layer (q+k+v, o, gate+up, down) on one stream, every layer copy's "
+                          "calls captured as one HIP graph and replayed",
+                "ms_per_layer": round(gf, 4), "tokens_per_s": round(T / gf * 1e3, 1),
+                "delta_only": {"ms_per_layer": round(gd, 4),
+                               "packed_delta_GBps": round(delta_bytes / (gd * 1e-3) / 1e9, 1),
+                               "pct_of_hbm_peak": round(100 * delta_bytes / (gd * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}}
         if base_legs:
             res["baselines"] = {}
             for bname, leg in base_legs.items():
