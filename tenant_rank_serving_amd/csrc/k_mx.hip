@@ -668,6 +668,9 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
   const int mj = blockIdx.y / ug.nact;
   const MatParams P = ug.mp[mj];
   const ActEntry e = ug.act[blockIdx.y];   // the work items of the group's matrices, one after another
+  // every field in hand before the first branch: one scalar round trip
+  asm volatile("" ::"s"(P.tv), "s"(P.ybase), "s"(P.y), "s"(P.out), "s"(P.rs), "s"(e.base), "s"(e.n8), "s"(e.n3),
+               "s"(e.n2), "s"(e.k), "s"(e.p0), "s"(e.p1), "s"(n), "s"(in), "s"(perm), "s"(T));
   const int out = P.out;
   if (g * kGroup >= out) return;
   const int rs = P.rs;
@@ -724,17 +727,19 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
     w[1] = v.y;
     w[2] = v.z;
   };
-  // fp16 dequantized 8-bit U weights of this lane's output row (first kU8Max
-  // pairs); loaded behind the first window's A-prep inputs and codes
-  float u8w[kU8Max];
-  auto load_u8w = [&]() __attribute__((always_inline)) {
-    const int np8 = (int)round_up(s8.n, 4);
+  // 8-bit U weights of this lane's output row (first kU8Max pairs): scale
+  // word and code, loaded behind the first window's A-prep inputs and codes,
+  // dequantized to fp16 in the epilogue
+  uint32_t u8s[kU8Max], u8c[kU8Max];
+  // (with no 8-bit pairs both point at the buffer's first word: every load stays inside it)
+  const int ous8 = s8.n > 0 ? (int)L.off[DC_REG_US8] + g * (int)round_up(s8.n, 4) * 4 : 0;
+  const int ouc8 = s8.n > 0 ? (int)L.off[DC_REG_UC8] + orow * s8.n : 0;
+  auto load_u8 = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kU8Max; ++i) {
-      const int ii = min(i, s8.n > 0 ? s8.n - 1 : 0);
-      const uint32_t e = s8.n > 0 ? s8.us[(size_t)g * np8 + ii] : 0u;
-      const float code = s8.n > 0 ? (float)s8.uc[(size_t)orow * s8.n + ii] : 0.f;
-      u8w[i] = (float)(_Float16)(f16f(e & 0xFFFFu) * (code - f16f(e >> 16)));
+    for (int i = 0; i < kU8Max; ++i) {   // unconditional (unused past s8.n): straight-line waits
+      const int i8 = min(i, max(s8.n - 1, 0));
+      u8s[i] = __builtin_amdgcn_raw_buffer_load_b32(rten, ous8 + i8 * 4, 0, 0);
+      u8c[i] = __builtin_amdgcn_raw_buffer_load_b8(rten, ouc8 + i8, 0, 0);
     }
   };
   // rows 12-15 of every op carry no piece: zero once
@@ -757,38 +762,64 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     // the epilogue's inputs, in flight during the pass: lane group q writes
     // tokens 2q and 2q + 1 of the pass (their original indices, then W x and
-    // t of the 8-bit pairs)
+    // t of the 8-bit pairs).  The indices go out first: the W x loads wait
+    // for them alone.
     int tko[2];
     float ybo[2] = {0.f, 0.f}, t8o[2][kU8Max];
 #pragma unroll
     for (int h = 0; h < 2; ++h) tko[h] = perm[pb + min(2 * q + h, nt - 1)];
+    auto epi_loads = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rw = min(2 * q + h, nt - 1);
+#pragma unroll
+        for (int i = 0; i < kU8Max; ++i)
+          t8o[h][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rt, ((pb + rw) * rs + i) * 4, 0, 0));
+      }
+      if (pb == p0) load_u8();
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ybo[h] = gload(ybase ? ybase + (size_t)tko[h] * out + orow : tv);
+    };
+    auto epi_select = [&]() __attribute__((always_inline)) {   // values past what the matrix has are zero
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        ybo[h] = ybase ? ybo[h] : 0.f;
+#pragma unroll
+        for (int i = 0; i < kU8Max; ++i) t8o[h][i] = i < s8.n ? t8o[h][i] : 0.f;
+      }
+    };
     // A operands of chunks [cw0, cw0 + wc) for the pass's token rows.  Thread
     // tid takes chunk pcl of the window and rows 4h..4h+3: with one op per
     // chunk the 512 threads cover 16 chunks x rows 0-3, with two 8 chunks x
-    // both halves.  The first window's loads go out ahead of the code ring's
-    // first loads (vmcnt is in order: behind them they would wait for the
-    // whole burst).
+    // both halves.  The inputs (scale/zero words, t) are loaded apart from
+    // the math, so that the first window's code ring and the epilogue's
+    // inputs go out in the same burst behind them (vmcnt is in order: the
+    // math then waits for its own loads only).
     const int pcl = nops == 1 ? tid >> 5 : (tid & 255) >> 5;
     const int hh = nops == 1 ? 0 : tid >> 8;
-    auto aprep = [&](int cw0, int wc, bool first) __attribute__((always_inline)) {
+    struct APIn {
+      u32x4 usw;
+      f32x4 tt[4];
+    };
+    auto aprep_load = [&](int cw0, APIn& ai) __attribute__((always_inline)) {
+      const int c = cw0 + pcl;
+      const bool three = c < nc3;
+      const int li = (three ? c : c - nc3) * kGroup + m0;
+      ai.usw = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, li * 4 + (three ? ou3 : ou2), 0, 0));
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        ai.tt[r] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rt, ((pb + min(4 * hh + r, nt - 1)) * rs + (three ? tb3 : tb2) + li) * 4, 0, 0));
+    };
+    auto aprep = [&](int cw0, int wc, const APIn& ai) __attribute__((always_inline)) {
       const int c = cw0 + pcl;
       const bool cok = pcl < wc;
       const bool three = c < nc3;
       const int sn = three ? seg3.n : seg2.n;
       const int li = (three ? c : c - nc3) * kGroup + m0;
-      const u32x4 usw = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, li * 4, three ? ou3 : ou2, 0));
-      f32x4 tt[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        tt[r] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       rt, ((pb + min(4 * hh + r, nt - 1)) * rs + (three ? tb3 : tb2) + li) * 4, 0, 0));
-      if (first) {
-#pragma unroll
-        for (int d = 0; d < kUDepth; ++d) load(cr[d], d);
-        if (pb == p0) load_u8w();
-      }
+      const u32x4 usw = ai.usw;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int r = 4 * hh + r4;
@@ -798,7 +829,7 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const bool ok = cok && li + u < sn;
-          tp[u] = ok ? f16f(usw[u] & 0xFFFFu) * tt[r4][u] : 0.f;
+          tp[u] = ok ? f16f(usw[u] & 0xFFFFu) * ai.tt[r4][u] : 0.f;
           mx = fmaxf(mx, fabsf(tp[u]));
         }
         mx = fmaxf(mx, swz_xor<1>(mx));
@@ -866,21 +897,10 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
       load(cur, c + kUDepth);
       asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));   // sums land here, not deferred to the end
     };
-    __syncthreads();   // the previous pass's operands and sums are consumed
+    if (pb != p0) __syncthreads();   // the previous pass's operands and sums are consumed
     if (lane < kURows) S.cz[wave][lane] = 0.f;   // this wave's z t' sums of the pass
-    if (nc == 0 && pb == p0) load_u8w();
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {   // every pass, also one with no 3/2-bit chunks
-      const int rw = min(2 * q + h, nt - 1);
-      if (ybase) ybo[h] = ybase[(size_t)tko[h] * out + orow];
-#pragma unroll
-      for (int i = 0; i < kU8Max; ++i) t8o[h][i] = i < s8.n ? tv[(size_t)(pb + rw) * rs + i] : 0.f;
-    }
-    for (int cw0 = 0; cw0 < nc; cw0 += wcap) {
-      const int wc = min(wcap, nc - cw0);
-      if (cw0 > 0) __syncthreads();   // the previous window's operands are consumed
-      aprep(cw0, wc, cw0 == 0);
-      __syncthreads();
+    // the matrix-core ops of window [cw0, cw0 + wc)
+    auto run = [&](int cw0, int wc) __attribute__((always_inline)) {
       int c0 = cw0;
       for (; c0 + kUDepth <= cw0 + wc; c0 += kUDepth) {
 #pragma unroll
@@ -890,6 +910,34 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll
       for (int d = 0; d < kUDepth - 1; ++d)
         if (c0 + d < cw0 + wc) step(c0 + d, c0 + d - cw0, cr[d]);
+    };
+    if (nc == 0) {   // no 3/2-bit chunks: only the 8-bit pairs and W x
+      epi_loads();
+      __syncthreads();   // every wave's zeroed sums are seen
+    } else {
+      // the first window, outside any loop: one burst of loads (A-prep
+      // inputs, the code ring, the epilogue's inputs), then the math
+      const int wc = min(wcap, nc);
+      APIn ai;
+      aprep_load(0, ai);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int d = 0; d < kUDepth; ++d) load(cr[d], d);
+      __builtin_amdgcn_sched_barrier(0);
+      epi_loads();
+      __builtin_amdgcn_sched_barrier(0);
+      aprep(0, wc, ai);
+      __syncthreads();
+      run(0, wc);
+    }
+    for (int cw0 = wcap; cw0 < nc; cw0 += wcap) {
+      const int wc = min(wcap, nc - cw0);
+      __syncthreads();   // the previous window's operands are consumed
+      APIn ai;
+      aprep_load(cw0, ai);
+      aprep(cw0, wc, ai);
+      __syncthreads();
+      run(cw0, wc);
     }
     // ---- epilogue: each token's three piece rows, sum_i z t' per token row, 8-bit pairs, W x, one rounding
     f32x4 tot[2];
@@ -901,7 +949,12 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
         tot[op][r] = v + __shfl_xor(v, 32, 64);
       }
     }
-    __syncthreads();
+    // every wave's z t' sums were written before the last window's barrier
+    epi_select();
+    float u8w[kU8Max];
+#pragma unroll
+    for (int i = 0; i < kU8Max; ++i)
+      u8w[i] = (float)(_Float16)(f16f(u8s[i] & 0xFFFFu) * ((float)u8c[i] - f16f(u8s[i] >> 16)));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {   // lane group q writes tokens 2q and 2q + 1
       const int rw = 2 * q + h;

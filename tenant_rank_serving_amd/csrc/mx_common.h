@@ -31,6 +31,12 @@ constexpr int kScaleFp6Code = 130;   // 2^3: fp6 element q/8 -> q
 constexpr int kXFrag = 256;          // bytes of x fragments per (token, 128-group)
 constexpr int kBufFlags = 0x00020000; // buffer resource word 3: raw 32-bit dwords, bounds-checked
 
+// A load the compiler emits as a global access: a flat load also counts
+// against lgkmcnt, so every later LDS wait would wait for its memory trip too.
+__device__ __forceinline__ float gload(const float* p) {
+  return *(const __attribute__((address_space(1))) float*)p;
+}
+
 __device__ __forceinline__ float f16f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 
 __device__ __forceinline__ uint16_t to_bf16(float f) {
