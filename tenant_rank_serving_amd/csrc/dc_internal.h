@@ -144,8 +144,15 @@ struct ActEntry {
   int32_t n8, n3, n2;
   int32_t k;
   int32_t p0, p1;
+  // Delta-CoMe calls: byte offsets of the DC_REG_* regions of the tenant's
+  // packed buffer and its size, worked out once per item by the routing
+  // block (every wave of a V or U block would otherwise redo it in scalar
+  // arithmetic); zero for the backbone-only bucket and the baselines
+  uint32_t off[DC_REG_COUNT];
+  uint32_t total;
+  uint32_t pad_[2];
 };
-static_assert(sizeof(ActEntry) == 32, "one 32-byte load per block");
+static_assert(sizeof(ActEntry) == 96, "two scalar loads per block");
 constexpr int kChunkRows = 8;   // token rows per work item (one V-side and one U-side pass)
 // Work items of a call of n tenants and T tokens: at most one partly filled
 // chunk per bucket (n tenants + the backbone-only bucket) plus T / kChunkRows.

@@ -55,6 +55,13 @@ __device__ __forceinline__ Seg seg_of(const Tenant& tn, const Layout& L, int whi
   return s;
 }
 
+// The region offsets of a work item's packed buffer (sizes are not carried).
+__device__ __forceinline__ void layout_of_item(const ActEntry& e, Layout* L) {
+#pragma unroll
+  for (int i = 0; i < DC_REG_COUNT; ++i) L->off[i] = e.off[i];
+  L->total = e.total;
+}
+
 struct SegArg {
   int32_t v[DC_MAX_TENANTS + 1];
 };
@@ -70,7 +77,7 @@ struct SegArg {
 // group sum; the other blocks also zero t and, when the backbone product is
 // split over K, W x (both are accumulated with float atomics).
 __device__ __forceinline__ void list_active(const Tenant& mine, int32_t n, const int* so, int32_t cap,
-                                            ActEntry* __restrict__ act) {
+                                            ActEntry* __restrict__ act, int32_t out, int32_t in, bool layouts) {
   __shared__ int wsum[4];
   const int tid = threadIdx.x, b = tid, lane = tid & 63, wave = tid >> 6;
   // work items of bucket b: its rows in chunks of kChunkRows
@@ -90,13 +97,20 @@ __device__ __forceinline__ void list_active(const Tenant& mine, int32_t n, const
     total += wsum[w];
   }
   lds_barrier();   // wsum is read: a next call may write it
+  ActEntry e{};
+  e.base = b < n ? mine.base : nullptr;
+  e.n8 = b < n ? mine.n8 : 0;
+  e.n3 = b < n ? mine.n3 : 0;
+  e.n2 = b < n ? mine.n2 : 0;
+  e.k = b;
+  if (layouts && b < n && items > 0) {
+    Layout L;
+    layout_of(out, in, e.n8, e.n3, e.n2, &L);
+#pragma unroll
+    for (int i = 0; i < DC_REG_COUNT; ++i) e.off[i] = (uint32_t)L.off[i];
+    e.total = (uint32_t)L.total;
+  }
   for (int j = 0; j < items; ++j) {
-    ActEntry e;
-    e.base = b < n ? mine.base : nullptr;
-    e.n8 = b < n ? mine.n8 : 0;
-    e.n3 = b < n ? mine.n3 : 0;
-    e.n2 = b < n ? mine.n2 : 0;
-    e.k = b;
     e.p0 = so[b] + j * kChunkRows;
     e.p1 = min(so[b] + (j + 1) * kChunkRows, so[b + 1]);
     act[pos + j] = e;
@@ -124,6 +138,7 @@ struct PrepMats {
   int32_t nyb[kMaxGroup];
   uint32_t* cnt[kMaxGroup];   // arrival counters of the fixed-order sums
   int32_t ncnt[kMaxGroup];
+  int32_t layouts;            // Delta-CoMe buffers: the work items carry their region offsets
 };
 
 template <int M>
@@ -167,7 +182,7 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
       }
       lds_barrier();
 #pragma unroll
-      for (int j = 0; j < M; ++j) list_active(mine[j], n, so, cap, pm.act[j]);
+      for (int j = 0; j < M; ++j) list_active(mine[j], n, so, cap, pm.act[j], pm.params[j].out, in, pm.layouts != 0);
       return;
     }
     __shared__ int cnt[DC_MAX_TENANTS + 1];   // tokens per bucket
@@ -212,7 +227,7 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
     }
     lds_barrier();
 #pragma unroll
-    for (int j = 0; j < M; ++j) list_active(mine[j], n, so, cap, pm.act[j]);
+    for (int j = 0; j < M; ++j) list_active(mine[j], n, so, cap, pm.act[j], pm.params[j].out, in, pm.layouts != 0);
     for (int c0 = 0; c0 < T; c0 += blockDim.x) {
       const int t = c0 + tid;
       int b = -1;
@@ -600,7 +615,7 @@ __global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t in, const uint
   const int s = blockIdx.x % ns;
   if (b >= v_blocks(tn.n8, tn.n3, tn.n2)) return;
   Layout L;
-  layout_of(out, in, tn.n8, tn.n3, tn.n2, &L);
+  layout_of_item(e, &L);
   if (tn.n8 > 0) {
     if (b == 0) {
       vside_8bit(tn, L, in, s, x, perm, p0, p1, vo);
@@ -671,6 +686,8 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
   // every field in hand before the first branch: one scalar round trip
   asm volatile("" ::"s"(P.tv), "s"(P.ybase), "s"(P.y), "s"(P.out), "s"(P.rs), "s"(e.base), "s"(e.n8), "s"(e.n3),
                "s"(e.n2), "s"(e.k), "s"(e.p0), "s"(e.p1), "s"(n), "s"(in), "s"(perm), "s"(T));
+  asm volatile("" ::"s"(e.off[DC_REG_UC8]), "s"(e.off[DC_REG_UC3]), "s"(e.off[DC_REG_UC2]), "s"(e.off[DC_REG_US8]),
+               "s"(e.off[DC_REG_US3]), "s"(e.off[DC_REG_US2]), "s"(e.total));
   const int out = P.out;
   if (g * kGroup >= out) return;
   const int rs = P.rs;
@@ -697,7 +714,7 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
   tn.n2 = e.n2;
   tn.pad_ = 0;
   Layout L;
-  layout_of(out, in, tn.n8, tn.n3, tn.n2, &L);
+  layout_of_item(e, &L);
   const Seg seg3 = seg_of(tn, L, 1), seg2 = seg_of(tn, L, 2), s8 = seg_of(tn, L, 0);
   const int tb3 = t_base(tn.n8, tn.n3, 1), tb2 = t_base(tn.n8, tn.n3, 2);
   const int np3 = (int)round_up(seg3.n, 4), np2 = (int)round_up(seg2.n, 4);
@@ -801,17 +818,23 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
       u32x4 usw;
       f32x4 tt[4];
     };
-    auto aprep_load = [&](int cw0, APIn& ai) __attribute__((always_inline)) {
+    // Threads past the window's chunks or their segment's ranks, and token
+    // rows past the pass's, load nothing: their offset is the resource's
+    // record count, out of range, so the load returns zeros without a memory
+    // request (the math masks those values anyway).
+    auto aprep_load = [&](int cw0, int wc, APIn& ai) __attribute__((always_inline)) {
       const int c = cw0 + pcl;
       const bool three = c < nc3;
       const int li = (three ? c : c - nc3) * kGroup + m0;
+      const bool live = pcl < wc && li < (three ? seg3.n : seg2.n);
       ai.usw = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, li * 4 + (three ? ou3 : ou2), 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, live ? li * 4 + (three ? ou3 : ou2) : (int)L.total, 0, 0));
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         ai.tt[r] = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       rt, ((pb + min(4 * hh + r, nt - 1)) * rs + (three ? tb3 : tb2) + li) * 4, 0, 0));
+                       rt, live && 4 * hh + r < nt ? ((pb + 4 * hh + r) * rs + (three ? tb3 : tb2) + li) * 4 : T * rs * 4,
+                       0, 0));
     };
     auto aprep = [&](int cw0, int wc, const APIn& ai) __attribute__((always_inline)) {
       const int c = cw0 + pcl;
@@ -919,7 +942,7 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
       // inputs, the code ring, the epilogue's inputs), then the math
       const int wc = min(wcap, nc);
       APIn ai;
-      aprep_load(0, ai);
+      aprep_load(0, wc, ai);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int d = 0; d < kUDepth; ++d) load(cr[d], d);
@@ -934,7 +957,7 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
       const int wc = min(wcap, nc - cw0);
       __syncthreads();   // the previous window's operands are consumed
       APIn ai;
-      aprep_load(cw0, ai);
+      aprep_load(cw0, wc, ai);
       aprep(cw0, wc, ai);
       __syncthreads();
       run(cw0, wc);
@@ -1027,6 +1050,7 @@ int launch_apply(const ApplyArgs& a) {
     pm.nyb[j] = A.W && a.wl.nks == kMaxAtomicTerms ? a.T * A.out : 0;
     pm.cnt[j] = cnt;
     pm.ncnt[j] = M.ncnt;
+    pm.layouts = a.kind == kKindDeltaCoMe;
     if (A.W) bm[nbm++] = BaseMat{A.W, ybase, bpt, A.out, rb}, rb += A.out / kBaseRows;
     pm.params[j] = MatParams{tv,   reinterpret_cast<float*>(wsp(M.vpt)), cnt, ybase, A.y, bpt, A.out, M.rs, M.vb,
                              a.wl.nks};
