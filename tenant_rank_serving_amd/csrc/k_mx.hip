@@ -655,12 +655,15 @@ __global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t in, const uint
 // synchronization, one op per four live tokens per chunk, the codes of the
 // next kUDepth chunks in flight in a register ring (buffer loads on one
 // resource for the tenant's whole buffer, the region in the uniform offset).
+// The first window's loads go out as one burst: A-prep inputs, the 8-bit
+// pairs' inputs, the ring, W x; the barriers order LDS only and leave the
+// burst in flight.
 // The epilogue sums each token's three piece rows, takes sum_i z_ig t'_i
 // off, adds the 8-bit pairs and W x and rounds once to bf16.
 constexpr int kURows = 8;     // token rows per pass
 constexpr int kUWaves = 8;    // waves per block, one 16-row tile each
 constexpr int kU8Max = 2;     // 8-bit pairs whose U weights a lane keeps in registers
-constexpr int kUDepth = 4;    // chunks of codes in flight per lane
+constexpr int kUDepth = 4;    // chunks of codes in flight per lane (register ring)
 constexpr int kUWin = 16;     // A operands per window (chunks x ops): 16 chunks with one op, 8 with two
 
 struct ULds {
@@ -694,7 +697,7 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
   const float* __restrict__ tv = P.tv;
   const float* __restrict__ ybase = P.ybase;
   uint16_t* __restrict__ y = P.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 15, q = lane >> 4;
   const int p0 = e.p0, p1 = e.p1;
   if (p0 >= p1) return;
@@ -731,6 +734,8 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
   // the lane's byte offset of K-block kb of its row in the 3- or 2-bit code region
   const int rw3 = (int)u_row_words(seg3.n, 3), rw2 = (int)u_row_words(seg2.n, 2);
   const int kbn3 = (seg3.n + kKBlock - 1) / kKBlock, kbn2 = (seg2.n + kKBlock - 1) / kKBlock;
+  // the 12 bytes of chunk c of this lane's codes from its K-block's start
+  // (a 2-bit chunk uses 8); past the last chunk: the last again
   auto load = [&](uint32_t (&w)[3], int c) __attribute__((always_inline)) {
     c = min(c, nc - 1);
     const bool three = c < nc3;
@@ -771,7 +776,9 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
   const int m0 = kb4 * 32 + part * 4;
   const int lg_even = 2 * (kb4 & 1), hw = (kb4 >= 2 ? 8 : 0) + part;   // lane group, 16-bit word
   const int ps = col >> 2, tr4 = col & 3;   // MFMA lane's A row: piece ps of token 4 op + tr4
-  for (int pb = p0; pb < p1; pb += kURows) {
+  static_assert(kChunkRows == kURows, "a work item is one pass");
+  {
+    const int pb = p0;
     const int nt = min(kURows, p1 - pb);
     const int nops = (nt + 3) >> 2;   // matrix-core ops per tile and chunk
     const int wcap = kUWin / nops;     // chunks per window (a multiple of kUDepth)
@@ -781,11 +788,13 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
     // tokens 2q and 2q + 1 of the pass (their original indices, then W x and
     // t of the 8-bit pairs).  The indices go out first: the W x loads wait
     // for them alone.
+    // The token indices go out first: the W x loads, last in the burst,
+    // wait for them alone.
     int tko[2];
     float ybo[2] = {0.f, 0.f}, t8o[2][kU8Max];
 #pragma unroll
     for (int h = 0; h < 2; ++h) tko[h] = perm[pb + min(2 * q + h, nt - 1)];
-    auto epi_loads = [&]() __attribute__((always_inline)) {
+    auto epi_loads_t8 = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int rw = min(2 * q + h, nt - 1);
@@ -793,9 +802,17 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
         for (int i = 0; i < kU8Max; ++i)
           t8o[h][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rt, ((pb + rw) * rs + i) * 4, 0, 0));
       }
-      if (pb == p0) load_u8();
+      load_u8();
+    };
+    // two loads whether or not there is a W x (then two distinct words of t,
+    // unused): straight-line code, so the waits for earlier loads are exact
+    auto epi_loads_yb = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) ybo[h] = gload(ybase ? ybase + (size_t)tko[h] * out + orow : tv);
+      for (int h = 0; h < 2; ++h) ybo[h] = gload(ybase ? ybase + (size_t)tko[h] * out + orow : tv + h);
+    };
+    auto epi_loads = [&]() __attribute__((always_inline)) {
+      epi_loads_t8();
+      epi_loads_yb();
     };
     auto epi_select = [&]() __attribute__((always_inline)) {   // values past what the matrix has are zero
 #pragma unroll
@@ -920,7 +937,6 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
       load(cur, c + kUDepth);
       asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));   // sums land here, not deferred to the end
     };
-    if (pb != p0) __syncthreads();   // the previous pass's operands and sums are consumed
     if (lane < kURows) S.cz[wave][lane] = 0.f;   // this wave's z t' sums of the pass
     // the matrix-core ops of window [cw0, cw0 + wc)
     auto run = [&](int cw0, int wc) __attribute__((always_inline)) {
@@ -939,27 +955,29 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
       __syncthreads();   // every wave's zeroed sums are seen
     } else {
       // the first window, outside any loop: one burst of loads (A-prep
-      // inputs, the code ring, the epilogue's inputs), then the math
+      // inputs, the 8-bit pairs' inputs, the code ring, then W x once the
+      // token indices are in), then the math
       const int wc = min(wcap, nc);
       APIn ai;
       aprep_load(0, wc, ai);
+      epi_loads_t8();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int d = 0; d < kUDepth; ++d) load(cr[d], d);
       __builtin_amdgcn_sched_barrier(0);
-      epi_loads();
+      epi_loads_yb();
       __builtin_amdgcn_sched_barrier(0);
       aprep(0, wc, ai);
-      __syncthreads();
+      lds_barrier_keep_vm();
       run(0, wc);
     }
     for (int cw0 = wcap; cw0 < nc; cw0 += wcap) {
       const int wc = min(wcap, nc - cw0);
-      __syncthreads();   // the previous window's operands are consumed
+      lds_barrier_keep_vm();   // the previous window's operands are consumed
       APIn ai;
       aprep_load(cw0, wc, ai);
       aprep(cw0, wc, ai);
-      __syncthreads();
+      lds_barrier_keep_vm();
       run(cw0, wc);
     }
     // ---- epilogue: each token's three piece rows, sum_i z t' per token row, 8-bit pairs, W x, one rounding

@@ -137,6 +137,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The same for a kernel with LDS-DMA loads in flight: a fence would wait for
+// them too (vmcnt(0)).  The stores it orders are plain LDS stores (complete
+// at lgkmcnt(0)); DMA-filled LDS is read only by the wave that loads it,
+// after its own count-based wait.
+__device__ __forceinline__ void lds_barrier_keep_vm() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ v8i v8_of(const uint4& a, const uint4& b) {
   return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
