@@ -405,7 +405,7 @@ __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, i
   const int gn = min(kVSlice, gi_n - g0);   // groups in this slice
   const int glast = g0 + gn - 1;
   const int np = (int)round_up(sg.n, 4);
-  const int npass = (p1 - p0 + kVRows - 1) / kVRows;
+  static_assert(kChunkRows == kVRows, "a work item is one pass");
   VBuf P;
   P.rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sg.vc), 0, (int)round_up(sg.n, 16) * gi_n * 16 * B,
                                           kBufFlags);
@@ -421,24 +421,27 @@ __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, i
     // (t, group, q, col), i.e. lane * b words into the tile's group block
     P.oc[h] = (uint32_t)(((tile0 + h) * gi_n * 64 + lane) * 4 * B);
     P.oz[h] = (uint32_t)(4 * (rv[h] ? li[h] : 0));
-    sig[h] = rv[h] ? sigma[sg.lo + li[h]] : 0.f;
+    sig[h] = rv[h] ? gload(sigma + sg.lo + li[h]) : 0.f;   // a global load: a flat one would make every wait drain
   }
   const int tr = col & 7;              // token row of this lane's A operand
   const int piece = col >> 3;          // 0: hi pieces, 1: lo pieces
-  for (int ip = 0; ip < npass; ++ip) {
-    const int pb = p0 + ip * kVRows;
+  {
+    const int pb = p0;
     const int nt = min(kVRows, p1 - pb);
     VStage st;
     v_stage_load(st, xf, xsc, xsum, gi_n, g0, pb, nt);   // ahead of the ring: vmcnt is in order
-    VGrp<B> ring[kDepth] = {};   // defined on every path: no values carried across passes
-    if (live_wave) {
+    // Every wave issues the ring's first loads, also one with no rank of the
+    // segment (its code offsets are past the region: out of range, no memory
+    // request): loads on every path keep the waits for the x tiles exact.
+    VGrp<B> ring[kDepth];
 #pragma unroll
-      for (int d = 0; d < kDepth; ++d) v_load_grp<B>(ring[d], P, np, min(g0 + d, glast));
+    for (int d = 0; d < kDepth; ++d) {   // in group order: the first group's wait leaves the rest in flight
+      v_load_grp<B>(ring[d], P, np, min(g0 + d, glast));
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();   // LDS reuse across passes
     v_stage_store(S, st);
     __syncthreads();
-    if (!live_wave) continue;
+    if (!live_wave) return;
     const bool live = tr < nt;
     f32x4 acc[kVTiles];
 #pragma unroll

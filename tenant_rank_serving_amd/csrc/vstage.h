@@ -135,7 +135,10 @@ __device__ __forceinline__ void v_stage_store(VLds& S, const VStage& st) {
 #pragma unroll
   for (int u = 0; u < kVSlice / 2; ++u)
     S.frag[gh + 2 * u][rw][k16] = make_int4(st.v[u].x, st.v[u].y, st.v[u].z, st.v[u].w);
-  if (tid < kVRows * kVSlice) {
+  // every thread stores (threads tid and tid + 128 write the same values):
+  // a conditional store would sink these loads behind the code loads that
+  // follow them, and waiting for them would then drain those too
+  {
     const int sr = tid & 7, sgl = (tid >> 3) & (kVSlice - 1);
     S.sc[sgl][sr] = st.scw;
     S.xs[sgl][sr] = st.xsv;
