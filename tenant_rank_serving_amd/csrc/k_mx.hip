@@ -599,9 +599,12 @@ __global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t in, const uint
     return;
   }
   const int yy = blockIdx.y - g.red_rows;
-  const int mj = yy / g.nact, item = yy % g.nact;
+  // rows item-major, matrix fastest: every matrix's work items (listed
+  // first) run before the empty entries of any
+  const int mg = (gridDim.y - g.red_rows) / g.nact;   // matrices of the group
+  const int mj = yy % mg, item = yy / mg;
   const MatParams P = g.mp[mj];
-  const ActEntry e = g.act[yy];   // the item-th work item of matrix mj
+  const ActEntry e = g.act[mj * g.nact + item];   // the item-th work item of matrix mj
   const VOut vo{P.tv, P.vpt, P.vcnt, P.rs, g.ns, g.T, P.vb};
   const int out = P.out;
   const int p0 = e.p0, p1 = e.p1;
@@ -686,9 +689,12 @@ struct UGroup {
 __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) k_uside(int32_t n, int32_t in, const int32_t* __restrict__ perm,
                                                         int32_t T, UGroup ug) {
   const int g = blockIdx.x;
-  const int mj = blockIdx.y / ug.nact;
+  // rows item-major, matrix fastest: every matrix's work items (listed
+  // first) run before the empty entries of any
+  const int mg = gridDim.y / ug.nact;   // matrices of the group
+  const int mj = blockIdx.y % mg, item = blockIdx.y / mg;
   const MatParams P = ug.mp[mj];
-  const ActEntry e = ug.act[blockIdx.y];   // the work items of the group's matrices, one after another
+  const ActEntry e = ug.act[mj * ug.nact + item];
   // every field in hand before the first branch: one scalar round trip
   asm volatile("" ::"s"(P.tv), "s"(P.ybase), "s"(P.y), "s"(P.out), "s"(P.rs), "s"(e.base), "s"(e.n8), "s"(e.n3),
                "s"(e.n2), "s"(e.k), "s"(e.p0), "s"(e.p1), "s"(n), "s"(in), "s"(perm), "s"(T));
