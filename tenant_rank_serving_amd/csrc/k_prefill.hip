@@ -267,6 +267,30 @@ __global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* __r
   }
 }
 
+// ----------------------------------------------------------------- t split
+// In place, per token row of the launch's tenants: t'[p] = t[p] 2^-e(tok)
+// as fp16 hi = fp16(t') and lo = fp16(t' - hi), stored as one word hi |
+// lo << 16 where t[p] was: once per (token, rank), not once per row tile of
+// the U product.  Thread: 4 consecutive ranks of one token.
+__global__ void __launch_bounds__(256) k_pf_t(float* __restrict__ tw, const uint32_t* __restrict__ tmax, int32_t tok0,
+                                              int32_t ntok, int32_t ldt) {
+  const int per = ldt / 4;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)ntok * per) return;
+  const int tok = tok0 + (int)(i / per), c = (int)(i % per) * 4;
+  const float tinv = pow2(-scale_exp(__uint_as_float(tmax[tok])));
+  f32x4* p = reinterpret_cast<f32x4*>(tw + (size_t)tok * ldt + c);
+  const f32x4 v = *p;
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x = v[e] * tinv;
+    const uint32_t h = f16b(x);
+    o[e] = h | (f16b(x - f16v(h)) << 16);
+  }
+  *reinterpret_cast<uint4*>(p) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // ----------------------------------------------------------------- U product
 // C[o][tok] = sum_p Û[o][p] (t_hi + t_lo)[tok][p], t' = t 2^-e(tok);
 // y = bf16(W x + C 2^e).  Block = 128 rows x 128 tokens, K in chunks of one
@@ -286,8 +310,7 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
   const int og = o0 / kGroup;   // the tile's 128-row scale group
   const int tl_s = min(t0 + arow, N - 1);
   const int tok_s = s0 + tl_s;
-  const float tinv = pow2(-scale_exp(__uint_as_float(tmax[tok_s])));
-  const float* tsrc = tw + (size_t)tok_s * ldt + 16 * hs;
+  const float* tsrc = tw + (size_t)tok_s * ldt + 16 * hs;   // packed fp16 pairs (k_pf_t)
   uint32_t cw[4], sz[16];
   uint32_t bsel = 0;
   f32x4 tr[4];
@@ -313,8 +336,24 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
       if (nw > 1) cw[1] = wp[1];
       if (nw > 2) cw[2] = wp[2];
     }
+    // the 16 scale words, four 16-byte loads (pad4 rows, li0 a multiple of
+    // 16: aligned), words past the segment's pairs zeroed (a zero scale
+    // makes their values zero)
+    {
+      const uint4* sp = reinterpret_cast<const uint4*>(sg.us + (size_t)og * np4 + min(li0, max(np4 - 16, 0)));
+      const bool whole = li0 + 16 <= np4;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sz[e] = li0 + e < sg.n ? sg.us[(size_t)og * np4 + li0 + e] : 0u;
+      for (int j = 0; j < 4; ++j) {
+        const uint4 v = whole ? sp[j] : make_uint4(0u, 0u, 0u, 0u);
+        sz[4 * j] = v.x; sz[4 * j + 1] = v.y; sz[4 * j + 2] = v.z; sz[4 * j + 3] = v.w;
+      }
+      if (!whole) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sz[e] = li0 + e < sg.n ? sg.us[(size_t)og * np4 + li0 + e] : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sz[e] = li0 + e < sg.n ? sz[e] : 0u;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) tr[j] = *reinterpret_cast<const f32x4*>(tsrc + pk + 4 * j);
   };
@@ -332,15 +371,16 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
     uint4* da = reinterpret_cast<uint4*>(&lds[s][0][arow * kPUPad + hs * 32]);
     da[0] = make_uint4(h[0], h[1], h[2], h[3]);
     da[1] = make_uint4(h[4], h[5], h[6], h[7]);
+    // t'[p] arrives as one word hi | lo << 16: two ranks' words give a hi
+    // word and a lo word
     uint32_t hi[8], lo[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; e += 2) {
-        const float v0 = tr[j][e] * tinv, v1 = tr[j][e + 1] * tinv;
-        const uint32_t h0 = f16b(v0), h1 = f16b(v1);
-        hi[2 * j + e / 2] = h0 | (h1 << 16);
-        lo[2 * j + e / 2] = f16b(v0 - f16v(h0)) | (f16b(v1 - f16v(h1)) << 16);
+        const uint32_t w0 = __float_as_uint(tr[j][e]), w1 = __float_as_uint(tr[j][e + 1]);
+        hi[2 * j + e / 2] = (w0 & 0xFFFFu) | (w1 << 16);
+        lo[2 * j + e / 2] = (w0 >> 16) | (w1 & 0xFFFF0000u);
       }
     uint4* dh = reinterpret_cast<uint4*>(&lds[s][1][arow * kPUPad + hs * 32]);
     uint4* dl = reinterpret_cast<uint4*>(&lds[s][2][arow * kPUPad + hs * 32]);
@@ -486,6 +526,9 @@ int launch_dense_prefill(const ApplyArgs& a) {
     // grid x a multiple of 8, so that blockIdx.x mod 8 is the XCD the tile order assumes
     hipLaunchKernelGGL(k_pf_v, dim3((tv + 7) / 8 * 8, (unsigned)cnt), dim3(256), 0, st, b, a.x, a.in, a.wl.drp, xsc,
                        tw, tmax);
+    const int tok0 = b.t[0].s0, ntok = b.t[cnt - 1].s0 + b.t[cnt - 1].nt - tok0;   // the batch's segments are contiguous
+    const size_t nth = (size_t)ntok * (a.wl.drp / 4);
+    hipLaunchKernelGGL(k_pf_t, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st, tw, tmax, tok0, ntok, a.wl.drp);
     hipLaunchKernelGGL(k_pf_u, dim3((tu + 7) / 8 * 8, (unsigned)cnt), dim3(256), 0, st, b, A.out, a.wl.drp, tw, tmax,
                        ybase, A.y);
   }
