@@ -361,12 +361,14 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
     uint32_t h[8];
     if (bsel == 8) {   // cw holds this thread's 16 codes, one byte each
       Dequant<8, 0, 0, 16, false>::run(cw, sz, h);
-    } else if (bsel == 3) {   // cw holds the K-block's 32 codes
-      if (hs == 0) Dequant<3, 0, 0, 16, false>::run(cw, sz, h);
-      else Dequant<3, 16, 0, 16, false>::run(cw, sz, h);
-    } else {
-      if (hs == 0) Dequant<2, 0, 0, 16, false>::run(cw, sz, h);
-      else Dequant<2, 16, 0, 16, false>::run(cw, sz, h);
+    } else if (bsel == 3) {   // cw holds the K-block's 32 codes: this half's 16 from bit 48 hs
+      // (the halves select their bits before one dequant: a branch on hs
+      // would run both dequants on every wave, half the lanes idle)
+      const uint32_t w[2] = {hs ? (cw[1] >> 16) | (cw[2] << 16) : cw[0], hs ? cw[2] >> 16 : cw[1]};
+      Dequant<3, 0, 0, 16, false>::run(w, sz, h);
+    } else {   // 2-bit: this half's 16 codes are word hs
+      const uint32_t w[1] = {hs ? cw[1] : cw[0]};
+      Dequant<2, 0, 0, 16, false>::run(w, sz, h);
     }
     uint4* da = reinterpret_cast<uint4*>(&lds[s][0][arow * kPUPad + hs * 32]);
     da[0] = make_uint4(h[0], h[1], h[2], h[3]);
