@@ -251,6 +251,44 @@ dc_status dc_error_table(int32_t r, int32_t in, int32_t ncal, const float* sigma
                          size_t ws_bytes, void* stream);
 
 /*
+ * dc_svd -- the r leading singular pairs of a delta on the GPU: the first
+ * step of compressing it ([P1] technical principles: the delta's low-rank
+ * decomposition; [P4] §2.4 step 1: SVD of the delta, then bit allocation and
+ * quantization), so that a tenant can be onboarded without a host SVD.  The
+ * outputs are dc_pack_device's inputs.  Synchronous: returns when they are
+ * written (it waits on `stream` between sweeps).
+ *   delta   device fp32 [out][in] row-major, 4-byte aligned; out, in >= 1
+ *   r       pairs wanted, 0 <= r <= min(out, in)
+ *   U       device fp32 [r][out], row i = u_i
+ *   sigma   device fp32 [r], descending (index order on ties)
+ *   V       device fp32 [r][in], row i = v_i
+ *   ws      device workspace, 256-byte aligned, of ws_bytes >=
+ *           dc_svd_workspace_bytes(out, in) (about 16 m^2 bytes for
+ *           m = min(out, in))
+ *   sweeps  host int32 or NULL: Jacobi sweeps run
+ * Each pair is signed so that the largest-magnitude entry of v_i is positive
+ * (lowest index on ties); for sigma_i = 0 the vector derived from the other
+ * (u_i when out >= in, else v_i) is zero.
+ * Method: G = A^T A (in <= out) or A A^T, m x m, summed in fp64 from the
+ * fp32 entries; its eigenpairs by block Jacobi (32-index blocks, pairs of
+ * blocks diagonalized in LDS, sweeps of a round-robin tournament) until every
+ * pair of a sweep is diagonal to |G_ab| <= 1e-13 (sqrt(|G_aa G_bb|) +
+ * trace(G) / 10); sigma_i = sqrt(lambda_i) and the other vectors as
+ * A v_i / sigma_i (resp. A^T u_i / sigma_i) in fp64 sums.  Accuracy:
+ * sigma_i to about 1e-16 sigma_1^2 / sigma_i^2 relative (the Gram matrix
+ * squares the condition), vectors to about 1e-14 trace(G) over the gap
+ * between their eigenvalue and the neighbouring ones.
+ * Errors: DC_ERR_INVALID_ARG (NULL, r out of range), DC_ERR_SHAPE (out or
+ * in < 1), DC_ERR_ALIGN, DC_ERR_BUFFER, DC_ERR_UNSUPPORTED (min(out, in) >
+ * 16384, or out * in of 2^31 or more), DC_ERR_RANGE (a non-finite entry, or
+ * no convergence within 40 sweeps: outputs unspecified), DC_ERR_HIP.
+ * Allocates nothing; writes U, sigma, V and the workspace.
+ */
+size_t dc_svd_workspace_bytes(int32_t out, int32_t in);
+dc_status dc_svd(int32_t out, int32_t in, int32_t r, const float* delta, float* U, float* sigma, float* V, void* ws,
+                 size_t ws_bytes, int32_t* sweeps, void* stream);
+
+/*
  * dc_pack_codes -- pack already-quantized codes (host, synchronous).
  *   codes_u  host uint8 [r][out], code of u_i at row o (< 2^b of its segment)
  *   codes_v  host uint8 [r][in]

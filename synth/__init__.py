@@ -156,6 +156,19 @@ def sigma_profile(r: int) -> np.ndarray:
     return (0.05 * i ** -0.8).astype(np.float32)
 
 
+def spectral_delta(seed: int, out: int, inn: int) -> np.ndarray:
+    """fp32 delta [out][in] = U0 diag(sigma) V0^T with orthonormal U0, V0
+    (QR of Gaussian matrices) and sigma_i = 0.05 i^-0.8 over min(out, in)
+    pairs: a few large singular values and a long tail, the spectrum shape the
+    pages describe for fine-tuning deltas.  Draw order: U0, V0."""
+    rng = np.random.default_rng(seed)
+    m = min(out, inn)
+    u0, _ = np.linalg.qr(rng.standard_normal((out, m)))
+    v0, _ = np.linalg.qr(rng.standard_normal((inn, m)))
+    s = sigma_profile(m).astype(np.float64)
+    return ((u0 * s) @ v0.T).astype(np.float32)
+
+
 def random_delta_codes(rng: np.random.Generator, out: int, inn: int,
                        n8: int, n3: int, n2: int) -> DeltaCodes:
     """Uniform codes, log-normal fp16 scales, uniform integer zeros."""

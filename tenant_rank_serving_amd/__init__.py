@@ -13,5 +13,5 @@ from ._lib import (  # noqa: F401
     DC_KIND_BITDELTA, DC_KIND_LOWRANK, BaselineGroupCall, BaselineView, dc_apply_baseline_multitenant,
     dc_apply_baseline_multitenant_group, dc_baseline_algorithmic_bytes, dc_baseline_bytes,
     dc_baseline_workspace_bytes, dc_pack_bitdelta, dc_pack_lowrank,
-    DC_ERR_MAX_WIDTHS, dc_error_table, dc_error_table_workspace_bytes,
+    DC_ERR_MAX_WIDTHS, dc_error_table, dc_error_table_workspace_bytes, dc_svd, dc_svd_workspace_bytes,
 )

@@ -37,12 +37,12 @@ EXPORTS = ("dc_status_string", "dc_check_spec", "dc_packed_bytes", "dc_algorithm
            "dc_apply_multitenant_group_timed", "dc_baseline_bytes", "dc_baseline_algorithmic_bytes",
            "dc_pack_lowrank", "dc_pack_bitdelta", "dc_baseline_workspace_bytes",
            "dc_apply_baseline_multitenant", "dc_apply_baseline_multitenant_group",
-           "dc_error_table_workspace_bytes", "dc_error_table")
+           "dc_error_table_workspace_bytes", "dc_error_table", "dc_svd_workspace_bytes", "dc_svd")
 DC_ERR_MAX_WIDTHS = 8
 DC_KIND_LOWRANK, DC_KIND_BITDELTA = 1, 2
 _SIZE_FNS = ("dc_status_string", "dc_packed_bytes", "dc_algorithmic_bytes", "dc_workspace_bytes",
              "dc_group_workspace_bytes", "dc_baseline_bytes", "dc_baseline_algorithmic_bytes",
-             "dc_baseline_workspace_bytes", "dc_error_table_workspace_bytes")
+             "dc_baseline_workspace_bytes", "dc_error_table_workspace_bytes", "dc_svd_workspace_bytes")
 STAGES = ("route", "xprep", "base", "vside", "uside")
 
 
@@ -130,6 +130,9 @@ def lib() -> ctypes.CDLL:
         L.dc_error_table_workspace_bytes.restype = ctypes.c_size_t
         L.dc_error_table_workspace_bytes.argtypes = [i32, i32, i32]
         L.dc_error_table.argtypes = [i32, i32, i32, _P, _P, _P, _P, i32, _P, _P, _P, ctypes.c_size_t, _P]
+        L.dc_svd_workspace_bytes.restype = ctypes.c_size_t
+        L.dc_svd_workspace_bytes.argtypes = [i32, i32]
+        L.dc_svd.argtypes = [i32, i32, i32, _P, _P, _P, _P, _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32), _P]
         for name in EXPORTS:
             if name not in _SIZE_FNS:
                 getattr(L, name).restype = ctypes.c_int32
@@ -520,3 +523,19 @@ def dc_error_table(sigma, V, X, widths, err, flag, ws, stream=None) -> None:
     _check(lib().dc_error_table(int(r), int(inn), int(ncal), _dptr(sigma, "sigma"), _dptr(V, "V"), _dptr(X, "X"),
                                 w.ctypes.data, int(w.size), _dptr(err, "err"), _dptr(flag, "flag"), _dptr(ws, "ws"),
                                 ws.numel() * ws.element_size(), _stream(stream)), "dc_error_table")
+
+
+def dc_svd_workspace_bytes(out: int, inn: int) -> int:
+    return int(lib().dc_svd_workspace_bytes(int(out), int(inn)))
+
+
+def dc_svd(delta, r: int, U, sigma, V, ws, stream=None) -> int:
+    """delta fp32 [out][in] (device tensor); U fp32 [r][out], sigma fp32 [r],
+    V fp32 [r][in] (device) are written; returns the Jacobi sweeps run.
+    Synchronous."""
+    out, inn = delta.shape
+    sw = ctypes.c_int32(0)
+    _check(lib().dc_svd(int(out), int(inn), int(r), _dptr(delta, "delta"), _dptr(U, "U"), _dptr(sigma, "sigma"),
+                        _dptr(V, "V"), _dptr(ws, "ws"), ws.numel() * ws.element_size(), ctypes.byref(sw),
+                        _stream(stream)), "dc_svd")
+    return int(sw.value)

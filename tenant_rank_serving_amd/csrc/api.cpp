@@ -410,4 +410,25 @@ dc_status dc_dequant(const dc_delta_view* d, uint16_t* u_fp16, uint16_t* v_fp16,
   return dc::launch_dequant(t, d->spec.out, d->spec.in, u_fp16, v_fp16, stream) == 0 ? DC_OK : DC_ERR_HIP;
 }
 
+size_t dc_svd_workspace_bytes(int32_t out, int32_t in) {
+  if (out < 1 || in < 1 || (out < in ? out : in) > 16384) return 0;
+  return dc::svd_layout(out, in, 0).total;
+}
+
+dc_status dc_svd(int32_t out, int32_t in, int32_t r, const float* delta, float* U, float* sigma, float* V, void* ws,
+                 size_t ws_bytes, int32_t* sweeps, void* stream) {
+  if (sweeps) *sweeps = 0;
+  if (out < 1 || in < 1) return DC_ERR_SHAPE;
+  const int32_t m = out < in ? out : in;
+  if (r < 0 || r > m || !delta || !ws || (r > 0 && (!U || !sigma || !V))) return DC_ERR_INVALID_ARG;
+  if (m > 16384 || (size_t)out * in >= ((size_t)1 << 31)) return DC_ERR_UNSUPPORTED;
+  if (!aligned(delta, 4) || !aligned(ws, 256) || (U && !aligned(U, 4)) || (V && !aligned(V, 4)) ||
+      (sigma && !aligned(sigma, 4)))
+    return DC_ERR_ALIGN;
+  if (ws_bytes < dc_svd_workspace_bytes(out, in)) return DC_ERR_BUFFER;
+  if (r == 0) return DC_OK;   // nothing to write
+  const int st = dc::launch_svd(out, in, r, delta, U, sigma, V, static_cast<uint8_t*>(ws), sweeps, stream);
+  return st == 0 ? DC_OK : (st > 0 ? DC_ERR_RANGE : DC_ERR_HIP);
+}
+
 }  // extern "C"

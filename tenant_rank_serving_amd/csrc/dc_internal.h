@@ -426,4 +426,17 @@ int launch_error_table(int32_t r, int32_t in, int32_t ncal, const float* sigma, 
                        const int32_t* widths, int32_t nw, double* err, uint32_t* flag, float* dv, void* stream);
 int launch_pack(int32_t out, int32_t in, int32_t n8, int32_t n3, int32_t n2, const float* U, const float* sigma,
                 const float* V, uint8_t* dst, uint32_t* flag, void* stream);
+// On-device SVD of a delta (block Jacobi on the fp64 Gram matrix): the
+// workspace regions, the sweep cap and the convergence bound.
+constexpr int kSvdMaxSweeps = 40;
+constexpr double kSvdTol = 1e-13;
+struct SvdLayout {
+  int m, mp;   // min(out, in) and its padding to a multiple of 64
+  size_t G, W, Q, off, d, fac, perm, flag, total;
+};
+SvdLayout svd_layout(int32_t out, int32_t in, int32_t r);
+// 0: done; 1: a non-finite entry; 2: not converged in kSvdMaxSweeps; -1: HIP error
+int launch_svd(int32_t out, int32_t in, int32_t r, const float* A, float* U, float* sigma, float* V, uint8_t* ws,
+               int32_t* sweeps_used, void* stream);
+
 }  // namespace dc

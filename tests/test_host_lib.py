@@ -393,3 +393,28 @@ def test_error_table_argument_checks(L):
     assert et(r, inn, ncal, S, V + 4, Xc, wp, 4, E, F, WS, need, None) == trs.DC_ERR_ALIGN
     assert et(r, inn, ncal, S, V, Xc, wp, 4, E + 4, F, WS, need, None) == trs.DC_ERR_ALIGN
     assert et(-1, inn, ncal, S, V, Xc, wp, 4, E, F, WS, need, None) == trs.DC_ERR_INVALID_ARG
+
+
+def test_svd_argument_checks(L):
+    """dc_svd rejects bad arguments on the host before any launch."""
+    out, inn, r = 320, 200, 64
+    need = trs.dc_svd_workspace_bytes(out, inn)
+    mp = 256   # min(out, in) = 200 padded to a multiple of 64
+    assert need >= 2 * mp * mp * 8
+    assert trs.dc_svd_workspace_bytes(0, inn) == 0
+    assert trs.dc_svd_workspace_bytes(20000, 20000) == 0
+    sv = L.dc_svd
+    D, U, S, V = 0x100000, 0x200000, 0x300000, 0x400000
+    assert sv(out, inn, r, D, U, S, V, WS, need - 1, None, None) == trs.DC_ERR_BUFFER
+    assert sv(0, inn, r, D, U, S, V, WS, need, None, None) == trs.DC_ERR_SHAPE
+    assert sv(out, -1, r, D, U, S, V, WS, need, None, None) == trs.DC_ERR_SHAPE
+    assert sv(out, inn, -1, D, U, S, V, WS, need, None, None) == trs.DC_ERR_INVALID_ARG
+    assert sv(out, inn, inn + 1, D, U, S, V, WS, need, None, None) == trs.DC_ERR_INVALID_ARG
+    assert sv(out, inn, r, None, U, S, V, WS, need, None, None) == trs.DC_ERR_INVALID_ARG
+    assert sv(out, inn, r, D, None, S, V, WS, need, None, None) == trs.DC_ERR_INVALID_ARG
+    assert sv(out, inn, r, D, U, S, V, None, need, None, None) == trs.DC_ERR_INVALID_ARG
+    assert sv(out, inn, r, D + 2, U, S, V, WS, need, None, None) == trs.DC_ERR_ALIGN
+    assert sv(out, inn, r, D, U, S, V, WS + 16, need, None, None) == trs.DC_ERR_ALIGN
+    assert sv(20000, 20000, r, D, U, S, V, WS, need, None, None) == trs.DC_ERR_UNSUPPORTED
+    # r = 0 writes nothing and launches nothing
+    assert sv(out, inn, 0, D, None, None, None, WS, need, None, None) == trs.DC_OK
