@@ -382,6 +382,32 @@ def pack_bench(args):
         "ms": round(ms_e, 4), "product_TFLOPs_fp32": round(flops / (ms_e * 1e-3) / 1e12, 2),
         "oracle_ms_scaled": round(t_orc_e * r / nrow * 1e3, 1),
         "oracle_sample": "alloc.error_table on %d rows (%.2f s), scaled to %d rows" % (nrow, t_orc_e, r)}
+    # the SVD in front of the packer (dc_svd) on the layer's two shapes, the
+    # ranks the 1/16 budget keeps; the oracle's numpy SVD on a 1024 x 1024
+    # sample of the same spectrum, scaled by the cube of the size
+    svd = {}
+    for out, inn in ((4096, 4096), (11008, 4096)):
+        r = sum(synth.groups_for(out, inn, 16))
+        delta = torch.from_numpy(synth.spectral_delta(21, out, inn)).to(dev)
+        Us = torch.empty((r, out), device=dev)
+        ss = torch.empty((r,), device=dev)
+        Vs = torch.empty((r, inn), device=dev)
+        sws = torch.empty(trs.dc_svd_workspace_bytes(out, inn), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        sweeps = trs.dc_svd(delta, r, Us, ss, Vs, sws)
+        torch.cuda.synchronize()
+        svd["%dx%d" % (out, inn)] = {"pairs": r, "ms": round((time.perf_counter() - t0) * 1e3, 1), "sweeps": sweeps}
+        del sws, delta
+    small = synth.spectral_delta(22, 1024, 1024).astype(np.float64)
+    t0 = time.perf_counter()
+    quant.svd_pairs(small)
+    t_svd = time.perf_counter() - t0
+    svd["oracle_ms_4096x4096_scaled"] = round(t_svd * 64 * 1e3, 1)
+    svd["oracle_sample"] = "quant.svd_pairs (numpy, all host cores) on 1024 x 1024 (%.2f s), times 64" % t_svd
+    svd["workload"] = ("dc_svd: fp64 Gram matrix, block Jacobi, derived vectors; synthetic deltas with "
+                       "sigma_i = 0.05 i^-0.8 (host wall clock, synchronous call)")
+    line["svd"] = svd
     print(json.dumps(line), flush=True)
 
 

@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(256) k_bj_eig(const double* __restrict__ G, in
   const double before = offdiag();
   if (tid == 0) atomicMax(off, (unsigned long long)__double_as_longlong(before));
   double cur = before;
-  for (int sw = 0; sw < 16 && cur > kSvdTol * 1e-2; ++sw) {
+  for (int sw = 0; sw < 10 && cur > kSvdTol * 0.1; ++sw) {   // quadratic: a few sweeps
     for (int k = 0; k < kSP - 1; ++k) {
       if (tid < kSP / 2) {   // the round's rotations (stable symmetric Schur pair)
         int a, b;
