@@ -150,9 +150,20 @@ struct ActEntry {
   // arithmetic); zero for the backbone-only bucket and the baselines
   uint32_t off[DC_REG_COUNT];
   uint32_t total;
-  uint32_t pad_[2];
+  // Delta-CoMe calls, U side: the tenant's derived sizes, the same for every
+  // block of the item (the U blocks' waves would otherwise each work them
+  // out with scalar instructions, which the waves of a compute unit share):
+  // t positions of the 3- and 2-bit segments; scale-row lengths (ranks
+  // rounded up to 4) of the 8-, 3- and 2-bit segments; 128-rank chunks of
+  // the 3-bit segment and of both; words per U row, K-blocks and words of
+  // the last K-block of the 3- and 2-bit segments
+  int32_t tb3, tb2;
+  int32_t np8, np3, np2;
+  int32_t nc3, nc;
+  int32_t rw3, rw2, kbn3, kbn2, wl3, wl2;
+  uint32_t pad_[1];
 };
-static_assert(sizeof(ActEntry) == 96, "two scalar loads per block");
+static_assert(sizeof(ActEntry) == 144, "three scalar loads per block");
 constexpr int kChunkRows = 8;   // token rows per work item (one V-side and one U-side pass)
 // Work items of a call of n tenants and T tokens: at most one partly filled
 // chunk per bucket (n tenants + the backbone-only bucket) plus T / kChunkRows.

@@ -25,6 +25,8 @@
 // the vector ALU with the fp16 dequantized weights fp16(s(q - z)).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "dc_internal.h"
 
 namespace dc {
@@ -109,6 +111,19 @@ __device__ __forceinline__ void list_active(const Tenant& mine, int32_t n, const
 #pragma unroll
     for (int i = 0; i < DC_REG_COUNT; ++i) e.off[i] = (uint32_t)L.off[i];
     e.total = (uint32_t)L.total;
+    e.tb3 = t_base(e.n8, e.n3, 1);
+    e.tb2 = t_base(e.n8, e.n3, 2);
+    e.np8 = (int)round_up(e.n8, 4);
+    e.np3 = (int)round_up(e.n3, 4);
+    e.np2 = (int)round_up(e.n2, 4);
+    e.nc3 = (e.n3 + kGroup - 1) / kGroup;
+    e.nc = e.nc3 + (e.n2 + kGroup - 1) / kGroup;
+    e.rw3 = u_row_words(e.n3, 3);
+    e.rw2 = u_row_words(e.n2, 2);
+    e.kbn3 = (e.n3 + kKBlock - 1) / kKBlock;
+    e.kbn2 = (e.n2 + kKBlock - 1) / kKBlock;
+    e.wl3 = e.rw3 - (e.kbn3 - 1) * 3;
+    e.wl2 = e.rw2 - (e.kbn2 - 1) * 2;
   }
   for (int j = 0; j < items; ++j) {
     e.p0 = so[b] + j * kChunkRows;
@@ -362,6 +377,7 @@ struct VGrp {
 // uniform offset.
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 struct VBuf {
   __amdgpu_buffer_rsrc_t rc, rz;
   uint32_t oc[kVTiles], oz[kVTiles];
@@ -684,15 +700,19 @@ struct UGroup {
   const ActEntry* act;   // [m][nact] work items
   const MatParams* mp;   // [m] per-matrix parameters (workspace)
   int32_t nact;
+  int32_t m;             // matrices of the group
+  uint32_t mmagic;       // ceil(2^32 / m) for m > 1: y / m = mulhi(y, mmagic)
 };
 
 __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) k_uside(int32_t n, int32_t in, const int32_t* __restrict__ perm,
                                                         int32_t T, UGroup ug) {
   const int g = blockIdx.x;
   // rows item-major, matrix fastest: every matrix's work items (listed
-  // first) run before the empty entries of any
-  const int mg = gridDim.y / ug.nact;   // matrices of the group
-  const int mj = blockIdx.y % mg, item = blockIdx.y / mg;
+  // first) run before the empty entries of any.  item = y / m by a
+  // multiply-high (exact for y < 2^31), so the block does no division.
+  const int yy = blockIdx.y;
+  const int item = ug.m == 1 ? yy : (int)__umulhi((uint32_t)yy, ug.mmagic);
+  const int mj = yy - item * ug.m;
   const MatParams P = ug.mp[mj];
   const ActEntry e = ug.act[mj * ug.nact + item];
   // every field in hand before the first branch: one scalar round trip
@@ -700,6 +720,8 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
                "s"(e.n2), "s"(e.k), "s"(e.p0), "s"(e.p1), "s"(n), "s"(in), "s"(perm), "s"(T));
   asm volatile("" ::"s"(e.off[DC_REG_UC8]), "s"(e.off[DC_REG_UC3]), "s"(e.off[DC_REG_UC2]), "s"(e.off[DC_REG_US8]),
                "s"(e.off[DC_REG_US3]), "s"(e.off[DC_REG_US2]), "s"(e.total));
+  asm volatile("" ::"s"(e.tb3), "s"(e.tb2), "s"(e.np8), "s"(e.np3), "s"(e.np2), "s"(e.nc3), "s"(e.nc), "s"(e.rw3),
+               "s"(e.rw2), "s"(e.kbn3), "s"(e.kbn2), "s"(e.wl3), "s"(e.wl2));
   const int out = P.out;
   if (g * kGroup >= out) return;
   const int rs = P.rs;
@@ -719,56 +741,53 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
     return;
   }
   __shared__ ULds S;
-  Tenant tn;
-  tn.base = e.base;
-  tn.n8 = e.n8;
-  tn.n3 = e.n3;
-  tn.n2 = e.n2;
-  tn.pad_ = 0;
-  Layout L;
-  layout_of_item(e, &L);
-  const Seg seg3 = seg_of(tn, L, 1), seg2 = seg_of(tn, L, 2), s8 = seg_of(tn, L, 0);
-  const int tb3 = t_base(tn.n8, tn.n3, 1), tb2 = t_base(tn.n8, tn.n3, 2);
-  const int np3 = (int)round_up(seg3.n, 4), np2 = (int)round_up(seg2.n, 4);
-  const int nc3 = (seg3.n + 127) / 128, nc = nc3 + (seg2.n + 127) / 128;
-  const int gn = out / kGroup;
+  const int n8 = e.n8, n3 = e.n3, n2 = e.n2;
+  const int tb3 = e.tb3, tb2 = e.tb2;
+  const int nc3 = e.nc3, nc = e.nc, nc2 = nc - nc3;
+  const int tot = (int)e.total;
   const int orow = g * kGroup + wave * 16 + col;
   const __amdgpu_buffer_rsrc_t rt =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(tv), 0, T * rs * 4, kBufFlags);
-  // the tenant's whole packed buffer: code and scale regions go in the uniform offset
+  // the tenant's whole packed buffer; an offset of tot (its size) is out of
+  // range: such a load returns zeros without a memory request
   const __amdgpu_buffer_rsrc_t rten =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(tn.base), 0, (int)L.total, kBufFlags);
-  const int oc3 = (int)L.off[DC_REG_UC3], oc2 = (int)L.off[DC_REG_UC2];
-  const int ou3 = (int)L.off[DC_REG_US3] + g * np3 * 4, ou2 = (int)L.off[DC_REG_US2] + g * np2 * 4;
-  // the lane's byte offset of K-block kb of its row in the 3- or 2-bit code region
-  const int rw3 = (int)u_row_words(seg3.n, 3), rw2 = (int)u_row_words(seg2.n, 2);
-  const int kbn3 = (seg3.n + kKBlock - 1) / kKBlock, kbn2 = (seg2.n + kKBlock - 1) / kKBlock;
-  // the 12 bytes of chunk c of this lane's codes from its K-block's start
-  // (a 2-bit chunk uses 8); past the last chunk: the last again
-  auto load = [&](uint32_t (&w)[3], int c) __attribute__((always_inline)) {
-    c = min(c, nc - 1);
-    const bool three = c < nc3;
-    const int b = three ? 3 : 2;
-    const int kbn = three ? kbn3 : kbn2, rw = three ? rw3 : rw2;
-    const int kb = min(4 * (three ? c : c - nc3) + q, kbn - 1);
-    const int wl = rw - (kbn - 1) * b;   // words of the last K-block
-    const int off = ((orow >> 4) * 16 * rw + kb * 16 * b + (orow & 15) * (kb == kbn - 1 ? wl : b)) * 4;
-    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rten, off, three ? oc3 : oc2, 0);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(e.base), 0, tot, kBufFlags);
+  const int ou3 = (int)e.off[DC_REG_US3] + g * e.np3 * 4, ou2 = (int)e.off[DC_REG_US2] + g * e.np2 * 4;
+  // Codes of chunk c of this lane: K-block kb = 4c + q of row orow.  Full
+  // K-blocks of a 16-row tile sit 16 b words apart and hold b words per row;
+  // the last one holds wl words per row; past it nothing (offset tot).
+  const int row = orow & 15, tile = orow >> 4;
+  const int a3 = (int)e.off[DC_REG_UC3] + (tile * 16 * e.rw3 + q * 16 * 3 + row * 3) * 4;
+  const int l3 = (int)e.off[DC_REG_UC3] + (tile * 16 * e.rw3 + (e.kbn3 - 1) * 16 * 3 + row * e.wl3) * 4;
+  const int a2 = (int)e.off[DC_REG_UC2] + (tile * 16 * e.rw2 + q * 16 * 2 + row * 2) * 4;
+  const int l2 = (int)e.off[DC_REG_UC2] + (tile * 16 * e.rw2 + (e.kbn2 - 1) * 16 * 2 + row * e.wl2) * 4;
+  const int kl3 = e.kbn3 - 1, kl2 = e.kbn2 - 1;
+  auto load3 = [&](uint32_t (&w)[3], int c) __attribute__((always_inline)) {
+    const int kb = 4 * c + q;
+    const int off = kb < kl3 ? a3 + c * (4 * 16 * 3 * 4) : (kb == kl3 ? l3 : tot);
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rten, off, 0, 0);
     w[0] = v.x;
     w[1] = v.y;
     w[2] = v.z;
+  };
+  auto load2 = [&](uint32_t (&w)[2], int j) __attribute__((always_inline)) {
+    const int kb = 4 * j + q;
+    const int off = kb < kl2 ? a2 + j * (4 * 16 * 2 * 4) : (kb == kl2 ? l2 : tot);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rten, off, 0, 0);
+    w[0] = v.x;
+    w[1] = v.y;
   };
   // 8-bit U weights of this lane's output row (first kU8Max pairs): scale
   // word and code, loaded behind the first window's A-prep inputs and codes,
   // dequantized to fp16 in the epilogue
   uint32_t u8s[kU8Max], u8c[kU8Max];
   // (with no 8-bit pairs both point at the buffer's first word: every load stays inside it)
-  const int ous8 = s8.n > 0 ? (int)L.off[DC_REG_US8] + g * (int)round_up(s8.n, 4) * 4 : 0;
-  const int ouc8 = s8.n > 0 ? (int)L.off[DC_REG_UC8] + orow * s8.n : 0;
+  const int ous8 = n8 > 0 ? (int)e.off[DC_REG_US8] + g * e.np8 * 4 : 0;
+  const int ouc8 = n8 > 0 ? (int)e.off[DC_REG_UC8] + orow * n8 : 0;
   auto load_u8 = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kU8Max; ++i) {   // unconditional (unused past s8.n): straight-line waits
-      const int i8 = min(i, max(s8.n - 1, 0));
+    for (int i = 0; i < kU8Max; ++i) {   // unconditional (unused past n8): straight-line waits
+      const int i8 = min(i, max(n8 - 1, 0));
       u8s[i] = __builtin_amdgcn_raw_buffer_load_b32(rten, ous8 + i8 * 4, 0, 0);
       u8c[i] = __builtin_amdgcn_raw_buffer_load_b8(rten, ouc8 + i8, 0, 0);
     }
@@ -790,15 +809,18 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
     const int pb = p0;
     const int nt = min(kURows, p1 - pb);
     const int nops = (nt + 3) >> 2;   // matrix-core ops per tile and chunk
-    const int wcap = kUWin / nops;     // chunks per window (a multiple of kUDepth)
-    uint32_t cr[kUDepth][3];
+    const int wcap = nops == 1 ? kUWin : kUWin / 2;   // chunks per window
+    // The codes stream through two register rings: the 3-bit chunks (slot
+    // c % 2) and the 2-bit chunks (slot j % 4).  Windows start their 3-bit
+    // part on an even chunk and their 2-bit part on a multiple of 4, so the
+    // slots of an unrolled loop are fixed; a step past the last chunk reloads
+    // an out-of-range slot (zeros, no memory request).
+    uint32_t cr3[2][3], cr2[4][2];
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     // the epilogue's inputs, in flight during the pass: lane group q writes
     // tokens 2q and 2q + 1 of the pass (their original indices, then W x and
-    // t of the 8-bit pairs).  The indices go out first: the W x loads wait
-    // for them alone.
-    // The token indices go out first: the W x loads, last in the burst,
-    // wait for them alone.
+    // t of the 8-bit pairs).  The token indices go out first: the W x loads,
+    // last in the burst, wait for them alone.
     int tko[2];
     float ybo[2] = {0.f, 0.f}, t8o[2][kU8Max];
 #pragma unroll
@@ -819,25 +841,22 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll
       for (int h = 0; h < 2; ++h) ybo[h] = gload(ybase ? ybase + (size_t)tko[h] * out + orow : tv + h);
     };
-    auto epi_loads = [&]() __attribute__((always_inline)) {
-      epi_loads_t8();
-      epi_loads_yb();
-    };
     auto epi_select = [&]() __attribute__((always_inline)) {   // values past what the matrix has are zero
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         ybo[h] = ybase ? ybo[h] : 0.f;
 #pragma unroll
-        for (int i = 0; i < kU8Max; ++i) t8o[h][i] = i < s8.n ? t8o[h][i] : 0.f;
+        for (int i = 0; i < kU8Max; ++i) t8o[h][i] = i < n8 ? t8o[h][i] : 0.f;
       }
     };
-    // A operands of chunks [cw0, cw0 + wc) for the pass's token rows.  Thread
-    // tid takes chunk pcl of the window and rows 4h..4h+3: with one op per
-    // chunk the 512 threads cover 16 chunks x rows 0-3, with two 8 chunks x
-    // both halves.  The inputs (scale/zero words, t) are loaded apart from
-    // the math, so that the first window's code ring and the epilogue's
-    // inputs go out in the same burst behind them (vmcnt is in order: the
-    // math then waits for its own loads only).
+    // A operands of one window: its 3-bit chunks w3 .. w3 + n3w - 1, then
+    // its 2-bit chunks j0 .. j0 + n2w - 1, at window-local chunk index pcl,
+    // for the pass's token rows.  Thread tid takes chunk pcl and rows
+    // 4h..4h+3: with one op per chunk the 512 threads cover 16 chunks x rows
+    // 0-3, with two 8 chunks x both halves.  The inputs (scale/zero words, t)
+    // are loaded apart from the math, so that the first window's code rings
+    // and the epilogue's inputs go out in the same burst behind them (vmcnt
+    // is in order: the math then waits for its own loads only).
     const int pcl = nops == 1 ? tid >> 5 : (tid & 255) >> 5;
     const int hh = nops == 1 ? 0 : tid >> 8;
     struct APIn {
@@ -848,13 +867,12 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
     // rows past the pass's, load nothing: their offset is the resource's
     // record count, out of range, so the load returns zeros without a memory
     // request (the math masks those values anyway).
-    auto aprep_load = [&](int cw0, int wc, APIn& ai) __attribute__((always_inline)) {
-      const int c = cw0 + pcl;
-      const bool three = c < nc3;
-      const int li = (three ? c : c - nc3) * kGroup + m0;
-      const bool live = pcl < wc && li < (three ? seg3.n : seg2.n);
+    auto aprep_load = [&](int w3, int n3w, int j0, int n2w, APIn& ai) __attribute__((always_inline)) {
+      const bool three = pcl < n3w;
+      const int li = (three ? w3 + pcl : j0 + pcl - n3w) * kGroup + m0;
+      const bool live = pcl < n3w + n2w && li < (three ? n3 : n2);
       ai.usw = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, live ? li * 4 + (three ? ou3 : ou2) : (int)L.total, 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, live ? li * 4 + (three ? ou3 : ou2) : tot, 0, 0));
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         ai.tt[r] = __builtin_bit_cast(
@@ -862,12 +880,11 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
                        rt, live && 4 * hh + r < nt ? ((pb + 4 * hh + r) * rs + (three ? tb3 : tb2) + li) * 4 : T * rs * 4,
                        0, 0));
     };
-    auto aprep = [&](int cw0, int wc, const APIn& ai) __attribute__((always_inline)) {
-      const int c = cw0 + pcl;
-      const bool cok = pcl < wc;
-      const bool three = c < nc3;
-      const int sn = three ? seg3.n : seg2.n;
-      const int li = (three ? c : c - nc3) * kGroup + m0;
+    auto aprep = [&](int w3, int n3w, int j0, int n2w, const APIn& ai) __attribute__((always_inline)) {
+      const bool cok = pcl < n3w + n2w;
+      const bool three = pcl < n3w;
+      const int sn = three ? n3 : n2;
+      const int li = (three ? w3 + pcl : j0 + pcl - n3w) * kGroup + m0;
       const u32x4 usw = ai.usw;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -925,78 +942,102 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
         __builtin_amdgcn_sched_barrier(0);   // one token row at a time: bounded register use
       }
     };
-    // chunk c (window-local cl): matrix-core ops with the codes in cur, then
-    // the loads of chunk c + kUDepth into cur
-    auto step = [&](int c, int cl, uint32_t (&cur)[3]) __attribute__((always_inline)) {
-      const bool three = c < nc3;
-      const v8i bop = three ? b_fp6(cur[0], cur[1], cur[2]) : b_fp4(cur[0], cur[1]);
-      const int bs = three ? kScaleFp6Code : kScaleFp4Code;
+    // the matrix-core ops of window-local chunk cl against B operand bop
+    // (fp6 or fp4 codes); NOPS is the pass's ops per chunk
+    auto mops = [&](auto nops_c, int cl, const v8i& bop, auto three_c) __attribute__((always_inline)) {
+      constexpr int NOPS = decltype(nops_c)::value;
+      constexpr bool THREE = decltype(three_c)::value;
 #pragma unroll
-      for (int op = 0; op < 2; ++op) {
-        if (op < nops) {   // one A operand at a time: its registers are free again after hold()
-          const uint4* f = reinterpret_cast<const uint4*>(S.frag[cl * nops + op][q][col]);
-          const v8i a = v8_of(f[0], f[1]);
-          const int sa = ps < 3 ? (int)S.sc[cl][4 * op + tr4][q] - 5 * ps : 127;
-          f32x4 d = {0.f, 0.f, 0.f, 0.f};
-          d = three ? mma(a, bop, d, sa, kFmtFp6, kScaleFp6Code) : mma(a, bop, d, sa, kFmtFp4, kScaleFp4Code);
-          hold(d, a, bop, sa, bs);
-          acc[op] += d;
-        }
+      for (int op = 0; op < NOPS; ++op) {   // one A operand at a time: its registers are free again after hold()
+        const uint4* f = reinterpret_cast<const uint4*>(S.frag[cl * NOPS + op][q][col]);
+        const v8i a = v8_of(f[0], f[1]);
+        const int scv = S.sc[cl][4 * op + tr4][q];   // read by every lane: rows 12-15 take 127 below
+        const int sa = ps < 3 ? scv - 5 * ps : 127;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        d = THREE ? mma(a, bop, d, sa, kFmtFp6, kScaleFp6Code) : mma(a, bop, d, sa, kFmtFp4, kScaleFp4Code);
+        hold(d, a, bop, sa, THREE ? kScaleFp6Code : kScaleFp4Code);
+        acc[op] += d;
       }
-      load(cur, c + kUDepth);
       asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));   // sums land here, not deferred to the end
     };
-    if (lane < kURows) S.cz[wave][lane] = 0.f;   // this wave's z t' sums of the pass
-    // the matrix-core ops of window [cw0, cw0 + wc)
-    auto run = [&](int cw0, int wc) __attribute__((always_inline)) {
-      int c0 = cw0;
-      for (; c0 + kUDepth <= cw0 + wc; c0 += kUDepth) {
-#pragma unroll
-        for (int d = 0; d < kUDepth; ++d) step(c0 + d, c0 + d - cw0, cr[d]);
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using B3 = std::integral_constant<bool, true>;
+    using B2 = std::integral_constant<bool, false>;
+    // the matrix-core ops of one window; every step reloads its slot
+    // (straight-line loads, exact waits), the ops of a step past the
+    // window's chunks are skipped
+    auto run = [&](auto nops_c, int w3, int n3w, int j0, int n2w) __attribute__((always_inline)) {
+      for (int c = w3; c < w3 + n3w; c += 2) {
+        mops(nops_c, c - w3, b_fp6(cr3[0][0], cr3[0][1], cr3[0][2]), B3{});
+        load3(cr3[0], c + 2);
+        if (c + 1 < w3 + n3w) mops(nops_c, c + 1 - w3, b_fp6(cr3[1][0], cr3[1][1], cr3[1][2]), B3{});
+        load3(cr3[1], c + 3);
       }
-      // tail of the last window: fewer than kUDepth chunks (uniform guards)
+      for (int j = j0; j < j0 + n2w; j += 4) {
 #pragma unroll
-      for (int d = 0; d < kUDepth - 1; ++d)
-        if (c0 + d < cw0 + wc) step(c0 + d, c0 + d - cw0, cr[d]);
+        for (int d = 0; d < 4; ++d) {
+          if (d == 0 || j + d < j0 + n2w) mops(nops_c, n3w + j + d - j0, b_fp4(cr2[d][0], cr2[d][1]), B2{});
+          load2(cr2[d], j + d + 4);
+        }
+      }
     };
+    // window w: 3-bit chunks [w3, w3 + n3w), then 2-bit chunks [j0, j0 + n2w)
+    auto window = [&](int w3, int j0, int& n3w, int& n2w) __attribute__((always_inline)) {
+      n3w = min(nc3 - w3, wcap);
+      n2w = min(nc2 - j0, ((wcap - n3w) >> 2) << 2);
+    };
+    if (lane < kURows) S.cz[wave][lane] = 0.f;   // this wave's z t' sums of the pass
+    int w3 = 0, j0 = 0;
     if (nc == 0) {   // no 3/2-bit chunks: only the 8-bit pairs and W x
-      epi_loads();
+      epi_loads_t8();
+      epi_loads_yb();
       __syncthreads();   // every wave's zeroed sums are seen
     } else {
       // the first window, outside any loop: one burst of loads (A-prep
-      // inputs, the 8-bit pairs' inputs, the code ring, then W x once the
+      // inputs, the 8-bit pairs' inputs, both code rings, then W x once the
       // token indices are in), then the math
-      const int wc = min(wcap, nc);
+      int n3w, n2w;
+      window(w3, j0, n3w, n2w);
       APIn ai;
-      aprep_load(0, wc, ai);
+      aprep_load(w3, n3w, j0, n2w, ai);
       epi_loads_t8();
       __builtin_amdgcn_sched_barrier(0);
+      load3(cr3[0], 0);
+      load3(cr3[1], 1);
 #pragma unroll
-      for (int d = 0; d < kUDepth; ++d) load(cr[d], d);
+      for (int d = 0; d < 4; ++d) load2(cr2[d], d);
       __builtin_amdgcn_sched_barrier(0);
       epi_loads_yb();
       __builtin_amdgcn_sched_barrier(0);
-      aprep(0, wc, ai);
+      aprep(w3, n3w, j0, n2w, ai);
       lds_barrier_keep_vm();
-      run(0, wc);
+      if (nops == 1) run(I1{}, w3, n3w, j0, n2w);
+      else run(I2{}, w3, n3w, j0, n2w);
+      w3 += n3w;
+      j0 += n2w;
     }
-    for (int cw0 = wcap; cw0 < nc; cw0 += wcap) {
-      const int wc = min(wcap, nc - cw0);
+    while (w3 < nc3 || j0 < nc2) {
+      int n3w, n2w;
+      window(w3, j0, n3w, n2w);
       lds_barrier_keep_vm();   // the previous window's operands are consumed
       APIn ai;
-      aprep_load(cw0, wc, ai);
-      aprep(cw0, wc, ai);
+      aprep_load(w3, n3w, j0, n2w, ai);
+      aprep(w3, n3w, j0, n2w, ai);
       lds_barrier_keep_vm();
-      run(cw0, wc);
+      if (nops == 1) run(I1{}, w3, n3w, j0, n2w);
+      else run(I2{}, w3, n3w, j0, n2w);
+      w3 += n3w;
+      j0 += n2w;
     }
     // ---- epilogue: each token's three piece rows, sum_i z t' per token row, 8-bit pairs, W x, one rounding
-    f32x4 tot[2];
+    f32x4 tot4[2];
 #pragma unroll
     for (int op = 0; op < 2; ++op) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = acc[op][r] + swz_xor<16>(acc[op][r]);   // pieces 0+1, 2+(zero row)
-        tot[op][r] = v + __shfl_xor(v, 32, 64);
+        tot4[op][r] = v + __shfl_xor(v, 32, 64);
       }
     }
     // every wave's z t' sums were written before the last window's barrier
@@ -1005,21 +1046,23 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int i = 0; i < kU8Max; ++i)
       u8w[i] = (float)(_Float16)(f16f(u8s[i] & 0xFFFFu) * ((float)u8c[i] - f16f(u8s[i] >> 16)));
+    const uint32_t* __restrict__ us8 = reinterpret_cast<const uint32_t*>(e.base + e.off[DC_REG_US8]);
+    const uint8_t* __restrict__ uc8 = e.base + e.off[DC_REG_UC8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {   // lane group q writes tokens 2q and 2q + 1
       const int rw = 2 * q + h;
       if (rw < nt) {
-        const f32x4 tq = rw < 4 ? tot[0] : tot[1];
+        const f32x4 tq = rw < 4 ? tot4[0] : tot4[1];
         const int r = rw & 3;
         float v = r == 0 ? tq[0] : (r == 1 ? tq[1] : (r == 2 ? tq[2] : tq[3]));
 #pragma unroll
         for (int w8 = 0; w8 < kUWaves; ++w8) v -= S.cz[w8][rw];
 #pragma unroll
         for (int i = 0; i < kU8Max; ++i)
-          if (i < s8.n) v += u8w[i] * t8o[h][i];
-        for (int i = kU8Max; i < s8.n; ++i) {   // more 8-bit pairs than kept in registers
-          const uint32_t e = s8.us[(size_t)g * round_up(s8.n, 4) + i];
-          const float uh = (float)(_Float16)(f16f(e & 0xFFFFu) * ((float)s8.uc[(size_t)orow * s8.n + i] - f16f(e >> 16)));
+          if (i < n8) v += u8w[i] * t8o[h][i];
+        for (int i = kU8Max; i < n8; ++i) {   // more 8-bit pairs than kept in registers
+          const uint32_t ew = us8[(size_t)g * e.np8 + i];
+          const float uh = (float)(_Float16)(f16f(ew & 0xFFFFu) * ((float)uc8[(size_t)orow * n8 + i] - f16f(ew >> 16)));
           v += uh * tv[(size_t)(pb + rw) * rs + i];
         }
         y[(size_t)tko[h] * out + orow] = to_bf16(v + ybo[h]);
@@ -1159,6 +1202,8 @@ int launch_apply(const ApplyArgs& a) {
   ug.nact = a.wl.nact;
   ug.act = act_all;
   ug.mp = mp;
+  ug.m = m;
+  ug.mmagic = m > 1 ? (uint32_t)((0x100000000ull + (uint64_t)m - 1) / (uint64_t)m) : 0u;
   hipLaunchKernelGGL(k_uside, dim3((unsigned)(outmax / kGroup), (unsigned)(m * a.wl.nact)), dim3(kUWaves * 64), 0,
                      st, a.n, a.in, perm, a.T, ug);
   mark(DC_STAGE_COUNT);
