@@ -951,7 +951,8 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
       for (int op = 0; op < NOPS; ++op) {   // one A operand at a time: its registers are free again after hold()
         const uint4* f = reinterpret_cast<const uint4*>(S.frag[cl * NOPS + op][q][col]);
         const v8i a = v8_of(f[0], f[1]);
-        const int scv = S.sc[cl][4 * op + tr4][q];   // read by every lane: rows 12-15 take 127 below
+        int scv = S.sc[cl][4 * op + tr4][q];   // read by every lane (no branch): rows 12-15 take 127
+        asm volatile("" : "+v"(scv));
         const int sa = ps < 3 ? scv - 5 * ps : 127;
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
         d = THREE ? mma(a, bop, d, sa, kFmtFp6, kScaleFp6Code) : mma(a, bop, d, sa, kFmtFp4, kScaleFp4Code);
@@ -967,20 +968,33 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
     // the matrix-core ops of one window; every step reloads its slot
     // (straight-line loads, exact waits), the ops of a step past the
     // window's chunks are skipped
+    // The first round of each ring runs outside the loops and whether or not
+    // the window has chunks of that width: in a loop, or behind a branch, the
+    // wait for a slot must hold on every path into it, and would cover the
+    // loads issued behind the slot's (W x among them).  A step past the
+    // window's chunks skips its ops and reloads the chunk its slot holds
+    // (past the last chunk that is out of range: zeros, no memory request).
     auto run = [&](auto nops_c, int w3, int n3w, int j0, int n2w) __attribute__((always_inline)) {
-      for (int c = w3; c < w3 + n3w; c += 2) {
-        mops(nops_c, c - w3, b_fp6(cr3[0][0], cr3[0][1], cr3[0][2]), B3{});
-        load3(cr3[0], c + 2);
-        if (c + 1 < w3 + n3w) mops(nops_c, c + 1 - w3, b_fp6(cr3[1][0], cr3[1][1], cr3[1][2]), B3{});
-        load3(cr3[1], c + 3);
-      }
-      for (int j = j0; j < j0 + n2w; j += 4) {
+      auto step3 = [&](int c) __attribute__((always_inline)) {   // c - w3 even: slots 0 and 1
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const bool live = c + d < w3 + n3w;
+          if (live) mops(nops_c, c + d - w3, b_fp6(cr3[d][0], cr3[d][1], cr3[d][2]), B3{});
+          load3(cr3[d], live ? c + d + 2 : c + d);
+        }
+      };
+      auto step2 = [&](int j) __attribute__((always_inline)) {   // j - j0 a multiple of 4: slots 0-3
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          if (d == 0 || j + d < j0 + n2w) mops(nops_c, n3w + j + d - j0, b_fp4(cr2[d][0], cr2[d][1]), B2{});
-          load2(cr2[d], j + d + 4);
+          const bool live = j + d < j0 + n2w;
+          if (live) mops(nops_c, n3w + j + d - j0, b_fp4(cr2[d][0], cr2[d][1]), B2{});
+          load2(cr2[d], live ? j + d + 4 : j + d);
         }
-      }
+      };
+      step3(w3);
+      for (int c = w3 + 2; c < w3 + n3w; c += 2) step3(c);
+      step2(j0);
+      for (int j = j0 + 4; j < j0 + n2w; j += 4) step2(j);
     };
     // window w: 3-bit chunks [w3, w3 + n3w), then 2-bit chunks [j0, j0 + n2w)
     auto window = [&](int w3, int j0, int& n3w, int& n2w) __attribute__((always_inline)) {
