@@ -601,7 +601,18 @@ struct VGroup {
   int32_t red_rows;              // grid rows of partial-sum blocks
   int32_t nact;                  // work items per matrix
   int32_t ns, T;                 // V-side input slices, tokens
+  int32_t m;                     // matrices of the group
+  uint32_t mmagic, nsmagic;      // ceil(2^32 / m), ceil(2^32 / ns) (when above 1): division by multiply-high
 };
+
+// q / d for the block indices here (q < 2^16): the multiply-high by
+// ceil(2^32 / d) is exact for q < 2^32 / d; d = 1 passes magic 0.
+__device__ __forceinline__ int div_magic(int q, uint32_t magic) {
+  return magic == 0u ? q : (int)__umulhi((uint32_t)q, magic);
+}
+inline uint32_t magic_of(int d) {
+  return d > 1 ? (uint32_t)((0x100000000ull + (uint64_t)d - 1) / (uint64_t)d) : 0u;
+}
 
 __global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t in, const uint16_t* __restrict__ x,
                                                const int32_t* __restrict__ perm, const uint8_t* __restrict__ xf,
@@ -617,8 +628,8 @@ __global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t in, const uint
   const int yy = blockIdx.y - g.red_rows;
   // rows item-major, matrix fastest: every matrix's work items (listed
   // first) run before the empty entries of any
-  const int mg = (gridDim.y - g.red_rows) / g.nact;   // matrices of the group
-  const int mj = yy % mg, item = yy / mg;
+  const int item = div_magic(yy, g.mmagic);
+  const int mj = yy - item * g.m;
   const MatParams P = g.mp[mj];
   const ActEntry e = g.act[mj * g.nact + item];   // the item-th work item of matrix mj
   const VOut vo{P.tv, P.vpt, P.vcnt, P.rs, g.ns, g.T, P.vb};
@@ -632,9 +643,9 @@ __global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t in, const uint
   tn.n2 = e.n2;
   tn.pad_ = 0;
   const int ns = vo.ns;
-  const int bv = blockIdx.x / ns;   // rank block (counter index)
+  const int bv = div_magic(blockIdx.x, g.nsmagic);   // rank block (counter index)
   int b = bv;
-  const int s = blockIdx.x % ns;
+  const int s = blockIdx.x - bv * ns;
   if (b >= v_blocks(tn.n8, tn.n3, tn.n2)) return;
   Layout L;
   layout_of_item(e, &L);
@@ -701,17 +712,16 @@ struct UGroup {
   const MatParams* mp;   // [m] per-matrix parameters (workspace)
   int32_t nact;
   int32_t m;             // matrices of the group
-  uint32_t mmagic;       // ceil(2^32 / m) for m > 1: y / m = mulhi(y, mmagic)
+  uint32_t mmagic;       // ceil(2^32 / m) for m > 1 (div_magic)
 };
 
 __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) k_uside(int32_t n, int32_t in, const int32_t* __restrict__ perm,
                                                         int32_t T, UGroup ug) {
   const int g = blockIdx.x;
   // rows item-major, matrix fastest: every matrix's work items (listed
-  // first) run before the empty entries of any.  item = y / m by a
-  // multiply-high (exact for y < 2^31), so the block does no division.
+  // first) run before the empty entries of any
   const int yy = blockIdx.y;
-  const int item = ug.m == 1 ? yy : (int)__umulhi((uint32_t)yy, ug.mmagic);
+  const int item = div_magic(yy, ug.mmagic);
   const int mj = yy - item * ug.m;
   const MatParams P = ug.mp[mj];
   const ActEntry e = ug.act[mj * ug.nact + item];
@@ -1208,6 +1218,9 @@ int launch_apply(const ApplyArgs& a) {
   vg.mp = mp;
   vg.ns = a.wl.ns;
   vg.T = a.T;
+  vg.m = m;
+  vg.mmagic = magic_of(m);
+  vg.nsmagic = magic_of(a.wl.ns);
   if (vbmax > 0 || red > 0) {
     const unsigned gy = (unsigned)(vg.red_rows + (vbmax > 0 ? m * a.wl.nact : 0));
     hipLaunchKernelGGL(k_vside, dim3((unsigned)gx, gy), dim3(256), 0, st, a.n, a.in, a.x, perm, xf, xsc, xsum, vg);
@@ -1217,7 +1230,7 @@ int launch_apply(const ApplyArgs& a) {
   ug.act = act_all;
   ug.mp = mp;
   ug.m = m;
-  ug.mmagic = m > 1 ? (uint32_t)((0x100000000ull + (uint64_t)m - 1) / (uint64_t)m) : 0u;
+  ug.mmagic = magic_of(m);
   hipLaunchKernelGGL(k_uside, dim3((unsigned)(outmax / kGroup), (unsigned)(m * a.wl.nact)), dim3(kUWaves * 64), 0,
                      st, a.n, a.in, perm, a.T, ug);
   mark(DC_STAGE_COUNT);
