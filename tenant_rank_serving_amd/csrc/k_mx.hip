@@ -516,7 +516,8 @@ __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, i
 // (row, token) and adds sigma * partial into t.
 __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, const uint16_t* __restrict__ x,
                            const int32_t* __restrict__ perm, int p0, int p1, const VOut& vo) {
-  __shared__ float red[4][4][kVRows];   // [wave][row][token row]
+  constexpr int kR = 2;   // rows per step: few live registers, so the V kernel fits 4 waves per SIMD
+  __shared__ float red[4][kR][kVRows];   // [wave][row][token row]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const Seg sg = seg_of(tn, L, 0);
   const float* sigma = reinterpret_cast<const float*>(tn.base + L.off[DC_REG_SIGMA]);
@@ -531,21 +532,21 @@ __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, con
 #pragma unroll
     for (int t = 0; t < kVRows; ++t)
       xv[t] = *reinterpret_cast<const uint4*>(x + (size_t)perm[pb + min(t, nt - 1)] * in + ic);
-    for (int r0 = 0; r0 < sg.n; r0 += 4) {
-      uint2 cw[4];
-      uint32_t e[4];
+    for (int r0 = 0; r0 < sg.n; r0 += kR) {
+      uint2 cw[kR];
+      uint32_t e[kR];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kR; ++u) {
         const int i = min(r0 + u, sg.n - 1);
         cw[u] = *reinterpret_cast<const uint2*>(sg.vc + (size_t)i * in + ic);
         e[u] = sg.vs[(size_t)gi * np + i];
       }
-      // partials of the live (row, token) pairs only: with two 8-bit rows and
-      // a few tokens most of the 4 x kVRows pairs are padding
-      const int nu = min(4, sg.n - r0);
-      float part[4][kVRows];
+      // partials of the live (row, token) pairs only: with a few tokens most
+      // of the kR x kVRows pairs are padding
+      const int nu = min(kR, sg.n - r0);
+      float part[kR][kVRows];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kR; ++u) {
         if (u >= nu) break;
         const float sc = f16f(e[u] & 0xFFFFu), z = f16f(e[u] >> 16);
         const uint32_t cwu[2] = {cw[u].x, cw[u].y};
@@ -565,7 +566,7 @@ __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, con
       }
       // their wave sums
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kR; ++u)
 #pragma unroll
         for (int t = 0; t < kVRows; ++t) {
           if (u < nu && t < nt) {
@@ -580,7 +581,7 @@ __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, con
           }
         }
       __syncthreads();
-      if (tid < 4 * kVRows) {
+      if (tid < kR * kVRows) {
         const int u = tid / kVRows, t = tid % kVRows;
         if (r0 + u < sg.n && t < nt)
           v_put(vo, s, pb + t, r0 + u, sigma[r0 + u] * ((red[0][u][t] + red[1][u][t]) + (red[2][u][t] + red[3][u][t])));
@@ -614,7 +615,7 @@ inline uint32_t magic_of(int d) {
   return d > 1 ? (uint32_t)((0x100000000ull + (uint64_t)d - 1) / (uint64_t)d) : 0u;
 }
 
-__global__ void __launch_bounds__(256) k_vside(int32_t n, int32_t in, const uint16_t* __restrict__ x,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) k_vside(int32_t n, int32_t in, const uint16_t* __restrict__ x,
                                                const int32_t* __restrict__ perm, const uint8_t* __restrict__ xf,
                                                const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
                                                VGroup g) {
