@@ -27,6 +27,8 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kPfBufFlags = 0x00020000;   // buffer resource word 3: raw 32-bit dwords, bounds-checked
 
 constexpr int kPT = 128;                 // rows and tokens per tile
 constexpr int kPVK = 64;                 // V product: inputs per K chunk (half a 128-group)
@@ -81,16 +83,20 @@ struct Dequant {
 };
 
 struct PfSeg {
-  const uint8_t* vc;    // V codes
-  const uint32_t* vs;   // V scale | zero << 16, [in/128][pad4(n)]
-  const uint8_t* uc;    // U codes
-  const uint32_t* us;   // U scale | zero << 16, [out/128][pad4(n)]
+  int32_t ovc, ovs;     // byte offsets in the tenant's buffer: V codes, V scale | zero << 16 [in/128][pad4(n)]
+  int32_t ouc, ous;     // U codes, U scale | zero << 16 [out/128][pad4(n)]
   int32_t b, n, p0, glo;   // width, pairs, first padded rank, first global rank
 };
 
+// The operand loads go through one buffer resource over the tenant's whole
+// packed buffer: every load is issued on every path (an offset of total, its
+// size, is out of range and reads zeros), so the waits for them are exact.
 struct PfTenant {
+  const uint8_t* base;  // the packed buffer
+  int32_t total;        // its bytes
+  int32_t pad_;
   PfSeg s[3];           // 8-, 3- and 2-bit segments
-  const float* sigma;
+  int32_t osig;         // byte offset of sigma in the buffer
   int32_t rp;           // padded rank rows of the V product (a multiple of 128)
   int32_t kp;           // padded ranks of the U product's K (a multiple of 32)
   int32_t s0, nt;       // the segment's tokens
@@ -162,33 +168,29 @@ __global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* __r
     xi[it] = xsc[tok];
     so[it] = row * kPVPad + c * 16;
   }
-  uint32_t cw[8], sz = 0u;
-  uint4 rx[4];
+  u32x4 ca, cb;   // the code words as loaded: unpacked in swrite, so that
+  uint32_t sz;    // the loads stay in flight during the chunk's matrix-core ops
+  u32x4 rx[4];
   const int nk = in / kPVK;
+  const __amdgpu_buffer_rsrc_t rten =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(tn.base), 0, tn.total, kPfBufFlags);
+  // the lane's code words of chunk q of group g: 8 words (an 8-bit chunk
+  // uses 8, a 3-bit one 3, a 2-bit one 2; the rest is unused), two 16-byte
+  // loads at a dword-aligned offset; rows past the segment read zeros
   auto gload = [&](int kc) __attribute__((always_inline)) {
     const int g = kc >> 1, q = 2 * (kc & 1) + qs;
+    const int wo = sg.b == 8 ? (li * gi + g) * 32 + q * 8 : (int)v_chunk_word(li, g, q, gi, sg.b);
+    const int oc = valid ? sg.ovc + wo * 4 : tn.total;
+    ca = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, oc, 0, 0));
+    cb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, valid ? oc + 16 : tn.total, 0, 0));
+    sz = __builtin_amdgcn_raw_buffer_load_b32(rten, valid ? sg.ovs + (g * np4 + li) * 4 : tn.total, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) cw[j] = 0u;
-    sz = 0u;
-    if (valid) {
-      const uint32_t* vw = reinterpret_cast<const uint32_t*>(sg.vc);
-      if (sg.b == 8) {
-        const uint4* u = reinterpret_cast<const uint4*>(vw + ((size_t)li * gi + g) * 32 + q * 8);
-        const uint4 a = u[0], b = u[1];
-        cw[0] = a.x; cw[1] = a.y; cw[2] = a.z; cw[3] = a.w; cw[4] = b.x; cw[5] = b.y; cw[6] = b.z; cw[7] = b.w;
-      } else if (sg.b == 3) {
-        const uint32_t* u = vw + v_chunk_word(li, g, q, gi, 3);
-        cw[0] = u[0]; cw[1] = u[1]; cw[2] = u[2];
-      } else {
-        const uint2 u = *reinterpret_cast<const uint2*>(vw + v_chunk_word(li, g, q, gi, 2));
-        cw[0] = u.x; cw[1] = u.y;
-      }
-      sz = sg.vs[(size_t)g * np4 + li];
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) rx[it] = *reinterpret_cast<const uint4*>(xp[it] + (size_t)kc * kPVK);
+    for (int it = 0; it < 4; ++it) rx[it] = *reinterpret_cast<const u32x4*>(xp[it] + (size_t)kc * kPVK);
   };
   auto swrite = [&](int s) __attribute__((always_inline)) {
+    // the chunk's loads are used from here on (not hoisted into the matrix-core ops)
+    asm volatile("" : "+v"(ca), "+v"(cb), "+v"(sz), "+v"(rx[0]), "+v"(rx[1]), "+v"(rx[2]), "+v"(rx[3]));
+    const uint32_t cw[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
     uint32_t h[16];
     if (sg.b == 8) Dequant<8, 0, 0, 32, true>::run(cw, &sz, h);
     else if (sg.b == 3) Dequant<3, 0, 0, 32, true>::run(cw, &sz, h);
@@ -222,6 +224,7 @@ __global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* __r
   for (int kc = 0; kc < nk; ++kc) {
     const int s = kc & 1;
     gload(min(kc + 1, nk - 1));   // the last chunk loads itself again (unused)
+    __builtin_amdgcn_sched_barrier(0);   // the loads go out before the chunk's matrix-core ops
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       uint4 a[4], b[4];
@@ -236,11 +239,24 @@ __global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* __r
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a[i]), __builtin_bit_cast(h8, b[j]),
                                                              acc[i][j], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);   // the chunk's ops before the wait for the next chunk's loads
     swrite(s ^ 1);   // after the last chunk: unused
     __syncthreads();
   }
   // epilogue: lane holds token column (lane & 15) of token tile j and padded
-  // ranks 4 (lane >> 4) .. +3 of rank tile i
+  // ranks 4 (lane >> 4) .. +3 of rank tile i; sigma of those 16 ranks first
+  // (zero in the padding)
+  float sgm[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pp = o0 + 64 * wo + 16 * i + 4 * (lane >> 4) + r;
+      const PfSeg sr = seg_sel(tn, seg_of_pad(tn, pp));
+      const int l = pp - sr.p0;
+      sgm[i][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rten, l < sr.n ? tn.osig + (sr.glo + l) * 4 : tn.total, 0, 0));
+    }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tl = t0 + 64 * wt + 16 * j + (lane & 15);
@@ -254,11 +270,7 @@ __global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* __r
       f32x4 v;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int pp = p4 + r;
-        const PfSeg sr = seg_sel(tn, seg_of_pad(tn, pp));
-        const int l = pp - sr.p0;
-        const float sgm = l < sr.n ? tn.sigma[sr.glo + l] : 0.f;
-        v[r] = sgm * acc[i][j][r] * fwd;
+        v[r] = sgm[i][r] * acc[i][j][r] * fwd;
         mx = fmaxf(mx, fabsf(v[r]));
       }
       *reinterpret_cast<f32x4*>(tw + (size_t)tok * ldt + p4) = v;
@@ -310,54 +322,59 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
   const int og = o0 / kGroup;   // the tile's 128-row scale group
   const int tl_s = min(t0 + arow, N - 1);
   const int tok_s = s0 + tl_s;
-  const float* tsrc = tw + (size_t)tok_s * ldt + 16 * hs;   // packed fp16 pairs (k_pf_t)
-  uint32_t cw[4], sz[16];
+  // packed fp16 pairs (k_pf_t) of the tenant's t rows, through a buffer
+  // resource: its loads stay where they are issued
+  const __amdgpu_buffer_rsrc_t rtw = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(tw + (size_t)s0 * ldt), 0,
+                                                                       N * ldt * 4, kPfBufFlags);
+  const int tofs = (tl_s * ldt + 16 * hs) * 4;
+  // the chunk's loads as they arrive (unpacked in swrite, so that they stay
+  // in flight during the chunk's matrix-core ops)
+  u32x4 cd, szr[4];
+  uint32_t cd4;
+  int csh = 0, cli0 = 0, cn = 0;
   uint32_t bsel = 0;
   f32x4 tr[4];
   const int nk = tn.kp / kPUK;
+  const __amdgpu_buffer_rsrc_t rten =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(tn.base), 0, tn.total, kPfBufFlags);
   auto gload = [&](int kc) __attribute__((always_inline)) {
     const int pk = kc * kPUK;
     const PfSeg sg = seg_sel(tn, seg_of_pad(tn, pk));
     const int kbl = (pk - sg.p0) / kPUK, li0 = kbl * kPUK + 16 * hs;
     const int np4 = (int)round_up(sg.n, 4);
     bsel = (uint32_t)sg.b;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) cw[j] = 0u;
-    if (sg.b == 8) {   // bytes [out][n8]: this thread's 16 codes, one byte each
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t c = li0 + e < sg.n ? sg.uc[(size_t)o * sg.n + li0 + e] : 0u;
-        cw[e >> 2] |= c << (8 * (e & 3));
-      }
-    } else {
-      int nw;
-      const uint32_t* wp = reinterpret_cast<const uint32_t*>(sg.uc) + u_kblock_word(o, kbl, sg.n, sg.b, &nw);
-      cw[0] = wp[0];
-      if (nw > 1) cw[1] = wp[1];
-      if (nw > 2) cw[2] = wp[2];
-    }
+    // This thread's codes, the same loads for every width: 20 bytes from the
+    // dword below byte a, shifted down by a % 4.  8-bit: bytes [out][n8],
+    // its 16 codes from byte o n8 + li0 (the bytes past the segment's pairs
+    // meet zero scales below); 3/2-bit: the row's words of K-block kbl.
+    int nw;
+    const int a = sg.b == 8 ? sg.ouc + o * sg.n + li0 : sg.ouc + 4 * (int)u_kblock_word(o, kbl, sg.n, sg.b, &nw);
+    const int ad = a & ~3;
+    csh = a & 3;
+    cli0 = li0;
+    cn = sg.n;
+    cd = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, ad, 0, 0));
+    cd4 = __builtin_amdgcn_raw_buffer_load_b32(rten, ad + 16, 0, 0);
     // the 16 scale words, four 16-byte loads (pad4 rows, li0 a multiple of
-    // 16: aligned), words past the segment's pairs zeroed (a zero scale
-    // makes their values zero)
-    {
-      const uint4* sp = reinterpret_cast<const uint4*>(sg.us + (size_t)og * np4 + min(li0, max(np4 - 16, 0)));
-      const bool whole = li0 + 16 <= np4;
+    // 16: aligned); words past the segment's pairs are zeroed in swrite (a
+    // zero scale makes their values zero)
+    const int os = sg.ous + (og * np4 + li0) * 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 v = whole ? sp[j] : make_uint4(0u, 0u, 0u, 0u);
-        sz[4 * j] = v.x; sz[4 * j + 1] = v.y; sz[4 * j + 2] = v.z; sz[4 * j + 3] = v.w;
-      }
-      if (!whole) {
+    for (int j = 0; j < 4; ++j)
+      szr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, os + 16 * j, 0, 0));
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sz[e] = li0 + e < sg.n ? sg.us[(size_t)og * np4 + li0 + e] : 0u;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sz[e] = li0 + e < sg.n ? sz[e] : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) tr[j] = *reinterpret_cast<const f32x4*>(tsrc + pk + 4 * j);
+    for (int j = 0; j < 4; ++j)
+      tr[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rtw, tofs + (pk + 4 * j) * 4, 0, 0));
   };
   auto swrite = [&](int s) __attribute__((always_inline)) {
+    // the chunk's loads are used from here on (not hoisted into the matrix-core ops)
+    asm volatile("" : "+v"(cd), "+v"(cd4), "+v"(szr[0]), "+v"(szr[1]), "+v"(szr[2]), "+v"(szr[3]), "+v"(tr[0]),
+                 "+v"(tr[1]), "+v"(tr[2]), "+v"(tr[3]));
+    const uint32_t cw[4] = {__builtin_amdgcn_alignbyte(cd.y, cd.x, csh), __builtin_amdgcn_alignbyte(cd.z, cd.y, csh),
+                            __builtin_amdgcn_alignbyte(cd.w, cd.z, csh), __builtin_amdgcn_alignbyte(cd4, cd.w, csh)};
+    uint32_t sz[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sz[e] = cli0 + e < cn ? szr[e >> 2][e & 3] : 0u;
     uint32_t h[8];
     if (bsel == 8) {   // cw holds this thread's 16 codes, one byte each
       Dequant<8, 0, 0, 16, false>::run(cw, sz, h);
@@ -406,6 +423,7 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
     for (int kc = 0; kc < nk; ++kc) {
       const int s = kc & 1;
       gload(min(kc + 1, nk - 1));
+      __builtin_amdgcn_sched_barrier(0);   // the loads go out before the chunk's matrix-core ops
       uint4 a[4], bh[4], bl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const uint4*>(&lds[s][0][ra + 16 * i * kPUPad]);
@@ -423,6 +441,7 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a[i]), __builtin_bit_cast(h8, bl[j]),
                                                              acc[i][j], 0, 0, 0);
         }
+      __builtin_amdgcn_sched_barrier(0);   // the chunk's ops before the wait for the next chunk's loads
       swrite(s ^ 1);
       __syncthreads();
     }
@@ -499,6 +518,8 @@ int launch_dense_prefill(const ApplyArgs& a) {
       Layout L;
       layout_of(A.out, a.in, tn.n8, tn.n3, tn.n2, &L);
       PfTenant& p = b.t[cnt];
+      p.base = tn.base;
+      p.total = (int32_t)L.total;
       const int ns[3] = {tn.n8, tn.n3, tn.n2};
       int p0 = 0, glo = 0;
       for (int w = 0; w < 3; ++w) {
@@ -507,14 +528,14 @@ int launch_dense_prefill(const ApplyArgs& a) {
         sg.n = ns[w];
         sg.p0 = p0;
         sg.glo = glo;
-        sg.vc = tn.base + L.off[DC_REG_VC8 + w];
-        sg.vs = reinterpret_cast<const uint32_t*>(tn.base + L.off[DC_REG_VS8 + w]);
-        sg.uc = tn.base + L.off[DC_REG_UC8 + w];
-        sg.us = reinterpret_cast<const uint32_t*>(tn.base + L.off[DC_REG_US8 + w]);
+        sg.ovc = (int32_t)L.off[DC_REG_VC8 + w];
+        sg.ovs = (int32_t)L.off[DC_REG_VS8 + w];
+        sg.ouc = (int32_t)L.off[DC_REG_UC8 + w];
+        sg.ous = (int32_t)L.off[DC_REG_US8 + w];
         p0 += (int)round_up((size_t)ns[w], kKBlock);
         glo += ns[w];
       }
-      p.sigma = reinterpret_cast<const float*>(tn.base + L.off[DC_REG_SIGMA]);
+      p.osig = (int32_t)L.off[DC_REG_SIGMA];
       p.kp = p0;
       p.rp = pf_rank_pad(tn.n8, tn.n3, tn.n2);
       p.s0 = s0;
