@@ -139,7 +139,7 @@ __device__ __forceinline__ bool tile_of(int nto, int ntt, int& o0, int& t0) {
 // 64 inputs through two LDS buffers.  Staging thread: rank row tid/2, code
 // chunk tid%2 of the K chunk (32 codes, one word run), and token rows
 // 32 it + tid/8, 8 inputs each.
-__global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* __restrict__ x, int32_t in,
+__global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* x, int32_t in,
                                                  int32_t ldt, const float* __restrict__ xsc, float* __restrict__ tw,
                                                  uint32_t* __restrict__ tmax) {
   const PfTenant& tn = pb.t[blockIdx.y];
@@ -308,7 +308,7 @@ __global__ void __launch_bounds__(256) k_pf_t(float* __restrict__ tw, const uint
 // y = bf16(W x + C 2^e).  Block = 128 rows x 128 tokens, K in chunks of one
 // K-block of 32 padded ranks.  Staging thread: row tid/2, 16 ranks (half
 // tid%2 of the K-block) of U and of t.
-__global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_t ldt, const float* __restrict__ tw,
+__global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_t ldt, const float* tw,
                                                  const uint32_t* __restrict__ tmax, const float* __restrict__ ybase,
                                                  uint16_t* __restrict__ y) {
   const PfTenant& tn = pb.t[blockIdx.y];
@@ -327,22 +327,24 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
   const __amdgpu_buffer_rsrc_t rtw = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(tw + (size_t)s0 * ldt), 0,
                                                                        N * ldt * 4, kPfBufFlags);
   const int tofs = (tl_s * ldt + 16 * hs) * 4;
-  // the chunk's loads as they arrive (unpacked in swrite, so that they stay
-  // in flight during the chunk's matrix-core ops)
-  u32x4 cd, szr[4];
-  uint32_t cd4;
-  int csh = 0, cli0 = 0, cn = 0;
-  uint32_t bsel = 0;
-  f32x4 tr[4];
+  // a chunk's loads as they arrive (unpacked in swrite, so that they stay
+  // in flight during the matrix-core ops of the chunks before it)
+  struct In {
+    u32x4 cd, szr[4];   // code bytes, scale words
+    f32x4 tr[4];        // t pairs
+    uint32_t cd4;
+    int csh, cli0, cn, bsel;
+  };
+  In r0, r1;
   const int nk = tn.kp / kPUK;
   const __amdgpu_buffer_rsrc_t rten =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(tn.base), 0, tn.total, kPfBufFlags);
-  auto gload = [&](int kc) __attribute__((always_inline)) {
+  auto gload = [&](In& r, int kc) __attribute__((always_inline)) {
     const int pk = kc * kPUK;
     const PfSeg sg = seg_sel(tn, seg_of_pad(tn, pk));
     const int kbl = (pk - sg.p0) / kPUK, li0 = kbl * kPUK + 16 * hs;
     const int np4 = (int)round_up(sg.n, 4);
-    bsel = (uint32_t)sg.b;
+    r.bsel = sg.b;
     // This thread's codes, the same loads for every width: 20 bytes from the
     // dword below byte a, shifted down by a % 4.  8-bit: bytes [out][n8],
     // its 16 codes from byte o n8 + li0 (the bytes past the segment's pairs
@@ -350,31 +352,33 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
     int nw;
     const int a = sg.b == 8 ? sg.ouc + o * sg.n + li0 : sg.ouc + 4 * (int)u_kblock_word(o, kbl, sg.n, sg.b, &nw);
     const int ad = a & ~3;
-    csh = a & 3;
-    cli0 = li0;
-    cn = sg.n;
-    cd = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, ad, 0, 0));
-    cd4 = __builtin_amdgcn_raw_buffer_load_b32(rten, ad + 16, 0, 0);
+    r.csh = a & 3;
+    r.cli0 = li0;
+    r.cn = sg.n;
+    r.cd = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, ad, 0, 0));
+    r.cd4 = __builtin_amdgcn_raw_buffer_load_b32(rten, ad + 16, 0, 0);
     // the 16 scale words, four 16-byte loads (pad4 rows, li0 a multiple of
     // 16: aligned); words past the segment's pairs are zeroed in swrite (a
     // zero scale makes their values zero)
     const int os = sg.ous + (og * np4 + li0) * 4;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      szr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, os + 16 * j, 0, 0));
+      r.szr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rten, os + 16 * j, 0, 0));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      tr[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rtw, tofs + (pk + 4 * j) * 4, 0, 0));
+      r.tr[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rtw, tofs + (pk + 4 * j) * 4, 0, 0));
   };
-  auto swrite = [&](int s) __attribute__((always_inline)) {
+  auto swrite = [&](In& r, int s) __attribute__((always_inline)) {
     // the chunk's loads are used from here on (not hoisted into the matrix-core ops)
-    asm volatile("" : "+v"(cd), "+v"(cd4), "+v"(szr[0]), "+v"(szr[1]), "+v"(szr[2]), "+v"(szr[3]), "+v"(tr[0]),
-                 "+v"(tr[1]), "+v"(tr[2]), "+v"(tr[3]));
-    const uint32_t cw[4] = {__builtin_amdgcn_alignbyte(cd.y, cd.x, csh), __builtin_amdgcn_alignbyte(cd.z, cd.y, csh),
-                            __builtin_amdgcn_alignbyte(cd.w, cd.z, csh), __builtin_amdgcn_alignbyte(cd4, cd.w, csh)};
+    asm volatile("" : "+v"(r.cd), "+v"(r.cd4), "+v"(r.szr[0]), "+v"(r.szr[1]), "+v"(r.szr[2]), "+v"(r.szr[3]),
+                 "+v"(r.tr[0]), "+v"(r.tr[1]), "+v"(r.tr[2]), "+v"(r.tr[3]));
+    const int csh = r.csh;
+    const uint32_t cw[4] = {__builtin_amdgcn_alignbyte(r.cd.y, r.cd.x, csh), __builtin_amdgcn_alignbyte(r.cd.z, r.cd.y, csh),
+                            __builtin_amdgcn_alignbyte(r.cd.w, r.cd.z, csh), __builtin_amdgcn_alignbyte(r.cd4, r.cd.w, csh)};
     uint32_t sz[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sz[e] = cli0 + e < cn ? szr[e >> 2][e & 3] : 0u;
+    for (int e = 0; e < 16; ++e) sz[e] = r.cli0 + e < r.cn ? r.szr[e >> 2][e & 3] : 0u;
+    const int bsel = r.bsel;
     uint32_t h[8];
     if (bsel == 8) {   // cw holds this thread's 16 codes, one byte each
       Dequant<8, 0, 0, 16, false>::run(cw, sz, h);
@@ -397,7 +401,7 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; e += 2) {
-        const uint32_t w0 = __float_as_uint(tr[j][e]), w1 = __float_as_uint(tr[j][e + 1]);
+        const uint32_t w0 = __float_as_uint(r.tr[j][e]), w1 = __float_as_uint(r.tr[j][e + 1]);
         hi[2 * j + e / 2] = (w0 & 0xFFFFu) | (w1 << 16);
         lo[2 * j + e / 2] = (w0 >> 16) | (w1 & 0xFFFF0000u);
       }
@@ -416,33 +420,47 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (nk > 0) {
-    gload(0);
-    swrite(0);
-    __syncthreads();
-    for (int kc = 0; kc < nk; ++kc) {
-      const int s = kc & 1;
-      gload(min(kc + 1, nk - 1));
-      __builtin_amdgcn_sched_barrier(0);   // the loads go out before the chunk's matrix-core ops
-      uint4 a[4], bh[4], bl[4];
+  // chunk kc is in LDS stage kc & 1 while the registers hold chunk kc + 1
+  // and take chunk kc + 2 (two register sets, the loop unrolled by two)
+  auto mma_chunk = [&](int s) __attribute__((always_inline)) {
+    uint4 a[4], bh[4], bl[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const uint4*>(&lds[s][0][ra + 16 * i * kPUPad]);
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const uint4*>(&lds[s][0][ra + 16 * i * kPUPad]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bh[j] = *reinterpret_cast<const uint4*>(&lds[s][1][rb + 16 * j * kPUPad]);
+      bl[j] = *reinterpret_cast<const uint4*>(&lds[s][2][rb + 16 * j * kPUPad]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bh[j] = *reinterpret_cast<const uint4*>(&lds[s][1][rb + 16 * j * kPUPad]);
-        bl[j] = *reinterpret_cast<const uint4*>(&lds[s][2][rb + 16 * j * kPUPad]);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a[i]), __builtin_bit_cast(h8, bh[j]),
+                                                           acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a[i]), __builtin_bit_cast(h8, bl[j]),
+                                                           acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a[i]), __builtin_bit_cast(h8, bh[j]),
-                                                             acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a[i]), __builtin_bit_cast(h8, bl[j]),
-                                                             acc[i][j], 0, 0, 0);
-        }
+  };
+  if (nk > 0) {
+    gload(r0, 0);
+    swrite(r0, 0);
+    gload(r1, min(1, nk - 1));
+    __syncthreads();
+    for (int kc = 0; kc < nk; kc += 2) {
+      gload(r0, min(kc + 2, nk - 1));   // past the last chunk: the last again (unused)
+      asm volatile("" ::: "memory");   // the loads go out before the chunk's matrix-core ops
+      __builtin_amdgcn_sched_barrier(0);
+      mma_chunk(0);
       __builtin_amdgcn_sched_barrier(0);   // the chunk's ops before the wait for the next chunk's loads
-      swrite(s ^ 1);
+      swrite(r1, 1);
+      __syncthreads();
+      if (kc + 1 >= nk) break;
+      gload(r1, min(kc + 3, nk - 1));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      mma_chunk(1);
+      __builtin_amdgcn_sched_barrier(0);
+      swrite(r0, 0);
       __syncthreads();
     }
   }
