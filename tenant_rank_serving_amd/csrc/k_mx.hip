@@ -1010,7 +1010,9 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
     // window w: 3-bit chunks [w3, w3 + n3w), then 2-bit chunks [j0, j0 + n2w)
     auto window = [&](int w3, int j0, int& n3w, int& n2w) __attribute__((always_inline)) {
       n3w = min(nc3 - w3, wcap);
-      n2w = min(nc2 - j0, ((wcap - n3w) >> 2) << 2);
+      // all remaining 2-bit chunks if they fit (past the last one the ring
+      // reads out of range), else whole ring rounds
+      n2w = nc2 - j0 <= wcap - n3w ? nc2 - j0 : ((wcap - n3w) >> 2) << 2;
     };
     if (lane < kURows) S.cz[wave][lane] = 0.f;   // this wave's z t' sums of the pass
     int w3 = 0, j0 = 0;
