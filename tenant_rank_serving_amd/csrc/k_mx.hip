@@ -803,12 +803,14 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
       u8c[i] = __builtin_amdgcn_raw_buffer_load_b8(rten, ouc8 + i8, 0, 0);
     }
   };
-  // rows 12-15 of every op carry no piece: zero once
-  for (int i = tid; i < kUWin * 4 * 4; i += kUWaves * 64) {   // i = operand:4 lane group:2 row:2
-    uint4* p = reinterpret_cast<uint4*>(S.frag[i >> 4][(i >> 2) & 3][12 + (i & 3)]);
-    p[0] = make_uint4(0, 0, 0, 0);
-    p[1] = make_uint4(0, 0, 0, 0);
-  }
+  // rows 12-15 of every op carry no piece: zeroed once, behind the first loads
+  auto zero_rows = [&]() __attribute__((always_inline)) {
+    for (int i = tid; i < kUWin * 4 * 4; i += kUWaves * 64) {   // i = operand:4 lane group:2 row:2
+      uint4* p = reinterpret_cast<uint4*>(S.frag[i >> 4][(i >> 2) & 3][12 + (i & 3)]);
+      p[0] = make_uint4(0, 0, 0, 0);
+      p[1] = make_uint4(0, 0, 0, 0);
+    }
+  };
   // A-prep role: K-block kb4 and ranks m0..m0+3 of a chunk (which chunk and
   // rows depend on the pass: see aprep)
   const int kb4 = (tid >> 3) & 3, part = tid & 7;
@@ -830,12 +832,14 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     // the epilogue's inputs, in flight during the pass: lane group q writes
     // tokens 2q and 2q + 1 of the pass (their original indices, then W x and
-    // t of the 8-bit pairs).  The token indices go out first: the W x loads,
-    // last in the burst, wait for them alone.
+    // t of the 8-bit pairs).  The token indices go out right behind the
+    // A-prep inputs: the W x loads, last in the burst, wait for them alone.
     int tko[2];
     float ybo[2] = {0.f, 0.f}, t8o[2][kU8Max];
+    auto load_tko = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) tko[h] = perm[pb + min(2 * q + h, nt - 1)];
+      for (int h = 0; h < 2; ++h) tko[h] = perm[pb + min(2 * q + h, nt - 1)];
+    };
     auto epi_loads_t8 = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -1017,17 +1021,21 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
     if (lane < kURows) S.cz[wave][lane] = 0.f;   // this wave's z t' sums of the pass
     int w3 = 0, j0 = 0;
     if (nc == 0) {   // no 3/2-bit chunks: only the 8-bit pairs and W x
+      load_tko();
       epi_loads_t8();
       epi_loads_yb();
+      zero_rows();
       __syncthreads();   // every wave's zeroed sums are seen
     } else {
       // the first window, outside any loop: one burst of loads (A-prep
-      // inputs, the 8-bit pairs' inputs, both code rings, then W x once the
-      // token indices are in), then the math
+      // inputs first, the token indices, the 8-bit pairs' inputs, both code
+      // rings, then W x once the token indices are in), then the math
       int n3w, n2w;
       window(w3, j0, n3w, n2w);
       APIn ai;
       aprep_load(w3, n3w, j0, n2w, ai);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tko();
       epi_loads_t8();
       __builtin_amdgcn_sched_barrier(0);
       load3(cr3[0], 0);
@@ -1037,6 +1045,7 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
       __builtin_amdgcn_sched_barrier(0);
       epi_loads_yb();
       __builtin_amdgcn_sched_barrier(0);
+      zero_rows();
       aprep(w3, n3w, j0, n2w, ai);
       lds_barrier_keep_vm();
       if (nops == 1) run(I1{}, w3, n3w, j0, n2w);
