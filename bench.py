@@ -808,13 +808,19 @@ def main():
         g = (inn if side == "v" else out) // 128
         return (8 * n8 + 3 * n3 + 2 * n2) * n // 8 + r * g * 4 + (4 * r if side == "v" else 0)
 
-    # per launch = per grouped call: the sum over the group's matrices
+    # per launch = per grouped call: the sum over the group's matrices.  The
+    # V side reads x (bf16) and its tenants' V codes and scales and writes t
+    # (fp32, each routed token x the tenant's ranks); the U side reads its
+    # tenants' U codes and scales, t and W x (fp32, the step is fused) and
+    # writes y (bf16).
     gl = [g for g, _ in cl]
+    td = int((ids_h >= 0).sum())   # tokens routed to a tenant
+    rank = lambda sp: sp[2] + sp[3] + sp[4]
     per_launch = {
-        "vside": np.mean([sum(len(touched) * side_bytes(specs[m], "v") for m in g) + T * specs[g[0]][1] * 2
-                          for g in gl]),
-        "uside": np.mean([sum(len(touched) * side_bytes(specs[m], "u") + T * specs[m][0] * 2 for m in g)
-                          for g in gl]),
+        "vside": np.mean([sum(len(touched) * side_bytes(specs[m], "v") + td * rank(specs[m]) * 4 for m in g)
+                          + T * specs[g[0]][1] * 2 for g in gl]),
+        "uside": np.mean([sum(len(touched) * side_bytes(specs[m], "u") + td * rank(specs[m]) * 4
+                              + T * specs[m][0] * (4 + 2) for m in g) for g in gl]),
         "base": np.mean([sum(specs[m][0] * specs[m][1] * 2 for m in g) + T * specs[g[0]][1] * 2 for g in gl]),
     }
     # dom_live: the kernel's average duration per launch inside the
