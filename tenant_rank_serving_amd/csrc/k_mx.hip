@@ -78,8 +78,14 @@ struct SegArg {
 // 128-group) of x into fp8 hi/lo A fragments, their E8M0 scales and the
 // group sum; the other blocks also zero t and, when the backbone product is
 // split over K, W x (both are accumulated with float atomics).
-__device__ __forceinline__ void list_active(const Tenant& mine, int32_t n, const int* so, int32_t cap,
-                                            ActEntry* __restrict__ act, int32_t out, int32_t in, bool layouts) {
+// Work items of the buckets with tokens, in bucket order: thread b (bucket
+// b) gets its items' first list position and count, and every thread the
+// list length.  The same for every matrix of a group (the buckets are the
+// routing's), so it is worked out once.
+struct ActPos {
+  int pos, items, total;
+};
+__device__ __forceinline__ ActPos act_positions(int32_t n, const int* so) {
   __shared__ int wsum[4];
   const int tid = threadIdx.x, b = tid, lane = tid & 63, wave = tid >> 6;
   // work items of bucket b: its rows in chunks of kChunkRows
@@ -99,13 +105,21 @@ __device__ __forceinline__ void list_active(const Tenant& mine, int32_t n, const
     total += wsum[w];
   }
   lds_barrier();   // wsum is read: a next call may write it
+  return ActPos{pos, items, total};
+}
+
+// One matrix's work-item list: bucket b's items (its tenant record, region
+// offsets and derived U sizes, rows), then empty entries up to cap.
+__device__ __forceinline__ void act_write(const Tenant& mine, int32_t n, const int* so, const ActPos& ap, int32_t cap,
+                                          ActEntry* __restrict__ act, int32_t out, int32_t in, bool layouts) {
+  const int tid = threadIdx.x, b = tid;
   ActEntry e{};
   e.base = b < n ? mine.base : nullptr;
   e.n8 = b < n ? mine.n8 : 0;
   e.n3 = b < n ? mine.n3 : 0;
   e.n2 = b < n ? mine.n2 : 0;
   e.k = b;
-  if (layouts && b < n && items > 0) {
+  if (layouts && b < n && ap.items > 0) {
     Layout L;
     layout_of(out, in, e.n8, e.n3, e.n2, &L);
 #pragma unroll
@@ -125,12 +139,12 @@ __device__ __forceinline__ void list_active(const Tenant& mine, int32_t n, const
     e.wl3 = e.rw3 - (e.kbn3 - 1) * 3;
     e.wl2 = e.rw2 - (e.kbn2 - 1) * 2;
   }
-  for (int j = 0; j < items; ++j) {
+  for (int j = 0; j < ap.items; ++j) {
     e.p0 = so[b] + j * kChunkRows;
     e.p1 = min(so[b] + (j + 1) * kChunkRows, so[b + 1]);
-    act[pos + j] = e;
+    act[ap.pos + j] = e;
   }
-  for (int i = total + tid; i < cap; i += blockDim.x) {   // the rest of the list: empty entries
+  for (int i = ap.total + tid; i < cap; i += blockDim.x) {   // the rest of the list: empty entries
     ActEntry e{};
     e.k = -1;
     act[i] = e;
@@ -182,8 +196,10 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
     for (int j = 0; j < M; ++j)
       if (tid == j) pm.mp[j] = pm.params[j];
     __shared__ int so[DC_MAX_TENANTS + 2];   // bucket starts
-    // thread b's tenant records, read first: the kernel arguments live in
-    // memory and the indexing is per thread
+    // token tid's tenant id, then thread b's tenant records: both in flight
+    // together (the kernel arguments live in memory and the indexing is per
+    // thread)
+    const int k_first = mode == 1 && tid < T ? ids[tid] : -1;
     Tenant mine[M];
 #pragma unroll
     for (int j = 0; j < M; ++j) mine[j] = tid < n ? gt.t[j].t[tid] : Tenant{};
@@ -196,8 +212,9 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
         *flags = 0;
       }
       lds_barrier();
+      const ActPos ap = act_positions(n, so);
 #pragma unroll
-      for (int j = 0; j < M; ++j) list_active(mine[j], n, so, cap, pm.act[j], pm.params[j].out, in, pm.layouts != 0);
+      for (int j = 0; j < M; ++j) act_write(mine[j], n, so, ap, cap, pm.act[j], pm.params[j].out, in, pm.layouts != 0);
       return;
     }
     __shared__ int cnt[DC_MAX_TENANTS + 1];   // tokens per bucket
@@ -210,7 +227,7 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
     lds_barrier();
     int b0 = -1;   // bucket of token tid (the first chunk is kept for the placement below)
     for (int t = tid; t < T; t += blockDim.x) {
-      int k = ids[t];
+      int k = t == tid ? k_first : ids[t];
       if (k < -1 || k >= n) { bad = 1; k = -1; }
       const int b = k < 0 ? n : k;
       if (t == tid) b0 = b;
@@ -241,8 +258,9 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
       if (tid == 0) *flags = bad ? 1u : 0u;
     }
     lds_barrier();
+    const ActPos ap = act_positions(n, so);
 #pragma unroll
-    for (int j = 0; j < M; ++j) list_active(mine[j], n, so, cap, pm.act[j], pm.params[j].out, in, pm.layouts != 0);
+    for (int j = 0; j < M; ++j) act_write(mine[j], n, so, ap, cap, pm.act[j], pm.params[j].out, in, pm.layouts != 0);
     for (int c0 = 0; c0 < T; c0 += blockDim.x) {
       const int t = c0 + tid;
       int b = -1;
