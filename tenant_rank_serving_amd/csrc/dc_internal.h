@@ -161,10 +161,15 @@ struct ActEntry {
   int32_t np8, np3, np2;
   int32_t nc3, nc;
   int32_t rw3, rw2, kbn3, kbn2, wl3, wl2;
+  // the item's tokens (original indices) at routed rows p0 .. p1 - 1, the
+  // last one repeated past p1: the x staging and the epilogue read them from
+  // here instead of loading the permutation
+  int32_t tok[8];
   uint32_t pad_[1];
 };
-static_assert(sizeof(ActEntry) == 144, "three scalar loads per block");
+static_assert(sizeof(ActEntry) == 176, "four scalar loads per block");
 constexpr int kChunkRows = 8;   // token rows per work item (one V-side and one U-side pass)
+static_assert(kChunkRows == sizeof(ActEntry::tok) / sizeof(int32_t), "one token per item row");
 // Work items of a call of n tenants and T tokens: at most one partly filled
 // chunk per bucket (n tenants + the backbone-only bucket) plus T / kChunkRows.
 DC_HD inline int32_t act_capacity(int32_t n, int32_t T) { return n + 1 + (T + kChunkRows - 1) / kChunkRows; }

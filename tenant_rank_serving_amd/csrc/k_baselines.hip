@@ -120,7 +120,7 @@ __global__ void __launch_bounds__(256) k_bd(int32_t in, const int32_t* __restric
 #pragma unroll
     for (int h = 0; h < 2; ++h) oc[h] = (uint32_t)(((tile0 + h) * gi_n * 64 + lane) * 4);
     VStage st;
-    v_stage_load(st, xf, xsc, xsum, gi_n, g0, p0, nt);   // ahead of the ring: vmcnt is in order
+    v_stage_load(st, xf, xsc, xsum, gi_n, g0, tok8_of(e.tok), nt);   // ahead of the ring: vmcnt is in order
     uint32_t ring[kBdDepth][2];
 #pragma unroll
     for (int d = 0; d < kBdDepth; ++d)
@@ -273,7 +273,7 @@ __global__ void __launch_bounds__(256) k_lr_v(int32_t in, const uint16_t* __rest
       const int prow = p0 + min(rw, nt - 1);
       const int tk = perm[prow];
       const int gi = (k0 + kk) / kGroup;
-      const uint32_t w = xsc[(size_t)prow * (in / kGroup) + gi];
+      const uint32_t w = xsc[(size_t)tk * (in / kGroup) + gi];   // scale words in token order
       const int bmax = max(max((int)(w & 0xFFu), (int)((w >> 8) & 0xFFu)),
                            max((int)((w >> 16) & 0xFFu), (int)(w >> 24)));
       const float f = pow2f(127 - bmax);   // |x| * f < 256

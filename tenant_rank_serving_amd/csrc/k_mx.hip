@@ -68,6 +68,10 @@ struct SegArg {
   int32_t v[DC_MAX_TENANTS + 1];
 };
 
+// Rows of the routing permutation the routing block keeps in LDS for the
+// work items' token lists (past them it reads them back from memory).
+constexpr int kPermLds = 2048;
+
 // ------------------------------------------------------------------- prep
 // Block 0 routes the tokens (stable counting sort by tenant; bucket n holds
 // the backbone-only tokens) and lists the buckets that have tokens, each with
@@ -110,8 +114,10 @@ __device__ __forceinline__ ActPos act_positions(int32_t n, const int* so) {
 
 // One matrix's work-item list: bucket b's items (its tenant record, region
 // offsets and derived U sizes, rows), then empty entries up to cap.
+template <class TokAt>
 __device__ __forceinline__ void act_write(const Tenant& mine, int32_t n, const int* so, const ActPos& ap, int32_t cap,
-                                          ActEntry* __restrict__ act, int32_t out, int32_t in, bool layouts) {
+                                          ActEntry* __restrict__ act, int32_t out, int32_t in, bool layouts,
+                                          TokAt tok_at) {
   const int tid = threadIdx.x, b = tid;
   ActEntry e{};
   e.base = b < n ? mine.base : nullptr;
@@ -142,6 +148,8 @@ __device__ __forceinline__ void act_write(const Tenant& mine, int32_t n, const i
   for (int j = 0; j < ap.items; ++j) {
     e.p0 = so[b] + j * kChunkRows;
     e.p1 = min(so[b] + (j + 1) * kChunkRows, so[b + 1]);
+#pragma unroll
+    for (int r = 0; r < kChunkRows; ++r) e.tok[r] = tok_at(min(e.p0 + r, e.p1 - 1));
     act[ap.pos + j] = e;
   }
   for (int i = ap.total + tid; i < cap; i += blockDim.x) {   // the rest of the list: empty entries
@@ -214,7 +222,8 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
       lds_barrier();
       const ActPos ap = act_positions(n, so);
 #pragma unroll
-      for (int j = 0; j < M; ++j) act_write(mine[j], n, so, ap, cap, pm.act[j], pm.params[j].out, in, pm.layouts != 0);
+      for (int j = 0; j < M; ++j)
+        act_write(mine[j], n, so, ap, cap, pm.act[j], pm.params[j].out, in, pm.layouts != 0, [](int p) { return p; });
       return;
     }
     __shared__ int cnt[DC_MAX_TENANTS + 1];   // tokens per bucket
@@ -222,6 +231,7 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
     __shared__ __attribute__((aligned(16))) int bkt[256];
     __shared__ int bad;
     __shared__ int wsum[4];
+    __shared__ int permL[kPermLds];   // the permutation's first kPermLds rows, for the work items
     for (int b = tid; b <= n; b += blockDim.x) cnt[b] = 0;
     if (tid == 0) bad = 0;
     lds_barrier();
@@ -258,9 +268,6 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
       if (tid == 0) *flags = bad ? 1u : 0u;
     }
     lds_barrier();
-    const ActPos ap = act_positions(n, so);
-#pragma unroll
-    for (int j = 0; j < M; ++j) act_write(mine[j], n, so, ap, cap, pm.act[j], pm.params[j].out, in, pm.layouts != 0);
     for (int c0 = 0; c0 < T; c0 += blockDim.x) {
       const int t = c0 + tid;
       int b = -1;
@@ -283,12 +290,22 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
           rank += (v.x == b) + (v.y == b) + (v.z == b) + (v.w == b);
         }
         for (int j = tid & ~3; j < tid; ++j) rank += (bkt[j] == b);
-        perm[next[b] + rank] = t;
+        const int pos = next[b] + rank;
+        perm[pos] = t;
+        if (pos < kPermLds) permL[pos] = t;
       }
       lds_barrier();
       if (t < T) atomicAdd(&next[b], 1);
       lds_barrier();
     }
+    // past kPermLds rows the work items read the permutation back from
+    // memory: a full barrier makes this block's stores of it visible
+    if (T > kPermLds) __syncthreads();
+    const ActPos ap = act_positions(n, so);
+    auto tok_at = [&](int p) { return p < kPermLds ? permL[p] : perm[p]; };
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+      act_write(mine[j], n, so, ap, cap, pm.act[j], pm.params[j].out, in, pm.layouts != 0, tok_at);
     return;
   }
   const int gi_n = in / kGroup;
@@ -296,24 +313,9 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
   if (item >= (size_t)T * gi_n) return;
   const int lane = tid & 63;
   const int t = (int)(item / gi_n), gi = (int)(item % gi_n);
-  // sorted position of token t, as block 0 routes it (bucket, then token
-  // order): the fragments, scales and sums are stored in that order
-  int ps = t;
-  if (mode == 1) {
-    auto bucket = [&](int u) { const int kk = ids[u]; return (kk < 0 || kk >= n) ? n : kk; };
-    const int bt = bucket(t);
-    ps = 0;
-    for (int c0 = 0; c0 < T; c0 += 64) {
-      const int u = c0 + lane;
-      bool before = false;
-      if (u < T) {
-        const int b = bucket(u);
-        before = b < bt || (b == bt && u < t);
-      }
-      ps += __popcll(__ballot(before));
-    }
-  }
-  const size_t sitem = (size_t)ps * gi_n + gi;
+  // fragments, scales and sums in token order (the V side finds a work
+  // item's tokens in the item)
+  const size_t sitem = (size_t)t * gi_n + gi;
   const uint16_t* xr = x + (size_t)t * in + (size_t)gi * kGroup;
   const uint16_t x0 = xr[lane], x1 = xr[lane + 64];
   const float v0 = __uint_as_float((uint32_t)x0 << 16);   // element j = lane (chunk lane/32)
@@ -425,7 +427,7 @@ __device__ __forceinline__ void v_load_grp(VGrp<B>& c, const VBuf& p, int np, in
 // live_wave: any of the wave's tiles holds a rank of the segment.
 template <int B>
 __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, int in, int s,
-                          const int32_t* __restrict__ perm, int p0, int p1, const uint8_t* __restrict__ xf,
+                          const Tok8 tok, int p0, int p1, const uint8_t* __restrict__ xf,
                           const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
                           const float* __restrict__ sigma, const VOut& vo, VLds& S) {
   static_assert(kVTiles == 2, "hold2 covers two tiles");
@@ -463,7 +465,7 @@ __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, i
     const int pb = p0;
     const int nt = min(kVRows, p1 - pb);
     VStage st;
-    v_stage_load(st, xf, xsc, xsum, gi_n, g0, pb, nt);   // ahead of the ring: vmcnt is in order
+    v_stage_load(st, xf, xsc, xsum, gi_n, g0, tok, nt);   // ahead of the ring: vmcnt is in order
     // Every wave issues the ring's first loads, also one with no rank of the
     // segment (its code offsets are past the region: out of range, no memory
     // request): loads on every path keep the waits for the x tiles exact.
@@ -533,7 +535,7 @@ __device__ void vside_blk(const Seg& sg, int tbase, int tile0, bool live_wave, i
 // slice, a pass's kVRows token rows and 4 rows at a time; the block sums per
 // (row, token) and adds sigma * partial into t.
 __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, const uint16_t* __restrict__ x,
-                           const int32_t* __restrict__ perm, int p0, int p1, const VOut& vo) {
+                           const Tok8 tok, int p0, int p1, const VOut& vo) {
   constexpr int kR = 2;   // rows per step: few live registers, so the V kernel fits 4 waves per SIMD
   __shared__ float red[4][kR][kVRows];   // [wave][row][token row]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -549,7 +551,7 @@ __device__ void vside_8bit(const Tenant& tn, const Layout& L, int in, int s, con
     uint4 xv[kVRows];
 #pragma unroll
     for (int t = 0; t < kVRows; ++t)
-      xv[t] = *reinterpret_cast<const uint4*>(x + (size_t)perm[pb + min(t, nt - 1)] * in + ic);
+      xv[t] = *reinterpret_cast<const uint4*>(x + (size_t)pick8u(tok, min(t, nt - 1)) * in + ic);
     for (int r0 = 0; r0 < sg.n; r0 += kR) {
       uint2 cw[kR];
       uint32_t e[kR];
@@ -670,7 +672,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) k
   layout_of_item(e, &L);
   if (tn.n8 > 0) {
     if (b == 0) {
-      vside_8bit(tn, L, in, s, x, perm, p0, p1, vo);
+      vside_8bit(tn, L, in, s, x, tok8_of(e.tok), p0, p1, vo);
       v_combine(vo, item, bv, p0, p1, 0, tn.n8);
       return;
     }
@@ -685,9 +687,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) k
   const int sn = three ? tn.n3 : tn.n2;
   const int tb = t_base(tn.n8, tn.n3, three ? 1 : 2);
   if (three)
-    vside_blk<3>(seg_of(tn, L, 1), tb, tile0, tile0 * 16 < sn, in, s, perm, p0, p1, xf, xsc, xsum, sigma, vo, S);
+    vside_blk<3>(seg_of(tn, L, 1), tb, tile0, tile0 * 16 < sn, in, s, tok8_of(e.tok), p0, p1, xf, xsc, xsum, sigma, vo, S);
   else
-    vside_blk<2>(seg_of(tn, L, 2), tb, tile0, tile0 * 16 < sn, in, s, perm, p0, p1, xf, xsc, xsum, sigma, vo, S);
+    vside_blk<2>(seg_of(tn, L, 2), tb, tile0, tile0 * 16 < sn, in, s, tok8_of(e.tok), p0, p1, xf, xsc, xsum, sigma, vo, S);
   // ranks of this block: kVRanks consecutive ranks of its segment
   const int rb0 = (three ? b : b - b3) * kVRanks;
   v_combine(vo, item, bv, p0, p1, tb + rb0, min(kVRanks, sn - rb0));
@@ -751,6 +753,7 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
                "s"(e.off[DC_REG_US3]), "s"(e.off[DC_REG_US2]), "s"(e.total));
   asm volatile("" ::"s"(e.tb3), "s"(e.tb2), "s"(e.np8), "s"(e.np3), "s"(e.np2), "s"(e.nc3), "s"(e.nc), "s"(e.rw3),
                "s"(e.rw2), "s"(e.kbn3), "s"(e.kbn2), "s"(e.wl3), "s"(e.wl2));
+  const Tok8 etok = tok8_of(e.tok);
   const int out = P.out;
   if (g * kGroup >= out) return;
   const int rs = P.rs;
@@ -854,9 +857,9 @@ __global__ void __launch_bounds__(kUWaves * 64) __attribute__((amdgpu_waves_per_
     // A-prep inputs: the W x loads, last in the burst, wait for them alone.
     int tko[2];
     float ybo[2] = {0.f, 0.f}, t8o[2][kU8Max];
-    auto load_tko = [&]() __attribute__((always_inline)) {
+    auto load_tko = [&]() __attribute__((always_inline)) {   // from the work item's token list
 #pragma unroll
-      for (int h = 0; h < 2; ++h) tko[h] = perm[pb + min(2 * q + h, nt - 1)];
+      for (int h = 0; h < 2; ++h) tko[h] = pick8(etok, min(2 * q + h, nt - 1));
     };
     auto epi_loads_t8 = [&]() __attribute__((always_inline)) {
 #pragma unroll

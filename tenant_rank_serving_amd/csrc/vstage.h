@@ -99,8 +99,40 @@ struct VLds {
   float xs[kVSlice][kVRows];          // group sums of x
 };
 
-// x fragments, scale words and group sums of sorted rows [pb, pb + kVRows)
-// for groups [g0, g0 + kVSlice), staged into LDS in two steps so that the
+// A work item's token list, passed by value (in registers), and its entry
+// i (0..7, per lane) by selects on constant indices.
+struct Tok8 {
+  int32_t v[8];
+};
+__device__ __forceinline__ Tok8 tok8_of(const int32_t (&t)[8]) {
+  Tok8 r;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r.v[k] = t[k];
+  return r;
+}
+__device__ __forceinline__ int pick8(const Tok8& t, int i) {
+  int r = t.v[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) {
+    r = i == k ? t.v[k] : r;
+    asm volatile("" : "+v"(r));   // a chain of selects: not turned into an indexed private-memory table
+  }
+  return r;
+}
+// The same for an index that is the same on every lane (scalar selects).
+__device__ __forceinline__ int pick8u(const Tok8& t, int i) {
+  int r = t.v[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) {
+    r = i == k ? t.v[k] : r;
+    asm volatile("" : "+s"(r));
+  }
+  return r;
+}
+
+// x fragments, scale words and group sums of a work item's token rows
+// (tokens tok[0 .. nt), stored in token order) for groups [g0, g0 + kVSlice),
+// staged into LDS in two steps so that the
 // loads can go out ahead of the code ring.  Thread tid moves int4 (tid & 15)
 // of the fragment of row (tid >> 4) & 7 for groups (tid >> 7) + 2u; threads
 // < 128 move the scale word and group sum of row tid & 7 and group
@@ -114,17 +146,17 @@ struct VStage {
 
 __device__ __forceinline__ void v_stage_load(VStage& st, const uint8_t* __restrict__ xf,
                                              const uint32_t* __restrict__ xsc, const float* __restrict__ xsum,
-                                             int gi_n, int g0, int pb, int nt) {
+                                             int gi_n, int g0, const Tok8 tok, int nt) {
   const int tid = threadIdx.x;
   const int k16 = tid & 15, rw = (tid >> 4) & 7, gh = tid >> 7;
-  const size_t row = (size_t)(pb + min(rw, nt - 1)) * gi_n;
+  const size_t row = (size_t)pick8(tok, min(rw, nt - 1)) * gi_n;
 #pragma unroll
   for (int u = 0; u < kVSlice / 2; ++u) {
     const int gi = min(g0 + gh + 2 * u, gi_n - 1);
     st.v[u] = reinterpret_cast<const i32x4*>(xf + (row + gi) * kXFrag)[k16];
   }
   const int sr = tid & 7, sgl = (tid >> 3) & (kVSlice - 1);
-  const size_t srow = (size_t)(pb + min(sr, nt - 1)) * gi_n + min(g0 + sgl, gi_n - 1);
+  const size_t srow = (size_t)pick8(tok, min(sr, nt - 1)) * gi_n + min(g0 + sgl, gi_n - 1);
   st.scw = xsc[srow];
   st.xsv = xsum[srow];
 }

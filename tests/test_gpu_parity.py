@@ -431,6 +431,31 @@ def test_multitenant_many_tokens():
     check_multitenant(y2, w, x, np.where(bad >= len(specs), -1, bad), ds, 128, "mt 700 bad id")
 
 
+def test_multitenant_tokens_past_lds_permutation():
+    """More routed rows than the routing block keeps in LDS (2048): the work
+    items past them take their token lists from the permutation in memory.
+    Against the oracle (fused and delta-only) and, token by token, against
+    single-tenant calls without the backbone."""
+    note("multitenant 2600 tokens")
+    rng = np.random.default_rng(29)
+    specs = [(128, 256, 2, 8, 22), (128, 256, 1, 3, 40), (128, 256, 0, 9, 0)]
+    ds = [synth.small_delta(900 + k, *s) for k, s in enumerate(specs)]
+    views = [upload(s, d) for s, d in zip(specs, ds)]
+    w = synth.base_weight(rng, 128, 256)
+    T = 2600
+    ids = rng.integers(-1, len(specs), size=T).astype(np.int32)
+    x = synth.activations(rng, T, 256)
+    for wb in (w, None):
+        y, bits, flag = _mt_run(views, wb, x, ids)
+        assert flag == 0
+        check_multitenant(y, wb, x, ids, ds, 128, "mt 2600 %s" % ("fused" if wb is not None else "delta"))
+    _, bits, _ = _mt_run(views, None, x, ids)
+    for k in range(len(specs)):
+        sel = np.nonzero(ids == k)[0]
+        _, single = run_decode(ds[k], w, x[sel], with_base=False)
+        assert np.array_equal(bits[sel], single)
+
+
 GROUP_CASES = [
     # (outs, in, shapes per tenant, n, T, backbone per matrix)
     ((512, 128, 256), 384, [(2, 8, 22), (1, 3, 40), (0, 9, 0), (2, 0, 17), (3, 20, 30)], 5, 40, (True, False, True)),
