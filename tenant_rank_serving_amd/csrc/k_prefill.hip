@@ -152,7 +152,9 @@ __global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* x, 
   // this thread's rank row and its segment
   const int arow = tid >> 1, qs = tid & 1;
   const int p = o0 + arow;
-  const PfSeg sg = seg_sel(tn, seg_of_pad(tn, p));
+  // every wave's 32 rows are one K-block of one segment (segments are padded
+  // to 32 ranks): the segment is the same on every lane
+  const PfSeg sg = seg_sel(tn, __builtin_amdgcn_readfirstlane(seg_of_pad(tn, p)));
   const int li = p - sg.p0;
   const bool valid = li < sg.n;
   const int np4 = (int)round_up(sg.n, 4);
