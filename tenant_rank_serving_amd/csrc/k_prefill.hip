@@ -283,26 +283,30 @@ __global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* x, 
 
 // ----------------------------------------------------------------- t split
 // In place, per token row of the launch's tenants: t'[p] = t[p] 2^-e(tok)
-// as fp16 hi = fp16(t') and lo = fp16(t' - hi), stored as one word hi |
-// lo << 16 where t[p] was: once per (token, rank), not once per row tile of
-// the U product.  Thread: 4 consecutive ranks of one token.
+// as fp16 hi = fp16(t') and lo = fp16(t' - hi): once per (token, rank), not
+// once per row tile of the U product.  Each 8 ranks' 32 bytes become their 8
+// hi values, then their 8 lo values, so that the U product's staging copies
+// them into its operand tiles as they are.  Thread: 8 consecutive ranks of
+// one token.
 __global__ void __launch_bounds__(256) k_pf_t(float* __restrict__ tw, const uint32_t* __restrict__ tmax, int32_t tok0,
                                               int32_t ntok, int32_t ldt) {
-  const int per = ldt / 4;
+  const int per = ldt / 8;
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (size_t)ntok * per) return;
-  const int tok = tok0 + (int)(i / per), c = (int)(i % per) * 4;
+  const int tok = tok0 + (int)(i / per), c = (int)(i % per) * 8;
   const float tinv = pow2(-scale_exp(__uint_as_float(tmax[tok])));
   f32x4* p = reinterpret_cast<f32x4*>(tw + (size_t)tok * ldt + c);
-  const f32x4 v = *p;
-  uint32_t o[4];
+  const f32x4 v0 = p[0], v1 = p[1];
+  uint32_t hi[4], lo[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float x = v[e] * tinv;
-    const uint32_t h = f16b(x);
-    o[e] = h | (f16b(x - f16v(h)) << 16);
+  for (int e = 0; e < 8; e += 2) {
+    const float x0 = (e < 4 ? v0[e] : v1[e - 4]) * tinv, x1 = (e < 4 ? v0[e + 1] : v1[e - 3]) * tinv;
+    const uint32_t h0 = f16b(x0), h1 = f16b(x1);
+    hi[e / 2] = h0 | (h1 << 16);
+    lo[e / 2] = f16b(x0 - f16v(h0)) | (f16b(x1 - f16v(h1)) << 16);
   }
-  *reinterpret_cast<uint4*>(p) = make_uint4(o[0], o[1], o[2], o[3]);
+  reinterpret_cast<uint4*>(p)[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  reinterpret_cast<uint4*>(p)[1] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 }
 
 // ----------------------------------------------------------------- U product
@@ -324,7 +328,7 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
   const int og = o0 / kGroup;   // the tile's 128-row scale group
   const int tl_s = min(t0 + arow, N - 1);
   const int tok_s = s0 + tl_s;
-  // packed fp16 pairs (k_pf_t) of the tenant's t rows, through a buffer
+  // fp16 hi and lo values (k_pf_t) of the tenant's t rows, through a buffer
   // resource: its loads stay where they are issued
   const __amdgpu_buffer_rsrc_t rtw = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(tw + (size_t)s0 * ldt), 0,
                                                                        N * ldt * 4, kPfBufFlags);
@@ -396,23 +400,14 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
     uint4* da = reinterpret_cast<uint4*>(&lds[s][0][arow * kPUPad + hs * 32]);
     da[0] = make_uint4(h[0], h[1], h[2], h[3]);
     da[1] = make_uint4(h[4], h[5], h[6], h[7]);
-    // t'[p] arrives as one word hi | lo << 16: two ranks' words give a hi
-    // word and a lo word
-    uint32_t hi[8], lo[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        const uint32_t w0 = __float_as_uint(r.tr[j][e]), w1 = __float_as_uint(r.tr[j][e + 1]);
-        hi[2 * j + e / 2] = (w0 & 0xFFFFu) | (w1 << 16);
-        lo[2 * j + e / 2] = (w0 >> 16) | (w1 & 0xFFFF0000u);
-      }
+    // t' arrives as 8 hi values then 8 lo values per 8 ranks (k_pf_t): the
+    // operand tiles take them as they are
     uint4* dh = reinterpret_cast<uint4*>(&lds[s][1][arow * kPUPad + hs * 32]);
     uint4* dl = reinterpret_cast<uint4*>(&lds[s][2][arow * kPUPad + hs * 32]);
-    dh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    dh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
-    dl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    dl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+    dh[0] = __builtin_bit_cast(uint4, r.tr[0]);
+    dl[0] = __builtin_bit_cast(uint4, r.tr[1]);
+    dh[1] = __builtin_bit_cast(uint4, r.tr[2]);
+    dl[1] = __builtin_bit_cast(uint4, r.tr[3]);
   };
   const int wo = wave >> 1, wt = wave & 1;
   const int ra = (64 * wo + (lane & 15)) * kPUPad + (lane >> 4) * 16;
@@ -570,7 +565,7 @@ int launch_dense_prefill(const ApplyArgs& a) {
     hipLaunchKernelGGL(k_pf_v, dim3((tv + 7) / 8 * 8, (unsigned)cnt), dim3(256), 0, st, b, a.x, a.in, a.wl.drp, xsc,
                        tw, tmax);
     const int tok0 = b.t[0].s0, ntok = b.t[cnt - 1].s0 + b.t[cnt - 1].nt - tok0;   // the batch's segments are contiguous
-    const size_t nth = (size_t)ntok * (a.wl.drp / 4);
+    const size_t nth = (size_t)ntok * (a.wl.drp / 8);
     hipLaunchKernelGGL(k_pf_t, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st, tw, tmax, tok0, ntok, a.wl.drp);
     hipLaunchKernelGGL(k_pf_u, dim3((tu + 7) / 8 * 8, (unsigned)cnt), dim3(256), 0, st, b, A.out, a.wl.drp, tw, tmax,
                        ybase, A.y);
