@@ -69,14 +69,20 @@ __device__ __forceinline__ uint32_t code_of(const uint32_t* w) {
 
 // fp16 bits of s (q - z) for codes K0 .. K0 + N - 1 of w, two per word of
 // out; ONE: one scale word for all (a V chunk), else one per code (a U run).
+// Two codes at a time in packed fp16: 0x6400 | q is the fp16 value 1024 + q,
+// and the zero point is an integer of at most 8 bits (the quantizer's), so
+// (1024 + q) - (1024 + z) = q - z exactly and one fp16 multiply rounds
+// s (q - z) once, as the fp32 product rounded to fp16 would.
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 template <int B, int K0, int E, int N, bool ONE>
 struct Dequant {
   static __device__ __forceinline__ void run(const uint32_t* w, const uint32_t* sz, uint32_t* out) {
     if constexpr (E < N) {
-      const uint32_t s0 = ONE ? sz[0] : sz[E], s1 = ONE ? sz[0] : sz[E + 1];
-      const float v0 = f16v(s0 & 0xFFFFu) * ((float)code_of<B, K0 + E>(w) - f16v(s0 >> 16));
-      const float v1 = f16v(s1 & 0xFFFFu) * ((float)code_of<B, K0 + E + 1>(w) - f16v(s1 >> 16));
-      out[E / 2] = f16b(v0) | (f16b(v1) << 16);
+      const uint32_t qq = code_of<B, K0 + E>(w) | (code_of<B, K0 + E + 1>(w) << 16) | 0x64006400u;
+      const uint32_t sp = ONE ? (sz[0] & 0xFFFFu) * 0x10001u : (sz[E] & 0xFFFFu) | (sz[E + 1] << 16);
+      const uint32_t zp = ONE ? (sz[0] >> 16) * 0x10001u : (sz[E] >> 16) | (sz[E + 1] & 0xFFFF0000u);
+      const h2 d = __builtin_bit_cast(h2, qq) - (__builtin_bit_cast(h2, zp) + h2{(_Float16)1024.0f, (_Float16)1024.0f});
+      out[E / 2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, sp) * d);
       Dequant<B, K0, E + 2, N, ONE>::run(w, sz, out);
     }
   }
@@ -383,7 +389,11 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
                             __builtin_amdgcn_alignbyte(r.cd.w, r.cd.z, csh), __builtin_amdgcn_alignbyte(r.cd4, r.cd.w, csh)};
     uint32_t sz[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sz[e] = r.cli0 + e < r.cn ? r.szr[e >> 2][e & 3] : 0u;
+    for (int e = 0; e < 16; ++e) sz[e] = r.szr[e >> 2][e & 3];
+    if (r.cli0 + 16 > r.cn) {   // the segment's last K-block: words past its pairs are another row's
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sz[e] = r.cli0 + e < r.cn ? sz[e] : 0u;
+    }
     const int bsel = r.bsel;
     uint32_t h[8];
     if (bsel == 8) {   // cw holds this thread's 16 codes, one byte each
