@@ -107,6 +107,7 @@ struct GemmOp {
 struct GemmBatch {
   GemmOp op[kGBatch];
 };
+static_assert(kMaxGroup <= kGBatch, "a grouped call's backbone products fit one launch");
 
 __global__ void __launch_bounds__(256, 2) k_gemm(GemmBatch gb) {
   const GemmOp& op = gb.op[blockIdx.y];
@@ -393,8 +394,24 @@ int launch_base(const BaseMat* mats, int m, const uint16_t* x, const uint16_t* x
     bms.nm = m;
     const dim3 g((unsigned)rows, (unsigned)nks, (unsigned)((T + 63) / 64));
     hipLaunchKernelGGL(k_base_sk, g, dim3(kBaseWaves * 64), 0, st, bms, xt, in, T, nks);
-  } else {
-    return launch_tiled_base(mats[0].W, x, mats[0].ybase, mats[0].out, in, T, stream);
+  } else {   // every matrix of the group in one launch of the tiled product
+    GemmBatch gb{};
+    unsigned tiles = 0;
+    for (int j = 0; j < m; ++j) {
+      GemmOp& op = gb.op[j];
+      op.A = mats[j].W;
+      op.B = x;
+      op.M = mats[j].out;
+      op.N = T;
+      op.K = in;
+      op.ldb = in;
+      op.kb = in;
+      op.ldc = mats[j].out;
+      op.c32 = mats[j].ybase;
+      const unsigned tj = gemm_tiles(mats[j].out, T);
+      tiles = tj > tiles ? tj : tiles;
+    }
+    hipLaunchKernelGGL(k_gemm, dim3(tiles, (unsigned)m), dim3(256), 0, st, gb);
   }
   return (int)hipGetLastError();
 }

@@ -463,6 +463,8 @@ GROUP_CASES = [
     ((256, 384), 6144, [(2, 8, 22), (1, 30, 100), (0, 0, 0)], 3, 24, (True, True)),
     # four matrices of DC_MAX_TENANTS tenants: 12 KB of tenant records in one launch's arguments
     ((128, 256, 128, 384), 256, [(2, 8, 22), (0, 0, 0), (1, 12, 3), (0, 3, 40)], 128, 200, (True, True, False, True)),
+    # more than 256 tokens: the tiled backbone product, every matrix of the group in one launch
+    ((256, 128, 384), 256, [(2, 8, 22), (1, 3, 40), (0, 9, 0)], 3, 300, (True, True, True)),
 ]
 
 
@@ -747,6 +749,61 @@ def test_graph_replay_matches_eager():
                 assert t.equal(ys[i], ref[i]), "replay %d output %d" % (rep, i)
     check_multitenant(y_to_f64(ys[2]), w.cpu().numpy().view(np.uint16), xs[2].cpu().numpy().view(np.uint16),
                       ids.cpu().numpy(), ds, 256, "graph replay vs oracle")
+
+
+def test_graph_replay_fused_groups():
+    """Two fused grouped calls (m = 2, 2048 inputs: the backbone product has
+    four K ranges, whose partials are summed in a fixed order beside the V
+    side) captured as one HIP graph on one stream: every replay, with eager
+    work and synchronizations between the replays, gives the eager outputs
+    bit for bit, and the outputs match the oracle."""
+    note("graph replay fused groups")
+    t = torch()
+    outs, inn, n, T = (256, 128), 2048, 3, 24
+    shapes = [(2, 8, 22), (1, 3, 40), (0, 9, 0)]
+    rng = np.random.default_rng(77)
+    ds = [[synth.small_delta(3000 + 17 * j + k, outs[j], inn, *shapes[k]) for k in range(n)] for j in range(2)]
+    views = [[upload(d.spec, d) for d in row] for row in ds]
+    specs = [[d.spec for d in row] for row in ds]
+    ws_np = [synth.base_weight(rng, o, inn) for o in outs]
+    wd = [dev_u16(w) for w in ws_np]
+    ids = rng.integers(0, n, size=T).astype(np.int32)
+    idd = dev_i32(ids)
+    xs = [synth.activations(rng, T, inn) for _ in range(3)]
+    xd = [dev_u16(x) for x in xs]
+    ys = [[t.empty((T, o), dtype=t.int16, device="cuda") for o in outs] for _ in range(3)]
+    wss = [t.empty(trs.dc_group_workspace_bytes(specs, 2, T), dtype=t.uint8, device="cuda") for _ in range(2)]
+    s0 = t.cuda.Stream()
+    calls = [trs.GroupCall(views, wd, xd[i], idd, ys[i], wss[0], stream=s0.cuda_stream) for i in range(2)]
+    extra = trs.GroupCall(views, wd, xd[2], idd, ys[2], wss[1], stream=s0.cuda_stream)   # eager work between replays
+
+    def step():
+        for c in calls:
+            c()
+
+    with t.cuda.stream(s0):
+        step()
+        t.cuda.synchronize()
+        ref = [[y.clone() for y in row] for row in ys[:2]]
+        g = t.cuda.CUDAGraph()
+        with t.cuda.graph(g, stream=s0):
+            step()
+        t.cuda.synchronize()
+        for rep in range(4):
+            for row in ys[:2]:
+                for y in row:
+                    y.fill_(0x7FC0)
+            extra()
+            t.cuda.synchronize()
+            g.replay()
+            t.cuda.synchronize()
+            for i in range(2):
+                for j in range(2):
+                    assert t.equal(ys[i][j], ref[i][j]), "replay %d call %d matrix %d" % (rep, i, j)
+    for i in range(3):
+        for j in range(2):
+            check_multitenant(y_to_f64(ys[i][j]), ws_np[j], xs[i], ids, ds[j], outs[j],
+                              "graph fused group call %d matrix %d" % (i, j))
 
 
 # ------------------------------------------------------- quantize + pack on GPU
