@@ -112,20 +112,19 @@ __device__ __forceinline__ ActPos act_positions(int32_t n, const int* so) {
   return ActPos{pos, items, total};
 }
 
-// One matrix's work-item list: bucket b's items (its tenant record, region
-// offsets and derived U sizes, rows), then empty entries up to cap.
+// Bucket b's work items of one matrix (its tenant record, region offsets and
+// derived U sizes, rows) at list positions pos .. pos + items - 1.
 template <class TokAt>
-__device__ __forceinline__ void act_write(const Tenant& mine, int32_t n, const int* so, const ActPos& ap, int32_t cap,
-                                          ActEntry* __restrict__ act, int32_t out, int32_t in, bool layouts,
-                                          TokAt tok_at) {
-  const int tid = threadIdx.x, b = tid;
+__device__ __forceinline__ void act_write_bucket(const Tenant& mine, int b, int32_t n, const int* so, int pos,
+                                                 int items, ActEntry* __restrict__ act, int32_t out, int32_t in,
+                                                 bool layouts, TokAt tok_at) {
   ActEntry e{};
   e.base = b < n ? mine.base : nullptr;
   e.n8 = b < n ? mine.n8 : 0;
   e.n3 = b < n ? mine.n3 : 0;
   e.n2 = b < n ? mine.n2 : 0;
   e.k = b;
-  if (layouts && b < n && ap.items > 0) {
+  if (layouts && b < n && items > 0) {
     Layout L;
     layout_of(out, in, e.n8, e.n3, e.n2, &L);
 #pragma unroll
@@ -145,17 +144,12 @@ __device__ __forceinline__ void act_write(const Tenant& mine, int32_t n, const i
     e.wl3 = e.rw3 - (e.kbn3 - 1) * 3;
     e.wl2 = e.rw2 - (e.kbn2 - 1) * 2;
   }
-  for (int j = 0; j < ap.items; ++j) {
+  for (int j = 0; j < items; ++j) {
     e.p0 = so[b] + j * kChunkRows;
     e.p1 = min(so[b] + (j + 1) * kChunkRows, so[b + 1]);
 #pragma unroll
     for (int r = 0; r < kChunkRows; ++r) e.tok[r] = tok_at(min(e.p0 + r, e.p1 - 1));
-    act[ap.pos + j] = e;
-  }
-  for (int i = ap.total + tid; i < cap; i += blockDim.x) {   // the rest of the list: empty entries
-    ActEntry e{};
-    e.k = -1;
-    act[i] = e;
+    act[pos + j] = e;
   }
 }
 
@@ -177,6 +171,43 @@ struct PrepMats {
   int32_t ncnt[kMaxGroup];
   int32_t layouts;            // Delta-CoMe buffers: the work items carry their region offsets
 };
+
+// (matrix j, bucket b) pair of thread tid (j-major over M (n + 1) pairs): its
+// tenant record goes out with the routing's first loads.
+template <int M>
+__device__ __forceinline__ Tenant first_record(const GroupTables<M>& gt, int32_t n) {
+  const int tid = threadIdx.x, nb = n + 1;
+  const int j = tid / nb, b = tid - j * nb;
+  return tid < M * nb && b < n ? gt.t[j].t[b] : Tenant{};
+}
+
+// Every matrix's work-item list: the buckets' items (thread tid takes the
+// pairs tid, tid + 256, ..., so the matrices' lists are written side by
+// side), then empty entries up to cap.
+template <int M, class TokAt>
+__device__ __forceinline__ void act_write_all(const GroupTables<M>& gt, const Tenant& first, int32_t n,
+                                              const int* so, const ActPos& ap, int32_t cap, const PrepMats& pm,
+                                              int32_t in, TokAt tok_at) {
+  __shared__ int spos[DC_MAX_TENANTS + 1], sitems[DC_MAX_TENANTS + 1];
+  const int tid = threadIdx.x, nb = n + 1;
+  if (tid < nb) {
+    spos[tid] = ap.pos;
+    sitems[tid] = ap.items;
+  }
+  lds_barrier();
+  for (int idx = tid; idx < M * nb; idx += blockDim.x) {
+    const int j = idx / nb, b = idx - j * nb;
+    const Tenant mine = idx == tid ? first : (b < n ? gt.t[j].t[b] : Tenant{});
+    act_write_bucket(mine, b, n, so, spos[b], sitems[b], pm.act[j], pm.params[j].out, in, pm.layouts != 0, tok_at);
+  }
+#pragma unroll
+  for (int j = 0; j < M; ++j)
+    for (int i = ap.total + tid; i < cap; i += blockDim.x) {   // the rest of the list: empty entries
+      ActEntry e{};
+      e.k = -1;
+      pm.act[j][i] = e;
+    }
+}
 
 template <int M>
 __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t* __restrict__ x,
@@ -208,9 +239,7 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
     // together (the kernel arguments live in memory and the indexing is per
     // thread)
     const int k_first = mode == 1 && tid < T ? ids[tid] : -1;
-    Tenant mine[M];
-#pragma unroll
-    for (int j = 0; j < M; ++j) mine[j] = tid < n ? gt.t[j].t[tid] : Tenant{};
+    const Tenant first = first_record(gt, n);
     if (mode != 1) {
       for (int p = tid; p < T; p += blockDim.x) perm[p] = p;
       if (tid == 0) {
@@ -221,9 +250,7 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
       }
       lds_barrier();
       const ActPos ap = act_positions(n, so);
-#pragma unroll
-      for (int j = 0; j < M; ++j)
-        act_write(mine[j], n, so, ap, cap, pm.act[j], pm.params[j].out, in, pm.layouts != 0, [](int p) { return p; });
+      act_write_all(gt, first, n, so, ap, cap, pm, in, [](int p) { return p; });
       return;
     }
     __shared__ int cnt[DC_MAX_TENANTS + 1];   // tokens per bucket
@@ -303,9 +330,7 @@ __global__ void __launch_bounds__(256) k_prep(GroupTables<M> gt, const uint16_t*
     if (T > kPermLds) __syncthreads();
     const ActPos ap = act_positions(n, so);
     auto tok_at = [&](int p) { return p < kPermLds ? permL[p] : perm[p]; };
-#pragma unroll
-    for (int j = 0; j < M; ++j)
-      act_write(mine[j], n, so, ap, cap, pm.act[j], pm.params[j].out, in, pm.layouts != 0, tok_at);
+    act_write_all(gt, first, n, so, ap, cap, pm, in, tok_at);
     return;
   }
   const int gi_n = in / kGroup;
