@@ -316,7 +316,7 @@ inline bool ws_layout(int32_t T, int32_t in, int32_t n, int32_t m, const int32_t
   W->perm = take(4 * (size_t)T);
   W->nact = act_capacity(n, T);
   const size_t items = (size_t)T * (in / kGroup);
-  W->xf = take(256 * items);
+  W->xf = take(256 * items);   // 2 T in bytes: the dense prefill form keeps x' (fp16 [T][in]) here
   W->xsc = take(4 * items);
   W->xsum = take(4 * items);
   W->xt = take(2 * (size_t)in * round_up((size_t)T, 16));

@@ -145,7 +145,7 @@ __device__ __forceinline__ bool tile_of(int nto, int ntt, int& o0, int& t0) {
 // 64 inputs through two LDS buffers.  Staging thread: rank row tid/2, code
 // chunk tid%2 of the K chunk (32 codes, one word run), and token rows
 // 32 it + tid/8, 8 inputs each.
-__global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* x, int32_t in,
+__global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* xh, int32_t in,
                                                  int32_t ldt, const float* __restrict__ xsc, float* __restrict__ tw,
                                                  uint32_t* __restrict__ tmax) {
   const PfTenant& tn = pb.t[blockIdx.y];
@@ -164,16 +164,14 @@ __global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* x, 
   const int li = p - sg.p0;
   const bool valid = li < sg.n;
   const int np4 = (int)round_up(sg.n, 4);
-  // token rows of the x staging and their rescale
+  // token rows of the x' staging (x rescaled per token to fp16 by the prep kernel)
   const uint16_t* xp[4];
-  float xi[4];
   int so[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int row = it * 32 + (tid >> 3), c = tid & 7;
     const int tok = s0 + min(t0 + row, N - 1);
-    xp[it] = x + (size_t)tok * in + c * 8;
-    xi[it] = xsc[tok];
+    xp[it] = xh + (size_t)tok * in + c * 8;
     so[it] = row * kPVPad + c * 16;
   }
   u32x4 ca, cb;   // the code words as loaded: unpacked in swrite, so that
@@ -207,16 +205,8 @@ __global__ void __launch_bounds__(256, 2) k_pf_v(PfBatch pb, const uint16_t* x, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) dst[j] = make_uint4(h[4 * j], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const uint32_t wv[4] = {rx[it].x, rx[it].y, rx[it].z, rx[it].w};
-      uint32_t o[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float lo = __uint_as_float(wv[j] << 16) * xi[it], hi = __uint_as_float(wv[j] & 0xFFFF0000u) * xi[it];
-        o[j] = f16b(lo) | (f16b(hi) << 16);
-      }
-      *reinterpret_cast<uint4*>(&lds[s][1][so[it]]) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+    for (int it = 0; it < 4; ++it)
+      *reinterpret_cast<uint4*>(&lds[s][1][so[it]]) = make_uint4(rx[it].x, rx[it].y, rx[it].z, rx[it].w);
   };
   const int wo = wave >> 1, wt = wave & 1;
   const int ra = (64 * wo + (lane & 15)) * kPVPad + (lane >> 4) * 16;
@@ -489,11 +479,13 @@ __global__ void __launch_bounds__(256, 2) k_pf_u(PfBatch pb, int32_t out, int32_
   }
 }
 
-// Per token: the rescale 2^-e of x (largest |x| into [2^14, 2^15)); clears
-// the token's largest |t| and the call's status word.  One wave per token.
+// Per token: the rescale 2^-e of x (largest |x| into [2^14, 2^15)) and the
+// rescaled row x' = fp16(x 2^-e) [T][in] that the V product's staging copies
+// (once per token, not once per rank tile); clears the token's largest |t|
+// and the call's status word.  One wave per token.
 __global__ void __launch_bounds__(256) k_pf_prep(const uint16_t* __restrict__ x, int32_t T, int32_t in,
-                                                 float* __restrict__ xsc, uint32_t* __restrict__ tmax,
-                                                 uint32_t* __restrict__ flags) {
+                                                 float* __restrict__ xsc, uint16_t* __restrict__ xh,
+                                                 uint32_t* __restrict__ tmax, uint32_t* __restrict__ flags) {
   const int tok = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
   if (tok >= T) return;
@@ -508,9 +500,24 @@ __global__ void __launch_bounds__(256) k_pf_prep(const uint16_t* __restrict__ x,
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  const float xi = pow2(-scale_exp(m));   // the same on every lane
   if (lane == 0) {
-    xsc[tok] = pow2(-scale_exp(m));
+    xsc[tok] = xi;
     tmax[tok] = 0u;
+  }
+  // bf16 values times a power of two convert to fp16 exactly (unless 2^24
+  // below the token's largest); the second read of the row is from L2
+  uint16_t* orow = xh + (size_t)tok * in;
+  for (int k = lane * 8; k < in; k += 512) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + k);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = __uint_as_float(w[j] << 16) * xi, hi = __uint_as_float(w[j] & 0xFFFF0000u) * xi;
+      o[j] = f16b(lo) | (f16b(hi) << 16);
+    }
+    *reinterpret_cast<uint4*>(orow + k) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -529,8 +536,12 @@ int launch_dense_prefill(const ApplyArgs& a) {
   float* xsc = reinterpret_cast<float*>(a.ws + a.wl.dxs);
   uint32_t* tmax = reinterpret_cast<uint32_t*>(a.ws + a.wl.dtm);
   uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + a.wl.flags);
+  // x' (fp16 [T][in]) in the region of the decode kernels' x fragments, which
+  // this form does not use (2 T in bytes either way)
+  uint16_t* xh = reinterpret_cast<uint16_t*>(a.ws + a.wl.xf);
   if (A.W) launch_tiled_base(A.W, a.x, ybase, A.out, a.in, a.T, a.stream);
-  hipLaunchKernelGGL(k_pf_prep, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, st, a.x, a.T, a.in, xsc, tmax, flags);
+  hipLaunchKernelGGL(k_pf_prep, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, st, a.x, a.T, a.in, xsc, xh, tmax,
+                     flags);
   int k = 0;
   while (k < a.n) {   // tenants with tokens, kPfBatch per launch
     PfBatch b{};
@@ -572,7 +583,7 @@ int launch_dense_prefill(const ApplyArgs& a) {
     }
     if (cnt == 0) break;
     // grid x a multiple of 8, so that blockIdx.x mod 8 is the XCD the tile order assumes
-    hipLaunchKernelGGL(k_pf_v, dim3((tv + 7) / 8 * 8, (unsigned)cnt), dim3(256), 0, st, b, a.x, a.in, a.wl.drp, xsc,
+    hipLaunchKernelGGL(k_pf_v, dim3((tv + 7) / 8 * 8, (unsigned)cnt), dim3(256), 0, st, b, xh, a.in, a.wl.drp, xsc,
                        tw, tmax);
     const int tok0 = b.t[0].s0, ntok = b.t[cnt - 1].s0 + b.t[cnt - 1].nt - tok0;   // the batch's segments are contiguous
     const size_t nth = (size_t)ntok * (a.wl.drp / 8);
