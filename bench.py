@@ -421,7 +421,9 @@ def config_bench(args):
       c4  Mistral-7B layer (grouped-query k, v 1024x4096) at the 1/32 budget,
           16 tenants, 128 tokens (dc_apply_multitenant), 3 copies cycled.
     Fused (backbone + delta) and delta-only; flops are 2 T r (out + in) per
-    matrix for the delta and 2 T out in for the backbone."""
+    matrix for the delta and 2 T out in for the backbone.  c1 and c4 also run
+    the layer as grouped calls with every layer copy captured as one HIP graph
+    (key grouped_graph)."""
     import numpy as np
     import torch
 
@@ -527,17 +529,19 @@ def config_bench(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (args.steps * copies)
 
-    # c4: the layer as grouped calls (q+k+v, o, gate+up, down) on one stream,
-    # all layer copies captured as one HIP graph, replayed
+    # c1, c4: the layer as grouped calls (q+k+v, o, gate+up, down) on one
+    # stream, all layer copies captured as one HIP graph, replayed (c1: the
+    # one tenant's tokens all carry id 0)
     groups = [[0, 1, 2], [3], [4, 5], [6]]
     ym = [torch.empty((tmax, o), dtype=torch.int16, device=dev) for _, o, _ in mats]
+    gids = ids if w == "c4" else torch.zeros(tmax, dtype=torch.int32, device=dev)
 
     def grouped_graph_ms(T, fused):
         gstream = torch.cuda.Stream()
         gws = torch.empty(max(trs.dc_group_workspace_bytes([[specs[m]] * n_ten for m in g], len(g), T) for g in groups),
                           dtype=torch.uint8, device=dev)
-        calls = [trs.GroupCall([views[c][m] for m in g], [W[c][m] for m in g] if fused else None, X[g[0]][:T], ids,
-                               [ym[m][:T] for m in g], gws, stream=gstream.cuda_stream)
+        calls = [trs.GroupCall([views[c][m] for m in g], [W[c][m] for m in g] if fused else None, X[g[0]][:T],
+                               gids[:T], [ym[m][:T] for m in g], gws, stream=gstream.cuda_stream)
                  for c in range(copies) for g in groups]
         with torch.cuda.stream(gstream):
             for _ in range(max(args.warmup, 1)):
@@ -588,7 +592,7 @@ def config_bench(args):
             "bytes_per_layer": {"packed_delta": int(delta_bytes), "backbone": int(base_bytes), "x_y": int(xy)},
             "flops_per_layer": {"delta": f_delta, "backbone": f_base},
         }
-        if w == "c4":
+        if w in ("c1", "c4"):
             gf, gd = grouped_graph_ms(T, True), grouped_graph_ms(T, False)
             log("%s T=%d grouped + graph: fused %.4f ms/layer, delta-only %.4f ms/layer" % (w, T, gf, gd))
             res["grouped_graph"] = {
